@@ -1,0 +1,222 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE ONLY. Not part of the product path.
+ *
+ * A plain, slow, obviously correct fp64 CPU implementation of what the
+ * block-dequant GEMV computes. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call it. It shares no code, header,
+ * table or constant with the HIP library: it reads the canonical GGUF-style
+ * block bytes directly and writes everything out by the definitions.
+ *
+ * What is computed (the plain definition that the fused kernels reorder):
+ *   W[n][k] = d(n, k/32) * v(n, k)         dequantised weight, exact in double
+ *   y[n]    = sum_{k<K} W[n][k] * x[k]      natural k order, in double
+ *   a[n]    = sum_{k<K} |W[n][k] * x[k]|    magnitude sum used by the tolerance
+ *
+ * Sources (pages, not code):
+ *  - "EdgeRunner beats llama.cpp" (chriskarani.xyz), section "What worked",
+ *    item 2 "Fused Q8_0 dequant + GEMV": weights are read quantised and the
+ *    dequantisation happens inside the matrix-vector product, with no float
+ *    copy of the weights. The oracle is the unfused definition of that product.
+ *  - RunIT_Mac README, optimisation table: Q8_0 costs 1.06 bytes per weight and
+ *    Q4_0 0.56, i.e. 34 B and 18 B per 32-weight block (one fp16 scale each).
+ *  - RunIT_Mac README, kernel table: the GEMVs take fp32 activations and write
+ *    fp32 outputs ("f32in_f32out"); the data-flow figure accumulates in f32.
+ *  - robotnurse.io "We wrote our own inference engine", "Correctness first":
+ *    a slow reference of every layer is kept beside the GPU kernels as a
+ *    parity gate. This file is that reference for the GEMV.
+ *  - RunIT_Mac README, "Fused gate+up+silu": the gate and up projections and
+ *    the SiLU product are one step; out = silu(gate) * up.
+ *
+ * Readings where the pages are silent (each is also listed in the design notes):
+ *  - Block field order is the GGUF one: little-endian fp16 scale first, then
+ *    the quants.  Q8_0 quants are int8, the full range -128..127 is accepted.
+ *  - Q4_0: byte j (0..15) of the quant field holds element j in its low nibble
+ *    and element j+16 in its high nibble (GGUF convention); value = nibble - 8.
+ *  - fp16 decoding follows IEEE 754 binary16 exactly, subnormals included.
+ *  - silu(g) = g / (1 + exp(-g)).
+ *
+ * Exactness: the fp16 decode, the int->double conversion, d*q (<= 19
+ * significant bits) and (d*q)*x (<= 43 bits) are all exact in double, so the
+ * only rounding is in the running sum: |y - exact| <= K * 2^-53 * a[n].
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_Q8_0 = 1, ORACLE_Q4_0 = 2, ORACLE_F16 = 3 };
+
+/* IEEE 754 binary16 -> double, exact. */
+double oracle_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);                 /* zero and subnormals */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);     /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+static uint16_t read_le16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+/* Dequantised weight of element i (0..31) of one canonical block. */
+static double q8_0_weight(const uint8_t *blk, int i)
+{
+    double d = oracle_half_to_double(read_le16(blk));
+    int q = (int)(int8_t)blk[2 + i];
+    return d * (double)q;
+}
+
+static double q4_0_weight(const uint8_t *blk, int i)
+{
+    double d = oracle_half_to_double(read_le16(blk));
+    const uint8_t *qs = blk + 2;
+    int nib = (i < 16) ? (qs[i] & 0x0f) : (qs[i - 16] >> 4);
+    return d * (double)(nib - 8);
+}
+
+/* One output row: y = sum W[n][k] x[k], a = sum |W[n][k] x[k]|. */
+static void one_row(int kind, const uint8_t *w, const float *x, int64_t n, int64_t K,
+                    double *y, double *a)
+{
+    double sum = 0.0, asum = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double wk;
+        if (kind == ORACLE_Q8_0) {
+            const uint8_t *blk = w + (n * (K / 32) + k / 32) * 34;
+            wk = q8_0_weight(blk, (int)(k % 32));
+        } else if (kind == ORACLE_Q4_0) {
+            const uint8_t *blk = w + (n * (K / 32) + k / 32) * 18;
+            wk = q4_0_weight(blk, (int)(k % 32));
+        } else {
+            wk = oracle_half_to_double(read_le16(w + (n * K + k) * 2));
+        }
+        double p = wk * (double)x[k];
+        sum += p;
+        asum += fabs(p);
+    }
+    *y = sum;
+    *a = asum;
+}
+
+static int bad_args(int kind, int64_t N, int64_t K)
+{
+    if (N < 0 || K < 0) return 1;
+    if (kind != ORACLE_Q8_0 && kind != ORACLE_Q4_0 && kind != ORACLE_F16) return 1;
+    if (kind != ORACLE_F16 && K % 32 != 0) return 1;
+    return 0;
+}
+
+/* Rows [r0, r1) of y = W x. */
+int oracle_gemv_range(int kind, const void *w, const float *x, double *y, double *a,
+                      int64_t N, int64_t K, int64_t r0, int64_t r1)
+{
+    if (bad_args(kind, N, K) || r0 < 0 || r1 > N || r0 > r1) return 1;
+    for (int64_t n = r0; n < r1; ++n)
+        one_row(kind, (const uint8_t *)w, x, n, K, &y[n], a ? &a[n] : &(double){0});
+    return 0;
+}
+
+/* A chosen list of rows: y[i], a[i] belong to row rows[i]. */
+int oracle_gemv_rows(int kind, const void *w, const float *x, const int64_t *rows,
+                     int64_t nrows, double *y, double *a, int64_t N, int64_t K)
+{
+    if (bad_args(kind, N, K)) return 1;
+    for (int64_t i = 0; i < nrows; ++i) {
+        if (rows[i] < 0 || rows[i] >= N) return 1;
+        double dummy;
+        one_row(kind, (const uint8_t *)w, x, rows[i], K, &y[i], a ? &a[i] : &dummy);
+    }
+    return 0;
+}
+
+/* ---- static row ranges over plain pthreads ------------------------------ */
+
+struct job {
+    int kind;
+    const void *w;
+    const float *x;
+    double *y, *a;
+    int64_t N, K, r0, r1;
+};
+
+static void *job_main(void *p)
+{
+    struct job *j = (struct job *)p;
+    oracle_gemv_range(j->kind, j->w, j->x, j->y, j->a, j->N, j->K, j->r0, j->r1);
+    return NULL;
+}
+
+/* y = W x over all N rows, split into nthreads equal static row ranges. */
+int oracle_gemv(int kind, const void *w, const float *x, double *y, double *a,
+                int64_t N, int64_t K, int nthreads)
+{
+    if (bad_args(kind, N, K)) return 1;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads == 1 || N < nthreads)
+        return oracle_gemv_range(kind, w, x, y, a, N, K, 0, N);
+    pthread_t tid[256];
+    struct job jobs[256];
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = (struct job){kind, w, x, y, a, N, K, N * t / nthreads, N * (t + 1) / nthreads};
+        if (pthread_create(&tid[t], NULL, job_main, &jobs[t]) != 0) {
+            job_main(&jobs[t]);
+            tid[t] = 0;
+        }
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (tid[t]) pthread_join(tid[t], NULL);
+    return 0;
+}
+
+/* ---- gate/up with the SiLU product -------------------------------------- */
+
+double oracle_silu(double g) { return g / (1.0 + exp(-g)); }
+
+/* out[n] = silu(g[n]) * u[n], g = Wgate x, u = Wup x. g, u, ag, au may be
+ * returned for tolerance propagation (pass NULL to skip). */
+int oracle_gateup_silu(int kind, const void *gate, const void *up, const float *x,
+                       double *out, double *g, double *u, double *ag, double *au,
+                       int64_t N_ff, int64_t K, int nthreads)
+{
+    if (kind == ORACLE_F16 || bad_args(kind, N_ff, K)) return 1;
+    double *gg = g ? g : (double *)malloc(sizeof(double) * (size_t)(N_ff ? N_ff : 1));
+    double *uu = u ? u : (double *)malloc(sizeof(double) * (size_t)(N_ff ? N_ff : 1));
+    double *aag = ag ? ag : (double *)malloc(sizeof(double) * (size_t)(N_ff ? N_ff : 1));
+    double *aau = au ? au : (double *)malloc(sizeof(double) * (size_t)(N_ff ? N_ff : 1));
+    int rc = 1;
+    if (gg && uu && aag && aau) {
+        rc = oracle_gemv(kind, gate, x, gg, aag, N_ff, K, nthreads);
+        if (!rc) rc = oracle_gemv(kind, up, x, uu, aau, N_ff, K, nthreads);
+        if (!rc)
+            for (int64_t n = 0; n < N_ff; ++n) out[n] = oracle_silu(gg[n]) * uu[n];
+    }
+    if (!g) free(gg);
+    if (!u) free(uu);
+    if (!ag) free(aag);
+    if (!au) free(aau);
+    return rc;
+}
+
+/* ---- multi-row "verify": each activation row on its own ----------------- */
+
+/* Y[m][n] = sum_k W[n][k] X[m][k] for m < M; row m is exactly the M=1 result
+ * for X[m], which is what the verify pass must reproduce. */
+int oracle_verify(int kind, const void *w, const float *X, double *Y, double *A,
+                  int64_t N, int64_t K, int M, int nthreads)
+{
+    if (M < 1 || bad_args(kind, N, K)) return 1;
+    for (int m = 0; m < M; ++m) {
+        int rc = oracle_gemv(kind, w, X + (int64_t)m * K, Y + (int64_t)m * N,
+                             A ? A + (int64_t)m * N : NULL, N, K, nthreads);
+        if (rc) return rc;
+    }
+    return 0;
+}

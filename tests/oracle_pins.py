@@ -1,0 +1,302 @@
+"""Pins of the fp64 oracle to facts other than itself.
+
+Each pin is a function of a loaded oracle library ``L`` and raises
+AssertionError when the oracle disagrees with:
+  * IEEE binary16 decoding as numpy implements it (all 65536 patterns),
+  * the byte sizes the pages print (1.06 and 0.56 bytes per weight),
+  * hand-worked closed forms of single blocks (tests/golden/single_blocks.json),
+  * exact rational brute force on tiny random shapes (fractions.Fraction),
+  * textbook special cases that reduce to a float64 numpy matmul,
+  * invariants (exact scaling, zero blocks, row permutation),
+  * the composition rules of the fused and multi-row entry points.
+``test_oracle_mutants.py`` plants plausible mistakes in a copy of oracle.c and
+checks that every one of them trips at least one pin.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle as O
+from block_dequant_gemv_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---- tiny canonical block builders (test side, written from the format) ----
+
+def q8_block(scale_bits: int, quants) -> bytes:
+    quants = list(quants)
+    assert len(quants) == 32
+    return bytes([scale_bits & 0xFF, scale_bits >> 8]) + bytes(q & 0xFF for q in quants)
+
+
+def q4_block_from_bytes(scale_bits: int, qs) -> bytes:
+    qs = list(qs)
+    assert len(qs) == 16
+    return bytes([scale_bits & 0xFF, scale_bits >> 8]) + bytes(qs)
+
+
+def q4_block_from_values(scale_bits: int, vals) -> bytes:
+    """Encode 32 values in [-8, 7]: byte j = (v[j]+8) | (v[j+16]+8) << 4."""
+    vals = list(vals)
+    assert len(vals) == 32 and all(-8 <= v <= 7 for v in vals)
+    qs = [((vals[j] + 8) & 0xF) | (((vals[j + 16] + 8) & 0xF) << 4) for j in range(16)]
+    return q4_block_from_bytes(scale_bits, qs)
+
+
+def _u8(b: bytes) -> np.ndarray:
+    return np.frombuffer(b, dtype=np.uint8).copy()
+
+
+def _gemv(L, kind, w, x, N, K, threads=1):
+    return O.gemv(kind, w, x, N, K, threads=threads, L=L)
+
+
+# ---- independent exact decoding for brute force ----------------------------
+
+def _exact_weights(kind: str, w: np.ndarray, N: int, K: int):
+    """Fractions W[n][k] decoded with numpy's fp16 and the format definition."""
+    rows = []
+    if kind == "f16":
+        vals = w.view(np.uint16).astype("<u2").view(np.float16).astype(np.float64).reshape(N, K)
+        return [[Fraction(float(v)) for v in r] for r in vals]
+    bb = W.Q8_0_BLOCK_BYTES if kind == "q8_0" else W.Q4_0_BLOCK_BYTES
+    blocks = w.reshape(N, K // 32, bb)
+    for n in range(N):
+        row = []
+        for b in range(K // 32):
+            blk = blocks[n, b]
+            d = Fraction(float(blk[0:2].copy().view("<u2").view(np.float16)[0]))
+            if kind == "q8_0":
+                q = blk[2:].view(np.int8).astype(int)
+                row += [d * int(v) for v in q]
+            else:
+                qs = blk[2:].astype(int)
+                lo = [int(v) & 0xF for v in qs]
+                hi = [int(v) >> 4 for v in qs]
+                row += [d * (v - 8) for v in lo + hi]
+        rows.append(row)
+    return rows
+
+
+# ---- the pins --------------------------------------------------------------
+
+def pin_half_decode_all_patterns(L):
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([L.oracle_half_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def pin_format_sizes(L):
+    g = _golden("format_sizes.json")
+    assert round(g["q8_0"]["block_bytes"] / g["block_weights"], 2) == g["q8_0"]["printed_bytes_per_weight"]
+    assert round(g["q4_0"]["block_bytes"] / g["block_weights"], 2) == g["q4_0"]["printed_bytes_per_weight"]
+    # the oracle must step exactly one block size per 32 weights: a two-block
+    # row whose blocks differ is read as two independent blocks
+    for kind, bb in (("q8_0", 34), ("q4_0", 18)):
+        if kind == "q8_0":
+            blk0 = q8_block(0x3C00, [1] * 32)          # 1.0 * 1 * 32
+            blk1 = q8_block(0x4000, [-3] * 32)         # 2.0 * -3 * 32
+        else:
+            blk0 = q4_block_from_values(0x3C00, [1] * 32)
+            blk1 = q4_block_from_values(0x4000, [-3] * 32)
+        assert len(blk0) == bb
+        y, a = _gemv(L, kind, _u8(blk0 + blk1), np.ones(64, np.float32), 1, 64)
+        assert y[0] == 32.0 - 192.0 and a[0] == 32.0 + 192.0
+
+
+def pin_single_blocks(L):
+    cases = {c["id"]: c for c in _golden("single_blocks.json")["cases"]}
+    # E1
+    c = cases["E1_q8_0_ramp"]
+    assert 0.5 * sum(i - 16 for i in range(32)) == c["expected"]
+    y, _ = _gemv(L, "q8_0", _u8(q8_block(0x3800, [i - 16 for i in range(32)])), np.ones(32, np.float32), 1, 32)
+    assert y[0] == c["expected"]
+    # E2: -128 is a legal Q8_0 quant
+    c = cases["E2_q8_0_min_int8"]
+    y, a = _gemv(L, "q8_0", _u8(q8_block(0x3C00, [127, -128] + [0] * 30)), np.ones(32, np.float32), 1, 32)
+    assert y[0] == c["expected"] and a[0] == 255.0
+    # E3: nibble order, with x_k = k so that the two orders differ
+    c = cases["E3_q4_0_nibble_order"]
+    xk = np.arange(32, dtype=np.float32)
+    blk = _u8(q4_block_from_bytes(0x3400, range(16)))
+    y, _ = _gemv(L, "q4_0", blk, xk, 1, 32)
+    assert y[0] == c["expected"], (y[0], "interleaved order gives", c["interleaved_order_would_give"])
+    y1, _ = _gemv(L, "q4_0", blk, np.ones(32, np.float32), 1, 32)
+    assert y1[0] == c["x_all_ones_gives_for_both_orders"]
+    # E4: all-equal quants, closed form c * d * K
+    c = cases["E4a_q4_0_all_equal"]
+    K = c["K"]
+    w = _u8(q4_block_from_bytes(0x3800, [0xFF] * 16) * (K // 32))
+    y, _ = _gemv(L, "q4_0", w, np.ones(K, np.float32), 1, K)
+    assert y[0] == (15 - 8) * 0.5 * K == c["expected"]
+    c = cases["E4b_q8_0_all_equal"]
+    K = c["K"]
+    w = _u8(q8_block(0x3400, [3] * 32) * (K // 32))
+    y, _ = _gemv(L, "q8_0", w, np.ones(K, np.float32), 1, K)
+    assert y[0] == 3 * 0.25 * K == c["expected"]
+    # E4 with unequal scales and x: y = c * sum_b d_b * sum_{k in b} x_k
+    rng = np.random.default_rng(11)
+    K = 256
+    scales = [0x3000 + 0x100 * b for b in range(K // 32)]
+    x = rng.integers(-4, 5, K).astype(np.float32)
+    w = _u8(b"".join(q8_block(s, [-5] * 32) for s in scales))
+    y, _ = _gemv(L, "q8_0", w, x, 1, K)
+    ds = np.array(scales, np.uint16).view(np.float16).astype(np.float64)
+    assert y[0] == -5 * sum(ds[b] * float(x[32 * b:32 * b + 32].sum()) for b in range(K // 32))
+    # E5: subnormal scale kept exactly
+    c = cases["E5_subnormal_scale"]
+    y, _ = _gemv(L, "q8_0", _u8(q8_block(0x0001, [127] * 32)), np.ones(32, np.float32), 1, 32)
+    assert y[0] == c["expected"] == 32 * 127 * 2.0 ** -24
+
+
+def pin_silu(L):
+    c = {c["id"]: c for c in _golden("single_blocks.json")["cases"]}["E6_silu"]
+    for g, u, expect in c["points"]:
+        got = L.oracle_silu(g) * u
+        assert math.isfinite(got)
+        assert abs(got - expect) <= 1e-15 * max(1.0, abs(expect)), (g, got, expect)
+    # odd part and limits: silu(g) - silu(-g) = g; silu(g) -> g for large g
+    for g in (0.3, 2.5, 7.0):
+        assert abs((L.oracle_silu(g) - L.oracle_silu(-g)) - g) <= 1e-15 * g
+    assert L.oracle_silu(40.0) == 40.0
+
+
+def pin_bruteforce_exact(L):
+    rng = np.random.default_rng(1234)
+    for kind in ("q8_0", "q4_0", "f16"):
+        for N, K in ((1, 32), (3, 64), (4, 96), (2, 128), (4, 40 if kind == "f16" else 32)):
+            w = W.matrix(kind, N, K, rng)
+            x = rng.standard_normal(K).astype(np.float32)
+            y, a = _gemv(L, kind, w, x, N, K)
+            Wx = _exact_weights(kind, w, N, K)
+            for n in range(N):
+                prods = [Wx[n][k] * Fraction(float(x[k])) for k in range(K)]
+                exact = sum(prods, Fraction(0))
+                amag = sum((abs(p) for p in prods), Fraction(0))
+                bound = K * 2.0 ** -53 * float(amag)
+                assert abs(Fraction(y[n]) - exact) <= Fraction(bound), (kind, N, K, n)
+                assert abs(Fraction(a[n]) - amag) <= Fraction(bound), (kind, N, K, n)
+
+
+def pin_textbook(L):
+    rng = np.random.default_rng(77)
+    N, K = 16, 256
+    x = rng.standard_normal(K).astype(np.float32)
+    x64 = x.astype(np.float64)
+    # Q8_0 with every scale 1.0: W is the int8 matrix itself
+    q = rng.integers(-128, 128, size=(N * K // 32, 32), dtype=np.int8)
+    blocks = b"".join(q8_block(0x3C00, row.astype(int)) for row in q)
+    y, a = _gemv(L, "q8_0", _u8(blocks), x, N, K)
+    Wm = q.astype(np.float64).reshape(N, K)
+    ref = Wm @ x64
+    assert np.all(np.abs(y - ref) <= 1e-12 * (np.abs(Wm) @ np.abs(x64)))
+    # Q4_0 with every scale 1.0: W holds the integers v in [-8, 7]
+    v = rng.integers(-8, 8, size=(N * K // 32, 32))
+    blocks = b"".join(q4_block_from_values(0x3C00, row) for row in v)
+    y, _ = _gemv(L, "q4_0", _u8(blocks), x, N, K)
+    Wm = v.astype(np.float64).reshape(N, K)
+    assert np.all(np.abs(y - Wm @ x64) <= 1e-12 * (np.abs(Wm) @ np.abs(x64)))
+    # fp16 weights: numpy's own fp16 -> fp64 matmul
+    w16 = rng.normal(0, 0.02, N * K).astype(np.float16)
+    y, _ = _gemv(L, "f16", w16.view(np.uint16), x, N, K)
+    Wm = w16.astype(np.float64).reshape(N, K)
+    assert np.all(np.abs(y - Wm @ x64) <= 1e-12 * (np.abs(Wm) @ np.abs(x64)))
+
+
+def pin_invariants(L):
+    rng = np.random.default_rng(5)
+    for kind in ("q8_0", "q4_0", "f16"):
+        N, K = 12, 192
+        w = W.matrix(kind, N, K, rng)
+        x = rng.standard_normal(K).astype(np.float32)
+        y, a = _gemv(L, kind, w, x, N, K)
+        # exact power-of-two scaling
+        y2, a2 = _gemv(L, kind, w, (2 * x).astype(np.float32), N, K)
+        assert np.array_equal(y2, 2 * y) and np.array_equal(a2, 2 * a)
+        # row permutation permutes y (rows are independent)
+        perm = rng.permutation(N)
+        if kind == "f16":
+            wp = w.reshape(N, K)[perm].reshape(-1)
+        else:
+            bb = 34 if kind == "q8_0" else 18
+            wp = w.reshape(N, -1)[perm].reshape(-1)
+            assert w.size == N * (K // 32) * bb
+        yp, _ = _gemv(L, kind, wp, x, N, K)
+        assert np.array_equal(yp, y[perm])
+        if kind == "f16":
+            continue
+        # a zero scale silences a block: same y as the block's x set to zero
+        bb = 34 if kind == "q8_0" else 18
+        wz = w.reshape(N, K // 32, bb).copy()
+        wz[:, 2, 0:2] = 0
+        yz, _ = _gemv(L, kind, wz.reshape(-1), x, N, K)
+        xz = x.copy()
+        xz[64:96] = 0
+        yx, _ = _gemv(L, kind, w, xz, N, K)
+        assert np.array_equal(yz, yx)
+
+
+def pin_composites(L):
+    rng = np.random.default_rng(9)
+    for kind in ("q8_0", "q4_0"):
+        N, K = 10, 128
+        gate = W.matrix(kind, N, K, rng)
+        up = W.matrix(kind, N, K, rng)
+        x = rng.standard_normal(K).astype(np.float32)
+        out, g, u, ag, au = O.gateup_silu(kind, gate, up, x, N, K, L=L)
+        gy, ga = _gemv(L, kind, gate, x, N, K)
+        uy, ua = _gemv(L, kind, up, x, N, K)
+        assert np.array_equal(g, gy) and np.array_equal(u, uy)
+        assert np.array_equal(ag, ga) and np.array_equal(au, ua)
+        assert np.array_equal(out, np.array([L.oracle_silu(float(a)) for a in gy]) * uy)
+        # verify rows are independent M=1 products
+        X = rng.standard_normal((4, K)).astype(np.float32)
+        Y, A = O.verify(kind, gate, X, N, K, L=L)
+        for m in range(4):
+            ym, am = _gemv(L, kind, gate, X[m], N, K)
+            assert np.array_equal(Y[m], ym) and np.array_equal(A[m], am)
+        # chosen rows, and threads, give the same bits as the plain loop
+        rows = np.array([N - 1, 0, 3], np.int64)
+        yr, ar = O.gemv_rows(kind, gate, x, rows, N, K, L=L)
+        assert np.array_equal(yr, gy[rows]) and np.array_equal(ar, ga[rows])
+        yt, at = _gemv(L, kind, gate, x, N, K, threads=3)
+        assert np.array_equal(yt, gy) and np.array_equal(at, ga)
+
+
+def pin_rejects_bad_shapes(L):
+    w = np.zeros(34, np.uint8)
+    x = np.zeros(33, np.float32)
+    y = np.zeros(1)
+    a = np.zeros(1)
+    p = lambda arr: arr.ctypes.data_as(__import__("ctypes").c_void_p)  # noqa: E731
+    assert L.oracle_gemv(O.Q8_0, p(w), p(x), p(y), p(a), 1, 33, 1) != 0
+    assert L.oracle_gemv(O.Q4_0, p(w), p(x), p(y), p(a), 1, 48, 1) != 0
+    assert L.oracle_gemv(7, p(w), p(x), p(y), p(a), 1, 32, 1) != 0
+
+
+PINS = [
+    pin_half_decode_all_patterns,
+    pin_format_sizes,
+    pin_single_blocks,
+    pin_silu,
+    pin_bruteforce_exact,
+    pin_textbook,
+    pin_invariants,
+    pin_composites,
+    pin_rejects_bad_shapes,
+]

@@ -1,0 +1,59 @@
+"""Plant plausible mistakes in a copy of the oracle and check that the pins see them.
+
+Each mutant is a one-place textual edit of oracle/oracle.c (a dropped term, a
+wrong sign, index or offset, a transposed operand, a lost subnormal...). It is
+compiled into a temporary library on the CPU; at least one pin must fail on it.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle as O
+from oracle_pins import PINS
+
+SRC = os.path.join(os.path.dirname(O.__file__), "oracle.c")
+
+MUTANTS = {
+    "q4_interleaved_nibbles": ("(i < 16) ? (qs[i] & 0x0f) : (qs[i - 16] >> 4)",
+                               "(qs[i / 2] >> (4 * (i % 2))) & 0x0f"),
+    "q4_offset_sign": ("(double)(nib - 8)", "(double)(nib + 8)"),
+    "q4_no_offset": ("(double)(nib - 8)", "(double)(nib)"),
+    "subnormal_flushed": ("v = ldexp((double)m, -24);", "v = 0.0;"),
+    "exponent_bias": ("ldexp((double)(1024 + m), e - 25)", "ldexp((double)(1024 + m), e - 24)"),
+    "hidden_bit_dropped": ("ldexp((double)(1024 + m), e - 25)", "ldexp((double)(m), e - 25)"),
+    "q8_unsigned": ("(int)(int8_t)blk[2 + i]", "(int)blk[2 + i]"),
+    "last_weight_dropped": ("for (int64_t k = 0; k < K; ++k) {", "for (int64_t k = 0; k + 1 < K; ++k) {"),
+    "q8_row_transposed": ("w + (n * (K / 32) + k / 32) * 34", "w + ((k / 32) * 1 + n * 0) * 34"),
+    "q4_block_stride": ("w + (n * (K / 32) + k / 32) * 18", "w + (n * (K / 32) + k / 32) * 16"),
+    "f16_transposed": ("w + (n * K + k) * 2", "w + (k * K + n) * 2"),
+    "abs_dropped": ("asum += fabs(p);", "asum += p;"),
+    "silu_sign": ("g / (1.0 + exp(-g))", "g / (1.0 + exp(g))"),
+    "gateup_swapped": ("out[n] = oracle_silu(gg[n]) * uu[n]", "out[n] = oracle_silu(uu[n]) * gg[n]"),
+    "x_index_shifted": ("double p = wk * (double)x[k];", "double p = wk * (double)x[(k + 1) % K];"),
+    "sign_bit_ignored": ("return sign ? -v : v;", "return v;"),
+    "scale_byte_order": ("(uint16_t)(p[0] | (p[1] << 8))", "(uint16_t)(p[1] | (p[0] << 8))"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation site for {name} no longer exists in oracle.c"
+    mutated = src.replace(old, new, 1)
+    c_path = tmp_path / "mutant.c"
+    so_path = tmp_path / "libmutant.so"
+    c_path.write_text(mutated)
+    subprocess.check_call(["gcc", "-std=c11", "-O1", "-fPIC", "-shared", "-ffp-contract=off",
+                           "-o", str(so_path), str(c_path), "-lm", "-lpthread"])
+    L = O.lib(str(so_path))
+    caught = []
+    for pin in PINS:
+        try:
+            pin(L)
+        except AssertionError:
+            caught.append(pin.__name__)
+        except (ValueError, OverflowError, ZeroDivisionError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
