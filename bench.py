@@ -1,0 +1,466 @@
+"""Benchmark of the block-dequant GEMV path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline step (the decode weight set of a Qwen3-0.6B-shaped Q8_0 model, M=1):
+  fused QKV 4096x1024 -> O 1024x2048 -> fused gate|up 2x3072x1024 + SiLU ->
+  down 1024x3072 -> LM head 151936x1024.
+Each step reads the next of several device copies of the whole weight set
+(>= 1 GiB in total), so the weights are cold in the 256 MB Infinity Cache and
+the 4 MB L2s when a step reads them. `value` is algorithmic bytes moved per
+second over K timed steps (weights + scales + x + y, each read/written once).
+
+Also measured in the same run:
+  * every matrix of the five workload configurations, one call at a time, cold
+    (a 1 GiB read+write flush before each timed call) and warm, as median us per
+    call, GB/s and fraction of the 8 TB/s HBM3E peak;
+  * the roofline entry of the step's dominant kernel (HIP events on the stream
+    the kernels run on);
+  * the fp64 CPU oracle on the host cores (one thread and all threads) over one
+    step of the same workload (the cpu_baseline leg; the only use of oracle/).
+Prints one JSON line on stdout; a readable table goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_GBPS = 8000.0
+METRIC = "Q8_0/Q4_0 GEMV achieved HBM GB/s (% of 8 TB/s, cold); µs per call"
+COLD_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "block_dequant_gemv_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+
+class Call:
+    """One C-ABI call with its buffers and byte accounting."""
+
+    def __init__(self, label, fn, nbytes, kernel):
+        self.label, self.fn, self.nbytes, self.kernel = label, fn, nbytes, kernel
+
+
+def qkernel_name(qg, kind, N, K, M=1, epi="plain"):
+    p = qg.qg_plan_info(kind, N, K, M)
+    return f"qgemv<{kind},M{M},{epi},W{p['split_k_waves']},{'lds' if p['x_in_lds'] else 'gx'}>"
+
+
+def wbytes(kind, N, K):
+    from block_dequant_gemv_amd.workloads import matrix_bytes
+    return matrix_bytes(kind, N, K)
+
+
+def make_qgemv(qg, kind, packed, x, y, N, K, stream, label):
+    fn = qg.bound_call("qgemv_q8_0" if kind == "q8_0" else "qgemv_q4_0", packed.data_ptr(), x.data_ptr(),
+                       y.data_ptr(), N, K, stream)
+    return Call(label, fn, wbytes(kind, N, K) + 4 * K + 4 * N, qkernel_name(qg, kind, N, K))
+
+
+def make_gateup(qg, kind, packed, x, y, N_ff, K, stream, label):
+    fn = qg.bound_call("qgemv_fused_gateup_silu", qg.QTYPES[kind], packed.data_ptr(), x.data_ptr(), y.data_ptr(),
+                       N_ff, K, stream)
+    return Call(label, fn, 2 * wbytes(kind, N_ff, K) + 4 * K + 4 * N_ff,
+                qkernel_name(qg, kind, 2 * N_ff, K, epi="gateup"))
+
+
+def make_verify(qg, kind, packed, X, Y, N, K, M, stream, label):
+    fn = qg.bound_call("qgemv_verify", qg.QTYPES[kind], packed.data_ptr(), X.data_ptr(), Y.data_ptr(), N, K, M,
+                       stream)
+    return Call(label, fn, wbytes(kind, N, K) + 4 * M * K + 4 * M * N, qkernel_name(qg, kind, N, K, M))
+
+
+def make_f16(qg, w, x, y, N, K, stream, label):
+    fn = qg.bound_call("gemv_f16_splitk", w.data_ptr(), x.data_ptr(), y.data_ptr(), N, K, stream)
+    return Call(label, fn, 2 * N * K + 4 * K + 4 * N, "gemv_f16")
+
+
+# ---------------------------------------------------------------------------
+
+def build_step(qg, torch, wl, stream, copies):
+    """The headline decode set, packed once and cloned into `copies` device copies."""
+    dev = "cuda"
+    K = 1024
+    base = {}
+    base["qkv"] = qg.pack_concat("q8_0", [(wl.weight(n), wl.entry(n)[2]) for n in ("q_proj", "k_proj", "v_proj")],
+                                 K)
+    base["o"] = qg.pack_weights("q8_0", wl.weight("o_proj"), 1024, 2048)
+    base["gateup"] = qg.pack_gateup("q8_0", wl.weight("gate"), wl.weight("up"), 3072, 1024)
+    base["down"] = qg.pack_weights("q8_0", wl.weight("down"), 1024, 3072)
+    base["lm_head"] = qg.pack_weights("q8_0", wl.weight("lm_head"), 151936, 1024)
+    xs = {n: torch.from_numpy(wl.x(src)).to(dev) for n, src in
+          (("qkv", "q_proj"), ("o", "o_proj"), ("gateup", "gate"), ("down", "down"), ("lm_head", "lm_head"))}
+    ys = {"qkv": 4096, "o": 1024, "gateup": 3072, "down": 1024, "lm_head": 151936}
+    ys = {n: torch.empty(v, dtype=torch.float32, device=dev) for n, v in ys.items()}
+    sets = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(copies - 1)]
+    torch.cuda.synchronize()
+    steps = []
+    for s in sets:
+        steps.append([
+            make_qgemv(qg, "q8_0", s["qkv"], xs["qkv"], ys["qkv"], 4096, 1024, stream, "qkv 4096x1024"),
+            make_qgemv(qg, "q8_0", s["o"], xs["o"], ys["o"], 1024, 2048, stream, "o_proj 1024x2048"),
+            make_gateup(qg, "q8_0", s["gateup"], xs["gateup"], ys["gateup"], 3072, 1024, stream,
+                        "gate|up 2x3072x1024 silu"),
+            make_qgemv(qg, "q8_0", s["down"], xs["down"], ys["down"], 1024, 3072, stream, "down 1024x3072"),
+            make_qgemv(qg, "q8_0", s["lm_head"], xs["lm_head"], ys["lm_head"], 151936, 1024, stream,
+                       "lm_head 151936x1024"),
+        ])
+    return steps, sets, xs, ys
+
+
+def time_calls(torch, calls, reps, flush=None):
+    """Median/p10/p90 microseconds of each call, with an optional flush before each rep."""
+    out = {}
+    for c in calls:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in evs:
+            if flush is not None:
+                flush()
+            e0.record()
+            c.fn()
+            e1.record()
+        torch.cuda.synchronize()
+        us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+        out[c.label] = us
+    return out
+
+
+def per_config_calls(qg, torch, stream, step_calls):
+    """All five configurations as lists of calls (the headline step's calls reused for config 1)."""
+    from block_dequant_gemv_amd.workloads import Workload
+    dev = "cuda"
+    keep = []
+    res = {}
+
+    def t(a):
+        d = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        keep.append(d)
+        return d
+
+    def yb(n):
+        d = torch.empty(n, dtype=torch.float32, device=dev)
+        keep.append(d)
+        return d
+
+    wl = Workload(0)
+    p = qg.pack_weights("q8_0", wl.weight("w"), 1024, 1024)
+    keep.append(p)
+    res[0] = [make_qgemv(qg, "q8_0", p, t(wl.x("w")), yb(1024), 1024, 1024, stream, "c0 q8_0 1024x1024")]
+
+    res[1] = [Call("c1 " + c.label, c.fn, c.nbytes, c.kernel) for c in step_calls]
+
+    wl = Workload(2)
+    pg = qg.pack_gateup("q4_0", wl.weight("gate"), wl.weight("up"), 17408, 5120)
+    wl.drop("gate")
+    wl.drop("up")
+    pd = qg.pack_weights("q4_0", wl.weight("down"), 5120, 17408)
+    wl.drop("down")
+    pl = qg.pack_weights("q4_0", wl.weight("lm_head"), 248320, 5120)
+    wl.drop("lm_head")
+    keep += [pg, pd, pl]
+    res[2] = [
+        make_gateup(qg, "q4_0", pg, t(wl.x("gate")), yb(17408), 17408, 5120, stream, "c2 q4_0 gate|up 2x17408x5120"),
+        make_qgemv(qg, "q4_0", pd, t(wl.x("down")), yb(5120), 5120, 17408, stream, "c2 q4_0 down 5120x17408"),
+        make_qgemv(qg, "q4_0", pl, t(wl.x("lm_head")), yb(248320), 248320, 5120, stream,
+                   "c2 q4_0 lm_head 248320x5120"),
+    ]
+
+    wl = Workload(3)
+    res[3] = []
+    for name in ("square", "thin", "small"):
+        _, _, N, K, _ = wl.entry(name)
+        res[3].append(make_f16(qg, t(wl.weight(name)), t(wl.x(name)), yb(N), N, K, stream, f"c3 f16 {N}x{K}"))
+
+    wl = Workload(4)
+    res[4] = []
+    for name in ("q4_0_w", "q8_0_w"):
+        _, kind, N, K, _ = wl.entry(name)
+        pw = qg.pack_weights(kind, wl.weight(name), N, K)
+        keep.append(pw)
+        X = t(wl.x(name, M=6))
+        res[4].append(make_qgemv(qg, kind, pw, X[0:1].reshape(-1), yb(N), N, K, stream,
+                                 f"c4 {kind} {N}x{K} M=1"))
+        for M in range(2, 7):
+            res[4].append(make_verify(qg, kind, pw, X, yb(M * N), N, K, M, stream, f"c4 {kind} {N}x{K} M={M}"))
+    torch.cuda.synchronize()
+    return res, keep
+
+
+def cpu_baseline(wl, threads_all):
+    """The fp64 oracle over one headline step on the host: one thread, then all threads."""
+    import oracle as O
+
+    jobs = [
+        ("q8_0", np.concatenate([wl.weight(n) for n in ("q_proj", "k_proj", "v_proj")]), wl.x("q_proj"), 4096, 1024),
+        ("q8_0", wl.weight("o_proj"), wl.x("o_proj"), 1024, 2048),
+        ("gateup", None, wl.x("gate"), 3072, 1024),
+        ("q8_0", wl.weight("down"), wl.x("down"), 1024, 3072),
+        ("q8_0", wl.weight("lm_head"), wl.x("lm_head"), 151936, 1024),
+    ]
+    nbytes = 4476928 + 2240512 + 6701056 + 3358720 + 165918208
+
+    def one_step(threads):
+        t0 = time.perf_counter()
+        for kind, w, x, N, K in jobs:
+            if kind == "gateup":
+                O.gateup_silu("q8_0", wl.weight("gate"), wl.weight("up"), x, N, K, threads=threads)
+            else:
+                O.gemv(kind, w, x, N, K, threads=threads)
+        return time.perf_counter() - t0
+
+    t1 = one_step(1)
+    tall = sorted(one_step(threads_all) for _ in range(3))[1]
+    return {
+        "value": nbytes / tall / 1e9, "unit": "GB/s", "cores": threads_all, "kind": "oracle",
+        "sample": "one full headline step (qkv, o_proj, gate|up silu, down, lm_head; 182.7 MB), fp64, "
+                  f"median of 3 with {threads_all} threads",
+        "ms_per_step": tall * 1e3,
+        "single_thread": {"value": nbytes / t1 / 1e9, "unit": "GB/s", "cores": 1, "ms_per_step": t1 * 1e3},
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def hbm_reference(torch):
+    """Bandwidth of torch's own streaming kernels on 2 GiB buffers (well above the
+    256 MB Infinity Cache): a read-only reduction and a device copy."""
+    n = (2 << 30) // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    out = {}
+    for name, fn, nbytes in (("sum_read", lambda: a.sum(), 4 * n),):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(nbytes * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    b = torch.empty(n // 2, dtype=torch.float32, device="cuda")
+    src = a[: n // 2]
+    for _ in range(2):
+        b.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    out["copy"] = round(2 * 4 * (n // 2) * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
+def load_traffic(kernel: str):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    entry = t.get("kernels", {}).get(kernel)
+    return entry.get("bytes_per_launch") if entry else None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=15)
+    ap.add_argument("--reps", type=int, default=50, help="cold reps per call in the per-config table")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-config table")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--detail", default=None, help="write the full per-call results to this JSON file")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {max(args.gpus, world)} is not supported "
+              "(the GEMV shards by output rows with no communication; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_dequant_gemv_amd as qg
+    from block_dequant_gemv_amd.workloads import Workload
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream().cuda_stream
+    props = torch.cuda.get_device_properties(0)
+    log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs")
+
+    wl1 = Workload(1)
+    step_bytes_one = 4476928 + 2240512 + 6701056 + 3358720 + 165918208
+    copies = max(3, -(-COLD_BYTES // step_bytes_one))
+    steps, sets, xs, ys = build_step(qg, torch, wl1, stream, copies)
+    step_bytes = sum(c.nbytes for c in steps[0])
+    assert step_bytes == step_bytes_one
+
+    if args.calib_copy:
+        src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 5 x 256 MiB device-to-device")
+        del src, dst
+
+    # ---- headline: K timed steps ------------------------------------------------
+    for s in range(args.warmup):
+        for c in steps[s % copies]:
+            c.fn()
+    torch.cuda.synchronize()
+    K = args.steps
+    ncalls = len(steps[0])
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ncalls)]
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        for i, c in enumerate(steps[s % copies]):
+            evs[s][i][0].record()
+            c.fn()
+            evs[s][i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / K * 1e3
+    value = step_bytes * K / wall / 1e9
+    gpu_span_ms = evs[0][0][0].elapsed_time(evs[-1][-1][1])
+    durs = np.array([[e0.elapsed_time(e1) * 1e3 for e0, e1 in row] for row in evs])  # us [K][ncalls]
+
+    # per kernel instantiation: launches, total time, total algorithmic bytes
+    kern = {}
+    for i, c in enumerate(steps[0]):
+        k = kern.setdefault(c.kernel, {"launches": 0, "us": 0.0, "bytes": 0, "calls": []})
+        k["launches"] += K
+        k["us"] += float(durs[:, i].sum())
+        k["bytes"] += c.nbytes * K
+        k["calls"].append(c.label)
+    dom_name, dom = max(kern.items(), key=lambda kv: kv[1]["us"])
+    achieved = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
+    traffic = load_traffic(dom_name)
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+        "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
+        "kernel": dom_name, "calls": dom["calls"],
+        "avg_launch_us": round(dom["us"] / dom["launches"], 3),
+        "algorithmic_bytes_per_launch": dom["bytes"] // dom["launches"],
+    }
+    log(f"headline: {K} steps, {ms_per_step:.4f} ms/step wall, GPU span {gpu_span_ms / K:.4f} ms/step, "
+        f"{value:.1f} GB/s ({100 * value / PEAK_GBPS:.1f}% of 8 TB/s), {copies} weight copies")
+    for i, c in enumerate(steps[0]):
+        med = float(np.median(durs[:, i]))
+        log(f"  {c.label:28s} {med:8.2f} us  {c.nbytes / med / 1e3:8.1f} GB/s  [{c.kernel}]")
+    log(f"  dominant kernel {dom_name}: {achieved:.1f} GB/s, avg {roofline['avg_launch_us']} us/launch")
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {
+            "workload": "qwen3-0.6b-shaped q8_0 decode gemv set, M=1: qkv 4096x1024, o_proj 1024x2048, "
+                        "gate|up 2x3072x1024 + silu, down 1024x3072, lm_head 151936x1024",
+            "step_bytes": step_bytes, "cold": f"{copies} rotating device copies of the weights "
+                                             f"({copies * step_bytes / 1e9:.2f} GB)",
+            "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
+            "gpu_ms_per_step": round(gpu_span_ms / K, 5),
+            "device": props.name,
+        },
+        "roofline": roofline,
+    }
+
+    detail = {"headline_per_call_us": {c.label: float(np.median(durs[:, i])) for i, c in enumerate(steps[0])}}
+
+    # ---- reference streams: what plain torch kernels reach on this device ----------------
+    ref = hbm_reference(torch)
+    result["config"]["hbm_reference_GBps"] = ref
+    log(f"reference streams (torch, 2 GiB): read-only sum {ref['sum_read']:.0f} GB/s, "
+        f"copy {ref['copy']:.0f} GB/s (read+write)")
+
+    # ---- per-config cold / warm table ---------------------------------------------
+    if not args.no_configs:
+        flushbuf = torch.empty(COLD_BYTES // 4, dtype=torch.float32, device="cuda").fill_(0.0)
+
+        def flush():
+            flushbuf.add_(1.0)
+
+        cfg_calls, keep = per_config_calls(qg, torch, stream, steps[0])
+        table = {}
+        log(f"per-call table: median of {args.reps} cold calls (1 GiB flush before each) and warm calls")
+        for ci in sorted(cfg_calls):
+            calls = cfg_calls[ci]
+            for c in calls:
+                for _ in range(3):
+                    c.fn()
+            cold = time_calls(torch, calls, args.reps, flush)
+            warm = time_calls(torch, calls, max(10, args.reps // 2))
+            for c in calls:
+                u = cold[c.label]
+                med = float(np.median(u))
+                gbps = c.nbytes / med / 1e3
+                table[c.label] = {"us": round(med, 3), "us_p10": round(float(np.percentile(u, 10)), 3),
+                                  "us_p90": round(float(np.percentile(u, 90)), 3), "GBps": round(gbps, 1),
+                                  "pct": round(100 * gbps / PEAK_GBPS, 1), "bytes": c.nbytes,
+                                  "warm_us": round(float(np.median(warm[c.label])), 3), "kernel": c.kernel}
+                log(f"  {c.label:34s} cold {med:9.2f} us ({float(np.percentile(u, 10)):.2f}-"
+                    f"{float(np.percentile(u, 90)):.2f})  {gbps:8.1f} GB/s {100 * gbps / PEAK_GBPS:5.1f}%   "
+                    f"warm {table[c.label]['warm_us']:9.2f} us")
+        result["configs"] = {k: {"us": v["us"], "GBps": v["GBps"], "pct": v["pct"], "warm_us": v["warm_us"]}
+                             for k, v in table.items()}
+        detail["configs"] = table
+        del keep, flushbuf
+
+    # ---- CPU oracle baseline ----------------------------------------------------------
+    if not args.no_cpu:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        cb = cpu_baseline(wl1, threads)
+        result["cpu_baseline"] = cb
+        log(f"cpu oracle: {cb['value']:.3f} GB/s on {threads} threads, {cb['single_thread']['value']:.3f} GB/s "
+            f"on 1 thread ({cb['cpu_model']})")
+
+    if args.detail:
+        with open(args.detail, "w") as f:
+            json.dump({"result": result, "detail": detail}, f, indent=1)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,279 @@
+"""Python binding of libqgemv.so, the MI355X block-dequant GEMV library.
+
+A thin ctypes layer over the C ABI in include/qgemv.h: the functions have the
+same names and arguments, take torch tensors (device memory) or numpy arrays
+(host memory) and only marshal pointers, sizes and the HIP stream. Every step
+of the computation runs in the library's HIP kernels; there is no fallback.
+If the library is not built, or a call fails, an exception is raised.
+
+Build the library with ``python -m block_dequant_gemv_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+Q8_0 = 1
+Q4_0 = 2
+QTYPES = {"q8_0": Q8_0, "q4_0": Q4_0}
+
+QG_OK, QG_EINVAL, QG_EALIGN, QG_EUNSUPPORTED, QG_EHIP = range(5)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemv.so")
+
+# every function declared in include/qgemv.h
+SYMBOLS = (
+    "qg_packed_size", "qg_pack", "qg_pack_rows", "qg_pack_gateup",
+    "qg_pack_host", "qg_unpack_host", "qg_pack_gateup_host",
+    "qgemv_q8_0", "qgemv_q4_0", "gemv_f16_splitk", "qgemv_fused_gateup_silu", "qgemv_verify",
+    "qg_status_str", "qg_last_error", "qg_plan_info",
+)
+
+
+class QGError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn} failed with status {status}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libqgemv.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built: run python -m block_dequant_gemv_amd.build")
+        # torch bundles its own HIP runtime under the same soname as ROCm's. Load
+        # torch first so that libqgemv binds to that one runtime: the library
+        # receives torch's device pointers and streams, and two runtimes in one
+        # process would each try to own the device.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+        sig = {
+            "qg_packed_size": ([i32, i64, i64], sz),
+            "qg_pack": ([i32, vp, vp, i64, i64, vp], i32),
+            "qg_pack_rows": ([i32, vp, vp, i64, i64, i64, i64, vp], i32),
+            "qg_pack_gateup": ([i32, vp, vp, vp, i64, i64, vp], i32),
+            "qg_pack_host": ([i32, vp, vp, i64, i64], i32),
+            "qg_unpack_host": ([i32, vp, vp, i64, i64], i32),
+            "qg_pack_gateup_host": ([i32, vp, vp, vp, i64, i64], i32),
+            "qgemv_q8_0": ([vp, vp, vp, i64, i64, vp], i32),
+            "qgemv_q4_0": ([vp, vp, vp, i64, i64, vp], i32),
+            "gemv_f16_splitk": ([vp, vp, vp, i64, i64, vp], i32),
+            "qgemv_fused_gateup_silu": ([i32, vp, vp, vp, i64, i64, vp], i32),
+            "qgemv_verify": ([i32, vp, vp, vp, i64, i64, i32, vp], i32),
+            "qg_status_str": ([i32], ctypes.c_char_p),
+            "qg_last_error": ([], ctypes.c_char_p),
+            "qg_plan_info": ([i32, i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i64),
+                              ctypes.POINTER(i32)], i32),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _qtype(q) -> int:
+    return QTYPES[q] if isinstance(q, str) else int(q)
+
+
+def _check(fn: str, status: int):
+    if status != QG_OK:
+        raise QGError(fn, status, lib().qg_last_error().decode())
+
+
+def _stream(stream):
+    """hipStream_t of `stream` (None = torch's current stream on the current device)."""
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev(t, name: str, dtype=None):
+    """Device pointer of a contiguous torch CUDA tensor (None passes NULL through)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (CUDA/HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _host(a: np.ndarray, name: str):
+    if not isinstance(a, np.ndarray) or not a.flags.c_contiguous:
+        raise ValueError(f"{name} must be a C-contiguous numpy array")
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f32():
+    import torch
+    return torch.float32
+
+
+# ---- packing ---------------------------------------------------------------
+
+def qg_packed_size(qtype, N: int, K: int) -> int:
+    return int(lib().qg_packed_size(_qtype(qtype), N, K))
+
+
+def qg_pack(qtype, canonical, packed, N: int, K: int, stream=None):
+    _check("qg_pack", lib().qg_pack(_qtype(qtype), _dev(canonical, "canonical"), _dev(packed, "packed"),
+                                    N, K, _stream(stream)))
+
+
+def qg_pack_rows(qtype, canonical, packed, N_total: int, row0: int, nrows: int, K: int, stream=None):
+    _check("qg_pack_rows", lib().qg_pack_rows(_qtype(qtype), _dev(canonical, "canonical"), _dev(packed, "packed"),
+                                              N_total, row0, nrows, K, _stream(stream)))
+
+
+def qg_pack_gateup(qtype, gate, up, packed, N_ff: int, K: int, stream=None):
+    _check("qg_pack_gateup", lib().qg_pack_gateup(_qtype(qtype), _dev(gate, "gate"), _dev(up, "up"),
+                                                  _dev(packed, "packed"), N_ff, K, _stream(stream)))
+
+
+def qg_pack_host(qtype, canonical: np.ndarray, N: int, K: int) -> np.ndarray:
+    out = np.empty(qg_packed_size(qtype, N, K), np.uint8)
+    _check("qg_pack_host", lib().qg_pack_host(_qtype(qtype), _host(canonical, "canonical"), _host(out, "packed"),
+                                              N, K))
+    return out
+
+
+def qg_unpack_host(qtype, packed: np.ndarray, N: int, K: int) -> np.ndarray:
+    bb = 34 if _qtype(qtype) == Q8_0 else 18
+    out = np.empty(N * (K // 32) * bb, np.uint8)
+    _check("qg_unpack_host", lib().qg_unpack_host(_qtype(qtype), _host(packed, "packed"), _host(out, "canonical"),
+                                                  N, K))
+    return out
+
+
+def qg_pack_gateup_host(qtype, gate: np.ndarray, up: np.ndarray, N_ff: int, K: int) -> np.ndarray:
+    out = np.empty(qg_packed_size(qtype, 2 * N_ff, K), np.uint8)
+    _check("qg_pack_gateup_host", lib().qg_pack_gateup_host(_qtype(qtype), _host(gate, "gate"), _host(up, "up"),
+                                                            _host(out, "packed"), N_ff, K))
+    return out
+
+
+# ---- GEMVs -----------------------------------------------------------------
+
+def qgemv_q8_0(w_packed, x, y, N: int, K: int, stream=None):
+    _check("qgemv_q8_0", lib().qgemv_q8_0(_dev(w_packed, "w_packed"), _dev(x, "x", _f32()), _dev(y, "y", _f32()),
+                                          N, K, _stream(stream)))
+
+
+def qgemv_q4_0(w_packed, x, y, N: int, K: int, stream=None):
+    _check("qgemv_q4_0", lib().qgemv_q4_0(_dev(w_packed, "w_packed"), _dev(x, "x", _f32()), _dev(y, "y", _f32()),
+                                          N, K, _stream(stream)))
+
+
+def gemv_f16_splitk(w_f16, x, y, N: int, K: int, stream=None):
+    _check("gemv_f16_splitk", lib().gemv_f16_splitk(_dev(w_f16, "w_f16"), _dev(x, "x", _f32()), _dev(y, "y", _f32()),
+                                                    N, K, _stream(stream)))
+
+
+def qgemv_fused_gateup_silu(qtype, w_gateup_packed, x, y, N_ff: int, K: int, stream=None):
+    _check("qgemv_fused_gateup_silu",
+           lib().qgemv_fused_gateup_silu(_qtype(qtype), _dev(w_gateup_packed, "w_gateup_packed"),
+                                         _dev(x, "x", _f32()), _dev(y, "y", _f32()), N_ff, K, _stream(stream)))
+
+
+def qgemv_verify(qtype, w_packed, X, Y, N: int, K: int, M: int, stream=None):
+    _check("qgemv_verify", lib().qgemv_verify(_qtype(qtype), _dev(w_packed, "w_packed"), _dev(X, "X", _f32()),
+                                              _dev(Y, "Y", _f32()), N, K, M, _stream(stream)))
+
+
+def qgemv(qtype, w_packed, x, y, N: int, K: int, stream=None):
+    """qgemv_q8_0 or qgemv_q4_0 by qtype."""
+    (qgemv_q8_0 if _qtype(qtype) == Q8_0 else qgemv_q4_0)(w_packed, x, y, N, K, stream)
+
+
+# ---- diagnostics -----------------------------------------------------------
+
+def qg_status_str(status: int) -> str:
+    return lib().qg_status_str(status).decode()
+
+
+def qg_last_error() -> str:
+    return lib().qg_last_error().decode()
+
+
+def qg_plan_info(qtype, N: int, K: int, M: int = 1) -> dict:
+    w = ctypes.c_int()
+    g = ctypes.c_int64()
+    xl = ctypes.c_int()
+    _check("qg_plan_info", lib().qg_plan_info(_qtype(qtype), N, K, M, ctypes.byref(w), ctypes.byref(g),
+                                              ctypes.byref(xl)))
+    return {"split_k_waves": w.value, "workgroups": g.value, "x_in_lds": bool(xl.value)}
+
+
+# ---- load-time helpers (torch allocates; the library packs) ------------------
+
+def upload(a: np.ndarray, device="cuda"):
+    """Copy a host numpy array to a new device tensor (torch is the allocator)."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def pack_weights(qtype, canonical: np.ndarray, N: int, K: int, device="cuda", stream=None):
+    """Upload canonical blocks and re-tile them on the device; returns the packed uint8 tensor."""
+    import torch
+    canon_d = upload(canonical.view(np.uint8), device)
+    packed = torch.empty(qg_packed_size(qtype, N, K), dtype=torch.uint8, device=device)
+    qg_pack(qtype, canon_d, packed, N, K, stream)
+    torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
+    return packed
+
+
+def pack_concat(qtype, parts: list, K: int, device="cuda", stream=None):
+    """Pack canonical row blocks [(canonical, rows), ...] into one concatenated weight (e.g. QKV)."""
+    import torch
+    N = sum(r for _, r in parts)
+    packed = torch.empty(qg_packed_size(qtype, N, K), dtype=torch.uint8, device=device)
+    row0 = 0
+    keep = []
+    for canon, rows in parts:
+        c = upload(canon.view(np.uint8), device)
+        keep.append(c)
+        qg_pack_rows(qtype, c, packed, N, row0, rows, K, stream)
+        row0 += rows
+    torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
+    return packed
+
+
+def pack_gateup(qtype, gate: np.ndarray, up: np.ndarray, N_ff: int, K: int, device="cuda", stream=None):
+    """Upload gate and up projections and fuse them into one packed weight."""
+    import torch
+    g = upload(gate.view(np.uint8), device)
+    u = upload(up.view(np.uint8), device)
+    packed = torch.empty(qg_packed_size(qtype, 2 * N_ff, K), dtype=torch.uint8, device=device)
+    qg_pack_gateup(qtype, g, u, packed, N_ff, K, stream)
+    torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
+    return packed
+
+
+def bound_call(name: str, *args):
+    """A zero-argument callable for one C-ABI call with its arguments already
+    marshalled (raw pointers, sizes, stream handle): for timed loops, where
+    re-checking torch tensors on every launch would dominate small calls."""
+    fn = getattr(lib(), name)
+
+    def call():
+        st = fn(*args)
+        if st:
+            _check(name, st)
+    return call

@@ -1,0 +1,340 @@
+// qgemv_api.hip -- the C ABI of libqgemv (declared in include/qgemv.h).
+//
+// Every entry point checks its arguments on the host first (no HIP call before
+// the checks pass, so the checks run on a machine without a GPU), then picks a
+// launch plan and enqueues kernels on the caller's stream. Nothing here
+// allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "layout.h"
+#include "qgemv.h"
+#include "qgemv_kernels.h"
+
+using qgl::Geometry;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+qg_status fail(qg_status s, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+qg_status ok()
+{
+    g_last_error.clear();
+    return QG_OK;
+}
+
+qg_status hip_fail(hipError_t e, const char *what)
+{
+    return fail(QG_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb)
+{
+    uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool valid_qtype(int qt) { return qt == QG_Q8_0 || qt == QG_Q4_0; }
+
+// Shape limits: rows and K must index 64-bit byte offsets safely and the grid
+// must fit 2^31 workgroups.
+constexpr int64_t kMaxDim = (int64_t)1 << 40;
+
+qg_status check_qshape(int qt, int64_t N, int64_t K, const char *fn)
+{
+    if (!valid_qtype(qt)) return fail(QG_EUNSUPPORTED, "%s: unknown qtype %d", fn, qt);
+    if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim)
+        return fail(QG_EINVAL, "%s: N=%lld K=%lld must be positive", fn, (long long)N, (long long)K);
+    if (K % 32 != 0) return fail(QG_EINVAL, "%s: K=%lld is not a multiple of 32", fn, (long long)K);
+    if (N * (K / 32) > ((int64_t)1 << 42)) return fail(QG_EINVAL, "%s: matrix too large", fn);
+    return QG_OK;
+}
+
+// Wavefronts that split one tile along K. Depends only on (rows, K): small
+// row counts with long K get more wavefronts per tile so that the chip has
+// enough loads in flight; a decode call and a verify call of the same weight
+// always agree.
+int split_k_waves(int64_t rows, int64_t K)
+{
+    const int64_t n_tiles = (rows + qgl::kTileRows - 1) / qgl::kTileRows;
+    const int64_t nseg = (K / 32 + qgl::kSegBlocks - 1) / qgl::kSegBlocks;
+    int W = 1;
+    while (W < 4 && 2 * W <= nseg && n_tiles * W < 2048) W *= 2;
+    return W;
+}
+
+constexpr size_t kLdsLimit = 96 * 1024;   // above this, activations are read from global memory
+
+qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M)
+{
+    qgk::QPlan p;
+    const Geometry g = qgl::geometry(qt, rows, K);
+    p.W = split_k_waves(rows, K);
+    // About 4096 groups of wavefronts (16 per CU on 256 CUs); a group walks tpg
+    // consecutive row tiles, so large matrices are read as long sequential runs.
+    const int64_t target_groups = 4096 / p.W;
+    p.tpg = g.n_tiles / target_groups;
+    if (p.tpg < 1) p.tpg = 1;
+    const char *env = getenv("QG_TILES_PER_GROUP");
+    if (env && atoll(env) > 0) p.tpg = atoll(env);
+    const int64_t groups = (g.n_tiles + p.tpg - 1) / p.tpg;
+    int G;   // groups per workgroup
+    if (p.W > 1) {
+        G = 1;
+        p.block = 64 * p.W;
+    } else {
+        // many groups: 4 wavefronts share one LDS copy of x; few groups: one
+        // wavefront per workgroup so that the launch spreads over every CU
+        G = groups >= 2048 ? 4 : 1;
+        p.block = 64 * G;
+    }
+    p.grid = (groups + G - 1) / G;
+    const size_t xbytes = (size_t)M * (size_t)g.nseg * qgl::kSegWeights * sizeof(float);
+    p.x_in_lds = xbytes <= kLdsLimit;
+    p.lds_bytes = p.x_in_lds ? xbytes : 0;
+    return p;
+}
+
+hipStream_t as_stream(void *s) { return (hipStream_t)s; }
+
+qg_status run_qgemv(int qt, int epi, const void *w, const float *x, float *y, int64_t rows, int64_t n_out,
+                    int64_t K, int M, void *stream, const char *fn)
+{
+    qg_status st = check_qshape(qt, rows, K, fn);
+    if (st) return st;
+    if (!w || !x || !y) return fail(QG_EINVAL, "%s: null pointer", fn);
+    if (!aligned(w, 16)) return fail(QG_EALIGN, "%s: packed weights must be 16-byte aligned", fn);
+    if (!aligned(x, 16)) return fail(QG_EALIGN, "%s: activations must be 16-byte aligned", fn);
+    if (!aligned(y, 4)) return fail(QG_EALIGN, "%s: output must be 4-byte aligned", fn);
+    const Geometry g = qgl::geometry(qt, rows, K);
+    const size_t ybytes = (size_t)M * (size_t)n_out * sizeof(float);
+    const size_t xbytes = (size_t)M * (size_t)K * sizeof(float);
+    if (overlap(y, ybytes, x, xbytes)) return fail(QG_EINVAL, "%s: y overlaps x", fn);
+    if (overlap(y, ybytes, w, (size_t)g.total)) return fail(QG_EINVAL, "%s: y overlaps the weights", fn);
+
+    const qgk::QPlan p = make_qplan(qt, rows, K, M);
+    qgk::QArgs a;
+    a.geo = g;
+    a.n_out = n_out;
+    a.x_stride = K;
+    a.y_stride = n_out;
+    a.tpg = p.tpg;
+    hipError_t e = qgk::launch_qgemv(qt, M, epi, p, (const uint8_t *)w, x, y, a, as_stream(stream));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+qg_status check_pack(int qt, const void *canon, const void *packed, int64_t N, int64_t K, const char *fn)
+{
+    qg_status st = check_qshape(qt, N, K, fn);
+    if (st) return st;
+    if (!canon || !packed) return fail(QG_EINVAL, "%s: null pointer", fn);
+    return QG_OK;
+}
+
+void host_pack_rows(const Geometry &g, const uint8_t *canon, uint8_t *packed, int64_t row0, int64_t nrows,
+                    bool pad)
+{
+    const int cb = qgl::canon_block_bytes(g.qt);
+    for (int64_t r = 0; r < nrows; ++r)
+        for (int64_t b = 0; b < g.KB; ++b) qgl::pack_block(g, canon + (r * g.KB + b) * cb, packed, row0 + r, b);
+    if (pad)
+        for (int64_t r = g.N; r < g.n_tiles * qgl::kTileRows; ++r)
+            for (int64_t b = 0; b < g.KB; ++b) qgl::pack_block(g, nullptr, packed, r, b);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qg_packed_size(int qtype, int64_t N, int64_t K)
+{
+    if (!valid_qtype(qtype) || N <= 0 || K <= 0 || K % 32 || N > kMaxDim || K > kMaxDim) return 0;
+    return (size_t)qgl::geometry(qtype, N, K).total;
+}
+
+qg_status qg_pack(int qtype, const void *canonical, void *packed, int64_t N, int64_t K, void *stream)
+{
+    return qg_pack_rows(qtype, canonical, packed, N, 0, N, K, stream);
+}
+
+qg_status qg_pack_rows(int qtype, const void *canonical, void *packed, int64_t N_total, int64_t row0, int64_t nrows,
+                       int64_t K, void *stream)
+{
+    const char *fn = "qg_pack_rows";
+    qg_status st = check_pack(qtype, canonical, packed, N_total, K, fn);
+    if (st) return st;
+    if (row0 < 0 || nrows <= 0 || row0 + nrows > N_total)
+        return fail(QG_EINVAL, "%s: rows [%lld, %lld) outside [0, %lld)", fn, (long long)row0,
+                    (long long)(row0 + nrows), (long long)N_total);
+    if (!aligned(packed, 16)) return fail(QG_EALIGN, "%s: packed buffer must be 16-byte aligned", fn);
+    const Geometry g = qgl::geometry(qtype, N_total, K);
+    const size_t cbytes = (size_t)nrows * (size_t)g.KB * qgl::canon_block_bytes(qtype);
+    if (overlap(canonical, cbytes, packed, (size_t)g.total)) return fail(QG_EINVAL, "%s: buffers overlap", fn);
+    const bool last = row0 + nrows == N_total;
+    const int64_t rows_to_write = nrows + (last ? g.n_tiles * qgl::kTileRows - N_total : 0);
+    hipError_t e = qgk::launch_pack(g, (const uint8_t *)canonical, nullptr, (uint8_t *)packed, qgk::kPackRows, row0,
+                                    nrows, rows_to_write, last, as_stream(stream));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+qg_status qg_pack_gateup(int qtype, const void *gate, const void *up, void *packed, int64_t N_ff, int64_t K,
+                         void *stream)
+{
+    const char *fn = "qg_pack_gateup";
+    qg_status st = check_pack(qtype, gate, packed, 2 * N_ff, K, fn);
+    if (st) return st;
+    if (!up) return fail(QG_EINVAL, "%s: null pointer", fn);
+    if (!aligned(packed, 16)) return fail(QG_EALIGN, "%s: packed buffer must be 16-byte aligned", fn);
+    const Geometry g = qgl::geometry(qtype, 2 * N_ff, K);
+    const size_t cbytes = (size_t)N_ff * (size_t)g.KB * qgl::canon_block_bytes(qtype);
+    if (overlap(gate, cbytes, packed, (size_t)g.total) || overlap(up, cbytes, packed, (size_t)g.total))
+        return fail(QG_EINVAL, "%s: buffers overlap", fn);
+    hipError_t e = qgk::launch_pack(g, (const uint8_t *)gate, (const uint8_t *)up, (uint8_t *)packed,
+                                    qgk::kPackGateUp, 0, 2 * N_ff, g.n_tiles * qgl::kTileRows, true,
+                                    as_stream(stream));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+qg_status qg_pack_host(int qtype, const void *canonical_host, void *packed_host, int64_t N, int64_t K)
+{
+    qg_status st = check_pack(qtype, canonical_host, packed_host, N, K, "qg_pack_host");
+    if (st) return st;
+    const Geometry g = qgl::geometry(qtype, N, K);
+    memset(packed_host, 0, (size_t)g.total);
+    host_pack_rows(g, (const uint8_t *)canonical_host, (uint8_t *)packed_host, 0, N, true);
+    return ok();
+}
+
+qg_status qg_unpack_host(int qtype, const void *packed_host, void *canonical_host, int64_t N, int64_t K)
+{
+    qg_status st = check_pack(qtype, canonical_host, packed_host, N, K, "qg_unpack_host");
+    if (st) return st;
+    const Geometry g = qgl::geometry(qtype, N, K);
+    const int cb = qgl::canon_block_bytes(qtype);
+    for (int64_t r = 0; r < N; ++r)
+        for (int64_t b = 0; b < g.KB; ++b)
+            qgl::unpack_block(g, (const uint8_t *)packed_host, (uint8_t *)canonical_host + (r * g.KB + b) * cb, r, b);
+    return ok();
+}
+
+qg_status qg_pack_gateup_host(int qtype, const void *gate_host, const void *up_host, void *packed_host, int64_t N_ff,
+                              int64_t K)
+{
+    qg_status st = check_pack(qtype, gate_host, packed_host, 2 * N_ff, K, "qg_pack_gateup_host");
+    if (st) return st;
+    if (!up_host) return fail(QG_EINVAL, "qg_pack_gateup_host: null pointer");
+    const Geometry g = qgl::geometry(qtype, 2 * N_ff, K);
+    const int cb = qgl::canon_block_bytes(qtype);
+    memset(packed_host, 0, (size_t)g.total);
+    for (int64_t v = 0; v < 2 * N_ff; ++v) {
+        const uint8_t *base = (const uint8_t *)((v & 1) ? up_host : gate_host);
+        for (int64_t b = 0; b < g.KB; ++b)
+            qgl::pack_block(g, base + ((v >> 1) * g.KB + b) * cb, (uint8_t *)packed_host, v, b);
+    }
+    for (int64_t v = 2 * N_ff; v < g.n_tiles * qgl::kTileRows; ++v)
+        for (int64_t b = 0; b < g.KB; ++b) qgl::pack_block(g, nullptr, (uint8_t *)packed_host, v, b);
+    return ok();
+}
+
+qg_status qgemv_q8_0(const void *w_packed, const float *x, float *y, int64_t N, int64_t K, void *stream)
+{
+    return run_qgemv(QG_Q8_0, qgk::kEpiPlain, w_packed, x, y, N, N, K, 1, stream, "qgemv_q8_0");
+}
+
+qg_status qgemv_q4_0(const void *w_packed, const float *x, float *y, int64_t N, int64_t K, void *stream)
+{
+    return run_qgemv(QG_Q4_0, qgk::kEpiPlain, w_packed, x, y, N, N, K, 1, stream, "qgemv_q4_0");
+}
+
+qg_status qgemv_fused_gateup_silu(int qtype, const void *w_gateup_packed, const float *x, float *y, int64_t N_ff,
+                                  int64_t K, void *stream)
+{
+    if (N_ff <= 0 || N_ff > kMaxDim) return fail(QG_EINVAL, "qgemv_fused_gateup_silu: N_ff=%lld", (long long)N_ff);
+    return run_qgemv(qtype, qgk::kEpiGateUp, w_gateup_packed, x, y, 2 * N_ff, N_ff, K, 1, stream,
+                     "qgemv_fused_gateup_silu");
+}
+
+qg_status qgemv_verify(int qtype, const void *w_packed, const float *X, float *Y, int64_t N, int64_t K, int M,
+                       void *stream)
+{
+    if (M < 2 || M > 6) return fail(QG_EUNSUPPORTED, "qgemv_verify: M=%d outside 2..6", M);
+    return run_qgemv(qtype, qgk::kEpiPlain, w_packed, X, Y, N, N, K, M, stream, "qgemv_verify");
+}
+
+qg_status gemv_f16_splitk(const void *w_f16, const float *x, float *y, int64_t N, int64_t K, void *stream)
+{
+    const char *fn = "gemv_f16_splitk";
+    if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim)
+        return fail(QG_EINVAL, "%s: N=%lld K=%lld must be positive", fn, (long long)N, (long long)K);
+    if (!w_f16 || !x || !y) return fail(QG_EINVAL, "%s: null pointer", fn);
+    if (!aligned(w_f16, 2)) return fail(QG_EALIGN, "%s: weights must be 2-byte aligned", fn);
+    if (!aligned(x, 4) || !aligned(y, 4)) return fail(QG_EALIGN, "%s: x and y must be 4-byte aligned", fn);
+    if (overlap(y, (size_t)N * 4, x, (size_t)K * 4)) return fail(QG_EINVAL, "%s: y overlaps x", fn);
+    if (overlap(y, (size_t)N * 4, w_f16, (size_t)N * (size_t)K * 2))
+        return fail(QG_EINVAL, "%s: y overlaps the weights", fn);
+
+    qgk::F16Plan p;
+    p.vec = (K % 8 == 0) && aligned(w_f16, 16) && aligned(x, 16);
+    const int64_t units = p.vec ? K / 8 : K;       // work items along K
+    // rows per workgroup: register-block 4 rows when there are plenty of rows
+    p.R = N >= 2048 ? 4 : (N >= 512 ? 2 : 1);
+    // wavefronts per workgroup: enough lanes for ~1-2 units each, at most 16
+    int64_t waves = (units + 63) / 64;
+    if (p.R >= 2) waves = (waves + 1) / 2;
+    if (waves > 16) waves = 16;
+    if (waves < 1) waves = 1;
+    p.waves = (int)waves;
+    p.grid = (N + p.R - 1) / p.R;
+    hipError_t e = qgk::launch_f16(p, (const uint16_t *)w_f16, x, y, N, K, as_stream(stream));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+const char *qg_status_str(int status)
+{
+    switch (status) {
+    case QG_OK: return "QG_OK";
+    case QG_EINVAL: return "QG_EINVAL: invalid argument";
+    case QG_EALIGN: return "QG_EALIGN: misaligned pointer";
+    case QG_EUNSUPPORTED: return "QG_EUNSUPPORTED: unsupported type or row count";
+    case QG_EHIP: return "QG_EHIP: HIP runtime error";
+    default: return "unknown qg_status";
+    }
+}
+
+const char *qg_last_error(void) { return g_last_error.c_str(); }
+
+qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int *split_k_waves_out, int64_t *workgroups,
+                       int *x_in_lds)
+{
+    qg_status st = check_qshape(qtype, N, K, "qg_plan_info");
+    if (st) return st;
+    if (M < 1 || M > 6) return fail(QG_EUNSUPPORTED, "qg_plan_info: M=%d", M);
+    const qgk::QPlan p = make_qplan(qtype, N, K, M);
+    if (split_k_waves_out) *split_k_waves_out = p.W;
+    if (workgroups) *workgroups = p.grid;
+    if (x_in_lds) *x_in_lds = p.x_in_lds ? 1 : 0;
+    return ok();
+}
+
+}  // extern "C"

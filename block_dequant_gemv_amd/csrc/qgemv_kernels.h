@@ -1,0 +1,52 @@
+// qgemv_kernels.h -- internal interface between the C ABI (qgemv_api.hip) and
+// the kernels (qgemv_kernels.hip). Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace qgk {
+
+constexpr int kEpiPlain = 0;
+constexpr int kEpiGateUp = 1;
+constexpr int kPackRows = 0;
+constexpr int kPackGateUp = 1;
+
+// Kernel arguments of the quantised GEMV (passed by value).
+struct QArgs {
+    qgl::Geometry geo;   // packed-weight geometry (geo.N = packed rows)
+    int64_t n_out;       // outputs per activation row (N, or N_ff for gate|up)
+    int64_t x_stride;    // floats between activation rows (K)
+    int64_t y_stride;    // floats between output rows (N)
+    int64_t tpg;         // row tiles walked by one group of W wavefronts
+};
+
+// How one quantised call is split. W depends only on (qtype, rows, K) so that
+// the decode GEMV and the verify GEMV of the same weight add in the same order.
+struct QPlan {
+    int W;               // wavefronts splitting one row tile along K (1, 2, 4)
+    int64_t tpg;         // tiles per group
+    int64_t grid;        // workgroups
+    int block;           // threads per workgroup (64 * wavefronts)
+    bool x_in_lds;       // activations staged in LDS
+    size_t lds_bytes;    // dynamic LDS per workgroup
+};
+
+struct F16Plan {
+    int R;               // rows per workgroup (register-blocked)
+    int waves;           // wavefronts per workgroup splitting K
+    bool vec;            // 16-byte path (K % 8 == 0 and aligned pointers)
+    int64_t grid;
+};
+
+hipError_t launch_qgemv(int qt, int M, int epi, const QPlan &p, const uint8_t *wp, const float *x, float *y,
+                        const QArgs &a, hipStream_t s);
+hipError_t launch_f16(const F16Plan &p, const uint16_t *w, const float *x, float *y, int64_t N, int64_t K,
+                      hipStream_t s);
+hipError_t launch_pack(const qgl::Geometry &g, const uint8_t *canon, const uint8_t *canon_up, uint8_t *packed,
+                       int mode, int64_t row0, int64_t nrows, int64_t rows_to_write, bool zero_gaps,
+                       hipStream_t s);
+
+}  // namespace qgk

@@ -1,0 +1,557 @@
+// qgemv_kernels.hip -- gfx950 kernels of libqgemv.
+//
+// Quantised GEMV (Q8_0 / Q4_0), its fused gate|up SiLU epilogue and the
+// multi-row verify all come from ONE kernel template, so that a row's
+// floating-point operations are the same whatever M is:
+//
+//   per lane, per block of 32 weights, per activation row m:
+//     s = 0;  s = fma(v_e, x_e, s) for e = 0..31      (v_e = q or nibble-8, exact in fp16)
+//     acc = fma(d, s, acc)                             (d = the block's fp16 scale)
+//   acc of the 32 lanes that share a row: fixed butterfly (DPP + swizzle)
+//   split-K wavefronts (if any): partials added in wavefront order in LDS
+//
+// Nothing in that sequence depends on M, on which wavefront or workgroup
+// handles the row, or on how many tiles a wavefront walks, so row m of the
+// verify output equals the M=1 output bit for bit. The build uses
+// -ffp-contract=off and every multiply-add is an explicit fma.
+//
+// Memory: each lane loads 16-byte units of the packed planes (layout.h); a
+// wavefront load instruction reads 1 KiB contiguous. Activations are staged
+// once per workgroup into LDS in a lane-swizzled order (chunk c of block j at
+// float4 slot c*32 + j), so the 32 lanes of a row read consecutive 16-byte
+// LDS words (no bank conflicts) and the two row slots of a wavefront read the
+// same words (broadcast).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.h"
+#include "qgemv_kernels.h"
+
+namespace qgk {
+
+using namespace qgl;
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
+__device__ __forceinline__ float as_f(int v) { return __builtin_bit_cast(float, v); }
+__device__ __forceinline__ int as_i(float v) { return __builtin_bit_cast(int, v); }
+
+// fp16 magic: 0x6400 | m is the fp16 number 1024 + m for m < 1024.
+// Registers that hold the conversion constants for the whole kernel. gfx9 VOP3
+// instructions take no literal operand and read at most one SGPR, so the mask
+// of v_and_or_b32 lives in an SGPR and the fp16 magic in a VGPR; the opaque
+// moves keep the compiler from re-materialising them before every use.
+struct Consts {
+    uint32_t magic;    // VGPR 0x64006400
+    uint32_t m_lo;     // SGPR 0x000F000F
+    uint32_t m_hi;     // SGPR 0x00F000F0
+};
+
+__device__ __forceinline__ Consts make_consts()
+{
+    Consts c;
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(c.magic));
+    asm volatile("s_mov_b32 %0, 0xf000f" : "=s"(c.m_lo));
+    asm volatile("s_mov_b32 %0, 0xf000f0" : "=s"(c.m_hi));
+    return c;
+}
+
+// (a & mask) | c in one instruction.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c)
+{
+    uint32_t d;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(mask), "v"(c));
+    return d;
+}
+
+// Q4_0 dword -> the 8 weights (nibble - 8) as 4 fp16 pairs, elements (0,1) (2,3) (4,5) (6,7).
+// Nibbles at bits 0-3 / 16-19 give 1024 + q; nibbles at bits 4-7 / 20-23 give
+// 1024 + 16 q, which (x/16 - 72) maps to q - 8 exactly.
+__device__ __forceinline__ void q4_pairs(uint32_t w, const Consts &k, h2 (&p)[4])
+{
+    const h2 off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h2 off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const uint32_t w8 = w >> 8;
+    p[0] = as_h2(and_or(w, k.m_lo, k.magic)) + off;
+    p[1] = __builtin_elementwise_fma(as_h2(and_or(w, k.m_hi, k.magic)), sixteenth, off16);
+    p[2] = as_h2(and_or(w8, k.m_lo, k.magic)) + off;
+    p[3] = __builtin_elementwise_fma(as_h2(and_or(w8, k.m_hi, k.magic)), sixteenth, off16);
+}
+
+// Q8_0 dword (bytes q XOR 0x80) -> the 4 int8 weights as 2 fp16 pairs, elements (0,1) (2,3).
+// v_perm_b32 builds [byte, 0x64, byte, 0x64] = fp16 (1024 + q + 128) twice.
+__device__ __forceinline__ void q8_pairs(uint32_t w, h2 (&p)[2])
+{
+    const h2 off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    p[0] = as_h2(__builtin_amdgcn_perm(0x64646464u, w, 0x04010400u)) + off;
+    p[1] = as_h2(__builtin_amdgcn_perm(0x64646464u, w, 0x04030402u)) + off;
+}
+
+// Sum over the 32 lanes of one wavefront half (lanes 0-31 and 32-63 separately).
+// Butterfly: xor 1, xor 2 (quad_perm), mirror within 8, mirror within 16 (DPP),
+// xor 16 (ds_swizzle). Every lane of the half ends with the same bits.
+__device__ __forceinline__ float half_wave_sum(float v)
+{
+    v += as_f(__builtin_amdgcn_update_dpp(0, as_i(v), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+    v += as_f(__builtin_amdgcn_update_dpp(0, as_i(v), 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+    v += as_f(__builtin_amdgcn_update_dpp(0, as_i(v), 0x141, 0xF, 0xF, false)); // row_half_mirror
+    v += as_f(__builtin_amdgcn_update_dpp(0, as_i(v), 0x140, 0xF, 0xF, false)); // row_mirror
+    v += as_f(__builtin_amdgcn_ds_swizzle(as_i(v), 0x401F));                     // lane ^ 16 within 32
+    return v;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u)
+{
+    return g / (1.0f + expf(-g)) * u;
+}
+
+// One lane's packed data for one (row tile, segment): 16 bytes per row and
+// half-block, plus the fp16 scales of its 4 rows.
+template <int QT>
+struct Unit {
+    static constexpr int NH = (QT == kQ8_0) ? 2 : 1;
+    u32x4 q[kRowsPerLane][NH];
+    u32x2 sc;
+};
+
+// Issue the loads of tile t, segment s (t, s wave-uniform). Lanes j >= nb of a
+// ragged last segment load nothing.
+template <int QT>
+__device__ __forceinline__ void load_unit(Unit<QT> &u, const uint8_t *__restrict__ wp, const Geometry &g, int64_t t,
+                                          int64_t s, int slot, int j)
+{
+    constexpr int NH = Unit<QT>::NH;
+    constexpr int64_t seg_q = (int64_t)kTileRows * kSegBlocks * NH * kUnit;
+    const int nb = (int)seg_blocks(g, s);
+    if (j >= nb) return;
+    const uint8_t *base = wp + t * g.tile_q + s * seg_q;
+    const uint32_t lane_off = (uint32_t)(slot * nb + j) * kUnit;
+    const uint32_t ustride = (uint32_t)(kSlots * nb * kUnit);
+#pragma unroll
+    for (int b = 0; b < kRowsPerLane; ++b)
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+            u.q[b][h] = __builtin_nontemporal_load((const u32x4 *)(base + (uint32_t)(b * NH + h) * ustride + lane_off));
+    const uint8_t *sbase = wp + g.scale_off + t * g.tile_s + s * (int64_t)(kTileRows * kSegBlocks * 2);
+    u.sc = __builtin_nontemporal_load((const u32x2 *)(sbase + (uint32_t)(slot * nb + j) * (kRowsPerLane * 2)));
+}
+
+// acc[m][b] += d_b * sum_e v_e * x_m[e] over the lane's block of segment s.
+template <int QT, int M, bool XLDS>
+__device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][kRowsPerLane], const Consts &k,
+                                             const f32x4 *xs4, const float *__restrict__ x, int64_t x_stride,
+                                             int64_t nseg, int64_t s, int j)
+{
+    constexpr int B = kRowsPerLane;
+    float sb[M][B];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int b = 0; b < B; ++b) sb[m][b] = 0.0f;
+
+    // 8 float4 chunks of x per block; Q4_0 consumes 2 chunks per dword, Q8_0 one.
+#pragma unroll
+    for (int c = 0; c < 8; c += 2) {
+        f32x4 xv[2][M];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                if (XLDS)
+                    xv[cc][m] = xs4[((m * nseg + s) * 8 + c + cc) * 32 + j];
+                else
+                    xv[cc][m] = *(const f32x4 *)(x + m * x_stride + s * kSegWeights + j * 32 + (c + cc) * 4);
+            }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            h2 p[4];
+            if (QT == kQ4_0) {
+                q4_pairs(u.q[b][0][c >> 1], k, p);
+            } else {
+                h2 p01[2], p23[2];
+                q8_pairs(u.q[b][c >> 2][c & 3], p01);
+                q8_pairs(u.q[b][c >> 2][(c & 3) + 1], p23);
+                p[0] = p01[0];
+                p[1] = p01[1];
+                p[2] = p23[0];
+                p[3] = p23[1];
+            }
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                float s_ = sb[m][b];
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    s_ = __builtin_fmaf((float)p[2 * cc].x, xv[cc][m].x, s_);
+                    s_ = __builtin_fmaf((float)p[2 * cc].y, xv[cc][m].y, s_);
+                    s_ = __builtin_fmaf((float)p[2 * cc + 1].x, xv[cc][m].z, s_);
+                    s_ = __builtin_fmaf((float)p[2 * cc + 1].y, xv[cc][m].w, s_);
+                }
+                sb[m][b] = s_;
+            }
+        }
+    }
+    const h2 d01 = as_h2(u.sc.x), d23 = as_h2(u.sc.y);
+    const _Float16 d[4] = {d01.x, d01.y, d23.x, d23.y};
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[m][b] = __builtin_fmaf((float)d[b], sb[m][b], acc[m][b]);
+}
+
+// ---------------------------------------------------------------------------
+// Quantised GEMV. Template parameters:
+//   QT   kQ8_0 / kQ4_0
+//   M    activation rows (1 = decode GEMV, 2..6 = verify)
+//   EPI  kEpiPlain (y = W x) or kEpiGateUp (y = silu(gate) * up, M = 1)
+//   W    wavefronts that split one row tile along K (1, 2 or 4)
+//   XLDS activations staged in LDS (true) or read from global memory
+// W == 1: a workgroup holds blockDim/64 independent wavefronts, wavefront g of
+//         workgroup b walks tiles [(b*G + g) * tpg, ... + tpg).
+// W  > 1: a workgroup is W wavefronts sharing the tiles [b * tpg, b * tpg + tpg);
+//         wavefront w adds segments [nseg*w/W, nseg*(w+1)/W) of every tile and
+//         the W partial sums are combined in LDS in wavefront order.
+// Each wavefront walks its (tile, segment) sequence with the next unit's loads
+// in flight while the current one is computed.
+template <int QT, int M, int EPI, int W, bool XLDS>
+__global__ void __launch_bounds__(256)
+qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float *__restrict__ y, QArgs a)
+{
+    constexpr int B = kRowsPerLane;
+    extern __shared__ f32x4 xs4[];
+    __shared__ float red[(W > 1) ? W * M * kSlots * B : 1];  // [W][M][slot][b]
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int slot = lane >> 5, j = lane & 31;
+    const int wk = (W > 1) ? wave : 0;
+    const int64_t group = (W > 1) ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+
+    const Geometry &g = a.geo;
+    const int64_t K = g.K, nseg = g.nseg;
+    const int64_t t_begin = group * a.tpg;
+    const int64_t t_end = (t_begin + a.tpg < g.n_tiles) ? t_begin + a.tpg : g.n_tiles;
+    const int64_t s_begin = nseg * wk / W, s_end = nseg * (wk + 1) / W;
+
+    const Consts k = make_consts();
+    Unit<QT> ua, ub;
+    if (t_begin < t_end) load_unit<QT>(ua, wp, g, t_begin, s_begin, slot, j);
+
+    if (XLDS) {
+        // stage X[m][k] (k < nseg*1024, zero beyond K) as xs4[((m*nseg + seg)*8 + c)*32 + jj]
+        const int64_t nchunk = (int64_t)M * nseg * (kSegWeights / 4);
+        for (int64_t i = tid; i < nchunk; i += blockDim.x) {
+            const int64_t m = i / (nseg * (kSegWeights / 4));
+            const int64_t kk = (i - m * nseg * (kSegWeights / 4)) * 4;
+            const int64_t seg = kk / kSegWeights;
+            const int within = (int)(kk - seg * kSegWeights);
+            const int jj = within >> 5, c = (within & 31) >> 2;
+            f32x4 v;
+            const float *src = x + m * a.x_stride + kk;
+            v.x = (kk + 0 < K) ? src[0] : 0.0f;
+            v.y = (kk + 1 < K) ? src[1] : 0.0f;
+            v.z = (kk + 2 < K) ? src[2] : 0.0f;
+            v.w = (kk + 3 < K) ? src[3] : 0.0f;
+            xs4[((m * nseg + seg) * 8 + c) * 32 + jj] = v;
+        }
+        __syncthreads();
+    }
+    if (t_begin >= t_end) return;   // uniform across the workgroup when W > 1
+
+    float acc[M][B];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[m][b] = 0.0f;
+
+    int64_t t = t_begin, s = s_begin;
+
+    // Compute (t, s) from `cur` while the loads of the following unit go into
+    // `nxt`; finish the tile after its last segment. Returns false at the end.
+    auto step = [&](Unit<QT> &cur, Unit<QT> &nxt) -> bool {
+        int64_t sn = s + 1, tn = t;
+        if (sn == s_end) {
+            sn = s_begin;
+            tn = t + 1;
+        }
+        const bool more = tn < t_end;
+        if (more) load_unit<QT>(nxt, wp, g, tn, sn, slot, j);
+        if (j < (int)seg_blocks(g, s)) compute_unit<QT, M, XLDS>(cur, acc, k, xs4, x, a.x_stride, nseg, s, j);
+        if (s + 1 == s_end) {
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int b = 0; b < B; ++b) acc[m][b] = half_wave_sum(acc[m][b]);
+            if (W > 1) {
+                // fixed-order combine of the split-K partials: ((p0 + p1) + p2) + p3
+                if (j == 0) {
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+#pragma unroll
+                        for (int b = 0; b < B; ++b) red[((wk * M + m) * kSlots + slot) * B + b] = acc[m][b];
+                }
+                __syncthreads();
+                if (wk == 0) {
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+#pragma unroll
+                        for (int b = 0; b < B; ++b) {
+                            float v = red[((0 * M + m) * kSlots + slot) * B + b];
+#pragma unroll
+                            for (int w = 1; w < W; ++w) v += red[((w * M + m) * kSlots + slot) * B + b];
+                            acc[m][b] = v;
+                        }
+                }
+                __syncthreads();
+            }
+            if (wk == 0) {
+                const int64_t row0 = t * kTileRows + slot * kRowsPerLane;
+                if (EPI == kEpiPlain) {
+                    if (j < M * B) {
+                        float v = 0.0f;
+#pragma unroll
+                        for (int m = 0; m < M; ++m)
+#pragma unroll
+                            for (int b = 0; b < B; ++b)
+                                if (j == m * B + b) v = acc[m][b];
+                        const int m = j / B, b = j % B;
+                        if (row0 + b < a.n_out) y[m * a.y_stride + row0 + b] = v;
+                    }
+                } else {
+                    // rows b = 2p (gate) and 2p+1 (up) of the lane hold output n = row0/2 + p
+                    if (j < B / 2) {
+                        float gv = 0.0f, uv = 0.0f;
+#pragma unroll
+                        for (int p = 0; p < B / 2; ++p)
+                            if (j == p) {
+                                gv = acc[0][2 * p];
+                                uv = acc[0][2 * p + 1];
+                            }
+                        const int64_t n = row0 / 2 + j;
+                        if (n < a.n_out) y[n] = silu_mul(gv, uv);
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int b = 0; b < B; ++b) acc[m][b] = 0.0f;
+        }
+        t = tn;
+        s = sn;
+        return more;
+    };
+
+    for (;;) {
+        if (!step(ua, ub)) break;
+        if (!step(ub, ua)) break;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp16 split-K GEMV: a workgroup of nw wavefronts owns R rows; its 64*nw lanes
+// split K in 8-element chunks (16 bytes of weights per lane per row); partials
+// are summed per wavefront (butterfly) and then over wavefronts in order in LDS.
+template <int R, bool VEC>
+__global__ void __launch_bounds__(1024)
+gemv_f16_kernel(const uint16_t *__restrict__ w, const float *__restrict__ x, float *__restrict__ y, int64_t N,
+                int64_t K)
+{
+    __shared__ float red[16 * R];
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int wave = tid >> 6, lane = tid & 63, nwave = nthr >> 6;
+    const int64_t row0 = (int64_t)blockIdx.x * R;
+
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+
+    if (VEC) {
+        const int64_t nch = K >> 3;
+        for (int64_t c = tid; c < nch; c += nthr) {
+            const f32x4 xa = *(const f32x4 *)(x + c * 8);
+            const f32x4 xb = *(const f32x4 *)(x + c * 8 + 4);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if (row0 + r < N) {
+                    const u32x4 wv = *(const u32x4 *)(w + (row0 + r) * K + c * 8);
+                    const h2 p0 = as_h2(wv.x), p1 = as_h2(wv.y), p2 = as_h2(wv.z), p3 = as_h2(wv.w);
+                    float s_ = acc[r];
+                    s_ = __builtin_fmaf((float)p0.x, xa.x, s_);
+                    s_ = __builtin_fmaf((float)p0.y, xa.y, s_);
+                    s_ = __builtin_fmaf((float)p1.x, xa.z, s_);
+                    s_ = __builtin_fmaf((float)p1.y, xa.w, s_);
+                    s_ = __builtin_fmaf((float)p2.x, xb.x, s_);
+                    s_ = __builtin_fmaf((float)p2.y, xb.y, s_);
+                    s_ = __builtin_fmaf((float)p3.x, xb.z, s_);
+                    s_ = __builtin_fmaf((float)p3.y, xb.w, s_);
+                    acc[r] = s_;
+                }
+            }
+        }
+    } else {
+        const _Float16 *wh = (const _Float16 *)w;
+        for (int64_t k = tid; k < K; k += nthr) {
+            const float xk = x[k];
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                if (row0 + r < N) acc[r] = __builtin_fmaf((float)wh[(row0 + r) * K + k], xk, acc[r]);
+        }
+    }
+
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const float h = half_wave_sum(acc[r]);
+        const float tot = as_f(__builtin_amdgcn_readlane(as_i(h), 0)) + as_f(__builtin_amdgcn_readlane(as_i(h), 32));
+        if (lane == 0) red[wave * R + r] = tot;
+    }
+    __syncthreads();
+    if (tid < R && row0 + tid < N) {
+        float v = red[tid];
+        for (int wv = 1; wv < nwave; ++wv) v += red[wv * R + tid];
+        y[row0 + tid] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Load-time packing: one thread per (packed row, block).
+//   mode kPackRows:   packed rows [row0, row0 + nrows) <- canonical rows 0..nrows-1,
+//                     plus zero padding rows [N, n_tiles*8) when row0 + nrows == N
+//   mode kPackGateUp: virtual row v <- gate row v/2 (v even) / up row v/2 (v odd)
+__global__ void pack_kernel(Geometry g, const uint8_t *__restrict__ canon, const uint8_t *__restrict__ canon_up,
+                            uint8_t *__restrict__ packed, int mode, int64_t row0, int64_t nrows, int64_t nthreads)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nthreads) return;
+    const int64_t r = i / g.KB, blk = i - r * g.KB;
+    const int cb = canon_block_bytes(g.qt);
+    if (mode == kPackRows) {
+        const int64_t row = row0 + r;
+        const uint8_t *src = (r < nrows) ? canon + (r * g.KB + blk) * cb : nullptr;
+        pack_block(g, src, packed, row, blk);
+    } else {
+        const int64_t v = r;
+        const int64_t n = v >> 1;
+        const uint8_t *base = (v & 1) ? canon_up : canon;
+        const uint8_t *src = (v < g.N) ? base + (n * g.KB + blk) * cb : nullptr;
+        pack_block(g, src, packed, v, blk);
+    }
+}
+
+// Zero the alignment gaps between and after the two packed planes (so that a
+// packed buffer is fully determined by its canonical input).
+__global__ void zero_gaps_kernel(uint8_t *__restrict__ packed, int64_t a0, int64_t a1, int64_t b0, int64_t b1)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (a0 + i < a1) packed[a0 + i] = 0;
+    if (b0 + i < b1) packed[b0 + i] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// launch helpers (host side)
+
+template <int QT, int M, int EPI, int W, bool XLDS>
+static hipError_t launch_q(const uint8_t *wp, const float *x, float *y, const QArgs &a, int64_t grid, int block,
+                           size_t lds, hipStream_t stream)
+{
+    auto kern = qgemv_kernel<QT, M, EPI, W, XLDS>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(block), lds, stream, wp, x, y, a);
+    return hipGetLastError();
+}
+
+template <int QT, int M, int EPI, int W>
+static hipError_t dispatch_x(const uint8_t *wp, const float *x, float *y, const QArgs &a, int64_t grid, int block,
+                             size_t lds, bool xlds, hipStream_t s)
+{
+    return xlds ? launch_q<QT, M, EPI, W, true>(wp, x, y, a, grid, block, lds, s)
+                : launch_q<QT, M, EPI, W, false>(wp, x, y, a, grid, block, 0, s);
+}
+
+template <int QT, int M, int EPI>
+static hipError_t dispatch_w(const uint8_t *wp, const float *x, float *y, const QArgs &a, int W, int64_t grid,
+                             int block, size_t lds, bool xlds, hipStream_t s)
+{
+    switch (W) {
+    case 1: return dispatch_x<QT, M, EPI, 1>(wp, x, y, a, grid, block, lds, xlds, s);
+    case 2: return dispatch_x<QT, M, EPI, 2>(wp, x, y, a, grid, block, lds, xlds, s);
+    default: return dispatch_x<QT, M, EPI, 4>(wp, x, y, a, grid, block, lds, xlds, s);
+    }
+}
+
+template <int QT>
+static hipError_t dispatch_m(const uint8_t *wp, const float *x, float *y, const QArgs &a, int M, int epi, int W,
+                             int64_t grid, int block, size_t lds, bool xlds, hipStream_t s)
+{
+    if (epi == kEpiGateUp) return dispatch_w<QT, 1, kEpiGateUp>(wp, x, y, a, W, grid, block, lds, xlds, s);
+    switch (M) {
+    case 1: return dispatch_w<QT, 1, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, s);
+    case 2: return dispatch_w<QT, 2, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, s);
+    case 3: return dispatch_w<QT, 3, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, s);
+    case 4: return dispatch_w<QT, 4, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, s);
+    case 5: return dispatch_w<QT, 5, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, s);
+    default: return dispatch_w<QT, 6, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, s);
+    }
+}
+
+hipError_t launch_qgemv(int qt, int M, int epi, const QPlan &p, const uint8_t *wp, const float *x, float *y,
+                        const QArgs &a, hipStream_t s)
+{
+    if (qt == kQ8_0)
+        return dispatch_m<kQ8_0>(wp, x, y, a, M, epi, p.W, p.grid, p.block, p.lds_bytes, p.x_in_lds, s);
+    return dispatch_m<kQ4_0>(wp, x, y, a, M, epi, p.W, p.grid, p.block, p.lds_bytes, p.x_in_lds, s);
+}
+
+hipError_t launch_f16(const F16Plan &p, const uint16_t *w, const float *x, float *y, int64_t N, int64_t K,
+                      hipStream_t s)
+{
+    dim3 grid((unsigned)p.grid), block(p.waves * 64);
+    if (p.vec) {
+        switch (p.R) {
+        case 1: hipLaunchKernelGGL((gemv_f16_kernel<1, true>), grid, block, 0, s, w, x, y, N, K); break;
+        case 2: hipLaunchKernelGGL((gemv_f16_kernel<2, true>), grid, block, 0, s, w, x, y, N, K); break;
+        default: hipLaunchKernelGGL((gemv_f16_kernel<4, true>), grid, block, 0, s, w, x, y, N, K); break;
+        }
+    } else {
+        switch (p.R) {
+        case 1: hipLaunchKernelGGL((gemv_f16_kernel<1, false>), grid, block, 0, s, w, x, y, N, K); break;
+        case 2: hipLaunchKernelGGL((gemv_f16_kernel<2, false>), grid, block, 0, s, w, x, y, N, K); break;
+        default: hipLaunchKernelGGL((gemv_f16_kernel<4, false>), grid, block, 0, s, w, x, y, N, K); break;
+        }
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_pack(const Geometry &g, const uint8_t *canon, const uint8_t *canon_up, uint8_t *packed, int mode,
+                       int64_t row0, int64_t nrows, int64_t rows_to_write, bool zero_gaps, hipStream_t s)
+{
+    const int64_t nthreads = rows_to_write * g.KB;
+    const int block = 256;
+    if (nthreads > 0) {
+        const int64_t grid = (nthreads + block - 1) / block;
+        hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(block), 0, s, g, canon, canon_up, packed, mode,
+                           row0, nrows, nthreads);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (zero_gaps) {
+        const int64_t a0 = g.n_tiles * g.tile_q, a1 = g.scale_off;
+        const int64_t b0 = g.scale_off + g.n_tiles * g.tile_s, b1 = g.total;
+        const int64_t n = (a1 - a0 > b1 - b0) ? a1 - a0 : b1 - b0;   // each gap < 256 bytes
+        if (n > 0) {
+            hipLaunchKernelGGL(zero_gaps_kernel, dim3(1), dim3(256), 0, s, packed, a0, a1, b0, b1);
+            return hipGetLastError();
+        }
+    }
+    return hipSuccess;
+}
+
+}  // namespace qgk

@@ -1,0 +1,146 @@
+/*
+ * qgemv.h -- C ABI of libqgemv.so, block-dequant GEMV for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (the decode-time matrix-vector products of the
+ * from-scratch LLM engines on the pages):
+ *   y[n] = sum_k W[n][k] * x[k],   W[n][k] = d(n, k/32) * v(n, k)
+ * where W is read in a GGUF-style block-quantised form and dequantised inside
+ * the product ("EdgeRunner beats llama.cpp", What worked, item 2: fused Q8_0
+ * dequant + GEMV, no float copy of the weights).
+ *   Q8_0: 32 int8 quants + one fp16 scale per block, v = q            (34 B / 32 weights)
+ *   Q4_0: 32 4-bit quants + one fp16 scale per block, v = nibble - 8  (18 B / 32 weights)
+ * (RunIT_Mac README, optimisation table: 1.06 and 0.56 bytes per weight.)
+ * x and y are fp32 and the accumulation is fp32 (RunIT_Mac README, kernel table
+ * "f32in_f32out" names and the f32 data-flow figure).
+ *
+ * Conventions for every call below
+ *  - Pointers named *_host are host memory. Every other pointer is DEVICE
+ *    memory (hipMalloc / torch CUDA tensors), never a host mapping: the pages
+ *    measured running the weights off a memory-mapped file as their worst bug
+ *    (robotnurse.io "We wrote our own inference engine", What actually moved it, 1).
+ *  - stream is a hipStream_t passed as void*; NULL means the null stream.
+ *    Calls only enqueue work and return; results are valid once the caller has
+ *    synchronised that stream. Device faults surface at that synchronisation.
+ *  - The caller owns and frees every buffer. The GEMV calls allocate nothing
+ *    and keep no per-call state; they may be captured into a HIP graph.
+ *  - Arguments are checked on the host before any HIP call. A bad argument
+ *    returns QG_EINVAL / QG_EALIGN / QG_EUNSUPPORTED and enqueues nothing; a
+ *    failed launch returns QG_EHIP. qg_last_error() gives a thread-local
+ *    message for the last failure on the calling thread.
+ *  - Same inputs give bitwise the same outputs, run to run (no atomics, no
+ *    cross-workgroup reductions, fixed reduction trees).
+ *  - Quantised weights are re-tiled once, at load time, by qg_pack* into the
+ *    library's packed layout, the way the robotnurse.io post folds projections
+ *    once at load rather than per token (What actually moved it, 5). The packed
+ *    layout is internal: only qg_packed_size() and the pack/unpack calls know it.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QG_OK = 0,
+    QG_EINVAL = 1,       /* null pointer, bad size, overlapping buffers        */
+    QG_EALIGN = 2,       /* a pointer is not aligned as the call requires       */
+    QG_EUNSUPPORTED = 3, /* unknown qtype, or M outside 2..6 for verify         */
+    QG_EHIP = 4          /* the HIP runtime reported an error at launch         */
+} qg_status;
+
+typedef enum { QG_Q8_0 = 1, QG_Q4_0 = 2 } qg_qtype;
+
+/* ---- load-time packing --------------------------------------------------- */
+
+/* Bytes of the packed form of an N x K matrix of `qtype` (K % 32 == 0, N, K > 0).
+ * Returns 0 for invalid arguments. The packed form holds the same quant and
+ * scale bytes as the canonical one plus zero padding of the last row tile (up
+ * to 7 rows) and 256-byte alignment of its two planes. */
+size_t qg_packed_size(int qtype, int64_t N, int64_t K);
+
+/* Re-tile a canonical matrix already in device memory into the packed layout.
+ * canonical: N*K/32 GGUF-style blocks, row-major (row n = K/32 consecutive
+ *   blocks; block = little-endian fp16 scale then the quants; Q4_0 byte j holds
+ *   element j in its low nibble and element j+16 in its high nibble).
+ * packed: qg_packed_size(qtype, N, K) bytes, 16-byte aligned, not overlapping
+ *   canonical. Padding rows are written as zeros. Stream-ordered kernel. */
+qg_status qg_pack(int qtype, const void *canonical, void *packed, int64_t N, int64_t K, void *stream);
+
+/* Load-time concatenation (e.g. Q, K and V projections into one fused QKV
+ * weight, RunIT_Mac README "Fused QKV+bias"): pack the nrows canonical rows into
+ * rows [row0, row0 + nrows) of a packed N_total x K matrix. The call whose rows
+ * end at N_total also zero-fills the padding rows. Calls for disjoint row
+ * ranges may run in any order. */
+qg_status qg_pack_rows(int qtype, const void *canonical, void *packed, int64_t N_total,
+                       int64_t row0, int64_t nrows, int64_t K, void *stream);
+
+/* Load-time fusion of a gate and an up projection (each N_ff x K, canonical,
+ * device memory) into one packed weight for qgemv_fused_gateup_silu.
+ * packed: qg_packed_size(qtype, 2 * N_ff, K) bytes, 16-byte aligned.
+ * Gate row n and up row n are placed in the same wavefront's registers. */
+qg_status qg_pack_gateup(int qtype, const void *gate, const void *up, void *packed,
+                         int64_t N_ff, int64_t K, void *stream);
+
+/* Host-memory versions of the packer and its inverse (same bytes as the device
+ * packer). unpack(pack(B)) == B byte for byte. gate/up fusion on the host:
+ * qg_pack_gateup_host. */
+qg_status qg_pack_host(int qtype, const void *canonical_host, void *packed_host, int64_t N, int64_t K);
+qg_status qg_unpack_host(int qtype, const void *packed_host, void *canonical_host, int64_t N, int64_t K);
+qg_status qg_pack_gateup_host(int qtype, const void *gate_host, const void *up_host, void *packed_host,
+                              int64_t N_ff, int64_t K);
+
+/* ---- the GEMVs ----------------------------------------------------------- */
+
+/* y[N] = W x for a packed Q8_0 weight (N x K, K % 32 == 0); x: fp32 [K];
+ * y: fp32 [N]. w_packed 16-byte aligned, x and y 4-byte aligned, y must not
+ * overlap x or w_packed. A fused QKV projection is this call on the packed
+ * concatenation (qg_pack_rows); the caller slices y. */
+qg_status qgemv_q8_0(const void *w_packed, const float *x, float *y, int64_t N, int64_t K, void *stream);
+
+/* Same for a packed Q4_0 weight (weight value nibble - 8). */
+qg_status qgemv_q4_0(const void *w_packed, const float *x, float *y, int64_t N, int64_t K, void *stream);
+
+/* Unquantised fp16 weights, y = W x with W fp16 row-major [N][K] (any K >= 1,
+ * 2-byte aligned; the fast path needs K % 8 == 0 and 16-byte alignment), x fp32
+ * [K], y fp32 [N]. K is split across the wavefronts of one workgroup and the
+ * partial sums are combined in LDS in a fixed order: deterministic, no
+ * workspace, no atomics (robotnurse.io post, What actually moved it, 4: a
+ * split-K fp16 GEMV for the unquantised matrices). */
+qg_status gemv_f16_splitk(const void *w_f16, const float *x, float *y, int64_t N, int64_t K, void *stream);
+
+/* Fused gate+up with the SiLU epilogue (RunIT_Mac README "Fused gate+up+silu",
+ * one dispatch instead of three): y[n] = silu(g[n]) * u[n] for n < N_ff, where
+ * g = W_gate x, u = W_up x and silu(g) = g / (1 + exp(-g)).
+ * w_gateup_packed comes from qg_pack_gateup; x fp32 [K]; y fp32 [N_ff]. */
+qg_status qgemv_fused_gateup_silu(int qtype, const void *w_gateup_packed, const float *x, float *y,
+                                  int64_t N_ff, int64_t K, void *stream);
+
+/* Multi-row "verify" GEMV: Y[m][n] = sum_k W[n][k] X[m][k] for 2 <= M <= 6,
+ * X fp32 row-major [M][K], Y fp32 row-major [M][N]. The packed weights are
+ * streamed once for all M rows, and row m of Y is bit-for-bit (memcmp) equal
+ * to what qgemv_q8_0 / qgemv_q4_0 return for x = X[m] (robotnurse.io post,
+ * Update and "Correctness first": a 3-6-row verify pass in one weight stream,
+ * checked against the decode kernel with memcmp). */
+qg_status qgemv_verify(int qtype, const void *w_packed, const float *X, float *Y,
+                       int64_t N, int64_t K, int M, void *stream);
+
+/* ---- diagnostics --------------------------------------------------------- */
+
+const char *qg_status_str(int status);
+const char *qg_last_error(void);
+
+/* How a quantised call of this shape is split (for reports): waves that share
+ * one row tile along K, workgroups launched, and whether x is staged in LDS.
+ * Pure host function. Returns QG_OK or QG_EINVAL. */
+qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int *split_k_waves,
+                       int64_t *workgroups, int *x_in_lds);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

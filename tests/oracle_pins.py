@@ -300,3 +300,21 @@ PINS = [
     pin_composites,
     pin_rejects_bad_shapes,
 ]
+
+
+def failing_pins(lib_path: str) -> list[str]:
+    """Names of the pins that fail against the oracle library at lib_path."""
+    L = O.lib(lib_path)
+    failed = []
+    for pin in PINS:
+        try:
+            pin(L)
+        except (AssertionError, ValueError, OverflowError, ZeroDivisionError):
+            failed.append(pin.__name__)
+    return failed
+
+
+if __name__ == "__main__":
+    # python tests/oracle_pins.py <liboracle variant.so>: print the failing pins as JSON
+    import sys as _sys
+    print(json.dumps(failing_pins(_sys.argv[1])))

@@ -1,0 +1,180 @@
+"""Host-side tests of libqgemv: symbols, argument checks, the packer (no GPU needed).
+
+None of these makes a compute call: every entry point below is given arguments
+that its host-side checks reject before any HIP call is made.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import block_dequant_gemv_amd as qg
+from block_dequant_gemv_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemv.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(qg.LIB_PATH):
+        from block_dequant_gemv_amd import build
+        build.build()
+    return qg.lib()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(q\w+|gemv_\w+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert sorted(qg.SYMBOLS) == header_functions()
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", qg.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in header_functions():
+        assert name in exported, name
+        assert getattr(L, name) is not None
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert qg.qg_status_str(s).startswith("QG_")
+    assert "unknown" in qg.qg_status_str(99)
+
+
+def test_packed_size(L):
+    # N % 8 == 0, K % 1024 == 0: the packed form is exactly the canonical bytes
+    for kind, bb in (("q8_0", 34), ("q4_0", 18)):
+        for N, K in ((1024, 1024), (4096, 1024), (17408, 5120), (5120, 17408)):
+            assert qg.qg_packed_size(kind, N, K) == N * (K // 32) * bb
+    # ragged: padding rows up to a multiple of 8 and 256-byte plane alignment
+    # 9 rows -> 2 tiles of 8 rows; quant plane 16 rows * 2 blocks * 16 B = 512,
+    # scale plane 16 * 2 * 2 B = 64 -> 256 after alignment
+    assert qg.qg_packed_size("q4_0", 9, 64) == 512 + 256
+    assert qg.qg_packed_size("q8_0", 9, 64) == 1024 + 256
+    for bad in ((0, 32), (-1, 32), (8, 33), (8, 0)):
+        assert qg.qg_packed_size("q8_0", *bad) == 0
+    assert qg.qg_packed_size(7, 8, 32) == 0
+
+
+FAKE = 0x10000  # a 64 KiB-aligned address that is never dereferenced
+
+
+def call(L, name, *args):
+    return getattr(L, name)(*args)
+
+
+def test_argument_checks_return_codes_without_gpu(L):
+    null = None
+    f = FAKE
+    # null pointers
+    assert call(L, "qgemv_q8_0", null, f, f + 4096, 8, 32, null) == qg.QG_EINVAL
+    assert call(L, "qgemv_q4_0", f, null, f + 4096, 8, 32, null) == qg.QG_EINVAL
+    assert call(L, "gemv_f16_splitk", f, f + 4096, null, 8, 32, null) == qg.QG_EINVAL
+    # bad sizes
+    assert call(L, "qgemv_q8_0", f, f + (1 << 20), f + (2 << 20), 8, 48, null) == qg.QG_EINVAL
+    assert call(L, "qgemv_q4_0", f, f + (1 << 20), f + (2 << 20), 0, 64, null) == qg.QG_EINVAL
+    assert call(L, "gemv_f16_splitk", f, f + (1 << 20), f + (2 << 20), 8, -1, null) == qg.QG_EINVAL
+    # misalignment
+    assert call(L, "qgemv_q8_0", f + 8, f + (1 << 20), f + (2 << 20), 8, 32, null) == qg.QG_EALIGN
+    assert call(L, "qgemv_q8_0", f, f + (1 << 20) + 4, f + (2 << 20), 8, 32, null) == qg.QG_EALIGN
+    assert call(L, "qgemv_q8_0", f, f + (1 << 20), f + (2 << 20) + 2, 8, 32, null) == qg.QG_EALIGN
+    assert call(L, "gemv_f16_splitk", f + 1, f + (1 << 20), f + (2 << 20), 8, 32, null) == qg.QG_EALIGN
+    # overlapping output
+    assert call(L, "qgemv_q8_0", f, f + (1 << 20), f + (1 << 20) + 16, 8, 32, null) == qg.QG_EINVAL
+    assert call(L, "qgemv_q4_0", f, f + (1 << 20), f + 64, 8, 32, null) == qg.QG_EINVAL
+    assert call(L, "gemv_f16_splitk", f, f + (1 << 20), f + (1 << 20), 8, 32, null) == qg.QG_EINVAL
+    # unsupported qtype / row count
+    assert call(L, "qgemv_verify", 1, f, f + (1 << 20), f + (2 << 20), 8, 32, 1, null) == qg.QG_EUNSUPPORTED
+    assert call(L, "qgemv_verify", 1, f, f + (1 << 20), f + (2 << 20), 8, 32, 7, null) == qg.QG_EUNSUPPORTED
+    assert call(L, "qgemv_verify", 3, f, f + (1 << 20), f + (2 << 20), 8, 32, 2, null) == qg.QG_EUNSUPPORTED
+    assert call(L, "qgemv_fused_gateup_silu", 5, f, f + (1 << 20), f + (2 << 20), 8, 32, null) == qg.QG_EUNSUPPORTED
+    assert call(L, "qgemv_fused_gateup_silu", 1, f, f + (1 << 20), f + (2 << 20), 0, 32, null) == qg.QG_EINVAL
+    # verify: the M x K activations must not overlap the M x N outputs
+    assert call(L, "qgemv_verify", 2, f, f + (1 << 20), f + (1 << 20) + 4 * 32 * 3, 8, 32, 4, null) == qg.QG_EINVAL
+    # packers
+    assert call(L, "qg_pack", 1, null, f, 8, 32, null) == qg.QG_EINVAL
+    assert call(L, "qg_pack", 1, f, f + 8, 8, 32, null) == qg.QG_EALIGN
+    assert call(L, "qg_pack_rows", 2, f, f + (1 << 20), 8, 6, 4, 32, null) == qg.QG_EINVAL
+    assert call(L, "qg_pack_gateup", 2, f, null, f + (1 << 20), 8, 32, null) == qg.QG_EINVAL
+    assert call(L, "qg_pack", 1, f, f + 16, 8, 32, null) == qg.QG_EINVAL  # overlap
+    msg = qg.qg_last_error()
+    assert "overlap" in msg
+
+
+def test_plan_info_split_is_independent_of_m(L):
+    # the decode GEMV and the verify GEMV of a weight must add in the same order
+    for kind in ("q8_0", "q4_0"):
+        for N, K in ((1, 32), (100, 2080), (1024, 2048), (1024, 3072), (5120, 17408), (17408, 5120),
+                     (4096, 1024), (248320, 5120), (64, 65536)):
+            w1 = qg.qg_plan_info(kind, N, K, 1)["split_k_waves"]
+            for M in range(2, 7):
+                assert qg.qg_plan_info(kind, N, K, M)["split_k_waves"] == w1
+    assert qg.qg_plan_info("q4_0", 5120, 17408)["split_k_waves"] > 1
+    assert qg.qg_plan_info("q4_0", 248320, 5120)["split_k_waves"] == 1
+
+
+SHAPES = [(1, 32), (3, 64), (8, 1024), (9, 1056), (17, 2048), (24, 3104), (5, 5120)]
+
+
+@pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_pack_unpack_roundtrip(L, kind, N, K):
+    canon = W.matrix(kind, N, K, np.random.default_rng(N * 7 + K))
+    packed = qg.qg_pack_host(kind, canon, N, K)
+    assert packed.size == qg.qg_packed_size(kind, N, K)
+    back = qg.qg_unpack_host(kind, packed, N, K)
+    assert np.array_equal(back, canon)
+    # the packed form holds the same number of non-padding bytes
+    bb = 34 if kind == "q8_0" else 18
+    assert packed.size >= canon.size and canon.size == N * (K // 32) * bb
+
+
+@pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
+def test_pack_is_a_permutation_of_bytes(L, kind):
+    # The packed planes hold exactly the canonical quants (Q8_0 bytes XOR 0x80,
+    # Q4_0 nibbles moved within their block) and scales, plus zeros for the
+    # padding rows of the last tile.
+    N, K = 13, 1088
+    canon = W.matrix(kind, N, K, np.random.default_rng(3))
+    packed = qg.qg_pack_host(kind, canon, N, K)
+    bb, qb = (34, 32) if kind == "q8_0" else (18, 16)
+    KB = K // 32
+    rows_pad = (N + 7) // 8 * 8
+    blocks = canon.reshape(-1, bb)
+    qplane = packed[: rows_pad * KB * qb]
+    soff = (qplane.size + 255) // 256 * 256
+    splane = packed[soff: soff + rows_pad * KB * 2].copy().view("<u2")
+    pad_blocks = (rows_pad - N) * KB
+    if kind == "q8_0":
+        want_q = np.concatenate([blocks[:, 2:].reshape(-1) ^ 0x80, np.zeros(pad_blocks * qb, np.uint8)])
+        got_q = qplane
+    else:
+        q = blocks[:, 2:].reshape(-1)
+        want_q = np.concatenate([q & 0xF, q >> 4, np.zeros(pad_blocks * 32, np.uint8)])
+        got_q = np.concatenate([qplane & 0xF, qplane >> 4])
+    assert np.array_equal(np.sort(want_q), np.sort(got_q))
+    want_s = np.concatenate([blocks[:, 0:2].copy().view("<u2").reshape(-1), np.zeros(pad_blocks, np.uint16)])
+    assert np.array_equal(np.sort(want_s), np.sort(splane))
+    assert not packed[qplane.size:soff].any() and not packed[soff + splane.size * 2:].any()
+
+
+@pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
+def test_gateup_host_pack_interleaves_rows(L, kind):
+    N_ff, K = 11, 2048
+    rng = np.random.default_rng(21)
+    gate = W.matrix(kind, N_ff, K, rng)
+    up = W.matrix(kind, N_ff, K, rng)
+    bb = 34 if kind == "q8_0" else 18
+    inter = np.stack([gate.reshape(N_ff, -1), up.reshape(N_ff, -1)], axis=1).reshape(-1)
+    assert inter.size == 2 * N_ff * (K // 32) * bb
+    assert np.array_equal(qg.qg_pack_gateup_host(kind, gate, up, N_ff, K), qg.qg_pack_host(kind, inter, 2 * N_ff, K))
