@@ -67,14 +67,23 @@ qg_status check_qshape(int qt, int64_t N, int64_t K, const char *fn)
     return QG_OK;
 }
 
-// Wavefronts that split one tile along K. Depends only on (rows, K): small
-// row counts with long K get more wavefronts per tile so that the chip has
-// enough loads in flight; a decode call and a verify call of the same weight
-// always agree.
+int64_t env_int(const char *name, int64_t dflt)
+{
+    const char *v = getenv(name);
+    return (v && *v) ? atoll(v) : dflt;
+}
+
+// Wavefronts that split one tile along K. Depends only on (rows, K): a matrix
+// with few row tiles gets more wavefronts per tile so that the chip has enough
+// loads in flight. The decode and the verify call of the same weight always
+// get the same split, and so add in the same order. (QG_SPLIT_K overrides it
+// for launch-shape sweeps; it must then be the same for every call.)
 int split_k_waves(int64_t rows, int64_t K)
 {
     const int64_t n_tiles = (rows + qgl::kTileRows - 1) / qgl::kTileRows;
     const int64_t nseg = (K / 32 + qgl::kSegBlocks - 1) / qgl::kSegBlocks;
+    const int64_t forced = env_int("QG_SPLIT_K", 0);
+    if (forced == 1 || forced == 2 || forced == 4 || forced == 8) return forced <= nseg ? (int)forced : 1;
     int W = 1;
     while (W < 4 && 2 * W <= nseg && n_tiles * W < 2048) W *= 2;
     return W;
@@ -82,32 +91,42 @@ int split_k_waves(int64_t rows, int64_t K)
 
 constexpr size_t kLdsLimit = 96 * 1024;   // above this, activations are read from global memory
 
+// Launch shape (measured on MI355X with cold weights):
+//  - tiles per group: 1, or 2 for very tall matrices (>= 24K row tiles);
+//  - 4 wavefronts per workgroup share one LDS copy of the activations, fewer
+//    only when there are too few groups to cover the CUs;
+//  - for M = 1, activations are staged in LDS when a workgroup streams at least
+//    4x as many weight bytes as it stages, otherwise read from global memory
+//    (L2); with several activation rows (verify) each staged value is reused
+//    M times per weight, so LDS is used whenever it fits.
+// Tuning overrides (read on every call): QG_TILES_PER_GROUP, QG_WAVES_PER_WG
+// (split 1 only), QG_X_GLOBAL (0/1). None of them changes a row's operations.
 qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M)
 {
     qgk::QPlan p;
     const Geometry g = qgl::geometry(qt, rows, K);
     p.W = split_k_waves(rows, K);
-    // About 4096 groups of wavefronts (16 per CU on 256 CUs); a group walks tpg
-    // consecutive row tiles, so large matrices are read as long sequential runs.
-    const int64_t target_groups = 4096 / p.W;
-    p.tpg = g.n_tiles / target_groups;
-    if (p.tpg < 1) p.tpg = 1;
-    const char *env = getenv("QG_TILES_PER_GROUP");
-    if (env && atoll(env) > 0) p.tpg = atoll(env);
+    p.tpg = g.n_tiles >= 24000 ? 2 : 1;
+    const int64_t tpg_env = env_int("QG_TILES_PER_GROUP", 0);
+    if (tpg_env > 0) p.tpg = tpg_env;
     const int64_t groups = (g.n_tiles + p.tpg - 1) / p.tpg;
     int G;   // groups per workgroup
     if (p.W > 1) {
         G = 1;
         p.block = 64 * p.W;
     } else {
-        // many groups: 4 wavefronts share one LDS copy of x; few groups: one
-        // wavefront per workgroup so that the launch spreads over every CU
-        G = groups >= 2048 ? 4 : 1;
+        G = groups >= 512 ? 4 : (groups >= 256 ? 2 : 1);
+        const int64_t g_env = env_int("QG_WAVES_PER_WG", 0);
+        if (g_env == 1 || g_env == 2 || g_env == 4) G = (int)g_env;
         p.block = 64 * G;
     }
     p.grid = (groups + G - 1) / G;
     const size_t xbytes = (size_t)M * (size_t)g.nseg * qgl::kSegWeights * sizeof(float);
-    p.x_in_lds = xbytes <= kLdsLimit;
+    const double wg_weight_bytes = (double)G * (double)p.tpg * (double)(g.tile_q + g.tile_s);
+    bool lds = xbytes <= kLdsLimit && (M > 1 || wg_weight_bytes >= 4.0 * (double)xbytes);
+    const int64_t xg_env = env_int("QG_X_GLOBAL", -1);
+    if (xg_env == 0 || xg_env == 1) lds = xbytes <= kLdsLimit && xg_env == 0;
+    p.x_in_lds = lds;
     p.lds_bytes = p.x_in_lds ? xbytes : 0;
     return p;
 }

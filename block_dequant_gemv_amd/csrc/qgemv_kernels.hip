@@ -119,35 +119,45 @@ struct Unit {
     u32x2 sc;
 };
 
-// Issue the loads of tile t, segment s (t, s wave-uniform). Lanes j >= nb of a
-// ragged last segment load nothing.
+// Issue the loads of tile t, segment s (t, s wave-uniform). In a ragged last
+// segment lanes j >= nb load block nb-1 again (in bounds); their scales are
+// zeroed in compute_unit. With `real` false (no unit left) every lane loads
+// the first 16 bytes of the buffer instead, one cache line per wavefront.
+// The loop body thus always issues the same loads with no branch around them,
+// so the compiler's wait counts keep the next unit in flight while the
+// current one is computed.
 template <int QT>
 __device__ __forceinline__ void load_unit(Unit<QT> &u, const uint8_t *__restrict__ wp, const Geometry &g, int64_t t,
-                                          int64_t s, int slot, int j)
+                                          int64_t s, int slot, int j, bool real)
 {
     constexpr int NH = Unit<QT>::NH;
     constexpr int64_t seg_q = (int64_t)kTileRows * kSegBlocks * NH * kUnit;
+    t = real ? t : 0;
+    s = real ? s : 0;
     const int nb = (int)seg_blocks(g, s);
-    if (j >= nb) return;
+    const int jc = j < nb ? j : nb - 1;
     const uint8_t *base = wp + t * g.tile_q + s * seg_q;
-    const uint32_t lane_off = (uint32_t)(slot * nb + j) * kUnit;
-    const uint32_t ustride = (uint32_t)(kSlots * nb * kUnit);
+    const uint32_t lane_off = real ? (uint32_t)(slot * nb + jc) * kUnit : 0u;
+    const uint32_t ustride = real ? (uint32_t)(kSlots * nb * kUnit) : 0u;
 #pragma unroll
     for (int b = 0; b < kRowsPerLane; ++b)
 #pragma unroll
         for (int h = 0; h < NH; ++h)
             u.q[b][h] = __builtin_nontemporal_load((const u32x4 *)(base + (uint32_t)(b * NH + h) * ustride + lane_off));
     const uint8_t *sbase = wp + g.scale_off + t * g.tile_s + s * (int64_t)(kTileRows * kSegBlocks * 2);
-    u.sc = __builtin_nontemporal_load((const u32x2 *)(sbase + (uint32_t)(slot * nb + j) * (kRowsPerLane * 2)));
+    const uint32_t s_off = real ? (uint32_t)(slot * nb + jc) * (kRowsPerLane * 2) : 0u;
+    u.sc = __builtin_nontemporal_load((const u32x2 *)(sbase + s_off));
 }
 
 // acc[m][b] += d_b * sum_e v_e * x_m[e] over the lane's block of segment s.
 template <int QT, int M, bool XLDS>
 __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][kRowsPerLane], const Consts &k,
                                              const f32x4 *xs4, const float *__restrict__ x, int64_t x_stride,
-                                             int64_t nseg, int64_t s, int j)
+                                             int64_t nseg, int64_t s, int j, int nb)
 {
     constexpr int B = kRowsPerLane;
+    const bool live = j < nb;     // false only for lanes past the end of a ragged last segment
+    j = live ? j : nb - 1;
     float sb[M][B];
 #pragma unroll
     for (int m = 0; m < M; ++m)
@@ -195,7 +205,7 @@ __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][
             }
         }
     }
-    const h2 d01 = as_h2(u.sc.x), d23 = as_h2(u.sc.y);
+    const h2 d01 = as_h2(live ? u.sc.x : 0u), d23 = as_h2(live ? u.sc.y : 0u);
     const _Float16 d[4] = {d01.x, d01.y, d23.x, d23.y};
 #pragma unroll
     for (int m = 0; m < M; ++m)
@@ -208,7 +218,7 @@ __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][
 //   QT   kQ8_0 / kQ4_0
 //   M    activation rows (1 = decode GEMV, 2..6 = verify)
 //   EPI  kEpiPlain (y = W x) or kEpiGateUp (y = silu(gate) * up, M = 1)
-//   W    wavefronts that split one row tile along K (1, 2 or 4)
+//   W    wavefronts that split one row tile along K (1, 2, 4 or 8)
 //   XLDS activations staged in LDS (true) or read from global memory
 // W == 1: a workgroup holds blockDim/64 independent wavefronts, wavefront g of
 //         workgroup b walks tiles [(b*G + g) * tpg, ... + tpg).
@@ -217,8 +227,11 @@ __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][
 //         the W partial sums are combined in LDS in wavefront order.
 // Each wavefront walks its (tile, segment) sequence with the next unit's loads
 // in flight while the current one is computed.
+#ifndef QG_WAVES_PER_EU
+#define QG_WAVES_PER_EU 1
+#endif
 template <int QT, int M, int EPI, int W, bool XLDS>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QG_WAVES_PER_EU)))
 qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float *__restrict__ y, QArgs a)
 {
     constexpr int B = kRowsPerLane;
@@ -239,8 +252,10 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
     const int64_t s_begin = nseg * wk / W, s_end = nseg * (wk + 1) / W;
 
     const Consts k = make_consts();
+    // This wavefront's units, in order: (t, s) for t in [t_begin, t_end), s in [s_begin, s_end).
+    const int64_t n_units = (t_end > t_begin ? t_end - t_begin : 0) * (s_end - s_begin);
     Unit<QT> ua, ub;
-    if (t_begin < t_end) load_unit<QT>(ua, wp, g, t_begin, s_begin, slot, j);
+    load_unit<QT>(ua, wp, g, t_begin, s_begin, slot, j, n_units > 0);
 
     if (XLDS) {
         // stage X[m][k] (k < nseg*1024, zero beyond K) as xs4[((m*nseg + seg)*8 + c)*32 + jj]
@@ -261,7 +276,7 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
         }
         __syncthreads();
     }
-    if (t_begin >= t_end) return;   // uniform across the workgroup when W > 1
+    if (n_units == 0) return;   // uniform across the workgroup when W > 1
 
     float acc[M][B];
 #pragma unroll
@@ -269,19 +284,22 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
 #pragma unroll
         for (int b = 0; b < B; ++b) acc[m][b] = 0.0f;
 
-    int64_t t = t_begin, s = s_begin;
+    int64_t t = t_begin, s = s_begin;   // coordinates of unit u
+    int64_t u = 0;
 
-    // Compute (t, s) from `cur` while the loads of the following unit go into
-    // `nxt`; finish the tile after its last segment. Returns false at the end.
-    auto step = [&](Unit<QT> &cur, Unit<QT> &nxt) -> bool {
+    // Compute unit u from `cur` while the loads of unit u+1 go into `nxt`
+    // (a dummy one-line load after the last unit); finish the tile after its
+    // last segment.
+    auto step = [&](Unit<QT> &cur, Unit<QT> &nxt) {
         int64_t sn = s + 1, tn = t;
         if (sn == s_end) {
             sn = s_begin;
             tn = t + 1;
         }
-        const bool more = tn < t_end;
-        if (more) load_unit<QT>(nxt, wp, g, tn, sn, slot, j);
-        if (j < (int)seg_blocks(g, s)) compute_unit<QT, M, XLDS>(cur, acc, k, xs4, x, a.x_stride, nseg, s, j);
+        load_unit<QT>(nxt, wp, g, tn, sn, slot, j, u + 1 < n_units);
+        // keep the scheduler from sinking these loads into the compute below
+        __builtin_amdgcn_sched_barrier(0);
+        compute_unit<QT, M, XLDS>(cur, acc, k, xs4, x, a.x_stride, nseg, s, j, (int)seg_blocks(g, s));
         if (s + 1 == s_end) {
 #pragma unroll
             for (int m = 0; m < M; ++m)
@@ -344,13 +362,17 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
         }
         t = tn;
         s = sn;
-        return more;
+        ++u;
     };
 
-    for (;;) {
-        if (!step(ua, ub)) break;
-        if (!step(ub, ua)) break;
+    // A counted loop over pairs of units with no early exit, so that the only
+    // way back to the loop head is through both halves.
+    const int64_t n_pairs = n_units >> 1;
+    for (int64_t pr = 0; pr < n_pairs; ++pr) {
+        step(ua, ub);
+        step(ub, ua);
     }
+    if (n_units & 1) step(ua, ub);
 }
 
 // ---------------------------------------------------------------------------
@@ -483,7 +505,8 @@ static hipError_t dispatch_w(const uint8_t *wp, const float *x, float *y, const 
     switch (W) {
     case 1: return dispatch_x<QT, M, EPI, 1>(wp, x, y, a, grid, block, lds, xlds, s);
     case 2: return dispatch_x<QT, M, EPI, 2>(wp, x, y, a, grid, block, lds, xlds, s);
-    default: return dispatch_x<QT, M, EPI, 4>(wp, x, y, a, grid, block, lds, xlds, s);
+    case 4: return dispatch_x<QT, M, EPI, 4>(wp, x, y, a, grid, block, lds, xlds, s);
+    default: return dispatch_x<QT, M, EPI, 8>(wp, x, y, a, grid, block, lds, xlds, s);
     }
 }
 

@@ -1,0 +1,139 @@
+"""Summaries of rocprofv3 CSV output for this library's kernels.
+
+    python -m block_dequant_gemv_amd.prof trace  <dir>              # --kernel-trace --stats -f csv
+    python -m block_dequant_gemv_amd.prof traffic <fetch_dir> <write_dir> [--json out.json]
+
+`trace` groups the dispatches by kernel name and grid size (two calls of one
+kernel template with different shapes, e.g. the fused QKV and the LM head, show
+up as separate rows) and prints count, mean / median / min duration.
+
+`traffic` reads two counter runs (--pmc FETCH_SIZE, then --pmc WRITE_SIZE; the
+counters are KiB per dispatch) and prints the mean per launch shape. The bytes
+are scaled by the factor that makes a plain copy-like kernel of known traffic
+read and write exactly its size: `bench.py --calib-copy` runs torch.neg over a
+256 MiB buffer (256 MiB read, 256 MiB written per dispatch).
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import json
+import os
+import statistics as st
+import sys
+from collections import defaultdict
+
+CALIB_BYTES = 256 << 20
+
+
+def _rows(path_glob: str):
+    out = []
+    for p in sorted(glob.glob(path_glob, recursive=True)):
+        with open(p, newline="") as f:
+            out += list(csv.DictReader(f))
+    return out
+
+
+def _get(row: dict, *names, default=None):
+    low = {k.lower(): v for k, v in row.items()}
+    for n in names:
+        if n.lower() in low and low[n.lower()] not in (None, ""):
+            return low[n.lower()]
+    return default
+
+
+def _grid(row) -> int:
+    g = _get(row, "Grid_Size_X", "Grid_Size", "grid_size_x", default="0")
+    return int(float(g))
+
+
+def _wg(row) -> int:
+    g = _get(row, "Workgroup_Size_X", "Workgroup_Size", default="1")
+    return max(1, int(float(g)))
+
+
+def _short(name: str) -> str:
+    name = name.replace("void ", "")
+    cut = name.find("(")
+    return name[:cut] if cut > 0 else name
+
+
+def trace_summary(directory: str) -> str:
+    rows = _rows(os.path.join(directory, "**", "*kernel_trace.csv"))
+    groups = defaultdict(list)
+    for r in rows:
+        name = _short(_get(r, "Kernel_Name", default="?"))
+        t0 = int(_get(r, "Start_Timestamp", default="0"))
+        t1 = int(_get(r, "End_Timestamp", default="0"))
+        groups[(name, _grid(r) // _wg(r), _wg(r))].append((t1 - t0) / 1e3)
+    lines = [f"{'kernel':58s} {'workgroups':>10s} {'wg':>4s} {'n':>5s} {'mean_us':>9s} {'median_us':>9s} "
+             f"{'min_us':>8s} {'total_us':>10s}"]
+    for (name, wgs, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{name[:58]:58s} {wgs:10d} {wg:4d} {len(d):5d} {st.mean(d):9.2f} {st.median(d):9.2f} "
+                     f"{min(d):8.2f} {sum(d):10.1f}")
+    stats = _rows(os.path.join(directory, "**", "*kernel_stats.csv"))
+    if stats:
+        lines.append("")
+        lines.append("rocprofv3 kernel_stats.csv (per kernel name):")
+        keys = list(stats[0].keys())
+        lines.append(",".join(keys))
+        for r in stats:
+            lines.append(",".join(str(r[k]) for k in keys))
+    return "\n".join(lines)
+
+
+def _counter_means(directory: str, counter: str):
+    rows = _rows(os.path.join(directory, "**", "*counter_collection.csv"))
+    groups = defaultdict(list)
+    for r in rows:
+        if _get(r, "Counter_Name", default="") != counter:
+            continue
+        name = _short(_get(r, "Kernel_Name", default="?"))
+        groups[(name, _grid(r) // _wg(r), _wg(r))].append(float(_get(r, "Counter_Value", default="0")) * 1024.0)
+    return {k: st.mean(v) for k, v in groups.items()}, {k: len(v) for k, v in groups.items()}
+
+
+def traffic_summary(fetch_dir: str, write_dir: str):
+    fetch, nf = _counter_means(fetch_dir, "FETCH_SIZE")
+    write, nw = _counter_means(write_dir, "WRITE_SIZE")
+    # calibration: the torch.neg dispatches (exactly 256 MiB read and written)
+    def calib(d):
+        cands = [(k, v) for k, v in d.items() if "neg" in k[0].lower()]
+        if not cands:
+            raise SystemExit("no torch.neg calibration dispatch in the counter output "
+                             "(run bench.py with --calib-copy)")
+        return max(cands, key=lambda kv: kv[1])
+    cf, cw = calib(fetch), calib(write)
+    f_scale = CALIB_BYTES / cf[1]
+    w_scale = CALIB_BYTES / cw[1]
+    out = {"fetch_scale": f_scale, "write_scale": w_scale,
+           "fetch_calibration_kernel": cf[0][0] if cf else None,
+           "write_calibration_kernel": cw[0][0] if cw else None, "kernels": {}}
+    lines = [f"calibration (torch.neg over 256 MiB: {cf[0][0][:50]}): FETCH_SIZE x {f_scale:.4f}, "
+             f"WRITE_SIZE x {w_scale:.4f}",
+             f"{'kernel':58s} {'workgroups':>10s} {'wg':>4s} {'n':>4s} {'fetch_MB':>10s} {'write_MB':>10s}"]
+    for k in sorted(set(fetch) | set(write), key=lambda k: -fetch.get(k, 0)):
+        fb = fetch.get(k, 0.0) * f_scale
+        wb = write.get(k, 0.0) * w_scale
+        lines.append(f"{k[0][:58]:58s} {k[1]:10d} {k[2]:4d} {nf.get(k, 0):4d} {fb / 1e6:10.3f} {wb / 1e6:10.3f}")
+        out["kernels"][f"{k[0]}|{k[1]}x{k[2]}"] = {"fetch_bytes": fb, "write_bytes": wb}
+    return "\n".join(lines), out
+
+
+def main(argv):
+    if len(argv) >= 2 and argv[0] == "trace":
+        print(trace_summary(argv[1]))
+    elif len(argv) >= 3 and argv[0] == "traffic":
+        text, data = traffic_summary(argv[1], argv[2])
+        print(text)
+        if "--json" in argv:
+            with open(argv[argv.index("--json") + 1], "w") as f:
+                json.dump(data, f, indent=1)
+    else:
+        print(__doc__)
+        return 2
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))

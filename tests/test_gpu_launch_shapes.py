@@ -1,0 +1,60 @@
+"""Every kernel variant, forced through the launch-shape overrides, against the
+oracle; verify rows stay memcmp-equal to M=1 under the same split.
+
+The planner picks one shape per (type, rows, K); the overrides
+QG_SPLIT_K / QG_X_GLOBAL / QG_WAVES_PER_WG / QG_TILES_PER_GROUP reach the others.
+"""
+import itertools
+import os
+
+import numpy as np
+import pytest
+
+import block_dequant_gemv_amd as qg
+import oracle as O
+from block_dequant_gemv_amd import workloads as W
+from gpu_helpers import THREADS, announce, assert_linear, empty_f32, sync, to_dev
+
+pytestmark = pytest.mark.gpu
+
+KNOBS = ("QG_SPLIT_K", "QG_X_GLOBAL", "QG_WAVES_PER_WG", "QG_TILES_PER_GROUP")
+
+
+def _set(**kw):
+    for k in KNOBS:
+        os.environ.pop(k, None)
+    for k, v in kw.items():
+        os.environ[k] = str(v)
+
+
+@pytest.mark.parametrize("kind,N,K", [("q4_0", 203, 8192 + 96), ("q8_0", 77, 3072), ("q4_0", 1000, 1024)])
+def test_forced_launch_shapes(kind, N, K):
+    rng = np.random.default_rng(N * K)
+    canon = W.matrix(kind, N, K, rng)
+    packed = qg.pack_weights(kind, canon, N, K)
+    X = W.activation(K, rng, M=3)
+    Xd = to_dev(X)
+    Y_ref, A_ref = O.verify(kind, canon, X, N, K, threads=THREADS)
+    nseg = -(-K // 1024)
+    try:
+        for split, xg, wpw, tpg in itertools.product((1, 2, 4, 8), (0, 1), (1, 2, 4), (1, 3)):
+            if split > nseg or (split > 1 and wpw != 4):
+                continue
+            _set(QG_SPLIT_K=split, QG_X_GLOBAL=xg, QG_WAVES_PER_WG=wpw, QG_TILES_PER_GROUP=tpg)
+            ctx = f"{kind} {N}x{K} split={split} xglobal={xg} waves/wg={wpw} tiles/group={tpg}"
+            announce(ctx)
+            ys = []
+            for m in range(3):
+                y = empty_f32(N)
+                qg.qgemv(kind, packed, Xd[m].contiguous(), y, N, K)
+                ys.append(y)
+            Y = empty_f32(3 * N)
+            qg.qgemv_verify(kind, packed, Xd, Y, N, K, 3)
+            sync()
+            Yh = Y.cpu().numpy().reshape(3, N)
+            for m in range(3):
+                ym = ys[m].cpu().numpy()
+                assert_linear(ym, Y_ref[m], A_ref[m], ctx + f" row {m}")
+                assert Yh[m].tobytes() == ym.tobytes(), ctx + f" verify row {m} != M=1"
+    finally:
+        _set()
