@@ -23,8 +23,6 @@ Prints one JSON line on stdout; a readable table goes to stderr.
 from __future__ import annotations
 
 import argparse
-import glob
-import hashlib
 import json
 import os
 import sys
@@ -43,15 +41,6 @@ COLD_BYTES = 1 << 30
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "block_dequant_gemv_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 # ---------------------------------------------------------------------------
@@ -292,10 +281,11 @@ def load_traffic(kernel: str):
         return None
     with open(path) as f:
         t = json.load(f)
+    from block_dequant_gemv_amd.prof import kernel_source_hash
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
-    entry = t.get("kernels", {}).get(kernel)
-    return entry.get("bytes_per_launch") if entry else None
+    entry = t.get("calls", {}).get(kernel)
+    return round(entry["bytes_per_launch"]) if entry else None
 
 
 def main():

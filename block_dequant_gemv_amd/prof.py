@@ -2,6 +2,7 @@
 
     python -m block_dequant_gemv_amd.prof trace  <dir>              # --kernel-trace --stats -f csv
     python -m block_dequant_gemv_amd.prof traffic <fetch_dir> <write_dir> [--json out.json]
+                                              [--call LABEL=KERNEL|WORKGROUPSxWG ...]
 
 `trace` groups the dispatches by kernel name and grid size (two calls of one
 kernel template with different shapes, e.g. the fused QKV and the LM head, show
@@ -17,6 +18,7 @@ from __future__ import annotations
 
 import csv
 import glob
+import hashlib
 import json
 import os
 import statistics as st
@@ -24,6 +26,17 @@ import sys
 from collections import defaultdict
 
 CALIB_BYTES = 256 << 20
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the kernel sources; counter results are only valid for the sources they were taken on."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _rows(path_glob: str):
@@ -126,6 +139,14 @@ def main(argv):
     elif len(argv) >= 3 and argv[0] == "traffic":
         text, data = traffic_summary(argv[1], argv[2])
         print(text)
+        data["kernel_source_hash"] = kernel_source_hash()
+        data["calls"] = {}
+        for i, a in enumerate(argv):
+            if a == "--call":
+                label, key = argv[i + 1].split("=", 1)
+                k = data["kernels"][key]
+                data["calls"][label] = {"kernel": key, "fetch_bytes": k["fetch_bytes"], "write_bytes": k["write_bytes"],
+                                        "bytes_per_launch": k["fetch_bytes"] + k["write_bytes"]}
         if "--json" in argv:
             with open(argv[argv.index("--json") + 1], "w") as f:
                 json.dump(data, f, indent=1)
