@@ -89,7 +89,8 @@ int split_k_waves(int64_t rows, int64_t K)
     return W;
 }
 
-constexpr size_t kLdsLimit = 96 * 1024;   // above this, activations are read from global memory
+constexpr size_t kLdsLimit = 96 * 1024;        // single-row calls: above this, x is read from global memory
+constexpr size_t kLdsLimitMulti = 160 * 1024;  // verify calls: the whole LDS of a CU (gfx950)
 
 // Launch shape (measured on MI355X with cold weights):
 //  - tiles per group: 1, or 2 for very tall matrices (>= 24K row tiles);
@@ -100,7 +101,8 @@ constexpr size_t kLdsLimit = 96 * 1024;   // above this, activations are read fr
 //    (L2); with several activation rows (verify) each staged value is reused
 //    M times per weight, so LDS is used whenever it fits.
 // Tuning overrides (read on every call): QG_TILES_PER_GROUP, QG_WAVES_PER_WG
-// (split 1 only), QG_X_GLOBAL (0/1). None of them changes a row's operations.
+// (split 1 only), QG_X_GLOBAL (0/1), QG_PREFETCH (1/2). None of them changes a
+// row's operations.
 qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M)
 {
     qgk::QPlan p;
@@ -110,24 +112,34 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M)
     const int64_t tpg_env = env_int("QG_TILES_PER_GROUP", 0);
     if (tpg_env > 0) p.tpg = tpg_env;
     const int64_t groups = (g.n_tiles + p.tpg - 1) / p.tpg;
+    const size_t xbytes = (size_t)M * (size_t)g.nseg * qgl::kSegWeights * sizeof(float);
+    const size_t lds_limit = M > 1 ? kLdsLimitMulti : kLdsLimit;
     int G;   // groups per workgroup
     if (p.W > 1) {
         G = 1;
         p.block = 64 * p.W;
     } else {
         G = groups >= 512 ? 4 : (groups >= 256 ? 2 : 1);
+        // a verify call whose activations take more than half the LDS runs one
+        // workgroup per CU: give it 8 wavefronts
+        if (M > 1 && xbytes > 80 * 1024 && xbytes <= lds_limit && groups >= 2048) G = 8;
         const int64_t g_env = env_int("QG_WAVES_PER_WG", 0);
-        if (g_env == 1 || g_env == 2 || g_env == 4) G = (int)g_env;
+        if (g_env == 1 || g_env == 2 || g_env == 4 || g_env == 8) G = (int)g_env;
         p.block = 64 * G;
     }
     p.grid = (groups + G - 1) / G;
-    const size_t xbytes = (size_t)M * (size_t)g.nseg * qgl::kSegWeights * sizeof(float);
     const double wg_weight_bytes = (double)G * (double)p.tpg * (double)(g.tile_q + g.tile_s);
-    bool lds = xbytes <= kLdsLimit && (M > 1 || wg_weight_bytes >= 4.0 * (double)xbytes);
+    bool lds = xbytes <= lds_limit && (M > 1 || wg_weight_bytes >= 4.0 * (double)xbytes);
     const int64_t xg_env = env_int("QG_X_GLOBAL", -1);
-    if (xg_env == 0 || xg_env == 1) lds = xbytes <= kLdsLimit && xg_env == 0;
+    if (xg_env == 0 || xg_env == 1) lds = xbytes <= lds_limit && xg_env == 0;
     p.x_in_lds = lds;
     p.lds_bytes = p.x_in_lds ? xbytes : 0;
+    // Prefetch depth: one unit in flight ahead of the one being computed. A
+    // depth of 2 (single-row kernels only) measured no faster on any of the
+    // workload shapes and costs registers; it stays reachable for sweeps.
+    p.depth = 1;
+    const int64_t d_env = env_int("QG_PREFETCH", 0);
+    if (d_env == 1 || d_env == 2) p.depth = (int)d_env;
     return p;
 }
 
@@ -317,9 +329,15 @@ qg_status gemv_f16_splitk(const void *w_f16, const float *x, float *y, int64_t N
     const int64_t units = p.vec ? K / 8 : K;       // work items along K
     // rows per workgroup: register-block 4 rows when there are plenty of rows
     p.R = N >= 2048 ? 4 : (N >= 512 ? 2 : 1);
-    // wavefronts per workgroup: enough lanes for ~1-2 units each, at most 16
-    int64_t waves = (units + 63) / 64;
+    const int64_t r_env = env_int("QG_F16_ROWS", 0);
+    if (r_env == 1 || r_env == 2 || r_env == 4) p.R = (int)r_env;
+    // wavefronts per workgroup: one row per workgroup walks ~5 chunks per lane
+    // (measured best for the thin 256 x 5120 and 48 x 5120 matrices); register-
+    // blocked rows use ~1-2 chunks per lane. At most 16 wavefronts.
+    int64_t waves = p.R == 1 ? (units + 319) / 320 : (units + 63) / 64;
     if (p.R >= 2) waves = (waves + 1) / 2;
+    const int64_t w_env = env_int("QG_F16_WAVES", 0);
+    if (w_env > 0) waves = w_env;
     if (waves > 16) waves = 16;
     if (waves < 1) waves = 1;
     p.waves = (int)waves;

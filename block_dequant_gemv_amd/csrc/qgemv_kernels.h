@@ -30,6 +30,7 @@ struct QPlan {
     int64_t tpg;         // tiles per group
     int64_t grid;        // workgroups
     int block;           // threads per workgroup (64 * wavefronts)
+    int depth;           // units in flight ahead of the one being computed (1 or 2; 2 only for M = 1)
     bool x_in_lds;       // activations staged in LDS
     size_t lds_bytes;    // dynamic LDS per workgroup
 };

@@ -225,16 +225,17 @@ __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][
 // W  > 1: a workgroup is W wavefronts sharing the tiles [b * tpg, b * tpg + tpg);
 //         wavefront w adds segments [nseg*w/W, nseg*(w+1)/W) of every tile and
 //         the W partial sums are combined in LDS in wavefront order.
-// Each wavefront walks its (tile, segment) sequence with the next unit's loads
-// in flight while the current one is computed.
+// Each wavefront walks its (tile, segment) sequence with the loads of the next
+// D units in flight while the current one is computed (a ring of D+1 units).
 #ifndef QG_WAVES_PER_EU
 #define QG_WAVES_PER_EU 1
 #endif
-template <int QT, int M, int EPI, int W, bool XLDS>
+template <int QT, int M, int EPI, int W, bool XLDS, int D>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QG_WAVES_PER_EU)))
 qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float *__restrict__ y, QArgs a)
 {
     constexpr int B = kRowsPerLane;
+    constexpr int S = D + 1;   // ring size
     extern __shared__ f32x4 xs4[];
     __shared__ float red[(W > 1) ? W * M * kSlots * B : 1];  // [W][M][slot][b]
 
@@ -254,25 +255,52 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
     const Consts k = make_consts();
     // This wavefront's units, in order: (t, s) for t in [t_begin, t_end), s in [s_begin, s_end).
     const int64_t n_units = (t_end > t_begin ? t_end - t_begin : 0) * (s_end - s_begin);
-    Unit<QT> ua, ub;
-    load_unit<QT>(ua, wp, g, t_begin, s_begin, slot, j, n_units > 0);
+
+    // Load cursor: the unit whose loads are issued next (D units ahead of the compute cursor).
+    int64_t t_ld = t_begin, s_ld = s_begin, u_ld = 0;
+    auto advance = [&](int64_t &tt, int64_t &ss) {
+        if (++ss == s_end) {
+            ss = s_begin;
+            ++tt;
+        }
+    };
+    Unit<QT> ring[S];
+#pragma unroll
+    for (int r = 0; r < D; ++r) {
+        load_unit<QT>(ring[r], wp, g, t_ld, s_ld, slot, j, u_ld < n_units);
+        advance(t_ld, s_ld);
+        ++u_ld;
+    }
 
     if (XLDS) {
-        // stage X[m][k] (k < nseg*1024, zero beyond K) as xs4[((m*nseg + seg)*8 + c)*32 + jj]
-        const int64_t nchunk = (int64_t)M * nseg * (kSegWeights / 4);
-        for (int64_t i = tid; i < nchunk; i += blockDim.x) {
-            const int64_t m = i / (nseg * (kSegWeights / 4));
-            const int64_t kk = (i - m * nseg * (kSegWeights / 4)) * 4;
-            const int64_t seg = kk / kSegWeights;
-            const int within = (int)(kk - seg * kSegWeights);
-            const int jj = within >> 5, c = (within & 31) >> 2;
-            f32x4 v;
-            const float *src = x + m * a.x_stride + kk;
-            v.x = (kk + 0 < K) ? src[0] : 0.0f;
-            v.y = (kk + 1 < K) ? src[1] : 0.0f;
-            v.z = (kk + 2 < K) ? src[2] : 0.0f;
-            v.w = (kk + 3 < K) ? src[3] : 0.0f;
-            xs4[((m * nseg + seg) * 8 + c) * 32 + jj] = v;
+        // stage X[m][k] (k < nseg*1024, zero beyond K) as xs4[((m*nseg + seg)*8 + c)*32 + jj];
+        // K % 32 == 0, so a 16-byte chunk is either wholly inside K or wholly past it.
+        // Loads are issued in batches of 4 per thread before any LDS write.
+        const int64_t per_m = nseg * (kSegWeights / 4);
+        const int64_t nchunk = (int64_t)M * per_m;
+        const int nthr = blockDim.x;
+        for (int64_t base = tid; base < nchunk; base += 4 * (int64_t)nthr) {
+            f32x4 v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t i = base + (int64_t)q * nthr;
+                const int64_t m = i / per_m;
+                const int64_t kk = (i - m * per_m) * 4;
+                const bool inside = i < nchunk && kk < K;
+                v[q] = inside ? *(const f32x4 *)(x + m * a.x_stride + kk) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t i = base + (int64_t)q * nthr;
+                if (i < nchunk) {
+                    const int64_t m = i / per_m;
+                    const int64_t kk = (i - m * per_m) * 4;
+                    const int64_t seg = kk / kSegWeights;
+                    const int within = (int)(kk - seg * kSegWeights);
+                    const int jj = within >> 5, c = (within & 31) >> 2;
+                    xs4[((m * nseg + seg) * 8 + c) * 32 + jj] = v[q];
+                }
+            }
         }
         __syncthreads();
     }
@@ -284,19 +312,16 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
 #pragma unroll
         for (int b = 0; b < B; ++b) acc[m][b] = 0.0f;
 
-    int64_t t = t_begin, s = s_begin;   // coordinates of unit u
+    int64_t t = t_begin, s = s_begin;   // compute cursor: coordinates of unit u
     int64_t u = 0;
 
-    // Compute unit u from `cur` while the loads of unit u+1 go into `nxt`
-    // (a dummy one-line load after the last unit); finish the tile after its
+    // Issue the loads of unit u+D into `nxt` (a dummy one-line load past the
+    // last unit), then compute unit u from `cur` and finish the tile after its
     // last segment.
     auto step = [&](Unit<QT> &cur, Unit<QT> &nxt) {
-        int64_t sn = s + 1, tn = t;
-        if (sn == s_end) {
-            sn = s_begin;
-            tn = t + 1;
-        }
-        load_unit<QT>(nxt, wp, g, tn, sn, slot, j, u + 1 < n_units);
+        load_unit<QT>(nxt, wp, g, t_ld, s_ld, slot, j, u_ld < n_units);
+        advance(t_ld, s_ld);
+        ++u_ld;
         // keep the scheduler from sinking these loads into the compute below
         __builtin_amdgcn_sched_barrier(0);
         compute_unit<QT, M, XLDS>(cur, acc, k, xs4, x, a.x_stride, nseg, s, j, (int)seg_blocks(g, s));
@@ -360,19 +385,21 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
 #pragma unroll
                 for (int b = 0; b < B; ++b) acc[m][b] = 0.0f;
         }
-        t = tn;
-        s = sn;
+        advance(t, s);
         ++u;
     };
 
-    // A counted loop over pairs of units with no early exit, so that the only
-    // way back to the loop head is through both halves.
-    const int64_t n_pairs = n_units >> 1;
-    for (int64_t pr = 0; pr < n_pairs; ++pr) {
-        step(ua, ub);
-        step(ub, ua);
+    // A counted loop over groups of S units with no early exit, so that the only
+    // way back to the loop head is through every step; unit u lives in ring[u % S].
+    const int64_t n_groups = n_units / S;
+    for (int64_t gi = 0; gi < n_groups; ++gi) {
+#pragma unroll
+        for (int r = 0; r < S; ++r) step(ring[r], ring[(r + D) % S]);
     }
-    if (n_units & 1) step(ua, ub);
+    const int64_t rem = n_units - n_groups * S;
+#pragma unroll
+    for (int r = 0; r < S - 1; ++r)
+        if (r < rem) step(ring[r], ring[(r + D) % S]);
 }
 
 // ---------------------------------------------------------------------------
@@ -477,11 +504,11 @@ __global__ void zero_gaps_kernel(uint8_t *__restrict__ packed, int64_t a0, int64
 // ---------------------------------------------------------------------------
 // launch helpers (host side)
 
-template <int QT, int M, int EPI, int W, bool XLDS>
+template <int QT, int M, int EPI, int W, bool XLDS, int D>
 static hipError_t launch_q(const uint8_t *wp, const float *x, float *y, const QArgs &a, int64_t grid, int block,
                            size_t lds, hipStream_t stream)
 {
-    auto kern = qgemv_kernel<QT, M, EPI, W, XLDS>;
+    auto kern = qgemv_kernel<QT, M, EPI, W, XLDS, D>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -492,36 +519,40 @@ static hipError_t launch_q(const uint8_t *wp, const float *x, float *y, const QA
 
 template <int QT, int M, int EPI, int W>
 static hipError_t dispatch_x(const uint8_t *wp, const float *x, float *y, const QArgs &a, int64_t grid, int block,
-                             size_t lds, bool xlds, hipStream_t s)
+                             size_t lds, bool xlds, int depth, hipStream_t s)
 {
-    return xlds ? launch_q<QT, M, EPI, W, true>(wp, x, y, a, grid, block, lds, s)
-                : launch_q<QT, M, EPI, W, false>(wp, x, y, a, grid, block, 0, s);
+    // prefetch depth 2 is instantiated for the single-row kernels only
+    if (M == 1 && depth >= 2)
+        return xlds ? launch_q<QT, M, EPI, W, true, 2>(wp, x, y, a, grid, block, lds, s)
+                    : launch_q<QT, M, EPI, W, false, 2>(wp, x, y, a, grid, block, 0, s);
+    return xlds ? launch_q<QT, M, EPI, W, true, 1>(wp, x, y, a, grid, block, lds, s)
+                : launch_q<QT, M, EPI, W, false, 1>(wp, x, y, a, grid, block, 0, s);
 }
 
 template <int QT, int M, int EPI>
 static hipError_t dispatch_w(const uint8_t *wp, const float *x, float *y, const QArgs &a, int W, int64_t grid,
-                             int block, size_t lds, bool xlds, hipStream_t s)
+                             int block, size_t lds, bool xlds, int depth, hipStream_t s)
 {
     switch (W) {
-    case 1: return dispatch_x<QT, M, EPI, 1>(wp, x, y, a, grid, block, lds, xlds, s);
-    case 2: return dispatch_x<QT, M, EPI, 2>(wp, x, y, a, grid, block, lds, xlds, s);
-    case 4: return dispatch_x<QT, M, EPI, 4>(wp, x, y, a, grid, block, lds, xlds, s);
-    default: return dispatch_x<QT, M, EPI, 8>(wp, x, y, a, grid, block, lds, xlds, s);
+    case 1: return dispatch_x<QT, M, EPI, 1>(wp, x, y, a, grid, block, lds, xlds, depth, s);
+    case 2: return dispatch_x<QT, M, EPI, 2>(wp, x, y, a, grid, block, lds, xlds, depth, s);
+    case 4: return dispatch_x<QT, M, EPI, 4>(wp, x, y, a, grid, block, lds, xlds, depth, s);
+    default: return dispatch_x<QT, M, EPI, 8>(wp, x, y, a, grid, block, lds, xlds, depth, s);
     }
 }
 
 template <int QT>
 static hipError_t dispatch_m(const uint8_t *wp, const float *x, float *y, const QArgs &a, int M, int epi, int W,
-                             int64_t grid, int block, size_t lds, bool xlds, hipStream_t s)
+                             int64_t grid, int block, size_t lds, bool xlds, int depth, hipStream_t s)
 {
-    if (epi == kEpiGateUp) return dispatch_w<QT, 1, kEpiGateUp>(wp, x, y, a, W, grid, block, lds, xlds, s);
+    if (epi == kEpiGateUp) return dispatch_w<QT, 1, kEpiGateUp>(wp, x, y, a, W, grid, block, lds, xlds, depth, s);
     switch (M) {
-    case 1: return dispatch_w<QT, 1, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, s);
-    case 2: return dispatch_w<QT, 2, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, s);
-    case 3: return dispatch_w<QT, 3, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, s);
-    case 4: return dispatch_w<QT, 4, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, s);
-    case 5: return dispatch_w<QT, 5, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, s);
-    default: return dispatch_w<QT, 6, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, s);
+    case 1: return dispatch_w<QT, 1, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, depth, s);
+    case 2: return dispatch_w<QT, 2, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, depth, s);
+    case 3: return dispatch_w<QT, 3, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, depth, s);
+    case 4: return dispatch_w<QT, 4, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, depth, s);
+    case 5: return dispatch_w<QT, 5, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, depth, s);
+    default: return dispatch_w<QT, 6, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, depth, s);
     }
 }
 
@@ -529,8 +560,8 @@ hipError_t launch_qgemv(int qt, int M, int epi, const QPlan &p, const uint8_t *w
                         const QArgs &a, hipStream_t s)
 {
     if (qt == kQ8_0)
-        return dispatch_m<kQ8_0>(wp, x, y, a, M, epi, p.W, p.grid, p.block, p.lds_bytes, p.x_in_lds, s);
-    return dispatch_m<kQ4_0>(wp, x, y, a, M, epi, p.W, p.grid, p.block, p.lds_bytes, p.x_in_lds, s);
+        return dispatch_m<kQ8_0>(wp, x, y, a, M, epi, p.W, p.grid, p.block, p.lds_bytes, p.x_in_lds, p.depth, s);
+    return dispatch_m<kQ4_0>(wp, x, y, a, M, epi, p.W, p.grid, p.block, p.lds_bytes, p.x_in_lds, p.depth, s);
 }
 
 hipError_t launch_f16(const F16Plan &p, const uint16_t *w, const float *x, float *y, int64_t N, int64_t K,

@@ -2,7 +2,9 @@
 oracle; verify rows stay memcmp-equal to M=1 under the same split.
 
 The planner picks one shape per (type, rows, K); the overrides
-QG_SPLIT_K / QG_X_GLOBAL / QG_WAVES_PER_WG / QG_TILES_PER_GROUP reach the others.
+QG_SPLIT_K / QG_X_GLOBAL / QG_WAVES_PER_WG / QG_TILES_PER_GROUP / QG_PREFETCH
+reach the others (prefetch depth 2 exists for the single-row kernels; the
+verify kernels keep depth 1, and their rows must still match).
 """
 import itertools
 import os
@@ -17,7 +19,7 @@ from gpu_helpers import THREADS, announce, assert_linear, empty_f32, sync, to_de
 
 pytestmark = pytest.mark.gpu
 
-KNOBS = ("QG_SPLIT_K", "QG_X_GLOBAL", "QG_WAVES_PER_WG", "QG_TILES_PER_GROUP")
+KNOBS = ("QG_SPLIT_K", "QG_X_GLOBAL", "QG_WAVES_PER_WG", "QG_TILES_PER_GROUP", "QG_PREFETCH")
 
 
 def _set(**kw):
@@ -37,11 +39,11 @@ def test_forced_launch_shapes(kind, N, K):
     Y_ref, A_ref = O.verify(kind, canon, X, N, K, threads=THREADS)
     nseg = -(-K // 1024)
     try:
-        for split, xg, wpw, tpg in itertools.product((1, 2, 4, 8), (0, 1), (1, 2, 4), (1, 3)):
+        for split, xg, wpw, tpg, pf in itertools.product((1, 2, 4, 8), (0, 1), (1, 2, 4), (1, 3), (1, 2)):
             if split > nseg or (split > 1 and wpw != 4):
                 continue
-            _set(QG_SPLIT_K=split, QG_X_GLOBAL=xg, QG_WAVES_PER_WG=wpw, QG_TILES_PER_GROUP=tpg)
-            ctx = f"{kind} {N}x{K} split={split} xglobal={xg} waves/wg={wpw} tiles/group={tpg}"
+            _set(QG_SPLIT_K=split, QG_X_GLOBAL=xg, QG_WAVES_PER_WG=wpw, QG_TILES_PER_GROUP=tpg, QG_PREFETCH=pf)
+            ctx = f"{kind} {N}x{K} split={split} xglobal={xg} waves/wg={wpw} tiles/group={tpg} prefetch={pf}"
             announce(ctx)
             ys = []
             for m in range(3):
