@@ -14,8 +14,8 @@ Also measured in the same run:
   * every matrix of the five workload configurations, one call at a time, cold
     (each call's weight rotating through >= 1.2 GiB of device copies) and warm,
     as median us per call, GB/s and fraction of the 8 TB/s HBM3E peak;
-  * the roofline entry of the step's dominant kernel (HIP events on the stream
-    the kernels run on);
+  * the roofline entry of the step's dominant kernel: HIP events bound to each of
+    its launches in the timed steps receive the kernel's start and end times;
   * the fp64 CPU oracle on the host cores (one thread and all threads) over one
     step of the same workload (the cpu_baseline leg; the only use of oracle/).
 Prints one JSON line on stdout; a readable table goes to stderr.
@@ -123,14 +123,25 @@ def build_step(qg, torch, wl, stream, copies):
     return steps, sets, xs, ys
 
 
-def time_call(torch, fns, reps):
-    """Per-call event intervals (us) of `reps` calls cycling through `fns`, and the
-    mean us per call of a back-to-back batch bracketed by one event pair."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for i, (e0, e1) in enumerate(evs):
-        e0.record()
+def timing_events(torch, n):
+    """n timing events on the current stream, recorded once so that they exist
+    (torch creates the underlying hipEvent_t lazily) and can be bound to launches."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record()
+    return evs
+
+
+def time_call(qg, torch, fns, reps):
+    """Kernel durations (us) of `reps` calls cycling through `fns`, each launch
+    bound to an event pair that receives the kernel's start and end timestamps,
+    and the mean us per call of a back-to-back batch bracketed by one event pair
+    (kernel time plus the gap between dependent launches)."""
+    evs = timing_events(torch, 2 * reps)
+    torch.cuda.synchronize()
+    for i in range(reps):
+        qg.qg_time_next_launch(evs[2 * i], evs[2 * i + 1])
         fns[i % len(fns)]()
-        e1.record()
     nb = max(reps, len(fns))
     b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     b0.record()
@@ -138,7 +149,7 @@ def time_call(torch, fns, reps):
         fns[i % len(fns)]()
     b1.record()
     torch.cuda.synchronize()
-    us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+    us = np.array([evs[2 * i].elapsed_time(evs[2 * i + 1]) * 1e3 for i in range(reps)])
     return us, b0.elapsed_time(b1) * 1e3 / nb
 
 
@@ -352,36 +363,35 @@ def main():
         del src, dst
 
     # ---- headline: K timed steps ------------------------------------------------
-    # Two HIP events per step on the stream the kernels run on: one at the start
-    # of the step and one between the down projection and the LM head (the step's
-    # dominant call, last in the step), so the markers add as little as possible
-    # between the dependent launches. The LM head's duration is the time from its
-    # marker to the next step's start marker.
+    # One event pair brackets the K steps on the stream the kernels run on. Inside
+    # the region the only timing is on the LM head (the step's dominant call,
+    # last in the step): its launch is bound to an event pair that receives the
+    # kernel's own start and end timestamps (qg_time_next_launch), the same
+    # dispatch times a rocprofv3 kernel trace reports, with no marker queued
+    # between the dependent launches.
     for s in range(args.warmup):
         for c in steps[s % copies]:
             c.fn()
-    torch.cuda.synchronize()
     K = args.steps
     lm = len(steps[0]) - 1
-    ev_step = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-    ev_lm = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    span = timing_events(torch, 2)
+    ev_lm = timing_events(torch, 2 * K)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    span[0].record()
     for s in range(K):
-        ev_step[s].record()
         calls = steps[s % copies]
         for i in range(lm):
             calls[i].fn()
-        ev_lm[s].record()
+        qg.qg_time_next_launch(ev_lm[2 * s], ev_lm[2 * s + 1])
         calls[lm].fn()
-    ev_step[K].record()
+    span[1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / K * 1e3
     value = step_bytes * K / wall / 1e9
-    gpu_span_ms = ev_step[0].elapsed_time(ev_step[K])
-    lm_us = np.array([ev_lm[s].elapsed_time(ev_step[s + 1]) * 1e3 for s in range(K)])
-    head_us = np.array([ev_step[s].elapsed_time(ev_lm[s]) * 1e3 for s in range(K)])
+    gpu_span_ms = span[0].elapsed_time(span[1])
+    lm_us = np.array([ev_lm[2 * s].elapsed_time(ev_lm[2 * s + 1]) * 1e3 for s in range(K)])
     dom = steps[0][lm]
     avg_us = float(lm_us.mean())
     achieved = dom.nbytes / (avg_us * 1e-6) / 1e9
@@ -392,27 +402,33 @@ def main():
         "kernel": dom.kernel, "call": dom.label,
         "avg_launch_us": round(avg_us, 3), "launches": K,
         "algorithmic_bytes_per_launch": dom.nbytes,
+        "timing": "kernel start/end timestamps of each LM head launch in the timed steps (HIP events bound "
+                  "to the dispatch)",
     }
     log(f"headline: {K} steps, {ms_per_step:.4f} ms/step wall, GPU span {gpu_span_ms / K:.4f} ms/step, "
         f"{value:.1f} GB/s ({100 * value / PEAK_GBPS:.1f}% of 8 TB/s), {copies} weight copies")
-    log(f"  qkv + o_proj + gate|up + down: {float(np.median(head_us)):.2f} us per step (median)")
-    log(f"  {dom.label}: {float(np.median(lm_us)):.2f} us median, {avg_us:.2f} us mean -> "
+    log(f"  {dom.label}: kernel {float(np.median(lm_us)):.2f} us median, {avg_us:.2f} us mean -> "
         f"{achieved:.1f} GB/s ({100 * achieved / PEAK_GBPS:.1f}%)  [{dom.kernel}]")
 
-    # per-call breakdown of the same step, in a separate pass with an event pair
-    # around every call (reported, not used for `value`)
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in steps[0]]
-           for _ in range(K)]
+    # per-kernel breakdown of the same step, in a separate pass in which every
+    # launch is bound to an event pair (reported, not used for `value`)
+    ncall = len(steps[0])
+    evk = timing_events(torch, 2 * K * ncall)
+    torch.cuda.synchronize()
     for s in range(K):
         for i, c in enumerate(steps[s % copies]):
-            evs[s][i][0].record()
+            e = 2 * (s * ncall + i)
+            qg.qg_time_next_launch(evk[e], evk[e + 1])
             c.fn()
-            evs[s][i][1].record()
     torch.cuda.synchronize()
-    durs = np.array([[e0.elapsed_time(e1) * 1e3 for e0, e1 in row] for row in evs])  # us [K][ncalls]
+    durs = np.array([[evk[2 * (s * ncall + i)].elapsed_time(evk[2 * (s * ncall + i) + 1]) * 1e3
+                      for i in range(ncall)] for s in range(K)])  # us [K][ncall]
     for i, c in enumerate(steps[0]):
         med = float(np.median(durs[:, i]))
-        log(f"  per-call pass: {c.label:28s} {med:8.2f} us  {c.nbytes / med / 1e3:8.1f} GB/s  [{c.kernel}]")
+        log(f"  kernel: {c.label:28s} {med:8.2f} us  {c.nbytes / med / 1e3:8.1f} GB/s  [{c.kernel}]")
+    kern_sum = float(np.median(durs.sum(axis=1)))
+    log(f"  sum of the step's kernel times {kern_sum:.2f} us; GPU span per step {1e3 * gpu_span_ms / K:.2f} us "
+        f"(the rest is launch gaps)")
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
@@ -425,15 +441,15 @@ def main():
                                              f"({copies * step_bytes / 1e9:.2f} GB)",
             "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
             "gpu_ms_per_step": round(gpu_span_ms / K, 5),
-            "lm_head_us_median": round(float(np.median(lm_us)), 3),
-            "other_calls_us_median": round(float(np.median(head_us)), 3),
+            "lm_head_kernel_us_median": round(float(np.median(lm_us)), 3),
+            "kernel_us_per_step": round(kern_sum, 3),
             "device": props.name,
         },
         "roofline": roofline,
     }
 
-    detail = {"per_call_pass_us": {c.label: float(np.median(durs[:, i])) for i, c in enumerate(steps[0])},
-              "lm_head_us": lm_us.tolist(), "other_calls_us": head_us.tolist()}
+    detail = {"kernel_us": {c.label: float(np.median(durs[:, i])) for i, c in enumerate(steps[0])},
+              "lm_head_us": lm_us.tolist()}
 
     # ---- reference streams: what plain torch kernels reach on this device ----------------
     ref = hbm_reference(torch)
@@ -444,9 +460,9 @@ def main():
     # ---- per-config cold / warm table ---------------------------------------------
     # Cold: each call's weight rotates through >= 1.2 GiB of device copies (no
     # flush kernel: a read+write flush leaves dirty Infinity Cache lines whose
-    # write-back would slow the timed call). Per-call event intervals give the
-    # median and p10/p90 (they include ~2 us of marker and dispatch latency);
-    # `batch_us` is the mean of back-to-back calls through the same copies.
+    # write-back would slow the timed call). Kernel durations (events bound to
+    # each launch) give the median and p10/p90; `batch_us` is the mean of
+    # back-to-back calls through the same copies, launch gaps included.
     # Warm: the same copy again and again (served in part by the caches).
     if not args.no_configs:
         cfg_calls, keep = per_config_calls(qg, torch, stream, steps[0])
@@ -459,8 +475,9 @@ def main():
                 torch.cuda.synchronize()
                 for f in fns[:3]:
                     f()
-                u, batch = time_call(torch, fns, args.reps)
-                uw, _ = time_call(torch, [c.fn], max(10, args.reps // 2))
+                u, batch = time_call(qg, torch, fns, args.reps)
+                uw, _ = time_call(qg, torch, [c.fn], max(10, args.reps // 2))
+                ncopies = len(fns)
                 del fns, copies
                 med = float(np.median(u))
                 gbps = c.nbytes / med / 1e3
@@ -468,7 +485,8 @@ def main():
                                   "us_p90": round(float(np.percentile(u, 90)), 3), "GBps": round(gbps, 1),
                                   "pct": round(100 * gbps / PEAK_GBPS, 1), "batch_us": round(batch, 3),
                                   "batch_GBps": round(c.nbytes / batch / 1e3, 1), "bytes": c.nbytes,
-                                  "warm_us": round(float(np.median(uw)), 3), "kernel": c.kernel}
+                                  "warm_us": round(float(np.median(uw)), 3), "kernel": c.kernel,
+                                  "copies": ncopies, "us_each": [round(float(v), 2) for v in u]}
                 log(f"  {c.label:34s} cold {med:9.2f} us ({float(np.percentile(u, 10)):.2f}-"
                     f"{float(np.percentile(u, 90)):.2f})  {gbps:8.1f} GB/s {100 * gbps / PEAK_GBPS:5.1f}%   "
                     f"batch {batch:9.2f} us {c.nbytes / batch / 1e3:8.1f} GB/s   warm {float(np.median(uw)):8.2f} us")

@@ -28,7 +28,7 @@ SYMBOLS = (
     "qg_packed_size", "qg_pack", "qg_pack_rows", "qg_pack_gateup",
     "qg_pack_host", "qg_unpack_host", "qg_pack_gateup_host",
     "qgemv_q8_0", "qgemv_q4_0", "gemv_f16_splitk", "qgemv_fused_gateup_silu", "qgemv_verify",
-    "qg_status_str", "qg_last_error", "qg_plan_info",
+    "qg_status_str", "qg_last_error", "qg_plan_info", "qg_time_next_launch",
 )
 
 
@@ -74,6 +74,7 @@ def lib():
             "qg_last_error": ([], ctypes.c_char_p),
             "qg_plan_info": ([i32, i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i64),
                               ctypes.POINTER(i32)], i32),
+            "qg_time_next_launch": ([vp, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -219,6 +220,19 @@ def qg_plan_info(qtype, N: int, K: int, M: int = 1) -> dict:
     _check("qg_plan_info", lib().qg_plan_info(_qtype(qtype), N, K, M, ctypes.byref(w), ctypes.byref(g),
                                               ctypes.byref(xl)))
     return {"split_k_waves": w.value, "workgroups": g.value, "x_in_lds": bool(xl.value)}
+
+
+def qg_time_next_launch(start_event, stop_event):
+    """Bind two timing events (torch.cuda.Event that have been recorded once, so
+    that they exist, or raw hipEvent_t ints) to the next GEMV kernel this thread
+    launches; None, None clears."""
+    def handle(e):
+        if e is None or isinstance(e, int):
+            return e
+        if not e.cuda_event:
+            raise ValueError("record the event once before binding it (torch creates it lazily)")
+        return e.cuda_event
+    _check("qg_time_next_launch", lib().qg_time_next_launch(handle(start_event), handle(stop_event)))
 
 
 # ---- load-time helpers (torch allocates; the library packs) ------------------

@@ -29,6 +29,7 @@ qg_status fail(qg_status s, const char *fmt, ...)
     vsnprintf(buf, sizeof buf, fmt, ap);
     va_end(ap);
     g_last_error = buf;
+    qgk::set_launch_events(nullptr, nullptr);
     return s;
 }
 
@@ -108,7 +109,10 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M)
     qgk::QPlan p;
     const Geometry g = qgl::geometry(qt, rows, K);
     p.W = split_k_waves(rows, K);
-    p.tpg = g.n_tiles >= 24000 ? 2 : 1;
+    // One row tile per group: many short, independent wavefronts, which the
+    // hardware dispatcher balances across the CUs better than longer chains
+    // (measured on both LM-head shapes).
+    p.tpg = 1;
     const int64_t tpg_env = env_int("QG_TILES_PER_GROUP", 0);
     if (tpg_env > 0) p.tpg = tpg_env;
     const int64_t groups = (g.n_tiles + p.tpg - 1) / p.tpg;
@@ -371,6 +375,14 @@ qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int *split_k_wave
     if (split_k_waves_out) *split_k_waves_out = p.W;
     if (workgroups) *workgroups = p.grid;
     if (x_in_lds) *x_in_lds = p.x_in_lds ? 1 : 0;
+    return ok();
+}
+
+qg_status qg_time_next_launch(void *start_event, void *stop_event)
+{
+    if ((start_event == nullptr) != (stop_event == nullptr))
+        return fail(QG_EINVAL, "qg_time_next_launch: give both events or neither");
+    qgk::set_launch_events((hipEvent_t)start_event, (hipEvent_t)stop_event);
     return ok();
 }
 

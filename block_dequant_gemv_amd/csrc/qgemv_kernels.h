@@ -42,6 +42,11 @@ struct F16Plan {
     int64_t grid;
 };
 
+// Two timing events bound to the next GEMV kernel this thread launches: they
+// receive that kernel's own start and end timestamps. The launch takes them
+// and clears the setting; (nullptr, nullptr) clears it too.
+void set_launch_events(hipEvent_t start, hipEvent_t stop);
+
 hipError_t launch_qgemv(int qt, int M, int epi, const QPlan &p, const uint8_t *wp, const float *x, float *y,
                         const QArgs &a, hipStream_t s);
 hipError_t launch_f16(const F16Plan &p, const uint16_t *w, const float *x, float *y, int64_t N, int64_t K,

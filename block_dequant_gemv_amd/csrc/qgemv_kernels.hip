@@ -21,6 +21,7 @@
 // float4 slot c*32 + j), so the 32 lanes of a row read consecutive 16-byte
 // LDS words (no bank conflicts) and the two row slots of a wavefront read the
 // same words (broadcast).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -119,50 +120,79 @@ struct Unit {
     u32x2 sc;
 };
 
-// Issue the loads of tile t, segment s (t, s wave-uniform). In a ragged last
-// segment lanes j >= nb load block nb-1 again (in bounds); their scales are
-// zeroed in compute_unit. With `real` false (no unit left) every lane loads
-// the first 16 bytes of the buffer instead, one cache line per wavefront.
-// The loop body thus always issues the same loads with no branch around them,
-// so the compiler's wait counts keep the next unit in flight while the
-// current one is computed.
+// A lane's place in a segment: the byte offset of its first 16-byte quant
+// unit and the block whose activations it reads, for full segments and for a
+// ragged last segment of nb_last < 32 blocks. In the ragged segment lanes
+// j >= nb_last read block nb_last - 1 again (in bounds) and count as dead:
+// their scales are zeroed, so they add nothing.
+struct LanePlace {
+    uint32_t off_full, off_last;   // (slot * nb + jc) * 16 for nb = 32 / nb_last
+    uint32_t str_last;             // bytes between the b/h units of the last segment (wave-uniform)
+    int j_last;                    // jc in the last segment
+    bool live_last;
+};
+
+__device__ __forceinline__ LanePlace lane_place(const Geometry &g, int slot, int j)
+{
+    LanePlace p;
+    const int nb_last = (int)seg_blocks(g, g.nseg - 1);
+    p.j_last = j < nb_last ? j : nb_last - 1;
+    p.live_last = j < nb_last;
+    p.off_full = (uint32_t)(slot * kSegBlocks + j) * kUnit;
+    p.off_last = (uint32_t)(slot * nb_last + p.j_last) * kUnit;
+    p.str_last = (uint32_t)(kSlots * nb_last * kUnit);
+    return p;
+}
+
+// Issue the loads of tile t, segment s (t, s wave-uniform): a wave-uniform
+// base address plus the lane's 32-bit offset. With `real` false (no unit
+// left) every lane loads the first 16 bytes of the buffer instead, one cache
+// line per wavefront. The loop body thus always issues the same loads with no
+// branch around them, so the compiler's wait counts keep the next unit in
+// flight while the current one is computed.
 template <int QT>
 __device__ __forceinline__ void load_unit(Unit<QT> &u, const uint8_t *__restrict__ wp, const Geometry &g, int64_t t,
-                                          int64_t s, int slot, int j, bool real)
+                                          int64_t s, const LanePlace &lp, bool real)
 {
     constexpr int NH = Unit<QT>::NH;
     constexpr int64_t seg_q = (int64_t)kTileRows * kSegBlocks * NH * kUnit;
+    constexpr uint32_t str_full = (uint32_t)(kSlots * kSegBlocks * kUnit);
     t = real ? t : 0;
     s = real ? s : 0;
-    const int nb = (int)seg_blocks(g, s);
-    const int jc = j < nb ? j : nb - 1;
+    const bool last = s == g.nseg - 1;
+    const uint32_t off = real ? (last ? lp.off_last : lp.off_full) : 0u;
+    const uint32_t ustride = real ? (last ? lp.str_last : str_full) : 0u;
     const uint8_t *base = wp + t * g.tile_q + s * seg_q;
-    const uint32_t lane_off = real ? (uint32_t)(slot * nb + jc) * kUnit : 0u;
-    const uint32_t ustride = real ? (uint32_t)(kSlots * nb * kUnit) : 0u;
 #pragma unroll
     for (int b = 0; b < kRowsPerLane; ++b)
 #pragma unroll
-        for (int h = 0; h < NH; ++h)
-            u.q[b][h] = __builtin_nontemporal_load((const u32x4 *)(base + (uint32_t)(b * NH + h) * ustride + lane_off));
+        for (int h = 0; h < NH; ++h) {
+            const uint8_t *ub = base + (uint32_t)(b * NH + h) * ustride;
+            u.q[b][h] = __builtin_nontemporal_load((const u32x4 *)(ub + off));
+        }
+    // scales: (slot * nb + jc) * 8 bytes = half the quant offset
     const uint8_t *sbase = wp + g.scale_off + t * g.tile_s + s * (int64_t)(kTileRows * kSegBlocks * 2);
-    const uint32_t s_off = real ? (uint32_t)(slot * nb + jc) * (kRowsPerLane * 2) : 0u;
-    u.sc = __builtin_nontemporal_load((const u32x2 *)(sbase + s_off));
+    u.sc = __builtin_nontemporal_load((const u32x2 *)(sbase + (off >> 1)));
 }
 
 // acc[m][b] += d_b * sum_e v_e * x_m[e] over the lane's block of segment s.
+// j is the block whose activations the lane reads; live is false only for
+// lanes past the end of a ragged last segment.
 template <int QT, int M, bool XLDS>
 __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][kRowsPerLane], const Consts &k,
                                              const f32x4 *xs4, const float *__restrict__ x, int64_t x_stride,
-                                             int64_t nseg, int64_t s, int j, int nb)
+                                             int64_t nseg, int64_t s, int j, bool live)
 {
     constexpr int B = kRowsPerLane;
-    const bool live = j < nb;     // false only for lanes past the end of a ragged last segment
-    j = live ? j : nb - 1;
     float sb[M][B];
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
         for (int b = 0; b < B; ++b) sb[m][b] = 0.0f;
+    // LDS: row m, segment s, chunk c of block j at float4 m*nseg*256 + s*256 + c*32 + j
+    const uint32_t x_row = (uint32_t)nseg << 8;
+    const f32x4 *xl = xs4 + ((uint32_t)s << 8) + (uint32_t)j;
+    const float *xg = x + s * kSegWeights + j * 32;
 
     // 8 float4 chunks of x per block; Q4_0 consumes 2 chunks per dword, Q8_0 one.
 #pragma unroll
@@ -173,9 +203,9 @@ __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 if (XLDS)
-                    xv[cc][m] = xs4[((m * nseg + s) * 8 + c + cc) * 32 + j];
+                    xv[cc][m] = xl[m * x_row + (c + cc) * 32];
                 else
-                    xv[cc][m] = *(const f32x4 *)(x + m * x_stride + s * kSegWeights + j * 32 + (c + cc) * 4);
+                    xv[cc][m] = *(const f32x4 *)(xg + m * x_stride + (c + cc) * 4);
             }
 #pragma unroll
         for (int b = 0; b < B; ++b) {
@@ -253,6 +283,7 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
     const int64_t s_begin = nseg * wk / W, s_end = nseg * (wk + 1) / W;
 
     const Consts k = make_consts();
+    const LanePlace lp = lane_place(g, slot, j);
     // This wavefront's units, in order: (t, s) for t in [t_begin, t_end), s in [s_begin, s_end).
     const int64_t n_units = (t_end > t_begin ? t_end - t_begin : 0) * (s_end - s_begin);
 
@@ -267,38 +298,35 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
     Unit<QT> ring[S];
 #pragma unroll
     for (int r = 0; r < D; ++r) {
-        load_unit<QT>(ring[r], wp, g, t_ld, s_ld, slot, j, u_ld < n_units);
+        load_unit<QT>(ring[r], wp, g, t_ld, s_ld, lp, u_ld < n_units);
         advance(t_ld, s_ld);
         ++u_ld;
     }
 
     if (XLDS) {
-        // stage X[m][k] (k < nseg*1024, zero beyond K) as xs4[((m*nseg + seg)*8 + c)*32 + jj];
-        // K % 32 == 0, so a 16-byte chunk is either wholly inside K or wholly past it.
-        // Loads are issued in batches of 4 per thread before any LDS write.
-        const int64_t per_m = nseg * (kSegWeights / 4);
-        const int64_t nchunk = (int64_t)M * per_m;
-        const int nthr = blockDim.x;
-        for (int64_t base = tid; base < nchunk; base += 4 * (int64_t)nthr) {
-            f32x4 v[4];
+        // Stage row m of X as xs4[m*nseg*256 + seg*256 + c*32 + jj], where float4
+        // chunk i = seg*256 + jj*8 + c of the row holds x[4i .. 4i+3] (zero past K;
+        // K % 32 == 0, so a chunk is wholly inside K or wholly past it). Indexing
+        // is 32-bit shifts and masks (the staged area is at most LDS-sized); each
+        // thread issues its global loads in batches of 4 before writing LDS.
+        const uint32_t per_m = (uint32_t)nseg << 8;
+        const uint32_t k4 = (uint32_t)(K >> 2);
+        const uint32_t nthr = blockDim.x;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t i = base + (int64_t)q * nthr;
-                const int64_t m = i / per_m;
-                const int64_t kk = (i - m * per_m) * 4;
-                const bool inside = i < nchunk && kk < K;
-                v[q] = inside ? *(const f32x4 *)(x + m * a.x_stride + kk) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            }
+        for (int m = 0; m < M; ++m) {
+            const float *xm = x + (int64_t)m * a.x_stride;
+            f32x4 *dst = xs4 + (uint32_t)m * per_m;
+            for (uint32_t base = tid; base < per_m; base += 4 * nthr) {
+                f32x4 v[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t i = base + (int64_t)q * nthr;
-                if (i < nchunk) {
-                    const int64_t m = i / per_m;
-                    const int64_t kk = (i - m * per_m) * 4;
-                    const int64_t seg = kk / kSegWeights;
-                    const int within = (int)(kk - seg * kSegWeights);
-                    const int jj = within >> 5, c = (within & 31) >> 2;
-                    xs4[((m * nseg + seg) * 8 + c) * 32 + jj] = v[q];
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t i = base + q * nthr;
+                    v[q] = i < k4 ? *(const f32x4 *)(xm + 4 * (size_t)i) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t i = base + q * nthr;
+                    if (i < per_m) dst[(i & ~255u) | ((i & 7u) << 5) | ((i >> 3) & 31u)] = v[q];
                 }
             }
         }
@@ -312,19 +340,20 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
 #pragma unroll
         for (int b = 0; b < B; ++b) acc[m][b] = 0.0f;
 
-    int64_t t = t_begin, s = s_begin;   // compute cursor: coordinates of unit u
-    int64_t u = 0;
+    int64_t t = t_begin, s = s_begin;   // compute cursor: the unit being computed
 
     // Issue the loads of unit u+D into `nxt` (a dummy one-line load past the
     // last unit), then compute unit u from `cur` and finish the tile after its
     // last segment.
     auto step = [&](Unit<QT> &cur, Unit<QT> &nxt) {
-        load_unit<QT>(nxt, wp, g, t_ld, s_ld, slot, j, u_ld < n_units);
+        load_unit<QT>(nxt, wp, g, t_ld, s_ld, lp, u_ld < n_units);
         advance(t_ld, s_ld);
         ++u_ld;
         // keep the scheduler from sinking these loads into the compute below
         __builtin_amdgcn_sched_barrier(0);
-        compute_unit<QT, M, XLDS>(cur, acc, k, xs4, x, a.x_stride, nseg, s, j, (int)seg_blocks(g, s));
+        const bool last = s == nseg - 1;
+        compute_unit<QT, M, XLDS>(cur, acc, k, xs4, x, a.x_stride, nseg, s, last ? lp.j_last : j,
+                                  !last || lp.live_last);
         if (s + 1 == s_end) {
 #pragma unroll
             for (int m = 0; m < M; ++m)
@@ -386,7 +415,6 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
                 for (int b = 0; b < B; ++b) acc[m][b] = 0.0f;
         }
         advance(t, s);
-        ++u;
     };
 
     // A counted loop over groups of S units with no early exit, so that the only
@@ -504,6 +532,23 @@ __global__ void zero_gaps_kernel(uint8_t *__restrict__ packed, int64_t a0, int64
 // ---------------------------------------------------------------------------
 // launch helpers (host side)
 
+namespace {
+thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
+void take_launch_events(hipEvent_t &start, hipEvent_t &stop)
+{
+    start = t_ev_start;
+    stop = t_ev_stop;
+    t_ev_start = t_ev_stop = nullptr;
+}
+}  // namespace
+
+void set_launch_events(hipEvent_t start, hipEvent_t stop)
+{
+    t_ev_start = start;
+    t_ev_stop = stop;
+}
+
 template <int QT, int M, int EPI, int W, bool XLDS, int D>
 static hipError_t launch_q(const uint8_t *wp, const float *x, float *y, const QArgs &a, int64_t grid, int block,
                            size_t lds, hipStream_t stream)
@@ -513,7 +558,9 @@ static hipError_t launch_q(const uint8_t *wp, const float *x, float *y, const QA
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(block), lds, stream, wp, x, y, a);
+    hipEvent_t e0, e1;
+    take_launch_events(e0, e1);
+    hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(block), (uint32_t)lds, stream, e0, e1, 0u, wp, x, y, a);
     return hipGetLastError();
 }
 
@@ -567,18 +614,21 @@ hipError_t launch_qgemv(int qt, int M, int epi, const QPlan &p, const uint8_t *w
 hipError_t launch_f16(const F16Plan &p, const uint16_t *w, const float *x, float *y, int64_t N, int64_t K,
                       hipStream_t s)
 {
-    dim3 grid((unsigned)p.grid), block(p.waves * 64);
+    const dim3 grid((unsigned)p.grid), block(p.waves * 64);
+    hipEvent_t e0, e1;
+    take_launch_events(e0, e1);
+    auto go = [&](auto kern) { hipExtLaunchKernelGGL(kern, grid, block, 0u, s, e0, e1, 0u, w, x, y, N, K); };
     if (p.vec) {
         switch (p.R) {
-        case 1: hipLaunchKernelGGL((gemv_f16_kernel<1, true>), grid, block, 0, s, w, x, y, N, K); break;
-        case 2: hipLaunchKernelGGL((gemv_f16_kernel<2, true>), grid, block, 0, s, w, x, y, N, K); break;
-        default: hipLaunchKernelGGL((gemv_f16_kernel<4, true>), grid, block, 0, s, w, x, y, N, K); break;
+        case 1: go(gemv_f16_kernel<1, true>); break;
+        case 2: go(gemv_f16_kernel<2, true>); break;
+        default: go(gemv_f16_kernel<4, true>); break;
         }
     } else {
         switch (p.R) {
-        case 1: hipLaunchKernelGGL((gemv_f16_kernel<1, false>), grid, block, 0, s, w, x, y, N, K); break;
-        case 2: hipLaunchKernelGGL((gemv_f16_kernel<2, false>), grid, block, 0, s, w, x, y, N, K); break;
-        default: hipLaunchKernelGGL((gemv_f16_kernel<4, false>), grid, block, 0, s, w, x, y, N, K); break;
+        case 1: go(gemv_f16_kernel<1, false>); break;
+        case 2: go(gemv_f16_kernel<2, false>); break;
+        default: go(gemv_f16_kernel<4, false>); break;
         }
     }
     return hipGetLastError();

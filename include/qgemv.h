@@ -139,6 +139,18 @@ const char *qg_last_error(void);
 qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int *split_k_waves,
                        int64_t *workgroups, int *x_in_lds);
 
+/* Time the next GEMV kernel (qgemv_q8_0, qgemv_q4_0, gemv_f16_splitk,
+ * qgemv_fused_gateup_silu or qgemv_verify) that the calling thread launches.
+ * start_event and stop_event are hipEvent_t handles, created by the caller
+ * with timing enabled and owned by the caller. That call's kernel records its
+ * own start and end time into them (the dispatch's timestamps, which a
+ * kernel trace also reports), so hipEventElapsedTime(start, stop) gives the
+ * kernel's duration without the latency of event records queued around it.
+ * The setting is used by one call and then cleared; a call that fails, or
+ * (NULL, NULL), clears it too. Pack calls neither use nor clear it.
+ * Returns QG_OK, or QG_EINVAL when exactly one event is NULL. */
+qg_status qg_time_next_launch(void *start_event, void *stop_event);
+
 #ifdef __cplusplus
 }
 #endif

@@ -179,3 +179,29 @@ def test_run_to_run_bitwise_determinism(kind):
         outs.append(y)
     sync()
     assert all(torch.equal(o, outs[0]) for o in outs[1:])
+
+
+def test_timed_launch_matches_untimed_launch():
+    # binding timing events to a launch changes neither the kernel nor its output,
+    # and the binding is used by exactly one call
+    torch = torch_dev()
+    N, K = 1000, 2048
+    rng = np.random.default_rng(77)
+    for kind in ("q8_0", "q4_0"):
+        canon = W.matrix(kind, N, K, rng)
+        packed = qg.pack_weights(kind, canon, N, K)
+        xd = to_dev(W.activation(K, rng))
+        y0, y1, y2 = empty_f32(N), empty_f32(N), empty_f32(N)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for e in ev:
+            e.record()
+        announce(f"timed launch {kind} {N}x{K}")
+        qg.qgemv(kind, packed, xd, y0, N, K)
+        qg.qg_time_next_launch(ev[0], ev[1])
+        qg.qgemv(kind, packed, xd, y1, N, K)
+        qg.qgemv(kind, packed, xd, y2, N, K)
+        sync()
+        ms = ev[0].elapsed_time(ev[1])
+        assert 0.0 < ms < 1000.0, ms
+        a0, a1, a2 = (t.cpu().numpy() for t in (y0, y1, y2))
+        assert a0.tobytes() == a1.tobytes() == a2.tobytes()

@@ -111,6 +111,18 @@ def test_argument_checks_return_codes_without_gpu(L):
     assert "overlap" in msg
 
 
+def test_time_next_launch_arguments(L):
+    # host-only: binding or clearing events makes no HIP call
+    f = FAKE
+    assert call(L, "qg_time_next_launch", f, None) == qg.QG_EINVAL
+    assert call(L, "qg_time_next_launch", None, f) == qg.QG_EINVAL
+    assert call(L, "qg_time_next_launch", None, None) == qg.QG_OK
+    # a failed call clears a binding: the fake events are never handed to HIP
+    assert call(L, "qg_time_next_launch", f, f + 64) == qg.QG_OK
+    assert call(L, "qgemv_q8_0", None, f, f + 4096, 8, 32, None) == qg.QG_EINVAL
+    assert call(L, "qg_time_next_launch", None, None) == qg.QG_OK
+
+
 def test_plan_info_split_is_independent_of_m(L):
     # the decode GEMV and the verify GEMV of a weight must add in the same order
     for kind in ("q8_0", "q4_0"):
