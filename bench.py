@@ -56,7 +56,8 @@ class Call:
 
 def qkernel_name(qg, kind, N, K, M=1, epi="plain"):
     p = qg.qg_plan_info(kind, N, K, M)
-    return f"qgemv<{kind},M{M},{epi},W{p['split_k_waves']},{'lds' if p['x_in_lds'] else 'gx'}>"
+    form = "persist" if p["persistent"] else "tile"
+    return f"qgemv<{kind},M{M},{epi},{form},R{p['split_k_ways']},{'lds' if p['x_in_lds'] else 'gx'}>"
 
 
 def wbytes(kind, N, K):

@@ -73,7 +73,7 @@ def lib():
             "qg_status_str": ([i32], ctypes.c_char_p),
             "qg_last_error": ([], ctypes.c_char_p),
             "qg_plan_info": ([i32, i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i64),
-                              ctypes.POINTER(i32)], i32),
+                              ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
             "qg_time_next_launch": ([vp, vp], i32),
         }
         for name, (args, res) in sig.items():
@@ -217,9 +217,11 @@ def qg_plan_info(qtype, N: int, K: int, M: int = 1) -> dict:
     w = ctypes.c_int()
     g = ctypes.c_int64()
     xl = ctypes.c_int()
+    ps = ctypes.c_int()
     _check("qg_plan_info", lib().qg_plan_info(_qtype(qtype), N, K, M, ctypes.byref(w), ctypes.byref(g),
-                                              ctypes.byref(xl)))
-    return {"split_k_waves": w.value, "workgroups": g.value, "x_in_lds": bool(xl.value)}
+                                              ctypes.byref(xl), ctypes.byref(ps)))
+    return {"split_k_ways": w.value, "workgroups": g.value, "x_in_lds": bool(xl.value),
+            "persistent": bool(ps.value)}
 
 
 def qg_time_next_launch(start_event, stop_event):

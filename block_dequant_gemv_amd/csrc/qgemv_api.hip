@@ -6,6 +6,8 @@
 // allocates device memory.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -104,19 +106,80 @@ constexpr size_t kLdsLimitMulti = 160 * 1024;  // verify calls: the whole LDS of
 // Tuning overrides (read on every call): QG_TILES_PER_GROUP, QG_WAVES_PER_WG
 // (split 1 only), QG_X_GLOBAL (0/1), QG_PREFETCH (1/2). None of them changes a
 // row's operations.
+// CUs of the current device (cached per device); 256, the MI355X count, when
+// no device answers (host-only planning).
+int cu_count()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Persistent form (see qgemv_persist): used for matrices with fewer than
+// kPersistTiles row tiles but at least kPersistUnits (tile, segment) units.
+// There one tile per wavefront leaves the CUs unevenly loaded (2 or 3 small
+// workgroups per CU); smaller matrices are launch-bound and run faster in the
+// other form, larger ones balance themselves (measured). The choice and the K
+// split (ranges) depend only on (rows, K) and the device's CU count, never on
+// M, so the decode and the verify call of a weight run the same per-row
+// operations. QG_PERSIST=0/1 overrides the choice for launch-shape sweeps.
+constexpr int64_t kPersistTiles = 4096;
+constexpr int64_t kPersistUnits = 2048;   // below this many (tile, segment) units the other form is faster
+constexpr size_t kPartialBudget = 64 * 1024;   // LDS for the range partials at M = 6
+
+bool plan_persist(int64_t rows, int64_t K, int64_t *ranges, int64_t *grid, int64_t *max_tiles)
+{
+    const int64_t n_tiles = (rows + qgl::kTileRows - 1) / qgl::kTileRows;
+    const int64_t nseg = (K / 32 + qgl::kSegBlocks - 1) / qgl::kSegBlocks;
+    const int64_t forced = env_int("QG_PERSIST", -1);
+    if (forced == 0 || (forced != 1 && (n_tiles >= kPersistTiles || n_tiles * nseg < kPersistUnits))) return false;
+    *grid = std::min<int64_t>(cu_count(), n_tiles);
+    *max_tiles = (n_tiles + *grid - 1) / *grid;
+    // one segment per item when the partials fit, else the largest divisor of nseg that fits
+    int64_t r = std::min<int64_t>(nseg, 32);
+    while (r > 1 && (nseg % r != 0 || (size_t)(*max_tiles * r * 6 * qgl::kTileRows * 4) > kPartialBudget)) --r;
+    *ranges = r;
+    return true;
+}
+
 qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M)
 {
     qgk::QPlan p;
     const Geometry g = qgl::geometry(qt, rows, K);
+    const size_t xbytes = (size_t)M * (size_t)g.nseg * qgl::kSegWeights * sizeof(float);
+    const int64_t xg_env = env_int("QG_X_GLOBAL", -1);
+    int64_t ranges = 1, pgrid = 0, max_tiles = 0;
+    p.persist = plan_persist(rows, K, &ranges, &pgrid, &max_tiles);
+    p.depth = 1;
+    p.tpg = 1;
+    if (p.persist) {
+        p.ranges = (int)ranges;
+        p.max_tiles = max_tiles;
+        p.W = (int)ranges;
+        p.grid = pgrid;
+        const size_t part = ranges > 1 ? (size_t)max_tiles * ranges * M * qgl::kTileRows * 4 : 0;
+        bool lds = xbytes + part <= kLdsLimitMulti;
+        if (xg_env == 0 || xg_env == 1) lds = lds && xg_env == 0;
+        p.x_in_lds = lds;
+        p.lds_bytes = (lds ? xbytes : 0) + part;
+        p.block = qgk::persist_threads(qt, M, lds);
+        return p;
+    }
+    p.ranges = 1;
+    p.max_tiles = 0;
     p.W = split_k_waves(rows, K);
     // One row tile per group: many short, independent wavefronts, which the
     // hardware dispatcher balances across the CUs better than longer chains
     // (measured on both LM-head shapes).
-    p.tpg = 1;
     const int64_t tpg_env = env_int("QG_TILES_PER_GROUP", 0);
     if (tpg_env > 0) p.tpg = tpg_env;
     const int64_t groups = (g.n_tiles + p.tpg - 1) / p.tpg;
-    const size_t xbytes = (size_t)M * (size_t)g.nseg * qgl::kSegWeights * sizeof(float);
     const size_t lds_limit = M > 1 ? kLdsLimitMulti : kLdsLimit;
     int G;   // groups per workgroup
     if (p.W > 1) {
@@ -134,14 +197,12 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M)
     p.grid = (groups + G - 1) / G;
     const double wg_weight_bytes = (double)G * (double)p.tpg * (double)(g.tile_q + g.tile_s);
     bool lds = xbytes <= lds_limit && (M > 1 || wg_weight_bytes >= 4.0 * (double)xbytes);
-    const int64_t xg_env = env_int("QG_X_GLOBAL", -1);
     if (xg_env == 0 || xg_env == 1) lds = xbytes <= lds_limit && xg_env == 0;
     p.x_in_lds = lds;
     p.lds_bytes = p.x_in_lds ? xbytes : 0;
     // Prefetch depth: one unit in flight ahead of the one being computed. A
     // depth of 2 (single-row kernels only) measured no faster on any of the
     // workload shapes and costs registers; it stays reachable for sweeps.
-    p.depth = 1;
     const int64_t d_env = env_int("QG_PREFETCH", 0);
     if (d_env == 1 || d_env == 2) p.depth = (int)d_env;
     return p;
@@ -171,6 +232,8 @@ qg_status run_qgemv(int qt, int epi, const void *w, const float *x, float *y, in
     a.x_stride = K;
     a.y_stride = n_out;
     a.tpg = p.tpg;
+    a.n_wg = p.grid;
+    a.ranges = p.ranges;
     hipError_t e = qgk::launch_qgemv(qt, M, epi, p, (const uint8_t *)w, x, y, a, as_stream(stream));
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
@@ -365,16 +428,17 @@ const char *qg_status_str(int status)
 
 const char *qg_last_error(void) { return g_last_error.c_str(); }
 
-qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int *split_k_waves_out, int64_t *workgroups,
-                       int *x_in_lds)
+qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int *split_k_ways, int64_t *workgroups,
+                       int *x_in_lds, int *persistent)
 {
     qg_status st = check_qshape(qtype, N, K, "qg_plan_info");
     if (st) return st;
     if (M < 1 || M > 6) return fail(QG_EUNSUPPORTED, "qg_plan_info: M=%d", M);
     const qgk::QPlan p = make_qplan(qtype, N, K, M);
-    if (split_k_waves_out) *split_k_waves_out = p.W;
+    if (split_k_ways) *split_k_ways = p.W;
     if (workgroups) *workgroups = p.grid;
     if (x_in_lds) *x_in_lds = p.x_in_lds ? 1 : 0;
+    if (persistent) *persistent = p.persist ? 1 : 0;
     return ok();
 }
 

@@ -21,12 +21,18 @@ struct QArgs {
     int64_t x_stride;    // floats between activation rows (K)
     int64_t y_stride;    // floats between output rows (N)
     int64_t tpg;         // row tiles walked by one group of W wavefronts
+    // persistent form only
+    int64_t n_wg;        // workgroups; workgroup b owns tiles [b*n_tiles/n_wg, (b+1)*n_tiles/n_wg)
+    int64_t ranges;      // K ranges per tile (divides nseg); item = (tile, range)
 };
 
 // How one quantised call is split. W depends only on (qtype, rows, K) so that
 // the decode GEMV and the verify GEMV of the same weight add in the same order.
 struct QPlan {
-    int W;               // wavefronts splitting one row tile along K (1, 2, 4)
+    bool persist;        // persistent form: one workgroup per CU, (tile, K range) items
+    int ranges;          // persistent form: K ranges per tile (divides nseg)
+    int64_t max_tiles;   // persistent form: most tiles any workgroup owns
+    int W;               // classic form: wavefronts splitting one row tile along K (1, 2, 4, 8)
     int64_t tpg;         // tiles per group
     int64_t grid;        // workgroups
     int block;           // threads per workgroup (64 * wavefronts)
@@ -46,6 +52,17 @@ struct F16Plan {
 // receive that kernel's own start and end timestamps. The launch takes them
 // and clears the setting; (nullptr, nullptr) clears it too.
 void set_launch_events(hipEvent_t start, hipEvent_t stop);
+
+// Threads per workgroup of the persistent form (its launch bound): as many
+// wavefronts as one CU holds at the kernel's register count. Single-row
+// kernels fit 128 VGPRs (16 wavefronts); the multi-row kernels up to 168 (12
+// wavefronts) where they fit without spilling, else 256 (8).
+constexpr int persist_threads(int qt, int M, bool xlds)
+{
+    if (M == 1) return 1024;
+    if (qt == qgl::kQ4_0) return (M <= 4 || xlds) ? 768 : 512;
+    return (M <= 3 || (M == 4 && xlds)) ? 768 : 512;
+}
 
 hipError_t launch_qgemv(int qt, int M, int epi, const QPlan &p, const uint8_t *wp, const float *x, float *y,
                         const QArgs &a, hipStream_t s);

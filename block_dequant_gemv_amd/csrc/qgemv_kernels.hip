@@ -243,6 +243,75 @@ __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][
         for (int b = 0; b < B; ++b) acc[m][b] = __builtin_fmaf((float)d[b], sb[m][b], acc[m][b]);
 }
 
+// Stage row m of X as xs4[m*nseg*256 + seg*256 + c*32 + jj], where float4
+// chunk i = seg*256 + jj*8 + c of the row holds x[4i .. 4i+3] (zero past K;
+// K % 32 == 0, so a chunk is wholly inside K or wholly past it). Indexing is
+// 32-bit shifts and masks (the staged area is at most LDS-sized); each thread
+// issues its global loads in batches of 4 before writing LDS. The caller
+// synchronises the workgroup afterwards.
+template <int M>
+__device__ __forceinline__ void stage_x(f32x4 *xs4, const float *__restrict__ x, int64_t x_stride, int64_t nseg,
+                                        int64_t K)
+{
+    const uint32_t per_m = (uint32_t)nseg << 8;
+    const uint32_t k4 = (uint32_t)(K >> 2);
+    const uint32_t nthr = blockDim.x, tid = threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const float *xm = x + (int64_t)m * x_stride;
+        f32x4 *dst = xs4 + (uint32_t)m * per_m;
+        for (uint32_t base = tid; base < per_m; base += 4 * nthr) {
+            f32x4 v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t i = base + q * nthr;
+                v[q] = i < k4 ? *(const f32x4 *)(xm + 4 * (size_t)i) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t i = base + q * nthr;
+                if (i < per_m) dst[(i & ~255u) | ((i & 7u) << 5) | ((i >> 3) & 31u)] = v[q];
+            }
+        }
+    }
+}
+
+// Write the finished rows of tile t from the lanes of one slot (acc already
+// reduced over the slot's 32 lanes, so every lane holds the sums).
+//   plain:   lane j < M*B stores row b = j % B of activation row m = j / B
+//   gate|up: rows b = 2p (gate) and 2p+1 (up) give output n = row0/2 + p
+template <int M, int EPI>
+__device__ __forceinline__ void store_tile(const float (&acc)[M][kRowsPerLane], float *__restrict__ y, int64_t n_out,
+                                           int64_t y_stride, int64_t t, int slot, int j)
+{
+    constexpr int B = kRowsPerLane;
+    const int64_t row0 = t * kTileRows + slot * kRowsPerLane;
+    if (EPI == kEpiPlain) {
+        if (j < M * B) {
+            float v = 0.0f;
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int b = 0; b < B; ++b)
+                    if (j == m * B + b) v = acc[m][b];
+            const int m = j / B, b = j % B;
+            if (row0 + b < n_out) y[m * y_stride + row0 + b] = v;
+        }
+    } else {
+        if (j < B / 2) {
+            float gv = 0.0f, uv = 0.0f;
+#pragma unroll
+            for (int p = 0; p < B / 2; ++p)
+                if (j == p) {
+                    gv = acc[0][2 * p];
+                    uv = acc[0][2 * p + 1];
+                }
+            const int64_t n = row0 / 2 + j;
+            if (n < n_out) y[n] = silu_mul(gv, uv);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Quantised GEMV. Template parameters:
 //   QT   kQ8_0 / kQ4_0
@@ -304,32 +373,7 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
     }
 
     if (XLDS) {
-        // Stage row m of X as xs4[m*nseg*256 + seg*256 + c*32 + jj], where float4
-        // chunk i = seg*256 + jj*8 + c of the row holds x[4i .. 4i+3] (zero past K;
-        // K % 32 == 0, so a chunk is wholly inside K or wholly past it). Indexing
-        // is 32-bit shifts and masks (the staged area is at most LDS-sized); each
-        // thread issues its global loads in batches of 4 before writing LDS.
-        const uint32_t per_m = (uint32_t)nseg << 8;
-        const uint32_t k4 = (uint32_t)(K >> 2);
-        const uint32_t nthr = blockDim.x;
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const float *xm = x + (int64_t)m * a.x_stride;
-            f32x4 *dst = xs4 + (uint32_t)m * per_m;
-            for (uint32_t base = tid; base < per_m; base += 4 * nthr) {
-                f32x4 v[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t i = base + q * nthr;
-                    v[q] = i < k4 ? *(const f32x4 *)(xm + 4 * (size_t)i) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                }
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t i = base + q * nthr;
-                    if (i < per_m) dst[(i & ~255u) | ((i & 7u) << 5) | ((i >> 3) & 31u)] = v[q];
-                }
-            }
-        }
+        stage_x<M>(xs4, x, a.x_stride, nseg, K);
         __syncthreads();
     }
     if (n_units == 0) return;   // uniform across the workgroup when W > 1
@@ -381,34 +425,7 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
                 }
                 __syncthreads();
             }
-            if (wk == 0) {
-                const int64_t row0 = t * kTileRows + slot * kRowsPerLane;
-                if (EPI == kEpiPlain) {
-                    if (j < M * B) {
-                        float v = 0.0f;
-#pragma unroll
-                        for (int m = 0; m < M; ++m)
-#pragma unroll
-                            for (int b = 0; b < B; ++b)
-                                if (j == m * B + b) v = acc[m][b];
-                        const int m = j / B, b = j % B;
-                        if (row0 + b < a.n_out) y[m * a.y_stride + row0 + b] = v;
-                    }
-                } else {
-                    // rows b = 2p (gate) and 2p+1 (up) of the lane hold output n = row0/2 + p
-                    if (j < B / 2) {
-                        float gv = 0.0f, uv = 0.0f;
-#pragma unroll
-                        for (int p = 0; p < B / 2; ++p)
-                            if (j == p) {
-                                gv = acc[0][2 * p];
-                                uv = acc[0][2 * p + 1];
-                            }
-                        const int64_t n = row0 / 2 + j;
-                        if (n < a.n_out) y[n] = silu_mul(gv, uv);
-                    }
-                }
-            }
+            if (wk == 0) store_tile<M, EPI>(acc, y, a.n_out, a.y_stride, t, slot, j);
 #pragma unroll
             for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -428,6 +445,156 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
 #pragma unroll
     for (int r = 0; r < S - 1; ++r)
         if (r < rem) step(ring[r], ring[(r + D) % S]);
+}
+
+
+// ---------------------------------------------------------------------------
+// Persistent form of the quantised GEMV, for matrices with too few row tiles
+// to balance the CUs one tile per wavefront. One workgroup per CU: workgroup b
+// owns the contiguous tiles [T0, T1) = [b*n_tiles/n_wg, (b+1)*n_tiles/n_wg)
+// (the same number to within one) and stages the activations once. Each tile
+// splits along K into R = a.ranges equal ranges of nseg/R segments, and item
+// i = (tile T0 + i/R, range i%R) goes to wavefront i % G: the items, not whole
+// tiles, are spread over the wavefronts. A wavefront walks its items' units
+// with the next unit's loads in flight; after an item's last unit it reduces
+// the lanes (same butterfly as above) and, for R > 1, parks the 8-row partial
+// in LDS. When every wavefront is done, the partials of each row are added in
+// range order, ((p0 + p1) + p2) + ..., and stored (with the SiLU epilogue for
+// gate|up). For any M a row goes through the same operations, so the verify
+// rows still equal the M=1 rows bit for bit.
+template <int QT, int M, int EPI, bool XLDS>
+__global__ void __launch_bounds__(persist_threads(QT, M, XLDS))
+qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float *__restrict__ y, QArgs a)
+{
+    constexpr int B = kRowsPerLane;
+    constexpr int S = 2;   // ring: one unit in flight ahead of the one being computed
+    extern __shared__ f32x4 xs4[];
+
+    const int tid = threadIdx.x;
+    const int G = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int slot = lane >> 5, j = lane & 31;
+
+    const Geometry &g = a.geo;
+    const int64_t K = g.K, nseg = g.nseg;
+    const uint32_t R = (uint32_t)a.ranges;
+    const uint32_t L = (uint32_t)(nseg / R);   // segments per range
+    const int64_t T0 = (int64_t)blockIdx.x * g.n_tiles / a.n_wg;
+    const int64_t T1 = ((int64_t)blockIdx.x + 1) * g.n_tiles / a.n_wg;
+    const uint32_t n_items = (uint32_t)(T1 - T0) * R;
+    const uint32_t my_items = n_items > (uint32_t)wave ? (n_items - (uint32_t)wave + G - 1) / G : 0u;
+    const int64_t n_units = (int64_t)my_items * L;
+    float *part = (float *)(xs4 + (XLDS ? (uint32_t)M * ((uint32_t)nseg << 8) : 0u));   // [tile][range][m][8]
+
+    const Consts k = make_consts();
+    const LanePlace lp = lane_place(g, slot, j);
+
+    // A cursor over this wavefront's units: item i, its tile and range, segment s.
+    struct Cur {
+        uint32_t i, r;
+        int64_t t, s, s_end;
+    };
+    auto seat = [&](Cur &c) {
+        const uint32_t q = c.i / R;
+        c.r = c.i - q * R;
+        c.t = T0 + q;
+        c.s = (int64_t)c.r * L;
+        c.s_end = c.s + L;
+    };
+    auto advance = [&](Cur &c) {
+        if (++c.s == c.s_end) {
+            c.i += G;
+            seat(c);
+        }
+    };
+    Cur ld, cu;
+    ld.i = wave;
+    seat(ld);
+    cu = ld;
+    int64_t u_ld = 0;
+
+    Unit<QT> ring[S];
+    load_unit<QT>(ring[0], wp, g, ld.t, ld.s, lp, u_ld < n_units);
+    advance(ld);
+    ++u_ld;
+
+    if (XLDS) {
+        stage_x<M>(xs4, x, a.x_stride, nseg, K);
+        __syncthreads();
+    }
+
+    float acc[M][B];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[m][b] = 0.0f;
+
+    auto step = [&](Unit<QT> &cur, Unit<QT> &nxt) {
+        load_unit<QT>(nxt, wp, g, ld.t, ld.s, lp, u_ld < n_units);
+        advance(ld);
+        ++u_ld;
+        __builtin_amdgcn_sched_barrier(0);
+        const bool last = cu.s == nseg - 1;
+        compute_unit<QT, M, XLDS>(cur, acc, k, xs4, x, a.x_stride, nseg, cu.s, last ? lp.j_last : j,
+                                  !last || lp.live_last);
+        if (cu.s + 1 == cu.s_end) {
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int b = 0; b < B; ++b) acc[m][b] = half_wave_sum(acc[m][b]);
+            if (R == 1) {
+                store_tile<M, EPI>(acc, y, a.n_out, a.y_stride, cu.t, slot, j);
+            } else if (j == 0) {
+                float *pp = part + ((size_t)(cu.t - T0) * R + cu.r) * (M * kTileRows) + slot * B;
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int b = 0; b < B; ++b) pp[m * kTileRows + b] = acc[m][b];
+            }
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int b = 0; b < B; ++b) acc[m][b] = 0.0f;
+        }
+        advance(cu);
+    };
+
+    const int64_t n_groups = n_units / S;
+    for (int64_t gi = 0; gi < n_groups; ++gi) {
+        step(ring[0], ring[1]);
+        step(ring[1], ring[0]);
+    }
+    if (n_units - n_groups * S) step(ring[0], ring[1]);
+
+    if (R > 1) {
+        // every wavefront reaches this barrier (no early exit above)
+        __syncthreads();
+        const uint32_t ntile = (uint32_t)(T1 - T0);
+        if (EPI == kEpiPlain) {
+            for (uint32_t o = tid; o < ntile * (M * kTileRows); o += blockDim.x) {
+                const uint32_t tl = o / (M * kTileRows), rem = o - tl * (M * kTileRows);
+                const uint32_t m = rem / kTileRows, row = rem - m * kTileRows;
+                const float *pp = part + (size_t)tl * R * (M * kTileRows) + m * kTileRows + row;
+                float v = pp[0];
+                for (uint32_t r = 1; r < R; ++r) v += pp[(size_t)r * (M * kTileRows)];
+                const int64_t n = (T0 + tl) * kTileRows + row;
+                if (n < a.n_out) y[m * a.y_stride + n] = v;
+            }
+        } else {
+            for (uint32_t o = tid; o < ntile * (kTileRows / 2); o += blockDim.x) {
+                const uint32_t tl = o / (kTileRows / 2), q = o - tl * (kTileRows / 2);
+                const float *pp = part + (size_t)tl * R * kTileRows + 2 * q;
+                float gv = pp[0], uv = pp[1];
+                for (uint32_t r = 1; r < R; ++r) {
+                    gv += pp[(size_t)r * kTileRows];
+                    uv += pp[(size_t)r * kTileRows + 1];
+                }
+                const int64_t n = (T0 + tl) * (kTileRows / 2) + q;
+                if (n < a.n_out) y[n] = silu_mul(gv, uv);
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -569,9 +736,11 @@ static hipError_t dispatch_x(const uint8_t *wp, const float *x, float *y, const 
                              size_t lds, bool xlds, int depth, hipStream_t s)
 {
     // prefetch depth 2 is instantiated for the single-row kernels only
-    if (M == 1 && depth >= 2)
-        return xlds ? launch_q<QT, M, EPI, W, true, 2>(wp, x, y, a, grid, block, lds, s)
-                    : launch_q<QT, M, EPI, W, false, 2>(wp, x, y, a, grid, block, 0, s);
+    if constexpr (M == 1) {
+        if (depth >= 2)
+            return xlds ? launch_q<QT, M, EPI, W, true, 2>(wp, x, y, a, grid, block, lds, s)
+                        : launch_q<QT, M, EPI, W, false, 2>(wp, x, y, a, grid, block, 0, s);
+    }
     return xlds ? launch_q<QT, M, EPI, W, true, 1>(wp, x, y, a, grid, block, lds, s)
                 : launch_q<QT, M, EPI, W, false, 1>(wp, x, y, a, grid, block, 0, s);
 }
@@ -588,27 +757,52 @@ static hipError_t dispatch_w(const uint8_t *wp, const float *x, float *y, const 
     }
 }
 
-template <int QT>
-static hipError_t dispatch_m(const uint8_t *wp, const float *x, float *y, const QArgs &a, int M, int epi, int W,
-                             int64_t grid, int block, size_t lds, bool xlds, int depth, hipStream_t s)
+template <int QT, int M, int EPI>
+static hipError_t launch_persist(const uint8_t *wp, const float *x, float *y, const QArgs &a, const QPlan &p,
+                                 hipStream_t stream)
 {
-    if (epi == kEpiGateUp) return dispatch_w<QT, 1, kEpiGateUp>(wp, x, y, a, W, grid, block, lds, xlds, depth, s);
+    auto kern = p.x_in_lds ? qgemv_persist<QT, M, EPI, true> : qgemv_persist<QT, M, EPI, false>;
+    if (p.block != persist_threads(QT, M, p.x_in_lds)) return hipErrorInvalidConfiguration;
+    if (p.lds_bytes > 64 * 1024) {
+        hipError_t e =
+            hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_bytes);
+        if (e != hipSuccess) return e;
+    }
+    hipEvent_t e0, e1;
+    take_launch_events(e0, e1);
+    hipExtLaunchKernelGGL(kern, dim3((unsigned)p.grid), dim3(p.block), (uint32_t)p.lds_bytes, stream, e0, e1, 0u,
+                          wp, x, y, a);
+    return hipGetLastError();
+}
+
+template <int QT, int M, int EPI>
+static hipError_t dispatch_form(const uint8_t *wp, const float *x, float *y, const QArgs &a, const QPlan &p,
+                                hipStream_t s)
+{
+    if (p.persist) return launch_persist<QT, M, EPI>(wp, x, y, a, p, s);
+    return dispatch_w<QT, M, EPI>(wp, x, y, a, p.W, p.grid, p.block, p.lds_bytes, p.x_in_lds, p.depth, s);
+}
+
+template <int QT>
+static hipError_t dispatch_m(const uint8_t *wp, const float *x, float *y, const QArgs &a, int M, int epi,
+                             const QPlan &p, hipStream_t s)
+{
+    if (epi == kEpiGateUp) return dispatch_form<QT, 1, kEpiGateUp>(wp, x, y, a, p, s);
     switch (M) {
-    case 1: return dispatch_w<QT, 1, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, depth, s);
-    case 2: return dispatch_w<QT, 2, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, depth, s);
-    case 3: return dispatch_w<QT, 3, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, depth, s);
-    case 4: return dispatch_w<QT, 4, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, depth, s);
-    case 5: return dispatch_w<QT, 5, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, depth, s);
-    default: return dispatch_w<QT, 6, kEpiPlain>(wp, x, y, a, W, grid, block, lds, xlds, depth, s);
+    case 1: return dispatch_form<QT, 1, kEpiPlain>(wp, x, y, a, p, s);
+    case 2: return dispatch_form<QT, 2, kEpiPlain>(wp, x, y, a, p, s);
+    case 3: return dispatch_form<QT, 3, kEpiPlain>(wp, x, y, a, p, s);
+    case 4: return dispatch_form<QT, 4, kEpiPlain>(wp, x, y, a, p, s);
+    case 5: return dispatch_form<QT, 5, kEpiPlain>(wp, x, y, a, p, s);
+    default: return dispatch_form<QT, 6, kEpiPlain>(wp, x, y, a, p, s);
     }
 }
 
 hipError_t launch_qgemv(int qt, int M, int epi, const QPlan &p, const uint8_t *wp, const float *x, float *y,
                         const QArgs &a, hipStream_t s)
 {
-    if (qt == kQ8_0)
-        return dispatch_m<kQ8_0>(wp, x, y, a, M, epi, p.W, p.grid, p.block, p.lds_bytes, p.x_in_lds, p.depth, s);
-    return dispatch_m<kQ4_0>(wp, x, y, a, M, epi, p.W, p.grid, p.block, p.lds_bytes, p.x_in_lds, p.depth, s);
+    if (qt == kQ8_0) return dispatch_m<kQ8_0>(wp, x, y, a, M, epi, p, s);
+    return dispatch_m<kQ4_0>(wp, x, y, a, M, epi, p, s);
 }
 
 hipError_t launch_f16(const F16Plan &p, const uint16_t *w, const float *x, float *y, int64_t N, int64_t K,

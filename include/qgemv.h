@@ -133,11 +133,18 @@ qg_status qgemv_verify(int qtype, const void *w_packed, const float *X, float *Y
 const char *qg_status_str(int status);
 const char *qg_last_error(void);
 
-/* How a quantised call of this shape is split (for reports): waves that share
- * one row tile along K, workgroups launched, and whether x is staged in LDS.
- * Pure host function. Returns QG_OK or QG_EINVAL. */
-qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int *split_k_waves,
-                       int64_t *workgroups, int *x_in_lds);
+/* How a quantised call of this shape is launched (for reports). Outputs (each
+ * may be NULL):
+ *   split_k_ways  the number of K ranges a row tile's sum is split into (the
+ *                 partial sums of a row are added in range order);
+ *   workgroups    workgroups launched;
+ *   x_in_lds      1 when the activations are staged in LDS, 0 when read from L2;
+ *   persistent    1 for the persistent form (one workgroup per CU, used for
+ *                 matrices with few row tiles), 0 for one wavefront per tile.
+ * Host function: it only reads the current device's CU count (256 when no
+ * device answers). Returns QG_OK, QG_EINVAL or QG_EUNSUPPORTED. */
+qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int *split_k_ways,
+                       int64_t *workgroups, int *x_in_lds, int *persistent);
 
 /* Time the next GEMV kernel (qgemv_q8_0, qgemv_q4_0, gemv_f16_splitk,
  * qgemv_fused_gateup_silu or qgemv_verify) that the calling thread launches.

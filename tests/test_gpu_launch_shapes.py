@@ -2,9 +2,11 @@
 oracle; verify rows stay memcmp-equal to M=1 under the same split.
 
 The planner picks one shape per (type, rows, K); the overrides
-QG_SPLIT_K / QG_X_GLOBAL / QG_WAVES_PER_WG / QG_TILES_PER_GROUP / QG_PREFETCH
-reach the others (prefetch depth 2 exists for the single-row kernels; the
-verify kernels keep depth 1, and their rows must still match).
+QG_PERSIST / QG_SPLIT_K / QG_X_GLOBAL / QG_WAVES_PER_WG / QG_TILES_PER_GROUP /
+QG_PREFETCH reach the others: the one-wavefront-per-tile form with every split,
+activation source, workgroup size, tiles per group and prefetch depth (depth 2
+exists for the single-row kernels; the verify kernels keep depth 1, and their
+rows must still match), and the persistent form with activations in LDS or L2.
 """
 import itertools
 import os
@@ -19,7 +21,7 @@ from gpu_helpers import THREADS, announce, assert_linear, empty_f32, sync, to_de
 
 pytestmark = pytest.mark.gpu
 
-KNOBS = ("QG_SPLIT_K", "QG_X_GLOBAL", "QG_WAVES_PER_WG", "QG_TILES_PER_GROUP", "QG_PREFETCH")
+KNOBS = ("QG_PERSIST", "QG_SPLIT_K", "QG_X_GLOBAL", "QG_WAVES_PER_WG", "QG_TILES_PER_GROUP", "QG_PREFETCH")
 
 
 def _set(**kw):
@@ -38,12 +40,16 @@ def test_forced_launch_shapes(kind, N, K):
     Xd = to_dev(X)
     Y_ref, A_ref = O.verify(kind, canon, X, N, K, threads=THREADS)
     nseg = -(-K // 1024)
+    combos = [dict(QG_PERSIST=1, QG_X_GLOBAL=xg) for xg in (0, 1)]
+    for split, xg, wpw, tpg, pf in itertools.product((1, 2, 4, 8), (0, 1), (1, 2, 4), (1, 3), (1, 2)):
+        if split > nseg or (split > 1 and wpw != 4):
+            continue
+        combos.append(dict(QG_PERSIST=0, QG_SPLIT_K=split, QG_X_GLOBAL=xg, QG_WAVES_PER_WG=wpw,
+                           QG_TILES_PER_GROUP=tpg, QG_PREFETCH=pf))
     try:
-        for split, xg, wpw, tpg, pf in itertools.product((1, 2, 4, 8), (0, 1), (1, 2, 4), (1, 3), (1, 2)):
-            if split > nseg or (split > 1 and wpw != 4):
-                continue
-            _set(QG_SPLIT_K=split, QG_X_GLOBAL=xg, QG_WAVES_PER_WG=wpw, QG_TILES_PER_GROUP=tpg, QG_PREFETCH=pf)
-            ctx = f"{kind} {N}x{K} split={split} xglobal={xg} waves/wg={wpw} tiles/group={tpg} prefetch={pf}"
+        for combo in combos:
+            _set(**combo)
+            ctx = f"{kind} {N}x{K} " + " ".join(f"{k[3:].lower()}={v}" for k, v in combo.items())
             announce(ctx)
             ys = []
             for m in range(3):

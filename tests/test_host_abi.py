@@ -124,15 +124,20 @@ def test_time_next_launch_arguments(L):
 
 
 def test_plan_info_split_is_independent_of_m(L):
-    # the decode GEMV and the verify GEMV of a weight must add in the same order
+    # the decode GEMV and the verify GEMV of a weight must add in the same order:
+    # same form, same K split, whatever M is
     for kind in ("q8_0", "q4_0"):
         for N, K in ((1, 32), (100, 2080), (1024, 2048), (1024, 3072), (5120, 17408), (17408, 5120),
-                     (4096, 1024), (248320, 5120), (64, 65536)):
-            w1 = qg.qg_plan_info(kind, N, K, 1)["split_k_waves"]
+                     (4096, 1024), (248320, 5120), (151936, 1024), (64, 65536), (8, 32 * 1024 * 40)):
+            p1 = qg.qg_plan_info(kind, N, K, 1)
             for M in range(2, 7):
-                assert qg.qg_plan_info(kind, N, K, M)["split_k_waves"] == w1
-    assert qg.qg_plan_info("q4_0", 5120, 17408)["split_k_waves"] > 1
-    assert qg.qg_plan_info("q4_0", 248320, 5120)["split_k_waves"] == 1
+                pm = qg.qg_plan_info(kind, N, K, M)
+                assert (pm["split_k_ways"], pm["persistent"]) == (p1["split_k_ways"], p1["persistent"]), (N, K, M)
+    # the LM heads run one wavefront per tile; the mid-size matrices the persistent form
+    assert not qg.qg_plan_info("q4_0", 248320, 5120)["persistent"]
+    assert not qg.qg_plan_info("q8_0", 151936, 1024)["persistent"]
+    p = qg.qg_plan_info("q4_0", 5120, 17408)
+    assert p["persistent"] and p["split_k_ways"] > 1 and 17 % p["split_k_ways"] == 0
 
 
 SHAPES = [(1, 32), (3, 64), (8, 1024), (9, 1056), (17, 2048), (24, 3104), (5, 5120)]
