@@ -14,8 +14,9 @@ Also measured in the same run:
   * every matrix of the five workload configurations, one call at a time, cold
     (each call's weight rotating through >= 1.2 GiB of device copies) and warm,
     as median us per call, GB/s and fraction of the 8 TB/s HBM3E peak;
-  * the roofline entry of the step's dominant kernel: HIP events bound to each of
-    its launches in the timed steps receive the kernel's start and end times;
+  * the roofline entry of the step's dominant kernel: a second pass over the same
+    steps binds HIP events to every launch, which receive each kernel's own start
+    and end times;
   * the fp64 CPU oracle on the host cores (one thread and all threads) over one
     step of the same workload (the cpu_baseline leg; the only use of oracle/).
 Prints one JSON line on stdout; a readable table goes to stderr.
@@ -364,55 +365,41 @@ def main():
         del src, dst
 
     # ---- headline: K timed steps ------------------------------------------------
-    # One event pair brackets the K steps on the stream the kernels run on. Inside
-    # the region the only timing is on the LM head (the step's dominant call,
-    # last in the step): its launch is bound to an event pair that receives the
-    # kernel's own start and end timestamps (qg_time_next_launch), the same
-    # dispatch times a rocprofv3 kernel trace reports, with no marker queued
-    # between the dependent launches.
+    # The timed region is K plain steps: one event pair brackets them on the
+    # stream the kernels run on and nothing is recorded inside, so the region runs
+    # exactly as a caller's decode loop would. (Binding timing events to a launch
+    # costs the host ~20 us per launch, which would make the loop host-bound.)
     for s in range(args.warmup):
         for c in steps[s % copies]:
             c.fn()
     K = args.steps
     lm = len(steps[0]) - 1
     span = timing_events(torch, 2)
-    ev_lm = timing_events(torch, 2 * K)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     span[0].record()
     for s in range(K):
-        calls = steps[s % copies]
-        for i in range(lm):
-            calls[i].fn()
-        qg.qg_time_next_launch(ev_lm[2 * s], ev_lm[2 * s + 1])
-        calls[lm].fn()
+        for c in steps[s % copies]:
+            c.fn()
     span[1].record()
+    t_enq = time.perf_counter()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / K * 1e3
     value = step_bytes * K / wall / 1e9
     gpu_span_ms = span[0].elapsed_time(span[1])
-    lm_us = np.array([ev_lm[2 * s].elapsed_time(ev_lm[2 * s + 1]) * 1e3 for s in range(K)])
-    dom = steps[0][lm]
-    avg_us = float(lm_us.mean())
-    achieved = dom.nbytes / (avg_us * 1e-6) / 1e9
-    traffic = load_traffic(dom.label)
-    roofline = {
-        "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-        "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
-        "kernel": dom.kernel, "call": dom.label,
-        "avg_launch_us": round(avg_us, 3), "launches": K,
-        "algorithmic_bytes_per_launch": dom.nbytes,
-        "timing": "kernel start/end timestamps of each LM head launch in the timed steps (HIP events bound "
-                  "to the dispatch)",
-    }
-    log(f"headline: {K} steps, {ms_per_step:.4f} ms/step wall, GPU span {gpu_span_ms / K:.4f} ms/step, "
-        f"{value:.1f} GB/s ({100 * value / PEAK_GBPS:.1f}% of 8 TB/s), {copies} weight copies")
-    log(f"  {dom.label}: kernel {float(np.median(lm_us)):.2f} us median, {avg_us:.2f} us mean -> "
-        f"{achieved:.1f} GB/s ({100 * achieved / PEAK_GBPS:.1f}%)  [{dom.kernel}]")
+    host_us = (t_enq - t0) / K * 1e6
+    log(f"headline: {K} steps, {ms_per_step:.4f} ms/step wall, GPU span {gpu_span_ms / K:.4f} ms/step, host "
+        f"enqueue {host_us:.1f} us/step, {value:.1f} GB/s ({100 * value / PEAK_GBPS:.1f}% of 8 TB/s), "
+        f"{copies} weight copies")
 
-    # per-kernel breakdown of the same step, in a separate pass in which every
-    # launch is bound to an event pair (reported, not used for `value`)
+    # ---- kernel pass: the same K steps with every launch timed -----------------
+    # Each launch is bound to an event pair that receives the kernel's own start
+    # and end timestamps (qg_time_next_launch; the dispatch times a rocprofv3
+    # kernel trace reports), on the kernels' stream. Every launch is bound, so
+    # each kernel starts after a timed one, the same way in every step. This
+    # pass gives the roofline entry of the LM head (the dominant call) and each
+    # kernel's share of the step.
     ncall = len(steps[0])
     evk = timing_events(torch, 2 * K * ncall)
     torch.cuda.synchronize()
@@ -424,12 +411,28 @@ def main():
     torch.cuda.synchronize()
     durs = np.array([[evk[2 * (s * ncall + i)].elapsed_time(evk[2 * (s * ncall + i) + 1]) * 1e3
                       for i in range(ncall)] for s in range(K)])  # us [K][ncall]
+    lm_us = durs[:, lm]
+    dom = steps[0][lm]
+    avg_us = float(lm_us.mean())
+    achieved = dom.nbytes / (avg_us * 1e-6) / 1e9
+    traffic = load_traffic(dom.label)
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+        "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
+        "kernel": dom.kernel, "call": dom.label,
+        "avg_launch_us": round(avg_us, 3), "launches": K,
+        "algorithmic_bytes_per_launch": dom.nbytes,
+        "timing": "kernel start/end timestamps of the LM head launches of K decode steps with every launch bound "
+                  "to HIP events (qg_time_next_launch), right after the timed region",
+    }
     for i, c in enumerate(steps[0]):
         med = float(np.median(durs[:, i]))
         log(f"  kernel: {c.label:28s} {med:8.2f} us  {c.nbytes / med / 1e3:8.1f} GB/s  [{c.kernel}]")
     kern_sum = float(np.median(durs.sum(axis=1)))
-    log(f"  sum of the step's kernel times {kern_sum:.2f} us; GPU span per step {1e3 * gpu_span_ms / K:.2f} us "
-        f"(the rest is launch gaps)")
+    log(f"  {dom.label}: kernel {float(np.median(lm_us)):.2f} us median, {avg_us:.2f} us mean -> "
+        f"{achieved:.1f} GB/s ({100 * achieved / PEAK_GBPS:.1f}%)  [{dom.kernel}]")
+    log(f"  sum of the step's kernel times {kern_sum:.2f} us; the timed steps took {1e3 * gpu_span_ms / K:.2f} us of "
+        f"GPU time each")
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
@@ -442,6 +445,7 @@ def main():
                                              f"({copies * step_bytes / 1e9:.2f} GB)",
             "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
             "gpu_ms_per_step": round(gpu_span_ms / K, 5),
+            "host_enqueue_us_per_step": round(host_us, 2),
             "lm_head_kernel_us_median": round(float(np.median(lm_us)), 3),
             "kernel_us_per_step": round(kern_sum, 3),
             "device": props.name,

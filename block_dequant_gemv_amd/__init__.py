@@ -28,7 +28,7 @@ SYMBOLS = (
     "qg_packed_size", "qg_pack", "qg_pack_rows", "qg_pack_gateup",
     "qg_pack_host", "qg_unpack_host", "qg_pack_gateup_host",
     "qgemv_q8_0", "qgemv_q4_0", "gemv_f16_splitk", "qgemv_fused_gateup_silu", "qgemv_verify",
-    "qg_status_str", "qg_last_error", "qg_plan_info", "qg_time_next_launch",
+    "qg_status_str", "qg_last_error", "qg_plan_info", "qg_time_next_launch", "qg_reload_tuning",
 )
 
 
@@ -75,6 +75,7 @@ def lib():
             "qg_plan_info": ([i32, i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i64),
                               ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
             "qg_time_next_launch": ([vp, vp], i32),
+            "qg_reload_tuning": ([], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -222,6 +223,11 @@ def qg_plan_info(qtype, N: int, K: int, M: int = 1) -> dict:
                                               ctypes.byref(xl), ctypes.byref(ps)))
     return {"split_k_ways": w.value, "workgroups": g.value, "x_in_lds": bool(xl.value),
             "persistent": bool(ps.value)}
+
+
+def qg_reload_tuning():
+    """Re-read the QG_* launch-shape overrides from the environment."""
+    _check("qg_reload_tuning", lib().qg_reload_tuning())
 
 
 def qg_time_next_launch(start_event, stop_event):

@@ -76,6 +76,29 @@ int64_t env_int(const char *name, int64_t dflt)
     return (v && *v) ? atoll(v) : dflt;
 }
 
+// Launch-shape overrides for sweeps and tests (QG_SPLIT_K, QG_PERSIST,
+// QG_X_GLOBAL, QG_TILES_PER_GROUP, QG_WAVES_PER_WG, QG_PREFETCH, QG_F16_ROWS,
+// QG_F16_WAVES). They are read from the environment once, on first use, and
+// again on qg_reload_tuning(): a GEMV call itself reads no environment.
+enum TuneKey { kSplitK, kPersist, kXGlobal, kTilesPerGroup, kWavesPerWg, kPrefetch, kF16Rows, kF16Waves, kNumTune };
+const char *const kTuneNames[kNumTune] = {"QG_SPLIT_K",      "QG_PERSIST",      "QG_X_GLOBAL", "QG_TILES_PER_GROUP",
+                                          "QG_WAVES_PER_WG", "QG_PREFETCH",     "QG_F16_ROWS", "QG_F16_WAVES"};
+const int64_t kTuneDefaults[kNumTune] = {0, -1, -1, 0, 0, 0, 0, 0};
+std::atomic<int64_t> g_tune[kNumTune];
+std::atomic<bool> g_tune_loaded{false};
+
+void load_tuning()
+{
+    for (int i = 0; i < kNumTune; ++i) g_tune[i].store(env_int(kTuneNames[i], kTuneDefaults[i]), std::memory_order_relaxed);
+    g_tune_loaded.store(true, std::memory_order_release);
+}
+
+int64_t tune(TuneKey k)
+{
+    if (!g_tune_loaded.load(std::memory_order_acquire)) load_tuning();
+    return g_tune[k].load(std::memory_order_relaxed);
+}
+
 // Wavefronts that split one tile along K. Depends only on (rows, K): a matrix
 // with few row tiles gets more wavefronts per tile so that the chip has enough
 // loads in flight. The decode and the verify call of the same weight always
@@ -85,7 +108,7 @@ int split_k_waves(int64_t rows, int64_t K)
 {
     const int64_t n_tiles = (rows + qgl::kTileRows - 1) / qgl::kTileRows;
     const int64_t nseg = (K / 32 + qgl::kSegBlocks - 1) / qgl::kSegBlocks;
-    const int64_t forced = env_int("QG_SPLIT_K", 0);
+    const int64_t forced = tune(kSplitK);
     if (forced == 1 || forced == 2 || forced == 4 || forced == 8) return forced <= nseg ? (int)forced : 1;
     int W = 1;
     while (W < 4 && 2 * W <= nseg && n_tiles * W < 2048) W *= 2;
@@ -95,17 +118,18 @@ int split_k_waves(int64_t rows, int64_t K)
 constexpr size_t kLdsLimit = 96 * 1024;        // single-row calls: above this, x is read from global memory
 constexpr size_t kLdsLimitMulti = 160 * 1024;  // verify calls: the whole LDS of a CU (gfx950)
 
-// Launch shape (measured on MI355X with cold weights):
-//  - tiles per group: 1, or 2 for very tall matrices (>= 24K row tiles);
+// Launch shape of the one-wavefront-per-tile form (measured on MI355X with
+// cold weights):
+//  - one row tile per group of W wavefronts;
 //  - 4 wavefronts per workgroup share one LDS copy of the activations, fewer
 //    only when there are too few groups to cover the CUs;
 //  - for M = 1, activations are staged in LDS when a workgroup streams at least
 //    4x as many weight bytes as it stages, otherwise read from global memory
 //    (L2); with several activation rows (verify) each staged value is reused
 //    M times per weight, so LDS is used whenever it fits.
-// Tuning overrides (read on every call): QG_TILES_PER_GROUP, QG_WAVES_PER_WG
-// (split 1 only), QG_X_GLOBAL (0/1), QG_PREFETCH (1/2). None of them changes a
-// row's operations.
+// The overrides QG_TILES_PER_GROUP, QG_WAVES_PER_WG (split 1 only),
+// QG_X_GLOBAL (0/1) and QG_PREFETCH (1/2) change none of a row's operations.
+
 // CUs of the current device (cached per device); 256, the MI355X count, when
 // no device answers (host-only planning).
 int cu_count()
@@ -137,7 +161,7 @@ bool plan_persist(int64_t rows, int64_t K, int64_t *ranges, int64_t *grid, int64
 {
     const int64_t n_tiles = (rows + qgl::kTileRows - 1) / qgl::kTileRows;
     const int64_t nseg = (K / 32 + qgl::kSegBlocks - 1) / qgl::kSegBlocks;
-    const int64_t forced = env_int("QG_PERSIST", -1);
+    const int64_t forced = tune(kPersist);
     if (forced == 0 || (forced != 1 && (n_tiles >= kPersistTiles || n_tiles * nseg < kPersistUnits))) return false;
     *grid = std::min<int64_t>(cu_count(), n_tiles);
     *max_tiles = (n_tiles + *grid - 1) / *grid;
@@ -153,7 +177,7 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M)
     qgk::QPlan p;
     const Geometry g = qgl::geometry(qt, rows, K);
     const size_t xbytes = (size_t)M * (size_t)g.nseg * qgl::kSegWeights * sizeof(float);
-    const int64_t xg_env = env_int("QG_X_GLOBAL", -1);
+    const int64_t xg_env = tune(kXGlobal);
     int64_t ranges = 1, pgrid = 0, max_tiles = 0;
     p.persist = plan_persist(rows, K, &ranges, &pgrid, &max_tiles);
     p.depth = 1;
@@ -177,7 +201,7 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M)
     // One row tile per group: many short, independent wavefronts, which the
     // hardware dispatcher balances across the CUs better than longer chains
     // (measured on both LM-head shapes).
-    const int64_t tpg_env = env_int("QG_TILES_PER_GROUP", 0);
+    const int64_t tpg_env = tune(kTilesPerGroup);
     if (tpg_env > 0) p.tpg = tpg_env;
     const int64_t groups = (g.n_tiles + p.tpg - 1) / p.tpg;
     const size_t lds_limit = M > 1 ? kLdsLimitMulti : kLdsLimit;
@@ -190,7 +214,7 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M)
         // a verify call whose activations take more than half the LDS runs one
         // workgroup per CU: give it 8 wavefronts
         if (M > 1 && xbytes > 80 * 1024 && xbytes <= lds_limit && groups >= 2048) G = 8;
-        const int64_t g_env = env_int("QG_WAVES_PER_WG", 0);
+        const int64_t g_env = tune(kWavesPerWg);
         if (g_env == 1 || g_env == 2 || g_env == 4 || g_env == 8) G = (int)g_env;
         p.block = 64 * G;
     }
@@ -203,7 +227,7 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M)
     // Prefetch depth: one unit in flight ahead of the one being computed. A
     // depth of 2 (single-row kernels only) measured no faster on any of the
     // workload shapes and costs registers; it stays reachable for sweeps.
-    const int64_t d_env = env_int("QG_PREFETCH", 0);
+    const int64_t d_env = tune(kPrefetch);
     if (d_env == 1 || d_env == 2) p.depth = (int)d_env;
     return p;
 }
@@ -396,14 +420,14 @@ qg_status gemv_f16_splitk(const void *w_f16, const float *x, float *y, int64_t N
     const int64_t units = p.vec ? K / 8 : K;       // work items along K
     // rows per workgroup: register-block 4 rows when there are plenty of rows
     p.R = N >= 2048 ? 4 : (N >= 512 ? 2 : 1);
-    const int64_t r_env = env_int("QG_F16_ROWS", 0);
+    const int64_t r_env = tune(kF16Rows);
     if (r_env == 1 || r_env == 2 || r_env == 4) p.R = (int)r_env;
     // wavefronts per workgroup: one row per workgroup walks ~5 chunks per lane
     // (measured best for the thin 256 x 5120 and 48 x 5120 matrices); register-
     // blocked rows use ~1-2 chunks per lane. At most 16 wavefronts.
     int64_t waves = p.R == 1 ? (units + 319) / 320 : (units + 63) / 64;
     if (p.R >= 2) waves = (waves + 1) / 2;
-    const int64_t w_env = env_int("QG_F16_WAVES", 0);
+    const int64_t w_env = tune(kF16Waves);
     if (w_env > 0) waves = w_env;
     if (waves > 16) waves = 16;
     if (waves < 1) waves = 1;
@@ -439,6 +463,12 @@ qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int *split_k_ways
     if (workgroups) *workgroups = p.grid;
     if (x_in_lds) *x_in_lds = p.x_in_lds ? 1 : 0;
     if (persistent) *persistent = p.persist ? 1 : 0;
+    return ok();
+}
+
+qg_status qg_reload_tuning(void)
+{
+    load_tuning();
     return ok();
 }
 

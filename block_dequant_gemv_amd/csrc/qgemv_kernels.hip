@@ -247,20 +247,47 @@ __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][
 // chunk i = seg*256 + jj*8 + c of the row holds x[4i .. 4i+3] (zero past K;
 // K % 32 == 0, so a chunk is wholly inside K or wholly past it). Indexing is
 // 32-bit shifts and masks (the staged area is at most LDS-sized); each thread
-// issues its global loads in batches of 4 before writing LDS. The caller
+// issues its global loads in batches of 4 before writing LDS.
+//
+// The first batch of row 0 is split off (stage_x_issue): a kernel issues it
+// before its first weight loads, so that the few activation lines reach the
+// memory queues ahead of the weight stream instead of behind it, and writes it
+// (stage_x_finish, which also stages the rest) after them. The caller
 // synchronises the workgroup afterwards.
+struct XFirst {
+    f32x4 v[4];
+};
+
+__device__ __forceinline__ uint32_t x_slot(uint32_t i) { return (i & ~255u) | ((i & 7u) << 5) | ((i >> 3) & 31u); }
+
+__device__ __forceinline__ void stage_x_issue(XFirst &f, const float *__restrict__ x, int64_t K)
+{
+    const uint32_t k4 = (uint32_t)(K >> 2);
+    const uint32_t nthr = blockDim.x, tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t i = tid + q * nthr;
+        f.v[q] = i < k4 ? *(const f32x4 *)(x + 4 * (size_t)i) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+}
+
 template <int M>
-__device__ __forceinline__ void stage_x(f32x4 *xs4, const float *__restrict__ x, int64_t x_stride, int64_t nseg,
-                                        int64_t K)
+__device__ __forceinline__ void stage_x_finish(const XFirst &f, f32x4 *xs4, const float *__restrict__ x,
+                                               int64_t x_stride, int64_t nseg, int64_t K)
 {
     const uint32_t per_m = (uint32_t)nseg << 8;
     const uint32_t k4 = (uint32_t)(K >> 2);
     const uint32_t nthr = blockDim.x, tid = threadIdx.x;
 #pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t i = tid + q * nthr;
+        if (i < per_m) xs4[x_slot(i)] = f.v[q];
+    }
+#pragma unroll
     for (int m = 0; m < M; ++m) {
         const float *xm = x + (int64_t)m * x_stride;
         f32x4 *dst = xs4 + (uint32_t)m * per_m;
-        for (uint32_t base = tid; base < per_m; base += 4 * nthr) {
+        for (uint32_t base = tid + (m == 0 ? 4 * nthr : 0u); base < per_m; base += 4 * nthr) {
             f32x4 v[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -270,7 +297,7 @@ __device__ __forceinline__ void stage_x(f32x4 *xs4, const float *__restrict__ x,
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const uint32_t i = base + q * nthr;
-                if (i < per_m) dst[(i & ~255u) | ((i & 7u) << 5) | ((i >> 3) & 31u)] = v[q];
+                if (i < per_m) dst[x_slot(i)] = v[q];
             }
         }
     }
@@ -364,6 +391,8 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
             ++tt;
         }
     };
+    XFirst xf;
+    if (XLDS) stage_x_issue(xf, x, K);
     Unit<QT> ring[S];
 #pragma unroll
     for (int r = 0; r < D; ++r) {
@@ -373,7 +402,7 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
     }
 
     if (XLDS) {
-        stage_x<M>(xs4, x, a.x_stride, nseg, K);
+        stage_x_finish<M>(xf, xs4, x, a.x_stride, nseg, K);
         __syncthreads();
     }
     if (n_units == 0) return;   // uniform across the workgroup when W > 1
@@ -514,13 +543,15 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
     cu = ld;
     int64_t u_ld = 0;
 
+    XFirst xf;
+    if (XLDS) stage_x_issue(xf, x, K);
     Unit<QT> ring[S];
     load_unit<QT>(ring[0], wp, g, ld.t, ld.s, lp, u_ld < n_units);
     advance(ld);
     ++u_ld;
 
     if (XLDS) {
-        stage_x<M>(xs4, x, a.x_stride, nseg, K);
+        stage_x_finish<M>(xf, xs4, x, a.x_stride, nseg, K);
         __syncthreads();
     }
 

@@ -146,6 +146,16 @@ const char *qg_last_error(void);
 qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int *split_k_ways,
                        int64_t *workgroups, int *x_in_lds, int *persistent);
 
+/* Re-read the launch-shape overrides (QG_SPLIT_K, QG_PERSIST, QG_X_GLOBAL,
+ * QG_TILES_PER_GROUP, QG_WAVES_PER_WG, QG_PREFETCH, QG_F16_ROWS, QG_F16_WAVES)
+ * from the environment. They exist for launch-shape sweeps and tests and are
+ * read once, at the first call that plans a launch; the GEMV calls themselves
+ * read no environment. An override that changes a matrix's K split (QG_SPLIT_K,
+ * QG_PERSIST) changes its rows' rounding, so it must hold for the decode and
+ * the verify call alike. Not safe to call while another thread plans a launch
+ * with different overrides in effect. Returns QG_OK. */
+qg_status qg_reload_tuning(void);
+
 /* Time the next GEMV kernel (qgemv_q8_0, qgemv_q4_0, gemv_f16_splitk,
  * qgemv_fused_gateup_silu or qgemv_verify) that the calling thread launches.
  * start_event and stop_event are hipEvent_t handles, created by the caller

@@ -29,6 +29,7 @@ def _set(**kw):
         os.environ.pop(k, None)
     for k, v in kw.items():
         os.environ[k] = str(v)
+    qg.qg_reload_tuning()   # the library reads the overrides once, and on request
 
 
 @pytest.mark.parametrize("kind,N,K", [("q4_0", 203, 8192 + 96), ("q8_0", 77, 3072), ("q4_0", 1000, 1024)])

@@ -14,9 +14,13 @@ pytestmark = pytest.mark.gpu
 
 # (N, K): single block; under one tile; exactly one tile; a tile + 1 row; ragged
 # last segment; several segments; 3 segments (split 2 ways); c0 shape; 160
-# blocks per row; 17 segments (split 4 ways); activations too large for LDS.
+# blocks per row; 17 segments (split 4 ways); activations too large for LDS;
+# then two shapes that the planner gives the persistent form (>= 2048 tile x
+# segment units under 4096 tiles): 251 tiles with a ragged last row tile and a
+# ragged 3-block last segment (9 ranges, fewer tiles than CUs), and 413 tiles
+# of 5 segments (two tiles on some workgroups).
 SHAPES = [(1, 32), (7, 64), (8, 1024), (9, 1056), (33, 2080), (100, 3072), (1024, 1024), (257, 5120),
-          (640, 17408), (24, 32768), (50, 25632)]
+          (640, 17408), (24, 32768), (50, 25632), (2001, 8288), (3300, 5120)]
 
 
 @pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
@@ -98,7 +102,7 @@ def test_q8_0_full_int8_range_and_zero_scales():
 
 
 @pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
-@pytest.mark.parametrize("N_ff,K", [(1, 32), (7, 1056), (3072, 1024), (300, 5120), (100, 17408)])
+@pytest.mark.parametrize("N_ff,K", [(1, 32), (7, 1056), (3072, 1024), (300, 5120), (100, 17408), (2101, 5120)])
 def test_fused_gateup_silu_matches_oracle(kind, N_ff, K):
     rng = np.random.default_rng(77 + N_ff + K)
     gate = W.matrix(kind, N_ff, K, rng)

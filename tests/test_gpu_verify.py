@@ -10,9 +10,11 @@ from gpu_helpers import THREADS, announce, assert_linear, empty_f32, sync, to_de
 
 pytestmark = pytest.mark.gpu
 
-# the verify configuration's two weights, plus ragged / split-K / large-K shapes
+# the verify configuration's two weights, plus ragged / split-K / large-K shapes,
+# and two more shapes of the persistent form (the first weight is one too)
 CASES = [("q4_0", 17408, 5120), ("q8_0", 4096, 1024), ("q8_0", 33, 2080), ("q4_0", 9, 1056),
-         ("q4_0", 640, 17408), ("q8_0", 100, 3072), ("q4_0", 24, 32768)]
+         ("q4_0", 640, 17408), ("q8_0", 100, 3072), ("q4_0", 24, 32768), ("q4_0", 3300, 5120),
+         ("q8_0", 2001, 8288)]
 
 
 @pytest.mark.parametrize("kind,N,K", CASES)

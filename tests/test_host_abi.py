@@ -140,6 +140,18 @@ def test_plan_info_split_is_independent_of_m(L):
     assert p["persistent"] and p["split_k_ways"] > 1 and 17 % p["split_k_ways"] == 0
 
 
+def test_tuning_overrides_are_read_on_reload(L, monkeypatch):
+    # the launch-shape overrides are read once and on qg_reload_tuning(), not per call
+    assert qg.qg_plan_info("q4_0", 5120, 17408)["persistent"]
+    monkeypatch.setenv("QG_PERSIST", "0")
+    assert qg.qg_plan_info("q4_0", 5120, 17408)["persistent"]        # not re-read yet
+    qg.qg_reload_tuning()
+    assert not qg.qg_plan_info("q4_0", 5120, 17408)["persistent"]
+    monkeypatch.delenv("QG_PERSIST")
+    qg.qg_reload_tuning()
+    assert qg.qg_plan_info("q4_0", 5120, 17408)["persistent"]
+
+
 SHAPES = [(1, 32), (3, 64), (8, 1024), (9, 1056), (17, 2048), (24, 3104), (5, 5120)]
 
 
