@@ -124,7 +124,7 @@ constexpr size_t kLdsLimitMulti = 160 * 1024;  // verify calls: the whole LDS of
 //  - 4 wavefronts per workgroup share one LDS copy of the activations, fewer
 //    only when there are too few groups to cover the CUs;
 //  - for M = 1, activations are staged in LDS when a workgroup streams at least
-//    4x as many weight bytes as it stages, otherwise read from global memory
+//    2x as many weight bytes as it stages, otherwise read from global memory
 //    (L2); with several activation rows (verify) each staged value is reused
 //    M times per weight, so LDS is used whenever it fits.
 // The overrides QG_TILES_PER_GROUP, QG_WAVES_PER_WG (split 1 only),
@@ -220,7 +220,7 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M)
     }
     p.grid = (groups + G - 1) / G;
     const double wg_weight_bytes = (double)G * (double)p.tpg * (double)(g.tile_q + g.tile_s);
-    bool lds = xbytes <= lds_limit && (M > 1 || wg_weight_bytes >= 4.0 * (double)xbytes);
+    bool lds = xbytes <= lds_limit && (M > 1 || wg_weight_bytes >= 2.0 * (double)xbytes);
     if (xg_env == 0 || xg_env == 1) lds = xbytes <= lds_limit && xg_env == 0;
     p.x_in_lds = lds;
     p.lds_bytes = p.x_in_lds ? xbytes : 0;

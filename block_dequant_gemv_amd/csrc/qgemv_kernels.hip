@@ -353,11 +353,8 @@ __device__ __forceinline__ void store_tile(const float (&acc)[M][kRowsPerLane], 
 //         the W partial sums are combined in LDS in wavefront order.
 // Each wavefront walks its (tile, segment) sequence with the loads of the next
 // D units in flight while the current one is computed (a ring of D+1 units).
-#ifndef QG_WAVES_PER_EU
-#define QG_WAVES_PER_EU 1
-#endif
 template <int QT, int M, int EPI, int W, bool XLDS, int D>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QG_WAVES_PER_EU)))
+__global__ void __launch_bounds__(512)
 qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float *__restrict__ y, QArgs a)
 {
     constexpr int B = kRowsPerLane;
