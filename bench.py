@@ -111,18 +111,21 @@ def build_step(qg, torch, wl, stream, copies):
     ys = {n: torch.empty(v, dtype=torch.float32, device=dev) for n, v in ys.items()}
     sets = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(copies - 1)]
     torch.cuda.synchronize()
-    steps = []
-    for s in sets:
-        steps.append([
-            make_qgemv(qg, "q8_0", s["qkv"], xs["qkv"], ys["qkv"], 4096, 1024, stream, "qkv 4096x1024"),
-            make_qgemv(qg, "q8_0", s["o"], xs["o"], ys["o"], 1024, 2048, stream, "o_proj 1024x2048"),
-            make_gateup(qg, "q8_0", s["gateup"], xs["gateup"], ys["gateup"], 3072, 1024, stream,
-                        "gate|up 2x3072x1024 silu"),
-            make_qgemv(qg, "q8_0", s["down"], xs["down"], ys["down"], 1024, 3072, stream, "down 1024x3072"),
-            make_qgemv(qg, "q8_0", s["lm_head"], xs["lm_head"], ys["lm_head"], 151936, 1024, stream,
-                       "lm_head 151936x1024"),
-        ])
+    steps = [step_calls(qg, s, xs, ys, stream) for s in sets]
     return steps, sets, xs, ys
+
+
+def step_calls(qg, s, xs, ys, stream):
+    """The five calls of one decode step on weight set `s`, launched on `stream`."""
+    return [
+        make_qgemv(qg, "q8_0", s["qkv"], xs["qkv"], ys["qkv"], 4096, 1024, stream, "qkv 4096x1024"),
+        make_qgemv(qg, "q8_0", s["o"], xs["o"], ys["o"], 1024, 2048, stream, "o_proj 1024x2048"),
+        make_gateup(qg, "q8_0", s["gateup"], xs["gateup"], ys["gateup"], 3072, 1024, stream,
+                    "gate|up 2x3072x1024 silu"),
+        make_qgemv(qg, "q8_0", s["down"], xs["down"], ys["down"], 1024, 3072, stream, "down 1024x3072"),
+        make_qgemv(qg, "q8_0", s["lm_head"], xs["lm_head"], ys["lm_head"], 151936, 1024, stream,
+                   "lm_head 151936x1024"),
+    ]
 
 
 def timing_events(torch, n):

@@ -744,6 +744,20 @@ void set_launch_events(hipEvent_t start, hipEvent_t stop)
     t_ev_stop = stop;
 }
 
+// Launch `kern` on `stream`: with timing events bound, through hipExtLaunchKernel
+// (the events take the dispatch's start and end times); otherwise as a plain
+// launch, which a caller may also record into a HIP graph.
+template <typename Kern, typename... Args>
+static void launch(Kern kern, dim3 grid, dim3 block, uint32_t lds, hipStream_t stream, Args... args)
+{
+    hipEvent_t e0, e1;
+    take_launch_events(e0, e1);
+    if (e0 != nullptr)
+        hipExtLaunchKernelGGL(kern, grid, block, lds, stream, e0, e1, 0u, args...);
+    else
+        hipLaunchKernelGGL(kern, grid, block, lds, stream, args...);
+}
+
 template <int QT, int M, int EPI, int W, bool XLDS, int D>
 static hipError_t launch_q(const uint8_t *wp, const float *x, float *y, const QArgs &a, int64_t grid, int block,
                            size_t lds, hipStream_t stream)
@@ -753,9 +767,7 @@ static hipError_t launch_q(const uint8_t *wp, const float *x, float *y, const QA
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipEvent_t e0, e1;
-    take_launch_events(e0, e1);
-    hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(block), (uint32_t)lds, stream, e0, e1, 0u, wp, x, y, a);
+    launch(kern, dim3((unsigned)grid), dim3(block), (uint32_t)lds, stream, wp, x, y, a);
     return hipGetLastError();
 }
 
@@ -796,10 +808,7 @@ static hipError_t launch_persist(const uint8_t *wp, const float *x, float *y, co
             hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_bytes);
         if (e != hipSuccess) return e;
     }
-    hipEvent_t e0, e1;
-    take_launch_events(e0, e1);
-    hipExtLaunchKernelGGL(kern, dim3((unsigned)p.grid), dim3(p.block), (uint32_t)p.lds_bytes, stream, e0, e1, 0u,
-                          wp, x, y, a);
+    launch(kern, dim3((unsigned)p.grid), dim3(p.block), (uint32_t)p.lds_bytes, stream, wp, x, y, a);
     return hipGetLastError();
 }
 
@@ -837,9 +846,7 @@ hipError_t launch_f16(const F16Plan &p, const uint16_t *w, const float *x, float
                       hipStream_t s)
 {
     const dim3 grid((unsigned)p.grid), block(p.waves * 64);
-    hipEvent_t e0, e1;
-    take_launch_events(e0, e1);
-    auto go = [&](auto kern) { hipExtLaunchKernelGGL(kern, grid, block, 0u, s, e0, e1, 0u, w, x, y, N, K); };
+    auto go = [&](auto kern) { launch(kern, grid, block, 0u, s, w, x, y, N, K); };
     if (p.vec) {
         switch (p.R) {
         case 1: go(gemv_f16_kernel<1, true>); break;
