@@ -65,6 +65,8 @@ def _declare(L):
     L.oracle_gateup_silu.argtypes = [i32, vp, vp, fp, dp, dp, dp, dp, dp, i64, i64, i32]
     L.oracle_gateup_silu.restype = i32
     L.oracle_verify.argtypes = [i32, vp, fp, dp, dp, i64, i64, i32, i32]
+    L.oracle_gemv_epilogue.argtypes = [i32, vp, fp, fp, fp, dp, dp, i64, i64, i32]
+    L.oracle_gemv_epilogue.restype = i32
     L.oracle_verify.restype = i32
     return L
 
@@ -136,6 +138,28 @@ def gateup_silu(kind, gate: np.ndarray, up: np.ndarray, x: np.ndarray, N_ff: int
     return out, g, u, ag, au
 
 
+def gemv_epilogue(kind, w: np.ndarray, x: np.ndarray, N: int, K: int, bias=None, residual=None,
+                  threads: int = 1, L=None):
+    """out[n] = sum_k W[n][k] x[k] + bias[n] + residual[n] (either may be None); also the
+    product's magnitude sums."""
+    L = L or lib()
+    k = _kind(kind)
+    w = _check_w(k, w, N, K)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    r = None if residual is None else np.ascontiguousarray(residual, dtype=np.float32)
+    for v in (b, r):
+        if v is not None and v.shape != (N,):
+            raise ValueError("bias and residual must have N entries")
+    out = np.empty(N, np.float64)
+    a = np.empty(N, np.float64)
+    rc = L.oracle_gemv_epilogue(k, _ptr(w), _ptr(x), None if b is None else _ptr(b), None if r is None else _ptr(r),
+                                _ptr(out), _ptr(a), N, K, threads)
+    if rc:
+        raise ValueError("oracle_gemv_epilogue rejected its arguments")
+    return out, a
+
+
 def verify(kind, w: np.ndarray, X: np.ndarray, N: int, K: int, threads: int = 1, L=None):
     """Y[m] = W X[m] for each activation row m (each row is its own M=1 product)."""
     L = L or lib()
@@ -164,6 +188,21 @@ def silu(g: float, L=None) -> float:
 def linear_tol(a: np.ndarray) -> np.ndarray:
     """|y_gpu - y_ref| <= 1e-5 * sum_k |w_k x_k| + 1e-7 for every linear output."""
     return 1e-5 * a + 1e-7
+
+
+def epilogue_tol(a: np.ndarray, bias=None, residual=None, out=None, f16: bool = False) -> np.ndarray:
+    """Bound for an epilogue output: the linear bound widened by the magnitudes of
+    the fp32 addends (each addition rounds once in fp32), plus, for an fp16
+    output, the fp16 rounding of the fp32 value (at most 2^-11 of its magnitude,
+    or 2^-25 in the subnormal range)."""
+    mag = np.asarray(a, np.float64).copy()
+    for v in (bias, residual):
+        if v is not None:
+            mag = mag + np.abs(np.asarray(v, np.float64))
+    tol = linear_tol(mag)
+    if f16:
+        tol = tol + 2.0 ** -11 * (np.abs(np.asarray(out, np.float64)) + tol) + 2.0 ** -25
+    return tol
 
 
 def silu_tol(g: np.ndarray, u: np.ndarray, ag: np.ndarray, au: np.ndarray, out: np.ndarray) -> np.ndarray:

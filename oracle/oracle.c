@@ -26,6 +26,12 @@
  *    parity gate. This file is that reference for the GEMV.
  *  - RunIT_Mac README, "Fused gate+up+silu": the gate and up projections and
  *    the SiLU product are one step; out = silu(gate) * up.
+ *  - RunIT_Mac README, optimisation table and data-flow figure: the fused QKV
+ *    projection adds its bias in the same dispatch ("Fused QKV+bias"), and the
+ *    model keeps an f32 residual stream that projections add into;
+ *    robotnurse.io "We wrote our own inference engine", "What actually moved
+ *    it", item 5: some GEMVs write fp16 outputs. oracle_gemv_epilogue is the
+ *    product followed by those additions, in double.
  *
  * Readings where the pages are silent (each is also listed in the design notes):
  *  - Block field order is the GGUF one: little-endian fp16 scale first, then
@@ -217,6 +223,26 @@ int oracle_verify(int kind, const void *w, const float *X, double *Y, double *A,
         int rc = oracle_gemv(kind, w, X + (int64_t)m * K, Y + (int64_t)m * N,
                              A ? A + (int64_t)m * N : NULL, N, K, nthreads);
         if (rc) return rc;
+    }
+    return 0;
+}
+
+/* Epilogue variants of the product: out[n] = y[n] + bias[n] + residual[n], in
+ * double, with either addend absent when its pointer is NULL. An fp16 output
+ * is not rounded here: the oracle keeps the exact value and the tests bound
+ * the fp16 rounding on top of the linear tolerance. a[n] is the product's
+ * magnitude sum, as for oracle_gemv. */
+int oracle_gemv_epilogue(int kind, const void *w, const float *x, const float *bias, const float *residual,
+                         double *out, double *a, int64_t N, int64_t K, int threads)
+{
+    int rc = oracle_gemv(kind, w, x, out, a, N, K, threads);
+    if (rc)
+        return rc;
+    for (int64_t n = 0; n < N; ++n) {
+        if (bias)
+            out[n] += (double)bias[n];
+        if (residual)
+            out[n] += (double)residual[n];
     }
     return 0;
 }

@@ -278,6 +278,38 @@ def pin_composites(L):
         assert np.array_equal(yt, gy) and np.array_equal(at, ga)
 
 
+def pin_epilogue(L):
+    # the epilogue adds bias and residual to the product: with every scale zero the
+    # product is exactly 0 and the output is bias + residual (an exact double sum
+    # of two fp32 values); on the worked single block E1 (product -8) a bias of
+    # 0.5 and a residual of 0.25 give -7.25; with neither the plain product results
+    rng = np.random.default_rng(31)
+    for kind in ("q8_0", "q4_0"):
+        N, K = 7, 96
+        w = W.matrix(kind, N, K, rng)
+        bb = W.Q8_0_BLOCK_BYTES if kind == "q8_0" else W.Q4_0_BLOCK_BYTES
+        wz = w.reshape(N, K // 32, bb).copy()
+        wz[:, :, 0:2] = 0                          # scale fields: fp16 +0
+        wz = wz.reshape(-1)
+        x = rng.standard_normal(K).astype(np.float32)
+        b = rng.standard_normal(N).astype(np.float32)
+        r = rng.standard_normal(N).astype(np.float32)
+        out, a = O.gemv_epilogue(kind, wz, x, N, K, bias=b, residual=r, L=L)
+        assert np.array_equal(out, b.astype(np.float64) + r.astype(np.float64)) and np.all(a == 0.0)
+        out, _ = O.gemv_epilogue(kind, wz, x, N, K, bias=b, L=L)
+        assert np.array_equal(out, b.astype(np.float64))
+        out, _ = O.gemv_epilogue(kind, wz, x, N, K, residual=r, L=L)
+        assert np.array_equal(out, r.astype(np.float64))
+        y0, a0 = _gemv(L, kind, w, x, N, K)
+        out, a = O.gemv_epilogue(kind, w, x, N, K, L=L)
+        assert np.array_equal(out, y0) and np.array_equal(a, a0)
+    e1 = _u8(q8_block(0x3800, [i - 16 for i in range(32)]))
+    ones = np.ones(32, np.float32)
+    out, _ = O.gemv_epilogue("q8_0", e1, ones, 1, 32, bias=np.array([0.5], np.float32),
+                             residual=np.array([0.25], np.float32), L=L)
+    assert out[0] == -7.25, out
+
+
 def pin_rejects_bad_shapes(L):
     w = np.zeros(34, np.uint8)
     x = np.zeros(33, np.float32)
@@ -298,6 +330,7 @@ PINS = [
     pin_textbook,
     pin_invariants,
     pin_composites,
+    pin_epilogue,
     pin_rejects_bad_shapes,
 ]
 

@@ -36,6 +36,9 @@ MUTANTS = {
     "x_index_shifted": ("double p = wk * (double)x[k];", "double p = wk * (double)x[(k + 1) % K];"),
     "sign_bit_ignored": ("return sign ? -v : v;", "return v;"),
     "scale_byte_order": ("(uint16_t)(p[0] | (p[1] << 8))", "(uint16_t)(p[1] | (p[0] << 8))"),
+    "bias_dropped": ("out[n] += (double)bias[n];", "out[n] += 0.0;"),
+    "residual_subtracted": ("out[n] += (double)residual[n];", "out[n] -= (double)residual[n];"),
+    "residual_for_bias": ("out[n] += (double)bias[n];", "out[n] += (double)residual[n];"),
 }
 
 
