@@ -87,6 +87,17 @@ def make_verify(qg, kind, packed, X, Y, N, K, M, stream, label):
                 qkernel_name(qg, kind, N, K, M), packed, make)
 
 
+def make_epilogue(qg, kind, packed, x, bias, res, y, N, K, stream, label):
+    """qgemv_epilogue: y = ((W x) + bias) + residual, fp32 or fp16 (y's dtype)."""
+    out16 = y.element_size() == 2
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    make = lambda wp: qg.bound_call("qgemv_epilogue", qg.QTYPES[kind], wp, x.data_ptr(), ptr(bias),  # noqa: E731
+                                    ptr(res), y.data_ptr(), qg.QG_OUT_F16 if out16 else qg.QG_OUT_F32, N, K,
+                                    stream)
+    nbytes = wbytes(kind, N, K) + 4 * K + (2 if out16 else 4) * N + 4 * N * ((bias is not None) + (res is not None))
+    return Call(label, make(packed.data_ptr()), nbytes, qkernel_name(qg, kind, N, K, epi="affine"), packed, make)
+
+
 def make_f16(qg, w, x, y, N, K, stream, label):
     make = lambda wp: qg.bound_call("gemv_f16_splitk", wp, x.data_ptr(), y.data_ptr(), N, K, stream)  # noqa: E731
     return Call(label, make(w.data_ptr()), 2 * N * K + 4 * K + 4 * N, "gemv_f16", w, make)
@@ -191,7 +202,8 @@ def per_config_calls(qg, torch, stream, step_calls):
 
     res[1] = [Call("c1 " + c.label, c.fn, c.nbytes, c.kernel, c.weight, c.make) for c in step_calls]
 
-    wl = Workload(2)
+    wl1 = Workload(1)
+    wl = wl2 = Workload(2)
     pg = qg.pack_gateup("q4_0", wl.weight("gate"), wl.weight("up"), 17408, 5120)
     wl.drop("gate")
     wl.drop("up")
@@ -224,6 +236,26 @@ def per_config_calls(qg, torch, stream, step_calls):
                                  f"c4 {kind} {N}x{K} M=1"))
         for M in range(2, 7):
             res[4].append(make_verify(qg, kind, pw, X, yb(M * N), N, K, M, stream, f"c4 {kind} {N}x{K} M={M}"))
+    # epilogue variants (qgemv_epilogue) on weights of the configurations above:
+    # the fused QKV with its bias, the O projection added into the residual stream
+    # in place, the Q4_0 down projection with a residual, the LM head writing fp16
+    erng = np.random.default_rng(5)
+    by = {c.label: c for c in step_calls}
+    qkv, o, lm = by["qkv 4096x1024"], by["o_proj 1024x2048"], by["lm_head 151936x1024"]
+    vec = lambda n: t((0.5 * erng.standard_normal(n)).astype(np.float32))  # noqa: E731
+    y_o = t(erng.standard_normal(1024).astype(np.float32))
+    y16 = torch.empty(151936, dtype=torch.float16, device=dev)
+    keep.append(y16)
+    res[5] = [
+        make_epilogue(qg, "q8_0", qkv.weight, t(wl1.x("q_proj")), vec(4096), None, yb(4096), 4096, 1024, stream,
+                      "e q8_0 qkv 4096x1024 +bias"),
+        make_epilogue(qg, "q8_0", o.weight, t(wl1.x("o_proj")), None, y_o, y_o, 1024, 2048, stream,
+                      "e q8_0 o_proj 1024x2048 +=residual"),
+        make_epilogue(qg, "q4_0", pd, t(wl2.x("down")), None, vec(5120), yb(5120), 5120, 17408, stream,
+                      "e q4_0 down 5120x17408 +residual"),
+        make_epilogue(qg, "q8_0", lm.weight, t(wl1.x("lm_head")), None, None, y16, 151936, 1024, stream,
+                      "e q8_0 lm_head 151936x1024 fp16 out"),
+    ]
     torch.cuda.synchronize()
     return res, keep
 

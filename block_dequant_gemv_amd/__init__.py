@@ -20,6 +20,7 @@ Q4_0 = 2
 QTYPES = {"q8_0": Q8_0, "q4_0": Q4_0}
 
 QG_OK, QG_EINVAL, QG_EALIGN, QG_EUNSUPPORTED, QG_EHIP = range(5)
+QG_OUT_F32, QG_OUT_F16 = 0, 1
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemv.so")
 
@@ -27,7 +28,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemv.so
 SYMBOLS = (
     "qg_packed_size", "qg_pack", "qg_pack_rows", "qg_pack_gateup",
     "qg_pack_host", "qg_unpack_host", "qg_pack_gateup_host",
-    "qgemv_q8_0", "qgemv_q4_0", "gemv_f16_splitk", "qgemv_fused_gateup_silu", "qgemv_verify",
+    "qgemv_q8_0", "qgemv_q4_0", "qgemv_epilogue", "gemv_f16_splitk", "qgemv_fused_gateup_silu", "qgemv_verify",
     "qg_status_str", "qg_last_error", "qg_plan_info", "qg_time_next_launch", "qg_reload_tuning",
 )
 
@@ -67,6 +68,7 @@ def lib():
             "qg_pack_gateup_host": ([i32, vp, vp, vp, i64, i64], i32),
             "qgemv_q8_0": ([vp, vp, vp, i64, i64, vp], i32),
             "qgemv_q4_0": ([vp, vp, vp, i64, i64, vp], i32),
+            "qgemv_epilogue": ([i32, vp, vp, vp, vp, vp, i32, i64, i64, vp], i32),
             "gemv_f16_splitk": ([vp, vp, vp, i64, i64, vp], i32),
             "qgemv_fused_gateup_silu": ([i32, vp, vp, vp, i64, i64, vp], i32),
             "qgemv_verify": ([i32, vp, vp, vp, i64, i64, i32, vp], i32),
@@ -181,6 +183,18 @@ def qgemv_q8_0(w_packed, x, y, N: int, K: int, stream=None):
 def qgemv_q4_0(w_packed, x, y, N: int, K: int, stream=None):
     _check("qgemv_q4_0", lib().qgemv_q4_0(_dev(w_packed, "w_packed"), _dev(x, "x", _f32()), _dev(y, "y", _f32()),
                                           N, K, _stream(stream)))
+
+
+def qgemv_epilogue(qtype, w_packed, x, y, N: int, K: int, bias=None, residual=None, stream=None):
+    """y = ((W x) + bias) + residual; y's dtype (float32 or float16) selects the output type."""
+    import torch
+    if y.dtype not in (torch.float32, torch.float16):
+        raise ValueError(f"y must be float32 or float16, got {y.dtype}")
+    out_type = QG_OUT_F16 if y.dtype == torch.float16 else QG_OUT_F32
+    _check("qgemv_epilogue",
+           lib().qgemv_epilogue(_qtype(qtype), _dev(w_packed, "w_packed"), _dev(x, "x", _f32()),
+                                _dev(bias, "bias", _f32()), _dev(residual, "residual", _f32()), _dev(y, "y"),
+                                out_type, N, K, _stream(stream)))
 
 
 def gemv_f16_splitk(w_f16, x, y, N: int, K: int, stream=None):

@@ -234,20 +234,37 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M)
 
 hipStream_t as_stream(void *s) { return (hipStream_t)s; }
 
-qg_status run_qgemv(int qt, int epi, const void *w, const float *x, float *y, int64_t rows, int64_t n_out,
-                    int64_t K, int M, void *stream, const char *fn)
+// Addends and output type of the affine epilogue (kEpiAffine only).
+struct Affine {
+    const float *bias = nullptr;
+    const float *residual = nullptr;
+    int out_type = QG_OUT_F32;
+};
+
+qg_status run_qgemv(int qt, int epi, const void *w, const float *x, void *y, int64_t rows, int64_t n_out,
+                    int64_t K, int M, void *stream, const char *fn, const Affine &af = Affine())
 {
     qg_status st = check_qshape(qt, rows, K, fn);
     if (st) return st;
     if (!w || !x || !y) return fail(QG_EINVAL, "%s: null pointer", fn);
+    if (af.out_type != QG_OUT_F32 && af.out_type != QG_OUT_F16)
+        return fail(QG_EUNSUPPORTED, "%s: unknown output type %d", fn, af.out_type);
+    const bool f16 = af.out_type == QG_OUT_F16;
     if (!aligned(w, 16)) return fail(QG_EALIGN, "%s: packed weights must be 16-byte aligned", fn);
     if (!aligned(x, 16)) return fail(QG_EALIGN, "%s: activations must be 16-byte aligned", fn);
-    if (!aligned(y, 4)) return fail(QG_EALIGN, "%s: output must be 4-byte aligned", fn);
+    if (!aligned(y, f16 ? 2 : 4)) return fail(QG_EALIGN, "%s: output must be %d-byte aligned", fn, f16 ? 2 : 4);
+    if (!aligned(af.bias, 4) || !aligned(af.residual, 4))
+        return fail(QG_EALIGN, "%s: bias and residual must be 4-byte aligned", fn);
     const Geometry g = qgl::geometry(qt, rows, K);
-    const size_t ybytes = (size_t)M * (size_t)n_out * sizeof(float);
+    const size_t ybytes = (size_t)M * (size_t)n_out * (f16 ? 2 : sizeof(float));
     const size_t xbytes = (size_t)M * (size_t)K * sizeof(float);
+    const size_t abytes = (size_t)n_out * sizeof(float);
     if (overlap(y, ybytes, x, xbytes)) return fail(QG_EINVAL, "%s: y overlaps x", fn);
     if (overlap(y, ybytes, w, (size_t)g.total)) return fail(QG_EINVAL, "%s: y overlaps the weights", fn);
+    if (af.bias && overlap(y, ybytes, af.bias, abytes)) return fail(QG_EINVAL, "%s: y overlaps bias", fn);
+    // residual == y (fp32) is the in-place update y += W x; any other overlap is refused
+    if (af.residual && !(af.residual == y && !f16) && overlap(y, ybytes, af.residual, abytes))
+        return fail(QG_EINVAL, "%s: y overlaps residual (only residual == y with fp32 output is allowed)", fn);
 
     const qgk::QPlan p = make_qplan(qt, rows, K, M);
     qgk::QArgs a;
@@ -258,7 +275,10 @@ qg_status run_qgemv(int qt, int epi, const void *w, const float *x, float *y, in
     a.tpg = p.tpg;
     a.n_wg = p.grid;
     a.ranges = p.ranges;
-    hipError_t e = qgk::launch_qgemv(qt, M, epi, p, (const uint8_t *)w, x, y, a, as_stream(stream));
+    a.bias = af.bias;
+    a.residual = af.residual;
+    a.out_f16 = f16 ? 1 : 0;
+    hipError_t e = qgk::launch_qgemv(qt, M, epi, p, (const uint8_t *)w, x, (float *)y, a, as_stream(stream));
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
 }
@@ -386,6 +406,16 @@ qg_status qgemv_q8_0(const void *w_packed, const float *x, float *y, int64_t N, 
 qg_status qgemv_q4_0(const void *w_packed, const float *x, float *y, int64_t N, int64_t K, void *stream)
 {
     return run_qgemv(QG_Q4_0, qgk::kEpiPlain, w_packed, x, y, N, N, K, 1, stream, "qgemv_q4_0");
+}
+
+qg_status qgemv_epilogue(int qtype, const void *w_packed, const float *x, const float *bias, const float *residual,
+                         void *y, int out_type, int64_t N, int64_t K, void *stream)
+{
+    Affine af;
+    af.bias = bias;
+    af.residual = residual;
+    af.out_type = out_type;
+    return run_qgemv(qtype, qgk::kEpiAffine, w_packed, x, y, N, N, K, 1, stream, "qgemv_epilogue", af);
 }
 
 qg_status qgemv_fused_gateup_silu(int qtype, const void *w_gateup_packed, const float *x, float *y, int64_t N_ff,

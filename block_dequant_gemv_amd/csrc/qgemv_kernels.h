@@ -11,6 +11,7 @@ namespace qgk {
 
 constexpr int kEpiPlain = 0;
 constexpr int kEpiGateUp = 1;
+constexpr int kEpiAffine = 2;   // M = 1: y = ((W x) + bias) + residual, fp32 or fp16 output
 constexpr int kPackRows = 0;
 constexpr int kPackGateUp = 1;
 
@@ -24,6 +25,10 @@ struct QArgs {
     // persistent form only
     int64_t n_wg;        // workgroups; workgroup b owns tiles [b*n_tiles/n_wg, (b+1)*n_tiles/n_wg)
     int64_t ranges;      // K ranges per tile (divides nseg); item = (tile, range)
+    // kEpiAffine only (M = 1): fp32 addends (either may be null) and the output type
+    const float *bias;
+    const float *residual;
+    int out_f16;         // 1: y holds fp16 values (round to nearest even), 0: fp32
 };
 
 // How one quantised call is split. W depends only on (qtype, rows, K) so that

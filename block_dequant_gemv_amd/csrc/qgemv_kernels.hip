@@ -303,17 +303,38 @@ __device__ __forceinline__ void stage_x_finish(const XFirst &f, f32x4 *xs4, cons
     }
 }
 
+// Store output n of activation row m (n < n_out). The affine epilogue adds the
+// bias and then the residual to the finished product, one fp32 addition each,
+// and writes fp32 or fp16 (v_cvt_f16_f32, round to nearest even). The residual
+// is read before y[n] is written, so residual == y updates y in place.
+template <int M, int EPI>
+__device__ __forceinline__ void store_out(float *__restrict__ y, const QArgs &a, int m, int64_t n, float v)
+{
+    if (EPI == kEpiAffine) {
+        if (a.bias != nullptr) v = v + a.bias[n];
+        if (a.residual != nullptr) v = v + a.residual[n];
+        if (a.out_f16) {
+            ((_Float16 *)y)[n] = (_Float16)v;
+            return;
+        }
+        y[n] = v;
+    } else {
+        y[m * a.y_stride + n] = v;
+    }
+}
+
 // Write the finished rows of tile t from the lanes of one slot (acc already
 // reduced over the slot's 32 lanes, so every lane holds the sums).
-//   plain:   lane j < M*B stores row b = j % B of activation row m = j / B
-//   gate|up: rows b = 2p (gate) and 2p+1 (up) give output n = row0/2 + p
+//   plain, affine: lane j < M*B stores row b = j % B of activation row m = j / B
+//   gate|up:       rows b = 2p (gate) and 2p+1 (up) give output n = row0/2 + p
 template <int M, int EPI>
-__device__ __forceinline__ void store_tile(const float (&acc)[M][kRowsPerLane], float *__restrict__ y, int64_t n_out,
-                                           int64_t y_stride, int64_t t, int slot, int j)
+__device__ __forceinline__ void store_tile(const float (&acc)[M][kRowsPerLane], float *__restrict__ y, const QArgs &a,
+                                           int64_t t, int slot, int j)
 {
     constexpr int B = kRowsPerLane;
+    const int64_t n_out = a.n_out;
     const int64_t row0 = t * kTileRows + slot * kRowsPerLane;
-    if (EPI == kEpiPlain) {
+    if (EPI != kEpiGateUp) {
         if (j < M * B) {
             float v = 0.0f;
 #pragma unroll
@@ -322,7 +343,7 @@ __device__ __forceinline__ void store_tile(const float (&acc)[M][kRowsPerLane], 
                 for (int b = 0; b < B; ++b)
                     if (j == m * B + b) v = acc[m][b];
             const int m = j / B, b = j % B;
-            if (row0 + b < n_out) y[m * y_stride + row0 + b] = v;
+            if (row0 + b < n_out) store_out<M, EPI>(y, a, m, row0 + b, v);
         }
     } else {
         if (j < B / 2) {
@@ -343,7 +364,8 @@ __device__ __forceinline__ void store_tile(const float (&acc)[M][kRowsPerLane], 
 // Quantised GEMV. Template parameters:
 //   QT   kQ8_0 / kQ4_0
 //   M    activation rows (1 = decode GEMV, 2..6 = verify)
-//   EPI  kEpiPlain (y = W x) or kEpiGateUp (y = silu(gate) * up, M = 1)
+//   EPI  kEpiPlain (y = W x), kEpiGateUp (y = silu(gate) * up, M = 1) or
+//        kEpiAffine (y = ((W x) + bias) + residual, fp32 or fp16, M = 1)
 //   W    wavefronts that split one row tile along K (1, 2, 4 or 8)
 //   XLDS activations staged in LDS (true) or read from global memory
 // W == 1: a workgroup holds blockDim/64 independent wavefronts, wavefront g of
@@ -451,7 +473,7 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
                 }
                 __syncthreads();
             }
-            if (wk == 0) store_tile<M, EPI>(acc, y, a.n_out, a.y_stride, t, slot, j);
+            if (wk == 0) store_tile<M, EPI>(acc, y, a, t, slot, j);
 #pragma unroll
             for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -572,7 +594,7 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
 #pragma unroll
                 for (int b = 0; b < B; ++b) acc[m][b] = half_wave_sum(acc[m][b]);
             if (R == 1) {
-                store_tile<M, EPI>(acc, y, a.n_out, a.y_stride, cu.t, slot, j);
+                store_tile<M, EPI>(acc, y, a, cu.t, slot, j);
             } else if (j == 0) {
                 float *pp = part + ((size_t)(cu.t - T0) * R + cu.r) * (M * kTileRows) + slot * B;
 #pragma unroll
@@ -599,7 +621,7 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
         // every wavefront reaches this barrier (no early exit above)
         __syncthreads();
         const uint32_t ntile = (uint32_t)(T1 - T0);
-        if (EPI == kEpiPlain) {
+        if (EPI != kEpiGateUp) {
             for (uint32_t o = tid; o < ntile * (M * kTileRows); o += blockDim.x) {
                 const uint32_t tl = o / (M * kTileRows), rem = o - tl * (M * kTileRows);
                 const uint32_t m = rem / kTileRows, row = rem - m * kTileRows;
@@ -607,7 +629,7 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
                 float v = pp[0];
                 for (uint32_t r = 1; r < R; ++r) v += pp[(size_t)r * (M * kTileRows)];
                 const int64_t n = (T0 + tl) * kTileRows + row;
-                if (n < a.n_out) y[m * a.y_stride + n] = v;
+                if (n < a.n_out) store_out<M, EPI>(y, a, (int)m, n, v);
             }
         } else {
             for (uint32_t o = tid; o < ntile * (kTileRows / 2); o += blockDim.x) {
@@ -775,8 +797,9 @@ template <int QT, int M, int EPI, int W>
 static hipError_t dispatch_x(const uint8_t *wp, const float *x, float *y, const QArgs &a, int64_t grid, int block,
                              size_t lds, bool xlds, int depth, hipStream_t s)
 {
-    // prefetch depth 2 is instantiated for the single-row kernels only
-    if constexpr (M == 1) {
+    // prefetch depth 2 is instantiated for the single-row kernels without the
+    // affine epilogue only (elsewhere a request for it runs depth 1)
+    if constexpr (M == 1 && EPI != kEpiAffine) {
         if (depth >= 2)
             return xlds ? launch_q<QT, M, EPI, W, true, 2>(wp, x, y, a, grid, block, lds, s)
                         : launch_q<QT, M, EPI, W, false, 2>(wp, x, y, a, grid, block, 0, s);
@@ -825,6 +848,7 @@ static hipError_t dispatch_m(const uint8_t *wp, const float *x, float *y, const 
                              const QPlan &p, hipStream_t s)
 {
     if (epi == kEpiGateUp) return dispatch_form<QT, 1, kEpiGateUp>(wp, x, y, a, p, s);
+    if (epi == kEpiAffine) return dispatch_form<QT, 1, kEpiAffine>(wp, x, y, a, p, s);
     switch (M) {
     case 1: return dispatch_form<QT, 1, kEpiPlain>(wp, x, y, a, p, s);
     case 2: return dispatch_form<QT, 2, kEpiPlain>(wp, x, y, a, p, s);

@@ -104,6 +104,30 @@ qg_status qgemv_q8_0(const void *w_packed, const float *x, float *y, int64_t N, 
 /* Same for a packed Q4_0 weight (weight value nibble - 8). */
 qg_status qgemv_q4_0(const void *w_packed, const float *x, float *y, int64_t N, int64_t K, void *stream);
 
+/* Output element type of qgemv_epilogue. */
+typedef enum { QG_OUT_F32 = 0, QG_OUT_F16 = 1 } qg_out_type;
+
+/* Epilogue variants of the M=1 quantised GEMV, in the same dispatch:
+ *   y[n] = ((W x)[n] + bias[n]) + residual[n]
+ * The RunIT_Mac README adds the QKV bias inside the fused QKV kernel ("Fused
+ * QKV+bias", optimisation and kernel tables) and keeps an f32 residual stream
+ * that the projections add into (data-flow figure); the robotnurse.io post
+ * lists fp16-output GEMVs among its wins (What actually moved it, 5).
+ *  - qtype QG_Q8_0 / QG_Q4_0; w_packed from qg_pack / qg_pack_rows (16-byte
+ *    aligned); x fp32 [K] (16-byte aligned).
+ *  - (W x)[n] has exactly the bits that qgemv_q8_0 / qgemv_q4_0 return. Each
+ *    addition is one fp32 add, bias first; a NULL bias or residual is skipped,
+ *    so with both NULL and QG_OUT_F32 this call equals the plain one.
+ *  - bias, residual: fp32 [N], 4-byte aligned, or NULL.
+ *  - out_type QG_OUT_F32: y is fp32 [N] (4-byte aligned). QG_OUT_F16: y is
+ *    fp16 [N] (2-byte aligned), the fp32 result rounded to nearest even
+ *    (subnormals kept, overflow to infinity).
+ *  - residual may be the same buffer as y (in-place y += W x) with QG_OUT_F32;
+ *    any other overlap of y with x, the weights, bias or residual returns
+ *    QG_EINVAL. An unknown out_type returns QG_EUNSUPPORTED. */
+qg_status qgemv_epilogue(int qtype, const void *w_packed, const float *x, const float *bias,
+                         const float *residual, void *y, int out_type, int64_t N, int64_t K, void *stream);
+
 /* Unquantised fp16 weights, y = W x with W fp16 row-major [N][K] (any K >= 1,
  * 2-byte aligned; the fast path needs K % 8 == 0 and 16-byte alignment), x fp32
  * [K], y fp32 [N]. K is split across the wavefronts of one workgroup and the
@@ -156,8 +180,9 @@ qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int *split_k_ways
  * with different overrides in effect. Returns QG_OK. */
 qg_status qg_reload_tuning(void);
 
-/* Time the next GEMV kernel (qgemv_q8_0, qgemv_q4_0, gemv_f16_splitk,
- * qgemv_fused_gateup_silu or qgemv_verify) that the calling thread launches.
+/* Time the next GEMV kernel (qgemv_q8_0, qgemv_q4_0, qgemv_epilogue,
+ * gemv_f16_splitk, qgemv_fused_gateup_silu or qgemv_verify) that the calling
+ * thread launches.
  * start_event and stop_event are hipEvent_t handles, created by the caller
  * with timing enabled and owned by the caller. That call's kernel records its
  * own start and end time into them (the dispatch's timestamps, which a

@@ -111,6 +111,27 @@ def test_argument_checks_return_codes_without_gpu(L):
     assert "overlap" in msg
 
 
+def test_epilogue_argument_checks_without_gpu(L):
+    f = FAKE
+    w, x, y, b, r = f, f + (1 << 20), f + (2 << 20), f + (3 << 20), f + (4 << 20)
+    ep = lambda *a: call(L, "qgemv_epilogue", *a)  # noqa: E731
+    # (qtype, w, x, bias, residual, y, out_type, N, K, stream)
+    assert ep(1, None, x, b, r, y, 0, 8, 32, None) == qg.QG_EINVAL          # null weights
+    assert ep(1, w, x, b, r, None, 0, 8, 32, None) == qg.QG_EINVAL          # null output
+    assert ep(3, w, x, b, r, y, 0, 8, 32, None) == qg.QG_EUNSUPPORTED       # unknown qtype
+    assert ep(1, w, x, b, r, y, 2, 8, 32, None) == qg.QG_EUNSUPPORTED       # unknown output type
+    assert ep(2, w, x, b, r, y, 0, 8, 48, None) == qg.QG_EINVAL             # K % 32
+    assert ep(1, w, x, b + 2, r, y, 0, 8, 32, None) == qg.QG_EALIGN         # bias alignment
+    assert ep(1, w, x, b, r + 1, y, 0, 8, 32, None) == qg.QG_EALIGN         # residual alignment
+    assert ep(1, w, x, b, r, y + 2, 0, 8, 32, None) == qg.QG_EALIGN         # fp32 output alignment
+    assert ep(1, w, x, b, r, y + 1, 1, 8, 32, None) == qg.QG_EALIGN         # fp16 output alignment
+    assert ep(1, w, x, y + 16, r, y, 0, 8, 32, None) == qg.QG_EINVAL        # y overlaps bias
+    assert ep(1, w, x, b, y + 4, y, 0, 8, 32, None) == qg.QG_EINVAL         # y overlaps residual, shifted
+    assert ep(1, w, x, b, y, y, 1, 8, 32, None) == qg.QG_EINVAL             # in place needs fp32 output
+    assert ep(1, w, y - 16, b, r, y, 1, 8, 32, None) == qg.QG_EINVAL        # y overlaps x
+    assert "overlap" in qg.qg_last_error()
+
+
 def test_time_next_launch_arguments(L):
     # host-only: binding or clearing events makes no HIP call
     f = FAKE
