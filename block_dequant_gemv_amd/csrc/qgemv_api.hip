@@ -78,12 +78,15 @@ int64_t env_int(const char *name, int64_t dflt)
 
 // Launch-shape overrides for sweeps and tests (QG_SPLIT_K, QG_PERSIST,
 // QG_X_GLOBAL, QG_TILES_PER_GROUP, QG_WAVES_PER_WG, QG_PREFETCH, QG_F16_ROWS,
-// QG_F16_WAVES). They are read from the environment once, on first use, and
+// QG_F16_WAVES, QG_STRIDE_GROUPS). They are read from the environment once, on first use, and
 // again on qg_reload_tuning(): a GEMV call itself reads no environment.
-enum TuneKey { kSplitK, kPersist, kXGlobal, kTilesPerGroup, kWavesPerWg, kPrefetch, kF16Rows, kF16Waves, kNumTune };
-const char *const kTuneNames[kNumTune] = {"QG_SPLIT_K",      "QG_PERSIST",      "QG_X_GLOBAL", "QG_TILES_PER_GROUP",
-                                          "QG_WAVES_PER_WG", "QG_PREFETCH",     "QG_F16_ROWS", "QG_F16_WAVES"};
-const int64_t kTuneDefaults[kNumTune] = {0, -1, -1, 0, 0, 0, 0, 0};
+enum TuneKey {
+    kSplitK, kPersist, kXGlobal, kTilesPerGroup, kWavesPerWg, kPrefetch, kF16Rows, kF16Waves, kStrideGroups, kNumTune
+};
+const char *const kTuneNames[kNumTune] = {"QG_SPLIT_K",      "QG_PERSIST",  "QG_X_GLOBAL",  "QG_TILES_PER_GROUP",
+                                          "QG_WAVES_PER_WG", "QG_PREFETCH", "QG_F16_ROWS",  "QG_F16_WAVES",
+                                          "QG_STRIDE_GROUPS"};
+const int64_t kTuneDefaults[kNumTune] = {0, -1, -1, 0, 0, 0, 0, 0, -1};
 std::atomic<int64_t> g_tune[kNumTune];
 std::atomic<bool> g_tune_loaded{false};
 
@@ -182,6 +185,7 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M)
     p.persist = plan_persist(rows, K, &ranges, &pgrid, &max_tiles);
     p.depth = 1;
     p.tpg = 1;
+    p.tstride = 0;
     if (p.persist) {
         p.ranges = (int)ranges;
         p.max_tiles = max_tiles;
@@ -203,7 +207,14 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M)
     // (measured on both LM-head shapes).
     const int64_t tpg_env = tune(kTilesPerGroup);
     if (tpg_env > 0) p.tpg = tpg_env;
-    const int64_t groups = (g.n_tiles + p.tpg - 1) / p.tpg;
+    int64_t groups = (g.n_tiles + p.tpg - 1) / p.tpg;
+    // Grid-stride tile order (QG_STRIDE_GROUPS = number of groups, 0 = off).
+    p.tstride = 0;
+    const int64_t sg_env = tune(kStrideGroups);
+    if (sg_env > 0 && sg_env < g.n_tiles) {
+        p.tstride = sg_env;
+        groups = sg_env;
+    }
     const size_t lds_limit = M > 1 ? kLdsLimitMulti : kLdsLimit;
     int G;   // groups per workgroup
     if (p.W > 1) {
@@ -218,8 +229,14 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M)
         if (g_env == 1 || g_env == 2 || g_env == 4 || g_env == 8) G = (int)g_env;
         p.block = 64 * G;
     }
+    if (p.tstride > 0) {
+        // every group index below tstride must exist: round the groups up to whole workgroups
+        p.tstride = (groups + G - 1) / G * G;
+        if (p.tstride >= g.n_tiles) p.tstride = 0;
+    }
     p.grid = (groups + G - 1) / G;
-    const double wg_weight_bytes = (double)G * (double)p.tpg * (double)(g.tile_q + g.tile_s);
+    const double tiles_per_group = p.tstride > 0 ? (double)g.n_tiles / (double)p.tstride : (double)p.tpg;
+    const double wg_weight_bytes = (double)G * tiles_per_group * (double)(g.tile_q + g.tile_s);
     bool lds = xbytes <= lds_limit && (M > 1 || wg_weight_bytes >= 2.0 * (double)xbytes);
     if (xg_env == 0 || xg_env == 1) lds = xbytes <= lds_limit && xg_env == 0;
     p.x_in_lds = lds;
@@ -273,6 +290,7 @@ qg_status run_qgemv(int qt, int epi, const void *w, const float *x, void *y, int
     a.x_stride = K;
     a.y_stride = n_out;
     a.tpg = p.tpg;
+    a.tstride = p.tstride;
     a.n_wg = p.grid;
     a.ranges = p.ranges;
     a.bias = af.bias;

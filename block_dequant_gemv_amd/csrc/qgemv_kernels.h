@@ -21,7 +21,8 @@ struct QArgs {
     int64_t n_out;       // outputs per activation row (N, or N_ff for gate|up)
     int64_t x_stride;    // floats between activation rows (K)
     int64_t y_stride;    // floats between output rows (N)
-    int64_t tpg;         // row tiles walked by one group of W wavefronts
+    int64_t tpg;         // row tiles walked by one group of W wavefronts (tstride == 0)
+    int64_t tstride;     // > 0: group g walks tiles g, g + tstride, g + 2*tstride, ... (tstride = groups)
     // persistent form only
     int64_t n_wg;        // workgroups; workgroup b owns tiles [b*n_tiles/n_wg, (b+1)*n_tiles/n_wg)
     int64_t ranges;      // K ranges per tile (divides nseg); item = (tile, range)
@@ -38,7 +39,8 @@ struct QPlan {
     int ranges;          // persistent form: K ranges per tile (divides nseg)
     int64_t max_tiles;   // persistent form: most tiles any workgroup owns
     int W;               // classic form: wavefronts splitting one row tile along K (1, 2, 4, 8)
-    int64_t tpg;         // tiles per group
+    int64_t tpg;         // tiles per group (contiguous order)
+    int64_t tstride;     // > 0: grid-stride tile order over this many groups (tpg unused)
     int64_t grid;        // workgroups
     int block;           // threads per workgroup (64 * wavefronts)
     int depth;           // units in flight ahead of the one being computed (1 or 2; 2 only for M = 1)

@@ -368,11 +368,15 @@ __device__ __forceinline__ void store_tile(const float (&acc)[M][kRowsPerLane], 
 //        kEpiAffine (y = ((W x) + bias) + residual, fp32 or fp16, M = 1)
 //   W    wavefronts that split one row tile along K (1, 2, 4 or 8)
 //   XLDS activations staged in LDS (true) or read from global memory
-// W == 1: a workgroup holds blockDim/64 independent wavefronts, wavefront g of
-//         workgroup b walks tiles [(b*G + g) * tpg, ... + tpg).
-// W  > 1: a workgroup is W wavefronts sharing the tiles [b * tpg, b * tpg + tpg);
-//         wavefront w adds segments [nseg*w/W, nseg*(w+1)/W) of every tile and
-//         the W partial sums are combined in LDS in wavefront order.
+// W == 1: a workgroup holds blockDim/64 independent wavefronts; wavefront g of
+//         workgroup b is group b*G + g.
+// W  > 1: a workgroup is one group of W wavefronts; wavefront w adds segments
+//         [nseg*w/W, nseg*(w+1)/W) of every tile of the group and the W partial
+//         sums are combined in LDS in wavefront order.
+// Group q walks the tiles [q * tpg, q * tpg + tpg) (contiguous order) or, with
+// tstride > 0, the tiles q, q + tstride, q + 2*tstride, ... (grid-stride order:
+// the groups resident at any moment read one contiguous window of the weights).
+// Which group handles a tile changes none of its rows' operations.
 // Each wavefront walks its (tile, segment) sequence with the loads of the next
 // D units in flight while the current one is computed (a ring of D+1 units).
 template <int QT, int M, int EPI, int W, bool XLDS, int D>
@@ -393,21 +397,30 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
 
     const Geometry &g = a.geo;
     const int64_t K = g.K, nseg = g.nseg;
-    const int64_t t_begin = group * a.tpg;
-    const int64_t t_end = (t_begin + a.tpg < g.n_tiles) ? t_begin + a.tpg : g.n_tiles;
+    int64_t t_begin, t_step, my_tiles;
+    if (a.tstride > 0) {
+        t_begin = group;
+        t_step = a.tstride;
+        my_tiles = group < g.n_tiles ? (g.n_tiles - group + t_step - 1) / t_step : 0;
+    } else {
+        t_begin = group * a.tpg;
+        t_step = 1;
+        const int64_t t_end = (t_begin + a.tpg < g.n_tiles) ? t_begin + a.tpg : g.n_tiles;
+        my_tiles = t_end > t_begin ? t_end - t_begin : 0;
+    }
     const int64_t s_begin = nseg * wk / W, s_end = nseg * (wk + 1) / W;
 
     const Consts k = make_consts();
     const LanePlace lp = lane_place(g, slot, j);
-    // This wavefront's units, in order: (t, s) for t in [t_begin, t_end), s in [s_begin, s_end).
-    const int64_t n_units = (t_end > t_begin ? t_end - t_begin : 0) * (s_end - s_begin);
+    // This wavefront's units, in order: (t, s) for its tiles t, s in [s_begin, s_end).
+    const int64_t n_units = my_tiles * (s_end - s_begin);
 
     // Load cursor: the unit whose loads are issued next (D units ahead of the compute cursor).
     int64_t t_ld = t_begin, s_ld = s_begin, u_ld = 0;
     auto advance = [&](int64_t &tt, int64_t &ss) {
         if (++ss == s_end) {
             ss = s_begin;
-            ++tt;
+            tt += t_step;
         }
     };
     XFirst xf;

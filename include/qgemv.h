@@ -171,7 +171,8 @@ qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int *split_k_ways
                        int64_t *workgroups, int *x_in_lds, int *persistent);
 
 /* Re-read the launch-shape overrides (QG_SPLIT_K, QG_PERSIST, QG_X_GLOBAL,
- * QG_TILES_PER_GROUP, QG_WAVES_PER_WG, QG_PREFETCH, QG_F16_ROWS, QG_F16_WAVES)
+ * QG_TILES_PER_GROUP, QG_WAVES_PER_WG, QG_PREFETCH, QG_F16_ROWS, QG_F16_WAVES,
+ * QG_STRIDE_GROUPS)
  * from the environment. They exist for launch-shape sweeps and tests and are
  * read once, at the first call that plans a launch; the GEMV calls themselves
  * read no environment. An override that changes a matrix's K split (QG_SPLIT_K,

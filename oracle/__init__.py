@@ -68,6 +68,12 @@ def _declare(L):
     L.oracle_gemv_epilogue.argtypes = [i32, vp, fp, fp, fp, dp, dp, i64, i64, i32]
     L.oracle_gemv_epilogue.restype = i32
     L.oracle_verify.restype = i32
+    L.oracle_rmsnorm.argtypes = [fp, fp, ctypes.c_double, dp, i64]
+    L.oracle_rmsnorm.restype = i32
+    L.oracle_gemv_rmsnorm.argtypes = [i32, vp, fp, fp, ctypes.c_double, dp, dp, i64, i64]
+    L.oracle_gemv_rmsnorm.restype = i32
+    L.oracle_gateup_silu_rmsnorm.argtypes = [i32, vp, vp, fp, fp, ctypes.c_double, dp, dp, dp, dp, dp, i64, i64]
+    L.oracle_gateup_silu_rmsnorm.restype = i32
     return L
 
 
@@ -158,6 +164,50 @@ def gemv_epilogue(kind, w: np.ndarray, x: np.ndarray, N: int, K: int, bias=None,
     if rc:
         raise ValueError("oracle_gemv_epilogue rejected its arguments")
     return out, a
+
+
+def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float, L=None) -> np.ndarray:
+    """gamma * x / sqrt(mean(x^2) + eps) in fp64 (eps is used as given, e.g. an fp32 value)."""
+    L = L or lib()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    if gamma.shape != x.shape:
+        raise ValueError("gamma must have K entries")
+    out = np.empty(x.size, np.float64)
+    if L.oracle_rmsnorm(_ptr(x), _ptr(gamma), float(eps), _ptr(out), x.size):
+        raise ValueError("oracle_rmsnorm rejected its arguments")
+    return out
+
+
+def gemv_rmsnorm(kind, w: np.ndarray, x: np.ndarray, gamma: np.ndarray, eps: float, N: int, K: int, L=None):
+    """y = W rmsnorm(x) in fp64 (the normalised activation exact in double), and a = sum |W xn|."""
+    L = L or lib()
+    k = _kind(kind)
+    w = _check_w(k, w, N, K)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    assert x.size == K and gamma.size == K
+    y = np.empty(N, np.float64)
+    a = np.empty(N, np.float64)
+    if L.oracle_gemv_rmsnorm(k, _ptr(w), _ptr(x), _ptr(gamma), float(eps), _ptr(y), _ptr(a), N, K):
+        raise ValueError("oracle_gemv_rmsnorm rejected its arguments")
+    return y, a
+
+
+def gateup_silu_rmsnorm(kind, gate: np.ndarray, up: np.ndarray, x: np.ndarray, gamma: np.ndarray, eps: float,
+                        N_ff: int, K: int, L=None):
+    """out = silu(Wgate xn) * (Wup xn) with xn = rmsnorm(x); also g, u and their magnitude sums."""
+    L = L or lib()
+    k = _kind(kind)
+    gate = _check_w(k, gate, N_ff, K)
+    up = _check_w(k, up, N_ff, K)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    out, g, u, ag, au = (np.empty(N_ff, np.float64) for _ in range(5))
+    if L.oracle_gateup_silu_rmsnorm(k, _ptr(gate), _ptr(up), _ptr(x), _ptr(gamma), float(eps), _ptr(out), _ptr(g),
+                                    _ptr(u), _ptr(ag), _ptr(au), N_ff, K):
+        raise ValueError("oracle_gateup_silu_rmsnorm rejected its arguments")
+    return out, g, u, ag, au
 
 
 def verify(kind, w: np.ndarray, X: np.ndarray, N: int, K: int, threads: int = 1, L=None):

@@ -32,6 +32,10 @@
  *    robotnurse.io "We wrote our own inference engine", "What actually moved
  *    it", item 5: some GEMVs write fp16 outputs. oracle_gemv_epilogue is the
  *    product followed by those additions, in double.
+ *  - RunIT_Mac README, kernel table and data-flow figure: RMSNorm with f32
+ *    input, output and gamma precedes the projections; "EdgeRunner beats
+ *    llama.cpp", The progression, fused it into the GEMV (RMSNorm+GEMV).
+ *    oracle_rmsnorm and oracle_gemv_rmsnorm write that out in double.
  *
  * Readings where the pages are silent (each is also listed in the design notes):
  *  - Block field order is the GGUF one: little-endian fp16 scale first, then
@@ -40,6 +44,8 @@
  *    and element j+16 in its high nibble (GGUF convention); value = nibble - 8.
  *  - fp16 decoding follows IEEE 754 binary16 exactly, subnormals included.
  *  - silu(g) = g / (1 + exp(-g)).
+ *  - RMSNorm: out[k] = gamma[k] * x[k] / sqrt(mean(x^2) + eps), with eps >= 0
+ *    given by the caller (the pages name the operation, not its epsilon).
  *
  * Exactness: the fp16 decode, the int->double conversion, d*q (<= 19
  * significant bits) and (d*q)*x (<= 43 bits) are all exact in double, so the
@@ -245,4 +251,75 @@ int oracle_gemv_epilogue(int kind, const void *w, const float *x, const float *b
             out[n] += (double)residual[n];
     }
     return 0;
+}
+
+/* ---- RMSNorm and the RMSNorm-prologue product ---------------------------- */
+
+/* RMSNorm of one activation vector, in double (RunIT_Mac README, kernel table
+ * and data-flow figure: RMSNorm takes an f32 input and an f32 gamma and gives
+ * an f32 output; "EdgeRunner beats llama.cpp", The progression: the RMSNorm
+ * that precedes a projection fused into that GEMV):
+ *   out[k] = gamma[k] * x[k] / sqrt((1/K) * sum_j x[j]^2 + eps)
+ * eps >= 0 is the caller's (the pages give no value). */
+int oracle_rmsnorm(const float *x, const float *gamma, double eps, double *out, int64_t K)
+{
+    if (K <= 0 || !(eps >= 0.0))
+        return 1;
+    double ss = 0.0;
+    for (int64_t k = 0; k < K; ++k)
+        ss += (double)x[k] * (double)x[k];
+    double rms = sqrt(ss / (double)K + eps);
+    for (int64_t k = 0; k < K; ++k)
+        out[k] = (double)gamma[k] * (double)x[k] / rms;
+    return 0;
+}
+
+/* y = W * rmsnorm(x): the product of the normalised activation (kept exact in
+ * double) with the dequantised weights, plus a[n] = sum_k |W[n][k] * xn[k]|. */
+int oracle_gemv_rmsnorm(int kind, const void *w, const float *x, const float *gamma, double eps,
+                        double *y, double *a, int64_t N, int64_t K)
+{
+    if (bad_args(kind, N, K) || K == 0)
+        return 1;
+    double *xn = (double *)malloc(sizeof(double) * (size_t)K);
+    if (!xn)
+        return 1;
+    int rc = oracle_rmsnorm(x, gamma, eps, xn, K);
+    const uint8_t *wb = (const uint8_t *)w;
+    for (int64_t n = 0; !rc && n < N; ++n) {
+        double sum = 0.0, asum = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double wk;
+            if (kind == ORACLE_Q8_0)
+                wk = q8_0_weight(wb + (n * (K / 32) + k / 32) * 34, (int)(k % 32));
+            else if (kind == ORACLE_Q4_0)
+                wk = q4_0_weight(wb + (n * (K / 32) + k / 32) * 18, (int)(k % 32));
+            else
+                wk = oracle_half_to_double(read_le16(wb + (n * K + k) * 2));
+            double p = wk * xn[k];
+            sum += p;
+            asum += fabs(p);
+        }
+        y[n] = sum;
+        if (a)
+            a[n] = asum;
+    }
+    free(xn);
+    return rc;
+}
+
+/* The gate|up SiLU product on the normalised activation: out[n] =
+ * silu(g[n]) * u[n] with g = Wgate * rmsnorm(x), u = Wup * rmsnorm(x). */
+int oracle_gateup_silu_rmsnorm(int kind, const void *gate, const void *up, const float *x, const float *gamma,
+                               double eps, double *out, double *g, double *u, double *ag, double *au,
+                               int64_t N_ff, int64_t K)
+{
+    if (kind == ORACLE_F16)
+        return 1;
+    int rc = oracle_gemv_rmsnorm(kind, gate, x, gamma, eps, g, ag, N_ff, K);
+    if (!rc)
+        rc = oracle_gemv_rmsnorm(kind, up, x, gamma, eps, u, au, N_ff, K);
+    for (int64_t n = 0; !rc && n < N_ff; ++n)
+        out[n] = oracle_silu(g[n]) * u[n];
+    return rc;
 }

@@ -8,7 +8,8 @@ AssertionError when the oracle disagrees with:
   * exact rational brute force on tiny random shapes (fractions.Fraction),
   * textbook special cases that reduce to a float64 numpy matmul,
   * invariants (exact scaling, zero blocks, row permutation),
-  * the composition rules of the fused and multi-row entry points.
+  * the composition rules of the fused and multi-row entry points,
+  * closed forms of RMSNorm (a vector of ones with eps = 3; alternating +-c).
 ``test_oracle_mutants.py`` plants plausible mistakes in a copy of oracle.c and
 checks that every one of them trips at least one pin.
 """
@@ -310,6 +311,56 @@ def pin_epilogue(L):
     assert out[0] == -7.25, out
 
 
+def pin_rmsnorm(L):
+    # closed forms of gamma * x / sqrt(mean(x^2) + eps):
+    #  x = 1 everywhere, eps = 3, gamma = 2: 2 / sqrt(1 + 3) = 1 exactly, for any K
+    #  (a sum instead of the mean, a dropped eps or sqrt, or a dropped gamma all move it)
+    for K in (1, 5, 64, 1024):
+        out = O.rmsnorm(np.ones(K, np.float32), np.full(K, 2.0, np.float32), 3.0, L=L)
+        assert np.all(out == 1.0), (K, out[:4])
+    #  x = +-c alternating (c a power of two), eps = 0: every |x| equals the rms, so
+    #  out = +-gamma exactly, element by element (catches a shifted gamma or x index)
+    K = 96
+    sign = np.where(np.arange(K) % 2 == 0, 1.0, -1.0)
+    gam = (np.arange(K) + 1).astype(np.float32) / 8
+    for c in (0.25, 8.0, 2.0 ** -20):
+        out = O.rmsnorm((c * sign).astype(np.float32), gam, 0.0, L=L)
+        assert np.array_equal(out, sign * gam.astype(np.float64)), c
+    #  eps = 0: scaling x by a power of two changes nothing, bit for bit
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal(200).astype(np.float32)
+    g = rng.standard_normal(200).astype(np.float32)
+    assert np.array_equal(O.rmsnorm(x, g, 0.0, L=L), O.rmsnorm(x * np.float32(16), g, 0.0, L=L))
+    #  x = (3, 4), eps = 0: mean(x^2) = 12.5, so out^2 sums to K = 2 (both components squared)
+    out = O.rmsnorm(np.array([3, 4], np.float32), np.ones(2, np.float32), 0.0, L=L)
+    assert abs(out[0] ** 2 + out[1] ** 2 - 2.0) < 1e-15 and abs(out[1] / out[0] - 4.0 / 3.0) < 1e-15
+    # the product: with +-1 activations, eps = 0 and fp32 gamma the normalised vector
+    # is exactly +-gamma, so W rmsnorm(x) equals the plain product on that vector, bit for bit
+    for kind in ("q8_0", "q4_0", "f16"):
+        N, K = 9, 128
+        w = W.f16_matrix(N, K, rng) if kind == "f16" else W.matrix(kind, N, K, rng)
+        sign = np.where(rng.random(K) < 0.5, 1.0, -1.0).astype(np.float32)
+        gam = rng.standard_normal(K).astype(np.float32)
+        y, a = O.gemv_rmsnorm(kind, w, sign, gam, 0.0, N, K, L=L)
+        y0, a0 = _gemv(L, kind, w, sign * gam, N, K)
+        assert np.array_equal(y, y0) and np.array_equal(a, a0), kind
+    # gate|up on the normalised activation: silu(g) * u of the two products
+    kind, N, K = "q8_0", 5, 64
+    gate, up = W.matrix(kind, N, K, rng), W.matrix(kind, N, K, rng)
+    x = rng.standard_normal(K).astype(np.float32)
+    gam = rng.standard_normal(K).astype(np.float32)
+    out, gg, uu, ag, au = O.gateup_silu_rmsnorm(kind, gate, up, x, gam, 1e-6, N, K, L=L)
+    g1, a1 = O.gemv_rmsnorm(kind, gate, x, gam, 1e-6, N, K, L=L)
+    u1, b1 = O.gemv_rmsnorm(kind, up, x, gam, 1e-6, N, K, L=L)
+    assert np.array_equal(gg, g1) and np.array_equal(uu, u1) and np.array_equal(ag, a1) and np.array_equal(au, b1)
+    assert np.array_equal(out, np.array([O.silu(v, L=L) for v in g1]) * u1)
+    # the worked single block E1 (y = -8 for x = 1) with x = 1, eps = 3, gamma = 2:
+    # the normalised activation is 1 everywhere, so the product is still -8
+    e1 = _u8(q8_block(0x3800, [i - 16 for i in range(32)]))
+    y, _ = O.gemv_rmsnorm("q8_0", e1, np.ones(32, np.float32), np.full(32, 2.0, np.float32), 3.0, 1, 32, L=L)
+    assert y[0] == -8.0, y
+
+
 def pin_rejects_bad_shapes(L):
     w = np.zeros(34, np.uint8)
     x = np.zeros(33, np.float32)
@@ -331,6 +382,7 @@ PINS = [
     pin_invariants,
     pin_composites,
     pin_epilogue,
+    pin_rmsnorm,
     pin_rejects_bad_shapes,
 ]
 

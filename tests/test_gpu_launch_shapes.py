@@ -3,8 +3,9 @@ oracle; verify rows stay memcmp-equal to M=1 under the same split.
 
 The planner picks one shape per (type, rows, K); the overrides
 QG_PERSIST / QG_SPLIT_K / QG_X_GLOBAL / QG_WAVES_PER_WG / QG_TILES_PER_GROUP /
-QG_PREFETCH reach the others: the one-wavefront-per-tile form with every split,
-activation source, workgroup size, tiles per group and prefetch depth (depth 2
+QG_PREFETCH / QG_STRIDE_GROUPS reach the others: the one-wavefront-per-tile form
+with every split, activation source, workgroup size, tiles per group, grid-stride
+tile order and prefetch depth (depth 2
 exists for the single-row kernels; the verify kernels keep depth 1, and their
 rows must still match), and the persistent form with activations in LDS or L2.
 """
@@ -21,7 +22,8 @@ from gpu_helpers import THREADS, announce, assert_linear, empty_f32, sync, to_de
 
 pytestmark = pytest.mark.gpu
 
-KNOBS = ("QG_PERSIST", "QG_SPLIT_K", "QG_X_GLOBAL", "QG_WAVES_PER_WG", "QG_TILES_PER_GROUP", "QG_PREFETCH")
+KNOBS = ("QG_PERSIST", "QG_SPLIT_K", "QG_X_GLOBAL", "QG_WAVES_PER_WG", "QG_TILES_PER_GROUP", "QG_PREFETCH",
+         "QG_STRIDE_GROUPS")
 
 
 def _set(**kw):
@@ -42,6 +44,9 @@ def test_forced_launch_shapes(kind, N, K):
     Y_ref, A_ref = O.verify(kind, canon, X, N, K, threads=THREADS)
     nseg = -(-K // 1024)
     combos = [dict(QG_PERSIST=1, QG_X_GLOBAL=xg) for xg in (0, 1)]
+    # grid-stride tile order: groups walk tiles g, g + groups, ... (3 groups leave a ragged last round)
+    combos += [dict(QG_PERSIST=0, QG_STRIDE_GROUPS=sg, QG_WAVES_PER_WG=1, QG_SPLIT_K=split)
+               for sg in (3, 8) for split in (1, 2) if split <= nseg]
     for split, xg, wpw, tpg, pf in itertools.product((1, 2, 4, 8), (0, 1), (1, 2, 4), (1, 3), (1, 2)):
         if split > nseg or (split > 1 and wpw != 4):
             continue

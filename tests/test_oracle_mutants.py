@@ -39,6 +39,13 @@ MUTANTS = {
     "bias_dropped": ("out[n] += (double)bias[n];", "out[n] += 0.0;"),
     "residual_subtracted": ("out[n] += (double)residual[n];", "out[n] -= (double)residual[n];"),
     "residual_for_bias": ("out[n] += (double)bias[n];", "out[n] += (double)residual[n];"),
+    "rms_eps_dropped": ("sqrt(ss / (double)K + eps)", "sqrt(ss / (double)K)"),
+    "rms_sum_not_mean": ("sqrt(ss / (double)K + eps)", "sqrt(ss + eps)"),
+    "rms_sqrt_dropped": ("double rms = sqrt(ss / (double)K + eps);", "double rms = ss / (double)K + eps;"),
+    "rms_gamma_shifted": ("out[k] = (double)gamma[k] * (double)x[k] / rms;",
+                          "out[k] = (double)gamma[(k + 1) % K] * (double)x[k] / rms;"),
+    "rms_gamma_dropped": ("out[k] = (double)gamma[k] * (double)x[k] / rms;", "out[k] = (double)x[k] / rms;"),
+    "rms_product_unnormalised": ("double p = wk * xn[k];", "double p = wk * (double)x[k];"),
 }
 
 
