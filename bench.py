@@ -256,8 +256,79 @@ def per_config_calls(qg, torch, stream, step_calls):
         make_epilogue(qg, "q8_0", lm.weight, t(wl1.x("lm_head")), None, None, y16, 151936, 1024, stream,
                       "e q8_0 lm_head 151936x1024 fp16 out"),
     ]
+    # the RMSNorm-prologue experiment: each case is (label, weight, bytes, fused(wp), norm(), gemv(wp)), the
+    # unfused form being qg_rmsnorm into a separate buffer followed by the plain GEMV on it
+    eps = 1e-6
+    norm_cases = []
+
+    def norm_case(label, kind, packed, N, K, gateup):
+        x = t(erng.standard_normal(K).astype(np.float32))
+        g = t((1.0 + 0.25 * erng.standard_normal(K)).astype(np.float32))
+        xn = yb(K)
+        y = yb(N)
+        qt = qg.QTYPES[kind]
+        if gateup:
+            fused = lambda wp: qg.bound_call("qgemv_rmsnorm_gateup_silu", qt, wp, x.data_ptr(), g.data_ptr(),  # noqa
+                                             eps, y.data_ptr(), N, K, stream)
+            plain = lambda wp: qg.bound_call("qgemv_fused_gateup_silu", qt, wp, xn.data_ptr(), y.data_ptr(),  # noqa
+                                             N, K, stream)
+            nbytes = 2 * wbytes(kind, N, K) + 8 * K + 4 * N
+        else:
+            fused = lambda wp: qg.bound_call("qgemv_rmsnorm", qt, wp, x.data_ptr(), g.data_ptr(), eps,  # noqa
+                                             y.data_ptr(), N, K, stream)
+            plain = lambda wp: qg.bound_call("qgemv_q8_0" if kind == "q8_0" else "qgemv_q4_0", wp,  # noqa
+                                             xn.data_ptr(), y.data_ptr(), N, K, stream)
+            nbytes = wbytes(kind, N, K) + 8 * K + 4 * N
+        norm = qg.bound_call("qg_rmsnorm", x.data_ptr(), g.data_ptr(), eps, xn.data_ptr(), K, stream)
+        norm_cases.append((label, packed, nbytes, fused, norm, plain))
+
+    norm_case("n q8_0 qkv 4096x1024", "q8_0", qkv.weight, 4096, 1024, False)
+    norm_case("n q8_0 gate|up 2x3072x1024", "q8_0", by["gate|up 2x3072x1024 silu"].weight, 3072, 1024, True)
+    norm_case("n q8_0 lm_head 151936x1024", "q8_0", lm.weight, 151936, 1024, False)
+    norm_case("n q4_0 gate|up 2x17408x5120", "q4_0", pg, 17408, 5120, True)
+    norm_case("n q4_0 lm_head 248320x5120", "q4_0", pl, 248320, 5120, False)
+    res["norm"] = norm_cases
     torch.cuda.synchronize()
     return res, keep
+
+
+def rmsnorm_fusion(qg, torch, cases, reps):
+    """The RMSNorm-prologue experiment, cold (weights rotating over >= 1.2 GiB of
+    copies): the fused call (one dispatch) against qg_rmsnorm + the plain GEMV (two
+    dispatches). Kernel times come from events bound to each launch; the batch
+    times are back-to-back calls (pairs) with one event pair around the batch,
+    i.e. what a decode loop pays, dispatch gaps included."""
+    out = {}
+    log("rmsnorm prologue: fused (1 dispatch) vs qg_rmsnorm + GEMV (2 dispatches), cold weights")
+    for label, weight, nbytes, fused, norm, plain in cases:
+        copies = cold_copies(torch, weight)
+        f_fns = [fused(cp.data_ptr()) for cp in copies]
+        p_fns = [plain(cp.data_ptr()) for cp in copies]
+        for f in f_fns[:2] + p_fns[:2]:
+            f()
+        norm()
+        uf, bf = time_call(qg, torch, f_fns, reps)
+        un, _ = time_call(qg, torch, [norm], reps)
+        up, _ = time_call(qg, torch, p_fns, reps)
+        pairs = [(lambda p=p: (norm(), p())) for p in p_fns]
+        nb = max(reps, len(pairs))
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        b0.record()
+        for i in range(nb):
+            pairs[i % len(pairs)]()
+        b1.record()
+        torch.cuda.synchronize()
+        bu = b0.elapsed_time(b1) * 1e3 / nb
+        del f_fns, p_fns, pairs, copies
+        r = {"fused_us": round(float(np.median(uf)), 3), "norm_us": round(float(np.median(un)), 3),
+             "gemv_us": round(float(np.median(up)), 3), "fused_batch_us": round(bf, 3),
+             "unfused_batch_us": round(bu, 3), "bytes": nbytes}
+        out[label] = r
+        log(f"  {label:30s} fused {r['fused_us']:8.2f} us | norm {r['norm_us']:6.2f} + gemv {r['gemv_us']:8.2f} us"
+            f"   batch: fused {bf:8.2f} us, unfused {bu:8.2f} us ({100 * (bu - bf) / bu:+.1f}% saved by fusing)")
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(wl, threads_all):
@@ -508,6 +579,7 @@ def main():
         cfg_calls, keep = per_config_calls(qg, torch, stream, steps[0])
         table = {}
         log(f"per-call table: {args.reps} cold calls rotating over >= 1.2 GiB of weight copies, and warm calls")
+        norm_cases = cfg_calls.pop("norm")
         for ci in sorted(cfg_calls):
             for c in cfg_calls[ci]:
                 copies = cold_copies(torch, c.weight)
@@ -534,6 +606,8 @@ def main():
         result["configs"] = {k: {"us": v["us"], "GBps": v["GBps"], "pct": v["pct"], "batch_us": v["batch_us"],
                                  "warm_us": v["warm_us"]} for k, v in table.items()}
         detail["configs"] = table
+        result["rmsnorm_fusion"] = rmsnorm_fusion(qg, torch, norm_cases, args.reps)
+        del norm_cases
         del keep
 
     # ---- CPU oracle baseline ----------------------------------------------------------

@@ -29,6 +29,7 @@ SYMBOLS = (
     "qg_packed_size", "qg_pack", "qg_pack_rows", "qg_pack_gateup",
     "qg_pack_host", "qg_unpack_host", "qg_pack_gateup_host",
     "qgemv_q8_0", "qgemv_q4_0", "qgemv_epilogue", "gemv_f16_splitk", "qgemv_fused_gateup_silu", "qgemv_verify",
+    "qg_rmsnorm", "qgemv_rmsnorm", "qgemv_rmsnorm_gateup_silu",
     "qg_status_str", "qg_last_error", "qg_plan_info", "qg_time_next_launch", "qg_reload_tuning",
 )
 
@@ -69,6 +70,9 @@ def lib():
             "qgemv_q8_0": ([vp, vp, vp, i64, i64, vp], i32),
             "qgemv_q4_0": ([vp, vp, vp, i64, i64, vp], i32),
             "qgemv_epilogue": ([i32, vp, vp, vp, vp, vp, i32, i64, i64, vp], i32),
+            "qg_rmsnorm": ([vp, vp, ctypes.c_float, vp, i64, vp], i32),
+            "qgemv_rmsnorm": ([i32, vp, vp, vp, ctypes.c_float, vp, i64, i64, vp], i32),
+            "qgemv_rmsnorm_gateup_silu": ([i32, vp, vp, vp, ctypes.c_float, vp, i64, i64, vp], i32),
             "gemv_f16_splitk": ([vp, vp, vp, i64, i64, vp], i32),
             "qgemv_fused_gateup_silu": ([i32, vp, vp, vp, i64, i64, vp], i32),
             "qgemv_verify": ([i32, vp, vp, vp, i64, i64, i32, vp], i32),
@@ -195,6 +199,24 @@ def qgemv_epilogue(qtype, w_packed, x, y, N: int, K: int, bias=None, residual=No
            lib().qgemv_epilogue(_qtype(qtype), _dev(w_packed, "w_packed"), _dev(x, "x", _f32()),
                                 _dev(bias, "bias", _f32()), _dev(residual, "residual", _f32()), _dev(y, "y"),
                                 out_type, N, K, _stream(stream)))
+
+
+def qg_rmsnorm(x, gamma, eps: float, out, K: int, stream=None):
+    _check("qg_rmsnorm", lib().qg_rmsnorm(_dev(x, "x", _f32()), _dev(gamma, "gamma", _f32()), float(eps),
+                                          _dev(out, "out", _f32()), K, _stream(stream)))
+
+
+def qgemv_rmsnorm(qtype, w_packed, x, gamma, eps: float, y, N: int, K: int, stream=None):
+    _check("qgemv_rmsnorm", lib().qgemv_rmsnorm(_qtype(qtype), _dev(w_packed, "w_packed"), _dev(x, "x", _f32()),
+                                                _dev(gamma, "gamma", _f32()), float(eps), _dev(y, "y", _f32()),
+                                                N, K, _stream(stream)))
+
+
+def qgemv_rmsnorm_gateup_silu(qtype, w_gateup_packed, x, gamma, eps: float, y, N_ff: int, K: int, stream=None):
+    _check("qgemv_rmsnorm_gateup_silu",
+           lib().qgemv_rmsnorm_gateup_silu(_qtype(qtype), _dev(w_gateup_packed, "w_gateup_packed"),
+                                           _dev(x, "x", _f32()), _dev(gamma, "gamma", _f32()), float(eps),
+                                           _dev(y, "y", _f32()), N_ff, K, _stream(stream)))
 
 
 def gemv_f16_splitk(w_f16, x, y, N: int, K: int, stream=None):

@@ -175,9 +175,13 @@ bool plan_persist(int64_t rows, int64_t K, int64_t *ranges, int64_t *grid, int64
     return true;
 }
 
-qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M)
+// The RMSNorm prologue needs the activations staged in LDS: at most 160 KiB of them.
+constexpr int64_t kNormMaxK = (int64_t)(160 * 1024 / sizeof(float));
+
+qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M, bool norm = false)
 {
     qgk::QPlan p;
+    p.norm = norm;
     const Geometry g = qgl::geometry(qt, rows, K);
     const size_t xbytes = (size_t)M * (size_t)g.nseg * qgl::kSegWeights * sizeof(float);
     const int64_t xg_env = tune(kXGlobal);
@@ -193,7 +197,7 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M)
         p.grid = pgrid;
         const size_t part = ranges > 1 ? (size_t)max_tiles * ranges * M * qgl::kTileRows * 4 : 0;
         bool lds = xbytes + part <= kLdsLimitMulti;
-        if (xg_env == 0 || xg_env == 1) lds = lds && xg_env == 0;
+        if (!norm && (xg_env == 0 || xg_env == 1)) lds = lds && xg_env == 0;
         p.x_in_lds = lds;
         p.lds_bytes = (lds ? xbytes : 0) + part;
         p.block = qgk::persist_threads(qt, M, lds);
@@ -208,12 +212,14 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M)
     const int64_t tpg_env = tune(kTilesPerGroup);
     if (tpg_env > 0) p.tpg = tpg_env;
     int64_t groups = (g.n_tiles + p.tpg - 1) / p.tpg;
-    // Grid-stride tile order (QG_STRIDE_GROUPS = number of groups, 0 = off).
+    // Grid-stride tile order (QG_STRIDE_GROUPS = number of groups; off by
+    // default: in interleaved measurements it gained on some shapes and lost on
+    // others, the plain and the RMSNorm-prologue calls alike).
     p.tstride = 0;
-    const int64_t sg_env = tune(kStrideGroups);
-    if (sg_env > 0 && sg_env < g.n_tiles) {
-        p.tstride = sg_env;
-        groups = sg_env;
+    const int64_t sg = tune(kStrideGroups);
+    if (sg > 0 && sg < g.n_tiles) {
+        p.tstride = sg;
+        groups = sg;
     }
     const size_t lds_limit = M > 1 ? kLdsLimitMulti : kLdsLimit;
     int G;   // groups per workgroup
@@ -232,13 +238,17 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M)
     if (p.tstride > 0) {
         // every group index below tstride must exist: round the groups up to whole workgroups
         p.tstride = (groups + G - 1) / G * G;
-        if (p.tstride >= g.n_tiles) p.tstride = 0;
+        if (p.tstride >= g.n_tiles) {
+            p.tstride = 0;
+            groups = (g.n_tiles + p.tpg - 1) / p.tpg;
+        }
     }
     p.grid = (groups + G - 1) / G;
     const double tiles_per_group = p.tstride > 0 ? (double)g.n_tiles / (double)p.tstride : (double)p.tpg;
     const double wg_weight_bytes = (double)G * tiles_per_group * (double)(g.tile_q + g.tile_s);
     bool lds = xbytes <= lds_limit && (M > 1 || wg_weight_bytes >= 2.0 * (double)xbytes);
     if (xg_env == 0 || xg_env == 1) lds = xbytes <= lds_limit && xg_env == 0;
+    if (norm) lds = xbytes <= kLdsLimitMulti;   // the prologue normalises the staged copy
     p.x_in_lds = lds;
     p.lds_bytes = p.x_in_lds ? xbytes : 0;
     // Prefetch depth: one unit in flight ahead of the one being computed. A
@@ -258,8 +268,16 @@ struct Affine {
     int out_type = QG_OUT_F32;
 };
 
+// The RMSNorm prologue (qgemv_rmsnorm*): gamma [K] and eps.
+struct Norm {
+    bool on = false;
+    const float *gamma = nullptr;
+    float eps = 0.0f;
+};
+
 qg_status run_qgemv(int qt, int epi, const void *w, const float *x, void *y, int64_t rows, int64_t n_out,
-                    int64_t K, int M, void *stream, const char *fn, const Affine &af = Affine())
+                    int64_t K, int M, void *stream, const char *fn, const Affine &af = Affine(),
+                    const Norm &nm = Norm())
 {
     qg_status st = check_qshape(qt, rows, K, fn);
     if (st) return st;
@@ -272,6 +290,15 @@ qg_status run_qgemv(int qt, int epi, const void *w, const float *x, void *y, int
     if (!aligned(y, f16 ? 2 : 4)) return fail(QG_EALIGN, "%s: output must be %d-byte aligned", fn, f16 ? 2 : 4);
     if (!aligned(af.bias, 4) || !aligned(af.residual, 4))
         return fail(QG_EALIGN, "%s: bias and residual must be 4-byte aligned", fn);
+    if (nm.on) {
+        if (!nm.gamma) return fail(QG_EINVAL, "%s: null gamma", fn);
+        if (!aligned(nm.gamma, 16)) return fail(QG_EALIGN, "%s: gamma must be 16-byte aligned", fn);
+        if (!(nm.eps >= 0.0f) || nm.eps == __builtin_inff())
+            return fail(QG_EINVAL, "%s: eps must be finite and >= 0", fn);
+        if (K > kNormMaxK)
+            return fail(QG_EUNSUPPORTED, "%s: K=%lld above %lld (the normalised activations live in LDS)", fn,
+                        (long long)K, (long long)kNormMaxK);
+    }
     const Geometry g = qgl::geometry(qt, rows, K);
     const size_t ybytes = (size_t)M * (size_t)n_out * (f16 ? 2 : sizeof(float));
     const size_t xbytes = (size_t)M * (size_t)K * sizeof(float);
@@ -279,11 +306,14 @@ qg_status run_qgemv(int qt, int epi, const void *w, const float *x, void *y, int
     if (overlap(y, ybytes, x, xbytes)) return fail(QG_EINVAL, "%s: y overlaps x", fn);
     if (overlap(y, ybytes, w, (size_t)g.total)) return fail(QG_EINVAL, "%s: y overlaps the weights", fn);
     if (af.bias && overlap(y, ybytes, af.bias, abytes)) return fail(QG_EINVAL, "%s: y overlaps bias", fn);
+    if (nm.on && overlap(y, ybytes, nm.gamma, (size_t)K * sizeof(float)))
+        return fail(QG_EINVAL, "%s: y overlaps gamma", fn);
     // residual == y (fp32) is the in-place update y += W x; any other overlap is refused
     if (af.residual && !(af.residual == y && !f16) && overlap(y, ybytes, af.residual, abytes))
         return fail(QG_EINVAL, "%s: y overlaps residual (only residual == y with fp32 output is allowed)", fn);
 
-    const qgk::QPlan p = make_qplan(qt, rows, K, M);
+    const qgk::QPlan p = make_qplan(qt, rows, K, M, nm.on);
+    if (nm.on && !p.x_in_lds) return fail(QG_EUNSUPPORTED, "%s: activations do not fit in LDS", fn);
     qgk::QArgs a;
     a.geo = g;
     a.n_out = n_out;
@@ -296,6 +326,8 @@ qg_status run_qgemv(int qt, int epi, const void *w, const float *x, void *y, int
     a.bias = af.bias;
     a.residual = af.residual;
     a.out_f16 = f16 ? 1 : 0;
+    a.gamma = nm.gamma;
+    a.eps = nm.eps;
     hipError_t e = qgk::launch_qgemv(qt, M, epi, p, (const uint8_t *)w, x, (float *)y, a, as_stream(stream));
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
@@ -434,6 +466,45 @@ qg_status qgemv_epilogue(int qtype, const void *w_packed, const float *x, const 
     af.residual = residual;
     af.out_type = out_type;
     return run_qgemv(qtype, qgk::kEpiAffine, w_packed, x, y, N, N, K, 1, stream, "qgemv_epilogue", af);
+}
+
+qg_status qgemv_rmsnorm(int qtype, const void *w_packed, const float *x, const float *gamma, float eps, float *y,
+                        int64_t N, int64_t K, void *stream)
+{
+    Norm nm;
+    nm.on = true;
+    nm.gamma = gamma;
+    nm.eps = eps;
+    return run_qgemv(qtype, qgk::kEpiPlain, w_packed, x, y, N, N, K, 1, stream, "qgemv_rmsnorm", Affine(), nm);
+}
+
+qg_status qgemv_rmsnorm_gateup_silu(int qtype, const void *w_gateup_packed, const float *x, const float *gamma,
+                                    float eps, float *y, int64_t N_ff, int64_t K, void *stream)
+{
+    if (N_ff <= 0 || N_ff > kMaxDim)
+        return fail(QG_EINVAL, "qgemv_rmsnorm_gateup_silu: N_ff=%lld", (long long)N_ff);
+    Norm nm;
+    nm.on = true;
+    nm.gamma = gamma;
+    nm.eps = eps;
+    return run_qgemv(qtype, qgk::kEpiGateUp, w_gateup_packed, x, y, 2 * N_ff, N_ff, K, 1, stream,
+                     "qgemv_rmsnorm_gateup_silu", Affine(), nm);
+}
+
+qg_status qg_rmsnorm(const float *x, const float *gamma, float eps, float *out, int64_t K, void *stream)
+{
+    const char *fn = "qg_rmsnorm";
+    if (K <= 0 || K > kMaxDim) return fail(QG_EINVAL, "%s: K=%lld must be positive", fn, (long long)K);
+    if (!x || !gamma || !out) return fail(QG_EINVAL, "%s: null pointer", fn);
+    if (!aligned(x, 4) || !aligned(gamma, 4) || !aligned(out, 4))
+        return fail(QG_EALIGN, "%s: x, gamma and out must be 4-byte aligned", fn);
+    if (!(eps >= 0.0f) || eps == __builtin_inff()) return fail(QG_EINVAL, "%s: eps must be finite and >= 0", fn);
+    const size_t nb = (size_t)K * sizeof(float);
+    if (overlap(out, nb, x, nb) || overlap(out, nb, gamma, nb))
+        return fail(QG_EINVAL, "%s: out overlaps x or gamma", fn);
+    hipError_t e = qgk::launch_rmsnorm(x, gamma, eps, out, K, as_stream(stream));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
 }
 
 qg_status qgemv_fused_gateup_silu(int qtype, const void *w_gateup_packed, const float *x, float *y, int64_t N_ff,

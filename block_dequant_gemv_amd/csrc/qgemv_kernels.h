@@ -30,6 +30,10 @@ struct QArgs {
     const float *bias;
     const float *residual;
     int out_f16;         // 1: y holds fp16 values (round to nearest even), 0: fp32
+    // RMSNorm prologue only: the staged activations become (x * r) * gamma,
+    // r = 1 / sqrt(sum(x^2) / K + eps)
+    const float *gamma;
+    float eps;
 };
 
 // How one quantised call is split. W depends only on (qtype, rows, K) so that
@@ -46,6 +50,7 @@ struct QPlan {
     int depth;           // units in flight ahead of the one being computed (1 or 2; 2 only for M = 1)
     bool x_in_lds;       // activations staged in LDS
     size_t lds_bytes;    // dynamic LDS per workgroup
+    bool norm;           // RMSNorm prologue on the staged activations (M = 1, x_in_lds)
 };
 
 struct F16Plan {
@@ -73,6 +78,7 @@ constexpr int persist_threads(int qt, int M, bool xlds)
 
 hipError_t launch_qgemv(int qt, int M, int epi, const QPlan &p, const uint8_t *wp, const float *x, float *y,
                         const QArgs &a, hipStream_t s);
+hipError_t launch_rmsnorm(const float *x, const float *gamma, float eps, float *out, int64_t K, hipStream_t s);
 hipError_t launch_f16(const F16Plan &p, const uint16_t *w, const float *x, float *y, int64_t N, int64_t K,
                       hipStream_t s);
 hipError_t launch_pack(const qgl::Geometry &g, const uint8_t *canon, const uint8_t *canon_up, uint8_t *packed,

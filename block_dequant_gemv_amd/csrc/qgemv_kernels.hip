@@ -303,6 +303,56 @@ __device__ __forceinline__ void stage_x_finish(const XFirst &f, f32x4 *xs4, cons
     }
 }
 
+// Sum of squares of one thread's values, then of the workgroup: a per-thread fma
+// chain, the wavefront butterfly (both halves), then the wavefront partials added
+// in wavefront order through `red` (one float per wavefront). Every thread gets
+// the same bits. The caller's threads must all arrive; `red` is reused after a
+// barrier.
+__device__ __forceinline__ float block_sum(float s, float *red)
+{
+    const uint32_t nthr = blockDim.x, tid = threadIdx.x;
+    const float h = half_wave_sum(s);
+    const float w = as_f(__builtin_amdgcn_readlane(as_i(h), 0)) + as_f(__builtin_amdgcn_readlane(as_i(h), 32));
+    if ((tid & 63) == 0) red[tid >> 6] = w;
+    __syncthreads();
+    float t = red[0];
+    for (uint32_t i = 1; i < (nthr >> 6); ++i) t += red[i];
+    __syncthreads();
+    return t;
+}
+
+// 1 / sqrt(mean + eps), correctly rounded square root and division.
+__device__ __forceinline__ float rms_scale(float ss, int64_t K, float eps)
+{
+    return 1.0f / __builtin_sqrtf(ss / (float)K + eps);
+}
+
+// RMSNorm prologue: the staged activations (row 0, float4 chunk i at
+// xs4[x_slot(i)], zero past K) become (x * r) * gamma in place, with
+// r = 1 / sqrt(sum(x^2) / K + eps). Every thread of the workgroup must call it.
+__device__ __forceinline__ void norm_staged_x(f32x4 *xs4, float *red, const float *__restrict__ gamma, float eps,
+                                              int64_t K)
+{
+    const uint32_t k4 = (uint32_t)(K >> 2);
+    const uint32_t nthr = blockDim.x, tid = threadIdx.x;
+    float s = 0.0f;
+    for (uint32_t i = tid; i < k4; i += nthr) {
+        const f32x4 v = xs4[x_slot(i)];
+        s = __builtin_fmaf(v.x, v.x, s);
+        s = __builtin_fmaf(v.y, v.y, s);
+        s = __builtin_fmaf(v.z, v.z, s);
+        s = __builtin_fmaf(v.w, v.w, s);
+    }
+    const float r = rms_scale(block_sum(s, red), K, eps);
+    for (uint32_t i = tid; i < k4; i += nthr) {
+        const uint32_t sl = x_slot(i);
+        const f32x4 gm = *(const f32x4 *)(gamma + 4 * (size_t)i);
+        const f32x4 v = xs4[sl];
+        xs4[sl] = f32x4{(v.x * r) * gm.x, (v.y * r) * gm.y, (v.z * r) * gm.z, (v.w * r) * gm.w};
+    }
+    __syncthreads();
+}
+
 // Store output n of activation row m (n < n_out). The affine epilogue adds the
 // bias and then the residual to the finished product, one fp32 addition each,
 // and writes fp32 or fp16 (v_cvt_f16_f32, round to nearest even). The residual
@@ -379,14 +429,15 @@ __device__ __forceinline__ void store_tile(const float (&acc)[M][kRowsPerLane], 
 // Which group handles a tile changes none of its rows' operations.
 // Each wavefront walks its (tile, segment) sequence with the loads of the next
 // D units in flight while the current one is computed (a ring of D+1 units).
-template <int QT, int M, int EPI, int W, bool XLDS, int D>
+template <int QT, int M, int EPI, int W, bool XLDS, int D, bool NORM>
 __global__ void __launch_bounds__(512)
 qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float *__restrict__ y, QArgs a)
 {
+    static_assert(!NORM || (XLDS && M == 1), "the RMSNorm prologue works on staged single-row activations");
     constexpr int B = kRowsPerLane;
     constexpr int S = D + 1;   // ring size
     extern __shared__ f32x4 xs4[];
-    __shared__ float red[(W > 1) ? W * M * kSlots * B : 1];  // [W][M][slot][b]
+    __shared__ float red[(W > 1) ? W * M * kSlots * B : (NORM ? 8 : 1)];  // [W][M][slot][b]; norm: [wavefront]
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -437,6 +488,7 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
         stage_x_finish<M>(xf, xs4, x, a.x_stride, nseg, K);
         __syncthreads();
     }
+    if (NORM) norm_staged_x(xs4, red, a.gamma, a.eps, K);
     if (n_units == 0) return;   // uniform across the workgroup when W > 1
 
     float acc[M][B];
@@ -523,13 +575,15 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
 // range order, ((p0 + p1) + p2) + ..., and stored (with the SiLU epilogue for
 // gate|up). For any M a row goes through the same operations, so the verify
 // rows still equal the M=1 rows bit for bit.
-template <int QT, int M, int EPI, bool XLDS>
+template <int QT, int M, int EPI, bool XLDS, bool NORM>
 __global__ void __launch_bounds__(persist_threads(QT, M, XLDS))
 qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float *__restrict__ y, QArgs a)
 {
+    static_assert(!NORM || (XLDS && M == 1), "the RMSNorm prologue works on staged single-row activations");
     constexpr int B = kRowsPerLane;
     constexpr int S = 2;   // ring: one unit in flight ahead of the one being computed
     extern __shared__ f32x4 xs4[];
+    __shared__ float nred[NORM ? 16 : 1];
 
     const int tid = threadIdx.x;
     const int G = blockDim.x >> 6;
@@ -586,6 +640,7 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
         stage_x_finish<M>(xf, xs4, x, a.x_stride, nseg, K);
         __syncthreads();
     }
+    if (NORM) norm_staged_x(xs4, nred, a.gamma, a.eps, K);
 
     float acc[M][B];
 #pragma unroll
@@ -726,6 +781,22 @@ gemv_f16_kernel(const uint16_t *__restrict__ w, const float *__restrict__ x, flo
 }
 
 // ---------------------------------------------------------------------------
+// Standalone RMSNorm of one activation vector (one workgroup): out[k] =
+// (x[k] * r) * gamma[k], r = 1 / sqrt(sum(x^2) / K + eps), with the same
+// reduction scheme as the GEMV prologue.
+__global__ void __launch_bounds__(1024)
+rmsnorm_kernel(const float *__restrict__ x, const float *__restrict__ gamma, float eps, float *__restrict__ out,
+               int64_t K)
+{
+    __shared__ float red[16];
+    const int64_t tid = threadIdx.x, nthr = blockDim.x;
+    float s = 0.0f;
+    for (int64_t k = tid; k < K; k += nthr) s = __builtin_fmaf(x[k], x[k], s);
+    const float r = rms_scale(block_sum(s, red), K, eps);
+    for (int64_t k = tid; k < K; k += nthr) out[k] = (x[k] * r) * gamma[k];
+}
+
+// ---------------------------------------------------------------------------
 // Load-time packing: one thread per (packed row, block).
 //   mode kPackRows:   packed rows [row0, row0 + nrows) <- canonical rows 0..nrows-1,
 //                     plus zero padding rows [N, n_tiles*8) when row0 + nrows == N
@@ -793,11 +864,11 @@ static void launch(Kern kern, dim3 grid, dim3 block, uint32_t lds, hipStream_t s
         hipLaunchKernelGGL(kern, grid, block, lds, stream, args...);
 }
 
-template <int QT, int M, int EPI, int W, bool XLDS, int D>
+template <int QT, int M, int EPI, int W, bool XLDS, int D, bool NORM = false>
 static hipError_t launch_q(const uint8_t *wp, const float *x, float *y, const QArgs &a, int64_t grid, int block,
                            size_t lds, hipStream_t stream)
 {
-    auto kern = qgemv_kernel<QT, M, EPI, W, XLDS, D>;
+    auto kern = qgemv_kernel<QT, M, EPI, W, XLDS, D, NORM>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -808,8 +879,16 @@ static hipError_t launch_q(const uint8_t *wp, const float *x, float *y, const QA
 
 template <int QT, int M, int EPI, int W>
 static hipError_t dispatch_x(const uint8_t *wp, const float *x, float *y, const QArgs &a, int64_t grid, int block,
-                             size_t lds, bool xlds, int depth, hipStream_t s)
+                             size_t lds, bool xlds, int depth, bool norm, hipStream_t s)
 {
+    // the RMSNorm prologue: single-row plain and gate|up kernels, staged activations, depth 1
+    if constexpr (M == 1 && EPI != kEpiAffine) {
+        if (norm) {
+            if (!xlds) return hipErrorInvalidConfiguration;
+            return launch_q<QT, M, EPI, W, true, 1, true>(wp, x, y, a, grid, block, lds, s);
+        }
+    }
+    if (norm) return hipErrorInvalidConfiguration;
     // prefetch depth 2 is instantiated for the single-row kernels without the
     // affine epilogue only (elsewhere a request for it runs depth 1)
     if constexpr (M == 1 && EPI != kEpiAffine) {
@@ -823,13 +902,13 @@ static hipError_t dispatch_x(const uint8_t *wp, const float *x, float *y, const 
 
 template <int QT, int M, int EPI>
 static hipError_t dispatch_w(const uint8_t *wp, const float *x, float *y, const QArgs &a, int W, int64_t grid,
-                             int block, size_t lds, bool xlds, int depth, hipStream_t s)
+                             int block, size_t lds, bool xlds, int depth, bool norm, hipStream_t s)
 {
     switch (W) {
-    case 1: return dispatch_x<QT, M, EPI, 1>(wp, x, y, a, grid, block, lds, xlds, depth, s);
-    case 2: return dispatch_x<QT, M, EPI, 2>(wp, x, y, a, grid, block, lds, xlds, depth, s);
-    case 4: return dispatch_x<QT, M, EPI, 4>(wp, x, y, a, grid, block, lds, xlds, depth, s);
-    default: return dispatch_x<QT, M, EPI, 8>(wp, x, y, a, grid, block, lds, xlds, depth, s);
+    case 1: return dispatch_x<QT, M, EPI, 1>(wp, x, y, a, grid, block, lds, xlds, depth, norm, s);
+    case 2: return dispatch_x<QT, M, EPI, 2>(wp, x, y, a, grid, block, lds, xlds, depth, norm, s);
+    case 4: return dispatch_x<QT, M, EPI, 4>(wp, x, y, a, grid, block, lds, xlds, depth, norm, s);
+    default: return dispatch_x<QT, M, EPI, 8>(wp, x, y, a, grid, block, lds, xlds, depth, norm, s);
     }
 }
 
@@ -837,7 +916,16 @@ template <int QT, int M, int EPI>
 static hipError_t launch_persist(const uint8_t *wp, const float *x, float *y, const QArgs &a, const QPlan &p,
                                  hipStream_t stream)
 {
-    auto kern = p.x_in_lds ? qgemv_persist<QT, M, EPI, true> : qgemv_persist<QT, M, EPI, false>;
+    auto kern = p.x_in_lds ? qgemv_persist<QT, M, EPI, true, false> : qgemv_persist<QT, M, EPI, false, false>;
+    if (p.norm) {
+        // the RMSNorm prologue: single-row plain and gate|up kernels with staged activations
+        if constexpr (M == 1 && EPI != kEpiAffine) {
+            if (!p.x_in_lds) return hipErrorInvalidConfiguration;
+            kern = qgemv_persist<QT, M, EPI, true, true>;
+        } else {
+            return hipErrorInvalidConfiguration;
+        }
+    }
     if (p.block != persist_threads(QT, M, p.x_in_lds)) return hipErrorInvalidConfiguration;
     if (p.lds_bytes > 64 * 1024) {
         hipError_t e =
@@ -853,7 +941,7 @@ static hipError_t dispatch_form(const uint8_t *wp, const float *x, float *y, con
                                 hipStream_t s)
 {
     if (p.persist) return launch_persist<QT, M, EPI>(wp, x, y, a, p, s);
-    return dispatch_w<QT, M, EPI>(wp, x, y, a, p.W, p.grid, p.block, p.lds_bytes, p.x_in_lds, p.depth, s);
+    return dispatch_w<QT, M, EPI>(wp, x, y, a, p.W, p.grid, p.block, p.lds_bytes, p.x_in_lds, p.depth, p.norm, s);
 }
 
 template <int QT>
@@ -877,6 +965,12 @@ hipError_t launch_qgemv(int qt, int M, int epi, const QPlan &p, const uint8_t *w
 {
     if (qt == kQ8_0) return dispatch_m<kQ8_0>(wp, x, y, a, M, epi, p, s);
     return dispatch_m<kQ4_0>(wp, x, y, a, M, epi, p, s);
+}
+
+hipError_t launch_rmsnorm(const float *x, const float *gamma, float eps, float *out, int64_t K, hipStream_t s)
+{
+    launch(rmsnorm_kernel, dim3(1), dim3(1024), 0u, s, x, gamma, eps, out, K);
+    return hipGetLastError();
 }
 
 hipError_t launch_f16(const F16Plan &p, const uint16_t *w, const float *x, float *y, int64_t N, int64_t K,

@@ -143,6 +143,35 @@ qg_status gemv_f16_splitk(const void *w_f16, const float *x, float *y, int64_t N
 qg_status qgemv_fused_gateup_silu(int qtype, const void *w_gateup_packed, const float *x, float *y,
                                   int64_t N_ff, int64_t K, void *stream);
 
+/* RMSNorm of one activation vector (RunIT_Mac README, kernel table and
+ * data-flow figure: f32 input, f32 gamma, f32 output):
+ *   out[k] = (x[k] * r) * gamma[k],   r = 1 / sqrt(sum_j x[j]^2 / K + eps)
+ * in fp32: the sum of squares is a fixed-order reduction (deterministic), the
+ * square root and the division are correctly rounded. One workgroup. x, gamma,
+ * out fp32 [K] (K >= 1), 4-byte aligned; out must not overlap x or gamma; eps
+ * finite and >= 0 (the pages give no value; Qwen-style models use 1e-6). This
+ * is the unfused form of the prologue below. */
+qg_status qg_rmsnorm(const float *x, const float *gamma, float eps, float *out, int64_t K, void *stream);
+
+/* GEMV with the RMSNorm of its activation fused into the prologue ("EdgeRunner
+ * beats llama.cpp", The progression: RMSNorm+GEMV kernel fusion; the
+ * robotnurse.io post, Things that lost, measured the same fusion as a loss from
+ * L2 re-reads per threadgroup): y = W * rmsnorm(x), one dispatch. Every
+ * workgroup stages x in LDS, reduces sum(x^2) itself and normalises its copy,
+ * then runs the GEMV of qgemv_q8_0 / qgemv_q4_0 on it. Arguments as for those
+ * calls plus gamma fp32 [K] (16-byte aligned, not overlapping y) and eps as in
+ * qg_rmsnorm. K <= 40960 (the normalised copy lives in LDS), else
+ * QG_EUNSUPPORTED. The result is within the linear tolerance of the exact
+ * product on the exact normalised vector; it is not bitwise equal to
+ * qg_rmsnorm followed by the plain GEMV (another reduction order). */
+qg_status qgemv_rmsnorm(int qtype, const void *w_packed, const float *x, const float *gamma, float eps, float *y,
+                        int64_t N, int64_t K, void *stream);
+
+/* The fused gate|up SiLU GEMV with the same RMSNorm prologue:
+ * y[n] = silu(g[n]) * u[n], g = W_gate * rmsnorm(x), u = W_up * rmsnorm(x). */
+qg_status qgemv_rmsnorm_gateup_silu(int qtype, const void *w_gateup_packed, const float *x, const float *gamma,
+                                    float eps, float *y, int64_t N_ff, int64_t K, void *stream);
+
 /* Multi-row "verify" GEMV: Y[m][n] = sum_k W[n][k] X[m][k] for 2 <= M <= 6,
  * X fp32 row-major [M][K], Y fp32 row-major [M][N]. The packed weights are
  * streamed once for all M rows, and row m of Y is bit-for-bit (memcmp) equal
@@ -181,9 +210,9 @@ qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int *split_k_ways
  * with different overrides in effect. Returns QG_OK. */
 qg_status qg_reload_tuning(void);
 
-/* Time the next GEMV kernel (qgemv_q8_0, qgemv_q4_0, qgemv_epilogue,
- * gemv_f16_splitk, qgemv_fused_gateup_silu or qgemv_verify) that the calling
- * thread launches.
+/* Time the next kernel that the calling thread launches through qgemv_q8_0,
+ * qgemv_q4_0, qgemv_epilogue, qgemv_rmsnorm, qgemv_rmsnorm_gateup_silu,
+ * qg_rmsnorm, gemv_f16_splitk, qgemv_fused_gateup_silu or qgemv_verify.
  * start_event and stop_event are hipEvent_t handles, created by the caller
  * with timing enabled and owned by the caller. That call's kernel records its
  * own start and end time into them (the dispatch's timestamps, which a

@@ -132,6 +132,37 @@ def test_epilogue_argument_checks_without_gpu(L):
     assert "overlap" in qg.qg_last_error()
 
 
+def test_rmsnorm_argument_checks_without_gpu(L):
+    import ctypes as C
+    f = FAKE
+    w, x, g, y = f, f + (1 << 20), f + (2 << 20), f + (3 << 20)
+    e = C.c_float
+    rn = lambda *a: call(L, "qg_rmsnorm", *a)  # noqa: E731
+    gn = lambda *a: call(L, "qgemv_rmsnorm", *a)  # noqa: E731
+    gu = lambda *a: call(L, "qgemv_rmsnorm_gateup_silu", *a)  # noqa: E731
+    # qg_rmsnorm(x, gamma, eps, out, K, stream)
+    assert rn(None, g, e(1e-6), y, 8, None) == qg.QG_EINVAL
+    assert rn(x, g, e(1e-6), y, 0, None) == qg.QG_EINVAL
+    assert rn(x, g, e(-1.0), y, 8, None) == qg.QG_EINVAL
+    assert rn(x, g, e(float("inf")), y, 8, None) == qg.QG_EINVAL
+    assert rn(x, g, e(float("nan")), y, 8, None) == qg.QG_EINVAL
+    assert rn(x + 2, g, e(1e-6), y, 8, None) == qg.QG_EALIGN
+    assert rn(x, g, e(1e-6), x + 16, 8, None) == qg.QG_EINVAL      # out overlaps x
+    assert rn(x, g, e(1e-6), g, 8, None) == qg.QG_EINVAL           # out is gamma
+    # qgemv_rmsnorm(qtype, w, x, gamma, eps, y, N, K, stream)
+    assert gn(1, w, x, None, e(1e-6), y, 8, 32, None) == qg.QG_EINVAL
+    assert gn(1, w, x, g + 4, e(1e-6), y, 8, 32, None) == qg.QG_EALIGN
+    assert gn(2, w, x, g, e(-1e-3), y, 8, 32, None) == qg.QG_EINVAL
+    assert gn(2, w, x, g, e(1e-6), y, 8, 40960 + 32, None) == qg.QG_EUNSUPPORTED
+    assert gn(2, w, x, y - 16, e(1e-6), y, 8, 32, None) == qg.QG_EINVAL   # y overlaps gamma
+    assert gn(4, w, x, g, e(1e-6), y, 8, 32, None) == qg.QG_EUNSUPPORTED
+    assert gn(1, w, x, g, e(1e-6), y, 8, 48, None) == qg.QG_EINVAL
+    # qgemv_rmsnorm_gateup_silu(qtype, w, x, gamma, eps, y, N_ff, K, stream)
+    assert gu(1, w, x, g, e(1e-6), y, 0, 32, None) == qg.QG_EINVAL
+    assert gu(1, w, x, None, e(1e-6), y, 8, 32, None) == qg.QG_EINVAL
+    assert gu(2, w, x, g, e(1e-6), y, 8, 65536, None) == qg.QG_EUNSUPPORTED
+
+
 def test_time_next_launch_arguments(L):
     # host-only: binding or clearing events makes no HIP call
     f = FAKE
