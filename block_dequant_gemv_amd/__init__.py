@@ -29,7 +29,7 @@ SYMBOLS = (
     "qg_packed_size", "qg_pack", "qg_pack_rows", "qg_pack_gateup",
     "qg_pack_host", "qg_unpack_host", "qg_pack_gateup_host",
     "qgemv_q8_0", "qgemv_q4_0", "qgemv_epilogue", "gemv_f16_splitk", "qgemv_fused_gateup_silu", "qgemv_verify",
-    "qg_rmsnorm", "qgemv_rmsnorm", "qgemv_rmsnorm_gateup_silu",
+    "qg_rmsnorm", "qgemv_rmsnorm", "qgemv_rmsnorm_gateup_silu", "qg_prefill_workspace_size", "qgemm_prefill",
     "qg_status_str", "qg_last_error", "qg_plan_info", "qg_time_next_launch", "qg_reload_tuning",
 )
 
@@ -71,6 +71,8 @@ def lib():
             "qgemv_q4_0": ([vp, vp, vp, i64, i64, vp], i32),
             "qgemv_epilogue": ([i32, vp, vp, vp, vp, vp, i32, i64, i64, vp], i32),
             "qg_rmsnorm": ([vp, vp, ctypes.c_float, vp, i64, vp], i32),
+            "qg_prefill_workspace_size": ([i64, i64], sz),
+            "qgemm_prefill": ([i32, vp, vp, vp, i64, i64, i64, vp, sz, vp], i32),
             "qgemv_rmsnorm": ([i32, vp, vp, vp, ctypes.c_float, vp, i64, i64, vp], i32),
             "qgemv_rmsnorm_gateup_silu": ([i32, vp, vp, vp, ctypes.c_float, vp, i64, i64, vp], i32),
             "gemv_f16_splitk": ([vp, vp, vp, i64, i64, vp], i32),
@@ -217,6 +219,22 @@ def qgemv_rmsnorm_gateup_silu(qtype, w_gateup_packed, x, gamma, eps: float, y, N
            lib().qgemv_rmsnorm_gateup_silu(_qtype(qtype), _dev(w_gateup_packed, "w_gateup_packed"),
                                            _dev(x, "x", _f32()), _dev(gamma, "gamma", _f32()), float(eps),
                                            _dev(y, "y", _f32()), N_ff, K, _stream(stream)))
+
+
+def qg_prefill_workspace_size(M: int, K: int) -> int:
+    return int(lib().qg_prefill_workspace_size(M, K))
+
+
+def qgemm_prefill(qtype, w_packed, X, Y, N: int, K: int, M: int, workspace=None, stream=None):
+    """Y[M][N] = X W^T on the matrix cores. `workspace` is a uint8 device tensor of at
+    least qg_prefill_workspace_size(M, K) bytes (allocated here with torch if None)."""
+    import torch
+    if workspace is None:
+        workspace = torch.empty(qg_prefill_workspace_size(M, K), dtype=torch.uint8, device=X.device)
+    _check("qgemm_prefill", lib().qgemm_prefill(_qtype(qtype), _dev(w_packed, "w_packed"), _dev(X, "X", _f32()),
+                                                _dev(Y, "Y", _f32()), N, K, M, _dev(workspace, "workspace"),
+                                                workspace.numel() * workspace.element_size(), _stream(stream)))
+    return workspace
 
 
 def gemv_f16_splitk(w_f16, x, y, N: int, K: int, stream=None):

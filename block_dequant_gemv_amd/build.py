@@ -22,8 +22,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqgemv.so")
-SOURCES = ["qgemv_kernels.hip", "qgemv_api.hip"]
-HEADERS = ["layout.h", "qgemv_kernels.h"]
+SOURCES = ["qgemv_kernels.hip", "qgemm_kernels.hip", "qgemv_api.hip"]
+HEADERS = ["layout.h", "dequant.h", "qgemv_kernels.h", "qgemm_kernels.h"]
 
 
 def hipcc() -> str:

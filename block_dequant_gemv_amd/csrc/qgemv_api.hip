@@ -14,6 +14,7 @@
 #include <string>
 
 #include "layout.h"
+#include "qgemm_kernels.h"
 #include "qgemv.h"
 #include "qgemv_kernels.h"
 
@@ -78,15 +79,16 @@ int64_t env_int(const char *name, int64_t dflt)
 
 // Launch-shape overrides for sweeps and tests (QG_SPLIT_K, QG_PERSIST,
 // QG_X_GLOBAL, QG_TILES_PER_GROUP, QG_WAVES_PER_WG, QG_PREFETCH, QG_F16_ROWS,
-// QG_F16_WAVES, QG_STRIDE_GROUPS). They are read from the environment once, on first use, and
+// QG_F16_WAVES, QG_STRIDE_GROUPS, QG_GEMM_MT, QG_GEMM_WAVES). They are read from the environment once, on first use, and
 // again on qg_reload_tuning(): a GEMV call itself reads no environment.
 enum TuneKey {
-    kSplitK, kPersist, kXGlobal, kTilesPerGroup, kWavesPerWg, kPrefetch, kF16Rows, kF16Waves, kStrideGroups, kNumTune
+    kSplitK, kPersist, kXGlobal, kTilesPerGroup, kWavesPerWg, kPrefetch, kF16Rows, kF16Waves, kStrideGroups,
+    kGemmMT, kGemmWaves, kNumTune
 };
 const char *const kTuneNames[kNumTune] = {"QG_SPLIT_K",      "QG_PERSIST",  "QG_X_GLOBAL",  "QG_TILES_PER_GROUP",
                                           "QG_WAVES_PER_WG", "QG_PREFETCH", "QG_F16_ROWS",  "QG_F16_WAVES",
-                                          "QG_STRIDE_GROUPS"};
-const int64_t kTuneDefaults[kNumTune] = {0, -1, -1, 0, 0, 0, 0, 0, -1};
+                                          "QG_STRIDE_GROUPS", "QG_GEMM_MT", "QG_GEMM_WAVES"};
+const int64_t kTuneDefaults[kNumTune] = {0, -1, -1, 0, 0, 0, 0, 0, -1, 0, 0};
 std::atomic<int64_t> g_tune[kNumTune];
 std::atomic<bool> g_tune_loaded{false};
 
@@ -352,6 +354,14 @@ void host_pack_rows(const Geometry &g, const uint8_t *canon, uint8_t *packed, in
             for (int64_t b = 0; b < g.KB; ++b) qgl::pack_block(g, nullptr, packed, r, b);
 }
 
+// Small-M GEMM: activation rows are processed in tiles of 16 (the last one
+// padded with zeros); the workspace holds one unscale factor per padded row
+// (256-byte aligned block) and the split activations, M_pad * K * 2 halves.
+constexpr int64_t kGemmMaxM = (int64_t)1 << 20;
+
+int64_t gemm_m_pad(int64_t M) { return (M + qgk::kGemmTileM - 1) / qgk::kGemmTileM * qgk::kGemmTileM; }
+size_t gemm_unscale_bytes(int64_t M) { return (size_t)qgl::round_up(gemm_m_pad(M) * (int64_t)sizeof(float), 256); }
+
 }  // namespace
 
 extern "C" {
@@ -504,6 +514,67 @@ qg_status qg_rmsnorm(const float *x, const float *gamma, float eps, float *out, 
         return fail(QG_EINVAL, "%s: out overlaps x or gamma", fn);
     hipError_t e = qgk::launch_rmsnorm(x, gamma, eps, out, K, as_stream(stream));
     if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+// ---- small-M GEMM (prefill chunks) ------------------------------------------
+
+size_t qg_prefill_workspace_size(int64_t M, int64_t K)
+{
+    if (M <= 0 || M > kGemmMaxM || K <= 0 || K % 32 || K > kMaxDim) return 0;
+    return gemm_unscale_bytes(M) + (size_t)gemm_m_pad(M) * (size_t)K * 2 * sizeof(_Float16);
+}
+
+qg_status qgemm_prefill(int qtype, const void *w_packed, const float *X, float *Y, int64_t N, int64_t K, int64_t M,
+                        void *workspace, size_t workspace_bytes, void *stream)
+{
+    const char *fn = "qgemm_prefill";
+    qg_status st = check_qshape(qtype, N, K, fn);
+    if (st) return st;
+    if (M <= 0 || M > kGemmMaxM) return fail(QG_EINVAL, "%s: M=%lld outside 1..%lld", fn, (long long)M,
+                                             (long long)kGemmMaxM);
+    if (!w_packed || !X || !Y || !workspace) return fail(QG_EINVAL, "%s: null pointer", fn);
+    if (!aligned(w_packed, 16)) return fail(QG_EALIGN, "%s: packed weights must be 16-byte aligned", fn);
+    if (!aligned(X, 4) || !aligned(Y, 4)) return fail(QG_EALIGN, "%s: X and Y must be 4-byte aligned", fn);
+    if (!aligned(workspace, 256)) return fail(QG_EALIGN, "%s: workspace must be 256-byte aligned", fn);
+    const size_t need = qg_prefill_workspace_size(M, K);
+    if (workspace_bytes < need)
+        return fail(QG_EINVAL, "%s: workspace of %zu bytes, %zu needed (qg_prefill_workspace_size)", fn,
+                    workspace_bytes, need);
+    const Geometry g = qgl::geometry(qtype, N, K);
+    const size_t xb = (size_t)M * (size_t)K * sizeof(float), yb = (size_t)M * (size_t)N * sizeof(float);
+    if (overlap(Y, yb, X, xb) || overlap(Y, yb, w_packed, (size_t)g.total) || overlap(Y, yb, workspace, need))
+        return fail(QG_EINVAL, "%s: Y overlaps X, the weights or the workspace", fn);
+    if (overlap(workspace, need, X, xb) || overlap(workspace, need, w_packed, (size_t)g.total))
+        return fail(QG_EINVAL, "%s: the workspace overlaps X or the weights", fn);
+
+    const int64_t M_pad = gemm_m_pad(M);
+    float *unscale = (float *)workspace;
+    _Float16 *xs = (_Float16 *)((uint8_t *)workspace + gemm_unscale_bytes(M));
+    hipStream_t s = as_stream(stream);
+    // the split pass is not timed: a bound event pair goes to the first GEMM pass
+    hipError_t e = qgk::launch_split_x(qtype, X, xs, unscale, M, M_pad, K, s);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    // activation tiles per pass (LDS: 64 KiB each) and wavefronts per workgroup (16 weight rows each)
+    int MT = qgk::kGemmMaxMT;
+    const int64_t mt_env = tune(kGemmMT);
+    if (mt_env == 1 || mt_env == 2) MT = (int)mt_env;
+    int G = 8;
+    const int64_t g_env = tune(kGemmWaves);
+    if (g_env >= 1 && g_env <= 8) G = (int)g_env;
+    const int64_t n_mt = M_pad / qgk::kGemmTileM;
+    const int64_t grid = (g.n_tiles + 2 * G - 1) / (2 * G);
+    qgk::GemmArgs a;
+    a.geo = g;
+    a.N = N;
+    a.M = M;
+    a.y_stride = N;
+    for (int64_t mt0 = 0; mt0 < n_mt; mt0 += MT) {
+        a.mt0 = mt0;
+        const int mt = (int)std::min<int64_t>(MT, n_mt - mt0);
+        e = qgk::launch_qgemm(qtype, mt, (const uint8_t *)w_packed, xs, unscale, Y, a, grid, 64 * G, s);
+        if (e != hipSuccess) return hip_fail(e, fn);
+    }
     return ok();
 }
 

@@ -2,6 +2,7 @@
 // the kernels (qgemv_kernels.hip). Not installed; not part of the public ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -64,6 +65,21 @@ struct F16Plan {
 // receive that kernel's own start and end timestamps. The launch takes them
 // and clears the setting; (nullptr, nullptr) clears it too.
 void set_launch_events(hipEvent_t start, hipEvent_t stop);
+void take_launch_events(hipEvent_t &start, hipEvent_t &stop);
+
+// Launch `kern` on `stream`: with timing events bound, through hipExtLaunchKernel
+// (the events take the dispatch's start and end times); otherwise as a plain
+// launch, which a caller may also record into a HIP graph.
+template <typename Kern, typename... Args>
+inline void launch_timed(Kern kern, dim3 grid, dim3 block, uint32_t lds, hipStream_t stream, Args... args)
+{
+    hipEvent_t e0, e1;
+    take_launch_events(e0, e1);
+    if (e0 != nullptr)
+        hipExtLaunchKernelGGL(kern, grid, block, lds, stream, e0, e1, 0u, args...);
+    else
+        hipLaunchKernelGGL(kern, grid, block, lds, stream, args...);
+}
 
 // Threads per workgroup of the persistent form (its launch bound): as many
 // wavefronts as one CU holds at the kernel's register count. Single-row

@@ -29,10 +29,14 @@ CALIB_BYTES = 256 << 20
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 
+GEMV_SOURCES = ("layout.h", "dequant.h", "qgemv_kernels.h", "qgemv_kernels.hip", "qgemv_api.hip")
+
+
 def kernel_source_hash() -> str:
-    """Hash of the kernel sources; counter results are only valid for the sources they were taken on."""
+    """Hash of the GEMV path's sources (kernels, layout, launch planning); the counter
+    results of its kernels are only valid for the sources they were taken on."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
+    for p in [os.path.join(CSRC, n) for n in GEMV_SOURCES]:
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode())
             h.update(f.read())

@@ -1,0 +1,107 @@
+"""GPU parity of the small-M GEMM (qgemm_prefill, matrix cores) against the fp64
+oracle: Y[m] = W X[m] for every activation row, within the linear bound
+1e-5 * sum|w x| + 1e-7 of each output. Shapes span several row tiles and
+workgroups, a ragged last weight tile, a ragged last K segment, M below, at
+and across the 16-row activation tile and the 32-row pass, and the two pass
+widths (QG_GEMM_MT = 1 / 2)."""
+import os
+
+import numpy as np
+import pytest
+
+import block_dequant_gemv_amd as qg
+import oracle as O
+from block_dequant_gemv_amd import workloads as W
+from gpu_helpers import THREADS, announce, assert_linear, sync, to_dev, torch_dev
+
+pytestmark = pytest.mark.gpu
+
+# (N, K, M)
+SHAPES = [(4096, 1024, 16), (1024, 3072, 8), (300, 2080, 20), (33, 1056, 1), (257, 5120, 40), (2048, 17408, 3),
+          (1000, 1024, 64), (17408, 5120, 32)]
+
+
+def _run(kind, packed, X, N, K, M, tail=0, ws=None):
+    torch = torch_dev()
+    Y = torch.full((M * N + tail,), -9.0, dtype=torch.float32, device="cuda")
+    ws = qg.qgemm_prefill(kind, packed, to_dev(X), Y, N, K, M, workspace=ws)
+    sync()
+    out = Y.cpu().numpy()
+    return out[:M * N].reshape(M, N), out[M * N:], ws
+
+
+@pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
+@pytest.mark.parametrize("N,K,M", SHAPES)
+def test_gemm_matches_oracle(kind, N, K, M):
+    rng = np.random.default_rng(7000 + N + K + M)
+    canon = W.matrix(kind, N, K, rng)
+    X = W.activation(K, rng, M=M).reshape(M, K)
+    packed = qg.pack_weights(kind, canon, N, K)
+    announce(f"qgemm_prefill {kind} N={N} K={K} M={M}")
+    Y, tail, _ = _run(kind, packed, X, N, K, M, tail=9)
+    assert np.all(tail == -9.0), "wrote past Y"
+    Y_ref, A_ref = O.verify(kind, canon, X, N, K, threads=THREADS)
+    for m in range(M):
+        assert_linear(Y[m], Y_ref[m], A_ref[m], f"gemm {kind} {N}x{K} M={M} row {m}")
+
+
+@pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
+def test_gemm_pass_widths_and_determinism(kind):
+    N, K, M = 640, 5120, 48
+    rng = np.random.default_rng(31)
+    canon = W.matrix(kind, N, K, rng)
+    X = W.activation(K, rng, M=M).reshape(M, K)
+    packed = qg.pack_weights(kind, canon, N, K)
+    Y_ref, A_ref = O.verify(kind, canon, X, N, K, threads=THREADS)
+    outs = {}
+    try:
+        for mt in ("1", "2"):
+            os.environ["QG_GEMM_MT"] = mt
+            qg.qg_reload_tuning()
+            announce(f"qgemm_prefill {kind} passes of {mt} activation tiles")
+            Y, _, ws = _run(kind, packed, X, N, K, M)
+            Y2, _, _ = _run(kind, packed, X, N, K, M, ws=ws)
+            assert Y.tobytes() == Y2.tobytes(), "run-to-run bits differ"
+            for m in range(M):
+                assert_linear(Y[m], Y_ref[m], A_ref[m], f"gemm {kind} MT={mt} row {m}")
+            outs[mt] = Y
+    finally:
+        os.environ.pop("QG_GEMM_MT", None)
+        qg.qg_reload_tuning()
+    # the pass width changes which workgroup computes a row, not its operations
+    assert outs["1"].tobytes() == outs["2"].tobytes()
+
+
+@pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
+def test_gemm_row_scaling_handles_dynamic_range(kind):
+    # rows of very different magnitude (1e-6 .. 1e6, and an all-zero row): each row
+    # gets its own power-of-two scale before the fp16 split, so every row keeps
+    # the relative accuracy of the linear bound
+    N, K, M = 512, 2048, 6
+    rng = np.random.default_rng(5)
+    canon = W.matrix(kind, N, K, rng)
+    X = W.activation(K, rng, M=M).reshape(M, K)
+    X = X * np.array([1e-6, 1.0, 1e6, 3e-3, 0.0, 2.0 ** 20], np.float32)[:, None]
+    X[5, ::7] *= np.float32(1e-3)     # a wide spread inside one row as well
+    packed = qg.pack_weights(kind, canon, N, K)
+    announce(f"qgemm_prefill {kind} dynamic range")
+    Y, _, _ = _run(kind, packed, X.astype(np.float32), N, K, M)
+    Y_ref, A_ref = O.verify(kind, canon, X.astype(np.float32), N, K, threads=THREADS)
+    for m in range(M):
+        assert_linear(Y[m], Y_ref[m], A_ref[m], f"gemm {kind} dynamic range row {m}")
+    assert np.all(Y[4] == 0.0)
+
+
+def test_gemm_closed_form_exact():
+    # all-equal quants and scales with X = 1: every partial sum is an exact small
+    # integer multiple of d, so the GEMM returns c * d * K exactly in every output
+    torch = torch_dev()
+    K, N, M = 5120, 64, 17
+    for kind, blk, expect in (("q4_0", bytes([0x00, 0x38]) + bytes([0xFF] * 16), 7 * 0.5 * K),
+                              ("q8_0", bytes([0x00, 0x34]) + bytes([3] * 32), 3 * 0.25 * K)):
+        canon = np.frombuffer(blk * (N * K // 32), np.uint8).copy()
+        packed = qg.pack_weights(kind, canon, N, K)
+        announce(f"qgemm_prefill closed form {kind}")
+        Y, _, _ = _run(kind, packed, np.ones((M, K), np.float32), N, K, M)
+        assert np.all(Y == expect), (kind, Y.min(), Y.max())
+    del torch

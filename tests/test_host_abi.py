@@ -163,6 +163,28 @@ def test_rmsnorm_argument_checks_without_gpu(L):
     assert gu(2, w, x, g, e(1e-6), y, 8, 65536, None) == qg.QG_EUNSUPPORTED
 
 
+def test_gemm_argument_checks_without_gpu(L):
+    f = FAKE
+    w, x, y, ws = f, f + (1 << 24), f + (2 << 24), f + (3 << 24)
+    need = qg.qg_prefill_workspace_size(20, 1024)
+    assert need == 256 + 32 * 1024 * 4           # 20 rows padded to 32; one 256-byte block of row factors
+    assert qg.qg_prefill_workspace_size(0, 1024) == 0 and qg.qg_prefill_workspace_size(4, 1000) == 0
+    gm = lambda *a: call(L, "qgemm_prefill", *a)  # noqa: E731
+    # (qtype, w, X, Y, N, K, M, workspace, workspace_bytes, stream)
+    assert gm(1, w, x, y, 64, 1024, 0, ws, need, None) == qg.QG_EINVAL            # M = 0
+    assert gm(1, w, x, y, 64, 1024, 20, None, need, None) == qg.QG_EINVAL         # no workspace
+    assert gm(1, w, x, y, 64, 1024, 20, ws, need - 4, None) == qg.QG_EINVAL       # workspace too small
+    assert "qg_prefill_workspace_size" in qg.qg_last_error()
+    assert gm(1, w, x, y, 64, 1024, 20, ws + 16, need, None) == qg.QG_EALIGN      # workspace alignment
+    assert gm(1, w + 8, x, y, 64, 1024, 20, ws, need, None) == qg.QG_EALIGN       # weight alignment
+    assert gm(1, w, x + 2, y, 64, 1024, 20, ws, need, None) == qg.QG_EALIGN       # X alignment
+    assert gm(2, w, x, x + 64, 64, 1024, 20, ws, need, None) == qg.QG_EINVAL      # Y overlaps X
+    assert gm(2, w, x, y, 64, 1024, 20, y + 256, need, None) == qg.QG_EINVAL      # workspace overlaps Y
+    assert gm(2, w, x, y, 64, 1024, 20, x, need, None) == qg.QG_EINVAL            # workspace overlaps X
+    assert gm(3, w, x, y, 64, 1024, 20, ws, need, None) == qg.QG_EUNSUPPORTED     # unknown qtype
+    assert gm(1, w, x, y, 64, 1000, 20, ws, need, None) == qg.QG_EINVAL           # K % 32
+
+
 def test_time_next_launch_arguments(L):
     # host-only: binding or clearing events makes no HIP call
     f = FAKE
