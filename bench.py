@@ -288,6 +288,23 @@ def per_config_calls(qg, torch, stream, step_calls):
     norm_case("n q4_0 gate|up 2x17408x5120", "q4_0", pg, 17408, 5120, True)
     norm_case("n q4_0 lm_head 248320x5120", "q4_0", pl, 248320, 5120, False)
     res["norm"] = norm_cases
+
+    # the small-M GEMM for prefill chunks (qgemm_prefill) on the same weights, M rows at once
+    gemm_cases = []
+    for label, kind, packed, N, K in (("q8_0 lm_head 151936x1024", "q8_0", lm.weight, 151936, 1024),
+                                      ("q8_0 qkv 4096x1024", "q8_0", qkv.weight, 4096, 1024),
+                                      ("q4_0 down 5120x17408", "q4_0", pd, 5120, 17408),
+                                      ("q4_0 lm_head 248320x5120", "q4_0", pl, 248320, 5120)):
+        for M in (16, 32, 128):
+            X = t(erng.standard_normal((M, K)).astype(np.float32))
+            Y = yb(M * N)
+            ws = torch.empty(qg.qg_prefill_workspace_size(kind, N, K, M), dtype=torch.uint8, device=dev)
+            keep.append(ws)
+            make = (lambda wp, kind=kind, X=X, Y=Y, ws=ws, N=N, K=K, M=M:  # noqa: E731
+                    qg.bound_call("qgemm_prefill", qg.QTYPES[kind], wp, X.data_ptr(), Y.data_ptr(), N, K, M,
+                                  ws.data_ptr(), ws.numel(), stream))
+            gemm_cases.append((f"g {label} M={M}", kind, packed, N, K, M, make))
+    res["gemm"] = gemm_cases
     torch.cuda.synchronize()
     return res, keep
 
@@ -327,6 +344,42 @@ def rmsnorm_fusion(qg, torch, cases, reps):
         out[label] = r
         log(f"  {label:30s} fused {r['fused_us']:8.2f} us | norm {r['norm_us']:6.2f} + gemv {r['gemv_us']:8.2f} us"
             f"   batch: fused {bf:8.2f} us, unfused {bu:8.2f} us ({100 * (bu - bf) / bu:+.1f}% saved by fusing)")
+        torch.cuda.empty_cache()
+    return out
+
+
+def prefill_gemm(qg, torch, cases, table):
+    """The small-M GEMM (qgemm_prefill) for chunks of M activation rows, cold
+    (weights rotating over >= 1.2 GiB of copies): mean us per call over a batch
+    of back-to-back calls (the split, GEMM and K-sum kernels together), us per
+    activation row against the M = 1 GEMV of the same weight, useful TFLOP/s
+    (2 M N K per call) and the weight stream in GB/s."""
+    out = {}
+    log("prefill GEMM (qgemm_prefill, matrix cores): batch us per call, cold weights")
+    m1 = {"q8_0 lm_head 151936x1024": "c1 lm_head 151936x1024", "q8_0 qkv 4096x1024": "c1 qkv 4096x1024",
+          "q4_0 down 5120x17408": "c2 q4_0 down 5120x17408", "q4_0 lm_head 248320x5120": "c2 q4_0 lm_head 248320x5120"}
+    for label, kind, weight, N, K, M, make in cases:
+        copies = cold_copies(torch, weight)
+        fns = [make(cp.data_ptr()) for cp in copies]
+        for f in fns[:2]:
+            f()
+        nb = max(8, len(fns))
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        b0.record()
+        for i in range(nb):
+            fns[i % len(fns)]()
+        b1.record()
+        torch.cuda.synchronize()
+        us = b0.elapsed_time(b1) * 1e3 / nb
+        del fns, copies
+        base = table.get(m1[label.split(" M=")[0][2:]], {}).get("batch_us")
+        r = {"us": round(us, 2), "us_per_row": round(us / M, 3), "tflops": round(2.0 * M * N * K / us / 1e6, 1),
+             "weight_GBps": round(wbytes(kind, N, K) / us / 1e3, 1),
+             "m1_us_per_row": round(base, 3) if base else None}
+        out[label] = r
+        log(f"  {label:34s} {us:9.2f} us  {us / M:7.3f} us/row (M=1: {base or float('nan'):7.2f})  "
+            f"{r['tflops']:6.1f} TFLOP/s  weights {r['weight_GBps']:7.1f} GB/s")
         torch.cuda.empty_cache()
     return out
 
@@ -580,6 +633,7 @@ def main():
         table = {}
         log(f"per-call table: {args.reps} cold calls rotating over >= 1.2 GiB of weight copies, and warm calls")
         norm_cases = cfg_calls.pop("norm")
+        gemm_cases = cfg_calls.pop("gemm")
         for ci in sorted(cfg_calls):
             for c in cfg_calls[ci]:
                 copies = cold_copies(torch, c.weight)
@@ -608,6 +662,8 @@ def main():
         detail["configs"] = table
         result["rmsnorm_fusion"] = rmsnorm_fusion(qg, torch, norm_cases, args.reps)
         del norm_cases
+        result["prefill_gemm"] = prefill_gemm(qg, torch, gemm_cases, table)
+        del gemm_cases
         del keep
 
     # ---- CPU oracle baseline ----------------------------------------------------------

@@ -71,7 +71,7 @@ def lib():
             "qgemv_q4_0": ([vp, vp, vp, i64, i64, vp], i32),
             "qgemv_epilogue": ([i32, vp, vp, vp, vp, vp, i32, i64, i64, vp], i32),
             "qg_rmsnorm": ([vp, vp, ctypes.c_float, vp, i64, vp], i32),
-            "qg_prefill_workspace_size": ([i64, i64], sz),
+            "qg_prefill_workspace_size": ([i32, i64, i64, i64], sz),
             "qgemm_prefill": ([i32, vp, vp, vp, i64, i64, i64, vp, sz, vp], i32),
             "qgemv_rmsnorm": ([i32, vp, vp, vp, ctypes.c_float, vp, i64, i64, vp], i32),
             "qgemv_rmsnorm_gateup_silu": ([i32, vp, vp, vp, ctypes.c_float, vp, i64, i64, vp], i32),
@@ -221,16 +221,16 @@ def qgemv_rmsnorm_gateup_silu(qtype, w_gateup_packed, x, gamma, eps: float, y, N
                                            _dev(y, "y", _f32()), N_ff, K, _stream(stream)))
 
 
-def qg_prefill_workspace_size(M: int, K: int) -> int:
-    return int(lib().qg_prefill_workspace_size(M, K))
+def qg_prefill_workspace_size(qtype, N: int, K: int, M: int) -> int:
+    return int(lib().qg_prefill_workspace_size(_qtype(qtype), N, K, M))
 
 
 def qgemm_prefill(qtype, w_packed, X, Y, N: int, K: int, M: int, workspace=None, stream=None):
     """Y[M][N] = X W^T on the matrix cores. `workspace` is a uint8 device tensor of at
-    least qg_prefill_workspace_size(M, K) bytes (allocated here with torch if None)."""
+    least qg_prefill_workspace_size(qtype, N, K, M) bytes (allocated here with torch if None)."""
     import torch
     if workspace is None:
-        workspace = torch.empty(qg_prefill_workspace_size(M, K), dtype=torch.uint8, device=X.device)
+        workspace = torch.empty(qg_prefill_workspace_size(qtype, N, K, M), dtype=torch.uint8, device=X.device)
     _check("qgemm_prefill", lib().qgemm_prefill(_qtype(qtype), _dev(w_packed, "w_packed"), _dev(X, "X", _f32()),
                                                 _dev(Y, "Y", _f32()), N, K, M, _dev(workspace, "workspace"),
                                                 workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -17,19 +17,34 @@ struct GemmArgs {
     int64_t M;           // activation rows
     int64_t mt0;         // first 16-row activation tile of this pass
     int64_t y_stride;    // floats between output rows (N)
+    int64_t ksplit;      // K ranges (gridDim.y); range ky covers segments [nseg*ky/ksplit, nseg*(ky+1)/ksplit)
+    float *part;         // ksplit > 1: partial sums [ky][M][N] (summed in ky order by the reduce kernel)
 };
 
-// Rows of activations per matrix-core tile, and activation tiles per GEMM pass.
+// Rows of activations per matrix-core tile, activation tiles per GEMM pass (at
+// most), blocks of 32 weights per staged chunk of K.
 constexpr int kGemmTileM = 16;
 constexpr int kGemmMaxMT = 2;
+constexpr int kGemmChunk = 8;
+
+// LDS of one GEMM workgroup: the chunk's split activations (MT tiles x 2 KiB
+// per block) and the scales of its row tiles (2 slots x 4 rows x fp16 per block).
+constexpr size_t gemm_lds_bytes(int MT, int wg_tiles)
+{
+    return (size_t)MT * kGemmChunk * 128 * 16 + (size_t)wg_tiles * 2 * kGemmChunk * 8;
+}
+
+// Y[m][n] = sum over ky (in order) of part[ky][m][n], m < M, n < N.
+hipError_t launch_ksum(const float *part, float *Y, int64_t ksplit, int64_t M, int64_t N, hipStream_t s);
 
 // Split X fp32 [M][K] into the per-row scaled fp16 hi/lo parts the GEMM reads
 // (xs: M_pad * K * 2 halves, unscale: M_pad floats; M_pad = M rounded up to 16).
 hipError_t launch_split_x(int qt, const float *X, _Float16 *xs, float *unscale, int64_t M, int64_t M_pad, int64_t K,
                           hipStream_t s);
 
-// One GEMM pass over activation tiles [a.mt0, a.mt0 + MT), MT in {1, 2}.
-hipError_t launch_qgemm(int qt, int MT, const uint8_t *wp, const _Float16 *xs, const float *unscale, float *Y,
-                        const GemmArgs &a, int64_t grid, int block, hipStream_t s);
+// One GEMM pass over activation tiles [a.mt0, a.mt0 + MT), MT in {1, 2}, with
+// G wavefronts per workgroup (1..4) of RG 16-row groups each (1, 2 or 4).
+hipError_t launch_qgemm(int qt, int MT, int RG, int G, const uint8_t *wp, const _Float16 *xs, const float *unscale,
+                        float *Y, const GemmArgs &a, hipStream_t s);
 
 }  // namespace qgk

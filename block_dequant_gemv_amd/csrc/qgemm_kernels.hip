@@ -114,130 +114,214 @@ __device__ __forceinline__ void group_transpose(uint32_t (&v)[4])
 }
 
 // ---------------------------------------------------------------------------
-// The GEMM. A workgroup of G wavefronts owns 16 G weight rows (wavefront w:
-// row tiles 2 (blockIdx.x G + w) and + 1, i.e. 16 rows) and MT 16-row tiles of
-// activations starting at tile a.mt0. Per 1024-weight segment the workgroup
-// copies the segment's split activations into LDS (MT x 64 KiB), then every
-// wavefront walks the segment's blocks in groups of 4 (Q4_0) or 2 (Q8_0): one
-// 16-byte load per lane, the group transpose, the dequant, two MFMAs (hi, lo)
-// per activation tile and block, and acc = fma(d, S, acc).
-template <int QT, int MT>
-__global__ void __launch_bounds__(512)
+// The GEMM. A workgroup of G wavefronts owns 16 RG G weight rows: wavefront w
+// covers RG groups of 16 rows (row tiles 2 RG (blockIdx.x G + w) + 2 rg and
+// + 1 for group rg), for the MT 16-row activation tiles [a.mt0, a.mt0 + MT).
+// K is walked in chunks of kGemmChunk blocks. Per chunk the workgroup copies
+// into LDS the chunk's split activations (MT x 2 KiB per block) and the
+// scales of its rows, then each wavefront walks the chunk's blocks in load
+// groups of 4 (Q4_0) or 2 (Q8_0): one 16-byte load per lane and row group
+// (issued one group ahead), the group transpose, the dequant, and per block
+// and activation tile two MFMAs (hi, lo) per row group, each B operand read
+// once from LDS and used by the RG row groups; then acc = fma(d, S, acc).
+// Block sums are added per segment of 32 blocks and the segment sums in order.
+// With a.ksplit > 1, workgroup column blockIdx.y takes one range of segments
+// and writes its sums to a.part; launch_ksum then adds the ranges in order.
+template <int QT, int MT, int RG>
+__global__ void __launch_bounds__(256)
 qgemm_kernel(const uint8_t *__restrict__ wp, const _Float16 *__restrict__ xs, const float *__restrict__ unscale,
              float *__restrict__ Y, GemmArgs a)
 {
     constexpr int NH = (QT == kQ8_0) ? 2 : 1;
     constexpr int BPG = (QT == kQ8_0) ? 2 : 4;   // blocks per load group
-    extern __shared__ u32x4 lx[];                // [mt][block in segment][h][lane] x 16 B
+    constexpr int CB = kGemmChunk;               // blocks per staged chunk (a multiple of BPG)
+    extern __shared__ u32x4 lds[];
+    u32x4 *lx = lds;                                   // [mt][CB][h][64 lanes] x 16 B
+    u32x2 *lsc = (u32x2 *)(lds + MT * CB * 128);       // [tile of the workgroup][slot][CB] x 4 fp16
 
     const Geometry &g = a.geo;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int G = blockDim.x >> 6;
     const int i = lane & 15, c = lane >> 4;
-    const int64_t t_first = ((int64_t)blockIdx.x * G + wave) * 2;
+    const int64_t wg_tile0 = (int64_t)blockIdx.x * G * 2 * RG;   // first row tile of the workgroup
+    const int wg_tiles = G * 2 * RG;
+    const int64_t t_first = wg_tile0 + (int64_t)wave * 2 * RG;    // first row tile of this wavefront
     const int64_t t_last = g.n_tiles - 1;
-    // A operand: this lane loads the units of weight row t_first*8 + i
-    const int64_t tA = t_first + (i >> 3) < t_last ? t_first + (i >> 3) : t_last;
     const int slotA = (i & 7) >> 2, browA = i & 3;
-    // D layout: this lane's outputs are rows t_first*8 + 4c + r, r = 0..3
-    const int64_t tD = t_first + (c >> 1) < t_last ? t_first + (c >> 1) : t_last;
-    const int slotD = c & 1;
+    int64_t qoffA[RG];   // byte offset of this lane's A row in its tile (row group rg)
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+        int64_t t = t_first + 2 * rg + (i >> 3);
+        t = t < t_last ? t : t_last;
+        qoffA[rg] = t * g.tile_q;
+    }
     const Consts k = make_consts();
     constexpr int64_t seg_q = (int64_t)kTileRows * kSegBlocks * NH * kUnit;
     constexpr int64_t seg_s = (int64_t)kTileRows * kSegBlocks * 2;
 
-    f32x4 tot[MT], seg[MT];
+    f32x4 tot[RG][MT], seg[RG][MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) tot[mt] = seg[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) tot[rg][mt] = seg[rg][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int64_t s = 0; s < g.nseg; ++s) {
+    // Load group q of segment s (nb blocks): lane (i, c) loads the 16-byte unit
+    // of row i of each row group for block 4q + c (Q4_0) or block 2q + c/2, half
+    // c%2 (Q8_0); past a ragged segment's end it loads a valid unit, never used.
+    auto load_group = [&](u32x4 (&raw)[RG], int64_t s, int nb, int q) {
+        int jb = (QT == kQ4_0) ? 4 * q + c : 2 * q + (c >> 1);
+        const int hh = (QT == kQ4_0) ? 0 : (c & 1);
+        jb = jb < nb ? jb : nb - 1;
+        const int64_t off = s * seg_q + (int64_t)(((browA * NH + hh) * kSlots + slotA) * nb + jb) * kUnit;
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) raw[rg] = __builtin_nontemporal_load((const u32x4 *)(wp + qoffA[rg] + off));
+    };
+
+    const int64_t KB = g.KB;
+    const int64_t ky = blockIdx.y;
+    const int64_t s_begin = g.nseg * ky / a.ksplit, s_end = g.nseg * (ky + 1) / a.ksplit;
+    for (int64_t s = s_begin; s < s_end; ++s) {
         const int nb = (int)seg_blocks(g, s);
-        __syncthreads();   // the previous segment's activations are no longer read
-        {
-            const uint32_t per_mt = (uint32_t)nb * 128;   // 16-byte chunks per activation tile
-            for (uint32_t u = threadIdx.x; u < MT * per_mt; u += blockDim.x) {
-                const uint32_t mt = u / per_mt, r = u - mt * per_mt;
-                const u32x4 *src = (const u32x4 *)xs + ((a.mt0 + mt) * g.KB + s * kSegBlocks) * 128 + r;
-                lx[mt * (kSegBlocks * 128) + r] = *src;
-            }
-        }
-        __syncthreads();
-        const uint8_t *qa = wp + tA * g.tile_q + s * seg_q;
-        const uint8_t *sd = wp + g.scale_off + tD * g.tile_s + s * seg_s;
-        const int ngroups = (nb + BPG - 1) / BPG;
-        for (int q = 0; q < ngroups; ++q) {
-            int jb, hh;
-            if (QT == kQ4_0) {
-                jb = 4 * q + c;
-                hh = 0;
-            } else {
-                jb = 2 * q + (c >> 1);
-                hh = c & 1;
-            }
-            jb = jb < nb ? jb : nb - 1;   // past a ragged segment's end: a valid unit, never used
-            const u32x4 raw = __builtin_nontemporal_load(
-                (const u32x4 *)(qa + (int64_t)(((browA * NH + hh) * kSlots + slotA) * nb + jb) * kUnit));
-            uint32_t v[4] = {raw.x, raw.y, raw.z, raw.w};
-            group_transpose(v);
-#pragma unroll
-            for (int bb = 0; bb < BPG; ++bb) {
-                const int j = BPG * q + bb;
-                if (j >= nb) break;   // wave-uniform
-                h8 A;
-                if (QT == kQ4_0) {
-                    h2 p[4];
-                    q4_pairs(v[bb], k, p);
-                    A = h8{p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
-                } else {
-                    h2 p0[2], p1[2];
-                    q8_pairs(v[2 * bb], p0);
-                    q8_pairs(v[2 * bb + 1], p1);
-                    A = h8{p0[0].x, p0[0].y, p0[1].x, p0[1].y, p1[0].x, p1[0].y, p1[1].x, p1[1].y};
+        const int nch = (nb + CB - 1) / CB;
+        for (int ch = 0; ch < nch; ++ch) {
+            const int j0 = ch * CB;
+            const int nbc = nb - j0 < CB ? nb - j0 : CB;
+            u32x4 raw[RG];
+            load_group(raw, s, nb, j0 / BPG);   // the chunk's first group, ahead of the staging
+            __syncthreads();                     // the previous chunk's LDS is no longer read
+            {
+                // activations: MT tiles x CB blocks x 128 chunks of 16 B (blocks past nbc skipped);
+                // the index splits with shifts, CB being a power of two
+                static_assert((CB & (CB - 1)) == 0, "chunk size must be a power of two");
+                constexpr uint32_t lcb = __builtin_ctz(CB);
+                for (uint32_t u = threadIdx.x; u < MT * CB * 128; u += blockDim.x) {
+                    const uint32_t mt = u >> (lcb + 7), r = u & (CB * 128 - 1);
+                    if ((r >> 7) < (uint32_t)nbc)
+                        lx[u] = *((const u32x4 *)xs + ((a.mt0 + mt) * KB + s * kSegBlocks + j0) * 128 + r);
                 }
-                const u32x2 dd = *(const u32x2 *)(sd + (int64_t)(slotD * nb + j) * (kRowsPerLane * 2));
-                const h2 d01 = as_h2(dd.x), d23 = as_h2(dd.y);
-                const float d[4] = {(float)d01.x, (float)d01.y, (float)d23.x, (float)d23.y};
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const u32x4 bh = lx[(mt * kSegBlocks + j) * 128 + lane];
-                    const u32x4 bl = lx[(mt * kSegBlocks + j) * 128 + 64 + lane];
-                    f32x4 S = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(h8, bh),
-                                                                     f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-                    S = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(h8, bl), S, 0, 0, 0);
-                    seg[mt].x = __builtin_fmaf(d[0], S.x, seg[mt].x);
-                    seg[mt].y = __builtin_fmaf(d[1], S.y, seg[mt].y);
-                    seg[mt].z = __builtin_fmaf(d[2], S.z, seg[mt].z);
-                    seg[mt].w = __builtin_fmaf(d[3], S.w, seg[mt].w);
+                // scales of the workgroup's tiles: [tile][slot][block] x 8 B (4 rows)
+                for (uint32_t u = threadIdx.x; u < (uint32_t)wg_tiles * 2 * CB; u += blockDim.x) {
+                    const uint32_t tl = u >> (lcb + 1), sl = (u >> lcb) & 1, jj = u & (CB - 1);
+                    if (jj >= (uint32_t)nbc) continue;
+                    int64_t t = wg_tile0 + tl;
+                    t = t < t_last ? t : t_last;
+                    lsc[u] = *(const u32x2 *)(wp + g.scale_off + t * g.tile_s + s * seg_s +
+                                              (int64_t)(sl * nb + j0 + jj) * (kRowsPerLane * 2));
                 }
             }
+            __syncthreads();
+            const int ngroups = (nbc + BPG - 1) / BPG;
+            for (int qq = 0; qq < ngroups; ++qq) {
+                uint32_t v[RG][4];
+#pragma unroll
+                for (int rg = 0; rg < RG; ++rg) {
+                    v[rg][0] = raw[rg].x;
+                    v[rg][1] = raw[rg].y;
+                    v[rg][2] = raw[rg].z;
+                    v[rg][3] = raw[rg].w;
+                }
+                if (qq + 1 < ngroups) load_group(raw, s, nb, j0 / BPG + qq + 1);   // one group ahead
+#pragma unroll
+                for (int rg = 0; rg < RG; ++rg) group_transpose(v[rg]);
+#pragma unroll
+                for (int bb = 0; bb < BPG; ++bb) {
+                    const int jj = qq * BPG + bb;   // block within the chunk
+                    if (jj >= nbc) break;           // wave-uniform
+                    h8 A[RG];
+                    h2 d01[RG], d23[RG];
+#pragma unroll
+                    for (int rg = 0; rg < RG; ++rg) {
+                        if (QT == kQ4_0) {
+                            h2 p[4];
+                            q4_pairs(v[rg][bb], k, p);
+                            A[rg] = h8{p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
+                        } else {
+                            h2 p0[2], p1[2];
+                            q8_pairs(v[rg][2 * bb], p0);
+                            q8_pairs(v[rg][2 * bb + 1], p1);
+                            A[rg] = h8{p0[0].x, p0[0].y, p0[1].x, p0[1].y, p1[0].x, p1[0].y, p1[1].x, p1[1].y};
+                        }
+                        // rows 4c + r of row group rg: tile (wave*RG + rg)*2 + c/2 of the workgroup, slot c%2
+                        const u32x2 dd = lsc[(((wave * RG + rg) * 2 + (c >> 1)) * 2 + (c & 1)) * CB + jj];
+                        d01[rg] = as_h2(dd.x);
+                        d23[rg] = as_h2(dd.y);
+                    }
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const h8 bh = __builtin_bit_cast(h8, lx[(mt * CB + jj) * 128 + lane]);
+                        const h8 bl = __builtin_bit_cast(h8, lx[(mt * CB + jj) * 128 + 64 + lane]);
+                        f32x4 S[RG];
+#pragma unroll
+                        for (int rg = 0; rg < RG; ++rg)
+                            S[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[rg], bh, f32x4{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                           0, 0, 0);
+#pragma unroll
+                        for (int rg = 0; rg < RG; ++rg)
+                            S[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[rg], bl, S[rg], 0, 0, 0);
+#pragma unroll
+                        for (int rg = 0; rg < RG; ++rg) {
+                            f32x4 &acc = seg[rg][mt];
+                            acc.x = __builtin_fmaf((float)d01[rg].x, S[rg].x, acc.x);
+                            acc.y = __builtin_fmaf((float)d01[rg].y, S[rg].y, acc.y);
+                            acc.z = __builtin_fmaf((float)d23[rg].x, S[rg].z, acc.z);
+                            acc.w = __builtin_fmaf((float)d23[rg].y, S[rg].w, acc.w);
+                        }
+                    }
+                }
+            }
         }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            tot[mt].x += seg[mt].x;
-            tot[mt].y += seg[mt].y;
-            tot[mt].z += seg[mt].z;
-            tot[mt].w += seg[mt].w;
-            seg[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        }
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                tot[rg][mt].x += seg[rg][mt].x;
+                tot[rg][mt].y += seg[rg][mt].y;
+                tot[rg][mt].z += seg[rg][mt].z;
+                tot[rg][mt].w += seg[rg][mt].w;
+                seg[rg][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
     }
 
-    const int64_t n0 = t_first * kTileRows + 4 * c;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int64_t m = (a.mt0 + mt) * 16 + i;
         if (m >= a.M) continue;
         const float us = unscale[m];
-        float *yr = Y + m * a.y_stride;
-        const float o[4] = {tot[mt].x, tot[mt].y, tot[mt].z, tot[mt].w};
+        // with K ranges, each range's sum goes to its own partial buffer (the
+        // unscale is exact, so it may be applied before the ranges are added)
+        float *yr = (a.ksplit > 1 ? a.part + (ky * a.M + m) * a.N : Y + m * a.y_stride);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (n0 + r < a.N) yr[n0 + r] = o[r] * us;
+        for (int rg = 0; rg < RG; ++rg) {
+            const int64_t n0 = (t_first + 2 * rg) * kTileRows + 4 * c;
+            const float o[4] = {tot[rg][mt].x, tot[rg][mt].y, tot[rg][mt].z, tot[rg][mt].w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (n0 + r < a.N) yr[n0 + r] = o[r] * us;
+        }
     }
+}
+
+// Sum of the K-range partials in range order: one thread per output.
+__global__ void __launch_bounds__(256)
+ksum_kernel(const float *__restrict__ part, float *__restrict__ Y, int64_t ksplit, int64_t MN)
+{
+    const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (o >= MN) return;
+    float v = part[o];
+    for (int64_t r = 1; r < ksplit; ++r) v += part[r * MN + o];
+    Y[o] = v;
 }
 
 // ---------------------------------------------------------------------------
 // host side
+
+hipError_t launch_ksum(const float *part, float *Y, int64_t ksplit, int64_t M, int64_t N, hipStream_t s)
+{
+    const int64_t MN = M * N;
+    hipLaunchKernelGGL(ksum_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, s, part, Y, ksplit, MN);
+    return hipGetLastError();
+}
 
 hipError_t launch_split_x(int qt, const float *X, _Float16 *xs, float *unscale, int64_t M, int64_t M_pad, int64_t K,
                           hipStream_t s)
@@ -249,28 +333,41 @@ hipError_t launch_split_x(int qt, const float *X, _Float16 *xs, float *unscale, 
     return hipGetLastError();
 }
 
-template <int QT, int MT>
+template <int QT, int MT, int RG>
 static hipError_t launch_one(const uint8_t *wp, const _Float16 *xs, const float *unscale, float *Y,
-                             const GemmArgs &a, int64_t grid, int block, hipStream_t s)
+                             const GemmArgs &a, int G, hipStream_t s)
 {
-    auto kern = qgemm_kernel<QT, MT>;
-    const size_t lds = (size_t)MT * kSegBlocks * 128 * 16;
+    auto kern = qgemm_kernel<QT, MT, RG>;
+    const int64_t grid = (a.geo.n_tiles + 2 * RG * G - 1) / (2 * RG * G);
+    const dim3 grid3((unsigned)grid, (unsigned)a.ksplit);
+    const size_t lds = gemm_lds_bytes(MT, G * 2 * RG);
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    launch_timed(kern, dim3((unsigned)grid), dim3(block), (uint32_t)lds, s, wp, xs, unscale, Y, a);
+    launch_timed(kern, grid3, dim3(64 * G), (uint32_t)lds, s, wp, xs, unscale, Y, a);
     return hipGetLastError();
 }
 
-hipError_t launch_qgemm(int qt, int MT, const uint8_t *wp, const _Float16 *xs, const float *unscale, float *Y,
-                        const GemmArgs &a, int64_t grid, int block, hipStream_t s)
+template <int QT, int MT>
+static hipError_t launch_rg(const uint8_t *wp, const _Float16 *xs, const float *unscale, float *Y, const GemmArgs &a,
+                            int RG, int G, hipStream_t s)
+{
+    switch (RG) {
+    case 1: return launch_one<QT, MT, 1>(wp, xs, unscale, Y, a, G, s);
+    case 2: return launch_one<QT, MT, 2>(wp, xs, unscale, Y, a, G, s);
+    default: return launch_one<QT, MT, 4>(wp, xs, unscale, Y, a, G, s);
+    }
+}
+
+hipError_t launch_qgemm(int qt, int MT, int RG, int G, const uint8_t *wp, const _Float16 *xs, const float *unscale,
+                        float *Y, const GemmArgs &a, hipStream_t s)
 {
     if (qt == kQ8_0)
-        return MT == 1 ? launch_one<kQ8_0, 1>(wp, xs, unscale, Y, a, grid, block, s)
-                       : launch_one<kQ8_0, 2>(wp, xs, unscale, Y, a, grid, block, s);
-    return MT == 1 ? launch_one<kQ4_0, 1>(wp, xs, unscale, Y, a, grid, block, s)
-                   : launch_one<kQ4_0, 2>(wp, xs, unscale, Y, a, grid, block, s);
+        return MT == 1 ? launch_rg<kQ8_0, 1>(wp, xs, unscale, Y, a, RG, G, s)
+                       : launch_rg<kQ8_0, 2>(wp, xs, unscale, Y, a, RG, G, s);
+    return MT == 1 ? launch_rg<kQ4_0, 1>(wp, xs, unscale, Y, a, RG, G, s)
+                   : launch_rg<kQ4_0, 2>(wp, xs, unscale, Y, a, RG, G, s);
 }
 
 }  // namespace qgk

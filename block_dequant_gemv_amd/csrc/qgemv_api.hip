@@ -79,16 +79,18 @@ int64_t env_int(const char *name, int64_t dflt)
 
 // Launch-shape overrides for sweeps and tests (QG_SPLIT_K, QG_PERSIST,
 // QG_X_GLOBAL, QG_TILES_PER_GROUP, QG_WAVES_PER_WG, QG_PREFETCH, QG_F16_ROWS,
-// QG_F16_WAVES, QG_STRIDE_GROUPS, QG_GEMM_MT, QG_GEMM_WAVES). They are read from the environment once, on first use, and
+// QG_F16_WAVES, QG_STRIDE_GROUPS, QG_GEMM_MT, QG_GEMM_WAVES, QG_GEMM_ROWGROUPS,
+// QG_GEMM_KSPLIT). They are read from the environment once, on first use, and
 // again on qg_reload_tuning(): a GEMV call itself reads no environment.
 enum TuneKey {
     kSplitK, kPersist, kXGlobal, kTilesPerGroup, kWavesPerWg, kPrefetch, kF16Rows, kF16Waves, kStrideGroups,
-    kGemmMT, kGemmWaves, kNumTune
+    kGemmMT, kGemmWaves, kGemmRowGroups, kGemmKSplit, kNumTune
 };
 const char *const kTuneNames[kNumTune] = {"QG_SPLIT_K",      "QG_PERSIST",  "QG_X_GLOBAL",  "QG_TILES_PER_GROUP",
                                           "QG_WAVES_PER_WG", "QG_PREFETCH", "QG_F16_ROWS",  "QG_F16_WAVES",
-                                          "QG_STRIDE_GROUPS", "QG_GEMM_MT", "QG_GEMM_WAVES"};
-const int64_t kTuneDefaults[kNumTune] = {0, -1, -1, 0, 0, 0, 0, 0, -1, 0, 0};
+                                          "QG_STRIDE_GROUPS", "QG_GEMM_MT", "QG_GEMM_WAVES", "QG_GEMM_ROWGROUPS",
+                                          "QG_GEMM_KSPLIT"};
+const int64_t kTuneDefaults[kNumTune] = {0, -1, -1, 0, 0, 0, 0, 0, -1, 0, 0, 0, 0};
 std::atomic<int64_t> g_tune[kNumTune];
 std::atomic<bool> g_tune_loaded{false};
 
@@ -355,12 +357,50 @@ void host_pack_rows(const Geometry &g, const uint8_t *canon, uint8_t *packed, in
 }
 
 // Small-M GEMM: activation rows are processed in tiles of 16 (the last one
-// padded with zeros); the workspace holds one unscale factor per padded row
-// (256-byte aligned block) and the split activations, M_pad * K * 2 halves.
+// padded with zeros). The workspace holds, each part 256-byte aligned: one
+// unscale factor per padded row, the split activations (M_pad * K * 2
+// halves) and, when K is split across workgroups, the partial sums
+// (ksplit * M * N floats).
 constexpr int64_t kGemmMaxM = (int64_t)1 << 20;
 
 int64_t gemm_m_pad(int64_t M) { return (M + qgk::kGemmTileM - 1) / qgk::kGemmTileM * qgk::kGemmTileM; }
-size_t gemm_unscale_bytes(int64_t M) { return (size_t)qgl::round_up(gemm_m_pad(M) * (int64_t)sizeof(float), 256); }
+
+struct GemmPlan {
+    int MT, RG, G;
+    int64_t ksplit;
+    size_t off_xs, off_part, bytes;
+};
+
+// Launch plan of qgemm_prefill (depends on the shape and the device's CU count;
+// measured on MI355X): 4 wavefronts per workgroup, two activation tiles per
+// pass, two 16-row groups per wavefront (one where even a full K split would
+// leave fewer than two workgroups per CU), and the K segments split across
+// workgroups until there are about four workgroups per CU.
+GemmPlan plan_gemm(int qt, int64_t N, int64_t K, int64_t M)
+{
+    GemmPlan p;
+    const Geometry g = qgl::geometry(qt, N, K);
+    p.G = 4;
+    const int64_t g_env = tune(kGemmWaves);
+    if (g_env >= 1 && g_env <= 4) p.G = (int)g_env;
+    const int64_t wgs_rg2 = (g.n_tiles + 4 * p.G - 1) / (4 * p.G);
+    p.RG = wgs_rg2 * g.nseg >= 2 * (int64_t)cu_count() ? 2 : 1;
+    const int64_t rg_env = tune(kGemmRowGroups);
+    if (rg_env == 1 || rg_env == 2 || rg_env == 4) p.RG = (int)rg_env;
+    p.MT = qgk::kGemmMaxMT;
+    const int64_t mt_env = tune(kGemmMT);
+    if (mt_env == 1 || mt_env == 2) p.MT = (int)mt_env;
+    const int64_t wgs = (g.n_tiles + 2 * p.RG * p.G - 1) / (2 * p.RG * p.G);
+    const int64_t want = 4 * (int64_t)cu_count();
+    p.ksplit = wgs < want ? std::min<int64_t>(g.nseg, (want + wgs - 1) / wgs) : 1;
+    const int64_t ks_env = tune(kGemmKSplit);
+    if (ks_env >= 1) p.ksplit = std::min<int64_t>(g.nseg, ks_env);
+    const int64_t M_pad = gemm_m_pad(M);
+    p.off_xs = (size_t)qgl::round_up(M_pad * (int64_t)sizeof(float), 256);
+    p.off_part = p.off_xs + (size_t)qgl::round_up(M_pad * K * 2 * (int64_t)sizeof(_Float16), 256);
+    p.bytes = p.off_part + (p.ksplit > 1 ? (size_t)p.ksplit * (size_t)M * (size_t)N * sizeof(float) : 0);
+    return p;
+}
 
 }  // namespace
 
@@ -519,10 +559,12 @@ qg_status qg_rmsnorm(const float *x, const float *gamma, float eps, float *out, 
 
 // ---- small-M GEMM (prefill chunks) ------------------------------------------
 
-size_t qg_prefill_workspace_size(int64_t M, int64_t K)
+size_t qg_prefill_workspace_size(int qtype, int64_t N, int64_t K, int64_t M)
 {
-    if (M <= 0 || M > kGemmMaxM || K <= 0 || K % 32 || K > kMaxDim) return 0;
-    return gemm_unscale_bytes(M) + (size_t)gemm_m_pad(M) * (size_t)K * 2 * sizeof(_Float16);
+    if (!valid_qtype(qtype) || N <= 0 || N > kMaxDim || M <= 0 || M > kGemmMaxM || K <= 0 || K % 32 ||
+        K > kMaxDim)
+        return 0;
+    return plan_gemm(qtype, N, K, M).bytes;
 }
 
 qg_status qgemm_prefill(int qtype, const void *w_packed, const float *X, float *Y, int64_t N, int64_t K, int64_t M,
@@ -537,7 +579,8 @@ qg_status qgemm_prefill(int qtype, const void *w_packed, const float *X, float *
     if (!aligned(w_packed, 16)) return fail(QG_EALIGN, "%s: packed weights must be 16-byte aligned", fn);
     if (!aligned(X, 4) || !aligned(Y, 4)) return fail(QG_EALIGN, "%s: X and Y must be 4-byte aligned", fn);
     if (!aligned(workspace, 256)) return fail(QG_EALIGN, "%s: workspace must be 256-byte aligned", fn);
-    const size_t need = qg_prefill_workspace_size(M, K);
+    const GemmPlan p = plan_gemm(qtype, N, K, M);
+    const size_t need = p.bytes;
     if (workspace_bytes < need)
         return fail(QG_EINVAL, "%s: workspace of %zu bytes, %zu needed (qg_prefill_workspace_size)", fn,
                     workspace_bytes, need);
@@ -550,29 +593,27 @@ qg_status qgemm_prefill(int qtype, const void *w_packed, const float *X, float *
 
     const int64_t M_pad = gemm_m_pad(M);
     float *unscale = (float *)workspace;
-    _Float16 *xs = (_Float16 *)((uint8_t *)workspace + gemm_unscale_bytes(M));
+    _Float16 *xs = (_Float16 *)((uint8_t *)workspace + p.off_xs);
     hipStream_t s = as_stream(stream);
     // the split pass is not timed: a bound event pair goes to the first GEMM pass
     hipError_t e = qgk::launch_split_x(qtype, X, xs, unscale, M, M_pad, K, s);
     if (e != hipSuccess) return hip_fail(e, fn);
-    // activation tiles per pass (LDS: 64 KiB each) and wavefronts per workgroup (16 weight rows each)
-    int MT = qgk::kGemmMaxMT;
-    const int64_t mt_env = tune(kGemmMT);
-    if (mt_env == 1 || mt_env == 2) MT = (int)mt_env;
-    int G = 8;
-    const int64_t g_env = tune(kGemmWaves);
-    if (g_env >= 1 && g_env <= 8) G = (int)g_env;
     const int64_t n_mt = M_pad / qgk::kGemmTileM;
-    const int64_t grid = (g.n_tiles + 2 * G - 1) / (2 * G);
     qgk::GemmArgs a;
     a.geo = g;
     a.N = N;
     a.M = M;
     a.y_stride = N;
-    for (int64_t mt0 = 0; mt0 < n_mt; mt0 += MT) {
+    a.ksplit = p.ksplit;
+    a.part = p.ksplit > 1 ? (float *)((uint8_t *)workspace + p.off_part) : nullptr;
+    for (int64_t mt0 = 0; mt0 < n_mt; mt0 += p.MT) {
         a.mt0 = mt0;
-        const int mt = (int)std::min<int64_t>(MT, n_mt - mt0);
-        e = qgk::launch_qgemm(qtype, mt, (const uint8_t *)w_packed, xs, unscale, Y, a, grid, 64 * G, s);
+        const int mt = (int)std::min<int64_t>(p.MT, n_mt - mt0);
+        e = qgk::launch_qgemm(qtype, mt, p.RG, p.G, (const uint8_t *)w_packed, xs, unscale, Y, a, s);
+        if (e != hipSuccess) return hip_fail(e, fn);
+    }
+    if (p.ksplit > 1) {
+        e = qgk::launch_ksum(a.part, Y, p.ksplit, M, N, s);
         if (e != hipSuccess) return hip_fail(e, fn);
     }
     return ok();

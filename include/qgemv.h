@@ -183,10 +183,13 @@ qg_status qgemv_verify(int qtype, const void *w_packed, const float *X, float *Y
 
 /* ---- small-M GEMM (prefill chunks) ---------------------------------------- */
 
-/* Bytes of the workspace qgemm_prefill needs for M activation rows of length K
- * (0 for invalid arguments): M rounded up to 16 times K times 4 bytes, plus a
- * 256-byte-aligned block of per-row factors. */
-size_t qg_prefill_workspace_size(int64_t M, int64_t K);
+/* Bytes of the workspace qgemm_prefill needs for this weight shape and M
+ * activation rows (0 for invalid arguments): per-row factors, the split
+ * activations (M rounded up to 16, times K times 4 bytes) and, when the launch
+ * plan splits K across workgroups, ksplit * M * N partial sums. The plan
+ * depends on the current device's CU count: query on the device that runs the
+ * call. */
+size_t qg_prefill_workspace_size(int qtype, int64_t N, int64_t K, int64_t M);
 
 /* Y = X W^T for a chunk of M activation rows against a packed Q8_0 / Q4_0
  * weight, on the matrix cores: Y[m][n] = sum_k W[n][k] X[m][k], the dense side
@@ -194,14 +197,16 @@ size_t qg_prefill_workspace_size(int64_t M, int64_t K);
  * batching (GEMM kernel)"; the robotnurse.io post prefills in 128-token
  * chunks). X fp32 row-major [M][K], Y fp32 row-major [M][N], 1 <= M <= 2^20,
  * both 4-byte aligned; w_packed from qg_pack (16-byte aligned).
- * workspace: caller-owned device memory of qg_prefill_workspace_size(M, K)
- * bytes, 256-byte aligned, overlapping nothing else; it holds the activations
+ * workspace: caller-owned device memory of
+ * qg_prefill_workspace_size(qtype, N, K, M) bytes, 256-byte aligned, overlapping nothing else; it holds the activations
  * split into two fp16 parts (one power-of-two scale per row, 22 significant
- * bits) and is overwritten by every call. The weights are streamed once per
- * 32 activation rows. Each output is within 1e-5 * sum_k |W[n][k] X[m][k]|
- * + 1e-7 of the exact product for finite inputs; it is deterministic but not
- * bitwise equal to qgemv_q8_0 / qgemv_q4_0 / qgemv_verify (another order of
- * additions). Two kernels are enqueued (the split, then the GEMM passes);
+ * bits) and the partial sums of a K split, and is overwritten by every call.
+ * The weights are streamed once per 32 activation rows; matrices with few row
+ * tiles split K across workgroups and add the ranges in a fixed order. Each
+ * output is within 1e-5 * sum_k |W[n][k] X[m][k]| + 1e-7 of the exact product
+ * for finite inputs; it is deterministic but not bitwise equal to qgemv_q8_0
+ * / qgemv_q4_0 / qgemv_verify (another order of additions). Kernels enqueued:
+ * the split, the GEMM passes and, with a K split, the sum of the ranges;
  * qg_time_next_launch times the first GEMM pass. */
 qg_status qgemm_prefill(int qtype, const void *w_packed, const float *X, float *Y, int64_t N, int64_t K, int64_t M,
                         void *workspace, size_t workspace_bytes, void *stream);
@@ -226,7 +231,7 @@ qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int *split_k_ways
 
 /* Re-read the launch-shape overrides (QG_SPLIT_K, QG_PERSIST, QG_X_GLOBAL,
  * QG_TILES_PER_GROUP, QG_WAVES_PER_WG, QG_PREFETCH, QG_F16_ROWS, QG_F16_WAVES,
- * QG_STRIDE_GROUPS, QG_GEMM_MT, QG_GEMM_WAVES)
+ * QG_STRIDE_GROUPS, QG_GEMM_MT, QG_GEMM_WAVES, QG_GEMM_ROWGROUPS, QG_GEMM_KSPLIT)
  * from the environment. They exist for launch-shape sweeps and tests and are
  * read once, at the first call that plans a launch; the GEMV calls themselves
  * read no environment. An override that changes a matrix's K split (QG_SPLIT_K,

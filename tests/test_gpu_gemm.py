@@ -2,8 +2,9 @@
 oracle: Y[m] = W X[m] for every activation row, within the linear bound
 1e-5 * sum|w x| + 1e-7 of each output. Shapes span several row tiles and
 workgroups, a ragged last weight tile, a ragged last K segment, M below, at
-and across the 16-row activation tile and the 32-row pass, and the two pass
-widths (QG_GEMM_MT = 1 / 2)."""
+and across the 16-row activation tile and the 32-row pass, the two pass
+widths (QG_GEMM_MT = 1 / 2), 1, 2 and 4 row groups per wavefront and the K
+split across workgroups (with its partial sums added in a fixed order)."""
 import os
 
 import numpy as np
@@ -70,6 +71,39 @@ def test_gemm_pass_widths_and_determinism(kind):
         qg.qg_reload_tuning()
     # the pass width changes which workgroup computes a row, not its operations
     assert outs["1"].tobytes() == outs["2"].tobytes()
+
+
+@pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
+def test_gemm_launch_shapes(kind):
+    # every (row groups, workgroup size, K split) against the oracle; the K split
+    # changes the rounding of a row, the other knobs only who computes it
+    N, K, M = 300, 5120, 20
+    rng = np.random.default_rng(77)
+    canon = W.matrix(kind, N, K, rng)
+    X = W.activation(K, rng, M=M).reshape(M, K)
+    packed = qg.pack_weights(kind, canon, N, K)
+    Y_ref, A_ref = O.verify(kind, canon, X, N, K, threads=THREADS)
+    knobs = ("QG_GEMM_ROWGROUPS", "QG_GEMM_WAVES", "QG_GEMM_KSPLIT", "QG_GEMM_MT")
+    by_split = {}
+    try:
+        for rg, gw, ks in ((1, 4, 1), (2, 4, 1), (4, 4, 1), (4, 1, 1), (2, 2, 1), (1, 4, 2), (2, 3, 3), (4, 4, 5),
+                           (1, 1, 5)):
+            for kk in knobs:
+                os.environ.pop(kk, None)
+            os.environ.update(QG_GEMM_ROWGROUPS=str(rg), QG_GEMM_WAVES=str(gw), QG_GEMM_KSPLIT=str(ks))
+            qg.qg_reload_tuning()
+            announce(f"qgemm_prefill {kind} rowgroups={rg} waves={gw} ksplit={ks}")
+            Y, tail, _ = _run(kind, packed, X, N, K, M, tail=5)
+            assert np.all(tail == -9.0)
+            for m in range(M):
+                assert_linear(Y[m], Y_ref[m], A_ref[m], f"gemm {kind} rg={rg} g={gw} ks={ks} row {m}")
+            if ks in by_split:
+                assert Y.tobytes() == by_split[ks].tobytes(), "launch shape changed the bits at a fixed K split"
+            by_split[ks] = Y
+    finally:
+        for kk in knobs:
+            os.environ.pop(kk, None)
+        qg.qg_reload_tuning()
 
 
 @pytest.mark.parametrize("kind", ["q8_0", "q4_0"])

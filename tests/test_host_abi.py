@@ -166,9 +166,15 @@ def test_rmsnorm_argument_checks_without_gpu(L):
 def test_gemm_argument_checks_without_gpu(L):
     f = FAKE
     w, x, y, ws = f, f + (1 << 24), f + (2 << 24), f + (3 << 24)
-    need = qg.qg_prefill_workspace_size(20, 1024)
-    assert need == 256 + 32 * 1024 * 4           # 20 rows padded to 32; one 256-byte block of row factors
-    assert qg.qg_prefill_workspace_size(0, 1024) == 0 and qg.qg_prefill_workspace_size(4, 1000) == 0
+    # 20 rows padded to 32: one 256-byte block of row factors and 32 x 1024 x 4 bytes of split activations;
+    # a 64-row weight (8 row tiles, one workgroup) splits K only when it has several segments
+    need = qg.qg_prefill_workspace_size("q8_0", 64, 1024, 20)
+    assert need == 256 + 32 * 1024 * 4
+    with_split = qg.qg_prefill_workspace_size("q8_0", 64, 4096, 20)
+    assert with_split == 256 + 32 * 4096 * 4 + 4 * 20 * 64 * 4      # 4 segments -> 4 K ranges of partial sums
+    assert qg.qg_prefill_workspace_size("q8_0", 64, 1024, 0) == 0
+    assert qg.qg_prefill_workspace_size("q8_0", 64, 1000, 4) == 0
+    assert qg.qg_prefill_workspace_size(3, 64, 1024, 4) == 0
     gm = lambda *a: call(L, "qgemm_prefill", *a)  # noqa: E731
     # (qtype, w, X, Y, N, K, M, workspace, workspace_bytes, stream)
     assert gm(1, w, x, y, 64, 1024, 0, ws, need, None) == qg.QG_EINVAL            # M = 0
