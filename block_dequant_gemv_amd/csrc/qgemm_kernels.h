@@ -24,7 +24,7 @@ struct GemmArgs {
 // Rows of activations per matrix-core tile, activation tiles per GEMM pass (at
 // most), blocks of 32 weights per staged chunk of K.
 constexpr int kGemmTileM = 16;
-constexpr int kGemmMaxMT = 2;
+constexpr int kGemmMaxMT = 4;
 constexpr int kGemmChunk = 8;
 
 // LDS of one GEMM workgroup: the chunk's split activations (MT tiles x 2 KiB
@@ -42,8 +42,9 @@ hipError_t launch_ksum(const float *part, float *Y, int64_t ksplit, int64_t M, i
 hipError_t launch_split_x(int qt, const float *X, _Float16 *xs, float *unscale, int64_t M, int64_t M_pad, int64_t K,
                           hipStream_t s);
 
-// One GEMM pass over activation tiles [a.mt0, a.mt0 + MT), MT in {1, 2}, with
-// G wavefronts per workgroup (1..4) of RG 16-row groups each (1, 2 or 4).
+// One GEMM pass over activation tiles [a.mt0, a.mt0 + MT), MT in 1..4, with G
+// wavefronts per workgroup (1..4) of RG 16-row groups each (1, 2 or 4; a pass
+// of 3 tiles runs with one row group, of 4 tiles with at most two).
 hipError_t launch_qgemm(int qt, int MT, int RG, int G, const uint8_t *wp, const _Float16 *xs, const float *unscale,
                         float *Y, const GemmArgs &a, hipStream_t s);
 

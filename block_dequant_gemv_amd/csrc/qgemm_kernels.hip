@@ -360,14 +360,26 @@ static hipError_t launch_rg(const uint8_t *wp, const _Float16 *xs, const float *
     }
 }
 
+template <int QT>
+static hipError_t launch_mt(const uint8_t *wp, const _Float16 *xs, const float *unscale, float *Y, const GemmArgs &a,
+                            int MT, int RG, int G, hipStream_t s)
+{
+    switch (MT) {
+    case 1: return launch_rg<QT, 1>(wp, xs, unscale, Y, a, RG, G, s);
+    case 2: return launch_rg<QT, 2>(wp, xs, unscale, Y, a, RG, G, s);
+    case 3: return launch_one<QT, 3, 1>(wp, xs, unscale, Y, a, G, s);   // the tail pass of a 4-tile plan
+    default:
+        // four activation tiles: one or two row groups per wavefront (registers)
+        return RG == 1 ? launch_one<QT, 4, 1>(wp, xs, unscale, Y, a, G, s)
+                       : launch_one<QT, 4, 2>(wp, xs, unscale, Y, a, G, s);
+    }
+}
+
 hipError_t launch_qgemm(int qt, int MT, int RG, int G, const uint8_t *wp, const _Float16 *xs, const float *unscale,
                         float *Y, const GemmArgs &a, hipStream_t s)
 {
-    if (qt == kQ8_0)
-        return MT == 1 ? launch_rg<kQ8_0, 1>(wp, xs, unscale, Y, a, RG, G, s)
-                       : launch_rg<kQ8_0, 2>(wp, xs, unscale, Y, a, RG, G, s);
-    return MT == 1 ? launch_rg<kQ4_0, 1>(wp, xs, unscale, Y, a, RG, G, s)
-                   : launch_rg<kQ4_0, 2>(wp, xs, unscale, Y, a, RG, G, s);
+    if (qt == kQ8_0) return launch_mt<kQ8_0>(wp, xs, unscale, Y, a, MT, RG, G, s);
+    return launch_mt<kQ4_0>(wp, xs, unscale, Y, a, MT, RG, G, s);
 }
 
 }  // namespace qgk

@@ -372,8 +372,8 @@ struct GemmPlan {
 };
 
 // Launch plan of qgemm_prefill (depends on the shape and the device's CU count;
-// measured on MI355X): 4 wavefronts per workgroup, two activation tiles per
-// pass, two 16-row groups per wavefront (one where even a full K split would
+// measured on MI355X): 4 wavefronts per workgroup, two (Q4_0) or four (Q8_0)
+// activation tiles per pass, two 16-row groups per wavefront (one where even a full K split would
 // leave fewer than two workgroups per CU), and the K segments split across
 // workgroups until there are about four workgroups per CU.
 GemmPlan plan_gemm(int qt, int64_t N, int64_t K, int64_t M)
@@ -387,9 +387,12 @@ GemmPlan plan_gemm(int qt, int64_t N, int64_t K, int64_t M)
     p.RG = wgs_rg2 * g.nseg >= 2 * (int64_t)cu_count() ? 2 : 1;
     const int64_t rg_env = tune(kGemmRowGroups);
     if (rg_env == 1 || rg_env == 2 || rg_env == 4) p.RG = (int)rg_env;
-    p.MT = qgk::kGemmMaxMT;
+    // activation tiles per pass: 4 for Q8_0 (its heavier weight stream favours fewer passes:
+    // LM head 151936x1024 at M = 128, 431 -> 312 us), 2 for Q4_0 (4 cost occupancy there:
+    // 17408x5120 at M = 128, 164 -> 201 us)
+    p.MT = qt == QG_Q8_0 ? 4 : 2;
     const int64_t mt_env = tune(kGemmMT);
-    if (mt_env == 1 || mt_env == 2) p.MT = (int)mt_env;
+    if (mt_env >= 1 && mt_env <= qgk::kGemmMaxMT) p.MT = (int)mt_env;
     const int64_t wgs = (g.n_tiles + 2 * p.RG * p.G - 1) / (2 * p.RG * p.G);
     const int64_t want = 4 * (int64_t)cu_count();
     p.ksplit = wgs < want ? std::min<int64_t>(g.nseg, (want + wgs - 1) / wgs) : 1;
@@ -648,16 +651,15 @@ qg_status gemv_f16_splitk(const void *w_f16, const float *x, float *y, int64_t N
 
     qgk::F16Plan p;
     p.vec = (K % 8 == 0) && aligned(w_f16, 16) && aligned(x, 16);
-    const int64_t units = p.vec ? K / 8 : K;       // work items along K
-    // rows per workgroup: register-block 4 rows when there are plenty of rows
-    p.R = N >= 2048 ? 4 : (N >= 512 ? 2 : 1);
+    // One row per workgroup; one wavefront per row when there are enough rows to
+    // cover the CUs (each lane walks K/512 16-byte chunks of its row), four
+    // otherwise (measured on MI355X, cold: 5120 x 5120 10.1 us, 256 x 5120 and
+    // 48 x 5120 3.9 us, against 10.8 / 5.1 / 4.7 us for register-blocked rows).
+    // QG_F16_ROWS (1, 2, 4) and QG_F16_WAVES override the shape for sweeps.
+    p.R = 1;
     const int64_t r_env = tune(kF16Rows);
     if (r_env == 1 || r_env == 2 || r_env == 4) p.R = (int)r_env;
-    // wavefronts per workgroup: one row per workgroup walks ~5 chunks per lane
-    // (measured best for the thin 256 x 5120 and 48 x 5120 matrices); register-
-    // blocked rows use ~1-2 chunks per lane. At most 16 wavefronts.
-    int64_t waves = p.R == 1 ? (units + 319) / 320 : (units + 63) / 64;
-    if (p.R >= 2) waves = (waves + 1) / 2;
+    int64_t waves = N >= 1024 ? 1 : 4;
     const int64_t w_env = tune(kF16Waves);
     if (w_env > 0) waves = w_env;
     if (waves > 16) waves = 16;

@@ -201,7 +201,7 @@ size_t qg_prefill_workspace_size(int qtype, int64_t N, int64_t K, int64_t M);
  * qg_prefill_workspace_size(qtype, N, K, M) bytes, 256-byte aligned, overlapping nothing else; it holds the activations
  * split into two fp16 parts (one power-of-two scale per row, 22 significant
  * bits) and the partial sums of a K split, and is overwritten by every call.
- * The weights are streamed once per 32 activation rows; matrices with few row
+ * The weights are streamed once per 64 (Q8_0) or 32 (Q4_0) activation rows; matrices with few row
  * tiles split K across workgroups and add the ranges in a fixed order. Each
  * output is within 1e-5 * sum_k |W[n][k] X[m][k]| + 1e-7 of the exact product
  * for finite inputs; it is deterministic but not bitwise equal to qgemv_q8_0

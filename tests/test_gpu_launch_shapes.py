@@ -72,3 +72,32 @@ def test_forced_launch_shapes(kind, N, K):
                 assert Yh[m].tobytes() == ym.tobytes(), ctx + f" verify row {m} != M=1"
     finally:
         _set()
+
+
+@pytest.mark.parametrize("N,K", [(300, 5120), (37, 1000), (2049, 64)])
+def test_f16_forced_launch_shapes(N, K):
+    # every rows-per-workgroup / wavefronts-per-workgroup shape of the fp16 split-K
+    # GEMV against the oracle, and the same bits run to run at a fixed shape
+    rng = np.random.default_rng(N + K)
+    w = W.f16_matrix(N, K, rng)
+    x = W.activation(K, rng)
+    wd, xd = to_dev(w), to_dev(x)
+    y_ref, a_ref = O.gemv("f16", w, x, N, K, threads=THREADS)
+    try:
+        for r in (1, 2, 4):
+            for wv in (1, 3, 8, 16):
+                os.environ["QG_F16_ROWS"], os.environ["QG_F16_WAVES"] = str(r), str(wv)
+                qg.qg_reload_tuning()
+                ctx = f"f16 {N}x{K} rows={r} waves={wv}"
+                announce(ctx)
+                y0, y1 = empty_f32(N), empty_f32(N)
+                qg.gemv_f16_splitk(wd, xd, y0, N, K)
+                qg.gemv_f16_splitk(wd, xd, y1, N, K)
+                sync()
+                a0 = y0.cpu().numpy()
+                assert_linear(a0, y_ref, a_ref, ctx)
+                assert a0.tobytes() == y1.cpu().numpy().tobytes(), ctx + ": run-to-run bits differ"
+    finally:
+        os.environ.pop("QG_F16_ROWS", None)
+        os.environ.pop("QG_F16_WAVES", None)
+        qg.qg_reload_tuning()
