@@ -139,6 +139,41 @@ def step_calls(qg, s, xs, ys, stream):
     ]
 
 
+def graph_headline(qg, torch, sets, xs, ys, K, warmup, copies, step_bytes):
+    """Headline steps replayed from HIP graphs: one torch.cuda.CUDAGraph per weight
+    copy capturing that step's five launches on a side stream (the GEMV calls record
+    plain kernel launches and nothing else), then K replays cycling through the
+    copies, between synchronisations."""
+    side = torch.cuda.Stream()
+    graphs = []
+    for st in sets:
+        calls = step_calls(qg, st, xs, ys, side.cuda_stream)
+        with torch.cuda.stream(side):
+            for c in calls:
+                c.fn()
+        side.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side, capture_error_mode="thread_local"):
+            for c in calls:
+                c.fn()
+        graphs.append(g)
+    with torch.cuda.stream(side):
+        for s in range(warmup):
+            graphs[s % copies].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(side)
+        for s in range(K):
+            graphs[s % copies].replay()
+        e1.record(side)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    del graphs
+    return {"ms_per_step": round(wall / K * 1e3, 5), "gpu_ms_per_step": round(e0.elapsed_time(e1) / K, 5),
+            "value": round(step_bytes * K / wall / 1e9, 1)}
+
+
 def timing_events(torch, n):
     """n timing events on the current stream, recorded once so that they exist
     (torch creates the underlying hipEvent_t lazily) and can be bound to launches."""
@@ -552,6 +587,13 @@ def main():
         f"enqueue {host_us:.1f} us/step, {value:.1f} GB/s ({100 * value / PEAK_GBPS:.1f}% of 8 TB/s), "
         f"{copies} weight copies")
 
+    # ---- the same K steps replayed from HIP graphs --------------------------------
+    # One graph per weight copy holds the step's five launches (captured on a side
+    # stream); replaying them is what a decode loop that captures its step does.
+    graph = graph_headline(qg, torch, sets, xs, ys, K, args.warmup, copies, step_bytes)
+    log(f"graph replay: {graph['ms_per_step'] * 1e3:.1f} us/step, {graph['value']:.1f} GB/s "
+        f"({100 * graph['value'] / PEAK_GBPS:.1f}% of 8 TB/s)")
+
     # ---- kernel pass: the same K steps with every launch timed -----------------
     # Each launch is bound to an event pair that receives the kernel's own start
     # and end timestamps (qg_time_next_launch; the dispatch times a rocprofv3
@@ -610,6 +652,7 @@ def main():
             "device": props.name,
         },
         "roofline": roofline,
+        "graph_replay": graph,
     }
 
     detail = {"kernel_us": {c.label: float(np.median(durs[:, i])) for i, c in enumerate(steps[0])},

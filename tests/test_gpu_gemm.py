@@ -48,7 +48,7 @@ def test_gemm_matches_oracle(kind, N, K, M):
 
 @pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
 def test_gemm_pass_widths_and_determinism(kind):
-    N, K, M = 640, 5120, 48
+    N, K, M = 640, 5120, 72
     rng = np.random.default_rng(31)
     canon = W.matrix(kind, N, K, rng)
     X = W.activation(K, rng, M=M).reshape(M, K)
@@ -56,7 +56,7 @@ def test_gemm_pass_widths_and_determinism(kind):
     Y_ref, A_ref = O.verify(kind, canon, X, N, K, threads=THREADS)
     outs = {}
     try:
-        for mt in ("1", "2"):
+        for mt in ("1", "2", "3", "4"):
             os.environ["QG_GEMM_MT"] = mt
             qg.qg_reload_tuning()
             announce(f"qgemm_prefill {kind} passes of {mt} activation tiles")
@@ -70,7 +70,7 @@ def test_gemm_pass_widths_and_determinism(kind):
         os.environ.pop("QG_GEMM_MT", None)
         qg.qg_reload_tuning()
     # the pass width changes which workgroup computes a row, not its operations
-    assert outs["1"].tobytes() == outs["2"].tobytes()
+    assert outs["1"].tobytes() == outs["2"].tobytes() == outs["3"].tobytes() == outs["4"].tobytes()
 
 
 @pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
