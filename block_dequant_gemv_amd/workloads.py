@@ -9,14 +9,19 @@ Canonical formats (GGUF-style, little-endian):
   Q4_0 block, 18 B: fp16 scale d, then 16 bytes of nibbles; byte j holds
                     element j (low nibble) and element j+16 (high nibble);
                     weight = d * (nibble - 8).
+  Q4_K super-block, 144 B per 256 weights: fp16 d, fp16 dmin, 12 bytes of
+                    6-bit sub-block scales and mins, 128 bytes of nibbles.
   F16 matrix: row-major [N][K] IEEE binary16.
-A row of a quantised matrix is K/32 consecutive blocks.
+A row of a quantised matrix is K/32 consecutive blocks (K/256 for Q4_K).
 
 Value laws (the decode workloads the pages measure on are trained checkpoints;
 these seeded draws stand in for them, with the same shapes):
   Q8_0: q uniform integers in [-127, 127]; d = fp16(|N(0, 0.02)| / 127).
   Q4_0: each nibble uniform in 0..15 (a uniform byte carries two independent
         uniform nibbles); d = fp16(|N(0, 0.02)| / 8).
+  Q4_K: d = fp16(|N(0, 0.02)| / 480), dmin = fp16(|N(0, 0.02)| / 64); the 12
+        scale/min bytes and the 128 quant bytes uniform (so every 6-bit scale
+        and min and every nibble is uniform).
   F16 : w = fp16(N(0, 0.02)).
   x   : fp32(N(0, 1)) drawn in float64 and rounded to nearest.
 fp16 rounding is numpy's float64 -> float16 cast (round to nearest even).
@@ -27,6 +32,7 @@ import numpy as np
 
 Q8_0_BLOCK_BYTES = 34
 Q4_0_BLOCK_BYTES = 18
+Q4_K_BLOCK_BYTES = 144
 
 
 def _rng(seed):
@@ -68,6 +74,22 @@ def q4_0_matrix(N: int, K: int, seed, scale_sigma: float = 0.02) -> np.ndarray:
     return out.reshape(-1)
 
 
+def q4_k_matrix(N: int, K: int, seed, scale_sigma: float = 0.02) -> np.ndarray:
+    """Random Q4_K weight matrix as canonical bytes, shape (N * K/256 * 144,) uint8."""
+    if K % 256:
+        raise ValueError("Q4_K needs K % 256 == 0")
+    rng = _rng(seed)
+    nb = N * (K // 256)
+    d = fp16_bits(np.abs(rng.normal(0.0, scale_sigma, nb)) / 480.0)
+    dmin = fp16_bits(np.abs(rng.normal(0.0, scale_sigma, nb)) / 64.0)
+    rest = rng.integers(0, 256, size=(nb, 140), dtype=np.uint8)
+    out = np.empty((nb, Q4_K_BLOCK_BYTES), np.uint8)
+    out[:, 0:2] = d.astype("<u2").view(np.uint8).reshape(nb, 2)
+    out[:, 2:4] = dmin.astype("<u2").view(np.uint8).reshape(nb, 2)
+    out[:, 4:] = rest
+    return out.reshape(-1)
+
+
 def f16_matrix(N: int, K: int, seed, sigma: float = 0.02) -> np.ndarray:
     """Random fp16 row-major matrix as uint16 bit patterns, shape (N*K,)."""
     rng = _rng(seed)
@@ -86,6 +108,8 @@ def matrix(kind: str, N: int, K: int, seed) -> np.ndarray:
         return q8_0_matrix(N, K, seed)
     if kind == "q4_0":
         return q4_0_matrix(N, K, seed)
+    if kind == "q4_k":
+        return q4_k_matrix(N, K, seed)
     if kind == "f16":
         return f16_matrix(N, K, seed)
     raise ValueError(kind)
@@ -97,6 +121,8 @@ def matrix_bytes(kind: str, N: int, K: int) -> int:
         return N * (K // 32) * Q8_0_BLOCK_BYTES
     if kind == "q4_0":
         return N * (K // 32) * Q4_0_BLOCK_BYTES
+    if kind == "q4_k":
+        return N * (K // 256) * Q4_K_BLOCK_BYTES
     return N * K * 2
 
 

@@ -32,6 +32,10 @@
  *    robotnurse.io "We wrote our own inference engine", "What actually moved
  *    it", item 5: some GEMVs write fp16 outputs. oracle_gemv_epilogue is the
  *    product followed by those additions, in double.
+ *  - RunIT_Mac README, kernel table ("Fused Q4_K dequant + GEMV") and
+ *    quantisation table (Q4_K_M), EdgeRunner "Run it yourself" (loads Q4_K_M):
+ *    the Q4_K super-block, whose layout the pages do not give; it is read as
+ *    the published GGUF k-quant block (q4_k_weight below).
  *  - RunIT_Mac README, kernel table and data-flow figure: RMSNorm with f32
  *    input, output and gamma precedes the projections; "EdgeRunner beats
  *    llama.cpp", The progression, fused it into the GEMV (RMSNorm+GEMV).
@@ -57,7 +61,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_Q8_0 = 1, ORACLE_Q4_0 = 2, ORACLE_F16 = 3 };
+enum { ORACLE_Q8_0 = 1, ORACLE_Q4_0 = 2, ORACLE_F16 = 3, ORACLE_Q4_K = 4 };
 
 /* IEEE 754 binary16 -> double, exact. */
 double oracle_half_to_double(uint16_t h)
@@ -93,6 +97,43 @@ static double q4_0_weight(const uint8_t *blk, int i)
     return d * (double)(nib - 8);
 }
 
+/* Q4_K super-block (256 weights, 144 bytes; the GGUF k-quant block the pages
+ * name as Q4_K / Q4_K_M without describing it, read here as published for
+ * GGUF): fp16 d, fp16 dmin, 12 bytes holding eight 6-bit scales sc[j] and
+ * eight 6-bit mins mn[j] (one pair per sub-block of 32 weights), then 128
+ * bytes of 4-bit quants. Weight i of sub-block j = i / 32:
+ *   w = d * sc[j] * q_i - dmin * mn[j]
+ * Scale/min bytes u[0..11]: for j < 4, sc[j] = low 6 bits of u[j] and mn[j] =
+ * low 6 bits of u[j + 4]; for j >= 4, sc[j] = low nibble of u[j + 4] plus the
+ * top two bits of u[j - 4] as bits 4-5, and mn[j] = high nibble of u[j + 4]
+ * plus the top two bits of u[j] as bits 4-5. Quants: weights 64g .. 64g + 63
+ * use bytes 32g .. 32g + 31, weight 64g + l in the low nibble of byte 32g + l
+ * and weight 64g + 32 + l in its high nibble. d * sc * q (<= 21 significant
+ * bits) and dmin * mn (<= 17) are exact in double, and so is their
+ * difference, so w is exact. */
+static void q4_k_scale_min(const uint8_t *u, int j, int *sc, int *mn)
+{
+    if (j < 4) {
+        *sc = u[j] & 63;
+        *mn = u[j + 4] & 63;
+    } else {
+        *sc = (u[j + 4] & 15) | ((u[j - 4] >> 6) << 4);
+        *mn = (u[j + 4] >> 4) | ((u[j] >> 6) << 4);
+    }
+}
+
+static double q4_k_weight(const uint8_t *blk, int i)
+{
+    double d = oracle_half_to_double(read_le16(blk));
+    double dmin = oracle_half_to_double(read_le16(blk + 2));
+    int sc, mn;
+    q4_k_scale_min(blk + 4, i / 32, &sc, &mn);
+    const uint8_t *qs = blk + 16;
+    int g = i / 64, l = i % 64;
+    int q = (l < 32) ? (qs[32 * g + l] & 15) : (qs[32 * g + l - 32] >> 4);
+    return d * (double)sc * (double)q - dmin * (double)mn;
+}
+
 /* One output row: y = sum W[n][k] x[k], a = sum |W[n][k] x[k]|. */
 static void one_row(int kind, const uint8_t *w, const float *x, int64_t n, int64_t K,
                     double *y, double *a)
@@ -106,6 +147,9 @@ static void one_row(int kind, const uint8_t *w, const float *x, int64_t n, int64
         } else if (kind == ORACLE_Q4_0) {
             const uint8_t *blk = w + (n * (K / 32) + k / 32) * 18;
             wk = q4_0_weight(blk, (int)(k % 32));
+        } else if (kind == ORACLE_Q4_K) {
+            const uint8_t *blk = w + (n * (K / 256) + k / 256) * 144;
+            wk = q4_k_weight(blk, (int)(k % 256));
         } else {
             wk = oracle_half_to_double(read_le16(w + (n * K + k) * 2));
         }
@@ -120,8 +164,9 @@ static void one_row(int kind, const uint8_t *w, const float *x, int64_t n, int64
 static int bad_args(int kind, int64_t N, int64_t K)
 {
     if (N < 0 || K < 0) return 1;
-    if (kind != ORACLE_Q8_0 && kind != ORACLE_Q4_0 && kind != ORACLE_F16) return 1;
+    if (kind != ORACLE_Q8_0 && kind != ORACLE_Q4_0 && kind != ORACLE_F16 && kind != ORACLE_Q4_K) return 1;
     if (kind != ORACLE_F16 && K % 32 != 0) return 1;
+    if (kind == ORACLE_Q4_K && K % 256 != 0) return 1;
     return 0;
 }
 
@@ -294,6 +339,8 @@ int oracle_gemv_rmsnorm(int kind, const void *w, const float *x, const float *ga
                 wk = q8_0_weight(wb + (n * (K / 32) + k / 32) * 34, (int)(k % 32));
             else if (kind == ORACLE_Q4_0)
                 wk = q4_0_weight(wb + (n * (K / 32) + k / 32) * 18, (int)(k % 32));
+            else if (kind == ORACLE_Q4_K)
+                wk = q4_k_weight(wb + (n * (K / 256) + k / 256) * 144, (int)(k % 256));
             else
                 wk = oracle_half_to_double(read_le16(wb + (n * K + k) * 2));
             double p = wk * xn[k];

@@ -9,7 +9,8 @@ AssertionError when the oracle disagrees with:
   * textbook special cases that reduce to a float64 numpy matmul,
   * invariants (exact scaling, zero blocks, row permutation),
   * the composition rules of the fused and multi-row entry points,
-  * closed forms of RMSNorm (a vector of ones with eps = 3; alternating +-c).
+  * closed forms of RMSNorm (a vector of ones with eps = 3; alternating +-c),
+  * hand-worked Q4_K super-blocks (tests/golden/q4_k_blocks.json) and closed forms.
 ``test_oracle_mutants.py`` plants plausible mistakes in a copy of oracle.c and
 checks that every one of them trips at least one pin.
 """
@@ -361,6 +362,64 @@ def pin_rmsnorm(L):
     assert y[0] == -8.0, y
 
 
+def _q4_k_case(case) -> tuple[np.ndarray, np.ndarray]:
+    """Build one golden Q4_K super-block and its activation from a case record."""
+    blk = bytearray(144)
+    blk[0:2] = int(case["d_bits"]).to_bytes(2, "little")
+    blk[2:4] = int(case["dmin_bits"]).to_bytes(2, "little")
+    blk[4:16] = bytes(case["scales"])
+    if case["quant_byte"] in ("group0_low", "group0_high"):
+        for l in range(32):
+            blk[16 + l] = (l % 16) << (0 if case["quant_byte"] == "group0_low" else 4)
+    else:
+        blk[16:] = bytes([case["quant_byte"]] * 128)
+    x = {"ones": np.ones(256), "index": np.arange(256.0),
+         "subblock5": (np.arange(256) // 32 == 5) * 1.0, "subblock6": (np.arange(256) // 32 == 6) * 1.0}[case["x"]]
+    return np.frombuffer(bytes(blk), np.uint8).copy(), x.astype(np.float32)
+
+
+def pin_q4_k(L):
+    # hand-worked single super-blocks (tests/golden/q4_k_blocks.json): the 6-bit
+    # scale/min packing of the lower and upper sub-blocks, the min's sign, the
+    # nibble order inside a 64-weight group, a subnormal d
+    for case in _golden("q4_k_blocks.json")["cases"]:
+        blk, x = _q4_k_case(case)
+        y, a = _gemv(L, "q4_k", blk, x, 1, 256)
+        assert y[0] == case["expect"], (case["name"], y[0], case["expect"])
+    # closed form: every sub-block with scale s and min m, all quants c, two
+    # super-blocks with different d / dmin: y = sum_b (d_b s c - dmin_b m) * sum x
+    rng = np.random.default_rng(17)
+    for s_, m_, c in ((5, 3, 9), (63, 63, 15), (0, 17, 4)):
+        u = [(s_ & 63) | ((s_ >> 4) << 6) for _ in range(4)] + [(m_ & 63) | ((m_ >> 4) << 6) for _ in range(4)] + \
+            [(s_ & 15) | ((m_ & 15) << 4) for _ in range(4)]
+        blocks = []
+        expect = 0.0
+        x = rng.integers(-4, 5, size=512).astype(np.float32)
+        for b, (db, mb) in enumerate(((0x3800, 0x3400), (0x2C00, 0x3C00))):   # (0.5, 0.25), (1/16, 1.0)
+            blk = bytes([db & 255, db >> 8, mb & 255, mb >> 8]) + bytes(u) + bytes([c | (c << 4)] * 128)
+            blocks.append(blk)
+            dv, mv = float(np.array([db], np.uint16).view(np.float16)[0]), float(np.array([mb], np.uint16).view(np.float16)[0])
+            expect += (dv * s_ * c - mv * m_) * float(x[256 * b:256 * (b + 1)].astype(np.float64).sum())
+        w = np.frombuffer(b"".join(blocks), np.uint8).copy()
+        y, _ = _gemv(L, "q4_k", w, x, 1, 512)
+        assert y[0] == expect, (s_, m_, c, y[0], expect)
+    # invariants on random matrices: exact power-of-two scaling of x, row permutation
+    N, K = 5, 512
+    w = W.matrix("q4_k", N, K, rng)
+    x = rng.standard_normal(K).astype(np.float32)
+    y, a = _gemv(L, "q4_k", w, x, N, K)
+    y2, _ = _gemv(L, "q4_k", w, x * np.float32(4), N, K)
+    assert np.array_equal(y2, 4 * y)
+    perm = np.array([3, 0, 4, 1, 2])
+    wp = w.reshape(N, -1)[perm].reshape(-1).copy()
+    yp, _ = _gemv(L, "q4_k", wp, x, N, K)
+    assert np.array_equal(yp, y[perm])
+    # Q4_K rows must be whole super-blocks
+    p = lambda arr: arr.ctypes.data_as(__import__("ctypes").c_void_p)  # noqa: E731
+    ww, xx, yy, aa = np.zeros(144, np.uint8), np.zeros(288, np.float32), np.zeros(1), np.zeros(1)
+    assert L.oracle_gemv(O.Q4_K, p(ww), p(xx), p(yy), p(aa), 1, 288, 1) != 0
+
+
 def pin_rejects_bad_shapes(L):
     w = np.zeros(34, np.uint8)
     x = np.zeros(33, np.float32)
@@ -383,6 +442,7 @@ PINS = [
     pin_composites,
     pin_epilogue,
     pin_rmsnorm,
+    pin_q4_k,
     pin_rejects_bad_shapes,
 ]
 

@@ -46,6 +46,18 @@ MUTANTS = {
                           "out[k] = (double)gamma[(k + 1) % K] * (double)x[k] / rms;"),
     "rms_gamma_dropped": ("out[k] = (double)gamma[k] * (double)x[k] / rms;", "out[k] = (double)x[k] / rms;"),
     "rms_product_unnormalised": ("double p = wk * xn[k];", "double p = wk * (double)x[k];"),
+    "q4k_scale_from_min_byte": ("*sc = u[j] & 63;", "*sc = u[j + 4] & 63;"),
+    "q4k_upper_scale_bits_wrong_byte": ("*sc = (u[j + 4] & 15) | ((u[j - 4] >> 6) << 4);",
+                                        "*sc = (u[j + 4] & 15) | ((u[j] >> 6) << 4);"),
+    "q4k_upper_min_bits_wrong_byte": ("*mn = (u[j + 4] >> 4) | ((u[j] >> 6) << 4);",
+                                      "*mn = (u[j + 4] >> 4) | ((u[j - 4] >> 6) << 4);"),
+    "q4k_min_added": ("return d * (double)sc * (double)q - dmin * (double)mn;",
+                      "return d * (double)sc * (double)q + dmin * (double)mn;"),
+    "q4k_nibbles_interleaved": ("int q = (l < 32) ? (qs[32 * g + l] & 15) : (qs[32 * g + l - 32] >> 4);",
+                                "int q = (qs[32 * g + l / 2] >> (4 * (l % 2))) & 15;"),
+    "q4k_dmin_read_as_d": ("double dmin = oracle_half_to_double(read_le16(blk + 2));",
+                           "double dmin = oracle_half_to_double(read_le16(blk));"),
+    "q4k_superblock_stride": ("w + (n * (K / 256) + k / 256) * 144", "w + (n * (K / 256) + k / 256) * 128"),
 }
 
 
