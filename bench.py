@@ -67,7 +67,7 @@ def wbytes(kind, N, K):
 
 
 def make_qgemv(qg, kind, packed, x, y, N, K, stream, label):
-    name = "qgemv_q8_0" if kind == "q8_0" else "qgemv_q4_0"
+    name = "qgemv_" + kind
     make = lambda wp: qg.bound_call(name, wp, x.data_ptr(), y.data_ptr(), N, K, stream)  # noqa: E731
     return Call(label, make(packed.data_ptr()), wbytes(kind, N, K) + 4 * K + 4 * N, qkernel_name(qg, kind, N, K),
                 packed, make)
@@ -215,6 +215,7 @@ def cold_copies(torch, weight, budget=COLD_BYTES * 6 // 5):
 
 def per_config_calls(qg, torch, stream, step_calls):
     """All five configurations as lists of calls (the headline step's calls reused for config 1)."""
+    from block_dequant_gemv_amd import workloads as W
     from block_dequant_gemv_amd.workloads import Workload
     dev = "cuda"
     keep = []
@@ -291,6 +292,17 @@ def per_config_calls(qg, torch, stream, step_calls):
         make_epilogue(qg, "q8_0", lm.weight, t(wl1.x("lm_head")), None, None, y16, 151936, 1024, stream,
                       "e q8_0 lm_head 151936x1024 fp16 out"),
     ]
+    # the Q4_K GEMV (qgemv_q4_k) on the shapes of the Q4_0 configuration: 148 packed
+    # bytes (144 canonical) per 256 weights instead of 144 per 256
+    krng = np.random.default_rng(6)
+    res[6] = []
+    for label, N, K in (("down 5120x17408", 5120, 17408), ("gate 17408x5120", 17408, 5120),
+                        ("lm_head 248320x5120", 248320, 5120)):
+        canon = W.matrix("q4_k", N, K, krng)
+        pk = qg.pack_weights("q4_k", canon, N, K)
+        del canon
+        keep.append(pk)
+        res[6].append(make_qgemv(qg, "q4_k", pk, t(W.activation(K, krng)), yb(N), N, K, stream, f"k q4_k {label}"))
     # the RMSNorm-prologue experiment: each case is (label, weight, bytes, fused(wp), norm(), gemv(wp)), the
     # unfused form being qg_rmsnorm into a separate buffer followed by the plain GEMV on it
     eps = 1e-6

@@ -60,6 +60,19 @@ __device__ __forceinline__ void q4_pairs(uint32_t w, const Consts &k, h2 (&p)[4]
     p[3] = __builtin_elementwise_fma(as_h2(and_or(w8, k.m_hi, k.magic)), sixteenth, off16);
 }
 
+// Q4_K dword -> the 8 quants q (0..15, no offset) as 4 fp16 pairs, in the order
+// of q4_pairs, each pair masked out in place and read as fp16 subnormals: pairs
+// 0 and 2 hold q * 2^-24 (mantissa bits 0..3), pairs 1 and 3 hold q * 2^-20
+// (bits 4..7), all exact; the caller sums the two scales apart and rescales.
+__device__ __forceinline__ void q4k_pairs(uint32_t w, const Consts &k, h2 (&p)[4])
+{
+    const uint32_t w8 = w >> 8;
+    p[0] = as_h2(w & k.m_lo);
+    p[1] = as_h2(w & k.m_hi);
+    p[2] = as_h2(w8 & k.m_lo);
+    p[3] = as_h2(w8 & k.m_hi);
+}
+
 // Q8_0 dword (bytes q XOR 0x80) -> the 4 int8 weights as 2 fp16 pairs, elements (0,1) (2,3).
 // v_perm_b32 builds [byte, 0x64, byte, 0x64] = fp16 (1024 + q + 128) twice.
 __device__ __forceinline__ void q8_pairs(uint32_t w, h2 (&p)[2])

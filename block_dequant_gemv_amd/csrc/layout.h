@@ -28,6 +28,17 @@
 //        0x00F000F0 (before and after a shift by 8) yields element pairs
 //        (e, e+1) in the two fp16 halves of a register.
 // The nibble value is kept as stored (0..15); the -8 offset is applied in fp16.
+//
+// Q4_K (256-weight super-blocks of 8 sub-blocks of 32 weights; canonical
+// block: fp16 d, fp16 dmin, 12 bytes of 6-bit sub-block scales and mins, 128
+// bytes of nibbles, weight = d * sc * q - dmin * mn) is packed per 32-weight
+// sub-block like Q4_0: the quant plane holds its nibbles in the Q4_0
+// arrangement, the scale plane its two 6-bit values (byte 0: sc, byte 1: mn)
+// where Q4_0 keeps the fp16 scale, and a third plane holds the super-block's
+// d and dmin:
+//   super plane: [tile][segment][slot][super-block of the segment][b] x (d, dmin) fp16
+// so a lane's 16-byte load gets d and dmin of its 4 rows. 148 bytes per
+// 256 weights (144 canonical).
 #pragma once
 
 #include <stdint.h>
@@ -42,6 +53,8 @@ namespace qgl {
 
 constexpr int kQ8_0 = 1;
 constexpr int kQ4_0 = 2;
+constexpr int kQ4_K = 3;
+constexpr int kSuperBlocks = 8;   // Q4_K: 32-weight sub-blocks per super-block
 
 constexpr int kSlots = 2;         // rows processed side by side per wavefront
 constexpr int kLanesPerSlot = 32; // lanes sharing one row = blocks per segment
@@ -51,7 +64,11 @@ constexpr int kTileRows = kSlots * kRowsPerLane;
 constexpr int kUnit = 16;         // bytes per lane per load
 constexpr int kSegWeights = kSegBlocks * 32;
 
-QG_HD int canon_block_bytes(int qt) { return qt == kQ8_0 ? 34 : 18; }
+// Canonical bytes of one row of K weights (K % 32 == 0; K % 256 == 0 for Q4_K).
+QG_HD int64_t canon_row_bytes(int qt, int64_t K)
+{
+    return qt == kQ8_0 ? (K / 32) * 34 : (qt == kQ4_0 ? (K / 32) * 18 : (K / 256) * 144);
+}
 QG_HD int packed_quant_bytes(int qt) { return qt == kQ8_0 ? 32 : 16; }
 QG_HD int halves(int qt) { return qt == kQ8_0 ? 2 : 1; }
 
@@ -65,6 +82,8 @@ struct Geometry {
     int64_t tile_q;   // quant bytes per tile
     int64_t tile_s;   // scale bytes per tile
     int64_t scale_off;
+    int64_t tile_u;   // Q4_K super-scale bytes per tile (0 otherwise)
+    int64_t sup_off;  // Q4_K super-scale plane
     int64_t total;
 };
 
@@ -82,7 +101,9 @@ QG_HD Geometry geometry(int qt, int64_t N, int64_t K)
     g.tile_q = (int64_t)kTileRows * g.KB * packed_quant_bytes(qt);
     g.tile_s = (int64_t)kTileRows * g.KB * 2;
     g.scale_off = round_up(g.n_tiles * g.tile_q, 256);
-    g.total = g.scale_off + round_up(g.n_tiles * g.tile_s, 256);
+    g.tile_u = qt == kQ4_K ? (int64_t)kTileRows * (g.KB / kSuperBlocks) * 4 : 0;
+    g.sup_off = g.scale_off + round_up(g.n_tiles * g.tile_s, 256);
+    g.total = g.sup_off + round_up(g.n_tiles * g.tile_u, 256);
     return g;
 }
 
@@ -108,11 +129,59 @@ QG_HD int64_t scale_offset(const Geometry &g, int64_t t, int64_t seg, int slot, 
            ((int64_t)slot * nb + j) * kRowsPerLane * 2;
 }
 
+// Q4_K: byte offset of d, dmin of rows b = 0..3 (slot `slot`) for super-block sb of segment seg, tile t.
+QG_HD int64_t super_offset(const Geometry &g, int64_t t, int64_t seg, int slot, int sb)
+{
+    int64_t nsb = seg_blocks(g, seg) / kSuperBlocks;
+    return g.sup_off + t * g.tile_u + seg * (int64_t)kTileRows * (kSegBlocks / kSuperBlocks) * 4 +
+           ((int64_t)slot * nsb + sb) * kRowsPerLane * 4;
+}
+
 QG_HD int q4_nibble_pos(int e) { return e / 2 + 4 * (e % 2); }  // e in 0..7 within a dword
 
-// Write one canonical block (scale + quants) of row `row`, block `blk` into the packed buffer.
-// A null `canon` writes a zero block (padding rows).
-QG_HD void pack_block(const Geometry &g, const uint8_t *canon, uint8_t *packed, int64_t row, int64_t blk)
+// Q4_K: the 6-bit scale and min of sub-block j (0..7) from a super-block's 12 bytes u.
+QG_HD void q4_k_unpack_scale(const uint8_t *u, int j, uint8_t &sc, uint8_t &mn)
+{
+    if (j < 4) {
+        sc = (uint8_t)(u[j] & 63);
+        mn = (uint8_t)(u[j + 4] & 63);
+    } else {
+        sc = (uint8_t)((u[j + 4] & 15) | ((u[j - 4] >> 6) << 4));
+        mn = (uint8_t)((u[j + 4] >> 4) | ((u[j] >> 6) << 4));
+    }
+}
+
+// Q4_K: OR the bits of sub-block j's scale and min into the 12 bytes u (the inverse).
+QG_HD void q4_k_pack_scale(uint8_t *u, int j, uint8_t sc, uint8_t mn)
+{
+    if (j < 4) {
+        u[j] |= (uint8_t)(sc & 63);
+        u[j + 4] |= (uint8_t)(mn & 63);
+    } else {
+        u[j + 4] |= (uint8_t)((sc & 15) | ((mn & 15) << 4));
+        u[j - 4] |= (uint8_t)((sc >> 4) << 6);
+        u[j] |= (uint8_t)((mn >> 4) << 6);
+    }
+}
+
+// Nibble of element e (0..31) of 32-weight block blk of a canonical row: Q4_0
+// byte e / e-16 of the block; Q4_K sub-block j = blk % 8 of super-block blk / 8,
+// the low (j even) or high (j odd) nibbles of bytes 32 (j / 2) .. + 31.
+QG_HD uint32_t canon_nibble(int qt, const uint8_t *canon_row, int64_t blk, int e)
+{
+    if (qt == kQ4_0) {
+        const uint8_t *qs = canon_row + blk * 18 + 2;
+        return (e < 16) ? (qs[e] & 0x0Fu) : (uint32_t)(qs[e - 16] >> 4);
+    }
+    const int j = (int)(blk % kSuperBlocks);
+    const uint8_t *qs = canon_row + (blk / kSuperBlocks) * 144 + 16 + 32 * (j / 2);
+    return (j % 2 == 0) ? (qs[e] & 0x0Fu) : (uint32_t)(qs[e] >> 4);
+}
+
+// Write block `blk` (32 weights) of row `row` from the row's canonical bytes
+// `canon_row` into the packed buffer. A null `canon_row` writes a zero block
+// (padding rows).
+QG_HD void pack_block(const Geometry &g, const uint8_t *canon_row, uint8_t *packed, int64_t row, int64_t blk)
 {
     int64_t t = row / kTileRows;
     int rt = (int)(row % kTileRows);
@@ -120,29 +189,43 @@ QG_HD void pack_block(const Geometry &g, const uint8_t *canon, uint8_t *packed, 
     int64_t seg = blk / kSegBlocks;
     int j = (int)(blk % kSegBlocks);
     uint8_t *sp = packed + scale_offset(g, t, seg, slot, j) + b * 2;
-    sp[0] = canon ? canon[0] : 0;
-    sp[1] = canon ? canon[1] : 0;
     if (g.qt == kQ8_0) {
+        const uint8_t *c = canon_row ? canon_row + blk * 34 : nullptr;
+        sp[0] = c ? c[0] : 0;
+        sp[1] = c ? c[1] : 0;
         for (int h = 0; h < 2; ++h) {
             uint8_t *qp = packed + quant_offset(g, t, seg, b, h, slot, j);
-            for (int i = 0; i < 16; ++i) qp[i] = canon ? (uint8_t)(canon[2 + 16 * h + i] ^ 0x80) : 0;
+            for (int i = 0; i < 16; ++i) qp[i] = c ? (uint8_t)(c[2 + 16 * h + i] ^ 0x80) : 0;
         }
-    } else {
-        uint8_t *qp = packed + quant_offset(g, t, seg, b, 0, slot, j);
-        uint32_t dw[4] = {0, 0, 0, 0};
-        if (canon) {
-            for (int e = 0; e < 32; ++e) {
-                uint32_t nib = (e < 16) ? (canon[2 + e] & 0x0Fu) : (uint32_t)(canon[2 + e - 16] >> 4);
-                dw[e / 8] |= nib << (4 * q4_nibble_pos(e % 8));
-            }
-        }
-        for (int d = 0; d < 4; ++d)
-            for (int i = 0; i < 4; ++i) qp[4 * d + i] = (uint8_t)(dw[d] >> (8 * i));
+        return;
     }
+    if (g.qt == kQ4_0) {
+        const uint8_t *c = canon_row ? canon_row + blk * 18 : nullptr;
+        sp[0] = c ? c[0] : 0;
+        sp[1] = c ? c[1] : 0;
+    } else {
+        const uint8_t *sb = canon_row ? canon_row + (blk / kSuperBlocks) * 144 : nullptr;
+        uint8_t sc = 0, mn = 0;
+        if (sb) q4_k_unpack_scale(sb + 4, (int)(blk % kSuperBlocks), sc, mn);
+        sp[0] = sc;
+        sp[1] = mn;
+        if (blk % kSuperBlocks == 0) {
+            uint8_t *up = packed + super_offset(g, t, seg, slot, j / kSuperBlocks) + b * 4;
+            for (int i = 0; i < 4; ++i) up[i] = sb ? sb[i] : 0;
+        }
+    }
+    uint8_t *qp = packed + quant_offset(g, t, seg, b, 0, slot, j);
+    uint32_t dw[4] = {0, 0, 0, 0};
+    if (canon_row)
+        for (int e = 0; e < 32; ++e) dw[e / 8] |= canon_nibble(g.qt, canon_row, blk, e) << (4 * q4_nibble_pos(e % 8));
+    for (int d = 0; d < 4; ++d)
+        for (int i = 0; i < 4; ++i) qp[4 * d + i] = (uint8_t)(dw[d] >> (8 * i));
 }
 
-// Inverse of pack_block: rebuild the canonical block bytes.
-QG_HD void unpack_block(const Geometry &g, const uint8_t *packed, uint8_t *canon, int64_t row, int64_t blk)
+// Inverse of pack_block: rebuild block `blk` of the row's canonical bytes. For
+// Q4_K the block's bits are OR-ed into the super-block (whose bytes must start
+// at zero) and d, dmin are written with its first sub-block.
+QG_HD void unpack_block(const Geometry &g, const uint8_t *packed, uint8_t *canon_row, int64_t row, int64_t blk)
 {
     int64_t t = row / kTileRows;
     int rt = (int)(row % kTileRows);
@@ -150,25 +233,40 @@ QG_HD void unpack_block(const Geometry &g, const uint8_t *packed, uint8_t *canon
     int64_t seg = blk / kSegBlocks;
     int j = (int)(blk % kSegBlocks);
     const uint8_t *sp = packed + scale_offset(g, t, seg, slot, j) + b * 2;
-    canon[0] = sp[0];
-    canon[1] = sp[1];
     if (g.qt == kQ8_0) {
+        uint8_t *c = canon_row + blk * 34;
+        c[0] = sp[0];
+        c[1] = sp[1];
         for (int h = 0; h < 2; ++h) {
             const uint8_t *qp = packed + quant_offset(g, t, seg, b, h, slot, j);
-            for (int i = 0; i < 16; ++i) canon[2 + 16 * h + i] = (uint8_t)(qp[i] ^ 0x80);
+            for (int i = 0; i < 16; ++i) c[2 + 16 * h + i] = (uint8_t)(qp[i] ^ 0x80);
         }
-    } else {
-        const uint8_t *qp = packed + quant_offset(g, t, seg, b, 0, slot, j);
-        for (int i = 0; i < 16; ++i) canon[2 + i] = 0;
-        for (int e = 0; e < 32; ++e) {
-            int d = e / 8, p = q4_nibble_pos(e % 8);
-            uint32_t dw = (uint32_t)qp[4 * d] | ((uint32_t)qp[4 * d + 1] << 8) | ((uint32_t)qp[4 * d + 2] << 16) |
-                          ((uint32_t)qp[4 * d + 3] << 24);
-            uint8_t nib = (uint8_t)((dw >> (4 * p)) & 0xF);
-            if (e < 16) canon[2 + e] |= nib;
-            else canon[2 + e - 16] |= (uint8_t)(nib << 4);
-        }
+        return;
     }
+    const uint8_t *qp = packed + quant_offset(g, t, seg, b, 0, slot, j);
+    uint8_t nib[32];
+    for (int e = 0; e < 32; ++e) {
+        int d = e / 8, p = q4_nibble_pos(e % 8);
+        uint32_t dw = (uint32_t)qp[4 * d] | ((uint32_t)qp[4 * d + 1] << 8) | ((uint32_t)qp[4 * d + 2] << 16) |
+                      ((uint32_t)qp[4 * d + 3] << 24);
+        nib[e] = (uint8_t)((dw >> (4 * p)) & 0xF);
+    }
+    if (g.qt == kQ4_0) {
+        uint8_t *c = canon_row + blk * 18;
+        c[0] = sp[0];
+        c[1] = sp[1];
+        for (int i = 0; i < 16; ++i) c[2 + i] = (uint8_t)(nib[i] | (nib[i + 16] << 4));
+        return;
+    }
+    const int js = (int)(blk % kSuperBlocks);
+    uint8_t *sb = canon_row + (blk / kSuperBlocks) * 144;
+    q4_k_pack_scale(sb + 4, js, sp[0], sp[1]);
+    if (js == 0) {
+        const uint8_t *up = packed + super_offset(g, t, seg, slot, j / kSuperBlocks) + b * 4;
+        for (int i = 0; i < 4; ++i) sb[i] = up[i];
+    }
+    uint8_t *qs = sb + 16 + 32 * (js / 2);
+    for (int e = 0; e < 32; ++e) qs[e] |= (uint8_t)(js % 2 == 0 ? nib[e] : nib[e] << 4);
 }
 
 }  // namespace qgl

@@ -55,7 +55,10 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb)
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-bool valid_qtype(int qt) { return qt == QG_Q8_0 || qt == QG_Q4_0; }
+bool valid_qtype(int qt) { return qt == QG_Q8_0 || qt == QG_Q4_0 || qt == QG_Q4_K; }
+
+// K granularity of a quantised type: 32 weights per block, 256 per Q4_K super-block.
+int64_t k_unit(int qt) { return qt == QG_Q4_K ? 256 : 32; }
 
 // Shape limits: rows and K must index 64-bit byte offsets safely and the grid
 // must fit 2^31 workgroups.
@@ -66,7 +69,8 @@ qg_status check_qshape(int qt, int64_t N, int64_t K, const char *fn)
     if (!valid_qtype(qt)) return fail(QG_EUNSUPPORTED, "%s: unknown qtype %d", fn, qt);
     if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim)
         return fail(QG_EINVAL, "%s: N=%lld K=%lld must be positive", fn, (long long)N, (long long)K);
-    if (K % 32 != 0) return fail(QG_EINVAL, "%s: K=%lld is not a multiple of 32", fn, (long long)K);
+    if (K % k_unit(qt) != 0)
+        return fail(QG_EINVAL, "%s: K=%lld is not a multiple of %lld", fn, (long long)K, (long long)k_unit(qt));
     if (N * (K / 32) > ((int64_t)1 << 42)) return fail(QG_EINVAL, "%s: matrix too large", fn);
     return QG_OK;
 }
@@ -283,6 +287,8 @@ qg_status run_qgemv(int qt, int epi, const void *w, const float *x, void *y, int
                     int64_t K, int M, void *stream, const char *fn, const Affine &af = Affine(),
                     const Norm &nm = Norm())
 {
+    if (qt == QG_Q4_K && (epi != qgk::kEpiPlain || M != 1 || nm.on))
+        return fail(QG_EUNSUPPORTED, "%s: Q4_K weights have the plain single-row GEMV only (qgemv_q4_k)", fn);
     qg_status st = check_qshape(qt, rows, K, fn);
     if (st) return st;
     if (!w || !x || !y) return fail(QG_EINVAL, "%s: null pointer", fn);
@@ -348,9 +354,9 @@ qg_status check_pack(int qt, const void *canon, const void *packed, int64_t N, i
 void host_pack_rows(const Geometry &g, const uint8_t *canon, uint8_t *packed, int64_t row0, int64_t nrows,
                     bool pad)
 {
-    const int cb = qgl::canon_block_bytes(g.qt);
+    const int64_t rb = qgl::canon_row_bytes(g.qt, g.K);
     for (int64_t r = 0; r < nrows; ++r)
-        for (int64_t b = 0; b < g.KB; ++b) qgl::pack_block(g, canon + (r * g.KB + b) * cb, packed, row0 + r, b);
+        for (int64_t b = 0; b < g.KB; ++b) qgl::pack_block(g, canon + r * rb, packed, row0 + r, b);
     if (pad)
         for (int64_t r = g.N; r < g.n_tiles * qgl::kTileRows; ++r)
             for (int64_t b = 0; b < g.KB; ++b) qgl::pack_block(g, nullptr, packed, r, b);
@@ -411,7 +417,7 @@ extern "C" {
 
 size_t qg_packed_size(int qtype, int64_t N, int64_t K)
 {
-    if (!valid_qtype(qtype) || N <= 0 || K <= 0 || K % 32 || N > kMaxDim || K > kMaxDim) return 0;
+    if (!valid_qtype(qtype) || N <= 0 || K <= 0 || K % k_unit(qtype) || N > kMaxDim || K > kMaxDim) return 0;
     return (size_t)qgl::geometry(qtype, N, K).total;
 }
 
@@ -431,7 +437,7 @@ qg_status qg_pack_rows(int qtype, const void *canonical, void *packed, int64_t N
                     (long long)(row0 + nrows), (long long)N_total);
     if (!aligned(packed, 16)) return fail(QG_EALIGN, "%s: packed buffer must be 16-byte aligned", fn);
     const Geometry g = qgl::geometry(qtype, N_total, K);
-    const size_t cbytes = (size_t)nrows * (size_t)g.KB * qgl::canon_block_bytes(qtype);
+    const size_t cbytes = (size_t)nrows * (size_t)qgl::canon_row_bytes(qtype, K);
     if (overlap(canonical, cbytes, packed, (size_t)g.total)) return fail(QG_EINVAL, "%s: buffers overlap", fn);
     const bool last = row0 + nrows == N_total;
     const int64_t rows_to_write = nrows + (last ? g.n_tiles * qgl::kTileRows - N_total : 0);
@@ -450,7 +456,7 @@ qg_status qg_pack_gateup(int qtype, const void *gate, const void *up, void *pack
     if (!up) return fail(QG_EINVAL, "%s: null pointer", fn);
     if (!aligned(packed, 16)) return fail(QG_EALIGN, "%s: packed buffer must be 16-byte aligned", fn);
     const Geometry g = qgl::geometry(qtype, 2 * N_ff, K);
-    const size_t cbytes = (size_t)N_ff * (size_t)g.KB * qgl::canon_block_bytes(qtype);
+    const size_t cbytes = (size_t)N_ff * (size_t)qgl::canon_row_bytes(qtype, K);
     if (overlap(gate, cbytes, packed, (size_t)g.total) || overlap(up, cbytes, packed, (size_t)g.total))
         return fail(QG_EINVAL, "%s: buffers overlap", fn);
     hipError_t e = qgk::launch_pack(g, (const uint8_t *)gate, (const uint8_t *)up, (uint8_t *)packed,
@@ -475,10 +481,11 @@ qg_status qg_unpack_host(int qtype, const void *packed_host, void *canonical_hos
     qg_status st = check_pack(qtype, canonical_host, packed_host, N, K, "qg_unpack_host");
     if (st) return st;
     const Geometry g = qgl::geometry(qtype, N, K);
-    const int cb = qgl::canon_block_bytes(qtype);
+    const int64_t rb = qgl::canon_row_bytes(qtype, K);
+    if (qtype == QG_Q4_K) memset(canonical_host, 0, (size_t)(N * rb));   // Q4_K blocks are OR-ed together
     for (int64_t r = 0; r < N; ++r)
         for (int64_t b = 0; b < g.KB; ++b)
-            qgl::unpack_block(g, (const uint8_t *)packed_host, (uint8_t *)canonical_host + (r * g.KB + b) * cb, r, b);
+            qgl::unpack_block(g, (const uint8_t *)packed_host, (uint8_t *)canonical_host + r * rb, r, b);
     return ok();
 }
 
@@ -489,12 +496,11 @@ qg_status qg_pack_gateup_host(int qtype, const void *gate_host, const void *up_h
     if (st) return st;
     if (!up_host) return fail(QG_EINVAL, "qg_pack_gateup_host: null pointer");
     const Geometry g = qgl::geometry(qtype, 2 * N_ff, K);
-    const int cb = qgl::canon_block_bytes(qtype);
+    const int64_t rb = qgl::canon_row_bytes(qtype, K);
     memset(packed_host, 0, (size_t)g.total);
     for (int64_t v = 0; v < 2 * N_ff; ++v) {
         const uint8_t *base = (const uint8_t *)((v & 1) ? up_host : gate_host);
-        for (int64_t b = 0; b < g.KB; ++b)
-            qgl::pack_block(g, base + ((v >> 1) * g.KB + b) * cb, (uint8_t *)packed_host, v, b);
+        for (int64_t b = 0; b < g.KB; ++b) qgl::pack_block(g, base + (v >> 1) * rb, (uint8_t *)packed_host, v, b);
     }
     for (int64_t v = 2 * N_ff; v < g.n_tiles * qgl::kTileRows; ++v)
         for (int64_t b = 0; b < g.KB; ++b) qgl::pack_block(g, nullptr, (uint8_t *)packed_host, v, b);
@@ -564,7 +570,8 @@ qg_status qg_rmsnorm(const float *x, const float *gamma, float eps, float *out, 
 
 size_t qg_prefill_workspace_size(int qtype, int64_t N, int64_t K, int64_t M)
 {
-    if (!valid_qtype(qtype) || N <= 0 || N > kMaxDim || M <= 0 || M > kGemmMaxM || K <= 0 || K % 32 ||
+    if (!valid_qtype(qtype) || qtype == QG_Q4_K || N <= 0 || N > kMaxDim || M <= 0 || M > kGemmMaxM || K <= 0 ||
+        K % 32 ||
         K > kMaxDim)
         return 0;
     return plan_gemm(qtype, N, K, M).bytes;
@@ -576,6 +583,7 @@ qg_status qgemm_prefill(int qtype, const void *w_packed, const float *X, float *
     const char *fn = "qgemm_prefill";
     qg_status st = check_qshape(qtype, N, K, fn);
     if (st) return st;
+    if (qtype == QG_Q4_K) return fail(QG_EUNSUPPORTED, "%s: Q4_K weights have the GEMV only", fn);
     if (M <= 0 || M > kGemmMaxM) return fail(QG_EINVAL, "%s: M=%lld outside 1..%lld", fn, (long long)M,
                                              (long long)kGemmMaxM);
     if (!w_packed || !X || !Y || !workspace) return fail(QG_EINVAL, "%s: null pointer", fn);
@@ -620,6 +628,11 @@ qg_status qgemm_prefill(int qtype, const void *w_packed, const float *X, float *
         if (e != hipSuccess) return hip_fail(e, fn);
     }
     return ok();
+}
+
+qg_status qgemv_q4_k(const void *w_packed, const float *x, float *y, int64_t N, int64_t K, void *stream)
+{
+    return run_qgemv(QG_Q4_K, qgk::kEpiPlain, w_packed, x, y, N, N, K, 1, stream, "qgemv_q4_k");
 }
 
 qg_status qgemv_fused_gateup_silu(int qtype, const void *w_gateup_packed, const float *x, float *y, int64_t N_ff,
@@ -690,7 +703,7 @@ qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int *split_k_ways
 {
     qg_status st = check_qshape(qtype, N, K, "qg_plan_info");
     if (st) return st;
-    if (M < 1 || M > 6) return fail(QG_EUNSUPPORTED, "qg_plan_info: M=%d", M);
+    if (M < 1 || M > 6 || (qtype == QG_Q4_K && M != 1)) return fail(QG_EUNSUPPORTED, "qg_plan_info: M=%d", M);
     const qgk::QPlan p = make_qplan(qtype, N, K, M);
     if (split_k_ways) *split_k_ways = p.W;
     if (workgroups) *workgroups = p.grid;

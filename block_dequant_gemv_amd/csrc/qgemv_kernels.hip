@@ -52,12 +52,14 @@ __device__ __forceinline__ float silu_mul(float g, float u)
 }
 
 // One lane's packed data for one (row tile, segment): 16 bytes per row and
-// half-block, plus the fp16 scales of its 4 rows.
+// half-block, plus the fp16 scales of its 4 rows (Q4_K: their 6-bit scales and
+// mins, and in `sup` the d and dmin of their super-blocks).
 template <int QT>
 struct Unit {
     static constexpr int NH = (QT == kQ8_0) ? 2 : 1;
     u32x4 q[kRowsPerLane][NH];
     u32x2 sc;
+    u32x4 sup;
 };
 
 // A lane's place in a segment: the byte offset of its first 16-byte quant
@@ -68,6 +70,7 @@ struct Unit {
 struct LanePlace {
     uint32_t off_full, off_last;   // (slot * nb + jc) * 16 for nb = 32 / nb_last
     uint32_t str_last;             // bytes between the b/h units of the last segment (wave-uniform)
+    uint32_t sup_full, sup_last;   // Q4_K: (slot * nb/8 + jc/8) * 16, d and dmin of the 4 rows
     int j_last;                    // jc in the last segment
     bool live_last;
 };
@@ -81,6 +84,8 @@ __device__ __forceinline__ LanePlace lane_place(const Geometry &g, int slot, int
     p.off_full = (uint32_t)(slot * kSegBlocks + j) * kUnit;
     p.off_last = (uint32_t)(slot * nb_last + p.j_last) * kUnit;
     p.str_last = (uint32_t)(kSlots * nb_last * kUnit);
+    p.sup_full = (uint32_t)(slot * (kSegBlocks / kSuperBlocks) + j / kSuperBlocks) * kUnit;
+    p.sup_last = (uint32_t)(slot * (nb_last / kSuperBlocks) + p.j_last / kSuperBlocks) * kUnit;
     return p;
 }
 
@@ -113,16 +118,78 @@ __device__ __forceinline__ void load_unit(Unit<QT> &u, const uint8_t *__restrict
     // scales: (slot * nb + jc) * 8 bytes = half the quant offset
     const uint8_t *sbase = wp + g.scale_off + t * g.tile_s + s * (int64_t)(kTileRows * kSegBlocks * 2);
     u.sc = __builtin_nontemporal_load((const u32x2 *)(sbase + (off >> 1)));
+    if constexpr (QT == kQ4_K) {
+        const uint32_t so = real ? (last ? lp.sup_last : lp.sup_full) : 0u;
+        const uint8_t *ubase = wp + g.sup_off + t * g.tile_u + s * (int64_t)(kTileRows * (kSegBlocks / kSuperBlocks) * 4);
+        u.sup = __builtin_nontemporal_load((const u32x4 *)(ubase + so));
+    }
 }
 
 // acc[m][b] += d_b * sum_e v_e * x_m[e] over the lane's block of segment s.
 // j is the block whose activations the lane reads; live is false only for
 // lanes past the end of a ragged last segment.
+// Q4_K: acc[0][b] += d*sc * sum_e q_e x_e - dmin*mn * sum_e x_e over the lane's
+// sub-block (the weight's two terms summed apart, as the k-quant dot product
+// does): one fma per weight, and the sum of x shared by the 4 rows. The quants
+// arrive as fp16 subnormals q * 2^-24 (elements 0, 1 of each 4) and q * 2^-20
+// (elements 2, 3), summed in two accumulators and joined exactly up to one
+// rounding; the 2^24 goes into d*sc. d*sc and dmin*mn are exact (11-bit by 6-bit
+// products). Dead lanes of a ragged segment get zero scales and mins: they add 0.
+template <bool XLDS>
+__device__ __forceinline__ void compute_unit_q4k(const Unit<kQ4_K> &u, float (&acc)[1][kRowsPerLane],
+                                                 const Consts &k, const f32x4 *xs4, const float *__restrict__ x,
+                                                 int64_t s, int j, bool live)
+{
+    constexpr int B = kRowsPerLane;
+    float s24[B], s20[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) s24[b] = s20[b] = 0.0f;
+    float sx = 0.0f;
+    const f32x4 *xl = xs4 + ((uint32_t)s << 8) + (uint32_t)j;
+    const float *xg = x + s * kSegWeights + j * 32;
+#pragma unroll
+    for (int c = 0; c < 8; c += 2) {
+        f32x4 xv[2];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) xv[cc] = XLDS ? xl[(c + cc) * 32] : *(const f32x4 *)(xg + (c + cc) * 4);
+        sx = sx + (((xv[0].x + xv[0].y) + (xv[0].z + xv[0].w)) + ((xv[1].x + xv[1].y) + (xv[1].z + xv[1].w)));
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            h2 p[4];
+            q4k_pairs(u.q[b][0][c >> 1], k, p);
+            float lo = s24[b], hi = s20[b];
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                lo = __builtin_fmaf((float)p[2 * cc].x, xv[cc].x, lo);
+                lo = __builtin_fmaf((float)p[2 * cc].y, xv[cc].y, lo);
+                hi = __builtin_fmaf((float)p[2 * cc + 1].x, xv[cc].z, hi);
+                hi = __builtin_fmaf((float)p[2 * cc + 1].y, xv[cc].w, hi);
+            }
+            s24[b] = lo;
+            s20[b] = hi;
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const uint32_t sw = ((b < 2) ? u.sc.x : u.sc.y) >> (16 * (b & 1));   // byte 0: sc, byte 1: mn
+        const h2 dd = as_h2(u.sup[b]);                                        // (d, dmin)
+        const float scl = live ? (float)dd.x * (float)(sw & 0xFFu) * 16777216.0f : 0.0f;
+        const float mnv = live ? (float)dd.y * (float)((sw >> 8) & 0xFFu) : 0.0f;
+        const float sq = __builtin_fmaf(s20[b], 0.0625f, s24[b]);   // sum q x * 2^-24
+        acc[0][b] = acc[0][b] + __builtin_fmaf(scl, sq, -(mnv * sx));
+    }
+}
+
 template <int QT, int M, bool XLDS>
 __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][kRowsPerLane], const Consts &k,
                                              const f32x4 *xs4, const float *__restrict__ x, int64_t x_stride,
                                              int64_t nseg, int64_t s, int j, bool live)
 {
+    if constexpr (QT == kQ4_K) {
+        static_assert(M == 1, "Q4_K has the single-row GEMV only");
+        compute_unit_q4k<XLDS>(u, acc, k, xs4, x, s, j, live);
+        return;
+    }
     constexpr int B = kRowsPerLane;
     float sb[M][B];
 #pragma unroll
@@ -747,27 +814,32 @@ __global__ void pack_kernel(Geometry g, const uint8_t *__restrict__ canon, const
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= nthreads) return;
     const int64_t r = i / g.KB, blk = i - r * g.KB;
-    const int cb = canon_block_bytes(g.qt);
+    const int64_t rb = canon_row_bytes(g.qt, g.K);
     if (mode == kPackRows) {
         const int64_t row = row0 + r;
-        const uint8_t *src = (r < nrows) ? canon + (r * g.KB + blk) * cb : nullptr;
+        const uint8_t *src = (r < nrows) ? canon + r * rb : nullptr;
         pack_block(g, src, packed, row, blk);
     } else {
         const int64_t v = r;
         const int64_t n = v >> 1;
         const uint8_t *base = (v & 1) ? canon_up : canon;
-        const uint8_t *src = (v < g.N) ? base + (n * g.KB + blk) * cb : nullptr;
+        const uint8_t *src = (v < g.N) ? base + n * rb : nullptr;
         pack_block(g, src, packed, v, blk);
     }
 }
 
-// Zero the alignment gaps between and after the two packed planes (so that a
-// packed buffer is fully determined by its canonical input).
-__global__ void zero_gaps_kernel(uint8_t *__restrict__ packed, int64_t a0, int64_t a1, int64_t b0, int64_t b1)
+// Zero the alignment gaps after the packed planes (so that a packed buffer is
+// fully determined by its canonical input): [gap[2k], gap[2k+1]) for k < 3.
+struct Gaps {
+    int64_t b[6];
+};
+
+__global__ void zero_gaps_kernel(uint8_t *__restrict__ packed, Gaps gp)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (a0 + i < a1) packed[a0 + i] = 0;
-    if (b0 + i < b1) packed[b0 + i] = 0;
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+        if (gp.b[2 * k] + i < gp.b[2 * k + 1]) packed[gp.b[2 * k] + i] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -896,6 +968,11 @@ hipError_t launch_qgemv(int qt, int M, int epi, const QPlan &p, const uint8_t *w
                         const QArgs &a, hipStream_t s)
 {
     if (qt == kQ8_0) return dispatch_m<kQ8_0>(wp, x, y, a, M, epi, p, s);
+    if (qt == kQ4_K) {
+        // the plain single-row GEMV only (the C ABI refuses the other forms)
+        if (M != 1 || epi != kEpiPlain || p.norm) return hipErrorInvalidValue;
+        return dispatch_form<kQ4_K, 1, kEpiPlain>(wp, x, y, a, p, s);
+    }
     return dispatch_m<kQ4_0>(wp, x, y, a, M, epi, p, s);
 }
 
@@ -939,11 +1016,16 @@ hipError_t launch_pack(const Geometry &g, const uint8_t *canon, const uint8_t *c
         if (e != hipSuccess) return e;
     }
     if (zero_gaps) {
-        const int64_t a0 = g.n_tiles * g.tile_q, a1 = g.scale_off;
-        const int64_t b0 = g.scale_off + g.n_tiles * g.tile_s, b1 = g.total;
-        const int64_t n = (a1 - a0 > b1 - b0) ? a1 - a0 : b1 - b0;   // each gap < 256 bytes
-        if (n > 0) {
-            hipLaunchKernelGGL(zero_gaps_kernel, dim3(1), dim3(256), 0, s, packed, a0, a1, b0, b1);
+        Gaps gp;
+        gp.b[0] = g.n_tiles * g.tile_q;
+        gp.b[1] = g.scale_off;
+        gp.b[2] = g.scale_off + g.n_tiles * g.tile_s;
+        gp.b[3] = g.sup_off;
+        gp.b[4] = g.sup_off + g.n_tiles * g.tile_u;
+        gp.b[5] = g.total;
+        // each gap is under 256 bytes (plane alignment)
+        if (gp.b[1] > gp.b[0] || gp.b[3] > gp.b[2] || gp.b[5] > gp.b[4]) {
+            hipLaunchKernelGGL(zero_gaps_kernel, dim3(1), dim3(256), 0, s, packed, gp);
             return hipGetLastError();
         }
     }

@@ -52,20 +52,23 @@ typedef enum {
     QG_EHIP = 4          /* the HIP runtime reported an error at launch         */
 } qg_status;
 
-typedef enum { QG_Q8_0 = 1, QG_Q4_0 = 2 } qg_qtype;
+typedef enum { QG_Q8_0 = 1, QG_Q4_0 = 2, QG_Q4_K = 3 } qg_qtype;
 
 /* ---- load-time packing --------------------------------------------------- */
 
-/* Bytes of the packed form of an N x K matrix of `qtype` (K % 32 == 0, N, K > 0).
+/* Bytes of the packed form of an N x K matrix of `qtype` (K % 32 == 0, K % 256
+ * == 0 for QG_Q4_K, N, K > 0).
  * Returns 0 for invalid arguments. The packed form holds the same quant and
  * scale bytes as the canonical one plus zero padding of the last row tile (up
- * to 7 rows) and 256-byte alignment of its two planes. */
+ * to 7 rows) and 256-byte alignment of its two planes (three for Q4_K, whose
+ * super-block d and dmin get a plane of their own). */
 size_t qg_packed_size(int qtype, int64_t N, int64_t K);
 
 /* Re-tile a canonical matrix already in device memory into the packed layout.
  * canonical: N*K/32 GGUF-style blocks, row-major (row n = K/32 consecutive
  *   blocks; block = little-endian fp16 scale then the quants; Q4_0 byte j holds
- *   element j in its low nibble and element j+16 in its high nibble).
+ *   element j in its low nibble and element j+16 in its high nibble); for Q4_K
+ *   N*K/256 144-byte super-blocks, laid out as qgemv_q4_k states.
  * packed: qg_packed_size(qtype, N, K) bytes, 16-byte aligned, not overlapping
  *   canonical. Padding rows are written as zeros. Stream-ordered kernel. */
 qg_status qg_pack(int qtype, const void *canonical, void *packed, int64_t N, int64_t K, void *stream);
@@ -103,6 +106,19 @@ qg_status qgemv_q8_0(const void *w_packed, const float *x, float *y, int64_t N, 
 
 /* Same for a packed Q4_0 weight (weight value nibble - 8). */
 qg_status qgemv_q4_0(const void *w_packed, const float *x, float *y, int64_t N, int64_t K, void *stream);
+
+/* The same for a packed Q4_K weight (K % 256 == 0). Q4_K is the k-quant block
+ * of the RunIT_Mac README's "Fused Q4_K dequant + GEMV" kernel and Q4_K_M
+ * models (quantisation table); its layout is not on the pages and is read as
+ * the published GGUF block: per 256 weights an fp16 d and dmin, eight 6-bit
+ * sub-block scales sc and mins mn in 12 bytes, 128 bytes of 4-bit quants q;
+ * weight = d * sc * q - dmin * mn. Per 32-weight sub-block the product is
+ * summed as d*sc * sum(q x) - dmin*mn * sum(x) in fp32 (the two terms can
+ * cancel: the rounding scales with sum (|d sc q| + |dmin mn|) |x|).
+ * Q4_K packs with qg_pack / qg_pack_rows / qg_pack_host (148 bytes per 256
+ * weights) and is accepted by this GEMV only: the other GEMV calls, the verify
+ * and the prefill GEMM return QG_EUNSUPPORTED for it. */
+qg_status qgemv_q4_k(const void *w_packed, const float *x, float *y, int64_t N, int64_t K, void *stream);
 
 /* Output element type of qgemv_epilogue. */
 typedef enum { QG_OUT_F32 = 0, QG_OUT_F16 = 1 } qg_out_type;

@@ -1,0 +1,153 @@
+"""GPU parity of the Q4_K GEMV (qgemv_q4_k) against the fp64 oracle: shapes that
+span several row tiles, ragged row tiles, ragged last segments of 8, 16 and 24
+sub-blocks, split-K plans, the global-memory activation path and the
+persistent form; the device packer against the host packer; exact closed forms
+(a subnormal d, the min term alone); every forced launch shape; and the same
+bits run to run.
+
+Tolerance. The kernel sums d*sc * sum(q x) and dmin*mn * sum(x) per sub-block
+and subtracts them, so its rounding scales with sum (|d sc q| + |dmin mn|) |x|
+rather than with sum |w x| (the terms can cancel); the bound is 1e-5 of that
+magnitude + 1e-7, the linear bound of the other types with the two terms'
+magnitudes in place of |w|."""
+import itertools
+import os
+
+import numpy as np
+import pytest
+
+import block_dequant_gemv_amd as qg
+import oracle as O
+from block_dequant_gemv_amd import workloads as W
+from gpu_helpers import THREADS, announce, assert_linear, empty_f32, q4_k_term_bound, run_qgemv, sync, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# (N, K), K % 256 == 0: one super-block; under one tile; one tile; a tile + 1
+# row with an 8-block last segment; 16- and 24-block last segments; 3 full
+# segments; 5 segments; 17 segments (split-K); activations too large for LDS;
+# then the persistent form: 251 tiles with a ragged row tile and an 8-block last
+# segment, and 413 tiles of 5 segments.
+SHAPES = [(1, 256), (7, 512), (8, 1024), (9, 1280), (33, 1536), (40, 1792), (100, 3072), (257, 5120),
+          (640, 17408), (24, 32768), (2001, 8448), (3300, 5120)]
+
+
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_q4_k_matches_oracle(N, K):
+    rng = np.random.default_rng(4000 + N + K)
+    canon = W.matrix("q4_k", N, K, rng)
+    x = W.activation(K, rng)
+    announce(f"qgemv_q4_k N={N} K={K} plan={qg.qg_plan_info('q4_k', N, K)}")
+    y, tail = run_qgemv("q4_k", canon, x, N, K, canary=37)
+    assert np.all(tail == 12345.0), "wrote past y[N-1]"
+    y_ref, a_ref = O.gemv("q4_k", canon, x, N, K, threads=THREADS)
+    bound = q4_k_term_bound(canon, x, N, K, threads=THREADS)
+    assert np.all(bound >= a_ref * (1 - 1e-12))
+    assert_linear(y, y_ref, bound, f"q4_k {N}x{K}")
+
+
+def test_q4_k_pack_device_equals_host():
+    for N, K in ((1, 256), (9, 1280), (100, 3072), (37, 5120), (5, 1792)):
+        canon = W.matrix("q4_k", N, K, np.random.default_rng(N + K))
+        announce(f"qg_pack q4_k N={N} K={K}")
+        packed = qg.pack_weights("q4_k", canon, N, K)
+        assert np.array_equal(packed.cpu().numpy(), qg.qg_pack_host("q4_k", canon, N, K)), (N, K)
+    # load-time concatenation of row ranges
+    K = 1024
+    parts = [(W.matrix("q4_k", n, K, np.random.default_rng(n)), n) for n in (20, 9, 11)]
+    announce("qg_pack_rows q4_k concat")
+    packed = qg.pack_concat("q4_k", parts, K)
+    cat = np.concatenate([p for p, _ in parts])
+    assert np.array_equal(packed.cpu().numpy(), qg.qg_pack_host("q4_k", cat, 40, K))
+
+
+def _superblock(d: int, dmin: int, sc: int, mn: int, q: int) -> bytes:
+    """One canonical Q4_K super-block with every sub-block's scale sc and min mn
+    and every quant q (the 6-bit fields packed as the format stores them)."""
+    u = bytearray(12)
+    for j in range(8):
+        if j < 4:
+            u[j] |= sc
+            u[j + 4] |= mn
+        else:
+            u[j + 4] |= (sc & 15) | ((mn & 15) << 4)
+            u[j - 4] |= (sc >> 4) << 6
+            u[j] |= (mn >> 4) << 6
+    return d.to_bytes(2, "little") + dmin.to_bytes(2, "little") + bytes(u) + bytes([q | (q << 4)] * 128)
+
+
+@pytest.mark.parametrize("d,dmin,sc,mn,q,w", [
+    (0x3800, 0x3400, 3, 2, 7, 10.0),               # 0.5 * 3 * 7 - 0.25 * 2
+    (0x0001, 0x0000, 63, 0, 15, 945 * 2.0 ** -24),  # subnormal d, no flush to zero
+    (0x0000, 0x3C00, 0, 63, 15, -63.0),            # the min term alone
+    (0x3C00, 0x3C00, 63, 63, 0, -63.0),            # q = 0: only -dmin * mn remains
+])
+def test_q4_k_closed_forms_exact_on_gpu(d, dmin, sc, mn, q, w):
+    # every weight equal, x = 1: y = w * K exactly (every partial sum is exact)
+    N, K = 16, 5120
+    canon = np.frombuffer(_superblock(d, dmin, sc, mn, q) * (N * K // 256), np.uint8).copy()
+    announce(f"q4_k closed form d={d:#x} dmin={dmin:#x} sc={sc} mn={mn} q={q}")
+    y = run_qgemv("q4_k", canon, np.ones(K, np.float32), N, K)
+    assert np.all(y == np.float32(w * K)), (y[:4], w * K)
+    y_ref, _ = O.gemv("q4_k", canon, np.ones(K, np.float32), N, K)
+    assert np.all(y_ref == w * K)
+
+
+KNOBS = ("QG_PERSIST", "QG_SPLIT_K", "QG_X_GLOBAL", "QG_WAVES_PER_WG", "QG_TILES_PER_GROUP", "QG_PREFETCH",
+         "QG_STRIDE_GROUPS")
+
+
+def _set(**kw):
+    for k in KNOBS:
+        os.environ.pop(k, None)
+    for k, v in kw.items():
+        os.environ[k] = str(v)
+    qg.qg_reload_tuning()
+
+
+@pytest.mark.parametrize("N,K", [(203, 8192 + 256), (1000, 1024)])
+def test_q4_k_forced_launch_shapes(N, K):
+    rng = np.random.default_rng(N * K + 4)
+    canon = W.matrix("q4_k", N, K, rng)
+    packed = qg.pack_weights("q4_k", canon, N, K)
+    x = W.activation(K, rng)
+    xd = to_dev(x)
+    y_ref, _ = O.gemv("q4_k", canon, x, N, K, threads=THREADS)
+    bound = q4_k_term_bound(canon, x, N, K, threads=THREADS)
+    nseg = -(-K // 1024)
+    combos = [dict(QG_PERSIST=1, QG_X_GLOBAL=xg) for xg in (0, 1)]
+    combos += [dict(QG_PERSIST=0, QG_STRIDE_GROUPS=3, QG_WAVES_PER_WG=1, QG_SPLIT_K=split)
+               for split in (1, 2) if split <= nseg]
+    for split, xg, wpw, tpg, pf in itertools.product((1, 2, 4, 8), (0, 1), (1, 2, 4), (1, 3), (1, 2)):
+        if split > nseg or (split > 1 and wpw != 4):
+            continue
+        combos.append(dict(QG_PERSIST=0, QG_SPLIT_K=split, QG_X_GLOBAL=xg, QG_WAVES_PER_WG=wpw,
+                           QG_TILES_PER_GROUP=tpg, QG_PREFETCH=pf))
+    try:
+        for combo in combos:
+            _set(**combo)
+            ctx = f"q4_k {N}x{K} " + " ".join(f"{k[3:].lower()}={v}" for k, v in combo.items())
+            announce(ctx)
+            y = empty_f32(N)
+            qg.qgemv_q4_k(packed, xd, y, N, K)
+            sync()
+            assert_linear(y.cpu().numpy(), y_ref, bound, ctx)
+    finally:
+        _set()
+
+
+def test_q4_k_run_to_run_bitwise_determinism():
+    for N, K in ((1024, 1024), (640, 17408)):
+        rng = np.random.default_rng(98)
+        canon = W.matrix("q4_k", N, K, rng)
+        x = to_dev(W.activation(K, rng))
+        packed = qg.pack_weights("q4_k", canon, N, K)
+        announce(f"determinism q4_k {N}x{K}")
+        outs = []
+        for _ in range(10):
+            y = empty_f32(N)
+            qg.qgemv_q4_k(packed, x, y, N, K)
+            outs.append(y)
+        sync()
+        ref = outs[0].cpu().numpy().tobytes()
+        assert all(o.cpu().numpy().tobytes() == ref for o in outs[1:])

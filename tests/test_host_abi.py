@@ -64,6 +64,14 @@ def test_packed_size(L):
     for bad in ((0, 32), (-1, 32), (8, 33), (8, 0)):
         assert qg.qg_packed_size("q8_0", *bad) == 0
     assert qg.qg_packed_size(7, 8, 32) == 0
+    # Q4_K: 148 bytes per 256 weights (16 B of nibbles + 2 B of sc/mn per 32, and
+    # 4 B of d/dmin per 256) when the planes need no padding; K % 256 == 0
+    for N, K in ((1024, 1024), (4096, 1024), (17408, 5120), (5120, 17408)):
+        assert qg.qg_packed_size("q4_k", N, K) == N * (K // 256) * 148
+    # 8 x 256: quant 1024, scale 128 -> 256, super 32 -> 256
+    assert qg.qg_packed_size("q4_k", 8, 256) == 1024 + 256 + 256
+    for bad in ((8, 32), (8, 1056), (8, 0)):
+        assert qg.qg_packed_size("q4_k", *bad) == 0
 
 
 FAKE = 0x10000  # a 64 KiB-aligned address that is never dereferenced
@@ -96,7 +104,15 @@ def test_argument_checks_return_codes_without_gpu(L):
     # unsupported qtype / row count
     assert call(L, "qgemv_verify", 1, f, f + (1 << 20), f + (2 << 20), 8, 32, 1, null) == qg.QG_EUNSUPPORTED
     assert call(L, "qgemv_verify", 1, f, f + (1 << 20), f + (2 << 20), 8, 32, 7, null) == qg.QG_EUNSUPPORTED
-    assert call(L, "qgemv_verify", 3, f, f + (1 << 20), f + (2 << 20), 8, 32, 2, null) == qg.QG_EUNSUPPORTED
+    assert call(L, "qgemv_verify", 4, f, f + (1 << 20), f + (2 << 20), 8, 32, 2, null) == qg.QG_EUNSUPPORTED
+    # Q4_K: the plain single-row GEMV only, K a multiple of 256
+    assert call(L, "qgemv_verify", qg.Q4_K, f, f + (1 << 20), f + (2 << 20), 8, 256, 2, null) == qg.QG_EUNSUPPORTED
+    assert call(L, "qgemv_fused_gateup_silu", qg.Q4_K, f, f + (1 << 20), f + (2 << 20), 8, 256,
+                null) == qg.QG_EUNSUPPORTED
+    assert call(L, "qgemv_q4_k", f, f + (1 << 20), f + (2 << 20), 8, 32, null) == qg.QG_EINVAL
+    assert call(L, "qgemv_q4_k", f, f + (1 << 20), f + (2 << 20), 8, 1056, null) == qg.QG_EINVAL
+    assert call(L, "qgemv_q4_k", f + 8, f + (1 << 20), f + (2 << 20), 8, 256, null) == qg.QG_EALIGN
+    assert call(L, "qgemv_q4_k", f, f + (1 << 20), f + (1 << 20), 8, 256, null) == qg.QG_EINVAL
     assert call(L, "qgemv_fused_gateup_silu", 5, f, f + (1 << 20), f + (2 << 20), 8, 32, null) == qg.QG_EUNSUPPORTED
     assert call(L, "qgemv_fused_gateup_silu", 1, f, f + (1 << 20), f + (2 << 20), 0, 32, null) == qg.QG_EINVAL
     # verify: the M x K activations must not overlap the M x N outputs
@@ -233,19 +249,63 @@ def test_tuning_overrides_are_read_on_reload(L, monkeypatch):
 
 
 SHAPES = [(1, 32), (3, 64), (8, 1024), (9, 1056), (17, 2048), (24, 3104), (5, 5120)]
+# Q4_K: K % 256 == 0; ragged last segments of 8, 16 and 24 blocks
+Q4_K_SHAPES = [(1, 256), (3, 512), (8, 1024), (9, 1280), (17, 2048), (24, 2304), (5, 5120), (2, 1792)]
 
 
-@pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
-@pytest.mark.parametrize("N,K", SHAPES)
+@pytest.mark.parametrize("kind,N,K", [(k, n, kk) for k in ("q8_0", "q4_0") for n, kk in SHAPES] +
+                         [("q4_k", n, kk) for n, kk in Q4_K_SHAPES])
 def test_pack_unpack_roundtrip(L, kind, N, K):
     canon = W.matrix(kind, N, K, np.random.default_rng(N * 7 + K))
     packed = qg.qg_pack_host(kind, canon, N, K)
     assert packed.size == qg.qg_packed_size(kind, N, K)
     back = qg.qg_unpack_host(kind, packed, N, K)
     assert np.array_equal(back, canon)
-    # the packed form holds the same number of non-padding bytes
-    bb = 34 if kind == "q8_0" else 18
-    assert packed.size >= canon.size and canon.size == N * (K // 32) * bb
+    # the packed form holds at least the canonical bytes
+    assert packed.size >= canon.size and canon.size == W.matrix_bytes(kind, N, K)
+
+
+def test_q4_k_pack_places_every_field(L):
+    # One row, K = 256: each field of the canonical super-block, set alone, lands
+    # where the kernel reads it: d and dmin in the super plane (row 0, slot 0),
+    # sub-block j's 6-bit scale and min as bytes 0 and 1 of its scale-plane entry,
+    # and its nibbles in the Q4_0 arrangement of quant-plane block j.
+    N, K = 1, 256
+    size = qg.qg_packed_size("q4_k", N, K)
+    q_bytes, s_off = 8 * 8 * 16, 1024
+    u_off = s_off + 256
+    for j in range(8):
+        for sc, mn in ((1, 0), (0, 1), (63, 0), (0, 63), (37, 50)):
+            canon = np.zeros(144, np.uint8)
+            canon[0:4] = [0x11, 0x22, 0x33, 0x44]
+            u = canon[4:16]
+            if j < 4:
+                u[j] |= sc
+                u[j + 4] |= mn
+            else:
+                u[j + 4] |= (sc & 15) | ((mn & 15) << 4)
+                u[j - 4] |= (sc >> 4) << 6
+                u[j] |= (mn >> 4) << 6
+            packed = qg.qg_pack_host("q4_k", canon, N, K)
+            assert packed.size == size
+            assert list(packed[u_off:u_off + 4]) == [0x11, 0x22, 0x33, 0x44]
+            # scale plane: (slot 0 * nb + j) * 4 rows * 2 B, row 0
+            assert packed[s_off + j * 8] == sc and packed[s_off + j * 8 + 1] == mn
+            assert not packed[:q_bytes].any()
+    # weight 64 g + l (l < 32) is the low nibble of byte 32 g + l: sub-block 2 g,
+    # element l; weight 64 g + 32 + l the high nibble: sub-block 2 g + 1
+    for w in (0, 5, 31, 32, 63, 64, 100, 255):
+        canon = np.zeros(144, np.uint8)
+        g, l = w // 64, w % 64
+        canon[16 + 32 * g + (l % 32)] = 0x0F if l < 32 else 0xF0
+        packed = qg.qg_pack_host("q4_k", canon, N, K)
+        j, e = 2 * g + (l >= 32), l % 32
+        # row 0 is slot 0, b 0 of the only tile: block j's 16 B sit at j * 16
+        blk = packed[j * 16: j * 16 + 16]
+        dw = int.from_bytes(bytes(blk[4 * (e // 8): 4 * (e // 8) + 4]), "little")
+        pos = (e % 8) // 2 + 4 * ((e % 8) % 2)
+        assert (dw >> (4 * pos)) & 0xF == 0xF
+        assert int(np.unpackbits(packed[:q_bytes]).sum()) == 4
 
 
 @pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
