@@ -11,8 +11,10 @@ Canonical formats (GGUF-style, little-endian):
                     weight = d * (nibble - 8).
   Q4_K super-block, 144 B per 256 weights: fp16 d, fp16 dmin, 12 bytes of
                     6-bit sub-block scales and mins, 128 bytes of nibbles.
+  Q6_K super-block, 210 B per 256 weights: 128 bytes of low 4-bit parts, 64
+                    bytes of high 2-bit parts, 16 int8 scales, fp16 d last.
   F16 matrix: row-major [N][K] IEEE binary16.
-A row of a quantised matrix is K/32 consecutive blocks (K/256 for Q4_K).
+A row of a quantised matrix is K/32 consecutive blocks (K/256 for Q4_K, Q6_K).
 
 Value laws (the decode workloads the pages measure on are trained checkpoints;
 these seeded draws stand in for them, with the same shapes):
@@ -22,6 +24,9 @@ these seeded draws stand in for them, with the same shapes):
   Q4_K: d = fp16(|N(0, 0.02)| / 480), dmin = fp16(|N(0, 0.02)| / 64); the 12
         scale/min bytes and the 128 quant bytes uniform (so every 6-bit scale
         and min and every nibble is uniform).
+  Q6_K: the 192 quant bytes uniform (every 6-bit quant uniform in 0..63), the
+        16 scales uniform int8 in [-128, 127], d = fp16(|N(0, 0.02)| / 512)
+        (about half of the d are fp16 subnormals).
   F16 : w = fp16(N(0, 0.02)).
   x   : fp32(N(0, 1)) drawn in float64 and rounded to nearest.
 fp16 rounding is numpy's float64 -> float16 cast (round to nearest even).
@@ -33,6 +38,7 @@ import numpy as np
 Q8_0_BLOCK_BYTES = 34
 Q4_0_BLOCK_BYTES = 18
 Q4_K_BLOCK_BYTES = 144
+Q6_K_BLOCK_BYTES = 210
 
 
 def _rng(seed):
@@ -90,6 +96,19 @@ def q4_k_matrix(N: int, K: int, seed, scale_sigma: float = 0.02) -> np.ndarray:
     return out.reshape(-1)
 
 
+def q6_k_matrix(N: int, K: int, seed, scale_sigma: float = 0.02) -> np.ndarray:
+    """Random Q6_K weight matrix as canonical bytes, shape (N * K/256 * 210,) uint8."""
+    if K % 256:
+        raise ValueError("Q6_K needs K % 256 == 0")
+    rng = _rng(seed)
+    nb = N * (K // 256)
+    d = fp16_bits(np.abs(rng.normal(0.0, scale_sigma, nb)) / 512.0)
+    out = np.empty((nb, Q6_K_BLOCK_BYTES), np.uint8)
+    out[:, 0:208] = rng.integers(0, 256, size=(nb, 208), dtype=np.uint8)
+    out[:, 208:210] = d.astype("<u2").view(np.uint8).reshape(nb, 2)
+    return out.reshape(-1)
+
+
 def f16_matrix(N: int, K: int, seed, sigma: float = 0.02) -> np.ndarray:
     """Random fp16 row-major matrix as uint16 bit patterns, shape (N*K,)."""
     rng = _rng(seed)
@@ -110,6 +129,8 @@ def matrix(kind: str, N: int, K: int, seed) -> np.ndarray:
         return q4_0_matrix(N, K, seed)
     if kind == "q4_k":
         return q4_k_matrix(N, K, seed)
+    if kind == "q6_k":
+        return q6_k_matrix(N, K, seed)
     if kind == "f16":
         return f16_matrix(N, K, seed)
     raise ValueError(kind)
@@ -123,6 +144,8 @@ def matrix_bytes(kind: str, N: int, K: int) -> int:
         return N * (K // 32) * Q4_0_BLOCK_BYTES
     if kind == "q4_k":
         return N * (K // 256) * Q4_K_BLOCK_BYTES
+    if kind == "q6_k":
+        return N * (K // 256) * Q6_K_BLOCK_BYTES
     return N * K * 2
 
 

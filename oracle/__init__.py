@@ -23,8 +23,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-Q8_0, Q4_0, F16, Q4_K = 1, 2, 3, 4
-KINDS = {"q8_0": Q8_0, "q4_0": Q4_0, "f16": F16, "q4_k": Q4_K}
+Q8_0, Q4_0, F16, Q4_K, Q6_K = 1, 2, 3, 4, 5
+KINDS = {"q8_0": Q8_0, "q4_0": Q4_0, "f16": F16, "q4_k": Q4_K, "q6_k": Q6_K}
 
 
 def build(force: bool = False) -> str:
@@ -93,6 +93,8 @@ def _check_w(kind: int, w: np.ndarray, N: int, K: int):
         need = N * (K // 32) * 18
     elif kind == Q4_K:
         need = N * (K // 256) * 144
+    elif kind == Q6_K:
+        need = N * (K // 256) * 210
     else:
         need = N * K * 2
     if w.nbytes != need:

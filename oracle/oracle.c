@@ -36,6 +36,10 @@
  *    quantisation table (Q4_K_M), EdgeRunner "Run it yourself" (loads Q4_K_M):
  *    the Q4_K super-block, whose layout the pages do not give; it is read as
  *    the published GGUF k-quant block (q4_k_weight below).
+ *  - RunIT_Mac README, quantisation table (Q6_K supported) and the data-flow
+ *    note on Q8_0/Q5K/Q6K weights, EdgeRunner "Run it yourself" (loads Q6_K):
+ *    the Q6_K super-block, likewise not described on the pages and read as the
+ *    published GGUF block (q6_k_weight below).
  *  - RunIT_Mac README, kernel table and data-flow figure: RMSNorm with f32
  *    input, output and gamma precedes the projections; "EdgeRunner beats
  *    llama.cpp", The progression, fused it into the GEMV (RMSNorm+GEMV).
@@ -61,7 +65,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_Q8_0 = 1, ORACLE_Q4_0 = 2, ORACLE_F16 = 3, ORACLE_Q4_K = 4 };
+enum { ORACLE_Q8_0 = 1, ORACLE_Q4_0 = 2, ORACLE_F16 = 3, ORACLE_Q4_K = 4, ORACLE_Q6_K = 5 };
 
 /* IEEE 754 binary16 -> double, exact. */
 double oracle_half_to_double(uint16_t h)
@@ -134,25 +138,50 @@ static double q4_k_weight(const uint8_t *blk, int i)
     return d * (double)sc * (double)q - dmin * (double)mn;
 }
 
+/* Q6_K super-block (256 weights, 210 bytes; the GGUF k-quant block the pages
+ * name as Q6_K without describing it, read here as published for GGUF): 128
+ * bytes ql of low 4-bit parts, 64 bytes qh of high 2-bit parts, sixteen int8
+ * scales sc[0..15] (one per 16 weights), then the fp16 d. Weight i lies in
+ * half h = i / 128; with r = i % 128, group g = r / 32 and l = r % 32 its low 4
+ * bits are the low (g < 2) or high (g >= 2) nibble of ql[64h + 32(g % 2) + l]
+ * and its high 2 bits are bits 2g, 2g + 1 of qh[32h + l]:
+ *   q = low | high << 4 (0..63),   w = d * sc[i / 16] * (q - 32)
+ * d * sc * (q - 32) has <= 25 significant bits: exact in double. */
+static double q6_k_weight(const uint8_t *blk, int i)
+{
+    const uint8_t *ql = blk, *qh = blk + 128;
+    const int8_t *sc = (const int8_t *)(blk + 192);
+    double d = oracle_half_to_double(read_le16(blk + 208));
+    int h = i / 128, r = i % 128, g = r / 32, l = r % 32;
+    int lo = ql[64 * h + 32 * (g % 2) + l];
+    lo = (g < 2) ? (lo & 15) : (lo >> 4);
+    int hi = (qh[32 * h + l] >> (2 * g)) & 3;
+    int q = lo | (hi << 4);
+    return d * (double)sc[i / 16] * (double)(q - 32);
+}
+
+/* W[n][k] of an N x K matrix of `kind` from its canonical bytes w (rows of
+ * K/32 blocks, K/256 super-blocks or K fp16 values). */
+static double weight_at(int kind, const uint8_t *w, int64_t n, int64_t k, int64_t K)
+{
+    if (kind == ORACLE_Q8_0)
+        return q8_0_weight(w + (n * (K / 32) + k / 32) * 34, (int)(k % 32));
+    if (kind == ORACLE_Q4_0)
+        return q4_0_weight(w + (n * (K / 32) + k / 32) * 18, (int)(k % 32));
+    if (kind == ORACLE_Q4_K)
+        return q4_k_weight(w + (n * (K / 256) + k / 256) * 144, (int)(k % 256));
+    if (kind == ORACLE_Q6_K)
+        return q6_k_weight(w + (n * (K / 256) + k / 256) * 210, (int)(k % 256));
+    return oracle_half_to_double(read_le16(w + (n * K + k) * 2));
+}
+
 /* One output row: y = sum W[n][k] x[k], a = sum |W[n][k] x[k]|. */
 static void one_row(int kind, const uint8_t *w, const float *x, int64_t n, int64_t K,
                     double *y, double *a)
 {
     double sum = 0.0, asum = 0.0;
     for (int64_t k = 0; k < K; ++k) {
-        double wk;
-        if (kind == ORACLE_Q8_0) {
-            const uint8_t *blk = w + (n * (K / 32) + k / 32) * 34;
-            wk = q8_0_weight(blk, (int)(k % 32));
-        } else if (kind == ORACLE_Q4_0) {
-            const uint8_t *blk = w + (n * (K / 32) + k / 32) * 18;
-            wk = q4_0_weight(blk, (int)(k % 32));
-        } else if (kind == ORACLE_Q4_K) {
-            const uint8_t *blk = w + (n * (K / 256) + k / 256) * 144;
-            wk = q4_k_weight(blk, (int)(k % 256));
-        } else {
-            wk = oracle_half_to_double(read_le16(w + (n * K + k) * 2));
-        }
+        double wk = weight_at(kind, w, n, k, K);
         double p = wk * (double)x[k];
         sum += p;
         asum += fabs(p);
@@ -164,9 +193,11 @@ static void one_row(int kind, const uint8_t *w, const float *x, int64_t n, int64
 static int bad_args(int kind, int64_t N, int64_t K)
 {
     if (N < 0 || K < 0) return 1;
-    if (kind != ORACLE_Q8_0 && kind != ORACLE_Q4_0 && kind != ORACLE_F16 && kind != ORACLE_Q4_K) return 1;
+    if (kind != ORACLE_Q8_0 && kind != ORACLE_Q4_0 && kind != ORACLE_F16 && kind != ORACLE_Q4_K &&
+        kind != ORACLE_Q6_K)
+        return 1;
     if (kind != ORACLE_F16 && K % 32 != 0) return 1;
-    if (kind == ORACLE_Q4_K && K % 256 != 0) return 1;
+    if ((kind == ORACLE_Q4_K || kind == ORACLE_Q6_K) && K % 256 != 0) return 1;
     return 0;
 }
 
@@ -334,15 +365,7 @@ int oracle_gemv_rmsnorm(int kind, const void *w, const float *x, const float *ga
     for (int64_t n = 0; !rc && n < N; ++n) {
         double sum = 0.0, asum = 0.0;
         for (int64_t k = 0; k < K; ++k) {
-            double wk;
-            if (kind == ORACLE_Q8_0)
-                wk = q8_0_weight(wb + (n * (K / 32) + k / 32) * 34, (int)(k % 32));
-            else if (kind == ORACLE_Q4_0)
-                wk = q4_0_weight(wb + (n * (K / 32) + k / 32) * 18, (int)(k % 32));
-            else if (kind == ORACLE_Q4_K)
-                wk = q4_k_weight(wb + (n * (K / 256) + k / 256) * 144, (int)(k % 256));
-            else
-                wk = oracle_half_to_double(read_le16(wb + (n * K + k) * 2));
+            double wk = weight_at(kind, wb, n, k, K);
             double p = wk * xn[k];
             sum += p;
             asum += fabs(p);

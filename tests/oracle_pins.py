@@ -10,7 +10,9 @@ AssertionError when the oracle disagrees with:
   * invariants (exact scaling, zero blocks, row permutation),
   * the composition rules of the fused and multi-row entry points,
   * closed forms of RMSNorm (a vector of ones with eps = 3; alternating +-c),
-  * hand-worked Q4_K super-blocks (tests/golden/q4_k_blocks.json) and closed forms.
+  * hand-worked Q4_K super-blocks (tests/golden/q4_k_blocks.json) and closed forms;
+  * hand-worked Q6_K super-blocks (tests/golden/q6_k_blocks.json), closed forms and
+    the integer-matrix special case.
 ``test_oracle_mutants.py`` plants plausible mistakes in a copy of oracle.c and
 checks that every one of them trips at least one pin.
 """
@@ -420,6 +422,80 @@ def pin_q4_k(L):
     assert L.oracle_gemv(O.Q4_K, p(ww), p(xx), p(yy), p(aa), 1, 288, 1) != 0
 
 
+def _q6_k_case(case) -> tuple[np.ndarray, np.ndarray]:
+    """Build one golden Q6_K super-block and its activation from a case record."""
+    blk = bytearray(210)
+    for off, n, field in ((0, 128, case["ql"]), (128, 64, case["qh"])):
+        blk[off:off + n] = bytes([field["fill"]] * n)
+        for i, v in field["set"].items():
+            blk[off + int(i)] = v
+    blk[192:208] = np.array(case["scales"], np.int8).tobytes()
+    blk[208:210] = int(case["d_bits"]).to_bytes(2, "little")
+    x = {"ones": np.ones(256), "index": np.arange(256.0)}[case["x"]]
+    return np.frombuffer(bytes(blk), np.uint8).copy(), x.astype(np.float32)
+
+
+def q6_k_block_from_values(d_bits: int, scales, v) -> bytes:
+    """Encode 256 values v in [-32, 31] as one Q6_K super-block (the inverse of
+    the decode: q = v + 32 split into a low nibble and a high 2-bit part)."""
+    ql, qh = bytearray(128), bytearray(64)
+    for i in range(256):
+        q = int(v[i]) + 32
+        h, r = divmod(i, 128)
+        g, l = divmod(r, 32)
+        ql[64 * h + 32 * (g % 2) + l] |= (q & 15) << (4 * (g // 2))
+        qh[32 * h + l] |= (q >> 4) << (2 * g)
+    return bytes(ql) + bytes(qh) + np.array(scales, np.int8).tobytes() + int(d_bits).to_bytes(2, "little")
+
+
+def pin_q6_k(L):
+    # hand-worked single super-blocks (tests/golden/q6_k_blocks.json): the -32
+    # offset, the nibble and 2-bit fields of each 32-weight group in both halves,
+    # signed per-16 scales, scale -128 and a subnormal d stored last
+    for case in _golden("q6_k_blocks.json")["cases"]:
+        blk, x = _q6_k_case(case)
+        y, _ = _gemv(L, "q6_k", blk, x, 1, 256)
+        assert y[0] == case["expect"], (case["name"], y[0], case["expect"])
+    # closed form: every quant c, random scales, two super-blocks with different
+    # d: y = sum_b d_b (c - 32) sum_j sc_bj sum_{k in sub-block j} x_k
+    rng = np.random.default_rng(23)
+    for c in (0, 17, 32, 63):
+        x = rng.integers(-4, 5, size=512).astype(np.float32)
+        blocks, expect = [], 0.0
+        for b, db in enumerate((0x3800, 0x2C00)):    # 0.5, 1/16
+            sc = rng.integers(-128, 128, size=16)
+            blocks.append(q6_k_block_from_values(db, sc, [c - 32] * 256))
+            dv = float(np.array([db], np.uint16).view(np.float16)[0])
+            xs = x[256 * b:256 * (b + 1)].astype(np.float64).reshape(16, 16).sum(axis=1)
+            expect += dv * (c - 32) * float(np.dot(sc.astype(np.float64), xs))
+        y, _ = _gemv(L, "q6_k", np.frombuffer(b"".join(blocks), np.uint8).copy(), x, 1, 512)
+        assert y[0] == expect, (c, y[0], expect)
+    # textbook case: d = 1 and every scale 1 make W the integer matrix v in [-32, 31]
+    N, K = 8, 512
+    v = rng.integers(-32, 32, size=(N * K // 256, 256))
+    w = np.frombuffer(b"".join(q6_k_block_from_values(0x3C00, [1] * 16, row) for row in v), np.uint8).copy()
+    x = rng.standard_normal(K).astype(np.float32)
+    y, _ = _gemv(L, "q6_k", w, x, N, K)
+    Wm = v.astype(np.float64).reshape(N, K)
+    x64 = x.astype(np.float64)
+    assert np.all(np.abs(y - Wm @ x64) <= 1e-12 * (np.abs(Wm) @ np.abs(x64)))
+    # invariants on random matrices: exact power-of-two scaling of x, row permutation
+    N, K = 5, 512
+    w = W.matrix("q6_k", N, K, rng)
+    x = rng.standard_normal(K).astype(np.float32)
+    y, _ = _gemv(L, "q6_k", w, x, N, K)
+    y2, _ = _gemv(L, "q6_k", w, x * np.float32(4), N, K)
+    assert np.array_equal(y2, 4 * y)
+    perm = np.array([3, 0, 4, 1, 2])
+    wp = w.reshape(N, -1)[perm].reshape(-1).copy()
+    yp, _ = _gemv(L, "q6_k", wp, x, N, K)
+    assert np.array_equal(yp, y[perm])
+    # Q6_K rows must be whole super-blocks
+    p = lambda arr: arr.ctypes.data_as(__import__("ctypes").c_void_p)  # noqa: E731
+    ww, xx, yy, aa = np.zeros(210, np.uint8), np.zeros(288, np.float32), np.zeros(1), np.zeros(1)
+    assert L.oracle_gemv(O.Q6_K, p(ww), p(xx), p(yy), p(aa), 1, 288, 1) != 0
+
+
 def pin_rejects_bad_shapes(L):
     w = np.zeros(34, np.uint8)
     x = np.zeros(33, np.float32)
@@ -443,6 +519,7 @@ PINS = [
     pin_epilogue,
     pin_rmsnorm,
     pin_q4_k,
+    pin_q6_k,
     pin_rejects_bad_shapes,
 ]
 

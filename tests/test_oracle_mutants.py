@@ -58,6 +58,18 @@ MUTANTS = {
     "q4k_dmin_read_as_d": ("double dmin = oracle_half_to_double(read_le16(blk + 2));",
                            "double dmin = oracle_half_to_double(read_le16(blk));"),
     "q4k_superblock_stride": ("w + (n * (K / 256) + k / 256) * 144", "w + (n * (K / 256) + k / 256) * 128"),
+    "q6k_nibble_halves_swapped": ("lo = (g < 2) ? (lo & 15) : (lo >> 4);", "lo = (g < 2) ? (lo >> 4) : (lo & 15);"),
+    "q6k_ql_group_offset": ("ql[64 * h + 32 * (g % 2) + l]", "ql[64 * h + 32 * (g / 2) + l]"),
+    "q6k_ql_half_stride": ("ql[64 * h + 32 * (g % 2) + l]", "ql[32 * h + 32 * (g % 2) + l]"),
+    "q6k_qh_half_stride": ("qh[32 * h + l]", "qh[16 * h + l]"),
+    "q6k_qh_bit_order": ("(qh[32 * h + l] >> (2 * g)) & 3", "(qh[32 * h + l] >> (6 - 2 * g)) & 3"),
+    "q6k_fields_swapped": ("int q = lo | (hi << 4);", "int q = (lo << 2) | hi;"),
+    "q6k_scale_per_32": ("(double)sc[i / 16]", "(double)sc[i / 32]"),
+    "q6k_scale_unsigned": ("(double)sc[i / 16]", "(double)(uint8_t)sc[i / 16]"),
+    "q6k_offset_31": ("(double)(q - 32)", "(double)(q - 31)"),
+    "q6k_no_offset": ("(double)(q - 32)", "(double)(q)"),
+    "q6k_d_first": ("read_le16(blk + 208)", "read_le16(blk)"),
+    "q6k_superblock_stride": ("w + (n * (K / 256) + k / 256) * 210", "w + (n * (K / 256) + k / 256) * 208"),
 }
 
 
