@@ -292,17 +292,19 @@ def per_config_calls(qg, torch, stream, step_calls):
         make_epilogue(qg, "q8_0", lm.weight, t(wl1.x("lm_head")), None, None, y16, 151936, 1024, stream,
                       "e q8_0 lm_head 151936x1024 fp16 out"),
     ]
-    # the Q4_K GEMV (qgemv_q4_k) on the shapes of the Q4_0 configuration: 148 packed
-    # bytes (144 canonical) per 256 weights instead of 144 per 256
+    # the super-block GEMVs (qgemv_q4_k, qgemv_q6_k) on the shapes of the Q4_0
+    # configuration: 144 and 210 canonical bytes per 256 weights
     krng = np.random.default_rng(6)
     res[6] = []
-    for label, N, K in (("down 5120x17408", 5120, 17408), ("gate 17408x5120", 17408, 5120),
-                        ("lm_head 248320x5120", 248320, 5120)):
-        canon = W.matrix("q4_k", N, K, krng)
-        pk = qg.pack_weights("q4_k", canon, N, K)
-        del canon
-        keep.append(pk)
-        res[6].append(make_qgemv(qg, "q4_k", pk, t(W.activation(K, krng)), yb(N), N, K, stream, f"k q4_k {label}"))
+    for kind in ("q4_k", "q6_k"):
+        for label, N, K in (("down 5120x17408", 5120, 17408), ("gate 17408x5120", 17408, 5120),
+                            ("lm_head 248320x5120", 248320, 5120)):
+            canon = W.matrix(kind, N, K, krng)
+            pk = qg.pack_weights(kind, canon, N, K)
+            del canon
+            keep.append(pk)
+            res[6].append(make_qgemv(qg, kind, pk, t(W.activation(K, krng)), yb(N), N, K, stream,
+                                     f"k {kind} {label}"))
     # the RMSNorm-prologue experiment: each case is (label, weight, bytes, fused(wp), norm(), gemv(wp)), the
     # unfused form being qg_rmsnorm into a separate buffer followed by the plain GEMV on it
     eps = 1e-6

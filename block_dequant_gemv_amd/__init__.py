@@ -18,7 +18,8 @@ import numpy as np
 Q8_0 = 1
 Q4_0 = 2
 Q4_K = 3
-QTYPES = {"q8_0": Q8_0, "q4_0": Q4_0, "q4_k": Q4_K}
+Q6_K = 4
+QTYPES = {"q8_0": Q8_0, "q4_0": Q4_0, "q4_k": Q4_K, "q6_k": Q6_K}
 
 QG_OK, QG_EINVAL, QG_EALIGN, QG_EUNSUPPORTED, QG_EHIP = range(5)
 QG_OUT_F32, QG_OUT_F16 = 0, 1
@@ -29,7 +30,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemv.so
 SYMBOLS = (
     "qg_packed_size", "qg_pack", "qg_pack_rows", "qg_pack_gateup",
     "qg_pack_host", "qg_unpack_host", "qg_pack_gateup_host",
-    "qgemv_q8_0", "qgemv_q4_0", "qgemv_q4_k", "qgemv_epilogue", "gemv_f16_splitk", "qgemv_fused_gateup_silu", "qgemv_verify",
+    "qgemv_q8_0", "qgemv_q4_0", "qgemv_q4_k", "qgemv_q6_k", "qgemv_epilogue", "gemv_f16_splitk", "qgemv_fused_gateup_silu", "qgemv_verify",
     "qg_rmsnorm", "qgemv_rmsnorm", "qgemv_rmsnorm_gateup_silu", "qg_prefill_workspace_size", "qgemm_prefill",
     "qg_status_str", "qg_last_error", "qg_plan_info", "qg_time_next_launch", "qg_reload_tuning",
 )
@@ -71,6 +72,7 @@ def lib():
             "qgemv_q8_0": ([vp, vp, vp, i64, i64, vp], i32),
             "qgemv_q4_0": ([vp, vp, vp, i64, i64, vp], i32),
             "qgemv_q4_k": ([vp, vp, vp, i64, i64, vp], i32),
+            "qgemv_q6_k": ([vp, vp, vp, i64, i64, vp], i32),
             "qgemv_epilogue": ([i32, vp, vp, vp, vp, vp, i32, i64, i64, vp], i32),
             "qg_rmsnorm": ([vp, vp, ctypes.c_float, vp, i64, vp], i32),
             "qg_prefill_workspace_size": ([i32, i64, i64, i64], sz),
@@ -168,7 +170,7 @@ def qg_pack_host(qtype, canonical: np.ndarray, N: int, K: int) -> np.ndarray:
 
 def qg_unpack_host(qtype, packed: np.ndarray, N: int, K: int) -> np.ndarray:
     q = _qtype(qtype)
-    row = (K // 32) * 34 if q == Q8_0 else ((K // 32) * 18 if q == Q4_0 else (K // 256) * 144)
+    row = {Q8_0: (K // 32) * 34, Q4_0: (K // 32) * 18, Q4_K: (K // 256) * 144, Q6_K: (K // 256) * 210}[q]
     out = np.empty(N * row, np.uint8)
     _check("qg_unpack_host", lib().qg_unpack_host(_qtype(qtype), _host(packed, "packed"), _host(out, "canonical"),
                                                   N, K))
@@ -196,6 +198,11 @@ def qgemv_q4_0(w_packed, x, y, N: int, K: int, stream=None):
 
 def qgemv_q4_k(w_packed, x, y, N: int, K: int, stream=None):
     _check("qgemv_q4_k", lib().qgemv_q4_k(_dev(w_packed, "w_packed"), _dev(x, "x", _f32()), _dev(y, "y", _f32()),
+                                          N, K, _stream(stream)))
+
+
+def qgemv_q6_k(w_packed, x, y, N: int, K: int, stream=None):
+    _check("qgemv_q6_k", lib().qgemv_q6_k(_dev(w_packed, "w_packed"), _dev(x, "x", _f32()), _dev(y, "y", _f32()),
                                           N, K, _stream(stream)))
 
 
@@ -262,8 +269,9 @@ def qgemv_verify(qtype, w_packed, X, Y, N: int, K: int, M: int, stream=None):
 
 
 def qgemv(qtype, w_packed, x, y, N: int, K: int, stream=None):
-    """qgemv_q8_0, qgemv_q4_0 or qgemv_q4_k by qtype."""
-    {Q8_0: qgemv_q8_0, Q4_0: qgemv_q4_0, Q4_K: qgemv_q4_k}[_qtype(qtype)](w_packed, x, y, N, K, stream)
+    """qgemv_q8_0, qgemv_q4_0, qgemv_q4_k or qgemv_q6_k by qtype."""
+    {Q8_0: qgemv_q8_0, Q4_0: qgemv_q4_0, Q4_K: qgemv_q4_k, Q6_K: qgemv_q6_k}[_qtype(qtype)](w_packed, x, y, N, K,
+                                                                                         stream)
 
 
 # ---- diagnostics -----------------------------------------------------------

@@ -73,6 +73,25 @@ __device__ __forceinline__ void q4k_pairs(uint32_t w, const Consts &k, h2 (&p)[4
     p[3] = as_h2(w8 & k.m_hi);
 }
 
+// Q6_K: the low-nibble dword w (Q4_0 arrangement) and the row's dword h of high
+// 2-bit parts for these 8 elements -> 4 fp16 pairs of q - 32, exact. For the
+// second dword of a 16-element span (odd) the high parts sit 24 bits further
+// round; after the rotation both cases read pairs 0/1 from bits 4-5 / 8-9 of
+// the fp16 halves and pairs 2/3 from the same bits 2 higher.
+__device__ __forceinline__ void q6k_pairs(uint32_t w, uint32_t h, bool odd, const Consts &k, h2 (&p)[4])
+{
+    const h2 off = {(_Float16)-1056.0f, (_Float16)-1056.0f};
+    const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h2 off16 = {(_Float16)-96.0f, (_Float16)-96.0f};
+    const uint32_t a = odd ? __builtin_amdgcn_alignbit(h, h, 24) : h;
+    const uint32_t b2 = a >> 2;
+    const uint32_t w8 = w >> 8;
+    p[0] = as_h2(and_or(a, 0x00300030u, and_or(w, k.m_lo, k.magic))) + off;
+    p[1] = __builtin_elementwise_fma(as_h2(and_or(a, 0x03000300u, and_or(w, k.m_hi, k.magic))), sixteenth, off16);
+    p[2] = as_h2(and_or(b2, 0x00300030u, and_or(w8, k.m_lo, k.magic))) + off;
+    p[3] = __builtin_elementwise_fma(as_h2(and_or(b2, 0x03000300u, and_or(w8, k.m_hi, k.magic))), sixteenth, off16);
+}
+
 // Q8_0 dword (bytes q XOR 0x80) -> the 4 int8 weights as 2 fp16 pairs, elements (0,1) (2,3).
 // v_perm_b32 builds [byte, 0x64, byte, 0x64] = fp16 (1024 + q + 128) twice.
 __device__ __forceinline__ void q8_pairs(uint32_t w, h2 (&p)[2])

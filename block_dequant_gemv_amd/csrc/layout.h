@@ -39,6 +39,19 @@
 //   super plane: [tile][segment][slot][super-block of the segment][b] x (d, dmin) fp16
 // so a lane's 16-byte load gets d and dmin of its 4 rows. 148 bytes per
 // 256 weights (144 canonical).
+//
+// Q6_K (256-weight super-blocks; canonical block: 128 bytes of low 4-bit
+// parts, 64 bytes of high 2-bit parts, 16 int8 scales (one per 16 weights),
+// fp16 d; weight = d * sc * (q - 32)) is packed per 32-weight block: the low
+// nibbles in the Q4_0 arrangement as units b = 0..3 of the quant plane, the
+// high 2-bit parts as two more units (row pairs 0-1 and 2-3, 8 bytes a row),
+// the block's two int8 scales where Q4_0 keeps its fp16 scale, and d in the
+// super plane (2 bytes a row). A row's 8 bytes of high parts are two dwords,
+// each covering 16 elements: element e of the first 8 sits at bit pair
+// q6_hi_pos(e), the second 8 at that position rotated by 24, so that a shift
+// by 0 or 2 (first 8) or a rotation by 24 and a further shift by 2 (second 8)
+// lines each pair of elements up under bits 4-5 / 8-9 of the fp16 halves the
+// low nibbles occupy. 210 bytes per 256 weights, as canonical.
 #pragma once
 
 #include <stdint.h>
@@ -54,7 +67,8 @@ namespace qgl {
 constexpr int kQ8_0 = 1;
 constexpr int kQ4_0 = 2;
 constexpr int kQ4_K = 3;
-constexpr int kSuperBlocks = 8;   // Q4_K: 32-weight sub-blocks per super-block
+constexpr int kQ6_K = 4;
+constexpr int kSuperBlocks = 8;   // Q4_K, Q6_K: 32-weight blocks per super-block
 
 constexpr int kSlots = 2;         // rows processed side by side per wavefront
 constexpr int kLanesPerSlot = 32; // lanes sharing one row = blocks per segment
@@ -64,12 +78,17 @@ constexpr int kTileRows = kSlots * kRowsPerLane;
 constexpr int kUnit = 16;         // bytes per lane per load
 constexpr int kSegWeights = kSegBlocks * 32;
 
-// Canonical bytes of one row of K weights (K % 32 == 0; K % 256 == 0 for Q4_K).
+// Canonical bytes of one row of K weights (K % 32 == 0; K % 256 == 0 for Q4_K, Q6_K).
 QG_HD int64_t canon_row_bytes(int qt, int64_t K)
 {
-    return qt == kQ8_0 ? (K / 32) * 34 : (qt == kQ4_0 ? (K / 32) * 18 : (K / 256) * 144);
+    if (qt == kQ8_0) return (K / 32) * 34;
+    if (qt == kQ4_0) return (K / 32) * 18;
+    return (K / 256) * (qt == kQ4_K ? 144 : 210);
 }
-QG_HD int packed_quant_bytes(int qt) { return qt == kQ8_0 ? 32 : 16; }
+// Quant-plane bytes per row and 32-weight block (Q6_K: 16 of low nibbles + 8 of high parts).
+QG_HD constexpr int packed_quant_bytes(int qt) { return qt == kQ8_0 ? 32 : (qt == kQ6_K ? 24 : 16); }
+// Super-plane bytes per row and super-block (Q4_K: d, dmin; Q6_K: d).
+QG_HD int super_row_bytes(int qt) { return qt == kQ4_K ? 4 : (qt == kQ6_K ? 2 : 0); }
 QG_HD int halves(int qt) { return qt == kQ8_0 ? 2 : 1; }
 
 struct Geometry {
@@ -82,8 +101,8 @@ struct Geometry {
     int64_t tile_q;   // quant bytes per tile
     int64_t tile_s;   // scale bytes per tile
     int64_t scale_off;
-    int64_t tile_u;   // Q4_K super-scale bytes per tile (0 otherwise)
-    int64_t sup_off;  // Q4_K super-scale plane
+    int64_t tile_u;   // Q4_K / Q6_K super-scale bytes per tile (0 otherwise)
+    int64_t sup_off;  // Q4_K / Q6_K super-scale plane
     int64_t total;
 };
 
@@ -101,7 +120,7 @@ QG_HD Geometry geometry(int qt, int64_t N, int64_t K)
     g.tile_q = (int64_t)kTileRows * g.KB * packed_quant_bytes(qt);
     g.tile_s = (int64_t)kTileRows * g.KB * 2;
     g.scale_off = round_up(g.n_tiles * g.tile_q, 256);
-    g.tile_u = qt == kQ4_K ? (int64_t)kTileRows * (g.KB / kSuperBlocks) * 4 : 0;
+    g.tile_u = (int64_t)kTileRows * (g.KB / kSuperBlocks) * super_row_bytes(qt);
     g.sup_off = g.scale_off + round_up(g.n_tiles * g.tile_s, 256);
     g.total = g.sup_off + round_up(g.n_tiles * g.tile_u, 256);
     return g;
@@ -113,12 +132,35 @@ QG_HD int64_t seg_blocks(const Geometry &g, int64_t seg)
     return r < kSegBlocks ? r : kSegBlocks;
 }
 
-// Byte offset of 16-byte unit (b, h) of block j of row slot `slot` in segment seg of tile t.
-QG_HD int64_t quant_offset(const Geometry &g, int64_t t, int64_t seg, int b, int h, int slot, int j)
+// Byte offset of 16-byte unit u of block j of row slot `slot` in segment seg of tile t.
+QG_HD int64_t unit_offset(const Geometry &g, int64_t t, int64_t seg, int u, int slot, int j)
 {
     int64_t nb = seg_blocks(g, seg);
     return t * g.tile_q + seg * (int64_t)kTileRows * kSegBlocks * packed_quant_bytes(g.qt) +
-           (((int64_t)(b * halves(g.qt) + h) * kSlots + slot) * nb + j) * kUnit;
+           (((int64_t)u * kSlots + slot) * nb + j) * kUnit;
+}
+
+// Unit (b, h): row b's quants (half h of a Q8_0 block).
+QG_HD int64_t quant_offset(const Geometry &g, int64_t t, int64_t seg, int b, int h, int slot, int j)
+{
+    return unit_offset(g, t, seg, b * halves(g.qt) + h, slot, j);
+}
+
+// Q6_K: the unit of high 2-bit parts of rows 2bp, 2bp+1 (8 bytes each).
+QG_HD int64_t q6_hi_offset(const Geometry &g, int64_t t, int64_t seg, int bp, int slot, int j)
+{
+    return unit_offset(g, t, seg, kRowsPerLane + bp, slot, j);
+}
+
+// Q6_K: bit position of element e (0..15) of a 16-element span in its dword of
+// high parts. Elements 0..7 pair up as (0,1) (2,3) (4,5) (6,7) with the fp16
+// halves of the low-nibble pairs: 4 / 20, 8 / 24, then the same two +2; the
+// second 8 sit 24 bits further round.
+QG_HD int q6_hi_pos(int e)
+{
+    const int f = e % 8;
+    const int p = (f % 2) * 16 + 4 + 4 * ((f / 2) % 2) + 2 * (f / 4);
+    return (p + 24 * (e / 8)) % 32;
 }
 
 // Byte offset of the 4 scales (rows b = 0..3) of block j, slot `slot`, segment seg, tile t.
@@ -129,12 +171,14 @@ QG_HD int64_t scale_offset(const Geometry &g, int64_t t, int64_t seg, int slot, 
            ((int64_t)slot * nb + j) * kRowsPerLane * 2;
 }
 
-// Q4_K: byte offset of d, dmin of rows b = 0..3 (slot `slot`) for super-block sb of segment seg, tile t.
+// Q4_K / Q6_K: byte offset of the super-block scales (d, dmin / d) of rows b =
+// 0..3 (slot `slot`) for super-block sb of segment seg, tile t.
 QG_HD int64_t super_offset(const Geometry &g, int64_t t, int64_t seg, int slot, int sb)
 {
+    const int ub = super_row_bytes(g.qt);
     int64_t nsb = seg_blocks(g, seg) / kSuperBlocks;
-    return g.sup_off + t * g.tile_u + seg * (int64_t)kTileRows * (kSegBlocks / kSuperBlocks) * 4 +
-           ((int64_t)slot * nsb + sb) * kRowsPerLane * 4;
+    return g.sup_off + t * g.tile_u + seg * (int64_t)kTileRows * (kSegBlocks / kSuperBlocks) * ub +
+           ((int64_t)slot * nsb + sb) * kRowsPerLane * ub;
 }
 
 QG_HD int q4_nibble_pos(int e) { return e / 2 + 4 * (e % 2); }  // e in 0..7 within a dword
@@ -178,6 +222,24 @@ QG_HD uint32_t canon_nibble(int qt, const uint8_t *canon_row, int64_t blk, int e
     return (j % 2 == 0) ? (qs[e] & 0x0Fu) : (uint32_t)(qs[e] >> 4);
 }
 
+// Q6_K: low 4 bits and high 2 bits of element e (0..31) of 32-weight block blk
+// of a canonical row (super-block blk / 8; group jj = blk % 8 of it, in half jj / 4
+// with g = jj % 4: low bits in the low (g < 2) or high nibble of ql[64h + 32(g%2)
+// + e], high bits at bits 2g of qh[32h + e]).
+QG_HD uint32_t q6_canon_lo(const uint8_t *canon_row, int64_t blk, int e)
+{
+    const uint8_t *sb = canon_row + (blk / kSuperBlocks) * 210;
+    const int jj = (int)(blk % kSuperBlocks), h = jj / 4, g = jj % 4;
+    const uint8_t v = sb[64 * h + 32 * (g % 2) + e];
+    return g < 2 ? (v & 0x0Fu) : (uint32_t)(v >> 4);
+}
+QG_HD uint32_t q6_canon_hi(const uint8_t *canon_row, int64_t blk, int e)
+{
+    const uint8_t *sb = canon_row + (blk / kSuperBlocks) * 210;
+    const int jj = (int)(blk % kSuperBlocks), h = jj / 4, g = jj % 4;
+    return (uint32_t)(sb[128 + 32 * h + e] >> (2 * g)) & 3u;
+}
+
 // Write block `blk` (32 weights) of row `row` from the row's canonical bytes
 // `canon_row` into the packed buffer. A null `canon_row` writes a zero block
 // (padding rows).
@@ -197,6 +259,30 @@ QG_HD void pack_block(const Geometry &g, const uint8_t *canon_row, uint8_t *pack
             uint8_t *qp = packed + quant_offset(g, t, seg, b, h, slot, j);
             for (int i = 0; i < 16; ++i) qp[i] = c ? (uint8_t)(c[2 + 16 * h + i] ^ 0x80) : 0;
         }
+        return;
+    }
+    if (g.qt == kQ6_K) {
+        const uint8_t *sb = canon_row ? canon_row + (blk / kSuperBlocks) * 210 : nullptr;
+        const int jj = (int)(blk % kSuperBlocks);
+        sp[0] = sb ? sb[192 + 2 * jj] : 0;       // scale of elements 0..15
+        sp[1] = sb ? sb[192 + 2 * jj + 1] : 0;   // scale of elements 16..31
+        if (jj == 0) {
+            uint8_t *up = packed + super_offset(g, t, seg, slot, j / kSuperBlocks) + b * 2;
+            up[0] = sb ? sb[208] : 0;
+            up[1] = sb ? sb[209] : 0;
+        }
+        uint8_t *qp = packed + quant_offset(g, t, seg, b, 0, slot, j);
+        uint8_t *hp = packed + q6_hi_offset(g, t, seg, b / 2, slot, j) + (b % 2) * 8;
+        uint32_t dw[4] = {0, 0, 0, 0}, hw[2] = {0, 0};
+        if (canon_row)
+            for (int e = 0; e < 32; ++e) {
+                dw[e / 8] |= q6_canon_lo(canon_row, blk, e) << (4 * q4_nibble_pos(e % 8));
+                hw[e / 16] |= q6_canon_hi(canon_row, blk, e) << q6_hi_pos(e % 16);
+            }
+        for (int d = 0; d < 4; ++d)
+            for (int i = 0; i < 4; ++i) qp[4 * d + i] = (uint8_t)(dw[d] >> (8 * i));
+        for (int d = 0; d < 2; ++d)
+            for (int i = 0; i < 4; ++i) hp[4 * d + i] = (uint8_t)(hw[d] >> (8 * i));
         return;
     }
     if (g.qt == kQ4_0) {
@@ -240,6 +326,31 @@ QG_HD void unpack_block(const Geometry &g, const uint8_t *packed, uint8_t *canon
         for (int h = 0; h < 2; ++h) {
             const uint8_t *qp = packed + quant_offset(g, t, seg, b, h, slot, j);
             for (int i = 0; i < 16; ++i) c[2 + 16 * h + i] = (uint8_t)(qp[i] ^ 0x80);
+        }
+        return;
+    }
+    if (g.qt == kQ6_K) {
+        const int jj = (int)(blk % kSuperBlocks), h = jj / 4, gg = jj % 4;
+        uint8_t *sb = canon_row + (blk / kSuperBlocks) * 210;
+        sb[192 + 2 * jj] = sp[0];
+        sb[192 + 2 * jj + 1] = sp[1];
+        if (jj == 0) {
+            const uint8_t *up = packed + super_offset(g, t, seg, slot, j / kSuperBlocks) + b * 2;
+            sb[208] = up[0];
+            sb[209] = up[1];
+        }
+        const uint8_t *qp = packed + quant_offset(g, t, seg, b, 0, slot, j);
+        const uint8_t *hp = packed + q6_hi_offset(g, t, seg, b / 2, slot, j) + (b % 2) * 8;
+        for (int e = 0; e < 32; ++e) {
+            const int d = e / 8, hd = e / 16;
+            uint32_t dw = (uint32_t)qp[4 * d] | ((uint32_t)qp[4 * d + 1] << 8) | ((uint32_t)qp[4 * d + 2] << 16) |
+                          ((uint32_t)qp[4 * d + 3] << 24);
+            uint32_t hw = (uint32_t)hp[4 * hd] | ((uint32_t)hp[4 * hd + 1] << 8) |
+                          ((uint32_t)hp[4 * hd + 2] << 16) | ((uint32_t)hp[4 * hd + 3] << 24);
+            const uint32_t lo = (dw >> (4 * q4_nibble_pos(e % 8))) & 0xFu;
+            const uint32_t hi = (hw >> q6_hi_pos(e % 16)) & 3u;
+            sb[64 * h + 32 * (gg % 2) + e] |= (uint8_t)(gg < 2 ? lo : lo << 4);
+            sb[128 + 32 * h + e] |= (uint8_t)(hi << (2 * gg));
         }
         return;
     }

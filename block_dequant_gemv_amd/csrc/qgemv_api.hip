@@ -55,10 +55,13 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb)
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-bool valid_qtype(int qt) { return qt == QG_Q8_0 || qt == QG_Q4_0 || qt == QG_Q4_K; }
+bool valid_qtype(int qt) { return qt == QG_Q8_0 || qt == QG_Q4_0 || qt == QG_Q4_K || qt == QG_Q6_K; }
 
-// K granularity of a quantised type: 32 weights per block, 256 per Q4_K super-block.
-int64_t k_unit(int qt) { return qt == QG_Q4_K ? 256 : 32; }
+// The 256-weight super-block types: the plain single-row GEMV only.
+bool super_block_qtype(int qt) { return qt == QG_Q4_K || qt == QG_Q6_K; }
+
+// K granularity of a quantised type: 32 weights per block, 256 per Q4_K / Q6_K super-block.
+int64_t k_unit(int qt) { return super_block_qtype(qt) ? 256 : 32; }
 
 // Shape limits: rows and K must index 64-bit byte offsets safely and the grid
 // must fit 2^31 workgroups.
@@ -287,8 +290,9 @@ qg_status run_qgemv(int qt, int epi, const void *w, const float *x, void *y, int
                     int64_t K, int M, void *stream, const char *fn, const Affine &af = Affine(),
                     const Norm &nm = Norm())
 {
-    if (qt == QG_Q4_K && (epi != qgk::kEpiPlain || M != 1 || nm.on))
-        return fail(QG_EUNSUPPORTED, "%s: Q4_K weights have the plain single-row GEMV only (qgemv_q4_k)", fn);
+    if (super_block_qtype(qt) && (epi != qgk::kEpiPlain || M != 1 || nm.on))
+        return fail(QG_EUNSUPPORTED, "%s: Q4_K / Q6_K weights have the plain single-row GEMV only (qgemv_q4_k, qgemv_q6_k)",
+                    fn);
     qg_status st = check_qshape(qt, rows, K, fn);
     if (st) return st;
     if (!w || !x || !y) return fail(QG_EINVAL, "%s: null pointer", fn);
@@ -482,7 +486,8 @@ qg_status qg_unpack_host(int qtype, const void *packed_host, void *canonical_hos
     if (st) return st;
     const Geometry g = qgl::geometry(qtype, N, K);
     const int64_t rb = qgl::canon_row_bytes(qtype, K);
-    if (qtype == QG_Q4_K) memset(canonical_host, 0, (size_t)(N * rb));   // Q4_K blocks are OR-ed together
+    if (super_block_qtype(qtype))   // Q4_K / Q6_K blocks are OR-ed into their super-blocks
+        memset(canonical_host, 0, (size_t)(N * rb));
     for (int64_t r = 0; r < N; ++r)
         for (int64_t b = 0; b < g.KB; ++b)
             qgl::unpack_block(g, (const uint8_t *)packed_host, (uint8_t *)canonical_host + r * rb, r, b);
@@ -570,7 +575,7 @@ qg_status qg_rmsnorm(const float *x, const float *gamma, float eps, float *out, 
 
 size_t qg_prefill_workspace_size(int qtype, int64_t N, int64_t K, int64_t M)
 {
-    if (!valid_qtype(qtype) || qtype == QG_Q4_K || N <= 0 || N > kMaxDim || M <= 0 || M > kGemmMaxM || K <= 0 ||
+    if (!valid_qtype(qtype) || super_block_qtype(qtype) || N <= 0 || N > kMaxDim || M <= 0 || M > kGemmMaxM || K <= 0 ||
         K % 32 ||
         K > kMaxDim)
         return 0;
@@ -583,7 +588,7 @@ qg_status qgemm_prefill(int qtype, const void *w_packed, const float *X, float *
     const char *fn = "qgemm_prefill";
     qg_status st = check_qshape(qtype, N, K, fn);
     if (st) return st;
-    if (qtype == QG_Q4_K) return fail(QG_EUNSUPPORTED, "%s: Q4_K weights have the GEMV only", fn);
+    if (super_block_qtype(qtype)) return fail(QG_EUNSUPPORTED, "%s: Q4_K / Q6_K weights have the GEMV only", fn);
     if (M <= 0 || M > kGemmMaxM) return fail(QG_EINVAL, "%s: M=%lld outside 1..%lld", fn, (long long)M,
                                              (long long)kGemmMaxM);
     if (!w_packed || !X || !Y || !workspace) return fail(QG_EINVAL, "%s: null pointer", fn);
@@ -633,6 +638,11 @@ qg_status qgemm_prefill(int qtype, const void *w_packed, const float *X, float *
 qg_status qgemv_q4_k(const void *w_packed, const float *x, float *y, int64_t N, int64_t K, void *stream)
 {
     return run_qgemv(QG_Q4_K, qgk::kEpiPlain, w_packed, x, y, N, N, K, 1, stream, "qgemv_q4_k");
+}
+
+qg_status qgemv_q6_k(const void *w_packed, const float *x, float *y, int64_t N, int64_t K, void *stream)
+{
+    return run_qgemv(QG_Q6_K, qgk::kEpiPlain, w_packed, x, y, N, N, K, 1, stream, "qgemv_q6_k");
 }
 
 qg_status qgemv_fused_gateup_silu(int qtype, const void *w_gateup_packed, const float *x, float *y, int64_t N_ff,
@@ -703,7 +713,7 @@ qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int *split_k_ways
 {
     qg_status st = check_qshape(qtype, N, K, "qg_plan_info");
     if (st) return st;
-    if (M < 1 || M > 6 || (qtype == QG_Q4_K && M != 1)) return fail(QG_EUNSUPPORTED, "qg_plan_info: M=%d", M);
+    if (M < 1 || M > 6 || (super_block_qtype(qtype) && M != 1)) return fail(QG_EUNSUPPORTED, "qg_plan_info: M=%d", M);
     const qgk::QPlan p = make_qplan(qtype, N, K, M);
     if (split_k_ways) *split_k_ways = p.W;
     if (workgroups) *workgroups = p.grid;

@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "dequant.h"
 #include "layout.h"
 #include "qgemv_kernels.h"
@@ -53,13 +55,16 @@ __device__ __forceinline__ float silu_mul(float g, float u)
 
 // One lane's packed data for one (row tile, segment): 16 bytes per row and
 // half-block, plus the fp16 scales of its 4 rows (Q4_K: their 6-bit scales and
-// mins, and in `sup` the d and dmin of their super-blocks).
+// mins, and in `sup` the d and dmin of their super-blocks; Q6_K: their two int8
+// scales, in `hq` the high 2-bit parts of rows 0-1 and 2-3, and in `sup` d).
 template <int QT>
 struct Unit {
     static constexpr int NH = (QT == kQ8_0) ? 2 : 1;
+    using Sup = typename std::conditional<QT == kQ6_K, u32x2, u32x4>::type;
     u32x4 q[kRowsPerLane][NH];
     u32x2 sc;
-    u32x4 sup;
+    Sup sup;
+    u32x4 hq[2];
 };
 
 // A lane's place in a segment: the byte offset of its first 16-byte quant
@@ -70,7 +75,7 @@ struct Unit {
 struct LanePlace {
     uint32_t off_full, off_last;   // (slot * nb + jc) * 16 for nb = 32 / nb_last
     uint32_t str_last;             // bytes between the b/h units of the last segment (wave-uniform)
-    uint32_t sup_full, sup_last;   // Q4_K: (slot * nb/8 + jc/8) * 16, d and dmin of the 4 rows
+    uint32_t sup_full, sup_last;   // Q4_K / Q6_K: slot * nb/8 + jc/8, the super-block scales of the 4 rows
     int j_last;                    // jc in the last segment
     bool live_last;
 };
@@ -84,8 +89,8 @@ __device__ __forceinline__ LanePlace lane_place(const Geometry &g, int slot, int
     p.off_full = (uint32_t)(slot * kSegBlocks + j) * kUnit;
     p.off_last = (uint32_t)(slot * nb_last + p.j_last) * kUnit;
     p.str_last = (uint32_t)(kSlots * nb_last * kUnit);
-    p.sup_full = (uint32_t)(slot * (kSegBlocks / kSuperBlocks) + j / kSuperBlocks) * kUnit;
-    p.sup_last = (uint32_t)(slot * (nb_last / kSuperBlocks) + p.j_last / kSuperBlocks) * kUnit;
+    p.sup_full = (uint32_t)(slot * (kSegBlocks / kSuperBlocks) + j / kSuperBlocks);
+    p.sup_last = (uint32_t)(slot * (nb_last / kSuperBlocks) + p.j_last / kSuperBlocks);
     return p;
 }
 
@@ -100,7 +105,7 @@ __device__ __forceinline__ void load_unit(Unit<QT> &u, const uint8_t *__restrict
                                           int64_t s, const LanePlace &lp, bool real)
 {
     constexpr int NH = Unit<QT>::NH;
-    constexpr int64_t seg_q = (int64_t)kTileRows * kSegBlocks * NH * kUnit;
+    constexpr int64_t seg_q = (int64_t)kTileRows * kSegBlocks * packed_quant_bytes(QT);   // bytes per segment
     constexpr uint32_t str_full = (uint32_t)(kSlots * kSegBlocks * kUnit);
     t = real ? t : 0;
     s = real ? s : 0;
@@ -118,10 +123,16 @@ __device__ __forceinline__ void load_unit(Unit<QT> &u, const uint8_t *__restrict
     // scales: (slot * nb + jc) * 8 bytes = half the quant offset
     const uint8_t *sbase = wp + g.scale_off + t * g.tile_s + s * (int64_t)(kTileRows * kSegBlocks * 2);
     u.sc = __builtin_nontemporal_load((const u32x2 *)(sbase + (off >> 1)));
-    if constexpr (QT == kQ4_K) {
-        const uint32_t so = real ? (last ? lp.sup_last : lp.sup_full) : 0u;
-        const uint8_t *ubase = wp + g.sup_off + t * g.tile_u + s * (int64_t)(kTileRows * (kSegBlocks / kSuperBlocks) * 4);
-        u.sup = __builtin_nontemporal_load((const u32x4 *)(ubase + so));
+    if constexpr (QT == kQ4_K || QT == kQ6_K) {
+        constexpr uint32_t ub = (QT == kQ4_K) ? 4 : 2;   // super-plane bytes per row
+        const uint32_t so = real ? (last ? lp.sup_last : lp.sup_full) * (kRowsPerLane * ub) : 0u;
+        const uint8_t *ubase = wp + g.sup_off + t * g.tile_u + s * (int64_t)(kTileRows * (kSegBlocks / kSuperBlocks) * ub);
+        u.sup = __builtin_nontemporal_load((const typename Unit<QT>::Sup *)(ubase + so));
+    }
+    if constexpr (QT == kQ6_K) {
+#pragma unroll
+        for (int bp = 0; bp < 2; ++bp)
+            u.hq[bp] = __builtin_nontemporal_load((const u32x4 *)(base + (uint32_t)(kRowsPerLane + bp) * ustride + off));
     }
 }
 
@@ -180,6 +191,58 @@ __device__ __forceinline__ void compute_unit_q4k(const Unit<kQ4_K> &u, float (&a
     }
 }
 
+// Q6_K: acc[0][b] += d * (sc_lo * sum_{e<16} v_e x_e + sc_hi * sum_{e>=16} v_e x_e)
+// with v = q - 32 exact in fp16: the low nibble goes into a magic-number fp16
+// (1024 + q or 1024 + 16 q) as in Q4_0 and the high 2 bits are OR-ed in above it
+// from the row's dword of high parts (a shift by 0 / 2 for the first 16 elements'
+// dword halves, a rotation by 24 and a shift by 2 for the second), then -1056 or
+// (/16 - 96). One fp32 fma per weight, as for Q4_0; the int8 scales are exact
+// in fp32. Dead lanes of a ragged segment get d = 0.
+template <bool XLDS>
+__device__ __forceinline__ void compute_unit_q6k(const Unit<kQ6_K> &u, float (&acc)[1][kRowsPerLane],
+                                                 const Consts &k, const f32x4 *xs4, const float *__restrict__ x,
+                                                 int64_t s, int j, bool live)
+{
+    constexpr int B = kRowsPerLane;
+    float s16[B][2];
+#pragma unroll
+    for (int b = 0; b < B; ++b) s16[b][0] = s16[b][1] = 0.0f;
+    const f32x4 *xl = xs4 + ((uint32_t)s << 8) + (uint32_t)j;
+    const float *xg = x + s * kSegWeights + j * 32;
+#pragma unroll
+    for (int c = 0; c < 8; c += 2) {
+        f32x4 xv[2];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) xv[cc] = XLDS ? xl[(c + cc) * 32] : *(const f32x4 *)(xg + (c + cc) * 4);
+        const int dw = c >> 1;   // dword of 8 elements: 8 dw .. 8 dw + 7
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const u32x4 &hv = u.hq[b >> 1];
+            const uint32_t hd = hv[2 * (b & 1) + (dw >> 1)];
+            h2 p[4];
+            q6k_pairs(u.q[b][0][dw], hd, (dw & 1) != 0, k, p);
+            float s_ = s16[b][dw >> 1];
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                s_ = __builtin_fmaf((float)p[2 * cc].x, xv[cc].x, s_);
+                s_ = __builtin_fmaf((float)p[2 * cc].y, xv[cc].y, s_);
+                s_ = __builtin_fmaf((float)p[2 * cc + 1].x, xv[cc].z, s_);
+                s_ = __builtin_fmaf((float)p[2 * cc + 1].y, xv[cc].w, s_);
+            }
+            s16[b][dw >> 1] = s_;
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const uint32_t sw = ((b < 2) ? u.sc.x : u.sc.y) >> (16 * (b & 1));   // byte 0: sc_lo, byte 1: sc_hi
+        const float sc_lo = (float)(int8_t)(sw & 0xFFu);
+        const float sc_hi = (float)(int8_t)((sw >> 8) & 0xFFu);
+        const uint32_t dw = ((b < 2) ? u.sup.x : u.sup.y) >> (16 * (b & 1));
+        const float d = live ? (float)as_h2(dw).x : 0.0f;
+        acc[0][b] = __builtin_fmaf(d, __builtin_fmaf(sc_hi, s16[b][1], sc_lo * s16[b][0]), acc[0][b]);
+    }
+}
+
 template <int QT, int M, bool XLDS>
 __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][kRowsPerLane], const Consts &k,
                                              const f32x4 *xs4, const float *__restrict__ x, int64_t x_stride,
@@ -188,6 +251,11 @@ __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][
     if constexpr (QT == kQ4_K) {
         static_assert(M == 1, "Q4_K has the single-row GEMV only");
         compute_unit_q4k<XLDS>(u, acc, k, xs4, x, s, j, live);
+        return;
+    }
+    if constexpr (QT == kQ6_K) {
+        static_assert(M == 1, "Q6_K has the single-row GEMV only");
+        compute_unit_q6k<XLDS>(u, acc, k, xs4, x, s, j, live);
         return;
     }
     constexpr int B = kRowsPerLane;
@@ -968,10 +1036,11 @@ hipError_t launch_qgemv(int qt, int M, int epi, const QPlan &p, const uint8_t *w
                         const QArgs &a, hipStream_t s)
 {
     if (qt == kQ8_0) return dispatch_m<kQ8_0>(wp, x, y, a, M, epi, p, s);
-    if (qt == kQ4_K) {
+    if (qt == kQ4_K || qt == kQ6_K) {
         // the plain single-row GEMV only (the C ABI refuses the other forms)
         if (M != 1 || epi != kEpiPlain || p.norm) return hipErrorInvalidValue;
-        return dispatch_form<kQ4_K, 1, kEpiPlain>(wp, x, y, a, p, s);
+        return qt == kQ4_K ? dispatch_form<kQ4_K, 1, kEpiPlain>(wp, x, y, a, p, s)
+                           : dispatch_form<kQ6_K, 1, kEpiPlain>(wp, x, y, a, p, s);
     }
     return dispatch_m<kQ4_0>(wp, x, y, a, M, epi, p, s);
 }

@@ -52,23 +52,24 @@ typedef enum {
     QG_EHIP = 4          /* the HIP runtime reported an error at launch         */
 } qg_status;
 
-typedef enum { QG_Q8_0 = 1, QG_Q4_0 = 2, QG_Q4_K = 3 } qg_qtype;
+typedef enum { QG_Q8_0 = 1, QG_Q4_0 = 2, QG_Q4_K = 3, QG_Q6_K = 4 } qg_qtype;
 
 /* ---- load-time packing --------------------------------------------------- */
 
 /* Bytes of the packed form of an N x K matrix of `qtype` (K % 32 == 0, K % 256
- * == 0 for QG_Q4_K, N, K > 0).
+ * == 0 for QG_Q4_K and QG_Q6_K, N, K > 0).
  * Returns 0 for invalid arguments. The packed form holds the same quant and
  * scale bytes as the canonical one plus zero padding of the last row tile (up
- * to 7 rows) and 256-byte alignment of its two planes (three for Q4_K, whose
- * super-block d and dmin get a plane of their own). */
+ * to 7 rows) and 256-byte alignment of its two planes (three for Q4_K and
+ * Q6_K, whose super-block scales get a plane of their own). */
 size_t qg_packed_size(int qtype, int64_t N, int64_t K);
 
 /* Re-tile a canonical matrix already in device memory into the packed layout.
  * canonical: N*K/32 GGUF-style blocks, row-major (row n = K/32 consecutive
  *   blocks; block = little-endian fp16 scale then the quants; Q4_0 byte j holds
  *   element j in its low nibble and element j+16 in its high nibble); for Q4_K
- *   N*K/256 144-byte super-blocks, laid out as qgemv_q4_k states.
+ *   and Q6_K N*K/256 super-blocks of 144 / 210 bytes, laid out as qgemv_q4_k /
+ *   qgemv_q6_k state.
  * packed: qg_packed_size(qtype, N, K) bytes, 16-byte aligned, not overlapping
  *   canonical. Padding rows are written as zeros. Stream-ordered kernel. */
 qg_status qg_pack(int qtype, const void *canonical, void *packed, int64_t N, int64_t K, void *stream);
@@ -119,6 +120,19 @@ qg_status qgemv_q4_0(const void *w_packed, const float *x, float *y, int64_t N, 
  * weights) and is accepted by this GEMV only: the other GEMV calls, the verify
  * and the prefill GEMM return QG_EUNSUPPORTED for it. */
 qg_status qgemv_q4_k(const void *w_packed, const float *x, float *y, int64_t N, int64_t K, void *stream);
+
+/* The same for a packed Q6_K weight (K % 256 == 0). Q6_K is the k-quant block
+ * the RunIT_Mac README's quantisation table lists as supported and the
+ * EdgeRunner page ("Run it yourself") loads; its layout is not on the pages and
+ * is read as the published GGUF block: per 256 weights 128 bytes ql of low
+ * 4-bit parts, 64 bytes qh of high 2-bit parts, 16 int8 scales sc (one per 16
+ * weights), then fp16 d. Weight i (half h = i/128, g = (i%128)/32, l = i%32):
+ * q = (low (g < 2) or high nibble of ql[64h + 32(g%2) + l]) | (bits 2g..2g+1 of
+ * qh[32h + l]) << 4, weight = d * sc[i/16] * (q - 32). The quants are dequantised
+ * exactly (fp16 q - 32) and each 16-weight sum is scaled by its sc, then d.
+ * Packs with qg_pack / qg_pack_rows / qg_pack_host (210 bytes per 256 weights,
+ * as canonical); like Q4_K it is accepted by this GEMV only. */
+qg_status qgemv_q6_k(const void *w_packed, const float *x, float *y, int64_t N, int64_t K, void *stream);
 
 /* Output element type of qgemv_epilogue. */
 typedef enum { QG_OUT_F32 = 0, QG_OUT_F16 = 1 } qg_out_type;

@@ -1,15 +1,17 @@
-"""GPU parity of the Q4_K GEMV (qgemv_q4_k) against the fp64 oracle: shapes that
-span several row tiles, ragged row tiles, ragged last segments of 8, 16 and 24
-sub-blocks, split-K plans, the global-memory activation path and the
-persistent form; the device packer against the host packer; exact closed forms
-(a subnormal d, the min term alone); every forced launch shape; and the same
-bits run to run.
+"""GPU parity of the super-block GEMVs (qgemv_q4_k, qgemv_q6_k) against the fp64
+oracle: shapes that span several row tiles, ragged row tiles, ragged last
+segments of 8, 16 and 24 blocks, split-K plans, the global-memory activation
+path and the persistent form; the device packer against the host packer; exact
+closed forms (subnormal d; for Q4_K the min term alone, for Q6_K scale -128 and
+the quant extremes); every forced launch shape; and the same bits run to run.
 
-Tolerance. The kernel sums d*sc * sum(q x) and dmin*mn * sum(x) per sub-block
-and subtracts them, so its rounding scales with sum (|d sc q| + |dmin mn|) |x|
+Tolerance. Q6_K: the linear bound 1e-5 * sum |w x| + 1e-7 of the other types
+(each 16-weight sum of (q - 32) x is scaled by its int8 scale, then by d).
+Q4_K: the kernel sums d*sc * sum(q x) and dmin*mn * sum(x) per sub-block and
+subtracts them, so its rounding scales with sum (|d sc q| + |dmin mn|) |x|
 rather than with sum |w x| (the terms can cancel); the bound is 1e-5 of that
-magnitude + 1e-7, the linear bound of the other types with the two terms'
-magnitudes in place of |w|."""
+magnitude + 1e-7, the linear bound with the two terms' magnitudes in place of
+|w|."""
 import itertools
 import os
 
@@ -32,33 +34,45 @@ SHAPES = [(1, 256), (7, 512), (8, 1024), (9, 1280), (33, 1536), (40, 1792), (100
           (640, 17408), (24, 32768), (2001, 8448), (3300, 5120)]
 
 
-@pytest.mark.parametrize("N,K", SHAPES)
-def test_q4_k_matches_oracle(N, K):
-    rng = np.random.default_rng(4000 + N + K)
-    canon = W.matrix("q4_k", N, K, rng)
-    x = W.activation(K, rng)
-    announce(f"qgemv_q4_k N={N} K={K} plan={qg.qg_plan_info('q4_k', N, K)}")
-    y, tail = run_qgemv("q4_k", canon, x, N, K, canary=37)
-    assert np.all(tail == 12345.0), "wrote past y[N-1]"
-    y_ref, a_ref = O.gemv("q4_k", canon, x, N, K, threads=THREADS)
+KINDS = ["q4_k", "q6_k"]
+
+
+def _bound(kind, canon, x, N, K, a_ref):
+    """The tolerance's magnitude per row (see the module docstring)."""
+    if kind == "q6_k":
+        return a_ref
     bound = q4_k_term_bound(canon, x, N, K, threads=THREADS)
     assert np.all(bound >= a_ref * (1 - 1e-12))
-    assert_linear(y, y_ref, bound, f"q4_k {N}x{K}")
+    return bound
 
 
-def test_q4_k_pack_device_equals_host():
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_kquant_matches_oracle(kind, N, K):
+    rng = np.random.default_rng(4000 + N + K)
+    canon = W.matrix(kind, N, K, rng)
+    x = W.activation(K, rng)
+    announce(f"qgemv_{kind} N={N} K={K} plan={qg.qg_plan_info(kind, N, K)}")
+    y, tail = run_qgemv(kind, canon, x, N, K, canary=37)
+    assert np.all(tail == 12345.0), "wrote past y[N-1]"
+    y_ref, a_ref = O.gemv(kind, canon, x, N, K, threads=THREADS)
+    assert_linear(y, y_ref, _bound(kind, canon, x, N, K, a_ref), f"{kind} {N}x{K}")
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_kquant_pack_device_equals_host(kind):
     for N, K in ((1, 256), (9, 1280), (100, 3072), (37, 5120), (5, 1792)):
-        canon = W.matrix("q4_k", N, K, np.random.default_rng(N + K))
-        announce(f"qg_pack q4_k N={N} K={K}")
-        packed = qg.pack_weights("q4_k", canon, N, K)
-        assert np.array_equal(packed.cpu().numpy(), qg.qg_pack_host("q4_k", canon, N, K)), (N, K)
+        canon = W.matrix(kind, N, K, np.random.default_rng(N + K))
+        announce(f"qg_pack {kind} N={N} K={K}")
+        packed = qg.pack_weights(kind, canon, N, K)
+        assert np.array_equal(packed.cpu().numpy(), qg.qg_pack_host(kind, canon, N, K)), (N, K)
     # load-time concatenation of row ranges
     K = 1024
-    parts = [(W.matrix("q4_k", n, K, np.random.default_rng(n)), n) for n in (20, 9, 11)]
-    announce("qg_pack_rows q4_k concat")
-    packed = qg.pack_concat("q4_k", parts, K)
+    parts = [(W.matrix(kind, n, K, np.random.default_rng(n)), n) for n in (20, 9, 11)]
+    announce(f"qg_pack_rows {kind} concat")
+    packed = qg.pack_concat(kind, parts, K)
     cat = np.concatenate([p for p, _ in parts])
-    assert np.array_equal(packed.cpu().numpy(), qg.qg_pack_host("q4_k", cat, 40, K))
+    assert np.array_equal(packed.cpu().numpy(), qg.qg_pack_host(kind, cat, 40, K))
 
 
 def _superblock(d: int, dmin: int, sc: int, mn: int, q: int) -> bytes:
@@ -93,6 +107,29 @@ def test_q4_k_closed_forms_exact_on_gpu(d, dmin, sc, mn, q, w):
     assert np.all(y_ref == w * K)
 
 
+def _q6_k_superblock(d: int, sc: int, q: int) -> bytes:
+    """One canonical Q6_K super-block with every scale sc and every quant q."""
+    lo, hi = q & 15, q >> 4
+    return bytes([lo | (lo << 4)] * 128) + bytes([hi * 0x55] * 64) + bytes([sc & 255] * 16) + d.to_bytes(2, "little")
+
+
+@pytest.mark.parametrize("d,sc,q,w", [
+    (0x3800, 3, 40, 12.0),                         # 0.5 * 3 * (40 - 32)
+    (0x0001, -128, 63, -3968 * 2.0 ** -24),        # subnormal d, scale -128, q = 63
+    (0x3C00, 127, 0, -4064.0),                     # q = 0: 127 * -32
+    (0x3C00, -1, 32, 0.0),                         # q = 32 is zero
+])
+def test_q6_k_closed_forms_exact_on_gpu(d, sc, q, w):
+    # every weight equal, x = 1: y = w * K exactly (every partial sum is exact)
+    N, K = 16, 5120
+    canon = np.frombuffer(_q6_k_superblock(d, sc, q) * (N * K // 256), np.uint8).copy()
+    announce(f"q6_k closed form d={d:#x} sc={sc} q={q}")
+    y = run_qgemv("q6_k", canon, np.ones(K, np.float32), N, K)
+    assert np.all(y == np.float32(w * K)), (y[:4], w * K)
+    y_ref, _ = O.gemv("q6_k", canon, np.ones(K, np.float32), N, K)
+    assert np.all(y_ref == w * K)
+
+
 KNOBS = ("QG_PERSIST", "QG_SPLIT_K", "QG_X_GLOBAL", "QG_WAVES_PER_WG", "QG_TILES_PER_GROUP", "QG_PREFETCH",
          "QG_STRIDE_GROUPS")
 
@@ -105,15 +142,16 @@ def _set(**kw):
     qg.qg_reload_tuning()
 
 
+@pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("N,K", [(203, 8192 + 256), (1000, 1024)])
-def test_q4_k_forced_launch_shapes(N, K):
+def test_kquant_forced_launch_shapes(kind, N, K):
     rng = np.random.default_rng(N * K + 4)
-    canon = W.matrix("q4_k", N, K, rng)
-    packed = qg.pack_weights("q4_k", canon, N, K)
+    canon = W.matrix(kind, N, K, rng)
+    packed = qg.pack_weights(kind, canon, N, K)
     x = W.activation(K, rng)
     xd = to_dev(x)
-    y_ref, _ = O.gemv("q4_k", canon, x, N, K, threads=THREADS)
-    bound = q4_k_term_bound(canon, x, N, K, threads=THREADS)
+    y_ref, a_ref = O.gemv(kind, canon, x, N, K, threads=THREADS)
+    bound = _bound(kind, canon, x, N, K, a_ref)
     nseg = -(-K // 1024)
     combos = [dict(QG_PERSIST=1, QG_X_GLOBAL=xg) for xg in (0, 1)]
     combos += [dict(QG_PERSIST=0, QG_STRIDE_GROUPS=3, QG_WAVES_PER_WG=1, QG_SPLIT_K=split)
@@ -126,27 +164,28 @@ def test_q4_k_forced_launch_shapes(N, K):
     try:
         for combo in combos:
             _set(**combo)
-            ctx = f"q4_k {N}x{K} " + " ".join(f"{k[3:].lower()}={v}" for k, v in combo.items())
+            ctx = f"{kind} {N}x{K} " + " ".join(f"{k[3:].lower()}={v}" for k, v in combo.items())
             announce(ctx)
             y = empty_f32(N)
-            qg.qgemv_q4_k(packed, xd, y, N, K)
+            qg.qgemv(kind, packed, xd, y, N, K)
             sync()
             assert_linear(y.cpu().numpy(), y_ref, bound, ctx)
     finally:
         _set()
 
 
-def test_q4_k_run_to_run_bitwise_determinism():
+@pytest.mark.parametrize("kind", KINDS)
+def test_kquant_run_to_run_bitwise_determinism(kind):
     for N, K in ((1024, 1024), (640, 17408)):
         rng = np.random.default_rng(98)
-        canon = W.matrix("q4_k", N, K, rng)
+        canon = W.matrix(kind, N, K, rng)
         x = to_dev(W.activation(K, rng))
-        packed = qg.pack_weights("q4_k", canon, N, K)
-        announce(f"determinism q4_k {N}x{K}")
+        packed = qg.pack_weights(kind, canon, N, K)
+        announce(f"determinism {kind} {N}x{K}")
         outs = []
         for _ in range(10):
             y = empty_f32(N)
-            qg.qgemv_q4_k(packed, x, y, N, K)
+            qg.qgemv(kind, packed, x, y, N, K)
             outs.append(y)
         sync()
         ref = outs[0].cpu().numpy().tobytes()

@@ -72,6 +72,14 @@ def test_packed_size(L):
     assert qg.qg_packed_size("q4_k", 8, 256) == 1024 + 256 + 256
     for bad in ((8, 32), (8, 1056), (8, 0)):
         assert qg.qg_packed_size("q4_k", *bad) == 0
+    # Q6_K: as canonical, 210 bytes per 256 weights (24 B of quants + 2 B of
+    # scales per 32, 2 B of d per 256); 8 x 256: quant 1536, scale 128 -> 256,
+    # super 16 -> 256
+    for N, K in ((1024, 1024), (4096, 1024), (17408, 5120), (5120, 17408)):
+        assert qg.qg_packed_size("q6_k", N, K) == N * (K // 256) * 210
+    assert qg.qg_packed_size("q6_k", 8, 256) == 1536 + 256 + 256
+    for bad in ((8, 32), (8, 1056), (8, 0)):
+        assert qg.qg_packed_size("q6_k", *bad) == 0
 
 
 FAKE = 0x10000  # a 64 KiB-aligned address that is never dereferenced
@@ -113,6 +121,12 @@ def test_argument_checks_return_codes_without_gpu(L):
     assert call(L, "qgemv_q4_k", f, f + (1 << 20), f + (2 << 20), 8, 1056, null) == qg.QG_EINVAL
     assert call(L, "qgemv_q4_k", f + 8, f + (1 << 20), f + (2 << 20), 8, 256, null) == qg.QG_EALIGN
     assert call(L, "qgemv_q4_k", f, f + (1 << 20), f + (1 << 20), 8, 256, null) == qg.QG_EINVAL
+    assert call(L, "qgemv_verify", qg.Q6_K, f, f + (1 << 20), f + (2 << 20), 8, 256, 2, null) == qg.QG_EUNSUPPORTED
+    assert call(L, "qgemv_fused_gateup_silu", qg.Q6_K, f, f + (1 << 20), f + (2 << 20), 8, 256,
+                null) == qg.QG_EUNSUPPORTED
+    assert call(L, "qgemv_q6_k", f, f + (1 << 20), f + (2 << 20), 8, 1056, null) == qg.QG_EINVAL
+    assert call(L, "qgemv_q6_k", f + 8, f + (1 << 20), f + (2 << 20), 8, 256, null) == qg.QG_EALIGN
+    assert call(L, "qgemv_q6_k", f, f + (1 << 20), f + (1 << 20), 8, 256, null) == qg.QG_EINVAL
     assert call(L, "qgemv_fused_gateup_silu", 5, f, f + (1 << 20), f + (2 << 20), 8, 32, null) == qg.QG_EUNSUPPORTED
     assert call(L, "qgemv_fused_gateup_silu", 1, f, f + (1 << 20), f + (2 << 20), 0, 32, null) == qg.QG_EINVAL
     # verify: the M x K activations must not overlap the M x N outputs
@@ -254,7 +268,7 @@ Q4_K_SHAPES = [(1, 256), (3, 512), (8, 1024), (9, 1280), (17, 2048), (24, 2304),
 
 
 @pytest.mark.parametrize("kind,N,K", [(k, n, kk) for k in ("q8_0", "q4_0") for n, kk in SHAPES] +
-                         [("q4_k", n, kk) for n, kk in Q4_K_SHAPES])
+                         [(k, n, kk) for k in ("q4_k", "q6_k") for n, kk in Q4_K_SHAPES])
 def test_pack_unpack_roundtrip(L, kind, N, K):
     canon = W.matrix(kind, N, K, np.random.default_rng(N * 7 + K))
     packed = qg.qg_pack_host(kind, canon, N, K)
@@ -263,6 +277,47 @@ def test_pack_unpack_roundtrip(L, kind, N, K):
     assert np.array_equal(back, canon)
     # the packed form holds at least the canonical bytes
     assert packed.size >= canon.size and canon.size == W.matrix_bytes(kind, N, K)
+
+
+def test_q6_k_pack_places_every_field(L):
+    # One row, K = 256: d lands in the super plane (row 0, slot 0), block j's two
+    # int8 scales (weights 32j..32j+15 and 32j+16..32j+31) as bytes 0 and 1 of
+    # its scale-plane entry, and each weight's 6-bit quant splits into a nibble
+    # in the Q4_0 arrangement of quant unit 0 and a 2-bit part at its bit pair in
+    # the row's dwords of quant unit 4 (rows 0-1: row 0 in bytes 0..7).
+    N, K = 1, 256
+    s_off = 8 * 8 * 24          # quant plane: 8 rows x 8 blocks x 24 B
+    u_off = s_off + 256
+    canon = np.zeros(210, np.uint8)
+    canon[192:208] = np.arange(-8, 8, dtype=np.int8).view(np.uint8)
+    canon[208:210] = [0x34, 0x12]
+    packed = qg.qg_pack_host("q6_k", canon, N, K)
+    assert list(packed[u_off:u_off + 2]) == [0x34, 0x12]
+    for j in range(8):
+        assert packed[s_off + j * 8].view(np.int8) == 2 * j - 8
+        assert packed[s_off + j * 8 + 1].view(np.int8) == 2 * j - 7
+    # one tile, one segment of nb = 8 blocks: unit u of slot 0, block j at ((u * 2 + 0) * 8 + j) * 16
+
+    def hi_pos(e):
+        f = e % 8
+        p = (f % 2) * 16 + 4 + 4 * ((f // 2) % 2) + 2 * (f // 4)
+        return (p + 24 * (e // 8)) % 32
+    assert sorted(hi_pos(e) // 2 for e in range(16)) == list(range(16))   # the 16 bit pairs, once each
+    for w, q in ((0, 1), (5, 47), (31, 60), (33, 17), (70, 63), (100, 32), (130, 5), (255, 40)):
+        c = canon.copy()
+        h, r = divmod(w, 128)
+        g, l = divmod(r, 32)
+        c[64 * h + 32 * (g % 2) + l] |= (q & 15) << (4 * (g // 2))
+        c[128 + 32 * h + l] |= (q >> 4) << (2 * g)
+        p = qg.qg_pack_host("q6_k", c, N, K)
+        j, e = divmod(w, 32)
+        lo = int.from_bytes(bytes(p[((0 * 2) * 8 + j) * 16 + 4 * (e // 8):][:4]), "little")
+        assert (lo >> (4 * ((e % 8) // 2 + 4 * (e % 2)))) & 15 == q & 15, (w, q)
+        hi = int.from_bytes(bytes(p[((4 * 2) * 8 + j) * 16 + 4 * (e // 16):][:4]), "little")
+        assert (hi >> hi_pos(e % 16)) & 3 == q >> 4, (w, q)
+        # nothing else set in the quant plane
+        bits = int(np.unpackbits(p[:s_off]).sum())
+        assert bits == bin(q & 15).count("1") + bin(q >> 4).count("1"), (w, q)
 
 
 def test_q4_k_pack_places_every_field(L):
