@@ -531,6 +531,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=15)
     ap.add_argument("--reps", type=int, default=50, help="cold reps per call in the per-config table")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config table")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated label prefixes: time only the per-config rows that start with one of "
+                         "them, and skip the RMSNorm and prefill-GEMM legs (for profiler runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run torch.neg over 256 MiB, a plain copy-like kernel of known traffic "
@@ -691,8 +694,13 @@ def main():
         log(f"per-call table: {args.reps} cold calls rotating over >= 1.2 GiB of weight copies, and warm calls")
         norm_cases = cfg_calls.pop("norm")
         gemm_cases = cfg_calls.pop("gemm")
+        only = [o for o in args.only.split(",") if o] if args.only else None
+        if only:
+            norm_cases, gemm_cases = [], []
         for ci in sorted(cfg_calls):
             for c in cfg_calls[ci]:
+                if only and not any(c.label.startswith(o) for o in only):
+                    continue
                 copies = cold_copies(torch, c.weight)
                 fns = [c.fn] + [c.make(cp.data_ptr()) for cp in copies[1:]]
                 torch.cuda.synchronize()
