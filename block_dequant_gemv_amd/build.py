@@ -9,6 +9,10 @@ Flags:
   -fno-gpu-flush-denormals-to-zero  fp16 subnormal scales must survive.
   -Xclang -target-feature -Xclang -packed-fp32-ops
                                   no packed fp32 instructions are generated.
+  -mllvm -amdgpu-mfma-vgpr-form   (GEMM source only) the matrix-core results go to
+                                  ordinary VGPRs, which the per-block scale fma reads
+                                  directly, instead of accumulation registers that
+                                  need one v_accvgpr_read per value.
 """
 from __future__ import annotations
 
@@ -24,6 +28,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqgemv.so")
 SOURCES = ["qgemv_kernels.hip", "qgemm_kernels.hip", "qgemv_api.hip"]
 HEADERS = ["layout.h", "dequant.h", "qgemv_kernels.h", "qgemm_kernels.h"]
+SOURCE_FLAGS = {"qgemm_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -50,7 +55,7 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     procs = []
     for src in SOURCES:
         obj = os.path.join(build_dir, src.replace(".hip", ".o"))
-        cmd = [cc, *flags(), *(extra or []), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *flags(), *SOURCE_FLAGS.get(src, []), *(extra or []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), file=sys.stderr)
         procs.append((subprocess.Popen(cmd), src))
