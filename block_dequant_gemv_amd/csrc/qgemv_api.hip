@@ -290,9 +290,6 @@ qg_status run_qgemv(int qt, int epi, const void *w, const float *x, void *y, int
                     int64_t K, int M, void *stream, const char *fn, const Affine &af = Affine(),
                     const Norm &nm = Norm())
 {
-    if (super_block_qtype(qt) && (epi != qgk::kEpiPlain || M != 1 || nm.on))
-        return fail(QG_EUNSUPPORTED, "%s: Q4_K / Q6_K weights have the plain single-row GEMV only (qgemv_q4_k, qgemv_q6_k)",
-                    fn);
     qg_status st = check_qshape(qt, rows, K, fn);
     if (st) return st;
     if (!w || !x || !y) return fail(QG_EINVAL, "%s: null pointer", fn);
@@ -713,7 +710,7 @@ qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int *split_k_ways
 {
     qg_status st = check_qshape(qtype, N, K, "qg_plan_info");
     if (st) return st;
-    if (M < 1 || M > 6 || (super_block_qtype(qtype) && M != 1)) return fail(QG_EUNSUPPORTED, "qg_plan_info: M=%d", M);
+    if (M < 1 || M > 6) return fail(QG_EUNSUPPORTED, "qg_plan_info: M=%d", M);
     const qgk::QPlan p = make_qplan(qtype, N, K, M);
     if (split_k_ways) *split_k_ways = p.W;
     if (workgroups) *workgroups = p.grid;

@@ -139,45 +139,75 @@ __device__ __forceinline__ void load_unit(Unit<QT> &u, const uint8_t *__restrict
 // acc[m][b] += d_b * sum_e v_e * x_m[e] over the lane's block of segment s.
 // j is the block whose activations the lane reads; live is false only for
 // lanes past the end of a ragged last segment.
-// Q4_K: acc[0][b] += d*sc * sum_e q_e x_e - dmin*mn * sum_e x_e over the lane's
+// Q4_K: acc[m][b] += d*sc * sum_e q_e x_e - dmin*mn * sum_e x_e over the lane's
 // sub-block (the weight's two terms summed apart, as the k-quant dot product
-// does): one fma per weight, and the sum of x shared by the 4 rows. The quants
-// arrive as fp16 subnormals q * 2^-24 (elements 0, 1 of each 4) and q * 2^-20
-// (elements 2, 3), summed in two accumulators and joined exactly up to one
-// rounding; the 2^24 goes into d*sc. d*sc and dmin*mn are exact (11-bit by 6-bit
-// products). Dead lanes of a ragged segment get zero scales and mins: they add 0.
-template <bool XLDS>
-__device__ __forceinline__ void compute_unit_q4k(const Unit<kQ4_K> &u, float (&acc)[1][kRowsPerLane],
+// does): one fma per weight and row, and each row's sum of x shared by the 4
+// weight rows. The quants arrive as fp16 subnormals q * 2^-24 (elements 0, 1 of
+// each 4) and q * 2^-20 (elements 2, 3), summed in two accumulators and joined
+// exactly up to one rounding; the 2^24 goes into d*sc. d*sc and dmin*mn are
+// exact (11-bit by 6-bit products). Dead lanes of a ragged segment get zero
+// scales and mins: they add 0. Every activation row goes through the same
+// operations for any M.
+template <int M, bool XLDS>
+__device__ __forceinline__ void compute_unit_q4k(const Unit<kQ4_K> &u, float (&acc)[M][kRowsPerLane],
                                                  const Consts &k, const f32x4 *xs4, const float *__restrict__ x,
-                                                 int64_t s, int j, bool live)
+                                                 int64_t x_stride, int64_t nseg, int64_t s, int j, bool live)
 {
     constexpr int B = kRowsPerLane;
-    float s24[B], s20[B];
+    float s24[M][B], s20[M][B], sx[M];
 #pragma unroll
-    for (int b = 0; b < B; ++b) s24[b] = s20[b] = 0.0f;
-    float sx = 0.0f;
+    for (int m = 0; m < M; ++m) {
+        sx[m] = 0.0f;
+#pragma unroll
+        for (int b = 0; b < B; ++b) s24[m][b] = s20[m][b] = 0.0f;
+    }
+    const uint32_t x_row = (uint32_t)nseg << 8;
     const f32x4 *xl = xs4 + ((uint32_t)s << 8) + (uint32_t)j;
     const float *xg = x + s * kSegWeights + j * 32;
+    auto row_fma = [&](const h2 (&p)[4], const f32x4 (&xv)[2], int m, int b) {
+        float lo = s24[m][b], hi = s20[m][b];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            lo = __builtin_fmaf((float)p[2 * cc].x, xv[cc].x, lo);
+            lo = __builtin_fmaf((float)p[2 * cc].y, xv[cc].y, lo);
+            hi = __builtin_fmaf((float)p[2 * cc + 1].x, xv[cc].z, hi);
+            hi = __builtin_fmaf((float)p[2 * cc + 1].y, xv[cc].w, hi);
+        }
+        s24[m][b] = lo;
+        s20[m][b] = hi;
+    };
+    // Per dword of 8 elements. One activation row: its 2 float4 of x, then the 4
+    // weight rows one at a time. Several: the 4 weight rows' pairs once, then the
+    // activation rows one at a time (2 float4 of x live, not 2 M). Each
+    // accumulator sees the same operations in the same order either way.
 #pragma unroll
     for (int c = 0; c < 8; c += 2) {
-        f32x4 xv[2];
+        auto load_x = [&](f32x4 (&xv)[2], int m) {
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) xv[cc] = XLDS ? xl[(c + cc) * 32] : *(const f32x4 *)(xg + (c + cc) * 4);
-        sx = sx + (((xv[0].x + xv[0].y) + (xv[0].z + xv[0].w)) + ((xv[1].x + xv[1].y) + (xv[1].z + xv[1].w)));
+            for (int cc = 0; cc < 2; ++cc)
+                xv[cc] = XLDS ? xl[m * x_row + (c + cc) * 32] : *(const f32x4 *)(xg + m * x_stride + (c + cc) * 4);
+            sx[m] = sx[m] + (((xv[0].x + xv[0].y) + (xv[0].z + xv[0].w)) + ((xv[1].x + xv[1].y) + (xv[1].z + xv[1].w)));
+        };
+        if constexpr (M == 1) {
+            f32x4 xv[2];
+            load_x(xv, 0);
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-            h2 p[4];
-            q4k_pairs(u.q[b][0][c >> 1], k, p);
-            float lo = s24[b], hi = s20[b];
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                lo = __builtin_fmaf((float)p[2 * cc].x, xv[cc].x, lo);
-                lo = __builtin_fmaf((float)p[2 * cc].y, xv[cc].y, lo);
-                hi = __builtin_fmaf((float)p[2 * cc + 1].x, xv[cc].z, hi);
-                hi = __builtin_fmaf((float)p[2 * cc + 1].y, xv[cc].w, hi);
+            for (int b = 0; b < B; ++b) {
+                h2 p[4];
+                q4k_pairs(u.q[b][0][c >> 1], k, p);
+                row_fma(p, xv, 0, b);
             }
-            s24[b] = lo;
-            s20[b] = hi;
+        } else {
+            h2 p[B][4];
+#pragma unroll
+            for (int b = 0; b < B; ++b) q4k_pairs(u.q[b][0][c >> 1], k, p[b]);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                f32x4 xv[2];
+                load_x(xv, m);
+#pragma unroll
+                for (int b = 0; b < B; ++b) row_fma(p[b], xv, m, b);
+            }
         }
     }
 #pragma unroll
@@ -186,42 +216,51 @@ __device__ __forceinline__ void compute_unit_q4k(const Unit<kQ4_K> &u, float (&a
         const h2 dd = as_h2(u.sup[b]);                                        // (d, dmin)
         const float scl = live ? (float)dd.x * (float)(sw & 0xFFu) * 16777216.0f : 0.0f;
         const float mnv = live ? (float)dd.y * (float)((sw >> 8) & 0xFFu) : 0.0f;
-        const float sq = __builtin_fmaf(s20[b], 0.0625f, s24[b]);   // sum q x * 2^-24
-        acc[0][b] = acc[0][b] + __builtin_fmaf(scl, sq, -(mnv * sx));
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float sq = __builtin_fmaf(s20[m][b], 0.0625f, s24[m][b]);   // sum q x * 2^-24
+            acc[m][b] = acc[m][b] + __builtin_fmaf(scl, sq, -(mnv * sx[m]));
+        }
     }
 }
 
-// Q6_K: acc[0][b] += d * (sc_lo * sum_{e<16} v_e x_e + sc_hi * sum_{e>=16} v_e x_e)
+// Q6_K: acc[m][b] += d * (sc_lo * sum_{e<16} v_e x_e + sc_hi * sum_{e>=16} v_e x_e)
 // with v = q - 32 exact in fp16: the low nibble goes into a magic-number fp16
 // (1024 + q or 1024 + 16 q) as in Q4_0 and the high 2 bits are OR-ed in above it
 // from the row's dword of high parts (a shift by 0 / 2 for the first 16 elements'
 // dword halves, a rotation by 24 and a shift by 2 for the second), then -1056 or
-// (/16 - 96). One fp32 fma per weight, as for Q4_0; the int8 scales are exact
-// in fp32. Dead lanes of a ragged segment get d = 0.
-template <bool XLDS>
-__device__ __forceinline__ void compute_unit_q6k(const Unit<kQ6_K> &u, float (&acc)[1][kRowsPerLane],
+// (/16 - 96). One fp32 fma per weight and row, as for Q4_0; the int8 scales are
+// exact in fp32. Dead lanes of a ragged segment get d = 0. Every activation row
+// goes through the same operations for any M.
+template <int M, bool XLDS>
+__device__ __forceinline__ void compute_unit_q6k(const Unit<kQ6_K> &u, float (&acc)[M][kRowsPerLane],
                                                  const Consts &k, const f32x4 *xs4, const float *__restrict__ x,
-                                                 int64_t s, int j, bool live)
+                                                 int64_t x_stride, int64_t nseg, int64_t s, int j, bool live)
 {
     constexpr int B = kRowsPerLane;
-    float s16[B][2];
+    float s16[M][B][2];
 #pragma unroll
-    for (int b = 0; b < B; ++b) s16[b][0] = s16[b][1] = 0.0f;
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int b = 0; b < B; ++b) s16[m][b][0] = s16[m][b][1] = 0.0f;
+    const uint32_t x_row = (uint32_t)nseg << 8;
     const f32x4 *xl = xs4 + ((uint32_t)s << 8) + (uint32_t)j;
     const float *xg = x + s * kSegWeights + j * 32;
+    // Per dword of 8 elements, in the same two loop orders as Q4_K above.
 #pragma unroll
     for (int c = 0; c < 8; c += 2) {
-        f32x4 xv[2];
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) xv[cc] = XLDS ? xl[(c + cc) * 32] : *(const f32x4 *)(xg + (c + cc) * 4);
         const int dw = c >> 1;   // dword of 8 elements: 8 dw .. 8 dw + 7
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
+        auto pairs = [&](h2 (&p)[4], int b) {
             const u32x4 &hv = u.hq[b >> 1];
-            const uint32_t hd = hv[2 * (b & 1) + (dw >> 1)];
-            h2 p[4];
-            q6k_pairs(u.q[b][0][dw], hd, (dw & 1) != 0, k, p);
-            float s_ = s16[b][dw >> 1];
+            q6k_pairs(u.q[b][0][dw], hv[2 * (b & 1) + (dw >> 1)], (dw & 1) != 0, k, p);
+        };
+        auto load_x = [&](f32x4 (&xv)[2], int m) {
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+                xv[cc] = XLDS ? xl[m * x_row + (c + cc) * 32] : *(const f32x4 *)(xg + m * x_stride + (c + cc) * 4);
+        };
+        auto row_fma = [&](const h2 (&p)[4], const f32x4 (&xv)[2], int m, int b) {
+            float s_ = s16[m][b][dw >> 1];
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 s_ = __builtin_fmaf((float)p[2 * cc].x, xv[cc].x, s_);
@@ -229,7 +268,28 @@ __device__ __forceinline__ void compute_unit_q6k(const Unit<kQ6_K> &u, float (&a
                 s_ = __builtin_fmaf((float)p[2 * cc + 1].x, xv[cc].z, s_);
                 s_ = __builtin_fmaf((float)p[2 * cc + 1].y, xv[cc].w, s_);
             }
-            s16[b][dw >> 1] = s_;
+            s16[m][b][dw >> 1] = s_;
+        };
+        if constexpr (M == 1) {
+            f32x4 xv[2];
+            load_x(xv, 0);
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                h2 p[4];
+                pairs(p, b);
+                row_fma(p, xv, 0, b);
+            }
+        } else {
+            h2 p[B][4];
+#pragma unroll
+            for (int b = 0; b < B; ++b) pairs(p[b], b);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                f32x4 xv[2];
+                load_x(xv, m);
+#pragma unroll
+                for (int b = 0; b < B; ++b) row_fma(p[b], xv, m, b);
+            }
         }
     }
 #pragma unroll
@@ -239,7 +299,9 @@ __device__ __forceinline__ void compute_unit_q6k(const Unit<kQ6_K> &u, float (&a
         const float sc_hi = (float)(int8_t)((sw >> 8) & 0xFFu);
         const uint32_t dw = ((b < 2) ? u.sup.x : u.sup.y) >> (16 * (b & 1));
         const float d = live ? (float)as_h2(dw).x : 0.0f;
-        acc[0][b] = __builtin_fmaf(d, __builtin_fmaf(sc_hi, s16[b][1], sc_lo * s16[b][0]), acc[0][b]);
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            acc[m][b] = __builtin_fmaf(d, __builtin_fmaf(sc_hi, s16[m][b][1], sc_lo * s16[m][b][0]), acc[m][b]);
     }
 }
 
@@ -249,13 +311,11 @@ __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][
                                              int64_t nseg, int64_t s, int j, bool live)
 {
     if constexpr (QT == kQ4_K) {
-        static_assert(M == 1, "Q4_K has the single-row GEMV only");
-        compute_unit_q4k<XLDS>(u, acc, k, xs4, x, s, j, live);
+        compute_unit_q4k<M, XLDS>(u, acc, k, xs4, x, x_stride, nseg, s, j, live);
         return;
     }
     if constexpr (QT == kQ6_K) {
-        static_assert(M == 1, "Q6_K has the single-row GEMV only");
-        compute_unit_q6k<XLDS>(u, acc, k, xs4, x, s, j, live);
+        compute_unit_q6k<M, XLDS>(u, acc, k, xs4, x, x_stride, nseg, s, j, live);
         return;
     }
     constexpr int B = kRowsPerLane;
@@ -1036,12 +1096,8 @@ hipError_t launch_qgemv(int qt, int M, int epi, const QPlan &p, const uint8_t *w
                         const QArgs &a, hipStream_t s)
 {
     if (qt == kQ8_0) return dispatch_m<kQ8_0>(wp, x, y, a, M, epi, p, s);
-    if (qt == kQ4_K || qt == kQ6_K) {
-        // the plain single-row GEMV only (the C ABI refuses the other forms)
-        if (M != 1 || epi != kEpiPlain || p.norm) return hipErrorInvalidValue;
-        return qt == kQ4_K ? dispatch_form<kQ4_K, 1, kEpiPlain>(wp, x, y, a, p, s)
-                           : dispatch_form<kQ6_K, 1, kEpiPlain>(wp, x, y, a, p, s);
-    }
+    if (qt == kQ4_K) return dispatch_m<kQ4_K>(wp, x, y, a, M, epi, p, s);
+    if (qt == kQ6_K) return dispatch_m<kQ6_K>(wp, x, y, a, M, epi, p, s);
     return dispatch_m<kQ4_0>(wp, x, y, a, M, epi, p, s);
 }
 

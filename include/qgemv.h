@@ -116,9 +116,11 @@ qg_status qgemv_q4_0(const void *w_packed, const float *x, float *y, int64_t N, 
  * weight = d * sc * q - dmin * mn. Per 32-weight sub-block the product is
  * summed as d*sc * sum(q x) - dmin*mn * sum(x) in fp32 (the two terms can
  * cancel: the rounding scales with sum (|d sc q| + |dmin mn|) |x|).
- * Q4_K packs with qg_pack / qg_pack_rows / qg_pack_host (148 bytes per 256
- * weights) and is accepted by this GEMV only: the other GEMV calls, the verify
- * and the prefill GEMM return QG_EUNSUPPORTED for it. */
+ * Q4_K packs with qg_pack / qg_pack_rows / qg_pack_gateup / qg_pack_host (148
+ * bytes per 256 weights). The other GEMV calls (qgemv_epilogue,
+ * qgemv_fused_gateup_silu, qgemv_verify, qgemv_rmsnorm,
+ * qgemv_rmsnorm_gateup_silu) take it as qtype QG_Q4_K, with the same sums; the
+ * prefill GEMM returns QG_EUNSUPPORTED for it. */
 qg_status qgemv_q4_k(const void *w_packed, const float *x, float *y, int64_t N, int64_t K, void *stream);
 
 /* The same for a packed Q6_K weight (K % 256 == 0). Q6_K is the k-quant block
@@ -130,8 +132,9 @@ qg_status qgemv_q4_k(const void *w_packed, const float *x, float *y, int64_t N, 
  * q = (low (g < 2) or high nibble of ql[64h + 32(g%2) + l]) | (bits 2g..2g+1 of
  * qh[32h + l]) << 4, weight = d * sc[i/16] * (q - 32). The quants are dequantised
  * exactly (fp16 q - 32) and each 16-weight sum is scaled by its sc, then d.
- * Packs with qg_pack / qg_pack_rows / qg_pack_host (210 bytes per 256 weights,
- * as canonical); like Q4_K it is accepted by this GEMV only. */
+ * Packs with qg_pack / qg_pack_rows / qg_pack_gateup / qg_pack_host (210 bytes
+ * per 256 weights, as canonical); like Q4_K it is taken by every other GEMV
+ * call (qtype QG_Q6_K) but not by the prefill GEMM. */
 qg_status qgemv_q6_k(const void *w_packed, const float *x, float *y, int64_t N, int64_t K, void *stream);
 
 /* Output element type of qgemv_epilogue. */

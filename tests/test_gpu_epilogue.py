@@ -6,14 +6,15 @@ and the fp16 output is the fp32 result rounded to nearest even.
 Shapes cover both launch forms of the quantised GEMV: one wavefront group per
 row tile (fused QKV 4096x1024 with its bias; the 1024x2048 O projection split
 two ways along K, with the residual added in place; a ragged 9x1056) and the
-persistent form with K ranges combined in LDS (3300x5120, 640x17408)."""
+persistent form with K ranges combined in LDS (3300x5120, 640x17408); the Q4_K
+and Q6_K weights on two shapes each."""
 import numpy as np
 import pytest
 
 import block_dequant_gemv_amd as qg
 import oracle as O
 from block_dequant_gemv_amd import workloads as W
-from gpu_helpers import THREADS, announce, empty_f32, sync, to_dev, torch_dev
+from gpu_helpers import THREADS, announce, empty_f32, magnitude, sync, to_dev, torch_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -39,8 +40,8 @@ def _out(torch, n, f16, fill):
     return t
 
 
-@pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
-@pytest.mark.parametrize("N,K", SHAPES)
+@pytest.mark.parametrize("kind,N,K", [(k, n, kk) for k in ("q8_0", "q4_0") for n, kk in SHAPES] +
+                         [("q4_k", 4096, 1024), ("q4_k", 1024, 2048), ("q6_k", 3300, 5120), ("q6_k", 640, 17408)])
 def test_epilogue_matches_oracle_and_plain_bits(kind, N, K):
     torch = torch_dev()
     rng = np.random.default_rng(4242 + N + K)
@@ -87,7 +88,8 @@ def test_epilogue_matches_oracle_and_plain_bits(kind, N, K):
     assert got["bias16"].tobytes() == pb.astype(np.float16).tobytes(), f"{ctx}: fp16 rounding (bias)"
 
     # the oracle, with the tolerance widened only by the addends and the fp16 rounding
-    out_b, a = O.gemv_epilogue(kind, canon, x, N, K, bias=bias, threads=THREADS)
+    out_b, _ = O.gemv_epilogue(kind, canon, x, N, K, bias=bias, threads=THREADS)
+    a = magnitude(kind, lambda c: O.gemv_epilogue(kind, c, x, N, K, threads=THREADS)[1], canon)
     _assert_epilogue(got["bias"], out_b, a, ctx + " bias", bias=bias)
     out_r, _ = O.gemv_epilogue(kind, canon, x, N, K, residual=res, threads=THREADS)
     _assert_epilogue(got["res"], out_r, a, ctx + " residual", residual=res)

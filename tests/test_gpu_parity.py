@@ -7,8 +7,8 @@ import pytest
 import block_dequant_gemv_amd as qg
 import oracle as O
 from block_dequant_gemv_amd import workloads as W
-from gpu_helpers import (THREADS, announce, assert_linear, assert_silu, empty_f32, run_qgemv, sync, to_dev,
-                         torch_dev)
+from gpu_helpers import (THREADS, announce, assert_linear, assert_silu, empty_f32, magnitude, run_qgemv, sync,
+                         to_dev, torch_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -101,8 +101,10 @@ def test_q8_0_full_int8_range_and_zero_scales():
     assert_linear(y, y_ref, a_ref, "q8_0 int8 range")
 
 
-@pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
-@pytest.mark.parametrize("N_ff,K", [(1, 32), (7, 1056), (3072, 1024), (300, 5120), (100, 17408), (2101, 5120)])
+@pytest.mark.parametrize("kind,N_ff,K", [(k, n, kk) for k in ("q8_0", "q4_0")
+                                         for n, kk in ((1, 32), (7, 1056), (3072, 1024), (300, 5120), (100, 17408),
+                                                       (2101, 5120))] +
+                         [(k, n, kk) for k in ("q4_k", "q6_k") for n, kk in ((7, 1280), (300, 5120), (2101, 5120))])
 def test_fused_gateup_silu_matches_oracle(kind, N_ff, K):
     rng = np.random.default_rng(77 + N_ff + K)
     gate = W.matrix(kind, N_ff, K, rng)
@@ -115,7 +117,9 @@ def test_fused_gateup_silu_matches_oracle(kind, N_ff, K):
     sync()
     y = y.cpu().numpy()
     assert np.all(y[N_ff:] == -7.0)
-    out, g, u, ag, au = O.gateup_silu(kind, gate, up, x, N_ff, K, threads=THREADS)
+    out, g, u, _, _ = O.gateup_silu(kind, gate, up, x, N_ff, K, threads=THREADS)
+    ag = magnitude(kind, lambda c: O.gemv(kind, c, x, N_ff, K, threads=THREADS)[1], gate)
+    au = magnitude(kind, lambda c: O.gemv(kind, c, x, N_ff, K, threads=THREADS)[1], up)
     assert_silu(y[:N_ff], out, g, u, ag, au, f"gateup {kind} {N_ff}x{K}")
 
 

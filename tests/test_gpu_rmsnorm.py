@@ -16,7 +16,7 @@ import pytest
 import block_dequant_gemv_amd as qg
 import oracle as O
 from block_dequant_gemv_amd import workloads as W
-from gpu_helpers import THREADS, announce, assert_linear, assert_silu, empty_f32, sync, to_dev
+from gpu_helpers import THREADS, announce, assert_linear, assert_silu, empty_f32, magnitude, sync, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -48,8 +48,8 @@ def test_rmsnorm_matches_oracle(K):
 SHAPES = [(4096, 1024), (33, 2080), (3300, 5120), (5120, 17408), (640, 17408)]
 
 
-@pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
-@pytest.mark.parametrize("N,K", SHAPES)
+@pytest.mark.parametrize("kind,N,K", [(k, n, kk) for k in ("q8_0", "q4_0") for n, kk in SHAPES] +
+                         [(k, n, kk) for k in ("q4_k", "q6_k") for n, kk in ((4096, 1024), (3300, 5120), (640, 17408))])
 def test_gemv_rmsnorm_matches_oracle(kind, N, K):
     rng = np.random.default_rng(500 + N + K)
     canon = W.matrix(kind, N, K, rng)
@@ -62,12 +62,14 @@ def test_gemv_rmsnorm_matches_oracle(kind, N, K):
     sync()
     got = y.cpu().numpy()
     assert np.all(got[N:] == -5.0), "wrote past y[N-1]"
-    y_ref, a_ref = O.gemv_rmsnorm(kind, canon, x, g, float(EPS), N, K)
+    y_ref, _ = O.gemv_rmsnorm(kind, canon, x, g, float(EPS), N, K)
+    a_ref = magnitude(kind, lambda c: O.gemv_rmsnorm(kind, c, x, g, float(EPS), N, K)[1], canon)
     assert_linear(got[:N], y_ref, a_ref, f"rmsnorm gemv {kind} {N}x{K}")
 
 
-@pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
-@pytest.mark.parametrize("N_ff,K", [(3072, 1024), (100, 5120), (17408, 5120)])
+@pytest.mark.parametrize("kind,N_ff,K", [(k, n, kk) for k in ("q8_0", "q4_0")
+                                         for n, kk in ((3072, 1024), (100, 5120), (17408, 5120))] +
+                         [(k, 300, 5120) for k in ("q4_k", "q6_k")])
 def test_gateup_rmsnorm_matches_oracle(kind, N_ff, K):
     rng = np.random.default_rng(900 + N_ff + K)
     gate, up = W.matrix(kind, N_ff, K, rng), W.matrix(kind, N_ff, K, rng)
@@ -78,7 +80,9 @@ def test_gateup_rmsnorm_matches_oracle(kind, N_ff, K):
     announce(f"qgemv_rmsnorm_gateup_silu {kind} N_ff={N_ff} K={K}")
     qg.qgemv_rmsnorm_gateup_silu(kind, packed, to_dev(x), to_dev(g), float(EPS), y, N_ff, K)
     sync()
-    out, gg, uu, ag, au = O.gateup_silu_rmsnorm(kind, gate, up, x, g, float(EPS), N_ff, K)
+    out, gg, uu, _, _ = O.gateup_silu_rmsnorm(kind, gate, up, x, g, float(EPS), N_ff, K)
+    ag = magnitude(kind, lambda c: O.gemv_rmsnorm(kind, c, x, g, float(EPS), N_ff, K)[1], gate)
+    au = magnitude(kind, lambda c: O.gemv_rmsnorm(kind, c, x, g, float(EPS), N_ff, K)[1], up)
     assert_silu(y.cpu().numpy(), out, gg, uu, ag, au, f"rmsnorm gate|up {kind} {N_ff}x{K}")
 
 

@@ -6,7 +6,7 @@ import pytest
 import block_dequant_gemv_amd as qg
 import oracle as O
 from block_dequant_gemv_amd import workloads as W
-from gpu_helpers import THREADS, announce, assert_linear, empty_f32, sync, to_dev
+from gpu_helpers import THREADS, announce, assert_linear, empty_f32, magnitude, sync, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -14,7 +14,11 @@ pytestmark = pytest.mark.gpu
 # and two more shapes of the persistent form (the first weight is one too)
 CASES = [("q4_0", 17408, 5120), ("q8_0", 4096, 1024), ("q8_0", 33, 2080), ("q4_0", 9, 1056),
          ("q4_0", 640, 17408), ("q8_0", 100, 3072), ("q4_0", 24, 32768), ("q4_0", 3300, 5120),
-         ("q8_0", 2001, 8288)]
+         ("q8_0", 2001, 8288),
+         # the super-block types: one tile per wavefront group, K split four ways
+         # (200x4096), the persistent form (2001x8448 with an 8-block last segment)
+         ("q4_k", 1000, 1024), ("q4_k", 200, 4096), ("q4_k", 2001, 8448),
+         ("q6_k", 1000, 1024), ("q6_k", 200, 4096), ("q6_k", 3300, 5120)]
 
 
 @pytest.mark.parametrize("kind,N,K", CASES)
@@ -42,7 +46,8 @@ def test_verify_rows_bit_identical_to_m1(kind, N, K):
         assert np.all(Yh[M * N:] == 3.0), "wrote past Y[M-1][N-1]"
         for m in range(M):
             assert Yh[m * N:(m + 1) * N].tobytes() == ones[m].tobytes(), f"M={M} row {m} differs from M=1"
-    Y_ref, A_ref = O.verify(kind, canon, X, N, K, threads=THREADS)
+    Y_ref, _ = O.verify(kind, canon, X, N, K, threads=THREADS)
+    A_ref = magnitude(kind, lambda c: O.verify(kind, c, X, N, K, threads=THREADS)[1], canon)
     for m in range(6):
         assert_linear(ones[m], Y_ref[m], A_ref[m], f"verify {kind} {N}x{K} row {m}")
 

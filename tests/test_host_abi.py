@@ -112,18 +112,21 @@ def test_argument_checks_return_codes_without_gpu(L):
     # unsupported qtype / row count
     assert call(L, "qgemv_verify", 1, f, f + (1 << 20), f + (2 << 20), 8, 32, 1, null) == qg.QG_EUNSUPPORTED
     assert call(L, "qgemv_verify", 1, f, f + (1 << 20), f + (2 << 20), 8, 32, 7, null) == qg.QG_EUNSUPPORTED
-    assert call(L, "qgemv_verify", 4, f, f + (1 << 20), f + (2 << 20), 8, 32, 2, null) == qg.QG_EUNSUPPORTED
-    # Q4_K: the plain single-row GEMV only, K a multiple of 256
-    assert call(L, "qgemv_verify", qg.Q4_K, f, f + (1 << 20), f + (2 << 20), 8, 256, 2, null) == qg.QG_EUNSUPPORTED
-    assert call(L, "qgemv_fused_gateup_silu", qg.Q4_K, f, f + (1 << 20), f + (2 << 20), 8, 256,
-                null) == qg.QG_EUNSUPPORTED
+    assert call(L, "qgemv_verify", 5, f, f + (1 << 20), f + (2 << 20), 8, 32, 2, null) == qg.QG_EUNSUPPORTED
+    # Q4_K / Q6_K: every GEMV form, K a multiple of 256; not the prefill GEMM
+    for qt in (qg.Q4_K, qg.Q6_K):
+        assert call(L, "qgemv_verify", qt, f, f + (1 << 20), f + (2 << 20), 8, 1056, 2, null) == qg.QG_EINVAL
+        assert call(L, "qgemv_fused_gateup_silu", qt, f, f + (1 << 20), f + (2 << 20), 8, 1056,
+                    null) == qg.QG_EINVAL
+        assert call(L, "qgemv_epilogue", qt, f, f + (1 << 20), null, null, f + (2 << 20), qg.QG_OUT_F32, 8, 1056,
+                    null) == qg.QG_EINVAL
+        assert call(L, "qgemm_prefill", qt, f, f + (1 << 20), f + (2 << 20), 8, 256, 16, f + (3 << 20), 1 << 20,
+                    null) == qg.QG_EUNSUPPORTED
+        assert qg.qg_prefill_workspace_size(qt, 8, 256, 16) == 0
     assert call(L, "qgemv_q4_k", f, f + (1 << 20), f + (2 << 20), 8, 32, null) == qg.QG_EINVAL
     assert call(L, "qgemv_q4_k", f, f + (1 << 20), f + (2 << 20), 8, 1056, null) == qg.QG_EINVAL
     assert call(L, "qgemv_q4_k", f + 8, f + (1 << 20), f + (2 << 20), 8, 256, null) == qg.QG_EALIGN
     assert call(L, "qgemv_q4_k", f, f + (1 << 20), f + (1 << 20), 8, 256, null) == qg.QG_EINVAL
-    assert call(L, "qgemv_verify", qg.Q6_K, f, f + (1 << 20), f + (2 << 20), 8, 256, 2, null) == qg.QG_EUNSUPPORTED
-    assert call(L, "qgemv_fused_gateup_silu", qg.Q6_K, f, f + (1 << 20), f + (2 << 20), 8, 256,
-                null) == qg.QG_EUNSUPPORTED
     assert call(L, "qgemv_q6_k", f, f + (1 << 20), f + (2 << 20), 8, 1056, null) == qg.QG_EINVAL
     assert call(L, "qgemv_q6_k", f + 8, f + (1 << 20), f + (2 << 20), 8, 256, null) == qg.QG_EALIGN
     assert call(L, "qgemv_q6_k", f, f + (1 << 20), f + (1 << 20), 8, 256, null) == qg.QG_EINVAL
@@ -148,7 +151,7 @@ def test_epilogue_argument_checks_without_gpu(L):
     # (qtype, w, x, bias, residual, y, out_type, N, K, stream)
     assert ep(1, None, x, b, r, y, 0, 8, 32, None) == qg.QG_EINVAL          # null weights
     assert ep(1, w, x, b, r, None, 0, 8, 32, None) == qg.QG_EINVAL          # null output
-    assert ep(3, w, x, b, r, y, 0, 8, 32, None) == qg.QG_EUNSUPPORTED       # unknown qtype
+    assert ep(5, w, x, b, r, y, 0, 8, 32, None) == qg.QG_EUNSUPPORTED       # unknown qtype
     assert ep(1, w, x, b, r, y, 2, 8, 32, None) == qg.QG_EUNSUPPORTED       # unknown output type
     assert ep(2, w, x, b, r, y, 0, 8, 48, None) == qg.QG_EINVAL             # K % 32
     assert ep(1, w, x, b + 2, r, y, 0, 8, 32, None) == qg.QG_EALIGN         # bias alignment
@@ -185,7 +188,7 @@ def test_rmsnorm_argument_checks_without_gpu(L):
     assert gn(2, w, x, g, e(-1e-3), y, 8, 32, None) == qg.QG_EINVAL
     assert gn(2, w, x, g, e(1e-6), y, 8, 40960 + 32, None) == qg.QG_EUNSUPPORTED
     assert gn(2, w, x, y - 16, e(1e-6), y, 8, 32, None) == qg.QG_EINVAL   # y overlaps gamma
-    assert gn(4, w, x, g, e(1e-6), y, 8, 32, None) == qg.QG_EUNSUPPORTED
+    assert gn(5, w, x, g, e(1e-6), y, 8, 32, None) == qg.QG_EUNSUPPORTED
     assert gn(1, w, x, g, e(1e-6), y, 8, 48, None) == qg.QG_EINVAL
     # qgemv_rmsnorm_gateup_silu(qtype, w, x, gamma, eps, y, N_ff, K, stream)
     assert gu(1, w, x, g, e(1e-6), y, 0, 32, None) == qg.QG_EINVAL
@@ -217,7 +220,7 @@ def test_gemm_argument_checks_without_gpu(L):
     assert gm(2, w, x, x + 64, 64, 1024, 20, ws, need, None) == qg.QG_EINVAL      # Y overlaps X
     assert gm(2, w, x, y, 64, 1024, 20, y + 256, need, None) == qg.QG_EINVAL      # workspace overlaps Y
     assert gm(2, w, x, y, 64, 1024, 20, x, need, None) == qg.QG_EINVAL            # workspace overlaps X
-    assert gm(3, w, x, y, 64, 1024, 20, ws, need, None) == qg.QG_EUNSUPPORTED     # unknown qtype
+    assert gm(5, w, x, y, 64, 1024, 20, ws, need, None) == qg.QG_EUNSUPPORTED     # unknown qtype
     assert gm(1, w, x, y, 64, 1000, 20, ws, need, None) == qg.QG_EINVAL           # K % 32
 
 
