@@ -305,6 +305,12 @@ def per_config_calls(qg, torch, stream, step_calls):
             keep.append(pk)
             res[6].append(make_qgemv(qg, kind, pk, t(W.activation(K, krng)), yb(N), N, K, stream,
                                      f"k {kind} {label}"))
+            if label.startswith("gate"):
+                # the verify call on the same weight: M = 2..6 activation rows in one weight stream
+                X = t(W.activation(K, krng, M=6))
+                for M in range(2, 7):
+                    res[6].append(make_verify(qg, kind, pk, X, yb(M * N), N, K, M, stream,
+                                              f"k {kind} {N}x{K} M={M}"))
     # the RMSNorm-prologue experiment: each case is (label, weight, bytes, fused(wp), norm(), gemv(wp)), the
     # unfused form being qg_rmsnorm into a separate buffer followed by the plain GEMV on it
     eps = 1e-6
