@@ -25,13 +25,24 @@ struct GemmArgs {
 // most), blocks of 32 weights per staged chunk of K.
 constexpr int kGemmTileM = 16;
 constexpr int kGemmMaxMT = 4;
-constexpr int kGemmChunk = 8;
+constexpr int kGemmChunk = 4;
 
-// LDS of one GEMM workgroup: the chunk's split activations (MT tiles x 2 KiB
-// per block) and the scales of its row tiles (2 slots x 4 rows x fp16 per block).
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left free): the encoding of gfx9-family parts.
+constexpr int kVmcnt0 = 0x0F70;
+
+// 4-byte words of one staged chunk's scales (wg_tiles x 2 slots x kGemmChunk
+// blocks x 8 B), rounded up to whole 64-lane copies.
+constexpr int gemm_scale_words(int wg_tiles)
+{
+    return (wg_tiles * 2 * kGemmChunk * 2 + 63) / 64 * 64;
+}
+
+// LDS of one GEMM workgroup, two buffers (one chunk staged while the other is
+// read) of: the chunk's split activations (MT tiles x 2 KiB per block) and the
+// scales of its row tiles (2 slots x 4 rows x fp16 per block).
 constexpr size_t gemm_lds_bytes(int MT, int wg_tiles)
 {
-    return (size_t)MT * kGemmChunk * 128 * 16 + (size_t)wg_tiles * 2 * kGemmChunk * 8;
+    return 2 * ((size_t)MT * kGemmChunk * 128 * 16 + (size_t)gemm_scale_words(wg_tiles) * 4);
 }
 
 // Y[m][n] = sum over ky (in order) of part[ky][m][n], m < M, n < N.

@@ -117,13 +117,16 @@ __device__ __forceinline__ void group_transpose(uint32_t (&v)[4])
 // The GEMM. A workgroup of G wavefronts owns 16 RG G weight rows: wavefront w
 // covers RG groups of 16 rows (row tiles 2 RG (blockIdx.x G + w) + 2 rg and
 // + 1 for group rg), for the MT 16-row activation tiles [a.mt0, a.mt0 + MT).
-// K is walked in chunks of kGemmChunk blocks. Per chunk the workgroup copies
-// into LDS the chunk's split activations (MT x 2 KiB per block) and the
-// scales of its rows, then each wavefront walks the chunk's blocks in load
-// groups of 4 (Q4_0) or 2 (Q8_0): one 16-byte load per lane and row group
-// (issued one group ahead), the group transpose, the dequant, and per block
-// and activation tile two MFMAs (hi, lo) per row group, each B operand read
-// once from LDS and used by the RG row groups; then acc = fma(d, S, acc).
+// K is walked in chunks of kGemmChunk blocks, staged into two LDS buffers in
+// turn: the chunk's split activations (MT x 2 KiB per block) and the scales of
+// the workgroup's rows are copied with LDS-direct loads (global_load_lds, no
+// registers) one chunk ahead, so the copy of chunk c + 1 runs under the
+// matrix-core work of chunk c; one vmcnt wait and one barrier per chunk. Each
+// wavefront walks a chunk's blocks in load groups of 4 (Q4_0) or 2 (Q8_0): one
+// 16-byte load per lane and row group (issued one group ahead, across chunk
+// and segment ends), the group transpose, the dequant, and per block and
+// activation tile two MFMAs (hi, lo) per row group, each B operand read once
+// from LDS and used by the RG row groups; then acc = fma(d, S, acc).
 // Block sums are added per segment of 32 blocks and the segment sums in order.
 // With a.ksplit > 1, workgroup column blockIdx.y takes one range of segments
 // and writes its sums to a.part; launch_ksum then adds the ranges in order.
@@ -136,8 +139,9 @@ qgemm_kernel(const uint8_t *__restrict__ wp, const _Float16 *__restrict__ xs, co
     constexpr int BPG = (QT == kQ8_0) ? 2 : 4;   // blocks per load group
     constexpr int CB = kGemmChunk;               // blocks per staged chunk (a multiple of BPG)
     extern __shared__ u32x4 lds[];
-    u32x4 *lx = lds;                                   // [mt][CB][h][64 lanes] x 16 B
-    u32x2 *lsc = (u32x2 *)(lds + MT * CB * 128);       // [tile of the workgroup][slot][CB] x 4 fp16
+    u32x4 *lx = lds;   // 2 buffers x [mt][CB][h][64 lanes] x 16 B
+    // 2 buffers x [tile of the workgroup][slot][CB] x 4 fp16, in 4-byte words, padded to whole wavefront copies
+    uint32_t *lsc_base = (uint32_t *)(lds + 2 * MT * CB * 128);
 
     const Geometry &g = a.geo;
     const int lane = threadIdx.x & 63;
@@ -146,6 +150,7 @@ qgemm_kernel(const uint8_t *__restrict__ wp, const _Float16 *__restrict__ xs, co
     const int i = lane & 15, c = lane >> 4;
     const int64_t wg_tile0 = (int64_t)blockIdx.x * G * 2 * RG;   // first row tile of the workgroup
     const int wg_tiles = G * 2 * RG;
+    const int lsc_words = gemm_scale_words(wg_tiles);
     const int64_t t_first = wg_tile0 + (int64_t)wave * 2 * RG;    // first row tile of this wavefront
     const int64_t t_last = g.n_tiles - 1;
     const int slotA = (i & 7) >> 2, browA = i & 3;
@@ -181,106 +186,154 @@ qgemm_kernel(const uint8_t *__restrict__ wp, const _Float16 *__restrict__ xs, co
     const int64_t KB = g.KB;
     const int64_t ky = blockIdx.y;
     const int64_t s_begin = g.nseg * ky / a.ksplit, s_end = g.nseg * (ky + 1) / a.ksplit;
-    for (int64_t s = s_begin; s < s_end; ++s) {
-        const int nb = (int)seg_blocks(g, s);
-        const int nch = (nb + CB - 1) / CB;
-        for (int ch = 0; ch < nch; ++ch) {
-            const int j0 = ch * CB;
-            const int nbc = nb - j0 < CB ? nb - j0 : CB;
-            u32x4 raw[RG];
-            load_group(raw, s, nb, j0 / BPG);   // the chunk's first group, ahead of the staging
-            __syncthreads();                     // the previous chunk's LDS is no longer read
-            {
-                // activations: MT tiles x CB blocks x 128 chunks of 16 B (blocks past nbc skipped);
-                // the index splits with shifts, CB being a power of two
-                static_assert((CB & (CB - 1)) == 0, "chunk size must be a power of two");
-                constexpr uint32_t lcb = __builtin_ctz(CB);
-                for (uint32_t u = threadIdx.x; u < MT * CB * 128; u += blockDim.x) {
-                    const uint32_t mt = u >> (lcb + 7), r = u & (CB * 128 - 1);
-                    if ((r >> 7) < (uint32_t)nbc)
-                        lx[u] = *((const u32x4 *)xs + ((a.mt0 + mt) * KB + s * kSegBlocks + j0) * 128 + r);
-                }
-                // scales of the workgroup's tiles: [tile][slot][block] x 8 B (4 rows)
-                for (uint32_t u = threadIdx.x; u < (uint32_t)wg_tiles * 2 * CB; u += blockDim.x) {
-                    const uint32_t tl = u >> (lcb + 1), sl = (u >> lcb) & 1, jj = u & (CB - 1);
-                    if (jj >= (uint32_t)nbc) continue;
-                    int64_t t = wg_tile0 + tl;
-                    t = t < t_last ? t : t_last;
-                    lsc[u] = *(const u32x2 *)(wp + g.scale_off + t * g.tile_s + s * seg_s +
-                                              (int64_t)(sl * nb + j0 + jj) * (kRowsPerLane * 2));
-                }
+    // The K range as a flat sequence of chunks of CB blocks: every segment but the
+    // matrix's last holds 32 / CB of them.
+    constexpr int CPS = kSegBlocks / CB;
+    struct ChunkPos {
+        int64_t s;
+        int j0, nb, nbc;
+    };
+    auto chunk_at = [&](int64_t c) {
+        ChunkPos p;
+        p.s = s_begin + c / CPS;
+        p.j0 = (int)(c % CPS) * CB;
+        p.nb = (int)seg_blocks(g, p.s);
+        p.nbc = p.nb - p.j0 < CB ? p.nb - p.j0 : CB;
+        return p;
+    };
+    const int64_t n_chunks =
+        s_end > s_begin ? (s_end - s_begin - 1) * CPS + (seg_blocks(g, s_end - 1) + CB - 1) / CB : 0;
+
+    // Stage chunk c into buffer `buf` with LDS-direct loads (no registers; they
+    // complete under vmcnt): wavefront w copies 1 KiB pieces w, w + G, ... of the
+    // activations (MT tiles x nbc blocks x 2 KiB, each tile's run contiguous in
+    // the workspace and in LDS), then its share of the scales as 4-byte words
+    // (run (tile, slot) = CB entries of 8 B; words past the chunk's blocks or
+    // past the runs re-read a valid word and land in the padding).
+    auto stage = [&](int buf, int64_t c) {
+        const ChunkPos p = chunk_at(c);
+        u32x4 *lxd = lx + buf * (MT * CB * 128);
+        const int nkib = MT * p.nbc * 2;
+        for (int q = wave; q < nkib; q += G) {
+            const int mt = q / (p.nbc * 2), r = q - mt * (p.nbc * 2);
+            const u32x4 *src =
+                (const u32x4 *)xs + ((a.mt0 + mt) * KB + p.s * kSegBlocks + p.j0) * 128 + r * 64 + lane;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                             (__attribute__((address_space(3))) void *)(lxd + mt * CB * 128 + r * 64),
+                                             16, 0, 0);
+        }
+        uint32_t *lsd = (uint32_t *)(lsc_base + buf * lsc_words);
+        const int nwords = wg_tiles * 2 * CB * 2;
+        for (int q = wave; q * 64 < lsc_words; q += G) {
+            int wi = q * 64 + lane;
+            wi = wi < nwords ? wi : 0;
+            const int run = wi / (2 * CB), within = wi - run * (2 * CB);
+            const int tl = run >> 1, sl = run & 1;
+            int jj = within >> 1;
+            jj = jj < p.nbc ? jj : p.nbc - 1;
+            int64_t t = wg_tile0 + tl;
+            t = t < t_last ? t : t_last;
+            const uint8_t *src = wp + g.scale_off + t * g.tile_s + p.s * seg_s +
+                                 (int64_t)(sl * p.nb + p.j0 + jj) * (kRowsPerLane * 2) + (within & 1) * 4;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                             (__attribute__((address_space(3))) void *)(lsd + q * 64), 4, 0, 0);
+        }
+    };
+
+    u32x4 raw[RG];
+    if (n_chunks > 0) {
+        stage(0, 0);
+        const ChunkPos c0 = chunk_at(0);
+        load_group(raw, c0.s, c0.nb, c0.j0 / BPG);
+    }
+    for (int64_t ci = 0; ci < n_chunks; ++ci) {
+        // chunk ci staged (this wavefront's copies done, then everyone's), and every
+        // wavefront past chunk ci - 1, whose buffer the next chunk now takes
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        __syncthreads();
+        if (ci + 1 < n_chunks) stage((int)((ci + 1) & 1), ci + 1);
+        const ChunkPos cp = chunk_at(ci);
+        const int64_t s = cp.s;
+        const int nb = cp.nb, j0 = cp.j0, nbc = cp.nbc;
+        const u32x4 *lxb = lx + (ci & 1) * (MT * CB * 128);
+        const u32x2 *lscb = (const u32x2 *)(lsc_base + (ci & 1) * lsc_words);
+        const int ngroups = (nbc + BPG - 1) / BPG;
+        for (int qq = 0; qq < ngroups; ++qq) {
+            uint32_t v[RG][4];
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+                v[rg][0] = raw[rg].x;
+                v[rg][1] = raw[rg].y;
+                v[rg][2] = raw[rg].z;
+                v[rg][3] = raw[rg].w;
             }
-            __syncthreads();
-            const int ngroups = (nbc + BPG - 1) / BPG;
-            for (int qq = 0; qq < ngroups; ++qq) {
-                uint32_t v[RG][4];
+            // one group ahead: the next group of this chunk, else the next chunk's first
+            if (qq + 1 < ngroups) {
+                load_group(raw, s, nb, j0 / BPG + qq + 1);
+            } else if (ci + 1 < n_chunks) {
+                const ChunkPos cn = chunk_at(ci + 1);
+                load_group(raw, cn.s, cn.nb, cn.j0 / BPG);
+            }
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) group_transpose(v[rg]);
+#pragma unroll
+            for (int bb = 0; bb < BPG; ++bb) {
+                const int jj = qq * BPG + bb;   // block within the chunk
+                if (jj >= nbc) break;           // wave-uniform
+                h8 A[RG];
+                h2 d01[RG], d23[RG];
 #pragma unroll
                 for (int rg = 0; rg < RG; ++rg) {
-                    v[rg][0] = raw[rg].x;
-                    v[rg][1] = raw[rg].y;
-                    v[rg][2] = raw[rg].z;
-                    v[rg][3] = raw[rg].w;
+                    if (QT == kQ4_0) {
+                        h2 p[4];
+                        q4_pairs(v[rg][bb], k, p);
+                        A[rg] = h8{p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
+                    } else {
+                        h2 p0[2], p1[2];
+                        q8_pairs(v[rg][2 * bb], p0);
+                        q8_pairs(v[rg][2 * bb + 1], p1);
+                        A[rg] = h8{p0[0].x, p0[0].y, p0[1].x, p0[1].y, p1[0].x, p1[0].y, p1[1].x, p1[1].y};
+                    }
+                    // rows 4c + r of row group rg: tile (wave*RG + rg)*2 + c/2 of the workgroup, slot c%2
+                    const u32x2 dd = lscb[(((wave * RG + rg) * 2 + (c >> 1)) * 2 + (c & 1)) * CB + jj];
+                    d01[rg] = as_h2(dd.x);
+                    d23[rg] = as_h2(dd.y);
                 }
-                if (qq + 1 < ngroups) load_group(raw, s, nb, j0 / BPG + qq + 1);   // one group ahead
 #pragma unroll
-                for (int rg = 0; rg < RG; ++rg) group_transpose(v[rg]);
+                for (int mt = 0; mt < MT; ++mt) {
+                    const h8 bh = __builtin_bit_cast(h8, lxb[(mt * CB + jj) * 128 + lane]);
+                    const h8 bl = __builtin_bit_cast(h8, lxb[(mt * CB + jj) * 128 + 64 + lane]);
+                    f32x4 S[RG];
 #pragma unroll
-                for (int bb = 0; bb < BPG; ++bb) {
-                    const int jj = qq * BPG + bb;   // block within the chunk
-                    if (jj >= nbc) break;           // wave-uniform
-                    h8 A[RG];
-                    h2 d01[RG], d23[RG];
+                    for (int rg = 0; rg < RG; ++rg)
+                        S[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[rg], bh, f32x4{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                       0, 0, 0);
+#pragma unroll
+                    for (int rg = 0; rg < RG; ++rg)
+                        S[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[rg], bl, S[rg], 0, 0, 0);
 #pragma unroll
                     for (int rg = 0; rg < RG; ++rg) {
-                        if (QT == kQ4_0) {
-                            h2 p[4];
-                            q4_pairs(v[rg][bb], k, p);
-                            A[rg] = h8{p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
-                        } else {
-                            h2 p0[2], p1[2];
-                            q8_pairs(v[rg][2 * bb], p0);
-                            q8_pairs(v[rg][2 * bb + 1], p1);
-                            A[rg] = h8{p0[0].x, p0[0].y, p0[1].x, p0[1].y, p1[0].x, p1[0].y, p1[1].x, p1[1].y};
-                        }
-                        // rows 4c + r of row group rg: tile (wave*RG + rg)*2 + c/2 of the workgroup, slot c%2
-                        const u32x2 dd = lsc[(((wave * RG + rg) * 2 + (c >> 1)) * 2 + (c & 1)) * CB + jj];
-                        d01[rg] = as_h2(dd.x);
-                        d23[rg] = as_h2(dd.y);
-                    }
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const h8 bh = __builtin_bit_cast(h8, lx[(mt * CB + jj) * 128 + lane]);
-                        const h8 bl = __builtin_bit_cast(h8, lx[(mt * CB + jj) * 128 + 64 + lane]);
-                        f32x4 S[RG];
-#pragma unroll
-                        for (int rg = 0; rg < RG; ++rg)
-                            S[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[rg], bh, f32x4{0.0f, 0.0f, 0.0f, 0.0f},
-                                                                           0, 0, 0);
-#pragma unroll
-                        for (int rg = 0; rg < RG; ++rg)
-                            S[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[rg], bl, S[rg], 0, 0, 0);
-#pragma unroll
-                        for (int rg = 0; rg < RG; ++rg) {
-                            f32x4 &acc = seg[rg][mt];
-                            acc.x = __builtin_fmaf((float)d01[rg].x, S[rg].x, acc.x);
-                            acc.y = __builtin_fmaf((float)d01[rg].y, S[rg].y, acc.y);
-                            acc.z = __builtin_fmaf((float)d23[rg].x, S[rg].z, acc.z);
-                            acc.w = __builtin_fmaf((float)d23[rg].y, S[rg].w, acc.w);
-                        }
+                        f32x4 &acc = seg[rg][mt];
+                        acc.x = __builtin_fmaf((float)d01[rg].x, S[rg].x, acc.x);
+                        acc.y = __builtin_fmaf((float)d01[rg].y, S[rg].y, acc.y);
+                        acc.z = __builtin_fmaf((float)d23[rg].x, S[rg].z, acc.z);
+                        acc.w = __builtin_fmaf((float)d23[rg].y, S[rg].w, acc.w);
                     }
                 }
             }
         }
+        if (j0 + nbc == nb) {   // the segment's last chunk: add its sum, in segment order
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg)
+            for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                tot[rg][mt].x += seg[rg][mt].x;
-                tot[rg][mt].y += seg[rg][mt].y;
-                tot[rg][mt].z += seg[rg][mt].z;
-                tot[rg][mt].w += seg[rg][mt].w;
-                seg[rg][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            }
+                for (int mt = 0; mt < MT; ++mt) {
+                    tot[rg][mt].x += seg[rg][mt].x;
+                    tot[rg][mt].y += seg[rg][mt].y;
+                    tot[rg][mt].z += seg[rg][mt].z;
+                    tot[rg][mt].w += seg[rg][mt].w;
+                    seg[rg][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                }
+        }
     }
 
 #pragma unroll

@@ -394,10 +394,10 @@ GemmPlan plan_gemm(int qt, int64_t N, int64_t K, int64_t M)
     p.RG = wgs_rg2 * g.nseg >= 2 * (int64_t)cu_count() ? 2 : 1;
     const int64_t rg_env = tune(kGemmRowGroups);
     if (rg_env == 1 || rg_env == 2 || rg_env == 4) p.RG = (int)rg_env;
-    // activation tiles per pass: 4 for Q8_0 (its heavier weight stream favours fewer passes:
-    // LM head 151936x1024 at M = 128, 431 -> 312 us), 2 for Q4_0 (4 cost occupancy there:
-    // 17408x5120 at M = 128, 164 -> 201 us)
-    p.MT = qt == QG_Q8_0 ? 4 : 2;
+    // activation tiles per pass: 4, i.e. the weights are streamed once per 64 activation rows
+    // (measured with the double-buffered staging, cold, against 2: Q4_0 LM head 248320x5120
+    // at M = 128 1300 -> 1100 us, 17408x5120 138 -> 132 us; Q8_0 4096x1024 74 -> 50 us)
+    p.MT = 4;
     const int64_t mt_env = tune(kGemmMT);
     if (mt_env >= 1 && mt_env <= qgk::kGemmMaxMT) p.MT = (int)mt_env;
     const int64_t wgs = (g.n_tiles + 2 * p.RG * p.G - 1) / (2 * p.RG * p.G);
