@@ -35,6 +35,7 @@
 #include "dequant.h"
 #include "layout.h"
 #include "qgemm_kernels.h"
+#include "qgemv_kernels.h"
 
 namespace qgk {
 
@@ -394,10 +395,9 @@ static hipError_t launch_one(const uint8_t *wp, const _Float16 *xs, const float 
     const int64_t grid = (a.geo.n_tiles + 2 * RG * G - 1) / (2 * RG * G);
     const dim3 grid3((unsigned)grid, (unsigned)a.ksplit);
     const size_t lds = gemm_lds_bytes(MT, G * 2 * RG);
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    static std::atomic<int> lds_set[16];
+    hipError_t e = ensure_lds_limit((const void *)kern, lds, lds_set);
+    if (e != hipSuccess) return e;
     launch_timed(kern, grid3, dim3(64 * G), (uint32_t)lds, s, wp, xs, unscale, Y, a);
     return hipGetLastError();
 }

@@ -2,6 +2,8 @@
 // the kernels (qgemv_kernels.hip). Not installed; not part of the public ABI.
 #pragma once
 
+#include <atomic>
+
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -91,6 +93,28 @@ constexpr int persist_threads(int qt, int M, bool xlds)
     if (qt == qgl::kQ4_0) return (M <= 4 || xlds) ? 768 : 512;
     if (qt == qgl::kQ4_K || qt == qgl::kQ6_K) return M <= 2 ? 768 : 512;
     return (M <= 3 || (M == 4 && xlds)) ? 768 : 512;
+}
+
+// Raise a kernel's dynamic-LDS limit to `bytes` (needed above 64 KiB) unless it is
+// already that high on the current device. `set` is the caller's record for that
+// one kernel (one per template instantiation), so a decode loop pays for the
+// attribute call once per kernel and device, not once per launch.
+inline hipError_t ensure_lds_limit(const void *kern, size_t bytes, std::atomic<int> (&set)[16])
+{
+    if (bytes <= 64 * 1024) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::atomic<int> *rec = (dev >= 0 && dev < 16) ? &set[dev] : nullptr;
+    if (rec && rec->load(std::memory_order_relaxed) >= (int)bytes) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return e;
+    if (rec) {
+        int cur = rec->load(std::memory_order_relaxed);
+        while (cur < (int)bytes && !rec->compare_exchange_weak(cur, (int)bytes)) {
+        }
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_qgemv(int qt, int M, int epi, const QPlan &p, const uint8_t *wp, const float *x, float *y,

@@ -1001,10 +1001,9 @@ static hipError_t launch_q(const uint8_t *wp, const float *x, float *y, const QA
                            size_t lds, hipStream_t stream)
 {
     auto kern = qgemv_kernel<QT, M, EPI, W, XLDS, D, NORM>;
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    static std::atomic<int> lds_set[16];
+    hipError_t e = ensure_lds_limit((const void *)kern, lds, lds_set);
+    if (e != hipSuccess) return e;
     launch(kern, dim3((unsigned)grid), dim3(block), (uint32_t)lds, stream, wp, x, y, a);
     return hipGetLastError();
 }
@@ -1059,11 +1058,9 @@ static hipError_t launch_persist(const uint8_t *wp, const float *x, float *y, co
         }
     }
     if (p.block != persist_threads(QT, M, p.x_in_lds)) return hipErrorInvalidConfiguration;
-    if (p.lds_bytes > 64 * 1024) {
-        hipError_t e =
-            hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_bytes);
-        if (e != hipSuccess) return e;
-    }
+    static std::atomic<int> lds_set[3][16];   // one record per kernel chosen above
+    hipError_t e = ensure_lds_limit((const void *)kern, p.lds_bytes, lds_set[p.norm ? 2 : (p.x_in_lds ? 0 : 1)]);
+    if (e != hipSuccess) return e;
     launch(kern, dim3((unsigned)p.grid), dim3(p.block), (uint32_t)p.lds_bytes, stream, wp, x, y, a);
     return hipGetLastError();
 }
