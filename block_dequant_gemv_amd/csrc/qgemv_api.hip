@@ -116,16 +116,21 @@ int64_t tune(TuneKey k)
 // Wavefronts that split one tile along K. Depends only on (rows, K): a matrix
 // with few row tiles gets more wavefronts per tile so that the chip has enough
 // loads in flight. The decode and the verify call of the same weight always
-// get the same split, and so add in the same order. (QG_SPLIT_K overrides it
-// for launch-shape sweeps; it must then be the same for every call.)
+// get the same split, and so add in the same order. A tile of three segments
+// gets three wavefronts, one segment each: with two, one of them computes two
+// segments in a row, which made the 1024x3072 down projection about 1.1 us
+// slower back to back (measured). (QG_SPLIT_K overrides the choice for
+// launch-shape sweeps; it must then be the same for every call.)
 int split_k_waves(int64_t rows, int64_t K)
 {
     const int64_t n_tiles = (rows + qgl::kTileRows - 1) / qgl::kTileRows;
     const int64_t nseg = (K / 32 + qgl::kSegBlocks - 1) / qgl::kSegBlocks;
     const int64_t forced = tune(kSplitK);
-    if (forced == 1 || forced == 2 || forced == 4 || forced == 8) return forced <= nseg ? (int)forced : 1;
+    if (forced == 1 || forced == 2 || forced == 3 || forced == 4 || forced == 8)
+        return forced <= nseg ? (int)forced : 1;
     int W = 1;
     while (W < 4 && 2 * W <= nseg && n_tiles * W < 2048) W *= 2;
+    if (W == 2 && nseg == 3) W = 3;
     return W;
 }
 

@@ -45,7 +45,7 @@ struct QPlan {
     bool persist;        // persistent form: one workgroup per CU, (tile, K range) items
     int ranges;          // persistent form: K ranges per tile (divides nseg)
     int64_t max_tiles;   // persistent form: most tiles any workgroup owns
-    int W;               // classic form: wavefronts splitting one row tile along K (1, 2, 4, 8)
+    int W;               // classic form: wavefronts splitting one row tile along K (1, 2, 3, 4, 8)
     int64_t tpg;         // tiles per group (contiguous order)
     int64_t tstride;     // > 0: grid-stride tile order over this many groups (tpg unused)
     int64_t grid;        // workgroups

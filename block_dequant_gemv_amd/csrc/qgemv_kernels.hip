@@ -551,7 +551,7 @@ __device__ __forceinline__ void store_tile(const float (&acc)[M][kRowsPerLane], 
 //   M    activation rows (1 = decode GEMV, 2..6 = verify)
 //   EPI  kEpiPlain (y = W x), kEpiGateUp (y = silu(gate) * up, M = 1) or
 //        kEpiAffine (y = ((W x) + bias) + residual, fp32 or fp16, M = 1)
-//   W    wavefronts that split one row tile along K (1, 2, 4 or 8)
+//   W    wavefronts that split one row tile along K (1, 2, 3, 4 or 8)
 //   XLDS activations staged in LDS (true) or read from global memory
 // W == 1: a workgroup holds blockDim/64 independent wavefronts; wavefront g of
 //         workgroup b is group b*G + g.
@@ -1038,6 +1038,7 @@ static hipError_t dispatch_w(const uint8_t *wp, const float *x, float *y, const 
     switch (W) {
     case 1: return dispatch_x<QT, M, EPI, 1>(wp, x, y, a, grid, block, lds, xlds, depth, norm, s);
     case 2: return dispatch_x<QT, M, EPI, 2>(wp, x, y, a, grid, block, lds, xlds, depth, norm, s);
+    case 3: return dispatch_x<QT, M, EPI, 3>(wp, x, y, a, grid, block, lds, xlds, depth, norm, s);
     case 4: return dispatch_x<QT, M, EPI, 4>(wp, x, y, a, grid, block, lds, xlds, depth, norm, s);
     default: return dispatch_x<QT, M, EPI, 8>(wp, x, y, a, grid, block, lds, xlds, depth, norm, s);
     }

@@ -156,7 +156,7 @@ def test_kquant_forced_launch_shapes(kind, N, K):
     combos = [dict(QG_PERSIST=1, QG_X_GLOBAL=xg) for xg in (0, 1)]
     combos += [dict(QG_PERSIST=0, QG_STRIDE_GROUPS=3, QG_WAVES_PER_WG=1, QG_SPLIT_K=split)
                for split in (1, 2) if split <= nseg]
-    for split, xg, wpw, tpg, pf in itertools.product((1, 2, 4, 8), (0, 1), (1, 2, 4), (1, 3), (1, 2)):
+    for split, xg, wpw, tpg, pf in itertools.product((1, 2, 3, 4, 8), (0, 1), (1, 2, 4), (1, 3), (1, 2)):
         if split > nseg or (split > 1 and wpw != 4):
             continue
         combos.append(dict(QG_PERSIST=0, QG_SPLIT_K=split, QG_X_GLOBAL=xg, QG_WAVES_PER_WG=wpw,

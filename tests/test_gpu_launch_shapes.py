@@ -47,7 +47,7 @@ def test_forced_launch_shapes(kind, N, K):
     # grid-stride tile order: groups walk tiles g, g + groups, ... (3 groups leave a ragged last round)
     combos += [dict(QG_PERSIST=0, QG_STRIDE_GROUPS=sg, QG_WAVES_PER_WG=1, QG_SPLIT_K=split)
                for sg in (3, 8) for split in (1, 2) if split <= nseg]
-    for split, xg, wpw, tpg, pf in itertools.product((1, 2, 4, 8), (0, 1), (1, 2, 4), (1, 3), (1, 2)):
+    for split, xg, wpw, tpg, pf in itertools.product((1, 2, 3, 4, 8), (0, 1), (1, 2, 4), (1, 3), (1, 2)):
         if split > nseg or (split > 1 and wpw != 4):
             continue
         combos.append(dict(QG_PERSIST=0, QG_SPLIT_K=split, QG_X_GLOBAL=xg, QG_WAVES_PER_WG=wpw,
