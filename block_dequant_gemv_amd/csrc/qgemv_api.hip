@@ -87,17 +87,17 @@ int64_t env_int(const char *name, int64_t dflt)
 // Launch-shape overrides for sweeps and tests (QG_SPLIT_K, QG_PERSIST,
 // QG_X_GLOBAL, QG_TILES_PER_GROUP, QG_WAVES_PER_WG, QG_PREFETCH, QG_F16_ROWS,
 // QG_F16_WAVES, QG_STRIDE_GROUPS, QG_GEMM_MT, QG_GEMM_WAVES, QG_GEMM_ROWGROUPS,
-// QG_GEMM_KSPLIT). They are read from the environment once, on first use, and
+// QG_GEMM_KSPLIT, QG_F16_FORM). They are read from the environment once, on first use, and
 // again on qg_reload_tuning(): a GEMV call itself reads no environment.
 enum TuneKey {
     kSplitK, kPersist, kXGlobal, kTilesPerGroup, kWavesPerWg, kPrefetch, kF16Rows, kF16Waves, kStrideGroups,
-    kGemmMT, kGemmWaves, kGemmRowGroups, kGemmKSplit, kNumTune
+    kGemmMT, kGemmWaves, kGemmRowGroups, kGemmKSplit, kF16Form, kNumTune
 };
 const char *const kTuneNames[kNumTune] = {"QG_SPLIT_K",      "QG_PERSIST",  "QG_X_GLOBAL",  "QG_TILES_PER_GROUP",
                                           "QG_WAVES_PER_WG", "QG_PREFETCH", "QG_F16_ROWS",  "QG_F16_WAVES",
                                           "QG_STRIDE_GROUPS", "QG_GEMM_MT", "QG_GEMM_WAVES", "QG_GEMM_ROWGROUPS",
-                                          "QG_GEMM_KSPLIT"};
-const int64_t kTuneDefaults[kNumTune] = {0, -1, -1, 0, 0, 0, 0, 0, -1, 0, 0, 0, 0};
+                                          "QG_GEMM_KSPLIT", "QG_F16_FORM"};
+const int64_t kTuneDefaults[kNumTune] = {0, -1, -1, 0, 0, 0, 0, 0, -1, 0, 0, 0, 0, -1};
 std::atomic<int64_t> g_tune[kNumTune];
 std::atomic<bool> g_tune_loaded{false};
 
@@ -676,16 +676,37 @@ qg_status gemv_f16_splitk(const void *w_f16, const float *x, float *y, int64_t N
 
     qgk::F16Plan p;
     p.vec = (K % 8 == 0) && aligned(w_f16, 16) && aligned(x, 16);
-    // One row per workgroup; one wavefront per row when there are enough rows to
-    // cover the CUs (each lane walks K/512 16-byte chunks of its row), four
-    // otherwise (measured on MI355X, cold: 5120 x 5120 10.1 us, 256 x 5120 and
-    // 48 x 5120 3.9 us, against 10.8 / 5.1 / 4.7 us for register-blocked rows).
+    p.L = 0;
+    const int64_t w_env = tune(kF16Waves);
+    // Row form (one wavefront per row, the whole row's loads in flight at once,
+    // x from LDS) wherever K = 512 L, L <= 16: 4 rows per workgroup, 2 below
+    // 1024 rows. Measured on MI355X, cold, against the split-K form: 5120 x 5120
+    // 9.96 against 10.78 us, 5120 x 8192 15.3 against 17.2, 17408 x 4096 22.4
+    // against 27.0; 256 and 48 rows x 5120 the same (3.9 us, the dispatch
+    // floor) and a little faster back to back. QG_F16_FORM = 0 / 1 forces the
+    // split-K / row form (the latter where K allows it), QG_F16_WAVES = 2, 4, 8
+    // the rows per workgroup.
+    const int64_t form = tune(kF16Form);
+    const bool row_ok = p.vec && K % 512 == 0 && K / 512 <= qgk::kF16RowMaxL;
+    if (row_ok && form != 0) {
+        p.L = (int)(K / 512);
+        p.R = 1;
+        p.waves = (w_env == 2 || w_env == 4 || w_env == 8) ? (int)w_env : (N < 1024 ? 2 : 4);
+        p.grid = (N + p.waves - 1) / p.waves;
+        hipError_t e = qgk::launch_f16(p, (const uint16_t *)w_f16, x, y, N, K, as_stream(stream));
+        if (e != hipSuccess) return hip_fail(e, fn);
+        return ok();
+    }
+    // Split-K form (other K, or unaligned): one row per workgroup; one
+    // wavefront per row when there are enough rows to cover the CUs (each lane
+    // walks K/512 16-byte chunks of its row), four otherwise (measured on
+    // MI355X, cold: 256 x 5120 and 48 x 5120 3.9 us, against 5.1 / 4.7 us for
+    // register-blocked rows).
     // QG_F16_ROWS (1, 2, 4) and QG_F16_WAVES override the shape for sweeps.
     p.R = 1;
     const int64_t r_env = tune(kF16Rows);
     if (r_env == 1 || r_env == 2 || r_env == 4) p.R = (int)r_env;
     int64_t waves = N >= 1024 ? 1 : 4;
-    const int64_t w_env = tune(kF16Waves);
     if (w_env > 0) waves = w_env;
     if (waves > 16) waves = 16;
     if (waves < 1) waves = 1;

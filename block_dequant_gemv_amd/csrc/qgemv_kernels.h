@@ -57,11 +57,16 @@ struct QPlan {
 };
 
 struct F16Plan {
-    int R;               // rows per workgroup (register-blocked)
-    int waves;           // wavefronts per workgroup splitting K
+    int R;               // split-K form: rows per workgroup (register-blocked)
+    int waves;           // split-K form: wavefronts splitting K; row form: rows (wavefronts) per workgroup
     bool vec;            // 16-byte path (K % 8 == 0 and aligned pointers)
+    int L;               // 0: split-K form; 1..kF16RowMaxL: row form for K = 512 * L
     int64_t grid;
 };
+
+// The fp16 row form takes rows of K = 512 * L weights, L <= 16: each lane holds
+// L 16-byte chunks of its row at once (4 L registers).
+constexpr int kF16RowMaxL = 16;
 
 // Two timing events bound to the next GEMV kernel this thread launches: they
 // receive that kernel's own start and end timestamps. The launch takes them

@@ -916,6 +916,71 @@ gemv_f16_kernel(const uint16_t *__restrict__ w, const float *__restrict__ x, flo
 }
 
 // ---------------------------------------------------------------------------
+// fp16 GEMV, row form, for K = 512 * L: wavefront g of a workgroup of G owns
+// row blockIdx * G + g. Every thread first issues its share of x (K / 4
+// float4, at most XN per thread), then the wavefront issues all L of its row's
+// 1 KiB loads (lane l takes the 16-byte chunks l, l + 64, ..., l + 64 (L - 1));
+// loads complete in issue order, so writing x to LDS waits for x alone and the
+// barrier passes while the weights are still in flight. x goes to LDS as two
+// planes: float4 c of plane 0 holds x[8c .. 8c + 3], of plane 1
+// x[8c + 4 .. 8c + 7], so each lane reads 16 contiguous bytes from each plane
+// for its chunk c. A lane's sum is one fma chain over its chunks in order (8
+// products each), then the wavefront butterfly: at most 8 L + 6 = 134
+// roundings deep. Wavefronts past the last row load row N - 1 and store
+// nothing.
+template <int L, int G>
+__global__ void __launch_bounds__(64 * G)
+gemv_f16_row_kernel(const uint16_t *__restrict__ w, const float *__restrict__ x, float *__restrict__ y, int64_t N,
+                    int64_t K)
+{
+    constexpr uint32_t kChunks = 64 * L;                     // 16-byte chunks per row
+    constexpr uint32_t kX4 = 2 * kChunks;                    // float4 of x
+    constexpr uint32_t XN = (kX4 + 64 * G - 1) / (64 * G);   // x float4 per thread
+    extern __shared__ f32x4 xp[];                            // [2][kChunks]
+    const uint32_t tid = threadIdx.x, lane = tid & 63;
+    const int64_t row_raw = (int64_t)blockIdx.x * G + (tid >> 6);
+    const bool live = row_raw < N;
+    const int64_t row = live ? row_raw : N - 1;
+    const u32x4 *wr = (const u32x4 *)(w + row * K);
+    const f32x4 *x4 = (const f32x4 *)x;
+
+    f32x4 xv[XN];
+#pragma unroll
+    for (uint32_t r = 0; r < XN; ++r) {
+        const uint32_t q = tid + r * 64 * G;
+        xv[r] = x4[q < kX4 ? q : 0u];
+    }
+    u32x4 v[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) v[i] = __builtin_nontemporal_load(wr + lane + 64 * i);
+#pragma unroll
+    for (uint32_t r = 0; r < XN; ++r) {
+        const uint32_t q = tid + r * 64 * G;
+        if (q < kX4) xp[(q & 1) * kChunks + (q >> 1)] = xv[r];
+    }
+    __syncthreads();
+
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        const uint32_t c = lane + 64 * i;
+        const f32x4 xa = xp[c], xb = xp[kChunks + c];
+        const h2 p0 = as_h2(v[i].x), p1 = as_h2(v[i].y), p2 = as_h2(v[i].z), p3 = as_h2(v[i].w);
+        acc = __builtin_fmaf((float)p0.x, xa.x, acc);
+        acc = __builtin_fmaf((float)p0.y, xa.y, acc);
+        acc = __builtin_fmaf((float)p1.x, xa.z, acc);
+        acc = __builtin_fmaf((float)p1.y, xa.w, acc);
+        acc = __builtin_fmaf((float)p2.x, xb.x, acc);
+        acc = __builtin_fmaf((float)p2.y, xb.y, acc);
+        acc = __builtin_fmaf((float)p3.x, xb.z, acc);
+        acc = __builtin_fmaf((float)p3.y, xb.w, acc);
+    }
+    const float h = half_wave_sum(acc);
+    const float tot = as_f(__builtin_amdgcn_readlane(as_i(h), 0)) + as_f(__builtin_amdgcn_readlane(as_i(h), 32));
+    if (live && lane == 0) y[row] = tot;
+}
+
+// ---------------------------------------------------------------------------
 // Standalone RMSNorm of one activation vector (one workgroup): out[k] =
 // (x[k] * r) * gamma[k], r = 1 / sqrt(sum(x^2) / K + eps), with the same
 // reduction scheme as the GEMV prologue.
@@ -1110,6 +1175,39 @@ hipError_t launch_f16(const F16Plan &p, const uint16_t *w, const float *x, float
 {
     const dim3 grid((unsigned)p.grid), block(p.waves * 64);
     auto go = [&](auto kern) { launch(kern, grid, block, 0u, s, w, x, y, N, K); };
+    if (p.L > 0) {
+        // row form: K = 512 L, x staged in K * 4 bytes of LDS (at most 32 KiB)
+        if (!p.vec || p.L > kF16RowMaxL || K != 512 * (int64_t)p.L || (p.waves != 2 && p.waves != 4 && p.waves != 8))
+            return hipErrorInvalidConfiguration;
+        auto row = [&](auto kern) { launch(kern, grid, block, (uint32_t)(K * 4), s, w, x, y, N, K); };
+        auto rows = [&](auto lc) {
+            constexpr int Lc = decltype(lc)::value;
+            switch (p.waves) {
+            case 4: row(gemv_f16_row_kernel<Lc, 4>); break;
+            case 8: row(gemv_f16_row_kernel<Lc, 8>); break;
+            default: row(gemv_f16_row_kernel<Lc, 2>); break;
+            }
+        };
+        switch (p.L) {
+        case 1: rows(std::integral_constant<int, 1>{}); break;
+        case 2: rows(std::integral_constant<int, 2>{}); break;
+        case 3: rows(std::integral_constant<int, 3>{}); break;
+        case 4: rows(std::integral_constant<int, 4>{}); break;
+        case 5: rows(std::integral_constant<int, 5>{}); break;
+        case 6: rows(std::integral_constant<int, 6>{}); break;
+        case 7: rows(std::integral_constant<int, 7>{}); break;
+        case 8: rows(std::integral_constant<int, 8>{}); break;
+        case 9: rows(std::integral_constant<int, 9>{}); break;
+        case 10: rows(std::integral_constant<int, 10>{}); break;
+        case 11: rows(std::integral_constant<int, 11>{}); break;
+        case 12: rows(std::integral_constant<int, 12>{}); break;
+        case 13: rows(std::integral_constant<int, 13>{}); break;
+        case 14: rows(std::integral_constant<int, 14>{}); break;
+        case 15: rows(std::integral_constant<int, 15>{}); break;
+        default: rows(std::integral_constant<int, 16>{}); break;
+        }
+        return hipGetLastError();
+    }
     if (p.vec) {
         switch (p.R) {
         case 1: go(gemv_f16_kernel<1, true>); break;

@@ -162,11 +162,14 @@ qg_status qgemv_epilogue(int qtype, const void *w_packed, const float *x, const 
                          const float *residual, void *y, int out_type, int64_t N, int64_t K, void *stream);
 
 /* Unquantised fp16 weights, y = W x with W fp16 row-major [N][K] (any K >= 1,
- * 2-byte aligned; the fast path needs K % 8 == 0 and 16-byte alignment), x fp32
- * [K], y fp32 [N]. K is split across the wavefronts of one workgroup and the
- * partial sums are combined in LDS in a fixed order: deterministic, no
- * workspace, no atomics (robotnurse.io post, What actually moved it, 4: a
- * split-K fp16 GEMV for the unquantised matrices). */
+ * 2-byte aligned; the fast paths need K % 8 == 0 and 16-byte alignment), x fp32
+ * [K], y fp32 [N]. Each row's K is split across the lanes of one wavefront,
+ * and for short matrices across the wavefronts of one workgroup, with the
+ * partial sums combined in a fixed order: deterministic, no workspace, no
+ * atomics (robotnurse.io post, What actually moved it, 4: a split-K fp16 GEMV
+ * for the unquantised matrices). Matrices of at least 1024 rows with
+ * K = 512 L (L <= 16) and the 16-byte alignment run one wavefront per row with
+ * the whole row's loads in flight; others, split K over the wavefronts. */
 qg_status gemv_f16_splitk(const void *w_f16, const float *x, float *y, int64_t N, int64_t K, void *stream);
 
 /* Fused gate+up with the SiLU epilogue (RunIT_Mac README "Fused gate+up+silu",
@@ -264,7 +267,8 @@ qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int *split_k_ways
 
 /* Re-read the launch-shape overrides (QG_SPLIT_K, QG_PERSIST, QG_X_GLOBAL,
  * QG_TILES_PER_GROUP, QG_WAVES_PER_WG, QG_PREFETCH, QG_F16_ROWS, QG_F16_WAVES,
- * QG_STRIDE_GROUPS, QG_GEMM_MT, QG_GEMM_WAVES, QG_GEMM_ROWGROUPS, QG_GEMM_KSPLIT)
+ * QG_STRIDE_GROUPS, QG_GEMM_MT, QG_GEMM_WAVES, QG_GEMM_ROWGROUPS, QG_GEMM_KSPLIT,
+ * QG_F16_FORM)
  * from the environment. They exist for launch-shape sweeps and tests and are
  * read once, at the first call that plans a launch; the GEMV calls themselves
  * read no environment. An override that changes a matrix's K split (QG_SPLIT_K,

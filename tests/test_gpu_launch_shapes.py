@@ -77,13 +77,14 @@ def test_forced_launch_shapes(kind, N, K):
 @pytest.mark.parametrize("N,K", [(300, 5120), (37, 1000), (2049, 64)])
 def test_f16_forced_launch_shapes(N, K):
     # every rows-per-workgroup / wavefronts-per-workgroup shape of the fp16 split-K
-    # GEMV against the oracle, and the same bits run to run at a fixed shape
+    # form against the oracle, and the same bits run to run at a fixed shape
     rng = np.random.default_rng(N + K)
     w = W.f16_matrix(N, K, rng)
     x = W.activation(K, rng)
     wd, xd = to_dev(w), to_dev(x)
     y_ref, a_ref = O.gemv("f16", w, x, N, K, threads=THREADS)
     try:
+        os.environ["QG_F16_FORM"] = "0"
         for r in (1, 2, 4):
             for wv in (1, 3, 8, 16):
                 os.environ["QG_F16_ROWS"], os.environ["QG_F16_WAVES"] = str(r), str(wv)
@@ -98,6 +99,42 @@ def test_f16_forced_launch_shapes(N, K):
                 assert_linear(a0, y_ref, a_ref, ctx)
                 assert a0.tobytes() == y1.cpu().numpy().tobytes(), ctx + ": run-to-run bits differ"
     finally:
-        os.environ.pop("QG_F16_ROWS", None)
-        os.environ.pop("QG_F16_WAVES", None)
+        for k in ("QG_F16_ROWS", "QG_F16_WAVES", "QG_F16_FORM"):
+            os.environ.pop(k, None)
+        qg.qg_reload_tuning()
+
+
+# The row form (one wavefront per row, K = 512 L): L = 1 and L = 16, fewer rows
+# than one workgroup holds, ragged last workgroups, every rows-per-workgroup
+# choice, against the oracle; the same bits run to run; and the forced form on
+# a K the row form cannot take falls back to the split-K form.
+@pytest.mark.parametrize("N,K", [(1, 512), (3, 8192), (37, 1024), (1001, 5120), (2049, 512), (130, 8192)])
+def test_f16_row_form(N, K):
+    rng = np.random.default_rng(7 * N + K)
+    w = W.f16_matrix(N, K, rng)
+    x = W.activation(K, rng)
+    wd, xd = to_dev(w), to_dev(x)
+    y_ref, a_ref = O.gemv("f16", w, x, N, K, threads=THREADS)
+    try:
+        os.environ["QG_F16_FORM"] = "1"
+        for wv in (2, 4, 8, 0):
+            if wv:
+                os.environ["QG_F16_WAVES"] = str(wv)
+            else:
+                os.environ.pop("QG_F16_WAVES", None)
+            qg.qg_reload_tuning()
+            ctx = f"f16 row form {N}x{K} rows/wg={wv or 'default'}"
+            announce(ctx)
+            y0, y1 = empty_f32(N + 1), empty_f32(N)
+            y0[N:] = -7.0
+            qg.gemv_f16_splitk(wd, xd, y0, N, K)
+            qg.gemv_f16_splitk(wd, xd, y1, N, K)
+            sync()
+            a0 = y0.cpu().numpy()
+            assert a0[N] == -7.0, ctx + ": wrote past y"
+            assert_linear(a0[:N], y_ref, a_ref, ctx)
+            assert a0[:N].tobytes() == y1.cpu().numpy().tobytes(), ctx + ": run-to-run bits differ"
+    finally:
+        for k in ("QG_F16_WAVES", "QG_F16_FORM"):
+            os.environ.pop(k, None)
         qg.qg_reload_tuning()
