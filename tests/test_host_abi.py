@@ -253,6 +253,21 @@ def test_plan_info_split_is_independent_of_m(L):
     assert p["persistent"] and p["split_k_ways"] > 1 and 17 % p["split_k_ways"] == 0
 
 
+def test_plan_info_three_segments_get_three_wavefronts(L):
+    # a row tile of exactly three 1024-weight segments is split over three
+    # wavefronts (one segment each), for every type and every M; two or four
+    # segments keep the power-of-two split
+    for kind in ("q8_0", "q4_0", "q4_k", "q6_k"):
+        for N in (1, 77, 1024, 2048):
+            for M in range(1, 7):
+                assert qg.qg_plan_info(kind, N, 3072, M)["split_k_ways"] == 3, (kind, N, M)
+    assert qg.qg_plan_info("q8_0", 1024, 2048)["split_k_ways"] == 2
+    assert qg.qg_plan_info("q8_0", 1024, 4096)["split_k_ways"] == 4
+    # the one-wavefront-per-tile form with 2048 tiles or more: no split
+    p = qg.qg_plan_info("q8_0", 8 * 4096, 3072)
+    assert not p["persistent"] and p["split_k_ways"] == 1
+
+
 def test_tuning_overrides_are_read_on_reload(L, monkeypatch):
     # the launch-shape overrides are read once and on qg_reload_tuning(), not per call
     assert qg.qg_plan_info("q4_0", 5120, 17408)["persistent"]
