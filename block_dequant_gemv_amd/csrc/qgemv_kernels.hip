@@ -564,8 +564,21 @@ __device__ __forceinline__ void store_tile(const float (&acc)[M][kRowsPerLane], 
 // Which group handles a tile changes none of its rows' operations.
 // Each wavefront walks its (tile, segment) sequence with the loads of the next
 // D units in flight while the current one is computed (a ring of D+1 units).
+// A split workgroup (W > 1) has exactly W wavefronts. The k-quant kernels with
+// 5 or 6 activation rows declare that bound, which lets them use the
+// accumulation registers instead of spilling 44-336 bytes per lane to scratch
+// (measured: M = 6 on 8000 x 2048, Q6_K 23.4 -> 17.5 us, Q4_K 20.8 -> 18.1 us;
+// M = 5 with W = 2 about 10% faster). With fewer rows they spill little or
+// nothing, and the wider register budget only lowers their occupancy (Q6_K
+// M = 4 on the same matrix 11.1 -> 13.2 us), so every other instantiation keeps
+// the 512-thread bound.
+constexpr int qgemv_max_threads(int QT, int M, int W)
+{
+    return (W > 1 && M >= 5 && (QT == kQ4_K || QT == kQ6_K)) ? 64 * W : 512;
+}
+
 template <int QT, int M, int EPI, int W, bool XLDS, int D, bool NORM>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(qgemv_max_threads(QT, M, W))
 qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float *__restrict__ y, QArgs a)
 {
     static_assert(!NORM || (XLDS && M == 1), "the RMSNorm prologue works on staged single-row activations");

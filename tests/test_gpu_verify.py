@@ -18,7 +18,9 @@ CASES = [("q4_0", 17408, 5120), ("q8_0", 4096, 1024), ("q8_0", 33, 2080), ("q4_0
          # the super-block types: one tile per wavefront group, K split four ways
          # (200x4096), the persistent form (2001x8448 with an 8-block last segment)
          ("q4_k", 1000, 1024), ("q4_k", 200, 4096), ("q4_k", 2001, 8448),
-         ("q6_k", 1000, 1024), ("q6_k", 200, 4096), ("q6_k", 3300, 5120)]
+         ("q6_k", 1000, 1024), ("q6_k", 200, 4096), ("q6_k", 3300, 5120),
+         # three segments: K split three ways (one segment per wavefront)
+         ("q4_k", 1024, 3072), ("q6_k", 77, 3072), ("q8_0", 1024, 3072)]
 
 
 @pytest.mark.parametrize("kind,N,K", CASES)
