@@ -5,7 +5,8 @@ and the fp16 output is the fp32 result rounded to nearest even.
 
 Shapes cover both launch forms of the quantised GEMV: one wavefront group per
 row tile (fused QKV 4096x1024 with its bias; the 1024x2048 O projection split
-two ways along K, with the residual added in place; a ragged 9x1056) and the
+two ways along K, with the residual added in place; the 1024x3072 down projection
+split three ways; a ragged 9x1056) and the
 persistent form with K ranges combined in LDS (3300x5120, 640x17408); the Q4_K
 and Q6_K weights on two shapes each."""
 import numpy as np
@@ -18,7 +19,7 @@ from gpu_helpers import THREADS, announce, empty_f32, magnitude, sync, to_dev, t
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(4096, 1024), (1024, 2048), (9, 1056), (3300, 5120), (640, 17408)]
+SHAPES = [(4096, 1024), (1024, 2048), (1024, 3072), (9, 1056), (3300, 5120), (640, 17408)]
 TAIL = 5
 
 

@@ -43,9 +43,10 @@ def test_rmsnorm_matches_oracle(K):
     assert np.all(err <= 1e-5 * np.abs(ref) + 1e-30), float(np.max(err / (np.abs(ref) + 1e-30)))
 
 
-# (N, K): fused QKV (tile form), a ragged shape, the persistent form (3300x5120,
-# 5120x17408 with its K ranges), and K = 17408 in the tile form (68 KiB staged)
-SHAPES = [(4096, 1024), (33, 2080), (3300, 5120), (5120, 17408), (640, 17408)]
+# (N, K): fused QKV (tile form), a ragged shape, a three-way K split (1024x3072),
+# the persistent form (3300x5120, 5120x17408 with its K ranges), and K = 17408
+# in the tile form (68 KiB staged)
+SHAPES = [(4096, 1024), (33, 2080), (1024, 3072), (3300, 5120), (5120, 17408), (640, 17408)]
 
 
 @pytest.mark.parametrize("kind,N,K", [(k, n, kk) for k in ("q8_0", "q4_0") for n, kk in SHAPES] +
