@@ -27,8 +27,9 @@ constexpr int kGemmTileM = 16;
 constexpr int kGemmMaxMT = 4;
 constexpr int kGemmChunk = 4;
 
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left free): the encoding of gfx9-family parts.
-constexpr int kVmcnt0 = 0x0F70;
+// s_waitcnt vmcnt(n) for n < 16 (expcnt and lgkmcnt left free): the encoding of
+// gfx9-family parts (vmcnt bits 3:0, expcnt 6:4, lgkmcnt 11:8).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | n; }
 
 // 4-byte words of one staged chunk's scales (wg_tiles x 2 slots x kGemmChunk
 // blocks x 8 B), rounded up to whole 64-lane copies.

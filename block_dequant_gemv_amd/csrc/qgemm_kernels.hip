@@ -122,10 +122,10 @@ __device__ __forceinline__ void group_transpose(uint32_t (&v)[4])
 // turn: the chunk's split activations (MT x 2 KiB per block) and the scales of
 // the workgroup's rows are copied with LDS-direct loads (global_load_lds, no
 // registers) one chunk ahead, so the copy of chunk c + 1 runs under the
-// matrix-core work of chunk c; one vmcnt wait and one barrier per chunk. Each
-// wavefront walks a chunk's blocks in load groups of 4 (Q4_0) or 2 (Q8_0): one
-// 16-byte load per lane and row group (issued one group ahead, across chunk
-// and segment ends), the group transpose, the dequant, and per block and
+// matrix-core work of chunk c; one vmcnt wait and one barrier per chunk. The
+// weights of a chunk are loaded one chunk ahead too: load groups of 4 (Q4_0) or
+// 2 (Q8_0) blocks, one 16-byte load per lane and row group. Each wavefront
+// walks a chunk's groups: the group transpose, the dequant, and per block and
 // activation tile two MFMAs (hi, lo) per row group, each B operand read once
 // from LDS and used by the RG row groups; then acc = fma(d, S, acc).
 // Block sums are added per segment of 32 blocks and the segment sums in order.
@@ -241,42 +241,51 @@ qgemm_kernel(const uint8_t *__restrict__ wp, const _Float16 *__restrict__ xs, co
         }
     };
 
-    u32x4 raw[RG];
+    // All NG load groups of a chunk, loaded one chunk ahead (a ragged last chunk's
+    // extra groups load valid units that are never used).
+    constexpr int NG = CB / BPG;
+    auto load_chunk = [&](u32x4 (&raw)[NG][RG], int64_t c) {
+        const ChunkPos p = chunk_at(c);
+#pragma unroll
+        for (int q = 0; q < NG; ++q) load_group(raw[q], p.s, p.nb, p.j0 / BPG + q);
+    };
+    u32x4 rawn[NG][RG];
     if (n_chunks > 0) {
         stage(0, 0);
-        const ChunkPos c0 = chunk_at(0);
-        load_group(raw, c0.s, c0.nb, c0.j0 / BPG);
+        load_chunk(rawn, 0);
     }
     for (int64_t ci = 0; ci < n_chunks; ++ci) {
-        // chunk ci staged (this wavefront's copies done, then everyone's), and every
-        // wavefront past chunk ci - 1, whose buffer the next chunk now takes
-        __builtin_amdgcn_s_waitcnt(kVmcnt0);
-        __syncthreads();
-        if (ci + 1 < n_chunks) stage((int)((ci + 1) & 1), ci + 1);
-        const ChunkPos cp = chunk_at(ci);
-        const int64_t s = cp.s;
-        const int nb = cp.nb, j0 = cp.j0, nbc = cp.nbc;
-        const u32x4 *lxb = lx + (ci & 1) * (MT * CB * 128);
-        const u32x2 *lscb = (const u32x2 *)(lsc_base + (ci & 1) * lsc_words);
-        const int ngroups = (nbc + BPG - 1) / BPG;
-        for (int qq = 0; qq < ngroups; ++qq) {
-            uint32_t v[RG][4];
+        // Everything this wavefront issued is chunk ci's: its copies into buffer
+        // ci & 1 and its weight groups, both issued one chunk earlier. Take the
+        // weights into working registers; after the barrier every wavefront's
+        // copies are in LDS and every wavefront is past chunk ci - 1, whose buffer
+        // the next copies take. Nothing issued after a load comes between that
+        // load and its use, so no wait below covers the next chunk's loads.
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        uint32_t v[NG][RG][4];
+#pragma unroll
+        for (int q = 0; q < NG; ++q)
 #pragma unroll
             for (int rg = 0; rg < RG; ++rg) {
-                v[rg][0] = raw[rg].x;
-                v[rg][1] = raw[rg].y;
-                v[rg][2] = raw[rg].z;
-                v[rg][3] = raw[rg].w;
+                v[q][rg][0] = rawn[q][rg].x;
+                v[q][rg][1] = rawn[q][rg].y;
+                v[q][rg][2] = rawn[q][rg].z;
+                v[q][rg][3] = rawn[q][rg].w;
             }
-            // one group ahead: the next group of this chunk, else the next chunk's first
-            if (qq + 1 < ngroups) {
-                load_group(raw, s, nb, j0 / BPG + qq + 1);
-            } else if (ci + 1 < n_chunks) {
-                const ChunkPos cn = chunk_at(ci + 1);
-                load_group(raw, cn.s, cn.nb, cn.j0 / BPG);
-            }
+        __syncthreads();
+        if (ci + 1 < n_chunks) {
+            stage((int)((ci + 1) & 1), ci + 1);
+            load_chunk(rawn, ci + 1);
+        }
+        const ChunkPos cp = chunk_at(ci);
+        const int nb = cp.nb, nbc = cp.nbc, j0 = cp.j0;
+        const u32x4 *lxb = lx + (ci & 1) * (MT * CB * 128);
+        const u32x2 *lscb = (const u32x2 *)(lsc_base + (ci & 1) * lsc_words);
 #pragma unroll
-            for (int rg = 0; rg < RG; ++rg) group_transpose(v[rg]);
+        for (int qq = 0; qq < NG; ++qq) {
+            if (qq * BPG >= nbc) break;   // wave-uniform
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) group_transpose(v[qq][rg]);
 #pragma unroll
             for (int bb = 0; bb < BPG; ++bb) {
                 const int jj = qq * BPG + bb;   // block within the chunk
@@ -287,12 +296,12 @@ qgemm_kernel(const uint8_t *__restrict__ wp, const _Float16 *__restrict__ xs, co
                 for (int rg = 0; rg < RG; ++rg) {
                     if (QT == kQ4_0) {
                         h2 p[4];
-                        q4_pairs(v[rg][bb], k, p);
+                        q4_pairs(v[qq][rg][bb], k, p);
                         A[rg] = h8{p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
                     } else {
                         h2 p0[2], p1[2];
-                        q8_pairs(v[rg][2 * bb], p0);
-                        q8_pairs(v[rg][2 * bb + 1], p1);
+                        q8_pairs(v[qq][rg][2 * bb], p0);
+                        q8_pairs(v[qq][rg][2 * bb + 1], p1);
                         A[rg] = h8{p0[0].x, p0[0].y, p0[1].x, p0[1].y, p1[0].x, p1[0].y, p1[1].x, p1[1].y};
                     }
                     // rows 4c + r of row group rg: tile (wave*RG + rg)*2 + c/2 of the workgroup, slot c%2
