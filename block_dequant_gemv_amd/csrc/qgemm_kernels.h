@@ -26,16 +26,19 @@ struct GemmArgs {
 constexpr int kGemmTileM = 16;
 constexpr int kGemmMaxMT = 4;
 constexpr int kGemmChunk = 4;
+// Blocks per staged chunk for MT activation tiles per pass: one tile stages
+// 8 blocks at a time (fewer waits per K, twice the weights in flight).
+constexpr int gemm_chunk(int MT) { return MT == 1 ? 2 * kGemmChunk : kGemmChunk; }
 
 // s_waitcnt vmcnt(n) for n < 16 (expcnt and lgkmcnt left free): the encoding of
 // gfx9-family parts (vmcnt bits 3:0, expcnt 6:4, lgkmcnt 11:8).
 constexpr int vmcnt_imm(int n) { return 0x0F70 | n; }
 
-// 4-byte words of one staged chunk's scales (wg_tiles x 2 slots x kGemmChunk
-// blocks x 8 B), rounded up to whole 64-lane copies.
-constexpr int gemm_scale_words(int wg_tiles)
+// 4-byte words of one staged chunk's scales (wg_tiles x 2 slots x CB blocks x
+// 8 B), rounded up to whole 64-lane copies.
+constexpr int gemm_scale_words(int wg_tiles, int CB)
 {
-    return (wg_tiles * 2 * kGemmChunk * 2 + 63) / 64 * 64;
+    return (wg_tiles * 2 * CB * 2 + 63) / 64 * 64;
 }
 
 // LDS of one GEMM workgroup, two buffers (one chunk staged while the other is
@@ -43,7 +46,7 @@ constexpr int gemm_scale_words(int wg_tiles)
 // scales of its row tiles (2 slots x 4 rows x fp16 per block).
 constexpr size_t gemm_lds_bytes(int MT, int wg_tiles)
 {
-    return 2 * ((size_t)MT * kGemmChunk * 128 * 16 + (size_t)gemm_scale_words(wg_tiles) * 4);
+    return 2 * ((size_t)MT * gemm_chunk(MT) * 128 * 16 + (size_t)gemm_scale_words(wg_tiles, gemm_chunk(MT)) * 4);
 }
 
 // Y[m][n] = sum over ky (in order) of part[ky][m][n], m < M, n < N.

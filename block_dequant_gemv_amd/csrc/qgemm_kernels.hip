@@ -118,7 +118,7 @@ __device__ __forceinline__ void group_transpose(uint32_t (&v)[4])
 // The GEMM. A workgroup of G wavefronts owns 16 RG G weight rows: wavefront w
 // covers RG groups of 16 rows (row tiles 2 RG (blockIdx.x G + w) + 2 rg and
 // + 1 for group rg), for the MT 16-row activation tiles [a.mt0, a.mt0 + MT).
-// K is walked in chunks of kGemmChunk blocks, staged into two LDS buffers in
+// K is walked in chunks of CB = gemm_chunk(MT) blocks, staged into two LDS buffers in
 // turn: the chunk's split activations (MT x 2 KiB per block) and the scales of
 // the workgroup's rows are copied with LDS-direct loads (global_load_lds, no
 // registers) one chunk ahead, so the copy of chunk c + 1 runs under the
@@ -138,7 +138,7 @@ qgemm_kernel(const uint8_t *__restrict__ wp, const _Float16 *__restrict__ xs, co
 {
     constexpr int NH = (QT == kQ8_0) ? 2 : 1;
     constexpr int BPG = (QT == kQ8_0) ? 2 : 4;   // blocks per load group
-    constexpr int CB = kGemmChunk;               // blocks per staged chunk (a multiple of BPG)
+    constexpr int CB = gemm_chunk(MT);           // blocks per staged chunk (a multiple of BPG)
     extern __shared__ u32x4 lds[];
     u32x4 *lx = lds;   // 2 buffers x [mt][CB][h][64 lanes] x 16 B
     // 2 buffers x [tile of the workgroup][slot][CB] x 4 fp16, in 4-byte words, padded to whole wavefront copies
@@ -151,7 +151,7 @@ qgemm_kernel(const uint8_t *__restrict__ wp, const _Float16 *__restrict__ xs, co
     const int i = lane & 15, c = lane >> 4;
     const int64_t wg_tile0 = (int64_t)blockIdx.x * G * 2 * RG;   // first row tile of the workgroup
     const int wg_tiles = G * 2 * RG;
-    const int lsc_words = gemm_scale_words(wg_tiles);
+    const int lsc_words = gemm_scale_words(wg_tiles, CB);
     const int64_t t_first = wg_tile0 + (int64_t)wave * 2 * RG;    // first row tile of this wavefront
     const int64_t t_last = g.n_tiles - 1;
     const int slotA = (i & 7) >> 2, browA = i & 3;

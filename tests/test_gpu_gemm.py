@@ -17,9 +17,10 @@ from gpu_helpers import THREADS, announce, assert_linear, sync, to_dev, torch_de
 
 pytestmark = pytest.mark.gpu
 
-# (N, K, M)
+# (N, K, M); M = 80 runs a four-tile pass, then a one-tile pass (8-block chunks)
+# over a ragged 33-block K
 SHAPES = [(4096, 1024, 16), (1024, 3072, 8), (300, 2080, 20), (33, 1056, 1), (257, 5120, 40), (2048, 17408, 3),
-          (1000, 1024, 64), (17408, 5120, 32)]
+          (1000, 1024, 64), (17408, 5120, 32), (300, 1056, 80)]
 
 
 def _run(kind, packed, X, N, K, M, tail=0, ws=None):
