@@ -97,7 +97,7 @@ constexpr int persist_threads(int qt, int M, bool xlds)
     if (M == 1) return 1024;
     if (qt == qgl::kQ4_0) return (M <= 4 || xlds) ? 768 : 512;
     if (qt == qgl::kQ4_K || qt == qgl::kQ6_K) return M <= 2 ? 768 : 512;
-    return (M <= 3 || (M == 4 && xlds)) ? 768 : 512;
+    return (M <= 3 || xlds) ? 768 : 512;
 }
 
 // Raise a kernel's dynamic-LDS limit to `bytes` (needed above 64 KiB) unless it is

@@ -330,43 +330,60 @@ __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][
     const float *xg = x + s * kSegWeights + j * 32;
 
     // 8 float4 chunks of x per block; Q4_0 consumes 2 chunks per dword, Q8_0 one.
-#pragma unroll
-    for (int c = 0; c < 8; c += 2) {
-        f32x4 xv[2][M];
+    // Per dword of 8 elements, one activation row: its 2 float4 of x, then the 4
+    // weight rows one at a time. Several: the 4 weight rows' fp16 pairs once, then
+    // the activation rows one at a time (2 float4 of x live, not 2 M). Each
+    // accumulator sees the same 8 fmas in the same order either way.
+    auto pairs = [&](int b, int c, h2 (&p)[4]) {
+        if (QT == kQ4_0) {
+            q4_pairs(u.q[b][0][c >> 1], k, p);
+        } else {
+            h2 p01[2], p23[2];
+            q8_pairs(u.q[b][c >> 2][c & 3], p01);
+            q8_pairs(u.q[b][c >> 2][(c & 3) + 1], p23);
+            p[0] = p01[0];
+            p[1] = p01[1];
+            p[2] = p23[0];
+            p[3] = p23[1];
+        }
+    };
+    auto load_x = [&](f32x4 (&xv)[2], int m, int c) {
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
+            xv[cc] = XLDS ? xl[m * x_row + (c + cc) * 32] : *(const f32x4 *)(xg + m * x_stride + (c + cc) * 4);
+    };
+    auto row_fma = [&](const h2 (&p)[4], const f32x4 (&xv)[2], int m, int b) {
+        float s_ = sb[m][b];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            s_ = __builtin_fmaf((float)p[2 * cc].x, xv[cc].x, s_);
+            s_ = __builtin_fmaf((float)p[2 * cc].y, xv[cc].y, s_);
+            s_ = __builtin_fmaf((float)p[2 * cc + 1].x, xv[cc].z, s_);
+            s_ = __builtin_fmaf((float)p[2 * cc + 1].y, xv[cc].w, s_);
+        }
+        sb[m][b] = s_;
+    };
+#pragma unroll
+    for (int c = 0; c < 8; c += 2) {
+        if constexpr (M == 1) {
+            f32x4 xv[2];
+            load_x(xv, 0, c);
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                h2 p[4];
+                pairs(b, c, p);
+                row_fma(p, xv, 0, b);
+            }
+        } else {
+            h2 p[B][4];
+#pragma unroll
+            for (int b = 0; b < B; ++b) pairs(b, c, p[b]);
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                if (XLDS)
-                    xv[cc][m] = xl[m * x_row + (c + cc) * 32];
-                else
-                    xv[cc][m] = *(const f32x4 *)(xg + m * x_stride + (c + cc) * 4);
-            }
+                f32x4 xv[2];
+                load_x(xv, m, c);
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-            h2 p[4];
-            if (QT == kQ4_0) {
-                q4_pairs(u.q[b][0][c >> 1], k, p);
-            } else {
-                h2 p01[2], p23[2];
-                q8_pairs(u.q[b][c >> 2][c & 3], p01);
-                q8_pairs(u.q[b][c >> 2][(c & 3) + 1], p23);
-                p[0] = p01[0];
-                p[1] = p01[1];
-                p[2] = p23[0];
-                p[3] = p23[1];
-            }
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                float s_ = sb[m][b];
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
-                    s_ = __builtin_fmaf((float)p[2 * cc].x, xv[cc][m].x, s_);
-                    s_ = __builtin_fmaf((float)p[2 * cc].y, xv[cc][m].y, s_);
-                    s_ = __builtin_fmaf((float)p[2 * cc + 1].x, xv[cc][m].z, s_);
-                    s_ = __builtin_fmaf((float)p[2 * cc + 1].y, xv[cc][m].w, s_);
-                }
-                sb[m][b] = s_;
+                for (int b = 0; b < B; ++b) row_fma(p[b], xv, m, b);
             }
         }
     }
