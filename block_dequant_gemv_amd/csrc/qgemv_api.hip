@@ -206,6 +206,7 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M, bool norm = false)
     p.depth = 1;
     p.tpg = 1;
     p.tstride = 0;
+    p.phases = 1;
     if (p.persist) {
         p.ranges = (int)ranges;
         p.max_tiles = max_tiles;
@@ -213,9 +214,27 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M, bool norm = false)
         p.grid = pgrid;
         const size_t part = ranges > 1 ? (size_t)max_tiles * ranges * M * qgl::kTileRows * 4 : 0;
         bool lds = xbytes + part <= kLdsLimitMulti;
+        // Several activation rows that do not fit (M K 4 bytes above the LDS):
+        // walk the K ranges in the fewest phases whose largest activation window
+        // (ceil(ranges / phases) ranges) fits, instead of reading every unit's
+        // activations from L2 (5120 x 17408 at M = 3..6: 47-82 us from L2).
+        // Phases change which wavefront adds an item and when, not any row's
+        // operations.
+        const size_t seg_bytes = (size_t)M * qgl::kSegWeights * sizeof(float);   // one segment, M rows
+        const int64_t seg_per_range = g.nseg / ranges;
+        auto window = [&](int64_t ph) { return (size_t)((ranges + ph - 1) / ph * seg_per_range) * seg_bytes; };
+        if (!lds && M > 1 && !norm) {
+            for (int64_t ph = 2; ph <= ranges; ++ph)
+                if (window(ph) + part <= kLdsLimitMulti) {
+                    p.phases = (int)ph;
+                    lds = true;
+                    break;
+                }
+        }
         if (!norm && (xg_env == 0 || xg_env == 1)) lds = lds && xg_env == 0;
+        if (!lds) p.phases = 1;
         p.x_in_lds = lds;
-        p.lds_bytes = (lds ? xbytes : 0) + part;
+        p.lds_bytes = (lds ? window(p.phases) : 0) + part;
         p.block = qgk::persist_threads(qt, M, lds);
         return p;
     }
@@ -339,6 +358,7 @@ qg_status run_qgemv(int qt, int epi, const void *w, const float *x, void *y, int
     a.tstride = p.tstride;
     a.n_wg = p.grid;
     a.ranges = p.ranges;
+    a.phases = p.phases;
     a.bias = af.bias;
     a.residual = af.residual;
     a.out_f16 = f16 ? 1 : 0;

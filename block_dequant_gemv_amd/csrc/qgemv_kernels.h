@@ -29,6 +29,8 @@ struct QArgs {
     // persistent form only
     int64_t n_wg;        // workgroups; workgroup b owns tiles [b*n_tiles/n_wg, (b+1)*n_tiles/n_wg)
     int64_t ranges;      // K ranges per tile (divides nseg); item = (tile, range)
+    int64_t phases;      // divides ranges: the ranges are walked in phases of ranges/phases, each with
+                         // only its segments' activations staged in LDS (1: all at once)
     // kEpiAffine only (M = 1): fp32 addends (either may be null) and the output type
     const float *bias;
     const float *residual;
@@ -44,6 +46,8 @@ struct QArgs {
 struct QPlan {
     bool persist;        // persistent form: one workgroup per CU, (tile, K range) items
     int ranges;          // persistent form: K ranges per tile (divides nseg)
+    int phases;          // persistent form: phases of ranges/phases ranges (divides ranges), each
+                         // staging only its segments' activations
     int64_t max_tiles;   // persistent form: most tiles any workgroup owns
     int W;               // classic form: wavefronts splitting one row tile along K (1, 2, 3, 4, 8)
     int64_t tpg;         // tiles per group (contiguous order)

@@ -739,12 +739,15 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
 // in LDS. When every wavefront is done, the partials of each row are added in
 // range order, ((p0 + p1) + p2) + ..., and stored (with the SiLU epilogue for
 // gate|up). For any M a row goes through the same operations, so the verify
-// rows still equal the M=1 rows bit for bit.
-template <int QT, int M, int EPI, bool XLDS, bool NORM>
+// rows still equal the M=1 rows bit for bit. PHASED (several activation rows
+// that do not fit in LDS at once): the ranges are walked in phases, each
+// staging only its segments' activations (see the phase loop below).
+template <int QT, int M, int EPI, bool XLDS, bool NORM, bool PHASED = false>
 __global__ void __launch_bounds__(persist_threads(QT, M, XLDS))
 qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float *__restrict__ y, QArgs a)
 {
     static_assert(!NORM || (XLDS && M == 1), "the RMSNorm prologue works on staged single-row activations");
+    static_assert(!PHASED || (XLDS && !NORM), "phases stage windows of the activations");
     constexpr int B = kRowsPerLane;
     constexpr int S = 2;   // ring: one unit in flight ahead of the one being computed
     extern __shared__ f32x4 xs4[];
@@ -762,22 +765,28 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
     const uint32_t L = (uint32_t)(nseg / R);   // segments per range
     const int64_t T0 = (int64_t)blockIdx.x * g.n_tiles / a.n_wg;
     const int64_t T1 = ((int64_t)blockIdx.x + 1) * g.n_tiles / a.n_wg;
-    const uint32_t n_items = (uint32_t)(T1 - T0) * R;
-    const uint32_t my_items = n_items > (uint32_t)wave ? (n_items - (uint32_t)wave + G - 1) / G : 0u;
-    const int64_t n_units = (int64_t)my_items * L;
-    float *part = (float *)(xs4 + (XLDS ? (uint32_t)M * ((uint32_t)nseg << 8) : 0u));   // [tile][range][m][8]
+    // Phases: the ranges are walked in P phases; phase ph takes the ranges
+    // [r0, r1) = [R ph / P, R (ph + 1) / P), stages only the activations of
+    // their segments [r0 L, r1 L) (a window of nsegw segments; all of them when
+    // P = 1) and spreads its items i = (tile T0 + i / RP, range r0 + i % RP),
+    // RP = r1 - r0, over the wavefronts. The partials follow the largest window.
+    const uint32_t P = PHASED ? (uint32_t)a.phases : 1u;
+    const uint32_t nsegw_max = PHASED ? (R + P - 1) / P * L : (uint32_t)nseg;
+    float *part = (float *)(xs4 + (XLDS ? (uint32_t)M * (nsegw_max << 8) : 0u));   // [tile][range][m][8]
 
     const Consts k = make_consts();
     const LanePlace lp = lane_place(g, slot, j);
 
-    // A cursor over this wavefront's units: item i, its tile and range, segment s.
+    // A cursor over this wavefront's units of the phase whose first range is r0:
+    // item i, its tile and range, segment s.
     struct Cur {
         uint32_t i, r;
         int64_t t, s, s_end;
     };
+    uint32_t r0 = 0, RP = R;
     auto seat = [&](Cur &c) {
-        const uint32_t q = c.i / R;
-        c.r = c.i - q * R;
+        const uint32_t q = c.i / RP;
+        c.r = r0 + (c.i - q * RP);
         c.t = T0 + q;
         c.s = (int64_t)c.r * L;
         c.s_end = c.s + L;
@@ -788,24 +797,6 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
             seat(c);
         }
     };
-    Cur ld, cu;
-    ld.i = wave;
-    seat(ld);
-    cu = ld;
-    int64_t u_ld = 0;
-
-    XFirst xf;
-    if (XLDS) stage_x_issue(xf, x, K);
-    Unit<QT> ring[S];
-    load_unit<QT>(ring[0], wp, g, ld.t, ld.s, lp, u_ld < n_units);
-    advance(ld);
-    ++u_ld;
-
-    if (XLDS) {
-        stage_x_finish<M>(xf, xs4, x, a.x_stride, nseg, K);
-        __syncthreads();
-    }
-    if (NORM) norm_staged_x(xs4, nred, a.gamma, a.eps, K);
 
     float acc[M][B];
 #pragma unroll
@@ -813,42 +804,73 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
 #pragma unroll
         for (int b = 0; b < B; ++b) acc[m][b] = 0.0f;
 
-    auto step = [&](Unit<QT> &cur, Unit<QT> &nxt) {
-        load_unit<QT>(nxt, wp, g, ld.t, ld.s, lp, u_ld < n_units);
+    for (uint32_t ph = 0; ph < P; ++ph) {
+        r0 = PHASED ? R * ph / P : 0u;
+        RP = PHASED ? R * (ph + 1) / P - r0 : R;
+        const uint32_t nsegw = PHASED ? RP * L : (uint32_t)nseg;
+        const uint32_t n_items = (uint32_t)(T1 - T0) * RP;
+        const uint32_t my_items = n_items > (uint32_t)wave ? (n_items - (uint32_t)wave + G - 1) / G : 0u;
+        const int64_t n_units = (int64_t)my_items * L;
+        const int64_t s0 = PHASED ? (int64_t)r0 * L : 0;
+        const float *xw = x + s0 * kSegWeights;   // the window's first activation of row 0
+        const int64_t Kw = K - s0 * kSegWeights;  // activations of a row from the window on
+        if (PHASED && ph > 0) __syncthreads();    // every wavefront done with the previous window
+        Cur ld, cu;
+        ld.i = wave;
+        seat(ld);
+        cu = ld;
+        int64_t u_ld = 0;
+
+        XFirst xf;
+        if (XLDS) stage_x_issue(xf, xw, Kw);
+        Unit<QT> ring[S];
+        load_unit<QT>(ring[0], wp, g, ld.t, ld.s, lp, u_ld < n_units);
         advance(ld);
         ++u_ld;
-        __builtin_amdgcn_sched_barrier(0);
-        const bool last = cu.s == nseg - 1;
-        compute_unit<QT, M, XLDS>(cur, acc, k, xs4, x, a.x_stride, nseg, cu.s, last ? lp.j_last : j,
-                                  !last || lp.live_last);
-        if (cu.s + 1 == cu.s_end) {
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-#pragma unroll
-                for (int b = 0; b < B; ++b) acc[m][b] = half_wave_sum(acc[m][b]);
-            if (R == 1) {
-                store_tile<M, EPI>(acc, y, a, cu.t, slot, j);
-            } else if (j == 0) {
-                float *pp = part + ((size_t)(cu.t - T0) * R + cu.r) * (M * kTileRows) + slot * B;
+
+        if (XLDS) {
+            stage_x_finish<M>(xf, xs4, xw, a.x_stride, nsegw, Kw);
+            __syncthreads();
+        }
+        if (NORM) norm_staged_x(xs4, nred, a.gamma, a.eps, K);
+
+        auto step = [&](Unit<QT> &cur, Unit<QT> &nxt) {
+            load_unit<QT>(nxt, wp, g, ld.t, ld.s, lp, u_ld < n_units);
+            advance(ld);
+            ++u_ld;
+            __builtin_amdgcn_sched_barrier(0);
+            const bool last = cu.s == nseg - 1;
+            compute_unit<QT, M, XLDS>(cur, acc, k, xs4, x, a.x_stride, nsegw, cu.s - s0, last ? lp.j_last : j,
+                                      !last || lp.live_last);
+            if (cu.s + 1 == cu.s_end) {
 #pragma unroll
                 for (int m = 0; m < M; ++m)
 #pragma unroll
-                    for (int b = 0; b < B; ++b) pp[m * kTileRows + b] = acc[m][b];
+                    for (int b = 0; b < B; ++b) acc[m][b] = half_wave_sum(acc[m][b]);
+                if (R == 1) {
+                    store_tile<M, EPI>(acc, y, a, cu.t, slot, j);
+                } else if (j == 0) {
+                    float *pp = part + ((size_t)(cu.t - T0) * R + cu.r) * (M * kTileRows) + slot * B;
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+#pragma unroll
+                        for (int b = 0; b < B; ++b) pp[m * kTileRows + b] = acc[m][b];
+                }
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int b = 0; b < B; ++b) acc[m][b] = 0.0f;
             }
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-#pragma unroll
-                for (int b = 0; b < B; ++b) acc[m][b] = 0.0f;
-        }
-        advance(cu);
-    };
+            advance(cu);
+        };
 
-    const int64_t n_groups = n_units / S;
-    for (int64_t gi = 0; gi < n_groups; ++gi) {
-        step(ring[0], ring[1]);
-        step(ring[1], ring[0]);
+        const int64_t n_groups = n_units / S;
+        for (int64_t gi = 0; gi < n_groups; ++gi) {
+            step(ring[0], ring[1]);
+            step(ring[1], ring[0]);
+        }
+        if (n_units - n_groups * S) step(ring[0], ring[1]);
     }
-    if (n_units - n_groups * S) step(ring[0], ring[1]);
 
     if (R > 1) {
         // every wavefront reaches this barrier (no early exit above)
@@ -1144,6 +1166,17 @@ static hipError_t launch_persist(const uint8_t *wp, const float *x, float *y, co
                                  hipStream_t stream)
 {
     auto kern = p.x_in_lds ? qgemv_persist<QT, M, EPI, true, false> : qgemv_persist<QT, M, EPI, false, false>;
+    int which = p.norm ? 2 : (p.x_in_lds ? 0 : 1);
+    if (p.phases > 1) {
+        // several activation rows walked in phases (staged windows), plain store only
+        if constexpr (M > 1 && EPI == kEpiPlain) {
+            if (!p.x_in_lds || p.norm) return hipErrorInvalidConfiguration;
+            kern = qgemv_persist<QT, M, EPI, true, false, true>;
+            which = 3;
+        } else {
+            return hipErrorInvalidConfiguration;
+        }
+    }
     if (p.norm) {
         // the RMSNorm prologue: single-row plain and gate|up kernels with staged activations
         if constexpr (M == 1 && EPI != kEpiAffine) {
@@ -1154,8 +1187,8 @@ static hipError_t launch_persist(const uint8_t *wp, const float *x, float *y, co
         }
     }
     if (p.block != persist_threads(QT, M, p.x_in_lds)) return hipErrorInvalidConfiguration;
-    static std::atomic<int> lds_set[3][16];   // one record per kernel chosen above
-    hipError_t e = ensure_lds_limit((const void *)kern, p.lds_bytes, lds_set[p.norm ? 2 : (p.x_in_lds ? 0 : 1)]);
+    static std::atomic<int> lds_set[4][16];   // one record per kernel chosen above
+    hipError_t e = ensure_lds_limit((const void *)kern, p.lds_bytes, lds_set[which]);
     if (e != hipSuccess) return e;
     launch(kern, dim3((unsigned)p.grid), dim3(p.block), (uint32_t)p.lds_bytes, stream, wp, x, y, a);
     return hipGetLastError();

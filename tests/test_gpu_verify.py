@@ -20,7 +20,10 @@ CASES = [("q4_0", 17408, 5120), ("q8_0", 4096, 1024), ("q8_0", 33, 2080), ("q4_0
          ("q4_k", 1000, 1024), ("q4_k", 200, 4096), ("q4_k", 2001, 8448),
          ("q6_k", 1000, 1024), ("q6_k", 200, 4096), ("q6_k", 3300, 5120),
          # three segments: K split three ways (one segment per wavefront)
-         ("q4_k", 1024, 3072), ("q6_k", 77, 3072), ("q8_0", 1024, 3072)]
+         ("q4_k", 1024, 3072), ("q6_k", 77, 3072), ("q8_0", 1024, 3072),
+         # M K 4 bytes above the LDS from M = 3: the persistent form walks its 17 K
+         # ranges in phases, staging one window of activations at a time
+         ("q4_0", 5120, 17408), ("q6_k", 2001, 17408)]
 
 
 @pytest.mark.parametrize("kind,N,K", CASES)
