@@ -535,7 +535,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=15)
-    ap.add_argument("--reps", type=int, default=50, help="cold reps per call in the per-config table")
+    ap.add_argument("--reps", type=int, default=100, help="cold reps per call in the per-config table")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config table")
     ap.add_argument("--only", default=None,
                     help="comma-separated label prefixes: time only the per-config rows that start with one of "
