@@ -49,24 +49,27 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 // fp16 parts in B-operand order: xs[((mt * KB + b) * 2 + h) * 512 + lane * 8 + e]
 // with mt = m / 16, lane = 16 c + m % 16, h = 0 (hi) / 1 (lo), where (c, e)
 // is the position of the block's element in its lane (see above).
+constexpr int kSplitThreads = 1024;   // one workgroup per activation row
+
 template <int QT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kSplitThreads)
 split_x_kernel(const float *__restrict__ X, _Float16 *__restrict__ xs, float *__restrict__ unscale, int64_t M,
                int64_t K)
 {
-    __shared__ float red[4];
+    __shared__ float red[kSplitThreads / 64];
     const int64_t m = blockIdx.x;
     const int tid = threadIdx.x;
     const bool live = m < M;
     const float *xr = X + m * K;
     float mx = 0.0f;
     if (live)
-        for (int64_t k = tid; k < K; k += 256) mx = __builtin_fmaxf(mx, __builtin_fabsf(xr[k]));
+        for (int64_t k = tid; k < K; k += kSplitThreads) mx = __builtin_fmaxf(mx, __builtin_fabsf(xr[k]));
     // workgroup maximum (max is exact, so the order does not matter)
     for (int o = 32; o >= 1; o >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o));
     if ((tid & 63) == 0) red[tid >> 6] = mx;
     __syncthreads();
-    mx = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+    mx = red[0];
+    for (int w = 1; w < kSplitThreads / 64; ++w) mx = __builtin_fmaxf(mx, red[w]);
     // 2^e with max|x| * 2^e in [2^14, 2^15); 1 for a zero or non-finite maximum
     int e = 0;
     if (mx > 0.0f && mx <= 3.4028234663852886e38f) {
@@ -80,7 +83,7 @@ split_x_kernel(const float *__restrict__ X, _Float16 *__restrict__ xs, float *__
     const int64_t KB = K / 32;
     const int64_t mt = m >> 4;
     const int mi = (int)(m & 15);
-    for (int64_t k = tid; k < K; k += 256) {
+    for (int64_t k = tid; k < K; k += kSplitThreads) {
         const float v = live ? xr[k] * sc : 0.0f;
         const _Float16 hi = (_Float16)v;
         const _Float16 lo = (_Float16)(v - (float)hi);
@@ -390,9 +393,11 @@ hipError_t launch_split_x(int qt, const float *X, _Float16 *xs, float *unscale, 
                           hipStream_t s)
 {
     if (qt == kQ8_0)
-        hipLaunchKernelGGL(split_x_kernel<kQ8_0>, dim3((unsigned)M_pad), dim3(256), 0, s, X, xs, unscale, M, K);
+        hipLaunchKernelGGL(split_x_kernel<kQ8_0>, dim3((unsigned)M_pad), dim3(kSplitThreads), 0, s, X, xs, unscale,
+                           M, K);
     else
-        hipLaunchKernelGGL(split_x_kernel<kQ4_0>, dim3((unsigned)M_pad), dim3(256), 0, s, X, xs, unscale, M, K);
+        hipLaunchKernelGGL(split_x_kernel<kQ4_0>, dim3((unsigned)M_pad), dim3(kSplitThreads), 0, s, X, xs, unscale,
+                           M, K);
     return hipGetLastError();
 }
 
