@@ -149,7 +149,7 @@ qgemm_kernel(const uint8_t *__restrict__ wp, const _Float16 *__restrict__ xs, co
 
     const Geometry &g = a.geo;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: its arithmetic stays scalar
     const int G = blockDim.x >> 6;
     const int i = lane & 15, c = lane >> 4;
     const int64_t wg_tile0 = (int64_t)blockIdx.x * G * 2 * RG;   // first row tile of the workgroup
@@ -219,7 +219,9 @@ qgemm_kernel(const uint8_t *__restrict__ wp, const _Float16 *__restrict__ xs, co
         u32x4 *lxd = lx + buf * (MT * CB * 128);
         const int nkib = MT * p.nbc * 2;
         for (int q = wave; q < nkib; q += G) {
-            const int mt = q / (p.nbc * 2), r = q - mt * (p.nbc * 2);
+            // a full chunk's run per tile is 2 CB pieces (a power of two)
+            const int mt = MT == 1 ? 0 : (p.nbc == CB ? q / (2 * CB) : q / (p.nbc * 2));
+            const int r = q - mt * (p.nbc * 2);
             const u32x4 *src =
                 (const u32x4 *)xs + ((a.mt0 + mt) * KB + p.s * kSegBlocks + p.j0) * 128 + r * 64 + lane;
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
@@ -228,17 +230,21 @@ qgemm_kernel(const uint8_t *__restrict__ wp, const _Float16 *__restrict__ xs, co
         }
         uint32_t *lsd = (uint32_t *)(lsc_base + buf * lsc_words);
         const int nwords = wg_tiles * 2 * CB * 2;
+        // the workgroup's first tile and this segment (uniform), then per lane its
+        // tile (clamped to the matrix's last) and its place in the segment
+        const uint8_t *sbase = wp + g.scale_off + wg_tile0 * g.tile_s + p.s * seg_s;
+        const int tl_last = (int)(t_last - wg_tile0);
         for (int q = wave; q * 64 < lsc_words; q += G) {
             int wi = q * 64 + lane;
             wi = wi < nwords ? wi : 0;
             const int run = wi / (2 * CB), within = wi - run * (2 * CB);
-            const int tl = run >> 1, sl = run & 1;
+            int tl = run >> 1;
+            tl = tl < tl_last ? tl : tl_last;
+            const int sl = run & 1;
             int jj = within >> 1;
             jj = jj < p.nbc ? jj : p.nbc - 1;
-            int64_t t = wg_tile0 + tl;
-            t = t < t_last ? t : t_last;
-            const uint8_t *src = wp + g.scale_off + t * g.tile_s + p.s * seg_s +
-                                 (int64_t)(sl * p.nb + p.j0 + jj) * (kRowsPerLane * 2) + (within & 1) * 4;
+            const uint8_t *src = sbase + (uint64_t)(uint32_t)tl * (uint64_t)g.tile_s +
+                                 (uint32_t)((sl * p.nb + p.j0 + jj) * (kRowsPerLane * 2) + (within & 1) * 4);
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
                                              (__attribute__((address_space(3))) void *)(lsd + q * 64), 4, 0, 0);
         }
@@ -252,33 +258,35 @@ qgemm_kernel(const uint8_t *__restrict__ wp, const _Float16 *__restrict__ xs, co
 #pragma unroll
         for (int q = 0; q < NG; ++q) load_group(raw[q], p.s, p.nb, p.j0 / BPG + q);
     };
-    u32x4 rawn[NG][RG];
+    // Two register sets take turns: chunk ci computes from one while chunk
+    // ci + 1's weights load into the other (the loop is unrolled by two).
+    u32x4 rawA[NG][RG], rawB[NG][RG];
     if (n_chunks > 0) {
         stage(0, 0);
-        load_chunk(rawn, 0);
+        load_chunk(rawA, 0);
     }
-    for (int64_t ci = 0; ci < n_chunks; ++ci) {
+    auto chunk_step = [&](u32x4 (&cur)[NG][RG], u32x4 (&nxt)[NG][RG], int64_t ci) {
         // Everything this wavefront issued is chunk ci's: its copies into buffer
-        // ci & 1 and its weight groups, both issued one chunk earlier. Take the
-        // weights into working registers; after the barrier every wavefront's
-        // copies are in LDS and every wavefront is past chunk ci - 1, whose buffer
-        // the next copies take. Nothing issued after a load comes between that
-        // load and its use, so no wait below covers the next chunk's loads.
+        // ci & 1 and its weight groups, both issued one chunk earlier. After the
+        // barrier every wavefront's copies are in LDS and every wavefront is past
+        // chunk ci - 1, whose buffer the next copies take. Nothing issued after a
+        // load comes between that load and its use, so no wait below covers the
+        // next chunk's loads.
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         uint32_t v[NG][RG][4];
 #pragma unroll
         for (int q = 0; q < NG; ++q)
 #pragma unroll
             for (int rg = 0; rg < RG; ++rg) {
-                v[q][rg][0] = rawn[q][rg].x;
-                v[q][rg][1] = rawn[q][rg].y;
-                v[q][rg][2] = rawn[q][rg].z;
-                v[q][rg][3] = rawn[q][rg].w;
+                v[q][rg][0] = cur[q][rg].x;
+                v[q][rg][1] = cur[q][rg].y;
+                v[q][rg][2] = cur[q][rg].z;
+                v[q][rg][3] = cur[q][rg].w;
             }
         __syncthreads();
         if (ci + 1 < n_chunks) {
             stage((int)((ci + 1) & 1), ci + 1);
-            load_chunk(rawn, ci + 1);
+            load_chunk(nxt, ci + 1);
         }
         const ChunkPos cp = chunk_at(ci);
         const int nb = cp.nb, nbc = cp.nbc, j0 = cp.j0;
@@ -347,7 +355,13 @@ qgemm_kernel(const uint8_t *__restrict__ wp, const _Float16 *__restrict__ xs, co
                     seg[rg][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
                 }
         }
+    };
+    int64_t ci = 0;
+    for (; ci + 1 < n_chunks; ci += 2) {
+        chunk_step(rawA, rawB, ci);
+        chunk_step(rawB, rawA, ci + 1);
     }
+    if (ci < n_chunks) chunk_step(rawA, rawB, ci);
 
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
