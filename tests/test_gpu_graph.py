@@ -67,3 +67,33 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for (name, _, out), r in zip(calls, ref):
             assert out.cpu().numpy().tobytes() == r.cpu().numpy().tobytes(), f"replay {rep}: {name} differs from eager"
+
+
+def test_graph_capture_of_a_kernel_not_yet_launched():
+    # A verify call whose activations exceed LDS at once (Q4_0 5120x17408, M = 5:
+    # staged in phases, about 130 KiB of LDS) captured before the process has ever
+    # launched that kernel: its first launch, with the dynamic-LDS limit it needs,
+    # happens inside the capture. Every replay must equal an eager call made after.
+    torch = torch_dev()
+    rng = np.random.default_rng(2025)
+    kind, N, K, M = "q4_0", 5120, 17408, 5
+    w = qg.pack_weights(kind, W.matrix(kind, N, K, rng), N, K)
+    X = to_dev(W.activation(K, rng, M=M))
+    Y = empty_f32(M * N)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    announce("graph capture of a first launch (phased verify)")
+    with torch.cuda.graph(g, stream=side, capture_error_mode="thread_local"):
+        qg.qgemv_verify(kind, w, X, Y, N, K, M, side.cuda_stream)
+    ref = empty_f32(M * N)
+    qg.qgemv_verify(kind, w, X, ref, N, K, M)
+    torch.cuda.synchronize()
+    want = ref.cpu().numpy().tobytes()
+    for rep in range(3):
+        Y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        announce(f"graph replay {rep} (phased verify)")
+        g.replay()
+        torch.cuda.synchronize()
+        assert Y.cpu().numpy().tobytes() == want, f"replay {rep} differs from the eager call"
