@@ -22,8 +22,9 @@ CASES = [("q4_0", 17408, 5120), ("q8_0", 4096, 1024), ("q8_0", 33, 2080), ("q4_0
          # three segments: K split three ways (one segment per wavefront)
          ("q4_k", 1024, 3072), ("q6_k", 77, 3072), ("q8_0", 1024, 3072),
          # M K 4 bytes above the LDS from M = 3: the persistent form walks its 17 K
-         # ranges in phases, staging one window of activations at a time
-         ("q4_0", 5120, 17408), ("q6_k", 2001, 17408)]
+         # ranges in phases, staging one window of activations at a time; 17504
+         # has 18 ranges, the last segment 3 blocks long (zero-filled in its window)
+         ("q4_0", 5120, 17408), ("q6_k", 2001, 17408), ("q4_0", 3000, 17504)]
 
 
 @pytest.mark.parametrize("kind,N,K", CASES)
