@@ -129,7 +129,7 @@ int split_k_waves(int64_t rows, int64_t K)
     if (forced == 1 || forced == 2 || forced == 3 || forced == 4 || forced == 8)
         return forced <= nseg ? (int)forced : 1;
     int W = 1;
-    while (W < 4 && 2 * W <= nseg && n_tiles * W < 2048) W *= 2;
+    while (W < 8 && 2 * W <= nseg && n_tiles * W < 2048) W *= 2;
     if (W == 2 && nseg == 3) W = 3;
     return W;
 }
@@ -281,7 +281,10 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M, bool norm = false)
     p.grid = (groups + G - 1) / G;
     const double tiles_per_group = p.tstride > 0 ? (double)g.n_tiles / (double)p.tstride : (double)p.tpg;
     const double wg_weight_bytes = (double)G * tiles_per_group * (double)(g.tile_q + g.tile_s);
-    bool lds = xbytes <= lds_limit && (M > 1 || wg_weight_bytes >= 2.0 * (double)xbytes);
+    // A split tile's wavefronts (W > 1) take their activations from one staged copy
+    // (measured faster than each reading its range from L2, e.g. Q4_0 640 x 17408
+    // at W = 8: 8.1 against 8.6 us).
+    bool lds = xbytes <= lds_limit && (M > 1 || p.W > 1 || wg_weight_bytes >= 2.0 * (double)xbytes);
     if (xg_env == 0 || xg_env == 1) lds = xbytes <= lds_limit && xg_env == 0;
     if (norm) lds = xbytes <= kLdsLimitMulti;   // the prologue normalises the staged copy
     p.x_in_lds = lds;
