@@ -549,8 +549,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {max(args.gpus, world)} is not supported "
-              "(the GEMV shards by output rows with no communication; see the design notes)", file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU; --gpus {max(args.gpus, world)} is not supported "
+              "(the GEMV would shard by output rows with no communication)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -9,7 +9,7 @@ if ROOT not in sys.path:
 
 
 def pytest_configure(config):
-    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950); run with -m gpu on the GPU box")
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950); run with -m gpu on a machine with one")
 
 
 @pytest.fixture(scope="session")
