@@ -268,6 +268,20 @@ def test_plan_info_three_segments_get_three_wavefronts(L):
     assert not p["persistent"] and p["split_k_ways"] == 1
 
 
+def test_plan_info_long_rows_split_eight_ways_over_staged_activations(L):
+    # few row tiles and 16 or more segments: eight wavefronts per tile at every M,
+    # taking their activations from one staged copy whenever it fits in LDS
+    for kind in ("q8_0", "q4_0"):
+        for N, K in ((640, 17408), (1280, 8192), (24, 32768)):
+            for M in (1, 4, 6):
+                p = qg.qg_plan_info(kind, N, K, M)
+                assert not p["persistent"] and p["split_k_ways"] == 8, (kind, N, K, M, p)
+        assert qg.qg_plan_info(kind, 640, 17408)["x_in_lds"]
+        assert qg.qg_plan_info(kind, 1280, 8192, 2)["x_in_lds"]
+        # 16 segments but 4096 row tiles: one wavefront per tile
+        assert qg.qg_plan_info(kind, 8 * 4096, 16384)["split_k_ways"] == 1
+
+
 def test_tuning_overrides_are_read_on_reload(L, monkeypatch):
     # the launch-shape overrides are read once and on qg_reload_tuning(), not per call
     assert qg.qg_plan_info("q4_0", 5120, 17408)["persistent"]
