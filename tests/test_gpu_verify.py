@@ -24,7 +24,10 @@ CASES = [("q4_0", 17408, 5120), ("q8_0", 4096, 1024), ("q8_0", 33, 2080), ("q4_0
          # M K 4 bytes above the LDS from M = 3: the persistent form walks its 17 K
          # ranges in phases, staging one window of activations at a time; 17504
          # has 18 ranges, the last segment 3 blocks long (zero-filled in its window)
-         ("q4_0", 5120, 17408), ("q6_k", 2001, 17408), ("q4_0", 3000, 17504)]
+         ("q4_0", 5120, 17408), ("q6_k", 2001, 17408), ("q4_0", 3000, 17504),
+         # super-block types on 80 row tiles of 17 segments: K split eight ways at
+         # every M, activations from L2 at M = 5, 6 (kernels that spill to scratch)
+         ("q4_k", 640, 17408), ("q6_k", 640, 17408)]
 
 
 @pytest.mark.parametrize("kind,N,K", CASES)
