@@ -271,7 +271,7 @@ def test_plan_info_three_segments_get_three_wavefronts(L):
 def test_plan_info_long_rows_split_eight_ways_over_staged_activations(L):
     # few row tiles and 16 or more segments: eight wavefronts per tile at every M,
     # taking their activations from one staged copy whenever it fits in LDS
-    for kind in ("q8_0", "q4_0"):
+    for kind in ("q8_0", "q4_0", "q4_k", "q6_k"):
         for N, K in ((640, 17408), (1280, 8192), (24, 32768)):
             for M in (1, 4, 6):
                 p = qg.qg_plan_info(kind, N, K, M)
@@ -280,6 +280,9 @@ def test_plan_info_long_rows_split_eight_ways_over_staged_activations(L):
         assert qg.qg_plan_info(kind, 1280, 8192, 2)["x_in_lds"]
         # 16 segments but 4096 row tiles: one wavefront per tile
         assert qg.qg_plan_info(kind, 8 * 4096, 16384)["split_k_ways"] == 1
+        # M K 4 bytes over the 160 KiB of LDS (M >= 3 at K = 17408): every row from L2
+        assert qg.qg_plan_info(kind, 640, 17408, 2)["x_in_lds"]
+        assert not any(qg.qg_plan_info(kind, 640, 17408, M)["x_in_lds"] for M in (3, 4, 5, 6))
 
 
 def test_tuning_overrides_are_read_on_reload(L, monkeypatch):
