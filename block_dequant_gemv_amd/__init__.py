@@ -84,8 +84,8 @@ def lib():
             "qgemv_verify": ([i32, vp, vp, vp, i64, i64, i32, vp], i32),
             "qg_status_str": ([i32], ctypes.c_char_p),
             "qg_last_error": ([], ctypes.c_char_p),
-            "qg_plan_info": ([i32, i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i64),
-                              ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
+            "qg_plan_info": ([i32, i64, i64, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i64),
+                              ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i64)], i32),
             "qg_time_next_launch": ([vp, vp], i32),
             "qg_reload_tuning": ([], i32),
         }
@@ -284,15 +284,17 @@ def qg_last_error() -> str:
     return lib().qg_last_error().decode()
 
 
-def qg_plan_info(qtype, N: int, K: int, M: int = 1) -> dict:
+def qg_plan_info(qtype, N: int, K: int, M: int = 1, rmsnorm: bool = False) -> dict:
     w = ctypes.c_int()
     g = ctypes.c_int64()
     xl = ctypes.c_int()
     ps = ctypes.c_int()
-    _check("qg_plan_info", lib().qg_plan_info(_qtype(qtype), N, K, M, ctypes.byref(w), ctypes.byref(g),
-                                              ctypes.byref(xl), ctypes.byref(ps)))
+    lds = ctypes.c_int64()
+    _check("qg_plan_info", lib().qg_plan_info(_qtype(qtype), N, K, M, 1 if rmsnorm else 0, ctypes.byref(w),
+                                              ctypes.byref(g), ctypes.byref(xl), ctypes.byref(ps),
+                                              ctypes.byref(lds)))
     return {"split_k_ways": w.value, "workgroups": g.value, "x_in_lds": bool(xl.value),
-            "persistent": bool(ps.value)}
+            "persistent": bool(ps.value), "lds_bytes": lds.value}
 
 
 def qg_reload_tuning():

@@ -13,6 +13,13 @@ Flags:
                                   ordinary VGPRs, which the per-block scale fma reads
                                   directly, instead of accumulation registers that
                                   need one v_accvgpr_read per value.
+
+The quantised GEMV templates (csrc/qgemv_device.h) are instantiated by
+csrc/qgemv_inst.hip, compiled once per (qtype, activation rows) pair with
+-DQG_INST_QT / -DQG_INST_M, so that the instantiations build in parallel.
+The host pass of hipcc does not know the packed-fp32 target feature and says so
+once per compile; that one line is dropped from the compiler output, every other
+diagnostic is shown.
 """
 from __future__ import annotations
 
@@ -27,7 +34,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqgemv.so")
 SOURCES = ["qgemv_kernels.hip", "qgemm_kernels.hip", "qgemv_api.hip"]
-HEADERS = ["layout.h", "dequant.h", "qgemv_kernels.h", "qgemm_kernels.h"]
+HEADERS = ["layout.h", "dequant.h", "qgemv_kernels.h", "qgemv_device.h", "qgemm_kernels.h"]
+INST_SOURCE = "qgemv_inst.hip"
+# (qtype code of layout.h, activation rows): 1 = Q8_0, 2 = Q4_0, 3 = Q4_K, 4 = Q6_K
+INSTANCES = [(qt, m) for qt in (1, 2, 3, 4) for m in range(1, 7)]
+HOST_FEATURE_NOTE = "'-packed-fp32-ops' is not a recognized feature for this target"
 SOURCE_FLAGS = {"qgemm_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
@@ -46,23 +57,45 @@ def flags() -> list[str]:
             "-I", INCLUDE, "-I", CSRC]
 
 
+def compile_jobs(cc: str, build_dir: str, extra: list[str]) -> list[tuple[list[str], str, str]]:
+    """(command, object, label) of every translation unit."""
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
+        jobs.append(([cc, *flags(), *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj],
+                     obj, src))
+    for qt, m in INSTANCES:
+        obj = os.path.join(build_dir, f"qgemv_inst_t{qt}_m{m}.o")
+        jobs.append(([cc, *flags(), f"-DQG_INST_QT={qt}", f"-DQG_INST_M={m}", *extra, "-c",
+                      os.path.join(CSRC, INST_SOURCE), "-o", obj], obj, f"{INST_SOURCE} (qtype {qt}, M={m})"))
+    return jobs
+
+
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     """Compile every HIP source into block_dequant_gemv_amd/libqgemv.so (always rebuilds)."""
     cc = hipcc()
-    objs = []
     build_dir = os.path.join(PKG, "_build")
     os.makedirs(build_dir, exist_ok=True)
-    procs = []
-    for src in SOURCES:
-        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
-        cmd = [cc, *flags(), *SOURCE_FLAGS.get(src, []), *(extra or []), "-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd), file=sys.stderr)
-        procs.append((subprocess.Popen(cmd), src))
-        objs.append(obj)
-    for p, src in procs:
-        if p.wait() != 0:
-            raise RuntimeError(f"hipcc failed on {src}")
+    jobs = compile_jobs(cc, build_dir, list(extra or []))
+    width = max(1, min(len(jobs), os.cpu_count() or 1, 16))
+    pending, running, failed = list(jobs), [], []
+    while pending or running:
+        while pending and len(running) < width:
+            cmd, obj, label = pending.pop(0)
+            if verbose:
+                print(" ".join(cmd), file=sys.stderr)
+            running.append((subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True),
+                            label))
+        proc, label = running.pop(0)
+        out, _ = proc.communicate()
+        lines = [ln for ln in out.splitlines() if HOST_FEATURE_NOTE not in ln]
+        if lines:
+            print("\n".join(lines), file=sys.stderr)
+        if proc.returncode != 0:
+            failed.append(label)
+    if failed:
+        raise RuntimeError(f"hipcc failed on {', '.join(failed)}")
+    objs = [obj for _, obj, _ in jobs]
     tmp = LIB + ".tmp"
     link = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

@@ -134,8 +134,8 @@ int split_k_waves(int64_t rows, int64_t K)
     return W;
 }
 
-constexpr size_t kLdsLimit = 96 * 1024;        // single-row calls: above this, x is read from global memory
-constexpr size_t kLdsLimitMulti = 160 * 1024;  // verify calls: the whole LDS of a CU (gfx950)
+constexpr size_t kLdsLimit = 96 * 1024;                        // single-row calls: above this, x is read from L2
+constexpr size_t kLdsLimitMulti = qgk::kLdsPerWorkgroup;       // verify calls: the whole LDS of a CU (gfx950)
 
 // Launch shape of the one-wavefront-per-tile form (measured on MI355X with
 // cold weights):
@@ -191,8 +191,12 @@ bool plan_persist(int64_t rows, int64_t K, int64_t *ranges, int64_t *grid, int64
     return true;
 }
 
-// The RMSNorm prologue needs the activations staged in LDS: at most 160 KiB of them.
-constexpr int64_t kNormMaxK = (int64_t)(160 * 1024 / sizeof(float));
+// The RMSNorm prologue needs the activations staged in LDS: whole 1024-weight
+// segments of them next to the largest static array of the one-wavefront-per-tile
+// form (8 split-K wavefronts), i.e. K <= 39 * 1024 = 39936.
+constexpr int64_t kNormMaxK =
+    (int64_t)((kLdsLimitMulti - qgk::static_lds_bytes(qgk::tile_red_floats(1, 8, true))) /
+              (qgl::kSegWeights * sizeof(float))) * qgl::kSegWeights;
 
 qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M, bool norm = false)
 {
@@ -213,7 +217,9 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M, bool norm = false)
         p.W = (int)ranges;
         p.grid = pgrid;
         const size_t part = ranges > 1 ? (size_t)max_tiles * ranges * M * qgl::kTileRows * 4 : 0;
-        bool lds = xbytes + part <= kLdsLimitMulti;
+        // LDS left for the activations and the partials next to the static array
+        const size_t budget = kLdsLimitMulti - qgk::static_lds_bytes(qgk::persist_red_floats(norm));
+        bool lds = xbytes + part <= budget;
         // Several activation rows that do not fit (M K 4 bytes above the LDS):
         // walk the K ranges in the fewest phases whose largest activation window
         // (ceil(ranges / phases) ranges) fits, instead of reading every unit's
@@ -225,7 +231,7 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M, bool norm = false)
         auto window = [&](int64_t ph) { return (size_t)((ranges + ph - 1) / ph * seg_per_range) * seg_bytes; };
         if (!lds && M > 1 && !norm) {
             for (int64_t ph = 2; ph <= ranges; ++ph)
-                if (window(ph) + part <= kLdsLimitMulti) {
+                if (window(ph) + part <= budget) {
                     p.phases = (int)ph;
                     lds = true;
                     break;
@@ -233,10 +239,16 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M, bool norm = false)
         }
         if (!norm && (xg_env == 0 || xg_env == 1)) lds = lds && xg_env == 0;
         if (!lds) p.phases = 1;
-        p.x_in_lds = lds;
-        p.lds_bytes = (lds ? window(p.phases) : 0) + part;
-        p.block = qgk::persist_threads(qt, M, lds);
-        return p;
+        if (lds || !norm) {
+            p.x_in_lds = lds;
+            p.lds_bytes = (lds ? window(p.phases) : 0) + part;
+            p.block = qgk::persist_threads(qt, M, lds);
+            return p;
+        }
+        // The RMSNorm prologue needs the staged copy: when it does not fit next to
+        // the partials, use the other form, which needs no partials in LDS.
+        p.persist = false;
+        p.phases = 1;
     }
     p.ranges = 1;
     p.max_tiles = 0;
@@ -281,12 +293,15 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M, bool norm = false)
     p.grid = (groups + G - 1) / G;
     const double tiles_per_group = p.tstride > 0 ? (double)g.n_tiles / (double)p.tstride : (double)p.tpg;
     const double wg_weight_bytes = (double)G * tiles_per_group * (double)(g.tile_q + g.tile_s);
+    // The staged copy must fit next to the kernel's static array (the split-K
+    // partials of W > 1 wavefronts take up to 1.5 KiB).
+    const bool fits = xbytes + qgk::static_lds_bytes(qgk::tile_red_floats(M, p.W, norm)) <= kLdsLimitMulti;
     // A split tile's wavefronts (W > 1) take their activations from one staged copy
     // (measured faster than each reading its range from L2, e.g. Q4_0 640 x 17408
     // at W = 8: 8.1 against 8.6 us).
-    bool lds = xbytes <= lds_limit && (M > 1 || p.W > 1 || wg_weight_bytes >= 2.0 * (double)xbytes);
-    if (xg_env == 0 || xg_env == 1) lds = xbytes <= lds_limit && xg_env == 0;
-    if (norm) lds = xbytes <= kLdsLimitMulti;   // the prologue normalises the staged copy
+    bool lds = fits && xbytes <= lds_limit && (M > 1 || p.W > 1 || wg_weight_bytes >= 2.0 * (double)xbytes);
+    if (xg_env == 0 || xg_env == 1) lds = fits && xbytes <= lds_limit && xg_env == 0;
+    if (norm) lds = fits;   // the prologue normalises the staged copy
     p.x_in_lds = lds;
     p.lds_bytes = p.x_in_lds ? xbytes : 0;
     // Prefetch depth: one unit in flight ahead of the one being computed. A
@@ -754,17 +769,27 @@ const char *qg_status_str(int status)
 
 const char *qg_last_error(void) { return g_last_error.c_str(); }
 
-qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int *split_k_ways, int64_t *workgroups,
-                       int *x_in_lds, int *persistent)
+qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int rmsnorm, int *split_k_ways, int64_t *workgroups,
+                       int *x_in_lds, int *persistent, int64_t *lds_bytes)
 {
     qg_status st = check_qshape(qtype, N, K, "qg_plan_info");
     if (st) return st;
     if (M < 1 || M > 6) return fail(QG_EUNSUPPORTED, "qg_plan_info: M=%d", M);
-    const qgk::QPlan p = make_qplan(qtype, N, K, M);
+    const bool norm = rmsnorm != 0;
+    if (norm && M != 1) return fail(QG_EUNSUPPORTED, "qg_plan_info: the RMSNorm prologue takes M = 1");
+    if (norm && K > kNormMaxK)
+        return fail(QG_EUNSUPPORTED, "qg_plan_info: K=%lld above %lld (the normalised activations live in LDS)",
+                    (long long)K, (long long)kNormMaxK);
+    const qgk::QPlan p = make_qplan(qtype, N, K, M, norm);
+    if (norm && !p.x_in_lds) return fail(QG_EUNSUPPORTED, "qg_plan_info: activations do not fit in LDS");
     if (split_k_ways) *split_k_ways = p.W;
     if (workgroups) *workgroups = p.grid;
     if (x_in_lds) *x_in_lds = p.x_in_lds ? 1 : 0;
     if (persistent) *persistent = p.persist ? 1 : 0;
+    if (lds_bytes) {
+        const int floats = p.persist ? qgk::persist_red_floats(norm) : qgk::tile_red_floats(M, p.W, norm);
+        *lds_bytes = (int64_t)(qgk::static_lds_bytes(floats) + p.lds_bytes);
+    }
     return ok();
 }
 

@@ -1,0 +1,1026 @@
+// qgemv_device.h -- the quantised GEMV kernels of libqgemv (gfx950) and their
+// launch templates. Each (qtype, activation rows) pair is instantiated in a
+// translation unit of its own (qgemv_inst.hip), so they build in parallel.
+//
+// Quantised GEMV (Q8_0 / Q4_0), its fused gate|up SiLU epilogue and the
+// multi-row verify all come from ONE kernel template, so that a row's
+// floating-point operations are the same whatever M is:
+//
+//   per lane, per block of 32 weights, per activation row m:
+//     s = 0;  s = fma(v_e, x_e, s) for e = 0..31      (v_e = q or nibble-8, exact in fp16)
+//     acc = fma(d, s, acc)                             (d = the block's fp16 scale)
+//   acc of the 32 lanes that share a row: fixed butterfly (DPP + swizzle)
+//   split-K wavefronts (if any): partials added in wavefront order in LDS
+//
+// Nothing in that sequence depends on M, on which wavefront or workgroup
+// handles the row, or on how many tiles a wavefront walks, so row m of the
+// verify output equals the M=1 output bit for bit. The build uses
+// -ffp-contract=off and every multiply-add is an explicit fma.
+//
+// Memory: each lane loads 16-byte units of the packed planes (layout.h); a
+// wavefront load instruction reads 1 KiB contiguous. Activations are staged
+// once per workgroup into LDS in a lane-swizzled order (chunk c of block j at
+// float4 slot c*32 + j), so the 32 lanes of a row read consecutive 16-byte
+// LDS words (no bank conflicts) and the two row slots of a wavefront read the
+// same words (broadcast).
+#pragma once
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "dequant.h"
+#include "layout.h"
+#include "qgemv_kernels.h"
+
+namespace qgk {
+
+using namespace qgl;
+
+// Sum over the 32 lanes of one wavefront half (lanes 0-31 and 32-63 separately).
+// Butterfly: xor 1, xor 2 (quad_perm), mirror within 8, mirror within 16 (DPP),
+// xor 16 (ds_swizzle). Every lane of the half ends with the same bits.
+__device__ __forceinline__ float half_wave_sum(float v)
+{
+    v += as_f(__builtin_amdgcn_update_dpp(0, as_i(v), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+    v += as_f(__builtin_amdgcn_update_dpp(0, as_i(v), 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+    v += as_f(__builtin_amdgcn_update_dpp(0, as_i(v), 0x141, 0xF, 0xF, false)); // row_half_mirror
+    v += as_f(__builtin_amdgcn_update_dpp(0, as_i(v), 0x140, 0xF, 0xF, false)); // row_mirror
+    v += as_f(__builtin_amdgcn_ds_swizzle(as_i(v), 0x401F));                     // lane ^ 16 within 32
+    return v;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u)
+{
+    return g / (1.0f + expf(-g)) * u;
+}
+
+// One lane's packed data for one (row tile, segment): 16 bytes per row and
+// half-block, plus the fp16 scales of its 4 rows (Q4_K: their 6-bit scales and
+// mins, and in `sup` the d and dmin of their super-blocks; Q6_K: their two int8
+// scales, in `hq` the high 2-bit parts of rows 0-1 and 2-3, and in `sup` d).
+template <int QT>
+struct Unit {
+    static constexpr int NH = (QT == kQ8_0) ? 2 : 1;
+    using Sup = typename std::conditional<QT == kQ6_K, u32x2, u32x4>::type;
+    u32x4 q[kRowsPerLane][NH];
+    u32x2 sc;
+    Sup sup;
+    u32x4 hq[2];
+};
+
+// A lane's place in a segment: the byte offset of its first 16-byte quant
+// unit and the block whose activations it reads, for full segments and for a
+// ragged last segment of nb_last < 32 blocks. In the ragged segment lanes
+// j >= nb_last read block nb_last - 1 again (in bounds) and count as dead:
+// their scales are zeroed, so they add nothing.
+struct LanePlace {
+    uint32_t off_full, off_last;   // (slot * nb + jc) * 16 for nb = 32 / nb_last
+    uint32_t str_last;             // bytes between the b/h units of the last segment (wave-uniform)
+    uint32_t sup_full, sup_last;   // Q4_K / Q6_K: slot * nb/8 + jc/8, the super-block scales of the 4 rows
+    int j_last;                    // jc in the last segment
+    bool live_last;
+};
+
+__device__ __forceinline__ LanePlace lane_place(const Geometry &g, int slot, int j)
+{
+    LanePlace p;
+    const int nb_last = (int)seg_blocks(g, g.nseg - 1);
+    p.j_last = j < nb_last ? j : nb_last - 1;
+    p.live_last = j < nb_last;
+    p.off_full = (uint32_t)(slot * kSegBlocks + j) * kUnit;
+    p.off_last = (uint32_t)(slot * nb_last + p.j_last) * kUnit;
+    p.str_last = (uint32_t)(kSlots * nb_last * kUnit);
+    p.sup_full = (uint32_t)(slot * (kSegBlocks / kSuperBlocks) + j / kSuperBlocks);
+    p.sup_last = (uint32_t)(slot * (nb_last / kSuperBlocks) + p.j_last / kSuperBlocks);
+    return p;
+}
+
+// Issue the loads of tile t, segment s (t, s wave-uniform): a wave-uniform
+// base address plus the lane's 32-bit offset. With `real` false (no unit
+// left) every lane loads the first 16 bytes of the buffer instead, one cache
+// line per wavefront. The loop body thus always issues the same loads with no
+// branch around them, so the compiler's wait counts keep the next unit in
+// flight while the current one is computed.
+template <int QT>
+__device__ __forceinline__ void load_unit(Unit<QT> &u, const uint8_t *__restrict__ wp, const Geometry &g, int64_t t,
+                                          int64_t s, const LanePlace &lp, bool real)
+{
+    constexpr int NH = Unit<QT>::NH;
+    constexpr int64_t seg_q = (int64_t)kTileRows * kSegBlocks * packed_quant_bytes(QT);   // bytes per segment
+    constexpr uint32_t str_full = (uint32_t)(kSlots * kSegBlocks * kUnit);
+    t = real ? t : 0;
+    s = real ? s : 0;
+    const bool last = s == g.nseg - 1;
+    const uint32_t off = real ? (last ? lp.off_last : lp.off_full) : 0u;
+    const uint32_t ustride = real ? (last ? lp.str_last : str_full) : 0u;
+    const uint8_t *base = wp + t * g.tile_q + s * seg_q;
+#pragma unroll
+    for (int b = 0; b < kRowsPerLane; ++b)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            const uint8_t *ub = base + (uint32_t)(b * NH + h) * ustride;
+            u.q[b][h] = __builtin_nontemporal_load((const u32x4 *)(ub + off));
+        }
+    // scales: (slot * nb + jc) * 8 bytes = half the quant offset
+    const uint8_t *sbase = wp + g.scale_off + t * g.tile_s + s * (int64_t)(kTileRows * kSegBlocks * 2);
+    u.sc = __builtin_nontemporal_load((const u32x2 *)(sbase + (off >> 1)));
+    if constexpr (QT == kQ4_K || QT == kQ6_K) {
+        constexpr uint32_t ub = (QT == kQ4_K) ? 4 : 2;   // super-plane bytes per row
+        const uint32_t so = real ? (last ? lp.sup_last : lp.sup_full) * (kRowsPerLane * ub) : 0u;
+        const uint8_t *ubase = wp + g.sup_off + t * g.tile_u + s * (int64_t)(kTileRows * (kSegBlocks / kSuperBlocks) * ub);
+        u.sup = __builtin_nontemporal_load((const typename Unit<QT>::Sup *)(ubase + so));
+    }
+    if constexpr (QT == kQ6_K) {
+#pragma unroll
+        for (int bp = 0; bp < 2; ++bp)
+            u.hq[bp] = __builtin_nontemporal_load((const u32x4 *)(base + (uint32_t)(kRowsPerLane + bp) * ustride + off));
+    }
+}
+
+// acc[m][b] += d_b * sum_e v_e * x_m[e] over the lane's block of segment s.
+// j is the block whose activations the lane reads; live is false only for
+// lanes past the end of a ragged last segment.
+// Q4_K: acc[m][b] += d*sc * sum_e q_e x_e - dmin*mn * sum_e x_e over the lane's
+// sub-block (the weight's two terms summed apart, as the k-quant dot product
+// does): one fma per weight and row, and each row's sum of x shared by the 4
+// weight rows. The quants arrive as fp16 subnormals q * 2^-24 (elements 0, 1 of
+// each 4) and q * 2^-20 (elements 2, 3), summed in two accumulators and joined
+// exactly up to one rounding; the 2^24 goes into d*sc. d*sc and dmin*mn are
+// exact (11-bit by 6-bit products). Dead lanes of a ragged segment get zero
+// scales and mins: they add 0. Every activation row goes through the same
+// operations for any M.
+template <int M, bool XLDS>
+__device__ __forceinline__ void compute_unit_q4k(const Unit<kQ4_K> &u, float (&acc)[M][kRowsPerLane],
+                                                 const Consts &k, const f32x4 *xs4, const float *__restrict__ x,
+                                                 int64_t x_stride, int64_t nseg, int64_t s, int j, bool live)
+{
+    constexpr int B = kRowsPerLane;
+    float s24[M][B], s20[M][B], sx[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        sx[m] = 0.0f;
+#pragma unroll
+        for (int b = 0; b < B; ++b) s24[m][b] = s20[m][b] = 0.0f;
+    }
+    const uint32_t x_row = (uint32_t)nseg << 8;
+    const f32x4 *xl = xs4 + ((uint32_t)s << 8) + (uint32_t)j;
+    const float *xg = x + s * kSegWeights + j * 32;
+    auto row_fma = [&](const h2 (&p)[4], const f32x4 (&xv)[2], int m, int b) {
+        float lo = s24[m][b], hi = s20[m][b];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            lo = __builtin_fmaf((float)p[2 * cc].x, xv[cc].x, lo);
+            lo = __builtin_fmaf((float)p[2 * cc].y, xv[cc].y, lo);
+            hi = __builtin_fmaf((float)p[2 * cc + 1].x, xv[cc].z, hi);
+            hi = __builtin_fmaf((float)p[2 * cc + 1].y, xv[cc].w, hi);
+        }
+        s24[m][b] = lo;
+        s20[m][b] = hi;
+    };
+    // Per dword of 8 elements. One activation row: its 2 float4 of x, then the 4
+    // weight rows one at a time. Several: the 4 weight rows' pairs once, then the
+    // activation rows one at a time (2 float4 of x live, not 2 M). Each
+    // accumulator sees the same operations in the same order either way.
+#pragma unroll
+    for (int c = 0; c < 8; c += 2) {
+        auto load_x = [&](f32x4 (&xv)[2], int m) {
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+                xv[cc] = XLDS ? xl[m * x_row + (c + cc) * 32] : *(const f32x4 *)(xg + m * x_stride + (c + cc) * 4);
+            sx[m] = sx[m] + (((xv[0].x + xv[0].y) + (xv[0].z + xv[0].w)) + ((xv[1].x + xv[1].y) + (xv[1].z + xv[1].w)));
+        };
+        if constexpr (M == 1) {
+            f32x4 xv[2];
+            load_x(xv, 0);
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                h2 p[4];
+                q4k_pairs(u.q[b][0][c >> 1], k, p);
+                row_fma(p, xv, 0, b);
+            }
+        } else {
+            h2 p[B][4];
+#pragma unroll
+            for (int b = 0; b < B; ++b) q4k_pairs(u.q[b][0][c >> 1], k, p[b]);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                f32x4 xv[2];
+                load_x(xv, m);
+#pragma unroll
+                for (int b = 0; b < B; ++b) row_fma(p[b], xv, m, b);
+            }
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const uint32_t sw = ((b < 2) ? u.sc.x : u.sc.y) >> (16 * (b & 1));   // byte 0: sc, byte 1: mn
+        const h2 dd = as_h2(u.sup[b]);                                        // (d, dmin)
+        const float scl = live ? (float)dd.x * (float)(sw & 0xFFu) * 16777216.0f : 0.0f;
+        const float mnv = live ? (float)dd.y * (float)((sw >> 8) & 0xFFu) : 0.0f;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float sq = __builtin_fmaf(s20[m][b], 0.0625f, s24[m][b]);   // sum q x * 2^-24
+            acc[m][b] = acc[m][b] + __builtin_fmaf(scl, sq, -(mnv * sx[m]));
+        }
+    }
+}
+
+// Q6_K: acc[m][b] += d * (sc_lo * sum_{e<16} v_e x_e + sc_hi * sum_{e>=16} v_e x_e)
+// with v = q - 32 exact in fp16: the low nibble goes into a magic-number fp16
+// (1024 + q or 1024 + 16 q) as in Q4_0 and the high 2 bits are OR-ed in above it
+// from the row's dword of high parts (a shift by 0 / 2 for the first 16 elements'
+// dword halves, a rotation by 24 and a shift by 2 for the second), then -1056 or
+// (/16 - 96). One fp32 fma per weight and row, as for Q4_0; the int8 scales are
+// exact in fp32. Dead lanes of a ragged segment get d = 0. Every activation row
+// goes through the same operations for any M.
+template <int M, bool XLDS>
+__device__ __forceinline__ void compute_unit_q6k(const Unit<kQ6_K> &u, float (&acc)[M][kRowsPerLane],
+                                                 const Consts &k, const f32x4 *xs4, const float *__restrict__ x,
+                                                 int64_t x_stride, int64_t nseg, int64_t s, int j, bool live)
+{
+    constexpr int B = kRowsPerLane;
+    float s16[M][B][2];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int b = 0; b < B; ++b) s16[m][b][0] = s16[m][b][1] = 0.0f;
+    const uint32_t x_row = (uint32_t)nseg << 8;
+    const f32x4 *xl = xs4 + ((uint32_t)s << 8) + (uint32_t)j;
+    const float *xg = x + s * kSegWeights + j * 32;
+    // Per dword of 8 elements, in the same two loop orders as Q4_K above.
+#pragma unroll
+    for (int c = 0; c < 8; c += 2) {
+        const int dw = c >> 1;   // dword of 8 elements: 8 dw .. 8 dw + 7
+        auto pairs = [&](h2 (&p)[4], int b) {
+            const u32x4 &hv = u.hq[b >> 1];
+            q6k_pairs(u.q[b][0][dw], hv[2 * (b & 1) + (dw >> 1)], (dw & 1) != 0, k, p);
+        };
+        auto load_x = [&](f32x4 (&xv)[2], int m) {
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+                xv[cc] = XLDS ? xl[m * x_row + (c + cc) * 32] : *(const f32x4 *)(xg + m * x_stride + (c + cc) * 4);
+        };
+        auto row_fma = [&](const h2 (&p)[4], const f32x4 (&xv)[2], int m, int b) {
+            float s_ = s16[m][b][dw >> 1];
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                s_ = __builtin_fmaf((float)p[2 * cc].x, xv[cc].x, s_);
+                s_ = __builtin_fmaf((float)p[2 * cc].y, xv[cc].y, s_);
+                s_ = __builtin_fmaf((float)p[2 * cc + 1].x, xv[cc].z, s_);
+                s_ = __builtin_fmaf((float)p[2 * cc + 1].y, xv[cc].w, s_);
+            }
+            s16[m][b][dw >> 1] = s_;
+        };
+        if constexpr (M == 1) {
+            f32x4 xv[2];
+            load_x(xv, 0);
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                h2 p[4];
+                pairs(p, b);
+                row_fma(p, xv, 0, b);
+            }
+        } else {
+            h2 p[B][4];
+#pragma unroll
+            for (int b = 0; b < B; ++b) pairs(p[b], b);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                f32x4 xv[2];
+                load_x(xv, m);
+#pragma unroll
+                for (int b = 0; b < B; ++b) row_fma(p[b], xv, m, b);
+            }
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const uint32_t sw = ((b < 2) ? u.sc.x : u.sc.y) >> (16 * (b & 1));   // byte 0: sc_lo, byte 1: sc_hi
+        const float sc_lo = (float)(int8_t)(sw & 0xFFu);
+        const float sc_hi = (float)(int8_t)((sw >> 8) & 0xFFu);
+        const uint32_t dw = ((b < 2) ? u.sup.x : u.sup.y) >> (16 * (b & 1));
+        const float d = live ? (float)as_h2(dw).x : 0.0f;
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            acc[m][b] = __builtin_fmaf(d, __builtin_fmaf(sc_hi, s16[m][b][1], sc_lo * s16[m][b][0]), acc[m][b]);
+    }
+}
+
+template <int QT, int M, bool XLDS>
+__device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][kRowsPerLane], const Consts &k,
+                                             const f32x4 *xs4, const float *__restrict__ x, int64_t x_stride,
+                                             int64_t nseg, int64_t s, int j, bool live)
+{
+    if constexpr (QT == kQ4_K) {
+        compute_unit_q4k<M, XLDS>(u, acc, k, xs4, x, x_stride, nseg, s, j, live);
+        return;
+    }
+    if constexpr (QT == kQ6_K) {
+        compute_unit_q6k<M, XLDS>(u, acc, k, xs4, x, x_stride, nseg, s, j, live);
+        return;
+    }
+    constexpr int B = kRowsPerLane;
+    float sb[M][B];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int b = 0; b < B; ++b) sb[m][b] = 0.0f;
+    // LDS: row m, segment s, chunk c of block j at float4 m*nseg*256 + s*256 + c*32 + j
+    const uint32_t x_row = (uint32_t)nseg << 8;
+    const f32x4 *xl = xs4 + ((uint32_t)s << 8) + (uint32_t)j;
+    const float *xg = x + s * kSegWeights + j * 32;
+
+    // 8 float4 chunks of x per block; Q4_0 consumes 2 chunks per dword, Q8_0 one.
+    // Per dword of 8 elements, one activation row: its 2 float4 of x, then the 4
+    // weight rows one at a time. Several: the 4 weight rows' fp16 pairs once, then
+    // the activation rows one at a time (2 float4 of x live, not 2 M). Each
+    // accumulator sees the same 8 fmas in the same order either way.
+    auto pairs = [&](int b, int c, h2 (&p)[4]) {
+        if (QT == kQ4_0) {
+            q4_pairs(u.q[b][0][c >> 1], k, p);
+        } else {
+            h2 p01[2], p23[2];
+            q8_pairs(u.q[b][c >> 2][c & 3], p01);
+            q8_pairs(u.q[b][c >> 2][(c & 3) + 1], p23);
+            p[0] = p01[0];
+            p[1] = p01[1];
+            p[2] = p23[0];
+            p[3] = p23[1];
+        }
+    };
+    auto load_x = [&](f32x4 (&xv)[2], int m, int c) {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+            xv[cc] = XLDS ? xl[m * x_row + (c + cc) * 32] : *(const f32x4 *)(xg + m * x_stride + (c + cc) * 4);
+    };
+    auto row_fma = [&](const h2 (&p)[4], const f32x4 (&xv)[2], int m, int b) {
+        float s_ = sb[m][b];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            s_ = __builtin_fmaf((float)p[2 * cc].x, xv[cc].x, s_);
+            s_ = __builtin_fmaf((float)p[2 * cc].y, xv[cc].y, s_);
+            s_ = __builtin_fmaf((float)p[2 * cc + 1].x, xv[cc].z, s_);
+            s_ = __builtin_fmaf((float)p[2 * cc + 1].y, xv[cc].w, s_);
+        }
+        sb[m][b] = s_;
+    };
+#pragma unroll
+    for (int c = 0; c < 8; c += 2) {
+        if constexpr (M == 1) {
+            f32x4 xv[2];
+            load_x(xv, 0, c);
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                h2 p[4];
+                pairs(b, c, p);
+                row_fma(p, xv, 0, b);
+            }
+        } else {
+            h2 p[B][4];
+#pragma unroll
+            for (int b = 0; b < B; ++b) pairs(b, c, p[b]);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                f32x4 xv[2];
+                load_x(xv, m, c);
+#pragma unroll
+                for (int b = 0; b < B; ++b) row_fma(p[b], xv, m, b);
+            }
+        }
+    }
+    const h2 d01 = as_h2(live ? u.sc.x : 0u), d23 = as_h2(live ? u.sc.y : 0u);
+    const _Float16 d[4] = {d01.x, d01.y, d23.x, d23.y};
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[m][b] = __builtin_fmaf((float)d[b], sb[m][b], acc[m][b]);
+}
+
+// Stage row m of X as xs4[m*nseg*256 + seg*256 + c*32 + jj], where float4
+// chunk i = seg*256 + jj*8 + c of the row holds x[4i .. 4i+3] (zero past K;
+// K % 32 == 0, so a chunk is wholly inside K or wholly past it). Indexing is
+// 32-bit shifts and masks (the staged area is at most LDS-sized); each thread
+// issues its global loads in batches of 4 before writing LDS.
+//
+// The first batch of row 0 is split off (stage_x_issue): a kernel issues it
+// before its first weight loads, so that the few activation lines reach the
+// memory queues ahead of the weight stream instead of behind it, and writes it
+// (stage_x_finish, which also stages the rest) after them. The caller
+// synchronises the workgroup afterwards.
+struct XFirst {
+    f32x4 v[4];
+};
+
+__device__ __forceinline__ uint32_t x_slot(uint32_t i) { return (i & ~255u) | ((i & 7u) << 5) | ((i >> 3) & 31u); }
+
+__device__ __forceinline__ void stage_x_issue(XFirst &f, const float *__restrict__ x, int64_t K)
+{
+    const uint32_t k4 = (uint32_t)(K >> 2);
+    const uint32_t nthr = blockDim.x, tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t i = tid + q * nthr;
+        f.v[q] = i < k4 ? *(const f32x4 *)(x + 4 * (size_t)i) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+}
+
+template <int M>
+__device__ __forceinline__ void stage_x_finish(const XFirst &f, f32x4 *xs4, const float *__restrict__ x,
+                                               int64_t x_stride, int64_t nseg, int64_t K)
+{
+    const uint32_t per_m = (uint32_t)nseg << 8;
+    const uint32_t k4 = (uint32_t)(K >> 2);
+    const uint32_t nthr = blockDim.x, tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t i = tid + q * nthr;
+        if (i < per_m) xs4[x_slot(i)] = f.v[q];
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const float *xm = x + (int64_t)m * x_stride;
+        f32x4 *dst = xs4 + (uint32_t)m * per_m;
+        for (uint32_t base = tid + (m == 0 ? 4 * nthr : 0u); base < per_m; base += 4 * nthr) {
+            f32x4 v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t i = base + q * nthr;
+                v[q] = i < k4 ? *(const f32x4 *)(xm + 4 * (size_t)i) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t i = base + q * nthr;
+                if (i < per_m) dst[x_slot(i)] = v[q];
+            }
+        }
+    }
+}
+
+// Sum of squares of one thread's values, then of the workgroup: a per-thread fma
+// chain, the wavefront butterfly (both halves), then the wavefront partials added
+// in wavefront order through `red` (one float per wavefront). Every thread gets
+// the same bits. The caller's threads must all arrive; `red` is reused after a
+// barrier.
+__device__ __forceinline__ float block_sum(float s, float *red)
+{
+    const uint32_t nthr = blockDim.x, tid = threadIdx.x;
+    const float h = half_wave_sum(s);
+    const float w = as_f(__builtin_amdgcn_readlane(as_i(h), 0)) + as_f(__builtin_amdgcn_readlane(as_i(h), 32));
+    if ((tid & 63) == 0) red[tid >> 6] = w;
+    __syncthreads();
+    float t = red[0];
+    for (uint32_t i = 1; i < (nthr >> 6); ++i) t += red[i];
+    __syncthreads();
+    return t;
+}
+
+// 1 / sqrt(mean + eps), correctly rounded square root and division.
+__device__ __forceinline__ float rms_scale(float ss, int64_t K, float eps)
+{
+    return 1.0f / __builtin_sqrtf(ss / (float)K + eps);
+}
+
+// RMSNorm prologue: the staged activations (row 0, float4 chunk i at
+// xs4[x_slot(i)], zero past K) become (x * r) * gamma in place, with
+// r = 1 / sqrt(sum(x^2) / K + eps). Every thread of the workgroup must call it.
+__device__ __forceinline__ void norm_staged_x(f32x4 *xs4, float *red, const float *__restrict__ gamma, float eps,
+                                              int64_t K)
+{
+    const uint32_t k4 = (uint32_t)(K >> 2);
+    const uint32_t nthr = blockDim.x, tid = threadIdx.x;
+    float s = 0.0f;
+    for (uint32_t i = tid; i < k4; i += nthr) {
+        const f32x4 v = xs4[x_slot(i)];
+        s = __builtin_fmaf(v.x, v.x, s);
+        s = __builtin_fmaf(v.y, v.y, s);
+        s = __builtin_fmaf(v.z, v.z, s);
+        s = __builtin_fmaf(v.w, v.w, s);
+    }
+    const float r = rms_scale(block_sum(s, red), K, eps);
+    for (uint32_t i = tid; i < k4; i += nthr) {
+        const uint32_t sl = x_slot(i);
+        const f32x4 gm = *(const f32x4 *)(gamma + 4 * (size_t)i);
+        const f32x4 v = xs4[sl];
+        xs4[sl] = f32x4{(v.x * r) * gm.x, (v.y * r) * gm.y, (v.z * r) * gm.z, (v.w * r) * gm.w};
+    }
+    __syncthreads();
+}
+
+// Store output n of activation row m (n < n_out). The affine epilogue adds the
+// bias and then the residual to the finished product, one fp32 addition each,
+// and writes fp32 or fp16 (v_cvt_f16_f32, round to nearest even). The residual
+// is read before y[n] is written, so residual == y updates y in place.
+template <int M, int EPI>
+__device__ __forceinline__ void store_out(float *__restrict__ y, const QArgs &a, int m, int64_t n, float v)
+{
+    if (EPI == kEpiAffine) {
+        if (a.bias != nullptr) v = v + a.bias[n];
+        if (a.residual != nullptr) v = v + a.residual[n];
+        if (a.out_f16) {
+            ((_Float16 *)y)[n] = (_Float16)v;
+            return;
+        }
+        y[n] = v;
+    } else {
+        y[m * a.y_stride + n] = v;
+    }
+}
+
+// Write the finished rows of tile t from the lanes of one slot (acc already
+// reduced over the slot's 32 lanes, so every lane holds the sums).
+//   plain, affine: lane j < M*B stores row b = j % B of activation row m = j / B
+//   gate|up:       rows b = 2p (gate) and 2p+1 (up) give output n = row0/2 + p
+template <int M, int EPI>
+__device__ __forceinline__ void store_tile(const float (&acc)[M][kRowsPerLane], float *__restrict__ y, const QArgs &a,
+                                           int64_t t, int slot, int j)
+{
+    constexpr int B = kRowsPerLane;
+    const int64_t n_out = a.n_out;
+    const int64_t row0 = t * kTileRows + slot * kRowsPerLane;
+    if (EPI != kEpiGateUp) {
+        if (j < M * B) {
+            float v = 0.0f;
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int b = 0; b < B; ++b)
+                    if (j == m * B + b) v = acc[m][b];
+            const int m = j / B, b = j % B;
+            if (row0 + b < n_out) store_out<M, EPI>(y, a, m, row0 + b, v);
+        }
+    } else {
+        if (j < B / 2) {
+            float gv = 0.0f, uv = 0.0f;
+#pragma unroll
+            for (int p = 0; p < B / 2; ++p)
+                if (j == p) {
+                    gv = acc[0][2 * p];
+                    uv = acc[0][2 * p + 1];
+                }
+            const int64_t n = row0 / 2 + j;
+            if (n < n_out) y[n] = silu_mul(gv, uv);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Quantised GEMV. Template parameters:
+//   QT   kQ8_0 / kQ4_0
+//   M    activation rows (1 = decode GEMV, 2..6 = verify)
+//   EPI  kEpiPlain (y = W x), kEpiGateUp (y = silu(gate) * up, M = 1) or
+//        kEpiAffine (y = ((W x) + bias) + residual, fp32 or fp16, M = 1)
+//   W    wavefronts that split one row tile along K (1, 2, 3, 4 or 8)
+//   XLDS activations staged in LDS (true) or read from global memory
+// W == 1: a workgroup holds blockDim/64 independent wavefronts; wavefront g of
+//         workgroup b is group b*G + g.
+// W  > 1: a workgroup is one group of W wavefronts; wavefront w adds segments
+//         [nseg*w/W, nseg*(w+1)/W) of every tile of the group and the W partial
+//         sums are combined in LDS in wavefront order.
+// Group q walks the tiles [q * tpg, q * tpg + tpg) (contiguous order) or, with
+// tstride > 0, the tiles q, q + tstride, q + 2*tstride, ... (grid-stride order:
+// the groups resident at any moment read one contiguous window of the weights).
+// Which group handles a tile changes none of its rows' operations.
+// Each wavefront walks its (tile, segment) sequence with the loads of the next
+// D units in flight while the current one is computed (a ring of D+1 units).
+// A split workgroup (W > 1) has exactly W wavefronts. The k-quant kernels with
+// 5 or 6 activation rows declare that bound, which lets them use the
+// accumulation registers instead of spilling 44-336 bytes per lane to scratch
+// (measured: M = 6 on 8000 x 2048, Q6_K 23.4 -> 17.5 us, Q4_K 20.8 -> 18.1 us;
+// M = 5 with W = 2 about 10% faster). With fewer rows they spill little or
+// nothing, and the wider register budget only lowers their occupancy (Q6_K
+// M = 4 on the same matrix 11.1 -> 13.2 us), so every other instantiation keeps
+// the 512-thread bound.
+constexpr int qgemv_max_threads(int QT, int M, int W)
+{
+    return (W > 1 && M >= 5 && (QT == kQ4_K || QT == kQ6_K)) ? 64 * W : 512;
+}
+
+template <int QT, int M, int EPI, int W, bool XLDS, int D, bool NORM>
+__global__ void __launch_bounds__(qgemv_max_threads(QT, M, W))
+qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float *__restrict__ y, QArgs a)
+{
+    static_assert(!NORM || (XLDS && M == 1), "the RMSNorm prologue works on staged single-row activations");
+    constexpr int B = kRowsPerLane;
+    constexpr int S = D + 1;   // ring size
+    extern __shared__ f32x4 xs4[];
+    __shared__ float red[tile_red_floats(M, W, NORM)];  // [W][M][slot][b]; norm: [wavefront]
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int slot = lane >> 5, j = lane & 31;
+    const int wk = (W > 1) ? wave : 0;
+    const int64_t group = (W > 1) ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+
+    const Geometry &g = a.geo;
+    const int64_t K = g.K, nseg = g.nseg;
+    int64_t t_begin, t_step, my_tiles;
+    if (a.tstride > 0) {
+        t_begin = group;
+        t_step = a.tstride;
+        my_tiles = group < g.n_tiles ? (g.n_tiles - group + t_step - 1) / t_step : 0;
+    } else {
+        t_begin = group * a.tpg;
+        t_step = 1;
+        const int64_t t_end = (t_begin + a.tpg < g.n_tiles) ? t_begin + a.tpg : g.n_tiles;
+        my_tiles = t_end > t_begin ? t_end - t_begin : 0;
+    }
+    const int64_t s_begin = nseg * wk / W, s_end = nseg * (wk + 1) / W;
+
+    const Consts k = make_consts();
+    const LanePlace lp = lane_place(g, slot, j);
+    // This wavefront's units, in order: (t, s) for its tiles t, s in [s_begin, s_end).
+    const int64_t n_units = my_tiles * (s_end - s_begin);
+
+    // Load cursor: the unit whose loads are issued next (D units ahead of the compute cursor).
+    int64_t t_ld = t_begin, s_ld = s_begin, u_ld = 0;
+    auto advance = [&](int64_t &tt, int64_t &ss) {
+        if (++ss == s_end) {
+            ss = s_begin;
+            tt += t_step;
+        }
+    };
+    XFirst xf;
+    if (XLDS) stage_x_issue(xf, x, K);
+    Unit<QT> ring[S];
+#pragma unroll
+    for (int r = 0; r < D; ++r) {
+        load_unit<QT>(ring[r], wp, g, t_ld, s_ld, lp, u_ld < n_units);
+        advance(t_ld, s_ld);
+        ++u_ld;
+    }
+
+    if (XLDS) {
+        stage_x_finish<M>(xf, xs4, x, a.x_stride, nseg, K);
+        __syncthreads();
+    }
+    if (NORM) norm_staged_x(xs4, red, a.gamma, a.eps, K);
+    if (n_units == 0) return;   // uniform across the workgroup when W > 1
+
+    float acc[M][B];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[m][b] = 0.0f;
+
+    int64_t t = t_begin, s = s_begin;   // compute cursor: the unit being computed
+
+    // Issue the loads of unit u+D into `nxt` (a dummy one-line load past the
+    // last unit), then compute unit u from `cur` and finish the tile after its
+    // last segment.
+    auto step = [&](Unit<QT> &cur, Unit<QT> &nxt) {
+        load_unit<QT>(nxt, wp, g, t_ld, s_ld, lp, u_ld < n_units);
+        advance(t_ld, s_ld);
+        ++u_ld;
+        // keep the scheduler from sinking these loads into the compute below
+        __builtin_amdgcn_sched_barrier(0);
+        const bool last = s == nseg - 1;
+        compute_unit<QT, M, XLDS>(cur, acc, k, xs4, x, a.x_stride, nseg, s, last ? lp.j_last : j,
+                                  !last || lp.live_last);
+        if (s + 1 == s_end) {
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int b = 0; b < B; ++b) acc[m][b] = half_wave_sum(acc[m][b]);
+            if (W > 1) {
+                // fixed-order combine of the split-K partials: ((p0 + p1) + p2) + p3
+                if (j == 0) {
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+#pragma unroll
+                        for (int b = 0; b < B; ++b) red[((wk * M + m) * kSlots + slot) * B + b] = acc[m][b];
+                }
+                __syncthreads();
+                if (wk == 0) {
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+#pragma unroll
+                        for (int b = 0; b < B; ++b) {
+                            float v = red[((0 * M + m) * kSlots + slot) * B + b];
+#pragma unroll
+                            for (int w = 1; w < W; ++w) v += red[((w * M + m) * kSlots + slot) * B + b];
+                            acc[m][b] = v;
+                        }
+                }
+                __syncthreads();
+            }
+            if (wk == 0) store_tile<M, EPI>(acc, y, a, t, slot, j);
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int b = 0; b < B; ++b) acc[m][b] = 0.0f;
+        }
+        advance(t, s);
+    };
+
+    // A counted loop over groups of S units with no early exit, so that the only
+    // way back to the loop head is through every step; unit u lives in ring[u % S].
+    const int64_t n_groups = n_units / S;
+    for (int64_t gi = 0; gi < n_groups; ++gi) {
+#pragma unroll
+        for (int r = 0; r < S; ++r) step(ring[r], ring[(r + D) % S]);
+    }
+    const int64_t rem = n_units - n_groups * S;
+#pragma unroll
+    for (int r = 0; r < S - 1; ++r)
+        if (r < rem) step(ring[r], ring[(r + D) % S]);
+}
+
+
+// ---------------------------------------------------------------------------
+// Persistent form of the quantised GEMV, for matrices with too few row tiles
+// to balance the CUs one tile per wavefront. One workgroup per CU: workgroup b
+// owns the contiguous tiles [T0, T1) = [b*n_tiles/n_wg, (b+1)*n_tiles/n_wg)
+// (the same number to within one) and stages the activations once. Each tile
+// splits along K into R = a.ranges equal ranges of nseg/R segments, and item
+// i = (tile T0 + i/R, range i%R) goes to wavefront i % G: the items, not whole
+// tiles, are spread over the wavefronts. A wavefront walks its items' units
+// with the next unit's loads in flight; after an item's last unit it reduces
+// the lanes (same butterfly as above) and, for R > 1, parks the 8-row partial
+// in LDS. When every wavefront is done, the partials of each row are added in
+// range order, ((p0 + p1) + p2) + ..., and stored (with the SiLU epilogue for
+// gate|up). For any M a row goes through the same operations, so the verify
+// rows still equal the M=1 rows bit for bit. PHASED (several activation rows
+// that do not fit in LDS at once): the ranges are walked in phases, each
+// staging only its segments' activations (see the phase loop below).
+template <int QT, int M, int EPI, bool XLDS, bool NORM, bool PHASED = false>
+__global__ void __launch_bounds__(persist_threads(QT, M, XLDS))
+qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float *__restrict__ y, QArgs a)
+{
+    static_assert(!NORM || (XLDS && M == 1), "the RMSNorm prologue works on staged single-row activations");
+    static_assert(!PHASED || (XLDS && !NORM), "phases stage windows of the activations");
+    constexpr int B = kRowsPerLane;
+    constexpr int S = 2;   // ring: one unit in flight ahead of the one being computed
+    extern __shared__ f32x4 xs4[];
+    __shared__ float nred[persist_red_floats(NORM)];
+
+    const int tid = threadIdx.x;
+    const int G = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int slot = lane >> 5, j = lane & 31;
+
+    const Geometry &g = a.geo;
+    const int64_t K = g.K, nseg = g.nseg;
+    const uint32_t R = (uint32_t)a.ranges;
+    const uint32_t L = (uint32_t)(nseg / R);   // segments per range
+    const int64_t T0 = (int64_t)blockIdx.x * g.n_tiles / a.n_wg;
+    const int64_t T1 = ((int64_t)blockIdx.x + 1) * g.n_tiles / a.n_wg;
+    // Phases: the ranges are walked in P phases; phase ph takes the ranges
+    // [r0, r1) = [R ph / P, R (ph + 1) / P), stages only the activations of
+    // their segments [r0 L, r1 L) (a window of nsegw segments; all of them when
+    // P = 1) and spreads its items i = (tile T0 + i / RP, range r0 + i % RP),
+    // RP = r1 - r0, over the wavefronts. The partials follow the largest window.
+    const uint32_t P = PHASED ? (uint32_t)a.phases : 1u;
+    const uint32_t nsegw_max = PHASED ? (R + P - 1) / P * L : (uint32_t)nseg;
+    float *part = (float *)(xs4 + (XLDS ? (uint32_t)M * (nsegw_max << 8) : 0u));   // [tile][range][m][8]
+
+    const Consts k = make_consts();
+    const LanePlace lp = lane_place(g, slot, j);
+
+    // A cursor over this wavefront's units of the phase whose first range is r0:
+    // item i, its tile and range, segment s.
+    struct Cur {
+        uint32_t i, r;
+        int64_t t, s, s_end;
+    };
+    uint32_t r0 = 0, RP = R;
+    auto seat = [&](Cur &c) {
+        const uint32_t q = c.i / RP;
+        c.r = r0 + (c.i - q * RP);
+        c.t = T0 + q;
+        c.s = (int64_t)c.r * L;
+        c.s_end = c.s + L;
+    };
+    auto advance = [&](Cur &c) {
+        if (++c.s == c.s_end) {
+            c.i += G;
+            seat(c);
+        }
+    };
+
+    float acc[M][B];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[m][b] = 0.0f;
+
+    for (uint32_t ph = 0; ph < P; ++ph) {
+        r0 = PHASED ? R * ph / P : 0u;
+        RP = PHASED ? R * (ph + 1) / P - r0 : R;
+        const uint32_t nsegw = PHASED ? RP * L : (uint32_t)nseg;
+        const uint32_t n_items = (uint32_t)(T1 - T0) * RP;
+        const uint32_t my_items = n_items > (uint32_t)wave ? (n_items - (uint32_t)wave + G - 1) / G : 0u;
+        const int64_t n_units = (int64_t)my_items * L;
+        const int64_t s0 = PHASED ? (int64_t)r0 * L : 0;
+        const float *xw = x + s0 * kSegWeights;   // the window's first activation of row 0
+        const int64_t Kw = K - s0 * kSegWeights;  // activations of a row from the window on
+        if (PHASED && ph > 0) __syncthreads();    // every wavefront done with the previous window
+        Cur ld, cu;
+        ld.i = wave;
+        seat(ld);
+        cu = ld;
+        int64_t u_ld = 0;
+
+        XFirst xf;
+        if (XLDS) stage_x_issue(xf, xw, Kw);
+        Unit<QT> ring[S];
+        load_unit<QT>(ring[0], wp, g, ld.t, ld.s, lp, u_ld < n_units);
+        advance(ld);
+        ++u_ld;
+
+        if (XLDS) {
+            stage_x_finish<M>(xf, xs4, xw, a.x_stride, nsegw, Kw);
+            __syncthreads();
+        }
+        if (NORM) norm_staged_x(xs4, nred, a.gamma, a.eps, K);
+
+        auto step = [&](Unit<QT> &cur, Unit<QT> &nxt) {
+            load_unit<QT>(nxt, wp, g, ld.t, ld.s, lp, u_ld < n_units);
+            advance(ld);
+            ++u_ld;
+            __builtin_amdgcn_sched_barrier(0);
+            const bool last = cu.s == nseg - 1;
+            compute_unit<QT, M, XLDS>(cur, acc, k, xs4, x, a.x_stride, nsegw, cu.s - s0, last ? lp.j_last : j,
+                                      !last || lp.live_last);
+            if (cu.s + 1 == cu.s_end) {
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int b = 0; b < B; ++b) acc[m][b] = half_wave_sum(acc[m][b]);
+                if (R == 1) {
+                    store_tile<M, EPI>(acc, y, a, cu.t, slot, j);
+                } else if (j == 0) {
+                    float *pp = part + ((size_t)(cu.t - T0) * R + cu.r) * (M * kTileRows) + slot * B;
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+#pragma unroll
+                        for (int b = 0; b < B; ++b) pp[m * kTileRows + b] = acc[m][b];
+                }
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int b = 0; b < B; ++b) acc[m][b] = 0.0f;
+            }
+            advance(cu);
+        };
+
+        const int64_t n_groups = n_units / S;
+        for (int64_t gi = 0; gi < n_groups; ++gi) {
+            step(ring[0], ring[1]);
+            step(ring[1], ring[0]);
+        }
+        if (n_units - n_groups * S) step(ring[0], ring[1]);
+    }
+
+    if (R > 1) {
+        // every wavefront reaches this barrier (no early exit above)
+        __syncthreads();
+        const uint32_t ntile = (uint32_t)(T1 - T0);
+        if (EPI != kEpiGateUp) {
+            for (uint32_t o = tid; o < ntile * (M * kTileRows); o += blockDim.x) {
+                const uint32_t tl = o / (M * kTileRows), rem = o - tl * (M * kTileRows);
+                const uint32_t m = rem / kTileRows, row = rem - m * kTileRows;
+                const float *pp = part + (size_t)tl * R * (M * kTileRows) + m * kTileRows + row;
+                float v = pp[0];
+                for (uint32_t r = 1; r < R; ++r) v += pp[(size_t)r * (M * kTileRows)];
+                const int64_t n = (T0 + tl) * kTileRows + row;
+                if (n < a.n_out) store_out<M, EPI>(y, a, (int)m, n, v);
+            }
+        } else {
+            for (uint32_t o = tid; o < ntile * (kTileRows / 2); o += blockDim.x) {
+                const uint32_t tl = o / (kTileRows / 2), q = o - tl * (kTileRows / 2);
+                const float *pp = part + (size_t)tl * R * kTileRows + 2 * q;
+                float gv = pp[0], uv = pp[1];
+                for (uint32_t r = 1; r < R; ++r) {
+                    gv += pp[(size_t)r * kTileRows];
+                    uv += pp[(size_t)r * kTileRows + 1];
+                }
+                const int64_t n = (T0 + tl) * (kTileRows / 2) + q;
+                if (n < a.n_out) y[n] = silu_mul(gv, uv);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launch templates (host side)
+
+template <typename Kern, typename... Args>
+static void launch(Kern kern, dim3 grid, dim3 block, uint32_t lds, hipStream_t stream, Args... args)
+{
+    launch_timed(kern, grid, block, lds, stream, args...);
+}
+
+template <int QT, int M, int EPI, int W, bool XLDS, int D, bool NORM = false>
+static hipError_t launch_q(const uint8_t *wp, const float *x, float *y, const QArgs &a, int64_t grid, int block,
+                           size_t lds, hipStream_t stream)
+{
+    auto kern = qgemv_kernel<QT, M, EPI, W, XLDS, D, NORM>;
+    static std::atomic<int> lds_set[16];
+    hipError_t e = ensure_lds_limit((const void *)kern, lds, lds_set);
+    if (e != hipSuccess) return e;
+    launch(kern, dim3((unsigned)grid), dim3(block), (uint32_t)lds, stream, wp, x, y, a);
+    return hipGetLastError();
+}
+
+template <int QT, int M, int EPI, int W>
+static hipError_t dispatch_x(const uint8_t *wp, const float *x, float *y, const QArgs &a, int64_t grid, int block,
+                             size_t lds, bool xlds, int depth, bool norm, hipStream_t s)
+{
+    // the RMSNorm prologue: single-row plain and gate|up kernels, staged activations, depth 1
+    if constexpr (M == 1 && EPI != kEpiAffine) {
+        if (norm) {
+            if (!xlds) return hipErrorInvalidConfiguration;
+            return launch_q<QT, M, EPI, W, true, 1, true>(wp, x, y, a, grid, block, lds, s);
+        }
+    }
+    if (norm) return hipErrorInvalidConfiguration;
+    // prefetch depth 2 is instantiated for the single-row kernels without the
+    // affine epilogue only (elsewhere a request for it runs depth 1)
+    if constexpr (M == 1 && EPI != kEpiAffine) {
+        if (depth >= 2)
+            return xlds ? launch_q<QT, M, EPI, W, true, 2>(wp, x, y, a, grid, block, lds, s)
+                        : launch_q<QT, M, EPI, W, false, 2>(wp, x, y, a, grid, block, 0, s);
+    }
+    return xlds ? launch_q<QT, M, EPI, W, true, 1>(wp, x, y, a, grid, block, lds, s)
+                : launch_q<QT, M, EPI, W, false, 1>(wp, x, y, a, grid, block, 0, s);
+}
+
+template <int QT, int M, int EPI>
+static hipError_t dispatch_w(const uint8_t *wp, const float *x, float *y, const QArgs &a, int W, int64_t grid,
+                             int block, size_t lds, bool xlds, int depth, bool norm, hipStream_t s)
+{
+    switch (W) {
+    case 1: return dispatch_x<QT, M, EPI, 1>(wp, x, y, a, grid, block, lds, xlds, depth, norm, s);
+    case 2: return dispatch_x<QT, M, EPI, 2>(wp, x, y, a, grid, block, lds, xlds, depth, norm, s);
+    case 3: return dispatch_x<QT, M, EPI, 3>(wp, x, y, a, grid, block, lds, xlds, depth, norm, s);
+    case 4: return dispatch_x<QT, M, EPI, 4>(wp, x, y, a, grid, block, lds, xlds, depth, norm, s);
+    default: return dispatch_x<QT, M, EPI, 8>(wp, x, y, a, grid, block, lds, xlds, depth, norm, s);
+    }
+}
+
+template <int QT, int M, int EPI>
+static hipError_t launch_persist(const uint8_t *wp, const float *x, float *y, const QArgs &a, const QPlan &p,
+                                 hipStream_t stream)
+{
+    auto kern = p.x_in_lds ? qgemv_persist<QT, M, EPI, true, false> : qgemv_persist<QT, M, EPI, false, false>;
+    int which = p.norm ? 2 : (p.x_in_lds ? 0 : 1);
+    if (p.phases > 1) {
+        // several activation rows walked in phases (staged windows), plain store only
+        if constexpr (M > 1 && EPI == kEpiPlain) {
+            if (!p.x_in_lds || p.norm) return hipErrorInvalidConfiguration;
+            kern = qgemv_persist<QT, M, EPI, true, false, true>;
+            which = 3;
+        } else {
+            return hipErrorInvalidConfiguration;
+        }
+    }
+    if (p.norm) {
+        // the RMSNorm prologue: single-row plain and gate|up kernels with staged activations
+        if constexpr (M == 1 && EPI != kEpiAffine) {
+            if (!p.x_in_lds) return hipErrorInvalidConfiguration;
+            kern = qgemv_persist<QT, M, EPI, true, true>;
+        } else {
+            return hipErrorInvalidConfiguration;
+        }
+    }
+    if (p.block != persist_threads(QT, M, p.x_in_lds)) return hipErrorInvalidConfiguration;
+    static std::atomic<int> lds_set[4][16];   // one record per kernel chosen above
+    hipError_t e = ensure_lds_limit((const void *)kern, p.lds_bytes, lds_set[which]);
+    if (e != hipSuccess) return e;
+    launch(kern, dim3((unsigned)p.grid), dim3(p.block), (uint32_t)p.lds_bytes, stream, wp, x, y, a);
+    return hipGetLastError();
+}
+
+template <int QT, int M, int EPI>
+static hipError_t dispatch_form(const uint8_t *wp, const float *x, float *y, const QArgs &a, const QPlan &p,
+                                hipStream_t s)
+{
+    if (p.persist) return launch_persist<QT, M, EPI>(wp, x, y, a, p, s);
+    return dispatch_w<QT, M, EPI>(wp, x, y, a, p.W, p.grid, p.block, p.lds_bytes, p.x_in_lds, p.depth, p.norm, s);
+}
+
+// The single-row calls of type QT: plain, gate|up and affine epilogues, with or
+// without the RMSNorm prologue.
+template <int QT>
+hipError_t launch_qgemv_m1(int epi, const QPlan &p, const uint8_t *wp, const float *x, float *y, const QArgs &a,
+                           hipStream_t s)
+{
+    if (epi == kEpiGateUp) return dispatch_form<QT, 1, kEpiGateUp>(wp, x, y, a, p, s);
+    if (epi == kEpiAffine) return dispatch_form<QT, 1, kEpiAffine>(wp, x, y, a, p, s);
+    return dispatch_form<QT, 1, kEpiPlain>(wp, x, y, a, p, s);
+}
+
+// The verify calls of type QT with M activation rows (plain store).
+template <int QT, int M>
+hipError_t launch_qgemv_rows(const QPlan &p, const uint8_t *wp, const float *x, float *y, const QArgs &a,
+                             hipStream_t s)
+{
+    return dispatch_form<QT, M, kEpiPlain>(wp, x, y, a, p, s);
+}
+
+}  // namespace qgk

@@ -104,6 +104,24 @@ constexpr int persist_threads(int qt, int M, bool xlds)
     return (M <= 3 || xlds) ? 768 : 512;
 }
 
+// Static LDS of the quantised GEMV kernels. The kernels declare their arrays
+// with these sizes and the launch planner adds them to the dynamic activation
+// copy, so that a plan never asks for more than a CU's LDS:
+//   qgemv_kernel: `red`, the split-K partials [W][M][slot][row] for W > 1, one
+//     float per wavefront (at most 8) for the RMSNorm prologue, else one float;
+//   qgemv_persist: `nred`, one float per wavefront (at most 16) for the RMSNorm
+//     prologue, else one float.
+constexpr int tile_red_floats(int M, int W, bool norm)
+{
+    return W > 1 ? W * M * qgl::kSlots * qgl::kRowsPerLane : (norm ? 8 : 1);
+}
+constexpr int persist_red_floats(bool norm) { return norm ? 16 : 1; }
+// Bytes that a static array of `floats` floats occupies ahead of the dynamic
+// array, which is 16-byte aligned (f32x4).
+constexpr size_t static_lds_bytes(int floats) { return ((size_t)floats * sizeof(float) + 15) / 16 * 16; }
+// LDS of one workgroup on gfx950 (static plus dynamic).
+constexpr size_t kLdsPerWorkgroup = 160 * 1024;
+
 // Raise a kernel's dynamic-LDS limit to `bytes` (needed above 64 KiB) unless it is
 // already that high on the current device. `set` is the caller's record for that
 // one kernel (one per template instantiation), so a decode loop pays for the

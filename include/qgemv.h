@@ -196,8 +196,8 @@ qg_status qg_rmsnorm(const float *x, const float *gamma, float eps, float *out, 
  * workgroup stages x in LDS, reduces sum(x^2) itself and normalises its copy,
  * then runs the GEMV of qgemv_q8_0 / qgemv_q4_0 on it. Arguments as for those
  * calls plus gamma fp32 [K] (16-byte aligned, not overlapping y) and eps as in
- * qg_rmsnorm. K <= 40960 (the normalised copy lives in LDS), else
- * QG_EUNSUPPORTED. The result is within the linear tolerance of the exact
+ * qg_rmsnorm. K <= 39936 (the normalised copy lives in LDS, next to the
+ * kernel's own static arrays), else QG_EUNSUPPORTED. The result is within the linear tolerance of the exact
  * product on the exact normalised vector; it is not bitwise equal to
  * qg_rmsnorm followed by the plain GEMV (another reduction order). */
 qg_status qgemv_rmsnorm(int qtype, const void *w_packed, const float *x, const float *gamma, float eps, float *y,
@@ -252,18 +252,24 @@ qg_status qgemm_prefill(int qtype, const void *w_packed, const float *X, float *
 const char *qg_status_str(int status);
 const char *qg_last_error(void);
 
-/* How a quantised call of this shape is launched (for reports). Outputs (each
- * may be NULL):
+/* How a quantised call of this shape is launched (for reports and tests).
+ * Inputs: qtype, N, K as for the GEMV calls; M activation rows (1..6);
+ * rmsnorm 1 for the RMSNorm-prologue calls (M = 1 only), else 0.
+ * Outputs (each may be NULL):
  *   split_k_ways  the number of K ranges a row tile's sum is split into (the
  *                 partial sums of a row are added in range order);
  *   workgroups    workgroups launched;
  *   x_in_lds      1 when the activations are staged in LDS, 0 when read from L2;
  *   persistent    1 for the persistent form (one workgroup per CU, used for
- *                 matrices with few row tiles), 0 for one wavefront per tile.
+ *                 matrices with few row tiles), 0 for one wavefront per tile;
+ *   lds_bytes     LDS per workgroup, static arrays plus the dynamic part (at
+ *                 most the 160 KiB of a gfx950 CU).
  * Host function: it only reads the current device's CU count (256 when no
- * device answers). Returns QG_OK, QG_EINVAL or QG_EUNSUPPORTED. */
-qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int *split_k_ways,
-                       int64_t *workgroups, int *x_in_lds, int *persistent);
+ * device answers). Returns QG_OK, QG_EINVAL, or QG_EUNSUPPORTED where the
+ * call itself would (M outside 1..6; rmsnorm with M != 1, K > 39936, or
+ * activations that do not fit in LDS). */
+qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int rmsnorm, int *split_k_ways,
+                       int64_t *workgroups, int *x_in_lds, int *persistent, int64_t *lds_bytes);
 
 /* Re-read the launch-shape overrides (QG_SPLIT_K, QG_PERSIST, QG_X_GLOBAL,
  * QG_TILES_PER_GROUP, QG_WAVES_PER_WG, QG_PREFETCH, QG_F16_ROWS, QG_F16_WAVES,

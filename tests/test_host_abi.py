@@ -187,6 +187,10 @@ def test_rmsnorm_argument_checks_without_gpu(L):
     assert gn(1, w, x, g + 4, e(1e-6), y, 8, 32, None) == qg.QG_EALIGN
     assert gn(2, w, x, g, e(-1e-3), y, 8, 32, None) == qg.QG_EINVAL
     assert gn(2, w, x, g, e(1e-6), y, 8, 40960 + 32, None) == qg.QG_EUNSUPPORTED
+    # the normalised copy lives in LDS next to the kernel's static arrays: K <= 39936
+    assert gn(2, w, x, g, e(1e-6), y, 8, 40960, None) == qg.QG_EUNSUPPORTED
+    assert gn(2, w, x, g, e(1e-6), y, 8, 39936 + 32, None) == qg.QG_EUNSUPPORTED
+    assert gu(1, w, x, g, e(1e-6), y, 8, 40960, None) == qg.QG_EUNSUPPORTED
     assert gn(2, w, x, y - 16, e(1e-6), y, 8, 32, None) == qg.QG_EINVAL   # y overlaps gamma
     assert gn(5, w, x, g, e(1e-6), y, 8, 32, None) == qg.QG_EUNSUPPORTED
     assert gn(1, w, x, g, e(1e-6), y, 8, 48, None) == qg.QG_EINVAL
@@ -283,6 +287,55 @@ def test_plan_info_long_rows_split_eight_ways_over_staged_activations(L):
         # M K 4 bytes over the 160 KiB of LDS (M >= 3 at K = 17408): every row from L2
         assert qg.qg_plan_info(kind, 640, 17408, 2)["x_in_lds"]
         assert not any(qg.qg_plan_info(kind, 640, 17408, M)["x_in_lds"] for M in (3, 4, 5, 6))
+
+
+LDS_PER_CU = 160 * 1024
+
+
+def test_plan_lds_fits_a_cu(L):
+    # every plan's LDS (static arrays plus the staged activations, partials and
+    # phases) fits the 160 KiB of a gfx950 CU, at every M, for the RMSNorm
+    # prologue too; shapes at and around the boundaries of each form
+    shapes = [(8, 1024), (1280, 8192), (640, 17408), (24, 32768), (5120, 17408), (2001, 17408), (17408, 5120),
+              (1024, 39936), (5120, 39936), (8, 40960), (640, 40960), (2048, 16384), (248320, 5120)]
+    for kind in ("q8_0", "q4_0", "q4_k", "q6_k"):
+        for N, K in shapes:
+            for M in range(1, 7):
+                p = qg.qg_plan_info(kind, N, K, M)
+                assert 0 < p["lds_bytes"] <= LDS_PER_CU, (kind, N, K, M, p)
+            if K <= 39936:
+                p = qg.qg_plan_info(kind, N, K, 1, rmsnorm=True)
+                assert p["x_in_lds"] and p["lds_bytes"] <= LDS_PER_CU, (kind, N, K, p)
+
+
+def test_plan_staged_copy_at_the_lds_boundary(L):
+    # 1280 x 8192 at M = 5: the 5 staged rows take exactly 160 KiB and the eight
+    # split-K wavefronts' partials 1280 bytes more, so the rows come from L2
+    for kind in ("q8_0", "q4_0", "q4_k", "q6_k"):
+        p = qg.qg_plan_info(kind, 1280, 8192, 5)
+        assert p["split_k_ways"] == 8 and not p["x_in_lds"], (kind, p)
+        assert p["lds_bytes"] <= LDS_PER_CU
+        # four rows (128 KiB + 1 KiB) still fit
+        assert qg.qg_plan_info(kind, 1280, 8192, 4)["x_in_lds"]
+    # the RMSNorm prologue: K = 39936 (39 segments) fits next to the largest
+    # static array; 40960 does not, for any form
+    for kind in ("q8_0", "q4_0", "q4_k", "q6_k"):
+        for N in (8, 1024, 5120, 17408, 248320):
+            p = qg.qg_plan_info(kind, N, 39936, 1, rmsnorm=True)
+            assert p["x_in_lds"] and p["lds_bytes"] <= LDS_PER_CU, (kind, N, p)
+            with pytest.raises(qg.QGError) as err:
+                qg.qg_plan_info(kind, N, 40960, 1, rmsnorm=True)
+            assert err.value.status == qg.QG_EUNSUPPORTED
+    # a persistent RMSNorm plan whose partials do not fit next to the staged copy
+    # takes the one-wavefront-per-tile form instead of being refused: 24000 rows
+    # are 3000 tiles, 12 per CU, each split in 13 K ranges, 4992 bytes of
+    # partials next to 156 KiB of activations (5120 rows, 3 tiles per CU, fit)
+    p = qg.qg_plan_info("q4_0", 24000, 39936, 1, rmsnorm=True)
+    assert not p["persistent"] and p["x_in_lds"], p
+    assert qg.qg_plan_info("q4_0", 24000, 39936, 1)["persistent"]
+    assert qg.qg_plan_info("q4_0", 5120, 39936, 1, rmsnorm=True)["persistent"]
+    with pytest.raises(qg.QGError):
+        qg.qg_plan_info("q4_0", 5120, 1024, 2, rmsnorm=True)      # the prologue takes M = 1
 
 
 def test_tuning_overrides_are_read_on_reload(L, monkeypatch):
