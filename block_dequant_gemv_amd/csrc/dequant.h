@@ -60,17 +60,23 @@ __device__ __forceinline__ void q4_pairs(uint32_t w, const Consts &k, h2 (&p)[4]
     p[3] = __builtin_elementwise_fma(as_h2(and_or(w8, k.m_hi, k.magic)), sixteenth, off16);
 }
 
-// Q4_K dword -> the 8 quants q (0..15, no offset) as 4 fp16 pairs, in the order
-// of q4_pairs, each pair masked out in place and read as fp16 subnormals: pairs
-// 0 and 2 hold q * 2^-24 (mantissa bits 0..3), pairs 1 and 3 hold q * 2^-20
-// (bits 4..7), all exact; the caller sums the two scales apart and rescales.
-__device__ __forceinline__ void q4k_pairs(uint32_t w, const Consts &k, h2 (&p)[4])
+// Q4_K dword -> the 8 centred quants (q - c) * 2^-24 (q 0..15, c the
+// sub-block's centre, 0..15) as 4 fp16 pairs, in the order of q4_pairs. Each
+// pair of nibbles is masked out in place and read as fp16 subnormals: q * 2^-24
+// (mantissa bits 0..3: pairs 0 and 2), from which the centre pair c_lo =
+// c * 0x00010001 (= c * 2^-24 twice) is subtracted, or q * 2^-20 (bits 4..7:
+// pairs 1 and 3), scaled by 1/16 and the centre subtracted in one fma. Every
+// value involved is a multiple of 2^-24 below 2^-14 in magnitude, so each
+// result is exact.
+__device__ __forceinline__ void q4k_pairs(uint32_t w, const Consts &k, uint32_t c_lo, h2 (&p)[4])
 {
+    const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h2 c = as_h2(c_lo);
     const uint32_t w8 = w >> 8;
-    p[0] = as_h2(w & k.m_lo);
-    p[1] = as_h2(w & k.m_hi);
-    p[2] = as_h2(w8 & k.m_lo);
-    p[3] = as_h2(w8 & k.m_hi);
+    p[0] = as_h2(w & k.m_lo) - c;
+    p[1] = __builtin_elementwise_fma(as_h2(w & k.m_hi), sixteenth, -c);
+    p[2] = as_h2(w8 & k.m_lo) - c;
+    p[3] = __builtin_elementwise_fma(as_h2(w8 & k.m_hi), sixteenth, -c);
 }
 
 // Q6_K: the low-nibble dword w (Q4_0 arrangement) and the row's dword h of high

@@ -33,12 +33,16 @@
 // block: fp16 d, fp16 dmin, 12 bytes of 6-bit sub-block scales and mins, 128
 // bytes of nibbles, weight = d * sc * q - dmin * mn) is packed per 32-weight
 // sub-block like Q4_0: the quant plane holds its nibbles in the Q4_0
-// arrangement, the scale plane its two 6-bit values (byte 0: sc, byte 1: mn)
-// where Q4_0 keeps the fp16 scale, and a third plane holds the super-block's
-// d and dmin:
+// arrangement, the scale plane a 16-bit word per row where Q4_0 keeps the fp16
+// scale, and a third plane holds the super-block's d and dmin:
+//   scale word:  bits 0-3 the centre c, bits 4-9 sc, bits 10-15 mn
 //   super plane: [tile][segment][slot][super-block of the segment][b] x (d, dmin) fp16
 // so a lane's 16-byte load gets d and dmin of its 4 rows. 148 bytes per
-// 256 weights (144 canonical).
+// 256 weights (144 canonical). The centre c (0..15) is derived at load time
+// (q4_k_centre) and is not part of the canonical block: the GEMV sums each
+// sub-block as d*sc * sum((q - c) x) + (d*sc*c - dmin*mn) * sum(x), two terms
+// whose magnitudes are at most 3 |w| per weight, so its rounding scales with
+// sum |w x| even where d*sc*q and dmin*mn cancel.
 //
 // Q6_K (256-weight super-blocks; canonical block: 128 bytes of low 4-bit
 // parts, 64 bytes of high 2-bit parts, 16 int8 scales (one per 16 weights),
@@ -208,6 +212,46 @@ QG_HD void q4_k_pack_scale(uint8_t *u, int j, uint8_t sc, uint8_t mn)
     }
 }
 
+// Exact value of an fp16 bit pattern as a double (infinities and NaN included).
+QG_HD double half_bits_value(uint32_t h)
+{
+    const uint32_t e = (h >> 10) & 31u, m = h & 1023u;
+    double v;
+    if (e == 0)
+        v = (double)m * (1.0 / 16777216.0);   // subnormal: m * 2^-24
+    else if (e == 31)
+        v = m ? __builtin_nan("") : __builtin_inf();
+    else {
+        v = (double)(m | 1024u);
+        int s = (int)e - 25;                   // (1024 + m) * 2^(e - 25)
+        for (; s > 0; --s) v *= 2.0;
+        for (; s < 0; ++s) v *= 0.5;
+    }
+    return (h & 0x8000u) ? -v : v;
+}
+
+// Q4_K: the centre c of a sub-block with scale a = d*sc and min term b = dmin*mn
+// (weight = a q - b, q in 0..15): c = b / a rounded to the nearest integer (ties
+// down) and clamped to 0..15, or 0 when a is 0 or not finite. With this c every
+// weight satisfies |a (q - c)| + |a c - b| <= 3 |a q - b|: when b / a lies in
+// [-1/2, 15 + 1/2], |a c - b| <= |a| / 2 and a q - b is 0 only where q = c;
+// outside it, a (q - c) and a c - b have the same sign. Exact comparisons of
+// doubles (each product has at most 17 significant bits), so the host and the
+// device packer agree bit for bit.
+QG_HD uint32_t q4_k_centre(uint32_t d_bits, uint32_t dmin_bits, uint32_t sc, uint32_t mn)
+{
+    const double a = half_bits_value(d_bits) * (double)sc;
+    const double b2 = 2.0 * half_bits_value(dmin_bits) * (double)mn;
+    if (!(a != 0.0) || a - a != 0.0 || b2 - b2 != 0.0) return 0;
+    uint32_t c = 0;
+    for (int k = 0; k < 15; ++k)   // b / a > k + 1/2  <=>  2b > (2k + 1) a for a > 0, < for a < 0
+        c += (a > 0.0) ? (b2 > (2 * k + 1) * a) : (b2 < (2 * k + 1) * a);
+    return c;
+}
+
+// Q4_K scale word of a sub-block (see the layout above) and its fields.
+QG_HD uint32_t q4_k_scale_word(uint32_t centre, uint32_t sc, uint32_t mn) { return centre | (sc << 4) | (mn << 10); }
+
 // Nibble of element e (0..31) of 32-weight block blk of a canonical row: Q4_0
 // byte e / e-16 of the block; Q4_K sub-block j = blk % 8 of super-block blk / 8,
 // the low (j even) or high (j odd) nibbles of bytes 32 (j / 2) .. + 31.
@@ -292,9 +336,14 @@ QG_HD void pack_block(const Geometry &g, const uint8_t *canon_row, uint8_t *pack
     } else {
         const uint8_t *sb = canon_row ? canon_row + (blk / kSuperBlocks) * 144 : nullptr;
         uint8_t sc = 0, mn = 0;
-        if (sb) q4_k_unpack_scale(sb + 4, (int)(blk % kSuperBlocks), sc, mn);
-        sp[0] = sc;
-        sp[1] = mn;
+        uint32_t centre = 0;
+        if (sb) {
+            q4_k_unpack_scale(sb + 4, (int)(blk % kSuperBlocks), sc, mn);
+            centre = q4_k_centre(sb[0] | ((uint32_t)sb[1] << 8), sb[2] | ((uint32_t)sb[3] << 8), sc, mn);
+        }
+        const uint32_t word = q4_k_scale_word(centre, sc, mn);
+        sp[0] = (uint8_t)word;
+        sp[1] = (uint8_t)(word >> 8);
         if (blk % kSuperBlocks == 0) {
             uint8_t *up = packed + super_offset(g, t, seg, slot, j / kSuperBlocks) + b * 4;
             for (int i = 0; i < 4; ++i) up[i] = sb ? sb[i] : 0;
@@ -371,7 +420,8 @@ QG_HD void unpack_block(const Geometry &g, const uint8_t *packed, uint8_t *canon
     }
     const int js = (int)(blk % kSuperBlocks);
     uint8_t *sb = canon_row + (blk / kSuperBlocks) * 144;
-    q4_k_pack_scale(sb + 4, js, sp[0], sp[1]);
+    const uint32_t word = sp[0] | ((uint32_t)sp[1] << 8);   // the centre (bits 0-3) is derived, not stored
+    q4_k_pack_scale(sb + 4, js, (uint8_t)((word >> 4) & 63u), (uint8_t)(word >> 10));
     if (js == 0) {
         const uint8_t *up = packed + super_offset(g, t, seg, slot, j / kSuperBlocks) + b * 4;
         for (int i = 0; i < 4; ++i) sb[i] = up[i];

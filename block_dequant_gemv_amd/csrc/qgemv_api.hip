@@ -280,6 +280,7 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M, bool norm = false)
         if (M > 1 && xbytes > 80 * 1024 && xbytes <= lds_limit && groups >= 2048) G = 8;
         const int64_t g_env = tune(kWavesPerWg);
         if (g_env == 1 || g_env == 2 || g_env == 4 || g_env == 8) G = (int)g_env;
+        G = std::min(G, qgk::qgemv_max_threads(qt, M, 1) / 64);   // the kernel's launch bound
         p.block = 64 * G;
     }
     if (p.tstride > 0) {

@@ -143,14 +143,16 @@ __device__ __forceinline__ void load_unit(Unit<QT> &u, const uint8_t *__restrict
 // acc[m][b] += d_b * sum_e v_e * x_m[e] over the lane's block of segment s.
 // j is the block whose activations the lane reads; live is false only for
 // lanes past the end of a ragged last segment.
-// Q4_K: acc[m][b] += d*sc * sum_e q_e x_e - dmin*mn * sum_e x_e over the lane's
-// sub-block (the weight's two terms summed apart, as the k-quant dot product
-// does): one fma per weight and row, and each row's sum of x shared by the 4
-// weight rows. The quants arrive as fp16 subnormals q * 2^-24 (elements 0, 1 of
-// each 4) and q * 2^-20 (elements 2, 3), summed in two accumulators and joined
-// exactly up to one rounding; the 2^24 goes into d*sc. d*sc and dmin*mn are
-// exact (11-bit by 6-bit products). Dead lanes of a ragged segment get zero
-// scales and mins: they add 0. Every activation row goes through the same
+// Q4_K: acc[m][b] += d*sc * sum_e (q_e - c) x_e + (d*sc*c - dmin*mn) * sum_e x_e
+// over the lane's sub-block, c the sub-block's centre from the packed scale
+// word (layout.h): one fma per weight and row, and each row's sum of x shared
+// by the 4 weight rows. With the centre, both terms are bounded by 3 |w| per
+// weight (w = d*sc*q - dmin*mn), so the rounding scales with sum |w x| even
+// where d*sc*q and dmin*mn cancel. The centred quants arrive as exact fp16
+// subnormals (q - c) * 2^-24 and are summed in one fp32 fma chain of 32 per
+// row; the 2^24 goes into d*sc. d*sc and dmin*mn are exact (11-bit by 6-bit
+// products) and d*sc*c - dmin*mn is one fma. Dead lanes of a ragged segment
+// get zero terms: they add 0. Every activation row goes through the same
 // operations for any M.
 template <int M, bool XLDS>
 __device__ __forceinline__ void compute_unit_q4k(const Unit<kQ4_K> &u, float (&acc)[M][kRowsPerLane],
@@ -158,27 +160,32 @@ __device__ __forceinline__ void compute_unit_q4k(const Unit<kQ4_K> &u, float (&a
                                                  int64_t x_stride, int64_t nseg, int64_t s, int j, bool live)
 {
     constexpr int B = kRowsPerLane;
-    float s24[M][B], s20[M][B], sx[M];
+    float sq[M][B], sx[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         sx[m] = 0.0f;
 #pragma unroll
-        for (int b = 0; b < B; ++b) s24[m][b] = s20[m][b] = 0.0f;
+        for (int b = 0; b < B; ++b) sq[m][b] = 0.0f;
     }
     const uint32_t x_row = (uint32_t)nseg << 8;
     const f32x4 *xl = xs4 + ((uint32_t)s << 8) + (uint32_t)j;
     const float *xg = x + s * kSegWeights + j * 32;
+    // each row's scale word: bits 0-3 the centre c, 4-9 sc, 10-15 mn; the centre
+    // as the fp16 subnormal pair (c * 2^-24, c * 2^-24)
+    auto word = [&](int b) { return ((b < 2) ? u.sc.x : u.sc.y) >> (16 * (b & 1)); };
+    uint32_t c_lo[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) c_lo[b] = (word(b) & 15u) * 0x00010001u;
     auto row_fma = [&](const h2 (&p)[4], const f32x4 (&xv)[2], int m, int b) {
-        float lo = s24[m][b], hi = s20[m][b];
+        float t = sq[m][b];
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-            lo = __builtin_fmaf((float)p[2 * cc].x, xv[cc].x, lo);
-            lo = __builtin_fmaf((float)p[2 * cc].y, xv[cc].y, lo);
-            hi = __builtin_fmaf((float)p[2 * cc + 1].x, xv[cc].z, hi);
-            hi = __builtin_fmaf((float)p[2 * cc + 1].y, xv[cc].w, hi);
+            t = __builtin_fmaf((float)p[2 * cc].x, xv[cc].x, t);
+            t = __builtin_fmaf((float)p[2 * cc].y, xv[cc].y, t);
+            t = __builtin_fmaf((float)p[2 * cc + 1].x, xv[cc].z, t);
+            t = __builtin_fmaf((float)p[2 * cc + 1].y, xv[cc].w, t);
         }
-        s24[m][b] = lo;
-        s20[m][b] = hi;
+        sq[m][b] = t;
     };
     // Per dword of 8 elements. One activation row: its 2 float4 of x, then the 4
     // weight rows one at a time. Several: the 4 weight rows' pairs once, then the
@@ -198,13 +205,13 @@ __device__ __forceinline__ void compute_unit_q4k(const Unit<kQ4_K> &u, float (&a
 #pragma unroll
             for (int b = 0; b < B; ++b) {
                 h2 p[4];
-                q4k_pairs(u.q[b][0][c >> 1], k, p);
+                q4k_pairs(u.q[b][0][c >> 1], k, c_lo[b], p);
                 row_fma(p, xv, 0, b);
             }
         } else {
             h2 p[B][4];
 #pragma unroll
-            for (int b = 0; b < B; ++b) q4k_pairs(u.q[b][0][c >> 1], k, p[b]);
+            for (int b = 0; b < B; ++b) q4k_pairs(u.q[b][0][c >> 1], k, c_lo[b], p[b]);
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 f32x4 xv[2];
@@ -216,15 +223,14 @@ __device__ __forceinline__ void compute_unit_q4k(const Unit<kQ4_K> &u, float (&a
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-        const uint32_t sw = ((b < 2) ? u.sc.x : u.sc.y) >> (16 * (b & 1));   // byte 0: sc, byte 1: mn
+        const uint32_t sw = word(b);
         const h2 dd = as_h2(u.sup[b]);                                        // (d, dmin)
-        const float scl = live ? (float)dd.x * (float)(sw & 0xFFu) * 16777216.0f : 0.0f;
-        const float mnv = live ? (float)dd.y * (float)((sw >> 8) & 0xFFu) : 0.0f;
+        const float a = (float)dd.x * (float)((sw >> 4) & 63u);                // d*sc, exact
+        const float scl = live ? a * 16777216.0f : 0.0f;
+        const float ct = live ? __builtin_fmaf(a, (float)(sw & 15u), -((float)dd.y * (float)((sw >> 10) & 63u)))
+                              : 0.0f;                                          // d*sc*c - dmin*mn
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const float sq = __builtin_fmaf(s20[m][b], 0.0625f, s24[m][b]);   // sum q x * 2^-24
-            acc[m][b] = acc[m][b] + __builtin_fmaf(scl, sq, -(mnv * sx[m]));
-        }
+        for (int m = 0; m < M; ++m) acc[m][b] = acc[m][b] + __builtin_fmaf(scl, sq[m][b], ct * sx[m]);
     }
 }
 
@@ -585,19 +591,7 @@ __device__ __forceinline__ void store_tile(const float (&acc)[M][kRowsPerLane], 
 // Which group handles a tile changes none of its rows' operations.
 // Each wavefront walks its (tile, segment) sequence with the loads of the next
 // D units in flight while the current one is computed (a ring of D+1 units).
-// A split workgroup (W > 1) has exactly W wavefronts. The k-quant kernels with
-// 5 or 6 activation rows declare that bound, which lets them use the
-// accumulation registers instead of spilling 44-336 bytes per lane to scratch
-// (measured: M = 6 on 8000 x 2048, Q6_K 23.4 -> 17.5 us, Q4_K 20.8 -> 18.1 us;
-// M = 5 with W = 2 about 10% faster). With fewer rows they spill little or
-// nothing, and the wider register budget only lowers their occupancy (Q6_K
-// M = 4 on the same matrix 11.1 -> 13.2 us), so every other instantiation keeps
-// the 512-thread bound.
-constexpr int qgemv_max_threads(int QT, int M, int W)
-{
-    return (W > 1 && M >= 5 && (QT == kQ4_K || QT == kQ6_K)) ? 64 * W : 512;
-}
-
+// The launch bound is qgemv_max_threads (qgemv_kernels.h).
 template <int QT, int M, int EPI, int W, bool XLDS, int D, bool NORM>
 __global__ void __launch_bounds__(qgemv_max_threads(QT, M, W))
 qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float *__restrict__ y, QArgs a)

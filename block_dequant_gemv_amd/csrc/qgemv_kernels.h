@@ -92,15 +92,36 @@ inline void launch_timed(Kern kern, dim3 grid, dim3 block, uint32_t lds, hipStre
         hipLaunchKernelGGL(kern, grid, block, lds, stream, args...);
 }
 
+// Launch bound of the one-wavefront-per-tile form (qgemv_kernel). A split
+// workgroup (W > 1) has exactly W wavefronts. The k-quant kernels with 5 or 6
+// activation rows declare a bound of at most 256 threads (one wavefront per
+// SIMD), which lets them use the accumulation registers instead of spilling to
+// scratch (measured, split kernels: M = 6 on 8000 x 2048, Q6_K 23.4 -> 17.5 us,
+// Q4_K 20.8 -> 18.1 us; M = 5 with W = 2 about 10% faster); the planner keeps
+// their workgroups within it. With fewer rows they spill little or nothing,
+// and the wider register budget only lowers their occupancy (Q6_K M = 4 on the
+// same matrix 11.1 -> 13.2 us), so every other instantiation keeps the
+// 512-thread bound. Unsplit Q6_K rows fit 256 VGPRs at M = 5, 6 and keep it too.
+constexpr int qgemv_max_threads(int QT, int M, int W)
+{
+    if (M >= 5 && (QT == qgl::kQ4_K || QT == qgl::kQ6_K)) {
+        if (W > 1) return 64 * W;
+        if (QT == qgl::kQ4_K) return 256;
+    }
+    return 512;
+}
+
 // Threads per workgroup of the persistent form (its launch bound): as many
 // wavefronts as one CU holds at the kernel's register count. Single-row
 // kernels fit 128 VGPRs (16 wavefronts); the multi-row kernels up to 168 (12
-// wavefronts) where they fit without spilling, else 256 (8).
+// wavefronts) where they fit without spilling, else 256 (8); Q4_K with 5 or 6
+// rows 4 wavefronts (512 registers each, no scratch).
 constexpr int persist_threads(int qt, int M, bool xlds)
 {
     if (M == 1) return 1024;
     if (qt == qgl::kQ4_0) return (M <= 4 || xlds) ? 768 : 512;
-    if (qt == qgl::kQ4_K || qt == qgl::kQ6_K) return M <= 2 ? 768 : 512;
+    if (qt == qgl::kQ4_K) return M <= 2 ? 768 : (M <= 4 ? 512 : 256);
+    if (qt == qgl::kQ6_K) return M <= 2 ? 768 : 512;
     return (M <= 3 || xlds) ? 768 : 512;
 }
 

@@ -68,35 +68,6 @@ def assert_silu(y_gpu, out, g, u, ag, au, ctx: str):
     return float(np.max(err / tol)) if err.size else 0.0
 
 
-def q4_k_term_bound(canon: np.ndarray, x: np.ndarray, N: int, K: int, threads: int = 1) -> np.ndarray:
-    """sum_k (|d sc q_k| + |dmin mn|) |x_k| per row: the magnitude that bounds the
-    rounding of a Q4_K product whose two weight terms are summed apart (they can
-    cancel, so sum |w x| alone does not). Each half is the oracle's abs-sum on the
-    matrix with the other half's fp16 scale field set to zero."""
-    blocks = canon.reshape(-1, 144)
-    only_d, only_min = blocks.copy(), blocks.copy()
-    only_d[:, 2:4] = 0      # dmin = 0
-    only_min[:, 0:2] = 0    # d = 0
-    _, a_d = O.gemv("q4_k", only_d.reshape(-1), x, N, K, threads=threads)
-    _, a_m = O.gemv("q4_k", only_min.reshape(-1), x, N, K, threads=threads)
-    return a_d + a_m
-
-
-def magnitude(kind: str, abs_sum, canon: np.ndarray):
-    """The magnitude the linear tolerance scales with, per output: abs_sum(c) is an
-    oracle call's sum of |w x| on canonical weights c. Q4_K sums its d*sc and
-    dmin*mn terms apart, so there it is the sum of the two halves' abs-sums (each
-    on the matrix with the other half's fp16 scale field set to zero); every
-    other type uses abs_sum(canon) itself."""
-    if kind != "q4_k":
-        return abs_sum(canon)
-    blocks = canon.reshape(-1, 144)
-    only_d, only_min = blocks.copy(), blocks.copy()
-    only_d[:, 2:4] = 0      # dmin = 0
-    only_min[:, 0:2] = 0    # d = 0
-    return abs_sum(only_d.reshape(-1)) + abs_sum(only_min.reshape(-1))
-
-
 def run_qgemv(kind: str, canon: np.ndarray, x: np.ndarray, N: int, K: int, canary: int = 0):
     """Pack on the device, run qgemv_<kind>, return y (and the canary tail if asked)."""
     import block_dequant_gemv_amd as qg

@@ -16,7 +16,7 @@ import pytest
 import block_dequant_gemv_amd as qg
 import oracle as O
 from block_dequant_gemv_amd import workloads as W
-from gpu_helpers import THREADS, announce, assert_linear, assert_silu, empty_f32, magnitude, sync, to_dev
+from gpu_helpers import THREADS, announce, assert_linear, assert_silu, empty_f32, sync, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -63,8 +63,32 @@ def test_gemv_rmsnorm_matches_oracle(kind, N, K):
     sync()
     got = y.cpu().numpy()
     assert np.all(got[N:] == -5.0), "wrote past y[N-1]"
-    y_ref, _ = O.gemv_rmsnorm(kind, canon, x, g, float(EPS), N, K)
-    a_ref = magnitude(kind, lambda c: O.gemv_rmsnorm(kind, c, x, g, float(EPS), N, K)[1], canon)
+    y_ref, a_ref = O.gemv_rmsnorm(kind, canon, x, g, float(EPS), N, K)
+    assert_linear(got[:N], y_ref, a_ref, f"rmsnorm gemv {kind} {N}x{K}")
+
+
+# The largest K the prologue takes (39 segments, 156 KiB staged next to the
+# kernels' static arrays), in each form: one wavefront per tile with eight
+# split-K wavefronts (40 rows), the persistent form (1024 and 5120 rows, 13 K
+# ranges), and 24000 rows, whose persistent partials would not fit next to the
+# staged copy, so the plan takes the tile form (one wavefront per tile).
+@pytest.mark.parametrize("N,persistent", [(40, False), (1024, True), (5120, True), (24000, False)])
+def test_gemv_rmsnorm_largest_k(N, persistent):
+    kind, K = "q4_0", 39936
+    plan = qg.qg_plan_info(kind, N, K, 1, rmsnorm=True)
+    assert plan["persistent"] == persistent and plan["x_in_lds"] and plan["lds_bytes"] <= 160 * 1024, plan
+    rng = np.random.default_rng(700 + N)
+    canon = W.matrix(kind, N, K, rng)
+    x = W.activation(K, rng)
+    g = _gamma(K, rng)
+    packed = qg.pack_weights(kind, canon, N, K)
+    y = empty_f32(N + 4, fill=-5.0)
+    announce(f"qgemv_rmsnorm {kind} {N}x{K} plan={plan}")
+    qg.qgemv_rmsnorm(kind, packed, to_dev(x), to_dev(g), float(EPS), y[:N], N, K)
+    sync()
+    got = y.cpu().numpy()
+    assert np.all(got[N:] == -5.0), "wrote past y[N-1]"
+    y_ref, a_ref = O.gemv_rmsnorm(kind, canon, x, g, float(EPS), N, K)
     assert_linear(got[:N], y_ref, a_ref, f"rmsnorm gemv {kind} {N}x{K}")
 
 
@@ -81,9 +105,7 @@ def test_gateup_rmsnorm_matches_oracle(kind, N_ff, K):
     announce(f"qgemv_rmsnorm_gateup_silu {kind} N_ff={N_ff} K={K}")
     qg.qgemv_rmsnorm_gateup_silu(kind, packed, to_dev(x), to_dev(g), float(EPS), y, N_ff, K)
     sync()
-    out, gg, uu, _, _ = O.gateup_silu_rmsnorm(kind, gate, up, x, g, float(EPS), N_ff, K)
-    ag = magnitude(kind, lambda c: O.gemv_rmsnorm(kind, c, x, g, float(EPS), N_ff, K)[1], gate)
-    au = magnitude(kind, lambda c: O.gemv_rmsnorm(kind, c, x, g, float(EPS), N_ff, K)[1], up)
+    out, gg, uu, ag, au = O.gateup_silu_rmsnorm(kind, gate, up, x, g, float(EPS), N_ff, K)
     assert_silu(y.cpu().numpy(), out, gg, uu, ag, au, f"rmsnorm gate|up {kind} {N_ff}x{K}")
 
 

@@ -6,7 +6,7 @@ import pytest
 import block_dequant_gemv_amd as qg
 import oracle as O
 from block_dequant_gemv_amd import workloads as W
-from gpu_helpers import THREADS, announce, assert_linear, empty_f32, magnitude, sync, to_dev
+from gpu_helpers import THREADS, announce, assert_linear, empty_f32, sync, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -27,7 +27,11 @@ CASES = [("q4_0", 17408, 5120), ("q8_0", 4096, 1024), ("q8_0", 33, 2080), ("q4_0
          ("q4_0", 5120, 17408), ("q6_k", 2001, 17408), ("q4_0", 3000, 17504),
          # super-block types on 80 row tiles of 17 segments: K split eight ways at
          # every M, activations from L2 at M = 5, 6 (kernels that spill to scratch)
-         ("q4_k", 640, 17408), ("q6_k", 640, 17408)]
+         ("q4_k", 640, 17408), ("q6_k", 640, 17408),
+         # eight split-K wavefronts over 8 segments: four staged rows take 128 KiB of
+         # LDS; five rows (exactly 160 KiB) plus the partials do not fit, so M = 5, 6
+         # read their activations from L2
+         ("q4_0", 1280, 8192), ("q8_0", 1280, 8192)]
 
 
 @pytest.mark.parametrize("kind,N,K", CASES)
@@ -55,8 +59,7 @@ def test_verify_rows_bit_identical_to_m1(kind, N, K):
         assert np.all(Yh[M * N:] == 3.0), "wrote past Y[M-1][N-1]"
         for m in range(M):
             assert Yh[m * N:(m + 1) * N].tobytes() == ones[m].tobytes(), f"M={M} row {m} differs from M=1"
-    Y_ref, _ = O.verify(kind, canon, X, N, K, threads=THREADS)
-    A_ref = magnitude(kind, lambda c: O.verify(kind, c, X, N, K, threads=THREADS)[1], canon)
+    Y_ref, A_ref = O.verify(kind, canon, X, N, K, threads=THREADS)
     for m in range(6):
         assert_linear(ones[m], Y_ref[m], A_ref[m], f"verify {kind} {N}x{K} row {m}")
 

@@ -408,11 +408,50 @@ def test_q6_k_pack_places_every_field(L):
         assert bits == bin(q & 15).count("1") + bin(q >> 4).count("1"), (w, q)
 
 
+def _q4_k_centre(d_bits: int, dmin_bits: int, sc: int, mn: int) -> int:
+    """The load-time centre of a Q4_K sub-block, from its definition in exact
+    rational arithmetic: dmin*mn / (d*sc) rounded to the nearest integer (ties
+    down), clamped to 0..15; 0 when d*sc is 0."""
+    from fractions import Fraction
+    f16 = lambda b: Fraction(float(np.array([b], np.uint16).view(np.float16)[0]))  # noqa: E731
+    a, b = f16(d_bits) * sc, f16(dmin_bits) * mn
+    if a == 0:
+        return 0
+    r = b / a
+    c = int(np.floor(r))
+    if r - c > Fraction(1, 2):
+        c += 1
+    return min(15, max(0, c))
+
+
+def test_q4_k_centre_values(L):
+    # the centre stored in the low 4 bits of the scale word, against its definition
+    cases = [(0x3C00, 0x3C00, 1, 0), (0x3C00, 0x3C00, 2, 15), (0x3C00, 0x3C00, 2, 16), (0x3C00, 0x3C00, 2, 17),
+             (0x3C00, 0x4000, 16, 32), (0x3C00, 0x3C00, 1, 63), (0x3C00, 0x3C00, 0, 5), (0x0000, 0x3C00, 9, 9),
+             (0xBC00, 0x3C00, 4, 20), (0x3C00, 0xBC00, 4, 20), (0xBC00, 0xBC00, 4, 20), (0x0001, 0x0003, 63, 21),
+             (0x7BFF, 0x0001, 63, 63), (0x0001, 0x7BFF, 63, 63), (0x3555, 0x2AAA, 7, 11)]
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        cases.append((int(rng.integers(0, 0x7C00)) | (0x8000 if rng.random() < 0.1 else 0),
+                      int(rng.integers(0, 0x7C00)), int(rng.integers(0, 64)), int(rng.integers(0, 64))))
+    for d, dmin, sc, mn in cases:
+        canon = np.zeros(144, np.uint8)
+        canon[0:4] = [d & 255, d >> 8, dmin & 255, dmin >> 8]
+        canon[4] = sc
+        canon[8] = mn
+        packed = qg.qg_pack_host("q4_k", canon, 1, 256)
+        word = int(packed[1024]) | (int(packed[1025]) << 8)
+        assert word & 15 == _q4_k_centre(d, dmin, sc, mn), (hex(d), hex(dmin), sc, mn, word & 15)
+        assert (word >> 4) & 63 == sc and word >> 10 == mn
+        assert np.array_equal(qg.qg_unpack_host("q4_k", packed, 1, 256), canon)
+
+
 def test_q4_k_pack_places_every_field(L):
     # One row, K = 256: each field of the canonical super-block, set alone, lands
     # where the kernel reads it: d and dmin in the super plane (row 0, slot 0),
-    # sub-block j's 6-bit scale and min as bytes 0 and 1 of its scale-plane entry,
-    # and its nibbles in the Q4_0 arrangement of quant-plane block j.
+    # sub-block j's 6-bit scale and min in bits 4-9 and 10-15 of its scale-plane
+    # word (bits 0-3: the centre), and its nibbles in the Q4_0 arrangement of
+    # quant-plane block j.
     N, K = 1, 256
     size = qg.qg_packed_size("q4_k", N, K)
     q_bytes, s_off = 8 * 8 * 16, 1024
@@ -433,7 +472,8 @@ def test_q4_k_pack_places_every_field(L):
             assert packed.size == size
             assert list(packed[u_off:u_off + 4]) == [0x11, 0x22, 0x33, 0x44]
             # scale plane: (slot 0 * nb + j) * 4 rows * 2 B, row 0
-            assert packed[s_off + j * 8] == sc and packed[s_off + j * 8 + 1] == mn
+            word = int(packed[s_off + j * 8]) | (int(packed[s_off + j * 8 + 1]) << 8)
+            assert word == _q4_k_centre(0x2211, 0x4433, sc, mn) | (sc << 4) | (mn << 10), (j, sc, mn, hex(word))
             assert not packed[:q_bytes].any()
     # weight 64 g + l (l < 32) is the low nibble of byte 32 g + l: sub-block 2 g,
     # element l; weight 64 g + 32 + l the high nibble: sub-block 2 g + 1
