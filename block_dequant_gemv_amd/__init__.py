@@ -32,7 +32,7 @@ SYMBOLS = (
     "qg_pack_host", "qg_unpack_host", "qg_pack_gateup_host",
     "qgemv_q8_0", "qgemv_q4_0", "qgemv_q4_k", "qgemv_q6_k", "qgemv_epilogue", "gemv_f16_splitk", "qgemv_fused_gateup_silu", "qgemv_verify",
     "qg_rmsnorm", "qgemv_rmsnorm", "qgemv_rmsnorm_gateup_silu", "qg_prefill_workspace_size", "qgemm_prefill",
-    "qg_status_str", "qg_last_error", "qg_plan_info", "qg_time_next_launch", "qg_reload_tuning",
+    "qg_status_str", "qg_last_error", "qg_plan_info", "qg_f16_plan_info", "qg_time_next_launch", "qg_reload_tuning",
 )
 
 
@@ -86,6 +86,8 @@ def lib():
             "qg_last_error": ([], ctypes.c_char_p),
             "qg_plan_info": ([i32, i64, i64, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i64),
                               ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i64)], i32),
+            "qg_f16_plan_info": ([i64, i64, vp, vp, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                  ctypes.POINTER(i64)], i32),
             "qg_time_next_launch": ([vp, vp], i32),
             "qg_reload_tuning": ([], i32),
         }
@@ -295,6 +297,20 @@ def qg_plan_info(qtype, N: int, K: int, M: int = 1, rmsnorm: bool = False) -> di
                                               ctypes.byref(lds)))
     return {"split_k_ways": w.value, "workgroups": g.value, "x_in_lds": bool(xl.value),
             "persistent": bool(ps.value), "lds_bytes": lds.value}
+
+
+F16_FORMS = {0: "lane-split", 1: "row", 2: "split-K row"}
+
+
+def qg_f16_plan_info(N: int, K: int, w_addr: int = 0, x_addr: int = 0) -> dict:
+    """The form gemv_f16_splitk takes for this shape; w_addr and x_addr are the
+    addresses whose alignment it inspects (0: 16-byte aligned)."""
+    f = ctypes.c_int()
+    wv = ctypes.c_int()
+    g = ctypes.c_int64()
+    _check("qg_f16_plan_info", lib().qg_f16_plan_info(N, K, w_addr or 0x10000, x_addr or 0x10000, ctypes.byref(f),
+                                                      ctypes.byref(wv), ctypes.byref(g)))
+    return {"form": F16_FORMS[f.value], "waves": wv.value, "workgroups": g.value}
 
 
 def qg_reload_tuning():

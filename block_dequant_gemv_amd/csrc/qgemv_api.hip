@@ -87,17 +87,17 @@ int64_t env_int(const char *name, int64_t dflt)
 // Launch-shape overrides for sweeps and tests (QG_SPLIT_K, QG_PERSIST,
 // QG_X_GLOBAL, QG_TILES_PER_GROUP, QG_WAVES_PER_WG, QG_PREFETCH, QG_F16_ROWS,
 // QG_F16_WAVES, QG_STRIDE_GROUPS, QG_GEMM_MT, QG_GEMM_WAVES, QG_GEMM_ROWGROUPS,
-// QG_GEMM_KSPLIT, QG_F16_FORM). They are read from the environment once, on first use, and
+// QG_GEMM_KSPLIT, QG_F16_FORM, QG_F16_CPL). They are read from the environment once, on first use, and
 // again on qg_reload_tuning(): a GEMV call itself reads no environment.
 enum TuneKey {
     kSplitK, kPersist, kXGlobal, kTilesPerGroup, kWavesPerWg, kPrefetch, kF16Rows, kF16Waves, kStrideGroups,
-    kGemmMT, kGemmWaves, kGemmRowGroups, kGemmKSplit, kF16Form, kNumTune
+    kGemmMT, kGemmWaves, kGemmRowGroups, kGemmKSplit, kF16Form, kF16Cpl, kNumTune
 };
 const char *const kTuneNames[kNumTune] = {"QG_SPLIT_K",      "QG_PERSIST",  "QG_X_GLOBAL",  "QG_TILES_PER_GROUP",
                                           "QG_WAVES_PER_WG", "QG_PREFETCH", "QG_F16_ROWS",  "QG_F16_WAVES",
                                           "QG_STRIDE_GROUPS", "QG_GEMM_MT", "QG_GEMM_WAVES", "QG_GEMM_ROWGROUPS",
-                                          "QG_GEMM_KSPLIT", "QG_F16_FORM"};
-const int64_t kTuneDefaults[kNumTune] = {0, -1, -1, 0, 0, 0, 0, 0, -1, 0, 0, 0, 0, -1};
+                                          "QG_GEMM_KSPLIT", "QG_F16_FORM", "QG_F16_CPL"};
+const int64_t kTuneDefaults[kNumTune] = {0, -1, -1, 0, 0, 0, 0, 0, -1, 0, 0, 0, 0, -1, 0};
 std::atomic<int64_t> g_tune[kNumTune];
 std::atomic<bool> g_tune_loaded{false};
 
@@ -456,6 +456,63 @@ GemmPlan plan_gemm(int qt, int64_t N, int64_t K, int64_t M)
     return p;
 }
 
+// Launch plan of gemv_f16_splitk (depends on the shape and on whether w and x
+// are 16-byte aligned). Three forms, all deterministic with a fixed order of
+// additions:
+//  - split-K row form (short matrices, fewer than 1024 rows): one row per
+//    workgroup, K split into consecutive ranges over its wavefronts (4 16-byte
+//    chunks per lane), partials added in wavefront order. Measured on MI355X,
+//    cold, back to back against the row form: 640 x 5120 3.70 against 4.10 us;
+//    48 and 256 rows x 5120 within 0.1-0.3 us (every form of these two reads
+//    the ~3.9 us dispatch floor by kernel timestamps);
+//  - row form (K = 512 L, L <= 16): one wavefront per row with the whole row's
+//    loads in flight at once, x staged in LDS once per workgroup of 4 rows.
+//    Measured on MI355X, cold, against the lane-split form: 5120 x 5120 9.96
+//    against 10.78 us, 5120 x 8192 15.3 against 17.2, 17408 x 4096 22.4
+//    against 27.0;
+//  - lane-split form (any other K, or unaligned pointers): one row per
+//    workgroup, K split over the lanes of one wavefront (four below 1024 rows)
+//    in 8-element chunks.
+// QG_F16_FORM = 0 / 1 / 2 forces the lane-split / row / split-K row form (where
+// K and the alignment allow it), QG_F16_CPL = 1, 2, 4 the chunks per lane of
+// the split-K row form, QG_F16_WAVES and QG_F16_ROWS the other forms' shapes.
+qgk::F16Plan plan_f16(int64_t N, int64_t K, const void *w_f16, const float *x)
+{
+    qgk::F16Plan p;
+    p.vec = (K % 8 == 0) && aligned(w_f16, 16) && aligned(x, 16);
+    p.L = 0;
+    p.cpl = 0;
+    p.R = 1;
+    const int64_t w_env = tune(kF16Waves);
+    const int64_t form = tune(kF16Form);
+    const int64_t nch = K / 8;
+    const int64_t cpl_env = tune(kF16Cpl);
+    const int64_t cpl = (cpl_env == 1 || cpl_env == 2 || cpl_env == 4) ? cpl_env : 4;
+    const bool wsplit_ok = p.vec && nch <= 16 * 64 * cpl && N <= INT32_MAX;   // one workgroup per row
+    if (wsplit_ok && (form == 2 || (form < 0 && N < 1024))) {
+        p.cpl = (int)cpl;
+        p.waves = (int)((nch + 64 * cpl - 1) / (64 * cpl));
+        p.grid = N;
+        return p;
+    }
+    const bool row_ok = p.vec && K % 512 == 0 && K / 512 <= qgk::kF16RowMaxL;
+    if (row_ok && form != 0) {
+        p.L = (int)(K / 512);
+        p.waves = (w_env == 2 || w_env == 4 || w_env == 8) ? (int)w_env : (N < 1024 ? 2 : 4);
+        p.grid = (N + p.waves - 1) / p.waves;
+        return p;
+    }
+    const int64_t r_env = tune(kF16Rows);
+    if (r_env == 1 || r_env == 2 || r_env == 4) p.R = (int)r_env;
+    int64_t waves = N >= 1024 ? 1 : 4;
+    if (w_env > 0) waves = w_env;
+    if (waves > 16) waves = 16;
+    if (waves < 1) waves = 1;
+    p.waves = (int)waves;
+    p.grid = (N + p.R - 1) / p.R;
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -713,44 +770,7 @@ qg_status gemv_f16_splitk(const void *w_f16, const float *x, float *y, int64_t N
     if (overlap(y, (size_t)N * 4, w_f16, (size_t)N * (size_t)K * 2))
         return fail(QG_EINVAL, "%s: y overlaps the weights", fn);
 
-    qgk::F16Plan p;
-    p.vec = (K % 8 == 0) && aligned(w_f16, 16) && aligned(x, 16);
-    p.L = 0;
-    const int64_t w_env = tune(kF16Waves);
-    // Row form (one wavefront per row, the whole row's loads in flight at once,
-    // x from LDS) wherever K = 512 L, L <= 16: 4 rows per workgroup, 2 below
-    // 1024 rows. Measured on MI355X, cold, against the split-K form: 5120 x 5120
-    // 9.96 against 10.78 us, 5120 x 8192 15.3 against 17.2, 17408 x 4096 22.4
-    // against 27.0; 256 and 48 rows x 5120 the same (3.9 us, the dispatch
-    // floor) and a little faster back to back. QG_F16_FORM = 0 / 1 forces the
-    // split-K / row form (the latter where K allows it), QG_F16_WAVES = 2, 4, 8
-    // the rows per workgroup.
-    const int64_t form = tune(kF16Form);
-    const bool row_ok = p.vec && K % 512 == 0 && K / 512 <= qgk::kF16RowMaxL;
-    if (row_ok && form != 0) {
-        p.L = (int)(K / 512);
-        p.R = 1;
-        p.waves = (w_env == 2 || w_env == 4 || w_env == 8) ? (int)w_env : (N < 1024 ? 2 : 4);
-        p.grid = (N + p.waves - 1) / p.waves;
-        hipError_t e = qgk::launch_f16(p, (const uint16_t *)w_f16, x, y, N, K, as_stream(stream));
-        if (e != hipSuccess) return hip_fail(e, fn);
-        return ok();
-    }
-    // Split-K form (other K, or unaligned): one row per workgroup; one
-    // wavefront per row when there are enough rows to cover the CUs (each lane
-    // walks K/512 16-byte chunks of its row), four otherwise (measured on
-    // MI355X, cold: 256 x 5120 and 48 x 5120 3.9 us, against 5.1 / 4.7 us for
-    // register-blocked rows).
-    // QG_F16_ROWS (1, 2, 4) and QG_F16_WAVES override the shape for sweeps.
-    p.R = 1;
-    const int64_t r_env = tune(kF16Rows);
-    if (r_env == 1 || r_env == 2 || r_env == 4) p.R = (int)r_env;
-    int64_t waves = N >= 1024 ? 1 : 4;
-    if (w_env > 0) waves = w_env;
-    if (waves > 16) waves = 16;
-    if (waves < 1) waves = 1;
-    p.waves = (int)waves;
-    p.grid = (N + p.R - 1) / p.R;
+    const qgk::F16Plan p = plan_f16(N, K, w_f16, x);
     hipError_t e = qgk::launch_f16(p, (const uint16_t *)w_f16, x, y, N, K, as_stream(stream));
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
@@ -791,6 +811,18 @@ qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int rmsnorm, int 
         const int floats = p.persist ? qgk::persist_red_floats(norm) : qgk::tile_red_floats(M, p.W, norm);
         *lds_bytes = (int64_t)(qgk::static_lds_bytes(floats) + p.lds_bytes);
     }
+    return ok();
+}
+
+qg_status qg_f16_plan_info(int64_t N, int64_t K, const void *w_f16, const float *x, int *form, int *waves,
+                           int64_t *workgroups)
+{
+    if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim)
+        return fail(QG_EINVAL, "qg_f16_plan_info: N=%lld K=%lld must be positive", (long long)N, (long long)K);
+    const qgk::F16Plan p = plan_f16(N, K, w_f16, x);
+    if (form) *form = p.cpl > 0 ? 2 : (p.L > 0 ? 1 : 0);
+    if (waves) *waves = p.waves;
+    if (workgroups) *workgroups = p.grid;
     return ok();
 }
 

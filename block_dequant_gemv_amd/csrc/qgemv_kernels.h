@@ -61,10 +61,12 @@ struct QPlan {
 };
 
 struct F16Plan {
-    int R;               // split-K form: rows per workgroup (register-blocked)
-    int waves;           // split-K form: wavefronts splitting K; row form: rows (wavefronts) per workgroup
+    int R;               // lane-split form: rows per workgroup (register-blocked)
+    int waves;           // lane-split and split-K row forms: wavefronts splitting K;
+                         // row form: rows (wavefronts) per workgroup
     bool vec;            // 16-byte path (K % 8 == 0 and aligned pointers)
-    int L;               // 0: split-K form; 1..kF16RowMaxL: row form for K = 512 * L
+    int L;               // 1..kF16RowMaxL: row form for K = 512 * L
+    int cpl;             // 1, 2, 4: split-K row form with cpl chunks per lane (L == 0)
     int64_t grid;
 };
 

@@ -137,6 +137,63 @@ gemv_f16_row_kernel(const uint16_t *__restrict__ w, const float *__restrict__ x,
 }
 
 // ---------------------------------------------------------------------------
+// fp16 GEMV, split-K row form, for short matrices (few rows, long K): one
+// workgroup per row, whose W = blockDim / 64 wavefronts own consecutive K
+// ranges of 64 CPL 16-byte chunks (8 weights) each: lane l of wavefront v takes
+// chunks 64 CPL v + 64 i + l, i < CPL, and chunks at or past K / 8 count as
+// nothing. Every lane issues all its weight and activation loads at once (the
+// activations straight from L2: each wavefront reads only its range), then one
+// fma chain over its chunks in order (8 products each), the wavefront
+// butterfly, and the W partial sums are added in wavefront order through LDS:
+// at most 8 CPL + 6 + W roundings. Needs K % 8 == 0 and 16-byte aligned w, x.
+template <int CPL>
+__global__ void __launch_bounds__(1024)
+gemv_f16_wsplit_kernel(const uint16_t *__restrict__ w, const float *__restrict__ x, float *__restrict__ y,
+                       int64_t N, int64_t K)
+{
+    __shared__ float red[16];
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwave = blockDim.x >> 6;
+    const int64_t row = blockIdx.x;
+    const uint32_t nch = (uint32_t)(K >> 3);
+    const u32x4 *wr = (const u32x4 *)(w + row * K);
+    const f32x4 *x4 = (const f32x4 *)x;
+    u32x4 v[CPL];
+    f32x4 xa[CPL], xb[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const uint32_t c = wave * (64u * CPL) + 64u * i + lane;
+        const uint32_t cc = c < nch ? c : 0u;
+        v[i] = __builtin_nontemporal_load(wr + cc);
+        xa[i] = x4[2 * cc];
+        xb[i] = x4[2 * cc + 1];
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const h2 p0 = as_h2(v[i].x), p1 = as_h2(v[i].y), p2 = as_h2(v[i].z), p3 = as_h2(v[i].w);
+        float t = acc;
+        t = __builtin_fmaf((float)p0.x, xa[i].x, t);
+        t = __builtin_fmaf((float)p0.y, xa[i].y, t);
+        t = __builtin_fmaf((float)p1.x, xa[i].z, t);
+        t = __builtin_fmaf((float)p1.y, xa[i].w, t);
+        t = __builtin_fmaf((float)p2.x, xb[i].x, t);
+        t = __builtin_fmaf((float)p2.y, xb[i].y, t);
+        t = __builtin_fmaf((float)p3.x, xb[i].z, t);
+        t = __builtin_fmaf((float)p3.y, xb[i].w, t);
+        acc = (wave * (64u * CPL) + 64u * i + lane < nch) ? t : acc;
+    }
+    const float h = half_wave_sum(acc);
+    const float tot = as_f(__builtin_amdgcn_readlane(as_i(h), 0)) + as_f(__builtin_amdgcn_readlane(as_i(h), 32));
+    if (lane == 0) red[wave] = tot;
+    __syncthreads();
+    if (tid == 0) {
+        float sum = red[0];
+        for (uint32_t u = 1; u < nwave; ++u) sum += red[u];
+        y[row] = sum;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Standalone RMSNorm of one activation vector (one workgroup): out[k] =
 // (x[k] * r) * gamma[k], r = 1 / sqrt(sum(x^2) / K + eps), with the same
 // reduction scheme as the GEMV prologue.
@@ -295,6 +352,19 @@ hipError_t launch_f16(const F16Plan &p, const uint16_t *w, const float *x, float
 {
     const dim3 grid((unsigned)p.grid), block(p.waves * 64);
     auto go = [&](auto kern) { launch(kern, grid, block, 0u, s, w, x, y, N, K); };
+    if (p.cpl > 0) {
+        // split-K row form: one row per workgroup, every chunk of the row covered
+        if (!p.vec || p.grid != N || p.waves < 1 || p.waves > 16 ||
+            (K / 8) > (int64_t)p.waves * 64 * p.cpl || (K / 8) <= (int64_t)(p.waves - 1) * 64 * p.cpl)
+            return hipErrorInvalidConfiguration;
+        switch (p.cpl) {
+        case 1: go(gemv_f16_wsplit_kernel<1>); break;
+        case 2: go(gemv_f16_wsplit_kernel<2>); break;
+        case 4: go(gemv_f16_wsplit_kernel<4>); break;
+        default: return hipErrorInvalidConfiguration;
+        }
+        return hipGetLastError();
+    }
     if (p.L > 0) {
         // row form: K = 512 L, x staged in K * 4 bytes of LDS (at most 32 KiB)
         if (!p.vec || p.L > kF16RowMaxL || K != 512 * (int64_t)p.L || (p.waves != 2 && p.waves != 4 && p.waves != 8))

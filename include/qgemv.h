@@ -26,7 +26,14 @@
  *  - Arguments are checked on the host before any HIP call. A bad argument
  *    returns QG_EINVAL / QG_EALIGN / QG_EUNSUPPORTED and enqueues nothing; a
  *    failed launch returns QG_EHIP. qg_last_error() gives a thread-local
- *    message for the last failure on the calling thread.
+ *    message for the last failure on the calling thread. Order of the checks:
+ *    sizes and types, null pointers, alignment, then overlaps.
+ *  - Alignment of the quantised GEMV calls (qgemv_q8_0, qgemv_q4_0, qgemv_q4_k,
+ *    qgemv_q6_k, qgemv_epilogue, qgemv_fused_gateup_silu, qgemv_verify,
+ *    qgemv_rmsnorm, qgemv_rmsnorm_gateup_silu): packed weights, x / X and gamma
+ *    16-byte aligned (the kernels read them with 16-byte loads); fp32 outputs,
+ *    bias and residual 4-byte aligned; fp16 outputs 2-byte aligned. Anything
+ *    less returns QG_EALIGN.
  *  - Same inputs give bitwise the same outputs, run to run (no atomics, no
  *    cross-workgroup reductions, fixed reduction trees).
  *  - Quantised weights are re-tiled once, at load time, by qg_pack* into the
@@ -100,12 +107,13 @@ qg_status qg_pack_gateup_host(int qtype, const void *gate_host, const void *up_h
 /* ---- the GEMVs ----------------------------------------------------------- */
 
 /* y[N] = W x for a packed Q8_0 weight (N x K, K % 32 == 0); x: fp32 [K];
- * y: fp32 [N]. w_packed 16-byte aligned, x and y 4-byte aligned, y must not
+ * y: fp32 [N]. w_packed and x 16-byte aligned, y 4-byte aligned; y must not
  * overlap x or w_packed. A fused QKV projection is this call on the packed
  * concatenation (qg_pack_rows); the caller slices y. */
 qg_status qgemv_q8_0(const void *w_packed, const float *x, float *y, int64_t N, int64_t K, void *stream);
 
-/* Same for a packed Q4_0 weight (weight value nibble - 8). */
+/* Same for a packed Q4_0 weight (weight value nibble - 8), with the same
+ * alignment (w_packed and x 16 bytes, y 4 bytes). */
 qg_status qgemv_q4_0(const void *w_packed, const float *x, float *y, int64_t N, int64_t K, void *stream);
 
 /* The same for a packed Q4_K weight (K % 256 == 0). Q4_K is the k-quant block
@@ -114,8 +122,11 @@ qg_status qgemv_q4_0(const void *w_packed, const float *x, float *y, int64_t N, 
  * the published GGUF block: per 256 weights an fp16 d and dmin, eight 6-bit
  * sub-block scales sc and mins mn in 12 bytes, 128 bytes of 4-bit quants q;
  * weight = d * sc * q - dmin * mn. Per 32-weight sub-block the product is
- * summed as d*sc * sum(q x) - dmin*mn * sum(x) in fp32 (the two terms can
- * cancel: the rounding scales with sum (|d sc q| + |dmin mn|) |x|).
+ * summed in fp32 as d*sc * sum((q - c) x) + (d*sc*c - dmin*mn) * sum(x), with
+ * c = dmin*mn / (d*sc) rounded and clamped to 0..15, which the packer derives at
+ * load time: both terms are bounded by 3 |w| per weight, so each output is
+ * within 1e-5 * sum |w x| + 1e-7 of the exact product like the other types,
+ * also where d*sc*q and dmin*mn cancel. Same alignment as qgemv_q4_0.
  * Q4_K packs with qg_pack / qg_pack_rows / qg_pack_gateup / qg_pack_host (148
  * bytes per 256 weights). The other GEMV calls (qgemv_epilogue,
  * qgemv_fused_gateup_silu, qgemv_verify, qgemv_rmsnorm,
@@ -162,20 +173,28 @@ qg_status qgemv_epilogue(int qtype, const void *w_packed, const float *x, const 
                          const float *residual, void *y, int out_type, int64_t N, int64_t K, void *stream);
 
 /* Unquantised fp16 weights, y = W x with W fp16 row-major [N][K] (any K >= 1,
- * 2-byte aligned; the fast paths need K % 8 == 0 and 16-byte alignment), x fp32
- * [K], y fp32 [N]. Each row's K is split across the lanes of one wavefront,
- * and for short matrices across the wavefronts of one workgroup, with the
- * partial sums combined in a fixed order: deterministic, no workspace, no
- * atomics (robotnurse.io post, What actually moved it, 4: a split-K fp16 GEMV
- * for the unquantised matrices). Matrices of at least 1024 rows with
- * K = 512 L (L <= 16) and the 16-byte alignment run one wavefront per row with
- * the whole row's loads in flight; others, split K over the wavefronts. */
+ * 2-byte aligned), x fp32 [K] (4-byte aligned), y fp32 [N] (4-byte aligned,
+ * not overlapping x or W). Each row's K is split, and the partial sums are
+ * combined in a fixed order: deterministic, no workspace, no atomics
+ * (robotnurse.io post, What actually moved it, 4: a split-K fp16 GEMV for the
+ * unquantised matrices). Forms, chosen by shape; the first two need K % 8 == 0
+ * and W and x 16-byte aligned, else the last form runs:
+ *  - fewer than 1024 rows and K <= 32768: one workgroup per row, K split into
+ *    consecutive ranges over up to 16 wavefronts, partials added in wavefront
+ *    order;
+ *  - otherwise, K = 512 L with L <= 16: one wavefront per row, K split over its
+ *    64 lanes, with the whole row's loads in flight at once;
+ *  - otherwise: one workgroup per row, K split over the lanes of one wavefront
+ *    (four below 1024 rows) in 8-element chunks, partials added in wavefront
+ *    order. */
 qg_status gemv_f16_splitk(const void *w_f16, const float *x, float *y, int64_t N, int64_t K, void *stream);
 
 /* Fused gate+up with the SiLU epilogue (RunIT_Mac README "Fused gate+up+silu",
  * one dispatch instead of three): y[n] = silu(g[n]) * u[n] for n < N_ff, where
  * g = W_gate x, u = W_up x and silu(g) = g / (1 + exp(-g)).
- * w_gateup_packed comes from qg_pack_gateup; x fp32 [K]; y fp32 [N_ff]. */
+ * w_gateup_packed comes from qg_pack_gateup (16-byte aligned); x fp32 [K]
+ * (16-byte aligned); y fp32 [N_ff] (4-byte aligned, not overlapping x or the
+ * weights). */
 qg_status qgemv_fused_gateup_silu(int qtype, const void *w_gateup_packed, const float *x, float *y,
                                   int64_t N_ff, int64_t K, void *stream);
 
@@ -195,7 +214,8 @@ qg_status qg_rmsnorm(const float *x, const float *gamma, float eps, float *out, 
  * L2 re-reads per threadgroup): y = W * rmsnorm(x), one dispatch. Every
  * workgroup stages x in LDS, reduces sum(x^2) itself and normalises its copy,
  * then runs the GEMV of qgemv_q8_0 / qgemv_q4_0 on it. Arguments as for those
- * calls plus gamma fp32 [K] (16-byte aligned, not overlapping y) and eps as in
+ * calls (w_packed and x 16-byte aligned, y 4-byte aligned) plus gamma fp32 [K]
+ * (16-byte aligned, not overlapping y) and eps as in
  * qg_rmsnorm. K <= 39936 (the normalised copy lives in LDS, next to the
  * kernel's own static arrays), else QG_EUNSUPPORTED. The result is within the linear tolerance of the exact
  * product on the exact normalised vector; it is not bitwise equal to
@@ -209,7 +229,9 @@ qg_status qgemv_rmsnorm_gateup_silu(int qtype, const void *w_gateup_packed, cons
                                     float eps, float *y, int64_t N_ff, int64_t K, void *stream);
 
 /* Multi-row "verify" GEMV: Y[m][n] = sum_k W[n][k] X[m][k] for 2 <= M <= 6,
- * X fp32 row-major [M][K], Y fp32 row-major [M][N]. The packed weights are
+ * X fp32 row-major [M][K] (16-byte aligned; K % 32 == 0 keeps every row
+ * 16-byte aligned), Y fp32 row-major [M][N] (4-byte aligned, not overlapping
+ * X or the weights), w_packed 16-byte aligned. The packed weights are
  * streamed once for all M rows, and row m of Y is bit-for-bit (memcmp) equal
  * to what qgemv_q8_0 / qgemv_q4_0 return for x = X[m] (robotnurse.io post,
  * Update and "Correctness first": a 3-6-row verify pass in one weight stream,
@@ -271,10 +293,20 @@ const char *qg_last_error(void);
 qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int rmsnorm, int *split_k_ways,
                        int64_t *workgroups, int *x_in_lds, int *persistent, int64_t *lds_bytes);
 
+/* How gemv_f16_splitk launches for this shape (for reports and tests). w_f16
+ * and x are only inspected for their 16-byte alignment, never read. Outputs
+ * (each may be NULL): form 2 = one workgroup per row with K split over its
+ * wavefronts, 1 = one wavefront per row, 0 = K split over the lanes of one or
+ * four wavefronts per row (the three forms of gemv_f16_splitk, in its order);
+ * waves = wavefronts per row (form 2, 0) or rows per workgroup (form 1);
+ * workgroups launched. Host function. Returns QG_OK or QG_EINVAL. */
+qg_status qg_f16_plan_info(int64_t N, int64_t K, const void *w_f16, const float *x, int *form, int *waves,
+                           int64_t *workgroups);
+
 /* Re-read the launch-shape overrides (QG_SPLIT_K, QG_PERSIST, QG_X_GLOBAL,
  * QG_TILES_PER_GROUP, QG_WAVES_PER_WG, QG_PREFETCH, QG_F16_ROWS, QG_F16_WAVES,
  * QG_STRIDE_GROUPS, QG_GEMM_MT, QG_GEMM_WAVES, QG_GEMM_ROWGROUPS, QG_GEMM_KSPLIT,
- * QG_F16_FORM)
+ * QG_F16_FORM, QG_F16_CPL)
  * from the environment. They exist for launch-shape sweeps and tests and are
  * read once, at the first call that plans a launch; the GEMV calls themselves
  * read no environment. An override that changes a matrix's K split (QG_SPLIT_K,

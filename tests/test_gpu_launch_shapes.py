@@ -138,3 +138,50 @@ def test_f16_row_form(N, K):
         for k in ("QG_F16_WAVES", "QG_F16_FORM"):
             os.environ.pop(k, None)
         qg.qg_reload_tuning()
+
+
+# The split-K row form (one workgroup per row, K split into consecutive ranges
+# over up to 16 wavefronts, 1, 2 or 4 16-byte chunks per lane, partials added
+# in wavefront order): the configuration's short matrices, one chunk in all,
+# ragged K (K / 8 not a multiple of 64), exactly 16 wavefronts (K = 16384 at 2
+# chunks per lane, 32768 at 4) and a K that 2 chunks per lane cannot cover in
+# 16 wavefronts (16392: that forced shape takes the lane-split form), against the oracle;
+# the same bits run to run; and the default plan of a short matrix is this form.
+@pytest.mark.parametrize("N,K", [(48, 5120), (256, 5120), (1, 8), (3, 1000), (37, 24), (5, 16384), (2, 16392),
+                                 (7, 32768), (1023, 512)])
+def test_f16_split_k_row_form(N, K):
+    rng = np.random.default_rng(11 * N + K)
+    w = W.f16_matrix(N, K, rng)
+    x = W.activation(K, rng)
+    wd, xd = to_dev(w), to_dev(x)
+    y_ref, a_ref = O.gemv("f16", w, x, N, K, threads=THREADS)
+    outs = {}
+    try:
+        for cpl in (0, 1, 2, 4):
+            os.environ["QG_F16_FORM"] = "2"
+            if cpl:
+                os.environ["QG_F16_CPL"] = str(cpl)
+            else:
+                os.environ.pop("QG_F16_CPL", None)
+            qg.qg_reload_tuning()
+            ctx = f"f16 split-K row form {N}x{K} chunks/lane={cpl or 'default'}"
+            announce(ctx)
+            y0, y1 = empty_f32(N + 1), empty_f32(N)
+            y0[N:] = -7.0
+            qg.gemv_f16_splitk(wd, xd, y0, N, K)
+            qg.gemv_f16_splitk(wd, xd, y1, N, K)
+            sync()
+            a0 = y0.cpu().numpy()
+            assert a0[N] == -7.0, ctx + ": wrote past y"
+            assert_linear(a0[:N], y_ref, a_ref, ctx)
+            assert a0[:N].tobytes() == y1.cpu().numpy().tobytes(), ctx + ": run-to-run bits differ"
+            outs[cpl] = a0[:N].tobytes()
+    finally:
+        for k in ("QG_F16_FORM", "QG_F16_CPL"):
+            os.environ.pop(k, None)
+        qg.qg_reload_tuning()
+    announce(f"f16 default plan {N}x{K}")
+    y = empty_f32(N)
+    qg.gemv_f16_splitk(wd, xd, y, N, K)
+    sync()
+    assert y.cpu().numpy().tobytes() == outs[0], "the default plan of a short matrix is the split-K row form"

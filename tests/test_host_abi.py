@@ -144,6 +144,60 @@ def test_argument_checks_return_codes_without_gpu(L):
     assert "overlap" in msg
 
 
+def _alignment_cases():
+    """(call, argument builder, {pointer: documented alignment}) for every entry
+    point that checks alignment, as include/qgemv.h states it. The builder takes
+    a dict of pointers; the output always overlaps the activations (or the
+    packed buffer the canonical one), so a call whose alignment checks pass
+    fails the overlap check that follows them, before any HIP call."""
+    import ctypes as C
+    e = C.c_float(1e-6)
+    N, K = 8, 256
+    return [
+        ("qgemv_q8_0", lambda p: (p["w"], p["x"], p["y"], N, K, None), {"w": 16, "x": 16, "y": 4}),
+        ("qgemv_q4_0", lambda p: (p["w"], p["x"], p["y"], N, K, None), {"w": 16, "x": 16, "y": 4}),
+        ("qgemv_q4_k", lambda p: (p["w"], p["x"], p["y"], N, K, None), {"w": 16, "x": 16, "y": 4}),
+        ("qgemv_q6_k", lambda p: (p["w"], p["x"], p["y"], N, K, None), {"w": 16, "x": 16, "y": 4}),
+        ("qgemv_epilogue", lambda p: (2, p["w"], p["x"], p["b"], p["r"], p["y"], qg.QG_OUT_F32, N, K, None),
+         {"w": 16, "x": 16, "b": 4, "r": 4, "y": 4}),
+        ("qgemv_epilogue", lambda p: (1, p["w"], p["x"], None, None, p["y"], qg.QG_OUT_F16, N, K, None),
+         {"w": 16, "x": 16, "y": 2}),
+        ("qgemv_fused_gateup_silu", lambda p: (3, p["w"], p["x"], p["y"], N, K, None), {"w": 16, "x": 16, "y": 4}),
+        ("qgemv_verify", lambda p: (4, p["w"], p["x"], p["y"], N, K, 3, None), {"w": 16, "x": 16, "y": 4}),
+        ("qgemv_rmsnorm", lambda p: (1, p["w"], p["x"], p["g"], e, p["y"], N, K, None),
+         {"w": 16, "x": 16, "g": 16, "y": 4}),
+        ("qgemv_rmsnorm_gateup_silu", lambda p: (2, p["w"], p["x"], p["g"], e, p["y"], N, K, None),
+         {"w": 16, "x": 16, "g": 16, "y": 4}),
+        ("gemv_f16_splitk", lambda p: (p["w"], p["x"], p["y"], N, K, None), {"w": 2, "x": 4, "y": 4}),
+        ("qgemm_prefill", lambda p: (1, p["w"], p["x"], p["y"], N, K, 4, p["s"], 1 << 20, None),
+         {"w": 16, "x": 4, "y": 4, "s": 256}),
+        ("qg_rmsnorm", lambda p: (p["x"], p["g"], e, p["y"], K, None), {"x": 4, "g": 4, "y": 4}),
+        ("qg_pack", lambda p: (1, p["c"], p["p"], N, K, None), {"p": 16}),
+        ("qg_pack_rows", lambda p: (2, p["c"], p["p"], N, 0, N, K, None), {"p": 16}),
+        ("qg_pack_gateup", lambda p: (1, p["c"], p["c2"], p["p"], N, K, None), {"p": 16}),
+    ]
+
+
+def test_documented_alignment_is_exactly_what_is_checked(L):
+    # every pointer at exactly its documented alignment passes the alignment
+    # checks (the call then fails on the deliberate overlap: QG_EINVAL), and at
+    # half of it is refused with QG_EALIGN
+    f = FAKE
+    base = {"w": f, "x": f + (1 << 20), "g": f + (2 << 20), "b": f + (3 << 20), "r": f + (4 << 20),
+            "s": f + (5 << 20), "c": f + (6 << 20), "c2": f + (7 << 20)}
+    base["y"] = base["x"] + 64          # overlaps x
+    base["p"] = base["c"] + 64          # overlaps the canonical input
+    for name, args, align in _alignment_cases():
+        for arg, a in align.items():
+            for off, want in ((a, qg.QG_EINVAL), (a // 2, qg.QG_EALIGN)):
+                ptrs = dict(base)
+                ptrs[arg] = base[arg] + off
+                got = call(L, name, *args(ptrs))
+                assert got == want, (name, arg, off, got, qg.qg_last_error())
+                if want == qg.QG_EINVAL:
+                    assert "overlap" in qg.qg_last_error() or "workspace" in qg.qg_last_error(), (name, arg)
+
+
 def test_epilogue_argument_checks_without_gpu(L):
     f = FAKE
     w, x, y, b, r = f, f + (1 << 20), f + (2 << 20), f + (3 << 20), f + (4 << 20)
@@ -336,6 +390,27 @@ def test_plan_staged_copy_at_the_lds_boundary(L):
     assert qg.qg_plan_info("q4_0", 5120, 39936, 1, rmsnorm=True)["persistent"]
     with pytest.raises(qg.QGError):
         qg.qg_plan_info("q4_0", 5120, 1024, 2, rmsnorm=True)      # the prologue takes M = 1
+
+
+def test_f16_form_rule_as_documented(L):
+    # gemv_f16_splitk: fewer than 1024 rows with K % 8 == 0, K <= 32768 and
+    # aligned w, x: split-K row form; else K = 512 L (L <= 16): row form; else
+    # the lane-split form; misaligned w or x (or K % 8 != 0) always the last
+    f = 0x10000
+    for N, K in ((48, 5120), (256, 5120), (1, 8), (1023, 32768), (640, 1000)):
+        p = qg.qg_f16_plan_info(N, K)
+        assert p["form"] == "split-K row" and p["workgroups"] == N, (N, K, p)
+        assert p["waves"] == -(-(K // 8) // 256) and p["waves"] <= 16
+    for N, K in ((1024, 5120), (5120, 5120), (17408, 512), (2049, 8192)):
+        p = qg.qg_f16_plan_info(N, K)
+        assert p["form"] == "row" and p["waves"] == 4, (N, K, p)
+    for N, K in ((1023, 32776), (5120, 1000), (1024, 8200), (5120, 8704), (300, 7)):
+        assert qg.qg_f16_plan_info(N, K)["form"] == "lane-split", (N, K)
+    for N, K in ((48, 5120), (5120, 5120)):
+        assert qg.qg_f16_plan_info(N, K, w_addr=f + 8)["form"] == "lane-split"
+        assert qg.qg_f16_plan_info(N, K, x_addr=f + 4)["form"] == "lane-split"
+    with pytest.raises(qg.QGError):
+        qg.qg_f16_plan_info(0, 8)
 
 
 def test_tuning_overrides_are_read_on_reload(L, monkeypatch):
