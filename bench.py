@@ -2,23 +2,32 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-Headline step (the decode weight set of a Qwen3-0.6B-shaped Q8_0 model, M=1):
-  fused QKV 4096x1024 -> O 1024x2048 -> fused gate|up 2x3072x1024 + SiLU ->
-  down 1024x3072 -> LM head 151936x1024.
-Each step reads the next of several device copies of the whole weight set
-(>= 1 GiB in total), so the weights are cold in the 256 MB Infinity Cache and
-the 4 MB L2s when a step reads them. `value` is algorithmic bytes moved per
-second over K timed steps (weights + scales + x + y, each read/written once).
+Headline step: the decode GEMVs of the 27B-class Q4_0 configuration, M = 1,
+one pass over its three matrices in order on one stream:
+  fused gate|up 2x17408x5120 + SiLU -> down 5120x17408 -> LM head 248320x5120
+(866.8 MB of weights, scales, activations and outputs per step). Each step
+reads the next of three device copies of the whole weight set (2.6 GB), so
+the weights are cold in the 256 MB Infinity Cache and the 4 MB L2s when a step
+reads them. `value` is algorithmic bytes moved per second over K timed steps
+(weights + scales + x + y, each read/written once), with the inputs already in
+device memory.
 
 Also measured in the same run:
+  * the roofline entry of the step's dominant kernel, the Q4_0 LM head (83% of
+    the step's bytes): a pass over the same steps binds HIP events to every
+    launch, which receive each kernel's own start and end times;
+  * the Qwen3-0.6B-shaped Q8_0 decode set (fused QKV, O, gate|up + SiLU, down,
+    LM head 151936x1024) as a second step, with its LM head's roofline;
   * every matrix of the five workload configurations, one call at a time, cold
     (each call's weight rotating through >= 1.2 GiB of device copies) and warm,
-    as median us per call, GB/s and fraction of the 8 TB/s HBM3E peak;
-  * the roofline entry of the step's dominant kernel: a second pass over the same
-    steps binds HIP events to every launch, which receive each kernel's own start
-    and end times;
-  * the fp64 CPU oracle on the host cores (one thread and all threads) over one
-    step of the same workload (the cpu_baseline leg; the only use of oracle/).
+    as median us per call, GB/s and fraction of the 8 TB/s HBM3E peak; the
+    epilogue, Q4_K / Q6_K, RMSNorm-prologue and prefill-GEMM rows;
+  * the three forms of the fp16 GEMV on the fp16 configuration's shapes;
+  * reference streams: a plain streaming read at the GEMVs' sizes and an empty
+    kernel (the library's measurement kernels), and torch's own copy and sum;
+  * the fp64 CPU oracle on the host cores, one thread and all of them, over
+    one headline step and every configuration's matrices (the cpu_baseline
+    leg; the only use of oracle/).
 Prints one JSON line on stdout; a readable table goes to stderr.
 """
 from __future__ import annotations
@@ -38,6 +47,30 @@ if ROOT not in sys.path:
 PEAK_GBPS = 8000.0
 METRIC = "Q8_0/Q4_0 GEMV achieved HBM GB/s (% of 8 TB/s, cold); µs per call"
 COLD_BYTES = 1 << 30
+
+# The two decode steps: (kind, label, weights, N, K) per call, in order. kind
+# "gemv" is a plain product, "gateup" the fused gate|up with its SiLU epilogue,
+# "qkv" the load-time concatenation of three projections.
+STEPS = {
+    "q4_0": {
+        "cfg": 2, "qtype": "q4_0",
+        "workload": "27b-class q4_0 decode gemv set, M=1: gate|up 2x17408x5120+silu, down 5120x17408, "
+                    "lm_head 248320x5120",
+        "calls": [("gateup", "gate|up 2x17408x5120 silu", ("gate", "up"), 17408, 5120),
+                  ("gemv", "down 5120x17408", "down", 5120, 17408),
+                  ("gemv", "lm_head 248320x5120", "lm_head", 248320, 5120)],
+    },
+    "q8_0": {
+        "cfg": 1, "qtype": "q8_0",
+        "workload": "qwen3-0.6b-shaped q8_0 decode gemv set, M=1: qkv 4096x1024, o 1024x2048, "
+                    "gate|up 2x3072x1024+silu, down 1024x3072, lm_head 151936x1024",
+        "calls": [("qkv", "qkv 4096x1024", ("q_proj", "k_proj", "v_proj"), 4096, 1024),
+                  ("gemv", "o_proj 1024x2048", "o_proj", 1024, 2048),
+                  ("gateup", "gate|up 2x3072x1024 silu", ("gate", "up"), 3072, 1024),
+                  ("gemv", "down 1024x3072", "down", 1024, 3072),
+                  ("gemv", "lm_head 151936x1024", "lm_head", 151936, 1024)],
+    },
+}
 
 
 def log(*a):
@@ -100,54 +133,147 @@ def make_epilogue(qg, kind, packed, x, bias, res, y, N, K, stream, label):
 
 def make_f16(qg, w, x, y, N, K, stream, label):
     make = lambda wp: qg.bound_call("gemv_f16_splitk", wp, x.data_ptr(), y.data_ptr(), N, K, stream)  # noqa: E731
-    return Call(label, make(w.data_ptr()), 2 * N * K + 4 * K + 4 * N, "gemv_f16", w, make)
+    form = qg.qg_f16_plan_info(N, K)["form"]
+    return Call(label, make(w.data_ptr()), 2 * N * K + 4 * K + 4 * N, f"gemv_f16<{form}>", w, make)
 
 
 # ---------------------------------------------------------------------------
 
-def build_step(qg, torch, wl, stream, copies):
-    """The headline decode set, packed once and cloned into `copies` device copies."""
-    dev = "cuda"
-    K = 1024
-    base = {}
-    base["qkv"] = qg.pack_concat("q8_0", [(wl.weight(n), wl.entry(n)[2]) for n in ("q_proj", "k_proj", "v_proj")],
-                                 K)
-    base["o"] = qg.pack_weights("q8_0", wl.weight("o_proj"), 1024, 2048)
-    base["gateup"] = qg.pack_gateup("q8_0", wl.weight("gate"), wl.weight("up"), 3072, 1024)
-    base["down"] = qg.pack_weights("q8_0", wl.weight("down"), 1024, 3072)
-    base["lm_head"] = qg.pack_weights("q8_0", wl.weight("lm_head"), 151936, 1024)
-    xs = {n: torch.from_numpy(wl.x(src)).to(dev) for n, src in
-          (("qkv", "q_proj"), ("o", "o_proj"), ("gateup", "gate"), ("down", "down"), ("lm_head", "lm_head"))}
-    ys = {"qkv": 4096, "o": 1024, "gateup": 3072, "down": 1024, "lm_head": 151936}
-    ys = {n: torch.empty(v, dtype=torch.float32, device=dev) for n, v in ys.items()}
+def build_step(qg, torch, which, stream, copies):
+    """One decode step's weights, packed once and cloned into `copies` device copies,
+    and the step's calls on each copy."""
+    from block_dequant_gemv_amd.workloads import Workload
+    spec = STEPS[which]
+    kind = spec["qtype"]
+    wl = Workload(spec["cfg"])
+    base, xs, ys = {}, {}, {}
+    for role, label, src, N, K in spec["calls"]:
+        if role == "qkv":
+            base[label] = qg.pack_concat(kind, [(wl.weight(n), wl.entry(n)[2]) for n in src], K)
+            xsrc, nout = src[0], N
+        elif role == "gateup":
+            base[label] = qg.pack_gateup(kind, wl.weight(src[0]), wl.weight(src[1]), N, K)
+            xsrc, nout = src[0], N
+        else:
+            base[label] = qg.pack_weights(kind, wl.weight(src), N, K)
+            xsrc, nout = src, N
+        for n in (src if isinstance(src, tuple) else (src,)):
+            wl.drop(n)
+        xs[label] = torch.from_numpy(wl.x(xsrc)).to("cuda")
+        ys[label] = torch.empty(nout, dtype=torch.float32, device="cuda")
     sets = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(copies - 1)]
     torch.cuda.synchronize()
-    steps = [step_calls(qg, s, xs, ys, stream) for s in sets]
+    steps = [step_calls(qg, which, s, xs, ys, stream) for s in sets]
     return steps, sets, xs, ys
 
 
-def step_calls(qg, s, xs, ys, stream):
-    """The five calls of one decode step on weight set `s`, launched on `stream`."""
-    return [
-        make_qgemv(qg, "q8_0", s["qkv"], xs["qkv"], ys["qkv"], 4096, 1024, stream, "qkv 4096x1024"),
-        make_qgemv(qg, "q8_0", s["o"], xs["o"], ys["o"], 1024, 2048, stream, "o_proj 1024x2048"),
-        make_gateup(qg, "q8_0", s["gateup"], xs["gateup"], ys["gateup"], 3072, 1024, stream,
-                    "gate|up 2x3072x1024 silu"),
-        make_qgemv(qg, "q8_0", s["down"], xs["down"], ys["down"], 1024, 3072, stream, "down 1024x3072"),
-        make_qgemv(qg, "q8_0", s["lm_head"], xs["lm_head"], ys["lm_head"], 151936, 1024, stream,
-                   "lm_head 151936x1024"),
-    ]
+def step_calls(qg, which, s, xs, ys, stream):
+    spec = STEPS[which]
+    kind = spec["qtype"]
+    out = []
+    for role, label, _, N, K in spec["calls"]:
+        if role == "gateup":
+            out.append(make_gateup(qg, kind, s[label], xs[label], ys[label], N, K, stream, label))
+        else:
+            out.append(make_qgemv(qg, kind, s[label], xs[label], ys[label], N, K, stream, label))
+    return out
 
 
-def graph_headline(qg, torch, sets, xs, ys, K, warmup, copies, step_bytes):
-    """Headline steps replayed from HIP graphs: one torch.cuda.CUDAGraph per weight
-    copy capturing that step's five launches on a side stream (the GEMV calls record
-    plain kernel launches and nothing else), then K replays cycling through the
-    copies, between synchronisations."""
+def step_bytes(which):
+    from block_dequant_gemv_amd.workloads import matrix_bytes
+    total = 0
+    for role, _, _, N, K in STEPS[which]["calls"]:
+        kind = STEPS[which]["qtype"]
+        if role == "gateup":
+            total += 2 * matrix_bytes(kind, N, K) + 4 * K + 4 * N
+        else:
+            total += matrix_bytes(kind, N, K) + 4 * K + 4 * N
+    return total
+
+
+def timing_events(torch, n):
+    """n timing events on the current stream, recorded once so that they exist
+    (torch creates the underlying hipEvent_t lazily) and can be bound to launches."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record()
+    return evs
+
+
+def run_steps(qg, torch, which, stream, K, warmup):
+    """K timed steps of a decode set, then a kernel pass over K more steps with every
+    launch bound to an event pair (the kernels' own start and end times)."""
+    nbytes = step_bytes(which)
+    copies = max(3, -(-COLD_BYTES // nbytes))
+    steps, sets, xs, ys = build_step(qg, torch, which, stream, copies)
+    assert sum(c.nbytes for c in steps[0]) == nbytes
+    # The timed region is K plain steps: one event pair brackets them on the
+    # stream the kernels run on and nothing is recorded inside, so the region runs
+    # exactly as a caller's decode loop would. (Binding timing events to a launch
+    # costs the host ~20 us per launch.)
+    for s in range(warmup):
+        for c in steps[s % copies]:
+            c.fn()
+    span = timing_events(torch, 2)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    span[0].record()
+    for s in range(K):
+        for c in steps[s % copies]:
+            c.fn()
+    span[1].record()
+    t_enq = time.perf_counter()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = span[0].elapsed_time(span[1])
+    # kernel pass: the same K steps, every launch bound to an event pair. Every
+    # launch is bound, so each kernel starts after a timed one, the same way in
+    # every step.
+    ncall = len(steps[0])
+    evk = timing_events(torch, 2 * K * ncall)
+    torch.cuda.synchronize()
+    for s in range(K):
+        for i, c in enumerate(steps[s % copies]):
+            e = 2 * (s * ncall + i)
+            qg.qg_time_next_launch(evk[e], evk[e + 1])
+            c.fn()
+    torch.cuda.synchronize()
+    durs = np.array([[evk[2 * (s * ncall + i)].elapsed_time(evk[2 * (s * ncall + i) + 1]) * 1e3
+                      for i in range(ncall)] for s in range(K)])  # us [K][ncall]
+    out = {"steps": steps, "sets": sets, "xs": xs, "ys": ys, "copies": copies, "bytes": nbytes, "wall": wall,
+           "gpu_ms": gpu_ms, "host_us": (t_enq - t0) / K * 1e6, "durs": durs}
+    return out
+
+
+def roofline_of(run, K):
+    """The roofline entry of a decode set's dominant call (its largest matrix)."""
+    steps, durs = run["steps"], run["durs"]
+    dom_i = max(range(len(steps[0])), key=lambda i: steps[0][i].nbytes)
+    dom = steps[0][dom_i]
+    us = durs[:, dom_i]
+    avg_us = float(us.mean())
+    achieved = dom.nbytes / (avg_us * 1e-6) / 1e9
+    return dom_i, {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+        "frac": round(achieved / PEAK_GBPS, 4), "traffic": load_traffic(dom.label),
+        "kernel": dom.kernel, "call": dom.label,
+        "avg_launch_us": round(avg_us, 3), "median_launch_us": round(float(np.median(us)), 3),
+        "p10_p90_us": [round(float(np.percentile(us, 10)), 3), round(float(np.percentile(us, 90)), 3)],
+        "launches": K, "algorithmic_bytes_per_launch": dom.nbytes,
+        "timing": "kernel start/end timestamps of the call's launches in K cold decode steps with every launch "
+                  "bound to HIP events (qg_time_next_launch), on the kernels' stream, right after the timed region",
+    }
+
+
+def graph_replay(torch, qg, which, run, K, warmup, stream_unused=None):
+    """The same K steps replayed from HIP graphs: one torch.cuda.CUDAGraph per weight
+    copy capturing that step's launches on a side stream (the GEMV calls record plain
+    kernel launches and nothing else), then K replays cycling through the copies."""
     side = torch.cuda.Stream()
     graphs = []
-    for st in sets:
-        calls = step_calls(qg, st, xs, ys, side.cuda_stream)
+    copies = run["copies"]
+    for st in run["sets"]:
+        calls = step_calls(qg, which, st, run["xs"], run["ys"], side.cuda_stream)
         with torch.cuda.stream(side):
             for c in calls:
                 c.fn()
@@ -161,26 +287,13 @@ def graph_headline(qg, torch, sets, xs, ys, K, warmup, copies, step_bytes):
         for s in range(warmup):
             graphs[s % copies].replay()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
-        e0.record(side)
         for s in range(K):
             graphs[s % copies].replay()
-        e1.record(side)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     del graphs
-    return {"ms_per_step": round(wall / K * 1e3, 5), "gpu_ms_per_step": round(e0.elapsed_time(e1) / K, 5),
-            "value": round(step_bytes * K / wall / 1e9, 1)}
-
-
-def timing_events(torch, n):
-    """n timing events on the current stream, recorded once so that they exist
-    (torch creates the underlying hipEvent_t lazily) and can be bound to launches."""
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    for e in evs:
-        e.record()
-    return evs
+    return {"ms_per_step": round(wall / K * 1e3, 5), "value": round(run["bytes"] * K / wall / 1e9, 1)}
 
 
 def time_call(qg, torch, fns, reps):
@@ -213,8 +326,9 @@ def cold_copies(torch, weight, budget=COLD_BYTES * 6 // 5):
     return [weight] + [weight.clone() for _ in range(n - 1)]
 
 
-def per_config_calls(qg, torch, stream, step_calls):
-    """All five configurations as lists of calls (the headline step's calls reused for config 1)."""
+def per_config_calls(qg, torch, stream, q4_step, q8_step):
+    """All five configurations as lists of calls (the two decode steps' calls reused
+    for configurations 1 and 2)."""
     from block_dequant_gemv_amd import workloads as W
     from block_dequant_gemv_amd.workloads import Workload
     dev = "cuda"
@@ -235,25 +349,8 @@ def per_config_calls(qg, torch, stream, step_calls):
     p = qg.pack_weights("q8_0", wl.weight("w"), 1024, 1024)
     keep.append(p)
     res[0] = [make_qgemv(qg, "q8_0", p, t(wl.x("w")), yb(1024), 1024, 1024, stream, "c0 q8_0 1024x1024")]
-
-    res[1] = [Call("c1 " + c.label, c.fn, c.nbytes, c.kernel, c.weight, c.make) for c in step_calls]
-
-    wl1 = Workload(1)
-    wl = wl2 = Workload(2)
-    pg = qg.pack_gateup("q4_0", wl.weight("gate"), wl.weight("up"), 17408, 5120)
-    wl.drop("gate")
-    wl.drop("up")
-    pd = qg.pack_weights("q4_0", wl.weight("down"), 5120, 17408)
-    wl.drop("down")
-    pl = qg.pack_weights("q4_0", wl.weight("lm_head"), 248320, 5120)
-    wl.drop("lm_head")
-    keep += [pg, pd, pl]
-    res[2] = [
-        make_gateup(qg, "q4_0", pg, t(wl.x("gate")), yb(17408), 17408, 5120, stream, "c2 q4_0 gate|up 2x17408x5120"),
-        make_qgemv(qg, "q4_0", pd, t(wl.x("down")), yb(5120), 5120, 17408, stream, "c2 q4_0 down 5120x17408"),
-        make_qgemv(qg, "q4_0", pl, t(wl.x("lm_head")), yb(248320), 248320, 5120, stream,
-                   "c2 q4_0 lm_head 248320x5120"),
-    ]
+    res[1] = [Call("c1 " + c.label, c.fn, c.nbytes, c.kernel, c.weight, c.make) for c in q8_step]
+    res[2] = [Call("c2 q4_0 " + c.label, c.fn, c.nbytes, c.kernel, c.weight, c.make) for c in q4_step]
 
     wl = Workload(3)
     res[3] = []
@@ -276,8 +373,12 @@ def per_config_calls(qg, torch, stream, step_calls):
     # the fused QKV with its bias, the O projection added into the residual stream
     # in place, the Q4_0 down projection with a residual, the LM head writing fp16
     erng = np.random.default_rng(5)
-    by = {c.label: c for c in step_calls}
-    qkv, o, lm = by["qkv 4096x1024"], by["o_proj 1024x2048"], by["lm_head 151936x1024"]
+    wl1, wl2 = Workload(1), Workload(2)
+    by8 = {c.label: c for c in q8_step}
+    by4 = {c.label: c for c in q4_step}
+    qkv, o, lm = by8["qkv 4096x1024"], by8["o_proj 1024x2048"], by8["lm_head 151936x1024"]
+    pd, pl, pg = by4["down 5120x17408"].weight, by4["lm_head 248320x5120"].weight, \
+        by4["gate|up 2x17408x5120 silu"].weight
     vec = lambda n: t((0.5 * erng.standard_normal(n)).astype(np.float32))  # noqa: E731
     y_o = t(erng.standard_normal(1024).astype(np.float32))
     y16 = torch.empty(151936, dtype=torch.float16, device=dev)
@@ -338,7 +439,7 @@ def per_config_calls(qg, torch, stream, step_calls):
         norm_cases.append((label, packed, nbytes, fused, norm, plain))
 
     norm_case("n q8_0 qkv 4096x1024", "q8_0", qkv.weight, 4096, 1024, False)
-    norm_case("n q8_0 gate|up 2x3072x1024", "q8_0", by["gate|up 2x3072x1024 silu"].weight, 3072, 1024, True)
+    norm_case("n q8_0 gate|up 2x3072x1024", "q8_0", by8["gate|up 2x3072x1024 silu"].weight, 3072, 1024, True)
     norm_case("n q8_0 lm_head 151936x1024", "q8_0", lm.weight, 151936, 1024, False)
     norm_case("n q4_0 gate|up 2x17408x5120", "q4_0", pg, 17408, 5120, True)
     norm_case("n q4_0 lm_head 248320x5120", "q4_0", pl, 248320, 5120, False)
@@ -439,38 +540,142 @@ def prefill_gemm(qg, torch, cases, table):
     return out
 
 
-def cpu_baseline(wl, threads_all):
-    """The fp64 oracle over one headline step on the host: one thread, then all threads."""
-    import oracle as O
+F16_FORM_ENV = {"lane-split": {"QG_F16_FORM": "0"}, "row": {"QG_F16_FORM": "1"},
+                "split-K row": {"QG_F16_FORM": "2"}}
 
-    jobs = [
-        ("q8_0", np.concatenate([wl.weight(n) for n in ("q_proj", "k_proj", "v_proj")]), wl.x("q_proj"), 4096, 1024),
-        ("q8_0", wl.weight("o_proj"), wl.x("o_proj"), 1024, 2048),
-        ("gateup", None, wl.x("gate"), 3072, 1024),
-        ("q8_0", wl.weight("down"), wl.x("down"), 1024, 3072),
-        ("q8_0", wl.weight("lm_head"), wl.x("lm_head"), 151936, 1024),
-    ]
-    nbytes = 4476928 + 2240512 + 6701056 + 3358720 + 165918208
 
-    def one_step(threads):
-        t0 = time.perf_counter()
-        for kind, w, x, N, K in jobs:
-            if kind == "gateup":
-                O.gateup_silu("q8_0", wl.weight("gate"), wl.weight("up"), x, N, K, threads=threads)
-            else:
-                O.gemv(kind, w, x, N, K, threads=threads)
-        return time.perf_counter() - t0
+def f16_forms(qg, torch, reps):
+    """The three forms of gemv_f16_splitk (forced by QG_F16_FORM) on the fp16
+    configuration's shapes and two between them, cold (weights rotating over
+    >= 1.2 GiB of copies): kernel median (events bound to each launch) and the
+    mean of back-to-back calls. The default form of each shape is marked."""
+    from block_dequant_gemv_amd import workloads as W
+    rng = np.random.default_rng(3)
+    out = {}
+    log("fp16 GEMV forms (cold): kernel median us / back-to-back us; * = the default form")
+    try:
+        for N, K in ((48, 5120), (256, 5120), (640, 5120), (1024, 5120), (5120, 5120)):
+            w = torch.from_numpy(W.f16_matrix(N, K, rng)).cuda()
+            x = torch.from_numpy(W.activation(K, rng)).cuda()
+            y = torch.empty(N, dtype=torch.float32, device="cuda")
+            for k in ("QG_F16_FORM", "QG_F16_CPL"):
+                os.environ.pop(k, None)
+            qg.qg_reload_tuning()
+            default = qg.qg_f16_plan_info(N, K)["form"]
+            copies = cold_copies(torch, w)
+            row = {}
+            for form, env in F16_FORM_ENV.items():
+                os.environ.update(env)
+                qg.qg_reload_tuning()
+                assert qg.qg_f16_plan_info(N, K)["form"] == form
+                fns = [qg.bound_call("gemv_f16_splitk", c.data_ptr(), x.data_ptr(), y.data_ptr(), N, K, 0)
+                       for c in copies]
+                for f in fns[:3]:
+                    f()
+                u, batch = time_call(qg, torch, fns, reps)
+                row[form] = {"us": round(float(np.median(u)), 3), "batch_us": round(batch, 3)}
+            out[f"{N}x{K}"] = {"default": default, **row}
+            log(f"  f16 {N:5d}x{K}: " + "   ".join(
+                f"{'*' if f == default else ' '}{f} {r['us']:6.2f} / {r['batch_us']:6.2f}" for f, r in row.items()))
+            del copies, w
+            torch.cuda.empty_cache()
+    finally:
+        for k in ("QG_F16_FORM", "QG_F16_CPL"):
+            os.environ.pop(k, None)
+        qg.qg_reload_tuning()
+    return out
 
-    t1 = one_step(1)
-    tall = sorted(one_step(threads_all) for _ in range(3))[1]
-    return {
-        "value": nbytes / tall / 1e9, "unit": "GB/s", "cores": threads_all, "kind": "oracle",
-        "sample": "one full headline step (qkv, o_proj, gate|up silu, down, lm_head; 182.7 MB), fp64, "
-                  f"median of 3 with {threads_all} threads",
-        "ms_per_step": tall * 1e3,
-        "single_thread": {"value": nbytes / t1 / 1e9, "unit": "GB/s", "cores": 1, "ms_per_step": t1 * 1e3},
-        "cpu_model": _cpu_model(),
-    }
+
+def reference_streams(qg, torch, reps):
+    """What this device streams: the library's streaming-read kernel over the
+    GEMVs' byte counts, cold (rotating over >= 1.2 GiB of buffers), and its empty
+    kernel (the floor of any dispatch), each as the kernel median (events bound to
+    the launch) and the mean of back-to-back launches; an empty kernel replayed
+    from a HIP graph; and torch's own 2 GiB read-only sum and copy."""
+    out = {"stream_read": {}}
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    log("reference streams (cold): streaming read, kernel median / back-to-back")
+    for label, nbytes in (("4.5 MB (qkv 4096x1024)", 4476928), ("50.2 MB (q4_0 5120x17408)", 50225152),
+                          ("100.4 MB (q4_0 gate|up)", 100360192), ("165.9 MB (q8_0 lm_head)", 165918208),
+                          ("716.2 MB (q4_0 lm_head)", 716175360)):
+        n = -(-nbytes // 1024) * 1024
+        buf = torch.zeros(n // 4, dtype=torch.int32, device="cuda")
+        copies = cold_copies(torch, buf)
+        fns = [qg.bound_call("qg_probe_stream", c.data_ptr(), n, sink.data_ptr(), 0) for c in copies]
+        for f in fns[:3]:
+            f()
+        u, batch = time_call(qg, torch, fns, reps)
+        med = float(np.median(u))
+        out["stream_read"][label] = {"bytes": n, "us": round(med, 3), "p10_us": round(float(np.percentile(u, 10)), 3),
+                                     "GBps": round(n / med / 1e3, 1), "pct": round(100 * n / med / 1e3 / PEAK_GBPS, 1),
+                                     "batch_us": round(batch, 3)}
+        log(f"  stream read {label:28s} {med:8.2f} us ({n / med / 1e3:7.1f} GB/s, "
+            f"{100 * n / med / 1e3 / PEAK_GBPS:4.1f}%)  batch {batch:8.2f} us")
+        del copies, buf, fns
+        torch.cuda.empty_cache()
+    empty = qg.bound_call("qg_probe_empty", 0)
+    empty()
+    u, batch = time_call(qg, torch, [empty], reps)
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side, capture_error_mode="thread_local"):
+        for _ in range(20):
+            qg.bound_call("qg_probe_empty", side.cuda_stream)()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(20):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_us = (time.perf_counter() - t0) / 400 * 1e6
+    out["empty_kernel"] = {"us": round(float(np.median(u)), 3), "batch_us": round(batch, 3),
+                           "graph_node_us": round(graph_us, 3)}
+    log(f"  empty kernel: {float(np.median(u)):.2f} us by kernel timestamps, {batch:.2f} us per launch back to back, "
+        f"{graph_us:.2f} us per node replayed from a HIP graph")
+    # torch's own 2 GiB kernels
+    n = (2 << 30) // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    for _ in range(2):
+        a.sum()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        a.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    out["torch_sum_read_GBps"] = round(4 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    b = torch.empty(n // 2, dtype=torch.float32, device="cuda")
+    src = a[: n // 2]
+    for _ in range(2):
+        b.copy_(src)
+    e0.record()
+    for _ in range(5):
+        b.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    out["torch_copy_GBps"] = round(2 * 4 * (n // 2) * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    log(f"  torch 2 GiB: read-only sum {out['torch_sum_read_GBps']:.0f} GB/s, copy {out['torch_copy_GBps']:.0f} GB/s")
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------
+# The fp64 CPU oracle (the cpu_baseline leg)
+
+def _host_cpus():
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        aff = None
+    quota = None
+    try:
+        q, per = open("/sys/fs/cgroup/cpu.max").read().split()
+        if q != "max":
+            quota = round(int(q) / int(per), 2)
+    except (OSError, ValueError):
+        pass
+    return {"cpu_count": os.cpu_count(), "affinity": aff, "cgroup_quota_cpus": quota, "cpu_model": _cpu_model()}
 
 
 def _cpu_model():
@@ -483,39 +688,89 @@ def _cpu_model():
     return "unknown"
 
 
-def hbm_reference(torch):
-    """Bandwidth of torch's own streaming kernels on 2 GiB buffers (well above the
-    256 MB Infinity Cache): a read-only reduction and a device copy."""
-    n = (2 << 30) // 4
-    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
-    out = {}
-    for name, fn, nbytes in (("sum_read", lambda: a.sum(), 4 * n),):
-        for _ in range(2):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(5):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        out[name] = round(nbytes * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
-    b = torch.empty(n // 2, dtype=torch.float32, device="cuda")
-    src = a[: n // 2]
-    for _ in range(2):
-        b.copy_(src)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
-        b.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    out["copy"] = round(2 * 4 * (n // 2) * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
-    del a, b
-    torch.cuda.empty_cache()
-    return out
+def cpu_baseline(threads_all):
+    """The fp64 oracle as it stands, on the host cores: one headline step (the
+    27B-class Q4_0 set) with one thread and with all of them, and every matrix of
+    the five configurations the same two ways (verify at M = 1 and M = 6)."""
+    import oracle as O
+    from block_dequant_gemv_amd.workloads import Workload
+
+    jobs = []   # (config, label, bytes, rows, fn(threads))
+
+    def gemv_job(cfg, label, wl, name, kind=None):
+        _, k, N, K, _ = wl.entry(name)
+        w, x = wl.weight(name), wl.x(name)
+        jobs.append((cfg, label, wbytes(k, N, K) + 4 * K + 4 * N, N,
+                     lambda th, w=w, x=x, k=k, N=N, K=K: O.gemv(k, w, x, N, K, threads=th)))
+
+    def gateup_job(cfg, label, wl, kind, N_ff, K):
+        g, u, x = wl.weight("gate"), wl.weight("up"), wl.x("gate")
+        jobs.append((cfg, label, 2 * wbytes(kind, N_ff, K) + 4 * K + 4 * N_ff, N_ff,
+                     lambda th: O.gateup_silu(kind, g, u, x, N_ff, K, threads=th)))
+
+    wl = Workload(2)
+    gateup_job(2, "c2 q4_0 gate|up 2x17408x5120 silu", wl, "q4_0", 17408, 5120)
+    gemv_job(2, "c2 q4_0 down 5120x17408", wl, "down")
+    gemv_job(2, "c2 q4_0 lm_head 248320x5120", wl, "lm_head")
+    wl = Workload(0)
+    gemv_job(0, "c0 q8_0 1024x1024", wl, "w")
+    wl = Workload(1)
+    qkv = np.concatenate([wl.weight(n) for n in ("q_proj", "k_proj", "v_proj")])
+    xq = wl.x("q_proj")
+    jobs.append((1, "c1 qkv 4096x1024", wbytes("q8_0", 4096, 1024) + 4 * 1024 + 4 * 4096, 4096,
+                 lambda th: O.gemv("q8_0", qkv, xq, 4096, 1024, threads=th)))
+    gemv_job(1, "c1 o_proj 1024x2048", wl, "o_proj")
+    gateup_job(1, "c1 gate|up 2x3072x1024 silu", wl, "q8_0", 3072, 1024)
+    gemv_job(1, "c1 down 1024x3072", wl, "down")
+    gemv_job(1, "c1 lm_head 151936x1024", wl, "lm_head")
+    wl = Workload(3)
+    for name in ("square", "thin", "small"):
+        _, _, N, K, _ = wl.entry(name)
+        gemv_job(3, f"c3 f16 {N}x{K}", wl, name)
+    wl = Workload(4)
+    for name in ("q4_0_w", "q8_0_w"):
+        _, kind, N, K, _ = wl.entry(name)
+        w, X = wl.weight(name), wl.x(name, M=6)
+        jobs.append((4, f"c4 {kind} {N}x{K} M=1", wbytes(kind, N, K) + 4 * K + 4 * N, N,
+                     lambda th, w=w, X=X, kind=kind, N=N, K=K: O.gemv(kind, w, np.ascontiguousarray(X[0]), N, K,
+                                                                      threads=th)))
+        jobs.append((4, f"c4 {kind} {N}x{K} M=6", wbytes(kind, N, K) + 24 * K + 24 * N, N,
+                     lambda th, w=w, X=X, kind=kind, N=N, K=K: O.verify(kind, w, X, N, K, threads=th)))
+
+    per = {}
+    for cfg, label, nbytes, rows, fn in jobs:
+        t0 = time.perf_counter()
+        fn(1)
+        t1 = time.perf_counter() - t0
+        reps = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn(threads_all)
+            reps.append(time.perf_counter() - t0)
+        ta = sorted(reps)[1]
+        used = threads_all if rows >= threads_all else 1   # the oracle runs rows < threads on one thread
+        per[label] = {"bytes": nbytes, "single_us": round(t1 * 1e6, 1), "all_us": round(ta * 1e6, 1),
+                      "all_threads": used, "single_GBps": round(nbytes / t1 / 1e9, 3),
+                      "all_GBps": round(nbytes / ta / 1e9, 3)}
+        log(f"  cpu oracle {label:36s} 1 thread {t1 * 1e3:9.2f} ms   {used} threads {ta * 1e3:9.2f} ms")
+    head = [lbl for cfg, lbl, *_ in jobs if cfg == 2]
+    hb = sum(per[l]["bytes"] for l in head)
+    t_all = sum(per[l]["all_us"] for l in head) * 1e-6
+    t_one = sum(per[l]["single_us"] for l in head) * 1e-6
+    return {
+        "value": round(hb / t_all / 1e9, 3), "unit": "GB/s", "cores": threads_all, "kind": "oracle",
+        "sample": "one full headline step (27b-class q4_0 gate|up+silu, down, lm_head; 866.8 MB), fp64, median of 3 "
+                  f"with {threads_all} threads; per_config: every matrix of the five configurations (verify at M=1 "
+                  "and M=6), one thread once and all threads median of 3",
+        "ms_per_step": round(t_all * 1e3, 3),
+        "single_thread": {"value": round(hb / t_one / 1e9, 3), "unit": "GB/s", "cores": 1,
+                          "ms_per_step": round(t_one * 1e3, 3)},
+        "host": _host_cpus(),
+        "per_config": per,
+    }
 
 
-def load_traffic(kernel: str):
+def load_traffic(label: str):
     """HBM traffic per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -526,20 +781,23 @@ def load_traffic(kernel: str):
     from block_dequant_gemv_amd.prof import kernel_source_hash
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
-    entry = t.get("calls", {}).get(kernel)
+    entry = t.get("calls", {}).get(label)
     return round(entry["bytes_per_launch"]) if entry else None
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=15)
     ap.add_argument("--reps", type=int, default=100, help="cold reps per call in the per-config table")
-    ap.add_argument("--no-configs", action="store_true", help="skip the per-config table")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config table and the legs after it (fp16 forms, reference streams)")
+    ap.add_argument("--no-q8-step", action="store_true", help="skip the Q8_0 decode step")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the headline steps")
     ap.add_argument("--only", default=None,
                     help="comma-separated label prefixes: time only the per-config rows that start with one of "
-                         "them, and skip the RMSNorm and prefill-GEMM legs (for profiler runs)")
+                         "them, and skip the RMSNorm, prefill-GEMM, fp16-form and reference-stream legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run torch.neg over 256 MiB, a plain copy-like kernel of known traffic "
@@ -555,20 +813,12 @@ def main():
 
     import torch
     import block_dequant_gemv_amd as qg
-    from block_dequant_gemv_amd.workloads import Workload
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream().cuda_stream
     props = torch.cuda.get_device_properties(0)
     log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs")
-
-    wl1 = Workload(1)
-    step_bytes_one = 4476928 + 2240512 + 6701056 + 3358720 + 165918208
-    copies = max(3, -(-COLD_BYTES // step_bytes_one))
-    steps, sets, xs, ys = build_step(qg, torch, wl1, stream, copies)
-    step_bytes = sum(c.nbytes for c in steps[0])
-    assert step_bytes == step_bytes_one
 
     if args.calib_copy:
         # counter calibration: an elementwise kernel that reads exactly 256 MiB and
@@ -581,111 +831,68 @@ def main():
         log("calibration: 5 x torch.neg over 256 MiB (256 MiB read + 256 MiB written each)")
         del src, dst
 
-    # ---- headline: K timed steps ------------------------------------------------
-    # The timed region is K plain steps: one event pair brackets them on the
-    # stream the kernels run on and nothing is recorded inside, so the region runs
-    # exactly as a caller's decode loop would. (Binding timing events to a launch
-    # costs the host ~20 us per launch, which would make the loop host-bound.)
-    for s in range(args.warmup):
-        for c in steps[s % copies]:
-            c.fn()
     K = args.steps
-    lm = len(steps[0]) - 1
-    span = timing_events(torch, 2)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    span[0].record()
-    for s in range(K):
-        for c in steps[s % copies]:
-            c.fn()
-    span[1].record()
-    t_enq = time.perf_counter()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall / K * 1e3
-    value = step_bytes * K / wall / 1e9
-    gpu_span_ms = span[0].elapsed_time(span[1])
-    host_us = (t_enq - t0) / K * 1e6
-    log(f"headline: {K} steps, {ms_per_step:.4f} ms/step wall, GPU span {gpu_span_ms / K:.4f} ms/step, host "
-        f"enqueue {host_us:.1f} us/step, {value:.1f} GB/s ({100 * value / PEAK_GBPS:.1f}% of 8 TB/s), "
-        f"{copies} weight copies")
-
-    # ---- the same K steps replayed from HIP graphs --------------------------------
-    # One graph per weight copy holds the step's five launches (captured on a side
-    # stream); replaying them is what a decode loop that captures its step does.
-    graph = graph_headline(qg, torch, sets, xs, ys, K, args.warmup, copies, step_bytes)
-    log(f"graph replay: {graph['ms_per_step'] * 1e3:.1f} us/step, {graph['value']:.1f} GB/s "
-        f"({100 * graph['value'] / PEAK_GBPS:.1f}% of 8 TB/s)")
-
-    # ---- kernel pass: the same K steps with every launch timed -----------------
-    # Each launch is bound to an event pair that receives the kernel's own start
-    # and end timestamps (qg_time_next_launch; the dispatch times a rocprofv3
-    # kernel trace reports), on the kernels' stream. Every launch is bound, so
-    # each kernel starts after a timed one, the same way in every step. This
-    # pass gives the roofline entry of the LM head (the dominant call) and each
-    # kernel's share of the step.
-    ncall = len(steps[0])
-    evk = timing_events(torch, 2 * K * ncall)
-    torch.cuda.synchronize()
-    for s in range(K):
-        for i, c in enumerate(steps[s % copies]):
-            e = 2 * (s * ncall + i)
-            qg.qg_time_next_launch(evk[e], evk[e + 1])
-            c.fn()
-    torch.cuda.synchronize()
-    durs = np.array([[evk[2 * (s * ncall + i)].elapsed_time(evk[2 * (s * ncall + i) + 1]) * 1e3
-                      for i in range(ncall)] for s in range(K)])  # us [K][ncall]
-    lm_us = durs[:, lm]
-    dom = steps[0][lm]
-    avg_us = float(lm_us.mean())
-    achieved = dom.nbytes / (avg_us * 1e-6) / 1e9
-    traffic = load_traffic(dom.label)
-    roofline = {
-        "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-        "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
-        "kernel": dom.kernel, "call": dom.label,
-        "avg_launch_us": round(avg_us, 3), "launches": K,
-        "algorithmic_bytes_per_launch": dom.nbytes,
-        "timing": "kernel start/end timestamps of the LM head launches of K decode steps with every launch bound "
-                  "to HIP events (qg_time_next_launch), right after the timed region",
-    }
-    for i, c in enumerate(steps[0]):
-        med = float(np.median(durs[:, i]))
+    # ---- headline: the Q4_0 decode set ---------------------------------------------
+    run4 = run_steps(qg, torch, "q4_0", stream, K, args.warmup)
+    value = run4["bytes"] * K / run4["wall"] / 1e9
+    ms_per_step = run4["wall"] / K * 1e3
+    log(f"headline (q4_0 set): {K} steps, {ms_per_step:.4f} ms/step wall, GPU span {run4['gpu_ms'] / K:.4f} "
+        f"ms/step, host enqueue {run4['host_us']:.1f} us/step, {value:.1f} GB/s ({100 * value / PEAK_GBPS:.1f}% "
+        f"of 8 TB/s), {run4['copies']} weight copies")
+    dom_i, roofline = roofline_of(run4, K)
+    for i, c in enumerate(run4["steps"][0]):
+        med = float(np.median(run4["durs"][:, i]))
         log(f"  kernel: {c.label:28s} {med:8.2f} us  {c.nbytes / med / 1e3:8.1f} GB/s  [{c.kernel}]")
-    kern_sum = float(np.median(durs.sum(axis=1)))
-    log(f"  {dom.label}: kernel {float(np.median(lm_us)):.2f} us median, {avg_us:.2f} us mean -> "
-        f"{achieved:.1f} GB/s ({100 * achieved / PEAK_GBPS:.1f}%)  [{dom.kernel}]")
-    log(f"  sum of the step's kernel times {kern_sum:.2f} us; the timed steps took {1e3 * gpu_span_ms / K:.2f} us of "
-        f"GPU time each")
+    log(f"  roofline: {roofline['call']} {roofline['avg_launch_us']:.2f} us mean -> {roofline['achieved']:.1f} GB/s "
+        f"({100 * roofline['frac']:.1f}% of 8 TB/s)")
+    kern_sum = float(np.median(run4["durs"].sum(axis=1)))
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {
-            "workload": "qwen3-0.6b-shaped q8_0 decode gemv set, M=1: qkv 4096x1024, o_proj 1024x2048, "
-                        "gate|up 2x3072x1024 + silu, down 1024x3072, lm_head 151936x1024",
-            "step_bytes": step_bytes, "cold": f"{copies} rotating device copies of the weights "
-                                             f"({copies * step_bytes / 1e9:.2f} GB)",
+            "workload": STEPS["q4_0"]["workload"],
+            "step_bytes": run4["bytes"],
+            "cold": f"{run4['copies']} rotating device copies of the weights "
+                    f"({run4['copies'] * run4['bytes'] / 1e9:.2f} GB)",
             "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
-            "gpu_ms_per_step": round(gpu_span_ms / K, 5),
-            "host_enqueue_us_per_step": round(host_us, 2),
-            "lm_head_kernel_us_median": round(float(np.median(lm_us)), 3),
+            "gpu_ms_per_step": round(run4["gpu_ms"] / K, 5),
+            "host_enqueue_us_per_step": round(run4["host_us"], 2),
             "kernel_us_per_step": round(kern_sum, 3),
+            "kernel_us_median": {c.label: round(float(np.median(run4["durs"][:, i])), 3)
+                                 for i, c in enumerate(run4["steps"][0])},
             "device": props.name,
         },
         "roofline": roofline,
-        "graph_replay": graph,
     }
+    detail = {"q4_0_kernel_us": {c.label: run4["durs"][:, i].tolist() for i, c in enumerate(run4["steps"][0])}}
+    if not args.no_graph:
+        result["graph_replay"] = graph_replay(torch, qg, "q4_0", run4, K, args.warmup)
+        log(f"graph replay (q4_0 set): {result['graph_replay']['ms_per_step'] * 1e3:.1f} us/step, "
+            f"{result['graph_replay']['value']:.1f} GB/s")
+    q4_step = run4["steps"][0]
 
-    detail = {"kernel_us": {c.label: float(np.median(durs[:, i])) for i, c in enumerate(steps[0])},
-              "lm_head_us": lm_us.tolist()}
-
-    # ---- reference streams: what plain torch kernels reach on this device ----------------
-    ref = hbm_reference(torch)
-    result["config"]["hbm_reference_GBps"] = ref
-    log(f"reference streams (torch, 2 GiB): read-only sum {ref['sum_read']:.0f} GB/s, "
-        f"copy {ref['copy']:.0f} GB/s (read+write)")
+    # ---- the Q8_0 decode set ---------------------------------------------------------
+    q8_step = None
+    if not args.no_q8_step or not args.no_configs:
+        run8 = run_steps(qg, torch, "q8_0", stream, K, args.warmup)
+        v8 = run8["bytes"] * K / run8["wall"] / 1e9
+        _, roof8 = roofline_of(run8, K)
+        result["q8_0_step"] = {"workload": STEPS["q8_0"]["workload"], "value": round(v8, 1), "unit": "GB/s",
+                               "ms_per_step": round(run8["wall"] / K * 1e3, 5), "step_bytes": run8["bytes"],
+                               "pct_of_peak": round(100 * v8 / PEAK_GBPS, 2), "roofline": roof8,
+                               "kernel_us_median": {c.label: round(float(np.median(run8["durs"][:, i])), 3)
+                                                    for i, c in enumerate(run8["steps"][0])}}
+        log(f"q8_0 set: {run8['wall'] / K * 1e6:.2f} us/step, {v8:.1f} GB/s ({100 * v8 / PEAK_GBPS:.1f}%); "
+            f"{roof8['call']} {roof8['avg_launch_us']:.2f} us mean ({100 * roof8['frac']:.1f}%)")
+        q8_step = run8["steps"][0]
+        keep8 = run8
+    # the headline's extra weight copies are no longer needed
+    del run4["steps"][1:], run4["sets"][1:]
+    if q8_step is not None:
+        del keep8["steps"][1:], keep8["sets"][1:]
+    torch.cuda.empty_cache()
 
     # ---- per-config cold / warm table ---------------------------------------------
     # Cold: each call's weight rotates through >= 1.2 GiB of device copies (no
@@ -695,7 +902,7 @@ def main():
     # back-to-back calls through the same copies, launch gaps included.
     # Warm: the same copy again and again (served in part by the caches).
     if not args.no_configs:
-        cfg_calls, keep = per_config_calls(qg, torch, stream, steps[0])
+        cfg_calls, keep = per_config_calls(qg, torch, stream, q4_step, q8_step)
         table = {}
         log(f"per-call table: {args.reps} cold calls rotating over >= 1.2 GiB of weight copies, and warm calls")
         norm_cases = cfg_calls.pop("norm")
@@ -736,14 +943,19 @@ def main():
         result["prefill_gemm"] = prefill_gemm(qg, torch, gemm_cases, table)
         del gemm_cases
         del keep
+        torch.cuda.empty_cache()
+        if not only:
+            result["f16_forms"] = f16_forms(qg, torch, args.reps)
+            result["reference_streams"] = reference_streams(qg, torch, args.reps)
 
     # ---- CPU oracle baseline ----------------------------------------------------------
     if not args.no_cpu:
-        threads = max(1, min(16, os.cpu_count() or 1))
-        cb = cpu_baseline(wl1, threads)
+        threads = max(1, min(256, os.cpu_count() or 1))   # the oracle runs at most 256 threads
+        log(f"cpu oracle (fp64): 1 thread and {threads} threads")
+        cb = cpu_baseline(threads)
         result["cpu_baseline"] = cb
         log(f"cpu oracle: {cb['value']:.3f} GB/s on {threads} threads, {cb['single_thread']['value']:.3f} GB/s "
-            f"on 1 thread ({cb['cpu_model']})")
+            f"on 1 thread over one headline step ({cb['host']})")
 
     if args.detail:
         with open(args.detail, "w") as f:

@@ -33,6 +33,7 @@ SYMBOLS = (
     "qgemv_q8_0", "qgemv_q4_0", "qgemv_q4_k", "qgemv_q6_k", "qgemv_epilogue", "gemv_f16_splitk", "qgemv_fused_gateup_silu", "qgemv_verify",
     "qg_rmsnorm", "qgemv_rmsnorm", "qgemv_rmsnorm_gateup_silu", "qg_prefill_workspace_size", "qgemm_prefill",
     "qg_status_str", "qg_last_error", "qg_plan_info", "qg_f16_plan_info", "qg_time_next_launch", "qg_reload_tuning",
+    "qg_probe_stream", "qg_probe_empty",
 )
 
 
@@ -89,6 +90,8 @@ def lib():
             "qg_f16_plan_info": ([i64, i64, vp, vp, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                   ctypes.POINTER(i64)], i32),
             "qg_time_next_launch": ([vp, vp], i32),
+            "qg_probe_stream": ([vp, sz, vp, vp], i32),
+            "qg_probe_empty": ([vp], i32),
             "qg_reload_tuning": ([], i32),
         }
         for name, (args, res) in sig.items():

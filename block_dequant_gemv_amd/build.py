@@ -33,7 +33,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqgemv.so")
-SOURCES = ["qgemv_kernels.hip", "qgemm_kernels.hip", "qgemv_api.hip"]
+SOURCES = ["qgemv_kernels.hip", "qgemm_kernels.hip", "qgemv_api.hip", "probe_kernels.hip"]
 HEADERS = ["layout.h", "dequant.h", "qgemv_kernels.h", "qgemv_device.h", "qgemm_kernels.h"]
 INST_SOURCE = "qgemv_inst.hip"
 # (qtype code of layout.h, activation rows): 1 = Q8_0, 2 = Q4_0, 3 = Q4_K, 4 = Q6_K

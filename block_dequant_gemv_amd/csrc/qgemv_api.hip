@@ -826,6 +826,26 @@ qg_status qg_f16_plan_info(int64_t N, int64_t K, const void *w_f16, const float 
     return ok();
 }
 
+qg_status qg_probe_stream(const void *buf, size_t bytes, uint32_t *sink, void *stream)
+{
+    const char *fn = "qg_probe_stream";
+    if (!buf || !sink) return fail(QG_EINVAL, "%s: null pointer", fn);
+    if (bytes == 0 || bytes % 1024 != 0 || bytes > ((size_t)1 << 40))
+        return fail(QG_EINVAL, "%s: bytes=%zu must be a positive multiple of 1024", fn, bytes);
+    if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(QG_EALIGN, "%s: buf 16-byte, sink 4-byte aligned", fn);
+    if (overlap(sink, 4, buf, bytes)) return fail(QG_EINVAL, "%s: sink overlaps buf", fn);
+    hipError_t e = qgk::launch_probe_stream(buf, bytes, sink, 0x9E3779B9u, as_stream(stream));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+qg_status qg_probe_empty(void *stream)
+{
+    hipError_t e = qgk::launch_probe_empty(as_stream(stream));
+    if (e != hipSuccess) return hip_fail(e, "qg_probe_empty");
+    return ok();
+}
+
 qg_status qg_reload_tuning(void)
 {
     load_tuning();

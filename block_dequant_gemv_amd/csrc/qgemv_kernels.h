@@ -172,6 +172,8 @@ hipError_t launch_qgemv(int qt, int M, int epi, const QPlan &p, const uint8_t *w
 hipError_t launch_rmsnorm(const float *x, const float *gamma, float eps, float *out, int64_t K, hipStream_t s);
 hipError_t launch_f16(const F16Plan &p, const uint16_t *w, const float *x, float *y, int64_t N, int64_t K,
                       hipStream_t s);
+hipError_t launch_probe_stream(const void *buf, uint64_t bytes, uint32_t *sink, uint32_t magic, hipStream_t s);
+hipError_t launch_probe_empty(hipStream_t s);
 hipError_t launch_pack(const qgl::Geometry &g, const uint8_t *canon, const uint8_t *canon_up, uint8_t *packed,
                        int mode, int64_t row0, int64_t nrows, int64_t rows_to_write, bool zero_gaps,
                        hipStream_t s);

@@ -29,7 +29,8 @@ CALIB_BYTES = 256 << 20
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 
-GEMV_SOURCES = ("layout.h", "dequant.h", "qgemv_kernels.h", "qgemv_kernels.hip", "qgemv_api.hip")
+GEMV_SOURCES = ("layout.h", "dequant.h", "qgemv_kernels.h", "qgemv_device.h", "qgemv_inst.hip",
+                "qgemv_kernels.hip", "qgemv_api.hip")
 
 
 def kernel_source_hash() -> str:

@@ -303,6 +303,20 @@ qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int rmsnorm, int 
 qg_status qg_f16_plan_info(int64_t N, int64_t K, const void *w_f16, const float *x, int *form, int *waves,
                            int64_t *workgroups);
 
+/* Measurement kernels (diagnostics; no GEMV uses them).
+ * qg_probe_stream: a plain streaming read of `bytes` bytes of device memory
+ * (a positive multiple of 1024; buf 16-byte aligned) with 16-byte nontemporal
+ * loads, each wavefront reading 8 KiB as 8 one-KiB load instructions issued at
+ * once, as the GEMV kernels stream their weights: what the device streams at
+ * that size, the ceiling a GEMV's weight stream is held against. `sink`
+ * (4 bytes of device memory, not overlapping buf) is written only if the XOR
+ * of the words read equals a fixed value, so in practice nothing is written.
+ * qg_probe_empty: an empty kernel (one wavefront): the floor of any dispatch.
+ * Both are stream-ordered, take qg_time_next_launch timing events, and return
+ * QG_OK, QG_EINVAL, QG_EALIGN or QG_EHIP. */
+qg_status qg_probe_stream(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+qg_status qg_probe_empty(void *stream);
+
 /* Re-read the launch-shape overrides (QG_SPLIT_K, QG_PERSIST, QG_X_GLOBAL,
  * QG_TILES_PER_GROUP, QG_WAVES_PER_WG, QG_PREFETCH, QG_F16_ROWS, QG_F16_WAVES,
  * QG_STRIDE_GROUPS, QG_GEMM_MT, QG_GEMM_WAVES, QG_GEMM_ROWGROUPS, QG_GEMM_KSPLIT,

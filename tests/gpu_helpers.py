@@ -8,7 +8,7 @@ import numpy as np
 
 import oracle as O
 
-THREADS = max(1, min(16, os.cpu_count() or 1))
+THREADS = max(1, min(256, len(os.sched_getaffinity(0))))   # the CPUs this process may run on
 
 
 def announce(msg: str):

@@ -198,6 +198,19 @@ def test_documented_alignment_is_exactly_what_is_checked(L):
                     assert "overlap" in qg.qg_last_error() or "workspace" in qg.qg_last_error(), (name, arg)
 
 
+def test_probe_argument_checks_without_gpu(L):
+    f = FAKE
+    pr = lambda *a: call(L, "qg_probe_stream", *a)  # noqa: E731
+    assert pr(None, 1024, f, None) == qg.QG_EINVAL
+    assert pr(f, 1024, None, None) == qg.QG_EINVAL
+    assert pr(f, 0, f + (1 << 20), None) == qg.QG_EINVAL
+    assert pr(f, 1000, f + (1 << 20), None) == qg.QG_EINVAL          # not a multiple of 1 KiB
+    assert pr(f + 8, 1024, f + (1 << 20), None) == qg.QG_EALIGN
+    assert pr(f, 1024, f + (1 << 20) + 2, None) == qg.QG_EALIGN
+    assert pr(f, 4096, f + 1024, None) == qg.QG_EINVAL               # sink inside buf
+    assert "overlap" in qg.qg_last_error()
+
+
 def test_epilogue_argument_checks_without_gpu(L):
     f = FAKE
     w, x, y, b, r = f, f + (1 << 20), f + (2 << 20), f + (3 << 20), f + (4 << 20)
