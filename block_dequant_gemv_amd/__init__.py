@@ -32,6 +32,7 @@ SYMBOLS = (
     "qg_pack_host", "qg_unpack_host", "qg_pack_gateup_host",
     "qgemv_q8_0", "qgemv_q4_0", "qgemv_q4_k", "qgemv_q6_k", "qgemv_epilogue", "gemv_f16_splitk", "qgemv_fused_gateup_silu", "qgemv_verify",
     "qg_rmsnorm", "qgemv_rmsnorm", "qgemv_rmsnorm_gateup_silu", "qg_prefill_workspace_size", "qgemm_prefill",
+    "qgemm_prefill_noalloc",
     "qg_status_str", "qg_last_error", "qg_plan_info", "qg_f16_plan_info", "qg_time_next_launch", "qg_reload_tuning",
     "qg_probe_stream", "qg_probe_empty",
 )
@@ -78,6 +79,7 @@ def lib():
             "qg_rmsnorm": ([vp, vp, ctypes.c_float, vp, i64, vp], i32),
             "qg_prefill_workspace_size": ([i32, i64, i64, i64], sz),
             "qgemm_prefill": ([i32, vp, vp, vp, i64, i64, i64, vp, sz, vp], i32),
+            "qgemm_prefill_noalloc": ([i32, vp, vp, vp, i64, i64, i64, vp], i32),
             "qgemv_rmsnorm": ([i32, vp, vp, vp, ctypes.c_float, vp, i64, i64, vp], i32),
             "qgemv_rmsnorm_gateup_silu": ([i32, vp, vp, vp, ctypes.c_float, vp, i64, i64, vp], i32),
             "gemv_f16_splitk": ([vp, vp, vp, i64, i64, vp], i32),
@@ -255,6 +257,18 @@ def qgemm_prefill(qtype, w_packed, X, Y, N: int, K: int, M: int, workspace=None,
                                                 _dev(Y, "Y", _f32()), N, K, M, _dev(workspace, "workspace"),
                                                 workspace.numel() * workspace.element_size(), _stream(stream)))
     return workspace
+
+
+QG_PREFILL_NOALLOC_MAX_BYTES = 64 << 20
+
+
+def qgemm_prefill_noalloc(qtype, w_packed, X, Y, N: int, K: int, M: int, stream=None):
+    """qgemm_prefill on the library's own per-GPU scratch array (no workspace,
+    nothing allocated); shapes whose workspace exceeds QG_PREFILL_NOALLOC_MAX_BYTES
+    are refused."""
+    _check("qgemm_prefill_noalloc",
+           lib().qgemm_prefill_noalloc(_qtype(qtype), _dev(w_packed, "w_packed"), _dev(X, "X", _f32()),
+                                       _dev(Y, "Y", _f32()), N, K, M, _stream(stream)))
 
 
 def gemv_f16_splitk(w_f16, x, y, N: int, K: int, stream=None):

@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdarg>
+#include <mutex>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -476,6 +477,101 @@ GemmPlan plan_gemm(int qt, int64_t N, int64_t K, int64_t M)
 // QG_F16_FORM = 0 / 1 / 2 forces the lane-split / row / split-K row form (where
 // K and the alignment allow it), QG_F16_CPL = 1, 2, 4 the chunks per lane of
 // the split-K row form, QG_F16_WAVES and QG_F16_ROWS the other forms' shapes.
+// Checks shared by the two prefill entry points (no HIP call): sizes, types,
+// null pointers, alignment.
+qg_status check_prefill(int qtype, const void *w_packed, const float *X, const float *Y, int64_t N, int64_t K,
+                        int64_t M, const char *fn)
+{
+    qg_status st = check_qshape(qtype, N, K, fn);
+    if (st) return st;
+    if (super_block_qtype(qtype)) return fail(QG_EUNSUPPORTED, "%s: Q4_K / Q6_K weights have the GEMV only", fn);
+    if (M <= 0 || M > kGemmMaxM) return fail(QG_EINVAL, "%s: M=%lld outside 1..%lld", fn, (long long)M,
+                                             (long long)kGemmMaxM);
+    if (!w_packed || !X || !Y) return fail(QG_EINVAL, "%s: null pointer", fn);
+    if (!aligned(w_packed, 16)) return fail(QG_EALIGN, "%s: packed weights must be 16-byte aligned", fn);
+    if (!aligned(X, 4) || !aligned(Y, 4)) return fail(QG_EALIGN, "%s: X and Y must be 4-byte aligned", fn);
+    return QG_OK;
+}
+
+// Y against X and the weights (after every alignment check).
+qg_status check_prefill_overlap(int qtype, const void *w_packed, const float *X, const float *Y, int64_t N,
+                                int64_t K, int64_t M, const char *fn)
+{
+    const Geometry g = qgl::geometry(qtype, N, K);
+    const size_t xb = (size_t)M * (size_t)K * sizeof(float), yb = (size_t)M * (size_t)N * sizeof(float);
+    if (overlap(Y, yb, X, xb) || overlap(Y, yb, w_packed, (size_t)g.total))
+        return fail(QG_EINVAL, "%s: Y overlaps X, the weights or the workspace", fn);
+    return QG_OK;
+}
+
+// Enqueue the split, the GEMM passes and (with a K split) the sum of the ranges
+// on `workspace` (plan_gemm(...).bytes bytes, 256-byte aligned).
+qg_status run_prefill(int qtype, const void *w_packed, const float *X, float *Y, int64_t N, int64_t K, int64_t M,
+                      void *workspace, void *stream, const char *fn)
+{
+    const GemmPlan p = plan_gemm(qtype, N, K, M);
+    const Geometry g = qgl::geometry(qtype, N, K);
+    const int64_t M_pad = gemm_m_pad(M);
+    float *unscale = (float *)workspace;
+    _Float16 *xs = (_Float16 *)((uint8_t *)workspace + p.off_xs);
+    hipStream_t s = as_stream(stream);
+    // the split pass is not timed: a bound event pair goes to the first GEMM pass
+    hipError_t e = qgk::launch_split_x(qtype, X, xs, unscale, M, M_pad, K, s);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    const int64_t n_mt = M_pad / qgk::kGemmTileM;
+    qgk::GemmArgs a;
+    a.geo = g;
+    a.N = N;
+    a.M = M;
+    a.y_stride = N;
+    a.ksplit = p.ksplit;
+    a.part = p.ksplit > 1 ? (float *)((uint8_t *)workspace + p.off_part) : nullptr;
+    for (int64_t mt0 = 0; mt0 < n_mt; mt0 += p.MT) {
+        a.mt0 = mt0;
+        const int mt = (int)std::min<int64_t>(p.MT, n_mt - mt0);
+        e = qgk::launch_qgemm(qtype, mt, p.RG, p.G, (const uint8_t *)w_packed, xs, unscale, Y, a, s);
+        if (e != hipSuccess) return hip_fail(e, fn);
+    }
+    if (p.ksplit > 1) {
+        e = qgk::launch_ksum(a.part, Y, p.ksplit, M, N, s);
+        if (e != hipSuccess) return hip_fail(e, fn);
+    }
+    return ok();
+}
+
+// Scratch of qgemm_prefill_noalloc: a file-scope device array, one copy per GPU
+// the library runs on, held until the process ends. In host code its name is a
+// host-side stand-in, not a device address; the device address is taken once
+// per device (with that device current) by hipGetSymbolAddress and used in its
+// place wherever host code needs the array's memory.
+constexpr size_t kNoAllocScratchBytes = QG_PREFILL_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+qg_status scratch_address(void **out, const char *fn)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    if (dev < 0 || dev >= kMaxDevices) return fail(QG_EUNSUPPORTED, "%s: device %d", fn, dev);
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return hip_fail(e, fn);
+            if (p == nullptr) return fail(QG_EHIP, "%s: no device address for the scratch array", fn);
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return QG_OK;
+}
+
 qgk::F16Plan plan_f16(int64_t N, int64_t K, const void *w_f16, const float *x)
 {
     qgk::F16Plan p;
@@ -684,53 +780,42 @@ qg_status qgemm_prefill(int qtype, const void *w_packed, const float *X, float *
                         void *workspace, size_t workspace_bytes, void *stream)
 {
     const char *fn = "qgemm_prefill";
-    qg_status st = check_qshape(qtype, N, K, fn);
+    qg_status st = check_prefill(qtype, w_packed, X, Y, N, K, M, fn);
     if (st) return st;
-    if (super_block_qtype(qtype)) return fail(QG_EUNSUPPORTED, "%s: Q4_K / Q6_K weights have the GEMV only", fn);
-    if (M <= 0 || M > kGemmMaxM) return fail(QG_EINVAL, "%s: M=%lld outside 1..%lld", fn, (long long)M,
-                                             (long long)kGemmMaxM);
-    if (!w_packed || !X || !Y || !workspace) return fail(QG_EINVAL, "%s: null pointer", fn);
-    if (!aligned(w_packed, 16)) return fail(QG_EALIGN, "%s: packed weights must be 16-byte aligned", fn);
-    if (!aligned(X, 4) || !aligned(Y, 4)) return fail(QG_EALIGN, "%s: X and Y must be 4-byte aligned", fn);
+    if (!workspace) return fail(QG_EINVAL, "%s: null pointer", fn);
     if (!aligned(workspace, 256)) return fail(QG_EALIGN, "%s: workspace must be 256-byte aligned", fn);
-    const GemmPlan p = plan_gemm(qtype, N, K, M);
-    const size_t need = p.bytes;
+    const size_t need = plan_gemm(qtype, N, K, M).bytes;
     if (workspace_bytes < need)
         return fail(QG_EINVAL, "%s: workspace of %zu bytes, %zu needed (qg_prefill_workspace_size)", fn,
                     workspace_bytes, need);
+    st = check_prefill_overlap(qtype, w_packed, X, Y, N, K, M, fn);
+    if (st) return st;
     const Geometry g = qgl::geometry(qtype, N, K);
     const size_t xb = (size_t)M * (size_t)K * sizeof(float), yb = (size_t)M * (size_t)N * sizeof(float);
-    if (overlap(Y, yb, X, xb) || overlap(Y, yb, w_packed, (size_t)g.total) || overlap(Y, yb, workspace, need))
-        return fail(QG_EINVAL, "%s: Y overlaps X, the weights or the workspace", fn);
+    if (overlap(Y, yb, workspace, need)) return fail(QG_EINVAL, "%s: Y overlaps X, the weights or the workspace", fn);
     if (overlap(workspace, need, X, xb) || overlap(workspace, need, w_packed, (size_t)g.total))
         return fail(QG_EINVAL, "%s: the workspace overlaps X or the weights", fn);
+    return run_prefill(qtype, w_packed, X, Y, N, K, M, workspace, stream, fn);
+}
 
-    const int64_t M_pad = gemm_m_pad(M);
-    float *unscale = (float *)workspace;
-    _Float16 *xs = (_Float16 *)((uint8_t *)workspace + p.off_xs);
-    hipStream_t s = as_stream(stream);
-    // the split pass is not timed: a bound event pair goes to the first GEMM pass
-    hipError_t e = qgk::launch_split_x(qtype, X, xs, unscale, M, M_pad, K, s);
-    if (e != hipSuccess) return hip_fail(e, fn);
-    const int64_t n_mt = M_pad / qgk::kGemmTileM;
-    qgk::GemmArgs a;
-    a.geo = g;
-    a.N = N;
-    a.M = M;
-    a.y_stride = N;
-    a.ksplit = p.ksplit;
-    a.part = p.ksplit > 1 ? (float *)((uint8_t *)workspace + p.off_part) : nullptr;
-    for (int64_t mt0 = 0; mt0 < n_mt; mt0 += p.MT) {
-        a.mt0 = mt0;
-        const int mt = (int)std::min<int64_t>(p.MT, n_mt - mt0);
-        e = qgk::launch_qgemm(qtype, mt, p.RG, p.G, (const uint8_t *)w_packed, xs, unscale, Y, a, s);
-        if (e != hipSuccess) return hip_fail(e, fn);
-    }
-    if (p.ksplit > 1) {
-        e = qgk::launch_ksum(a.part, Y, p.ksplit, M, N, s);
-        if (e != hipSuccess) return hip_fail(e, fn);
-    }
-    return ok();
+qg_status qgemm_prefill_noalloc(int qtype, const void *w_packed, const float *X, float *Y, int64_t N, int64_t K,
+                                int64_t M, void *stream)
+{
+    const char *fn = "qgemm_prefill_noalloc";
+    qg_status st = check_prefill(qtype, w_packed, X, Y, N, K, M, fn);
+    if (st) return st;
+    st = check_prefill_overlap(qtype, w_packed, X, Y, N, K, M, fn);
+    if (st) return st;
+    const size_t need = plan_gemm(qtype, N, K, M).bytes;
+    if (need > kNoAllocScratchBytes)
+        return fail(QG_EUNSUPPORTED,
+                    "%s: this shape needs %zu bytes of scratch, above the %zu bytes the library holds per GPU "
+                    "(call qgemm_prefill with a workspace of qg_prefill_workspace_size bytes)",
+                    fn, need, kNoAllocScratchBytes);
+    void *ws = nullptr;
+    st = scratch_address(&ws, fn);
+    if (st) return st;
+    return run_prefill(qtype, w_packed, X, Y, N, K, M, ws, stream, fn);
 }
 
 qg_status qgemv_q4_k(const void *w_packed, const float *x, float *y, int64_t N, int64_t K, void *stream)

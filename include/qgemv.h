@@ -269,6 +269,24 @@ size_t qg_prefill_workspace_size(int qtype, int64_t N, int64_t K, int64_t M);
 qg_status qgemm_prefill(int qtype, const void *w_packed, const float *X, float *Y, int64_t N, int64_t K, int64_t M,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* The same GEMM for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no workspace argument. Its scratch (the split activations, row factors and
+ * K-range partials that qgemm_prefill keeps in the caller's workspace) is one
+ * file-scope device array of QG_PREFILL_NOALLOC_MAX_BYTES (64 MiB) per GPU,
+ * held by the library until the process ends; the first call on each device
+ * takes the array's device address (hipGetSymbolAddress). The call allocates
+ * and frees nothing. A shape whose workspace (qg_prefill_workspace_size) is
+ * larger returns QG_EUNSUPPORTED before any HIP call. Every call on a GPU
+ * shares that GPU's array, which keeps the last call's contents (each call
+ * writes every scratch byte it reads first): calls that overlap in time on
+ * one GPU race, so issue them on one stream or otherwise serialise them.
+ * Arguments and results as for qgemm_prefill: Y is bit for bit what
+ * qgemm_prefill returns with a workspace. */
+#define QG_PREFILL_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+qg_status qgemm_prefill_noalloc(int qtype, const void *w_packed, const float *X, float *Y, int64_t N, int64_t K,
+                                int64_t M, void *stream);
+
 /* ---- diagnostics --------------------------------------------------------- */
 
 const char *qg_status_str(int status);

@@ -295,6 +295,27 @@ def test_gemm_argument_checks_without_gpu(L):
     assert gm(1, w, x, y, 64, 1000, 20, ws, need, None) == qg.QG_EINVAL           # K % 32
 
 
+def test_prefill_noalloc_checks_without_gpu(L):
+    # qgemm_prefill_noalloc: the prefill GEMM's checks, and shapes whose workspace
+    # exceeds the library's per-GPU scratch are refused before any HIP call
+    f = FAKE
+    w, x, y = f, f + (1 << 24), f + (2 << 24)
+    na = lambda *a: call(L, "qgemm_prefill_noalloc", *a)  # noqa: E731
+    # (qtype, w, X, Y, N, K, M, stream)
+    assert na(1, w, x, y, 64, 1024, 0, None) == qg.QG_EINVAL                     # M = 0
+    assert na(1, None, x, y, 64, 1024, 20, None) == qg.QG_EINVAL                 # null weights
+    assert na(1, w + 8, x, y, 64, 1024, 20, None) == qg.QG_EALIGN                # weight alignment
+    assert na(1, w, x + 2, y, 64, 1024, 20, None) == qg.QG_EALIGN                # X alignment
+    assert na(2, w, x, x + 64, 64, 1024, 20, None) == qg.QG_EINVAL               # Y overlaps X
+    assert na(3, w, x, y, 64, 1024, 20, None) == qg.QG_EUNSUPPORTED              # Q4_K: GEMV only
+    assert na(1, w, x, y, 64, 1000, 20, None) == qg.QG_EINVAL                    # K % 32
+    # Q4_0 5120 x 17408 at M = 256 needs 17 K ranges of partials: about 107 MB
+    need = qg.qg_prefill_workspace_size("q4_0", 5120, 17408, 256)
+    assert need > qg.QG_PREFILL_NOALLOC_MAX_BYTES
+    assert na(2, w, x, f + (1 << 34), 5120, 17408, 256, None) == qg.QG_EUNSUPPORTED
+    assert "qg_prefill_workspace_size" in qg.qg_last_error()
+
+
 def test_time_next_launch_arguments(L):
     # host-only: binding or clearing events makes no HIP call
     f = FAKE
