@@ -14,8 +14,8 @@ device memory.
 
 Also measured in the same run:
   * the roofline entry of the step's dominant kernel, the Q4_0 LM head (83% of
-    the step's bytes): a pass over the same steps binds HIP events to every
-    launch, which receive each kernel's own start and end times;
+    the step's bytes): every launch of the timed steps is bound to HIP events,
+    which receive the kernel's own start and end times;
   * the Qwen3-0.6B-shaped Q8_0 decode set (fused QKV, O, gate|up + SiLU, down,
     LM head 151936x1024) as a second step, with its LM head's roofline;
   * every matrix of the five workload configurations, one call at a time, cold
@@ -200,48 +200,54 @@ def timing_events(torch, n):
     return evs
 
 
-def run_steps(qg, torch, which, stream, K, warmup):
-    """K timed steps of a decode set, then a kernel pass over K more steps with every
-    launch bound to an event pair (the kernels' own start and end times)."""
+def run_steps(qg, torch, which, stream, K, warmup, bind_timed):
+    """K timed steps of a decode set, between synchronisations, with the kernels'
+    own start and end times for every launch (events bound to the launch, which
+    receive the dispatch's timestamps on the kernels' stream).
+    bind_timed: the events are bound inside the timed region itself (binding costs
+    the host ~20 us per launch, which a step of ~170 us of GPU work absorbs);
+    otherwise the timed region runs plain launches and a second pass over the same
+    K steps binds them (for steps too short to absorb the host cost)."""
     nbytes = step_bytes(which)
     copies = max(3, -(-COLD_BYTES // nbytes))
     steps, sets, xs, ys = build_step(qg, torch, which, stream, copies)
     assert sum(c.nbytes for c in steps[0]) == nbytes
-    # The timed region is K plain steps: one event pair brackets them on the
-    # stream the kernels run on and nothing is recorded inside, so the region runs
-    # exactly as a caller's decode loop would. (Binding timing events to a launch
-    # costs the host ~20 us per launch.)
+    ncall = len(steps[0])
     for s in range(warmup):
         for c in steps[s % copies]:
             c.fn()
+    evk = timing_events(torch, 2 * K * ncall)
     span = timing_events(torch, 2)
+
+    def bound_pass():
+        for s in range(K):
+            for i, c in enumerate(steps[s % copies]):
+                e = 2 * (s * ncall + i)
+                qg.qg_time_next_launch(evk[e], evk[e + 1])
+                c.fn()
+
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     span[0].record()
-    for s in range(K):
-        for c in steps[s % copies]:
-            c.fn()
+    if bind_timed:
+        bound_pass()
+    else:
+        for s in range(K):
+            for c in steps[s % copies]:
+                c.fn()
     span[1].record()
     t_enq = time.perf_counter()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = span[0].elapsed_time(span[1])
-    # kernel pass: the same K steps, every launch bound to an event pair. Every
-    # launch is bound, so each kernel starts after a timed one, the same way in
-    # every step.
-    ncall = len(steps[0])
-    evk = timing_events(torch, 2 * K * ncall)
-    torch.cuda.synchronize()
-    for s in range(K):
-        for i, c in enumerate(steps[s % copies]):
-            e = 2 * (s * ncall + i)
-            qg.qg_time_next_launch(evk[e], evk[e + 1])
-            c.fn()
-    torch.cuda.synchronize()
+    if not bind_timed:
+        torch.cuda.synchronize()
+        bound_pass()
+        torch.cuda.synchronize()
     durs = np.array([[evk[2 * (s * ncall + i)].elapsed_time(evk[2 * (s * ncall + i) + 1]) * 1e3
                       for i in range(ncall)] for s in range(K)])  # us [K][ncall]
     out = {"steps": steps, "sets": sets, "xs": xs, "ys": ys, "copies": copies, "bytes": nbytes, "wall": wall,
-           "gpu_ms": gpu_ms, "host_us": (t_enq - t0) / K * 1e6, "durs": durs}
+           "gpu_ms": gpu_ms, "host_us": (t_enq - t0) / K * 1e6, "durs": durs, "bound_in_timed": bind_timed}
     return out
 
 
@@ -260,8 +266,11 @@ def roofline_of(run, K):
         "avg_launch_us": round(avg_us, 3), "median_launch_us": round(float(np.median(us)), 3),
         "p10_p90_us": [round(float(np.percentile(us, 10)), 3), round(float(np.percentile(us, 90)), 3)],
         "launches": K, "algorithmic_bytes_per_launch": dom.nbytes,
-        "timing": "kernel start/end timestamps of the call's launches in K cold decode steps with every launch "
-                  "bound to HIP events (qg_time_next_launch), on the kernels' stream, right after the timed region",
+        "timing": ("kernel start/end timestamps of the call's launches in the K timed cold decode steps, every "
+                   "launch bound to HIP events (qg_time_next_launch) on the kernels' stream"
+                   if run["bound_in_timed"] else
+                   "kernel start/end timestamps of the call's launches in K cold decode steps with every launch "
+                   "bound to HIP events (qg_time_next_launch), on the kernels' stream, right after the timed region"),
     }
 
 
@@ -833,7 +842,7 @@ def main():
 
     K = args.steps
     # ---- headline: the Q4_0 decode set ---------------------------------------------
-    run4 = run_steps(qg, torch, "q4_0", stream, K, args.warmup)
+    run4 = run_steps(qg, torch, "q4_0", stream, K, args.warmup, bind_timed=True)
     value = run4["bytes"] * K / run4["wall"] / 1e9
     ms_per_step = run4["wall"] / K * 1e3
     log(f"headline (q4_0 set): {K} steps, {ms_per_step:.4f} ms/step wall, GPU span {run4['gpu_ms'] / K:.4f} "
@@ -876,7 +885,7 @@ def main():
     # ---- the Q8_0 decode set ---------------------------------------------------------
     q8_step = None
     if not args.no_q8_step or not args.no_configs:
-        run8 = run_steps(qg, torch, "q8_0", stream, K, args.warmup)
+        run8 = run_steps(qg, torch, "q8_0", stream, K, args.warmup, bind_timed=False)
         v8 = run8["bytes"] * K / run8["wall"] / 1e9
         _, roof8 = roofline_of(run8, K)
         result["q8_0_step"] = {"workload": STEPS["q8_0"]["workload"], "value": round(v8, 1), "unit": "GB/s",

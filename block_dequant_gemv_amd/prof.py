@@ -1,12 +1,19 @@
 """Summaries of rocprofv3 CSV output for this library's kernels.
 
-    python -m block_dequant_gemv_amd.prof trace  <dir>              # --kernel-trace --stats -f csv
+    python -m block_dequant_gemv_amd.prof trace  <dir> [--skip N]   # --kernel-trace --stats -f csv
+    python -m block_dequant_gemv_amd.prof counters <dir>
     python -m block_dequant_gemv_amd.prof traffic <fetch_dir> <write_dir> [--json out.json]
                                               [--call LABEL=KERNEL|WORKGROUPSxWG ...]
 
 `trace` groups the dispatches by kernel name and grid size (two calls of one
 kernel template with different shapes, e.g. the fused QKV and the LM head, show
 up as separate rows) and prints count, mean / median / min duration.
+
+`counters` reads one counter run (--pmc with any counters, plus --kernel-trace)
+and prints, per launch shape, the mean of every counter and of the dispatch
+time; with GRBM_GUI_ACTIVE it derives the shader clock (busy cycles per
+microsecond of dispatch), with SQ_WAVES and SQ_INSTS_VALU the VALU instructions
+per wavefront.
 
 `traffic` reads two counter runs (--pmc FETCH_SIZE, then --pmc WRITE_SIZE; the
 counters are KiB per dispatch) and prints the mean per launch shape. The bytes
@@ -76,16 +83,21 @@ def _short(name: str) -> str:
     return name[:cut] if cut > 0 else name
 
 
-def trace_summary(directory: str) -> str:
+def trace_summary(directory: str, skip: int = 0) -> str:
+    """Per launch shape, in dispatch order: count, mean / median / min duration;
+    with skip > 0 the first `skip` dispatches of every shape (warm-up) are left out."""
     rows = _rows(os.path.join(directory, "**", "*kernel_trace.csv"))
     groups = defaultdict(list)
     for r in rows:
         name = _short(_get(r, "Kernel_Name", default="?"))
         t0 = int(_get(r, "Start_Timestamp", default="0"))
         t1 = int(_get(r, "End_Timestamp", default="0"))
-        groups[(name, _grid(r) // _wg(r), _wg(r))].append((t1 - t0) / 1e3)
-    lines = [f"{'kernel':58s} {'workgroups':>10s} {'wg':>4s} {'n':>5s} {'mean_us':>9s} {'median_us':>9s} "
-             f"{'min_us':>8s} {'total_us':>10s}"]
+        groups[(name, _grid(r) // _wg(r), _wg(r))].append((t0, (t1 - t0) / 1e3))
+    groups = {k: [d for _, d in sorted(v)][skip:] for k, v in groups.items()}
+    groups = {k: v for k, v in groups.items() if v}
+    lines = ([f"the first {skip} dispatches of every launch shape left out"] if skip else []) + \
+        [f"{'kernel':58s} {'workgroups':>10s} {'wg':>4s} {'n':>5s} {'mean_us':>9s} {'median_us':>9s} "
+         f"{'min_us':>8s} {'total_us':>10s}"]
     for (name, wgs, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"{name[:58]:58s} {wgs:10d} {wg:4d} {len(d):5d} {st.mean(d):9.2f} {st.median(d):9.2f} "
                      f"{min(d):8.2f} {sum(d):10.1f}")
@@ -109,6 +121,45 @@ def _counter_means(directory: str, counter: str):
         name = _short(_get(r, "Kernel_Name", default="?"))
         groups[(name, _grid(r) // _wg(r), _wg(r))].append(float(_get(r, "Counter_Value", default="0")) * 1024.0)
     return {k: st.mean(v) for k, v in groups.items()}, {k: len(v) for k, v in groups.items()}
+
+
+def counter_summary(directory: str) -> str:
+    rows = _rows(os.path.join(directory, "**", "*counter_collection.csv"))
+    vals = defaultdict(lambda: defaultdict(list))
+    durs = defaultdict(dict)
+    names = set()
+    for r in rows:
+        key = (_short(_get(r, "Kernel_Name", default="?")), _grid(r) // _wg(r), _wg(r))
+        c = _get(r, "Counter_Name", default="")
+        names.add(c)
+        vals[key][c].append(float(_get(r, "Counter_Value", default="0")))
+        t0, t1 = _get(r, "Start_Timestamp"), _get(r, "End_Timestamp")
+        did = _get(r, "Dispatch_Id", "Correlation_Id", default=None)
+        if t0 is not None and t1 is not None and did is not None:
+            durs[key][did] = (int(t1) - int(t0)) / 1e3
+    cols = sorted(names)
+    lines = ["per launch shape: dispatches, mean dispatch time (us), mean of each counter per dispatch"
+             + (", clock_MHz = GRBM_GUI_ACTIVE / dispatch time" if "GRBM_GUI_ACTIVE" in names else "")
+             + (", valu_per_wave = SQ_INSTS_VALU / SQ_WAVES" if {"SQ_WAVES", "SQ_INSTS_VALU"} <= names else "")]
+    head = f"{'kernel':58s} {'wgs':>7s} {'wg':>5s} {'n':>4s} {'us':>9s} " + " ".join(f"{c:>20s}" for c in cols)
+    extra = []
+    if "GRBM_GUI_ACTIVE" in names:
+        extra.append("clock_MHz")
+    if {"SQ_WAVES", "SQ_INSTS_VALU"} <= names:
+        extra.append("valu_per_wave")
+    lines.append(head + "".join(f" {e:>14s}" for e in extra))
+    for key in sorted(vals, key=lambda k: -st.mean(durs[k].values()) if durs[k] else 0):
+        d = list(durs[key].values())
+        us = st.mean(d) if d else float("nan")
+        means = {c: st.mean(vals[key][c]) if vals[key][c] else float("nan") for c in cols}
+        line = f"{key[0][:58]:58s} {key[1]:7d} {key[2]:5d} {len(d):4d} {us:9.2f} " + \
+            " ".join(f"{means[c]:20.1f}" for c in cols)
+        if "clock_MHz" in extra:
+            line += f" {means['GRBM_GUI_ACTIVE'] / us:14.1f}"
+        if "valu_per_wave" in extra:
+            line += f" {means['SQ_INSTS_VALU'] / max(means['SQ_WAVES'], 1.0):14.1f}"
+        lines.append(line)
+    return "\n".join(lines)
 
 
 def traffic_summary(fetch_dir: str, write_dir: str):
@@ -140,7 +191,10 @@ def traffic_summary(fetch_dir: str, write_dir: str):
 
 def main(argv):
     if len(argv) >= 2 and argv[0] == "trace":
-        print(trace_summary(argv[1]))
+        skip = int(argv[argv.index("--skip") + 1]) if "--skip" in argv else 0
+        print(trace_summary(argv[1], skip))
+    elif len(argv) >= 2 and argv[0] == "counters":
+        print(counter_summary(argv[1]))
     elif len(argv) >= 3 and argv[0] == "traffic":
         text, data = traffic_summary(argv[1], argv[2])
         print(text)

@@ -1,0 +1,47 @@
+"""The rocprofv3 summaries behind profiles/ (block_dequant_gemv_amd.prof), on
+small hand-written CSV files in rocprofv3's column layout (no GPU needed)."""
+import os
+
+from block_dequant_gemv_amd import prof
+
+
+def _write(path, header, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        f.write(",".join(header) + "\n")
+        for r in rows:
+            f.write(",".join(str(v) for v in r) + "\n")
+
+
+def test_trace_summary_groups_by_launch_shape_and_skips_warmup(tmp_path):
+    hdr = ["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Start_Timestamp", "End_Timestamp"]
+    rows = []
+    # kernel A, 100 workgroups of 256: durations 10, 20 (warm-up) then 5 x 1 us
+    for i, d in enumerate([10, 20, 1, 1, 1, 1, 1]):
+        rows.append(["void qgk::a<1>(int)", 25600, 256, 1000 * i, 1000 * i + 1000 * d])
+    # the same kernel on another grid is its own row
+    rows.append(["void qgk::a<1>(int)", 512, 256, 50000, 52000])
+    _write(str(tmp_path / "t" / "run_kernel_trace.csv"), hdr, rows)
+    full = prof.trace_summary(str(tmp_path / "t"))
+    assert "qgk::a<1>" in full and "(int)" not in full
+    line = [ln for ln in full.splitlines() if " 100 " in ln][0].split()
+    assert line[3] == "7" and abs(float(line[4]) - 35 / 7) < 0.01
+    skipped = prof.trace_summary(str(tmp_path / "t"), skip=2)
+    line = [ln for ln in skipped.splitlines() if " 100 " in ln][0].split()
+    assert line[3] == "5" and float(line[4]) == 1.0 and float(line[5]) == 1.0
+    assert not [ln for ln in skipped.splitlines() if ln.split()[1:2] == ["2"]]   # 1 dispatch, skipped
+
+
+def test_counter_summary_derives_clock_and_valu_per_wave(tmp_path):
+    hdr = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Workgroup_Size", "Counter_Name", "Counter_Value",
+           "Start_Timestamp", "End_Timestamp"]
+    rows = []
+    for did in (1, 2):
+        for c, v in (("GRBM_GUI_ACTIVE", 200000), ("SQ_WAVES", 4000), ("SQ_INSTS_VALU", 1200000)):
+            rows.append([did, "qgk::k", 256000, 256, c, v, 0, 100000])   # 100 us each
+    _write(str(tmp_path / "c" / "run_counter_collection.csv"), hdr, rows)
+    text = prof.counter_summary(str(tmp_path / "c"))
+    line = [ln for ln in text.splitlines() if ln.startswith("qgk::k")][0].split()
+    # wgs 1000, wg 256, n 2, 100 us; clock 200000 / 100 = 2000 (cycles per us); 1200000 / 4000 = 300
+    assert line[1:5] == ["1000", "256", "2", "100.00"]
+    assert float(line[-2]) == 2000.0 and float(line[-1]) == 300.0
