@@ -98,10 +98,24 @@ __device__ __forceinline__ LanePlace lane_place(const Geometry &g, int slot, int
     return p;
 }
 
-// Issue the loads of tile t, segment s (t, s wave-uniform): a wave-uniform
-// base address plus the lane's 32-bit offset. With `real` false (no unit
-// left) every lane loads the first 16 bytes of the buffer instead, one cache
-// line per wavefront. The loop body thus always issues the same loads with no
+// Buffer descriptors: word 3 of a raw (untyped) buffer resource on gfx9, and
+// the cache policy of the weight loads (nontemporal: each byte is read once).
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kLoadNT = 2;
+
+// A raw buffer descriptor for `base` with `bytes` bytes in range: all (-1) or
+// none (0, for a unit past the end: its loads return zeros and read nothing).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const uint8_t *base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, bytes, kRsrcWord3);
+}
+
+// Issue the loads of tile t, segment s (t, s wave-uniform) as buffer loads: a
+// descriptor per plane based at the unit (scalar registers), the lane's 32-bit
+// offset, and the wave-uniform offset of row b / half h in the scalar offset,
+// so that no address arithmetic runs on the vector ALU. With `real` false (no
+// unit left) the descriptors cover no bytes: every load returns zeros without a
+// memory access. The loop body thus always issues the same loads with no
 // branch around them, so the compiler's wait counts keep the next unit in
 // flight while the current one is computed.
 template <int QT>
@@ -111,32 +125,38 @@ __device__ __forceinline__ void load_unit(Unit<QT> &u, const uint8_t *__restrict
     constexpr int NH = Unit<QT>::NH;
     constexpr int64_t seg_q = (int64_t)kTileRows * kSegBlocks * packed_quant_bytes(QT);   // bytes per segment
     constexpr uint32_t str_full = (uint32_t)(kSlots * kSegBlocks * kUnit);
-    t = real ? t : 0;
-    s = real ? s : 0;
     const bool last = s == g.nseg - 1;
-    const uint32_t off = real ? (last ? lp.off_last : lp.off_full) : 0u;
-    const uint32_t ustride = real ? (last ? lp.str_last : str_full) : 0u;
-    const uint8_t *base = wp + t * g.tile_q + s * seg_q;
+    const uint32_t off = last ? lp.off_last : lp.off_full;
+    const uint32_t ustride = last ? lp.str_last : str_full;
+    // wave-uniform by construction (the unit counters are); readfirstlane tells
+    // the compiler so, which keeps the descriptors in scalar registers
+    const int in_range = __builtin_amdgcn_readfirstlane(real ? -1 : 0);
+    const __amdgpu_buffer_rsrc_t rq = plane_rsrc(wp + t * g.tile_q + s * seg_q, in_range);
 #pragma unroll
     for (int b = 0; b < kRowsPerLane; ++b)
 #pragma unroll
-        for (int h = 0; h < NH; ++h) {
-            const uint8_t *ub = base + (uint32_t)(b * NH + h) * ustride;
-            u.q[b][h] = __builtin_nontemporal_load((const u32x4 *)(ub + off));
-        }
+        for (int h = 0; h < NH; ++h)
+            u.q[b][h] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)off, (int)((uint32_t)(b * NH + h) * ustride),
+                                                              kLoadNT);
     // scales: (slot * nb + jc) * 8 bytes = half the quant offset
-    const uint8_t *sbase = wp + g.scale_off + t * g.tile_s + s * (int64_t)(kTileRows * kSegBlocks * 2);
-    u.sc = __builtin_nontemporal_load((const u32x2 *)(sbase + (off >> 1)));
+    const __amdgpu_buffer_rsrc_t rs =
+        plane_rsrc(wp + g.scale_off + t * g.tile_s + s * (int64_t)(kTileRows * kSegBlocks * 2), in_range);
+    u.sc = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(off >> 1), 0, kLoadNT);
     if constexpr (QT == kQ4_K || QT == kQ6_K) {
         constexpr uint32_t ub = (QT == kQ4_K) ? 4 : 2;   // super-plane bytes per row
-        const uint32_t so = real ? (last ? lp.sup_last : lp.sup_full) * (kRowsPerLane * ub) : 0u;
-        const uint8_t *ubase = wp + g.sup_off + t * g.tile_u + s * (int64_t)(kTileRows * (kSegBlocks / kSuperBlocks) * ub);
-        u.sup = __builtin_nontemporal_load((const typename Unit<QT>::Sup *)(ubase + so));
+        const uint32_t so = (last ? lp.sup_last : lp.sup_full) * (kRowsPerLane * ub);
+        const __amdgpu_buffer_rsrc_t ru = plane_rsrc(
+            wp + g.sup_off + t * g.tile_u + s * (int64_t)(kTileRows * (kSegBlocks / kSuperBlocks) * ub), in_range);
+        if constexpr (QT == kQ4_K)
+            u.sup = __builtin_amdgcn_raw_buffer_load_b128(ru, (int)so, 0, kLoadNT);
+        else
+            u.sup = __builtin_amdgcn_raw_buffer_load_b64(ru, (int)so, 0, kLoadNT);
     }
     if constexpr (QT == kQ6_K) {
 #pragma unroll
         for (int bp = 0; bp < 2; ++bp)
-            u.hq[bp] = __builtin_nontemporal_load((const u32x4 *)(base + (uint32_t)(kRowsPerLane + bp) * ustride + off));
+            u.hq[bp] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)off,
+                                                             (int)((uint32_t)(kRowsPerLane + bp) * ustride), kLoadNT);
     }
 }
 
@@ -315,6 +335,28 @@ __device__ __forceinline__ void compute_unit_q6k(const Unit<kQ6_K> &u, float (&a
     }
 }
 
+// s[b] += the 8 products of weight row b's fp16 pairs p[b] (elements 0..7 of a
+// dword) with the activations xv, one fma each in element order, for the B rows
+// of a lane. The rows' chains are interleaved instruction by instruction: each
+// fma depends on the one B instructions back, not on the one before it (which
+// would cost a wait state per fma), and each accumulator still sees its 8 fmas
+// in element order.
+template <int B>
+__device__ __forceinline__ void rows_fma(const h2 (&p)[B][4], const f32x4 (&xv)[2], float (&s)[B])
+{
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) s[b] = __builtin_fmaf((float)p[b][2 * cc].x, xv[cc].x, s[b]);
+#pragma unroll
+        for (int b = 0; b < B; ++b) s[b] = __builtin_fmaf((float)p[b][2 * cc].y, xv[cc].y, s[b]);
+#pragma unroll
+        for (int b = 0; b < B; ++b) s[b] = __builtin_fmaf((float)p[b][2 * cc + 1].x, xv[cc].z, s[b]);
+#pragma unroll
+        for (int b = 0; b < B; ++b) s[b] = __builtin_fmaf((float)p[b][2 * cc + 1].y, xv[cc].w, s[b]);
+    }
+}
+
 template <int QT, int M, bool XLDS>
 __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][kRowsPerLane], const Consts &k,
                                              const f32x4 *xs4, const float *__restrict__ x, int64_t x_stride,
@@ -362,39 +404,16 @@ __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][
         for (int cc = 0; cc < 2; ++cc)
             xv[cc] = XLDS ? xl[m * x_row + (c + cc) * 32] : *(const f32x4 *)(xg + m * x_stride + (c + cc) * 4);
     };
-    auto row_fma = [&](const h2 (&p)[4], const f32x4 (&xv)[2], int m, int b) {
-        float s_ = sb[m][b];
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-            s_ = __builtin_fmaf((float)p[2 * cc].x, xv[cc].x, s_);
-            s_ = __builtin_fmaf((float)p[2 * cc].y, xv[cc].y, s_);
-            s_ = __builtin_fmaf((float)p[2 * cc + 1].x, xv[cc].z, s_);
-            s_ = __builtin_fmaf((float)p[2 * cc + 1].y, xv[cc].w, s_);
-        }
-        sb[m][b] = s_;
-    };
 #pragma unroll
     for (int c = 0; c < 8; c += 2) {
-        if constexpr (M == 1) {
+        h2 p[B][4];
+#pragma unroll
+        for (int b = 0; b < B; ++b) pairs(b, c, p[b]);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
             f32x4 xv[2];
-            load_x(xv, 0, c);
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                h2 p[4];
-                pairs(b, c, p);
-                row_fma(p, xv, 0, b);
-            }
-        } else {
-            h2 p[B][4];
-#pragma unroll
-            for (int b = 0; b < B; ++b) pairs(b, c, p[b]);
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                f32x4 xv[2];
-                load_x(xv, m, c);
-#pragma unroll
-                for (int b = 0; b < B; ++b) row_fma(p[b], xv, m, b);
-            }
+            load_x(xv, m, c);
+            rows_fma<B>(p, xv, sb[m]);
         }
     }
     const h2 d01 = as_h2(live ? u.sc.x : 0u), d23 = as_h2(live ? u.sc.y : 0u);
