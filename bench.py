@@ -808,6 +808,9 @@ def main():
                     help="comma-separated label prefixes: time only the per-config rows that start with one of "
                          "them, and skip the RMSNorm, prefill-GEMM, fp16-form and reference-stream legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="time only the cold calls of the per-config table (no warm column): every launch of a "
+                         "row's kernel is then cold, for profiler runs")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run torch.neg over 256 MiB, a plain copy-like kernel of known traffic "
                          "(counter calibration for rocprofv3 --pmc)")
@@ -929,7 +932,7 @@ def main():
                 for f in fns[:3]:
                     f()
                 u, batch = time_call(qg, torch, fns, args.reps)
-                uw, _ = time_call(qg, torch, [c.fn], max(10, args.reps // 2))
+                uw = np.array([np.nan]) if args.no_warm else time_call(qg, torch, [c.fn], max(10, args.reps // 2))[0]
                 ncopies = len(fns)
                 del fns, copies
                 med = float(np.median(u))
@@ -938,7 +941,8 @@ def main():
                                   "us_p90": round(float(np.percentile(u, 90)), 3), "GBps": round(gbps, 1),
                                   "pct": round(100 * gbps / PEAK_GBPS, 1), "batch_us": round(batch, 3),
                                   "batch_GBps": round(c.nbytes / batch / 1e3, 1), "bytes": c.nbytes,
-                                  "warm_us": round(float(np.median(uw)), 3), "kernel": c.kernel,
+                                  "warm_us": None if args.no_warm else round(float(np.median(uw)), 3),
+                                  "kernel": c.kernel,
                                   "copies": ncopies, "us_each": [round(float(v), 2) for v in u]}
                 log(f"  {c.label:34s} cold {med:9.2f} us ({float(np.percentile(u, 10)):.2f}-"
                     f"{float(np.percentile(u, 90)):.2f})  {gbps:8.1f} GB/s {100 * gbps / PEAK_GBPS:5.1f}%   "

@@ -2,6 +2,7 @@
 
     python -m block_dequant_gemv_amd.prof trace  <dir> [--skip N]   # --kernel-trace --stats -f csv
     python -m block_dequant_gemv_amd.prof counters <dir>
+    python -m block_dequant_gemv_amd.prof collect <out_dir>    # on a GPU machine
     python -m block_dequant_gemv_amd.prof traffic <fetch_dir> <write_dir> [--json out.json]
                                               [--call LABEL=KERNEL|WORKGROUPSxWG ...]
 
@@ -14,6 +15,18 @@ and prints, per launch shape, the mean of every counter and of the dispatch
 time; with GRBM_GUI_ACTIVE it derives the shader clock (busy cycles per
 microsecond of dispatch), with SQ_WAVES and SQ_INSTS_VALU the VALU instructions
 per wavefront.
+
+`collect` runs the profiler passes behind profiles/ (each rocprofv3 pass a
+child process of its own under `timeout -s KILL`, the program after `--`):
+  trace_step   --kernel-trace --stats of the headline decode step alone
+               (bench.py --no-configs --no-cpu --no-q8-step --no-graph)
+  trace_calls  --kernel-trace --stats of the per-call table, cold calls only
+               (bench.py --no-cpu --no-graph --no-warm)
+  fetch, write --pmc FETCH_SIZE / WRITE_SIZE of the headline step and the
+               configurations' calls (bench.py ... --calib-copy)
+  sq           --pmc SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_BUSY_CYCLES
+               SQ_INSTS_LDS GRBM_GUI_ACTIVE --kernel-trace, same calls
+and writes <out>/*.txt summaries that start with the command that made them.
 
 `traffic` reads two counter runs (--pmc FETCH_SIZE, then --pmc WRITE_SIZE; the
 counters are KiB per dispatch) and prints the mean per launch shape. The bytes
@@ -33,6 +46,8 @@ import sys
 from collections import defaultdict
 
 CALIB_BYTES = 256 << 20
+XCDS = 8        # MI355X: accelerator complex dies, each with its own GRBM
+SIMDS = 1024    # 256 CUs x 4 SIMDs
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 
@@ -138,15 +153,21 @@ def counter_summary(directory: str) -> str:
         if t0 is not None and t1 is not None and did is not None:
             durs[key][did] = (int(t1) - int(t0)) / 1e3
     cols = sorted(names)
-    lines = ["per launch shape: dispatches, mean dispatch time (us), mean of each counter per dispatch"
-             + (", clock_MHz = GRBM_GUI_ACTIVE / dispatch time" if "GRBM_GUI_ACTIVE" in names else "")
-             + (", valu_per_wave = SQ_INSTS_VALU / SQ_WAVES" if {"SQ_WAVES", "SQ_INSTS_VALU"} <= names else "")]
+    lines = ["per launch shape: dispatches, mean dispatch time (us), mean of each counter per dispatch (rocprofv3 sums "
+             "each counter over the device's 8 XCDs)"
+             + (";\nclock_MHz = GRBM_GUI_ACTIVE / 8 XCDs / dispatch time (the counter also runs for a few us around "
+                "the dispatch, so short kernels read high)" if "GRBM_GUI_ACTIVE" in names else "")
+             + (";\nvalu_per_wave = SQ_INSTS_VALU / SQ_WAVES" if {"SQ_WAVES", "SQ_INSTS_VALU"} <= names else "")
+             + (";\nvalu_busy = SQ_INSTS_VALU x 4 cycles (a wave64 instruction on a 16-lane SIMD) / (1024 SIMDs x "
+                "GRBM_GUI_ACTIVE / 8)" if {"GRBM_GUI_ACTIVE", "SQ_INSTS_VALU"} <= names else "")]
     head = f"{'kernel':58s} {'wgs':>7s} {'wg':>5s} {'n':>4s} {'us':>9s} " + " ".join(f"{c:>20s}" for c in cols)
     extra = []
     if "GRBM_GUI_ACTIVE" in names:
         extra.append("clock_MHz")
     if {"SQ_WAVES", "SQ_INSTS_VALU"} <= names:
         extra.append("valu_per_wave")
+    if {"GRBM_GUI_ACTIVE", "SQ_INSTS_VALU"} <= names:
+        extra.append("valu_busy")
     lines.append(head + "".join(f" {e:>14s}" for e in extra))
     for key in sorted(vals, key=lambda k: -st.mean(durs[k].values()) if durs[k] else 0):
         d = list(durs[key].values())
@@ -155,9 +176,11 @@ def counter_summary(directory: str) -> str:
         line = f"{key[0][:58]:58s} {key[1]:7d} {key[2]:5d} {len(d):4d} {us:9.2f} " + \
             " ".join(f"{means[c]:20.1f}" for c in cols)
         if "clock_MHz" in extra:
-            line += f" {means['GRBM_GUI_ACTIVE'] / us:14.1f}"
+            line += f" {means['GRBM_GUI_ACTIVE'] / XCDS / us:14.1f}"
         if "valu_per_wave" in extra:
             line += f" {means['SQ_INSTS_VALU'] / max(means['SQ_WAVES'], 1.0):14.1f}"
+        if "valu_busy" in extra:
+            line += f" {means['SQ_INSTS_VALU'] * 4 / (SIMDS * means['GRBM_GUI_ACTIVE'] / XCDS):14.3f}"
         lines.append(line)
     return "\n".join(lines)
 
@@ -189,12 +212,82 @@ def traffic_summary(fetch_dir: str, write_dir: str):
     return "\n".join(lines), out
 
 
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+STEP_ARGS = ["--no-configs", "--no-cpu", "--no-q8-step", "--no-graph", "--steps", "100", "--warmup", "15"]
+CALL_ARGS = ["--no-cpu", "--no-graph", "--no-warm", "--steps", "20", "--warmup", "5", "--reps", "60"]
+PMC_ARGS = ["--no-cpu", "--no-graph", "--no-warm", "--calib-copy", "--steps", "3", "--warmup", "2", "--reps", "5",
+            "--only", "c0,c1,c2,c3,c4,k"]
+SQ_COUNTERS = ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CYCLES", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE"]
+# the headline step's calls: bench.py label -> the kernel launch shape that runs it
+STEP_CALLS = {"gate|up 2x17408x5120 silu": "qgk::qgemv_kernel<2, 1, 1, 1, true, 1, false>|1088x256",
+              "down 5120x17408": "qgk::qgemv_persist<2, 1, 0, true, false, false>|256x1024",
+              "lm_head 248320x5120": "qgk::qgemv_kernel<2, 1, 0, 1, true, 1, false>|7760x256"}
+
+
+def _run_pass(name: str, prof_args: list, bench_args: list, out: str, limit: int):
+    """One rocprofv3 pass over bench.py; returns (command string, bench JSON line or None)."""
+    import subprocess
+    d = os.path.join(out, name)
+    cmd = ["timeout", "-s", "KILL", str(limit), "rocprofv3", *prof_args, "-f", "csv", "-d", d, "-o", "run", "--",
+           sys.executable, os.path.join(ROOT, "bench.py"), *bench_args]
+    shown = " ".join(["rocprofv3", *prof_args, "-f", "csv", "-d", f"<out>/{name}", "-o", "run", "--", "python3",
+                      "bench.py", *bench_args])
+    print(f"[prof] pass {name}: {shown}", file=sys.stderr, flush=True)
+    with open(os.path.join(out, name + ".log"), "w") as log:
+        r = subprocess.run(cmd, cwd="/tmp", stdout=subprocess.PIPE, stderr=log, text=True,
+                           env={**os.environ, "TMPDIR": "/tmp"})
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith('{"metric"')]
+    # rocprofv3 can exit 139 on its own after the program finished (its JSON line printed)
+    if r.returncode != 0 and not (r.returncode in (139, -11) and lines):
+        raise SystemExit(f"pass {name} failed with status {r.returncode} (see {name}.log)")
+    return shown, (json.loads(lines[-1]) if lines else None)
+
+
+def collect(out: str):
+    os.makedirs(out, exist_ok=True)
+    summaries = {}
+    cmd, res = _run_pass("trace_step", ["--kernel-trace", "--stats"], STEP_ARGS, out, 600)
+    roof = res["roofline"] if res else {}
+    summaries["trace_step"] = (
+        f"command: {cmd}\nsummary: python -m block_dequant_gemv_amd.prof trace <out>/trace_step --skip 15\n"
+        f"the same run's bench.py roofline (events bound to the timed launches): {roof.get('call')} "
+        f"{roof.get('avg_launch_us')} us mean over {roof.get('launches')} launches, "
+        f"{roof.get('achieved')} GB/s = {roof.get('frac')} of 8 TB/s; step {res.get('ms_per_step') if res else None} "
+        f"ms, {res.get('value') if res else None} GB/s\n\n" + trace_summary(os.path.join(out, "trace_step"), 15))
+    cmd, _ = _run_pass("trace_calls", ["--kernel-trace", "--stats"], CALL_ARGS, out, 900)
+    summaries["trace_calls"] = (f"command: {cmd}\nsummary: python -m block_dequant_gemv_amd.prof trace "
+                                f"<out>/trace_calls --skip 3\n\n" + trace_summary(os.path.join(out, "trace_calls"), 3))
+    cmd_f, _ = _run_pass("fetch", ["--pmc", "FETCH_SIZE"], PMC_ARGS, out, 600)
+    cmd_w, _ = _run_pass("write", ["--pmc", "WRITE_SIZE"], PMC_ARGS, out, 600)
+    text, data = traffic_summary(os.path.join(out, "fetch"), os.path.join(out, "write"))
+    data["kernel_source_hash"] = kernel_source_hash()
+    data["calls"] = {}
+    for label, key in STEP_CALLS.items():
+        k = data["kernels"].get(key)
+        if k:
+            data["calls"][label] = {"kernel": key, "fetch_bytes": k["fetch_bytes"], "write_bytes": k["write_bytes"],
+                                    "bytes_per_launch": k["fetch_bytes"] + k["write_bytes"]}
+    with open(os.path.join(out, "traffic.json"), "w") as f:
+        json.dump(data, f, indent=1)
+    summaries["traffic"] = (f"commands: {cmd_f}\n          {cmd_w}\nsummary: python -m block_dequant_gemv_amd.prof "
+                            f"traffic <out>/fetch <out>/write\n\n" + text)
+    cmd, _ = _run_pass("sq", ["--pmc", *SQ_COUNTERS, "--kernel-trace"], PMC_ARGS, out, 600)
+    summaries["sq"] = (f"command: {cmd}\nsummary: python -m block_dequant_gemv_amd.prof counters <out>/sq\n\n"
+                       + counter_summary(os.path.join(out, "sq")))
+    for name, text in summaries.items():
+        with open(os.path.join(out, name + ".txt"), "w") as f:
+            f.write(text + "\n")
+    print(f"[prof] summaries in {out}", file=sys.stderr)
+
+
 def main(argv):
     if len(argv) >= 2 and argv[0] == "trace":
         skip = int(argv[argv.index("--skip") + 1]) if "--skip" in argv else 0
         print(trace_summary(argv[1], skip))
     elif len(argv) >= 2 and argv[0] == "counters":
         print(counter_summary(argv[1]))
+    elif len(argv) >= 2 and argv[0] == "collect":
+        collect(argv[1])
     elif len(argv) >= 3 and argv[0] == "traffic":
         text, data = traffic_summary(argv[1], argv[2])
         print(text)

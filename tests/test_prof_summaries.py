@@ -42,6 +42,7 @@ def test_counter_summary_derives_clock_and_valu_per_wave(tmp_path):
     _write(str(tmp_path / "c" / "run_counter_collection.csv"), hdr, rows)
     text = prof.counter_summary(str(tmp_path / "c"))
     line = [ln for ln in text.splitlines() if ln.startswith("qgk::k")][0].split()
-    # wgs 1000, wg 256, n 2, 100 us; clock 200000 / 100 = 2000 (cycles per us); 1200000 / 4000 = 300
+    # wgs 1000, wg 256, n 2, 100 us; clock 200000 / 8 XCDs / 100 = 250 (cycles per us); 1200000 / 4000 = 300
+    # waves' instructions; VALU busy 1200000 * 4 / (1024 * 25000) = 0.1875
     assert line[1:5] == ["1000", "256", "2", "100.00"]
-    assert float(line[-2]) == 2000.0 and float(line[-1]) == 300.0
+    assert float(line[-3]) == 250.0 and float(line[-2]) == 300.0 and abs(float(line[-1]) - 0.1875) < 1e-3
