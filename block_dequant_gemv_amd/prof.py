@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 CSV output for this library's kernels.
 
-    python -m block_dequant_gemv_amd.prof trace  <dir> [--skip N]   # --kernel-trace --stats -f csv
+    python -m block_dequant_gemv_amd.prof trace  <dir> [--skip N] [--tail N]   # --kernel-trace --stats -f csv
     python -m block_dequant_gemv_amd.prof counters <dir>
     python -m block_dequant_gemv_amd.prof collect <out_dir>    # on a GPU machine
     python -m block_dequant_gemv_amd.prof traffic <fetch_dir> <write_dir> [--json out.json]
@@ -8,7 +8,9 @@
 
 `trace` groups the dispatches by kernel name and grid size (two calls of one
 kernel template with different shapes, e.g. the fused QKV and the LM head, show
-up as separate rows) and prints count, mean / median / min duration.
+up as separate rows) and prints count, mean / median / min duration; --skip N
+leaves out the first N dispatches of every shape, --tail N keeps only the last N
+(the headline's back-to-back roofline batch, which bench.py runs last).
 
 `counters` reads one counter run (--pmc with any counters, plus --kernel-trace)
 and prints, per launch shape, the mean of every counter and of the dispatch
@@ -98,9 +100,10 @@ def _short(name: str) -> str:
     return name[:cut] if cut > 0 else name
 
 
-def trace_summary(directory: str, skip: int = 0) -> str:
+def trace_summary(directory: str, skip: int = 0, tail: int = 0, stats_csv: bool = True) -> str:
     """Per launch shape, in dispatch order: count, mean / median / min duration;
-    with skip > 0 the first `skip` dispatches of every shape (warm-up) are left out."""
+    with skip > 0 the first `skip` dispatches of every shape (warm-up) are left
+    out; with tail > 0 only the last `tail` dispatches of every shape are kept."""
     rows = _rows(os.path.join(directory, "**", "*kernel_trace.csv"))
     groups = defaultdict(list)
     for r in rows:
@@ -109,14 +112,17 @@ def trace_summary(directory: str, skip: int = 0) -> str:
         t1 = int(_get(r, "End_Timestamp", default="0"))
         groups[(name, _grid(r) // _wg(r), _wg(r))].append((t0, (t1 - t0) / 1e3))
     groups = {k: [d for _, d in sorted(v)][skip:] for k, v in groups.items()}
+    if tail > 0:
+        groups = {k: v[-tail:] for k, v in groups.items()}
     groups = {k: v for k, v in groups.items() if v}
     lines = ([f"the first {skip} dispatches of every launch shape left out"] if skip else []) + \
+        ([f"the last {tail} dispatches of every launch shape only"] if tail else []) + \
         [f"{'kernel':58s} {'workgroups':>10s} {'wg':>4s} {'n':>5s} {'mean_us':>9s} {'median_us':>9s} "
          f"{'min_us':>8s} {'total_us':>10s}"]
     for (name, wgs, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"{name[:58]:58s} {wgs:10d} {wg:4d} {len(d):5d} {st.mean(d):9.2f} {st.median(d):9.2f} "
                      f"{min(d):8.2f} {sum(d):10.1f}")
-    stats = _rows(os.path.join(directory, "**", "*kernel_stats.csv"))
+    stats = _rows(os.path.join(directory, "**", "*kernel_stats.csv")) if stats_csv else []
     if stats:
         lines.append("")
         lines.append("rocprofv3 kernel_stats.csv (per kernel name):")
@@ -248,12 +254,19 @@ def collect(out: str):
     summaries = {}
     cmd, res = _run_pass("trace_step", ["--kernel-trace", "--stats"], STEP_ARGS, out, 600)
     roof = res["roofline"] if res else {}
+    k = roof.get("launches")
     summaries["trace_step"] = (
-        f"command: {cmd}\nsummary: python -m block_dequant_gemv_amd.prof trace <out>/trace_step --skip 15\n"
-        f"the same run's bench.py roofline (events bound to the timed launches): {roof.get('call')} "
-        f"{roof.get('avg_launch_us')} us mean over {roof.get('launches')} launches, "
-        f"{roof.get('achieved')} GB/s = {roof.get('frac')} of 8 TB/s; step {res.get('ms_per_step') if res else None} "
-        f"ms, {res.get('value') if res else None} GB/s\n\n" + trace_summary(os.path.join(out, "trace_step"), 15))
+        f"command: {cmd}\n"
+        f"summaries: python -m block_dequant_gemv_amd.prof trace <out>/trace_step --tail {k}\n"
+        f"           python -m block_dequant_gemv_amd.prof trace <out>/trace_step --skip 15\n"
+        f"the same run's bench.py: step {res.get('ms_per_step') if res else None} ms, "
+        f"{res.get('value') if res else None} GB/s (plain launches); roofline {roof.get('call')}: "
+        f"{roof.get('avg_launch_us')} us per launch over {k} launches back to back between two events, "
+        f"{roof.get('achieved')} GB/s = {roof.get('frac')} of 8 TB/s\n\n"
+        f"the back-to-back launches the roofline is taken from (the last {k} of every launch shape):\n"
+        + trace_summary(os.path.join(out, "trace_step"), 0, k or 0, stats_csv=False)
+        + "\n\nevery launch after the warm-up (timed steps, the bound-event pass and the back-to-back batches):\n"
+        + trace_summary(os.path.join(out, "trace_step"), 15))
     cmd, _ = _run_pass("trace_calls", ["--kernel-trace", "--stats"], CALL_ARGS, out, 900)
     summaries["trace_calls"] = (f"command: {cmd}\nsummary: python -m block_dequant_gemv_amd.prof trace "
                                 f"<out>/trace_calls --skip 3\n\n" + trace_summary(os.path.join(out, "trace_calls"), 3))
@@ -283,7 +296,8 @@ def collect(out: str):
 def main(argv):
     if len(argv) >= 2 and argv[0] == "trace":
         skip = int(argv[argv.index("--skip") + 1]) if "--skip" in argv else 0
-        print(trace_summary(argv[1], skip))
+        tail = int(argv[argv.index("--tail") + 1]) if "--tail" in argv else 0
+        print(trace_summary(argv[1], skip, tail))
     elif len(argv) >= 2 and argv[0] == "counters":
         print(counter_summary(argv[1]))
     elif len(argv) >= 2 and argv[0] == "collect":

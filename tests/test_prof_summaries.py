@@ -30,6 +30,12 @@ def test_trace_summary_groups_by_launch_shape_and_skips_warmup(tmp_path):
     line = [ln for ln in skipped.splitlines() if " 100 " in ln][0].split()
     assert line[3] == "5" and float(line[4]) == 1.0 and float(line[5]) == 1.0
     assert not [ln for ln in skipped.splitlines() if ln.split()[1:2] == ["2"]]   # 1 dispatch, skipped
+    # the last 3 dispatches of every shape: A's 1 us launches, and the other grid's single one
+    tail = prof.trace_summary(str(tmp_path / "t"), tail=3)
+    line = [ln for ln in tail.splitlines() if " 100 " in ln][0].split()
+    assert line[3] == "3" and float(line[4]) == 1.0
+    line = [ln for ln in tail.splitlines() if ln.split()[1:3] == ["2", "256"]][0].split()
+    assert line[3] == "1" and float(line[4]) == 2.0
 
 
 def test_counter_summary_derives_clock_and_valu_per_wave(tmp_path):
