@@ -2,7 +2,7 @@
 
     python -m block_dequant_gemv_amd.prof trace  <dir> [--skip N] [--tail N]   # --kernel-trace --stats -f csv
     python -m block_dequant_gemv_amd.prof counters <dir>
-    python -m block_dequant_gemv_amd.prof collect <out_dir>    # on a GPU machine
+    python -m block_dequant_gemv_amd.prof collect <out_dir> [--only trace_step,trace_calls,traffic,sq]
     python -m block_dequant_gemv_amd.prof traffic <fetch_dir> <write_dir> [--json out.json]
                                               [--call LABEL=KERNEL|WORKGROUPSxWG ...]
 
@@ -249,44 +249,51 @@ def _run_pass(name: str, prof_args: list, bench_args: list, out: str, limit: int
     return shown, (json.loads(lines[-1]) if lines else None)
 
 
-def collect(out: str):
+def collect(out: str, only=None):
+    """Run the profiler passes (all, or those named in `only`) and write their summaries."""
+    out = os.path.abspath(out)   # the passes run from /tmp
     os.makedirs(out, exist_ok=True)
     summaries = {}
-    cmd, res = _run_pass("trace_step", ["--kernel-trace", "--stats"], STEP_ARGS, out, 600)
-    roof = res["roofline"] if res else {}
-    k = roof.get("launches")
-    summaries["trace_step"] = (
-        f"command: {cmd}\n"
-        f"summaries: python -m block_dequant_gemv_amd.prof trace <out>/trace_step --tail {k}\n"
-        f"           python -m block_dequant_gemv_amd.prof trace <out>/trace_step --skip 15\n"
-        f"the same run's bench.py: step {res.get('ms_per_step') if res else None} ms, "
-        f"{res.get('value') if res else None} GB/s (plain launches); roofline {roof.get('call')}: "
-        f"{roof.get('avg_launch_us')} us per launch over {k} launches back to back between two events, "
-        f"{roof.get('achieved')} GB/s = {roof.get('frac')} of 8 TB/s\n\n"
-        f"the back-to-back launches the roofline is taken from (the last {k} of every launch shape):\n"
-        + trace_summary(os.path.join(out, "trace_step"), 0, k or 0, stats_csv=False)
-        + "\n\nevery launch after the warm-up (timed steps, the bound-event pass and the back-to-back batches):\n"
-        + trace_summary(os.path.join(out, "trace_step"), 15))
-    cmd, _ = _run_pass("trace_calls", ["--kernel-trace", "--stats"], CALL_ARGS, out, 900)
-    summaries["trace_calls"] = (f"command: {cmd}\nsummary: python -m block_dequant_gemv_amd.prof trace "
-                                f"<out>/trace_calls --skip 3\n\n" + trace_summary(os.path.join(out, "trace_calls"), 3))
-    cmd_f, _ = _run_pass("fetch", ["--pmc", "FETCH_SIZE"], PMC_ARGS, out, 600)
-    cmd_w, _ = _run_pass("write", ["--pmc", "WRITE_SIZE"], PMC_ARGS, out, 600)
-    text, data = traffic_summary(os.path.join(out, "fetch"), os.path.join(out, "write"))
-    data["kernel_source_hash"] = kernel_source_hash()
-    data["calls"] = {}
-    for label, key in STEP_CALLS.items():
-        k = data["kernels"].get(key)
-        if k:
-            data["calls"][label] = {"kernel": key, "fetch_bytes": k["fetch_bytes"], "write_bytes": k["write_bytes"],
-                                    "bytes_per_launch": k["fetch_bytes"] + k["write_bytes"]}
-    with open(os.path.join(out, "traffic.json"), "w") as f:
-        json.dump(data, f, indent=1)
-    summaries["traffic"] = (f"commands: {cmd_f}\n          {cmd_w}\nsummary: python -m block_dequant_gemv_amd.prof "
-                            f"traffic <out>/fetch <out>/write\n\n" + text)
-    cmd, _ = _run_pass("sq", ["--pmc", *SQ_COUNTERS, "--kernel-trace"], PMC_ARGS, out, 600)
-    summaries["sq"] = (f"command: {cmd}\nsummary: python -m block_dequant_gemv_amd.prof counters <out>/sq\n\n"
-                       + counter_summary(os.path.join(out, "sq")))
+    want = lambda name: only is None or name in only  # noqa: E731
+    if want("trace_step"):
+        cmd, res = _run_pass("trace_step", ["--kernel-trace", "--stats"], STEP_ARGS, out, 600)
+        roof = res["roofline"] if res else {}
+        k = roof.get("launches")
+        summaries["trace_step"] = (
+            f"command: {cmd}\n"
+            f"summaries: python -m block_dequant_gemv_amd.prof trace <out>/trace_step --tail {k}\n"
+            f"           python -m block_dequant_gemv_amd.prof trace <out>/trace_step --skip 15\n"
+            f"the same run's bench.py: step {res.get('ms_per_step') if res else None} ms, "
+            f"{res.get('value') if res else None} GB/s (plain launches); roofline {roof.get('call')}: "
+            f"{roof.get('avg_launch_us')} us per launch over {k} launches back to back between two events, "
+            f"{roof.get('achieved')} GB/s = {roof.get('frac')} of 8 TB/s\n\n"
+            f"the back-to-back launches the roofline is taken from (the last {k} of every launch shape):\n"
+            + trace_summary(os.path.join(out, "trace_step"), 0, k or 0, stats_csv=False)
+            + "\n\nevery launch after the warm-up (timed steps, the bound-event pass and the back-to-back batches):\n"
+            + trace_summary(os.path.join(out, "trace_step"), 15))
+    if want("trace_calls"):
+        cmd, _ = _run_pass("trace_calls", ["--kernel-trace", "--stats"], CALL_ARGS, out, 900)
+        summaries["trace_calls"] = (f"command: {cmd}\nsummary: python -m block_dequant_gemv_amd.prof trace "
+                                    f"<out>/trace_calls --skip 3\n\n" + trace_summary(os.path.join(out, "trace_calls"), 3))
+    if want("traffic"):
+        cmd_f, _ = _run_pass("fetch", ["--pmc", "FETCH_SIZE"], PMC_ARGS, out, 600)
+        cmd_w, _ = _run_pass("write", ["--pmc", "WRITE_SIZE"], PMC_ARGS, out, 600)
+        text, data = traffic_summary(os.path.join(out, "fetch"), os.path.join(out, "write"))
+        data["kernel_source_hash"] = kernel_source_hash()
+        data["calls"] = {}
+        for label, key in STEP_CALLS.items():
+            k = data["kernels"].get(key)
+            if k:
+                data["calls"][label] = {"kernel": key, "fetch_bytes": k["fetch_bytes"], "write_bytes": k["write_bytes"],
+                                        "bytes_per_launch": k["fetch_bytes"] + k["write_bytes"]}
+        with open(os.path.join(out, "traffic.json"), "w") as f:
+            json.dump(data, f, indent=1)
+        summaries["traffic"] = (f"commands: {cmd_f}\n          {cmd_w}\nsummary: python -m block_dequant_gemv_amd.prof "
+                                f"traffic <out>/fetch <out>/write\n\n" + text)
+    if want("sq"):
+        cmd, _ = _run_pass("sq", ["--pmc", *SQ_COUNTERS, "--kernel-trace"], PMC_ARGS, out, 600)
+        summaries["sq"] = (f"command: {cmd}\nsummary: python -m block_dequant_gemv_amd.prof counters <out>/sq\n\n"
+                           + counter_summary(os.path.join(out, "sq")))
     for name, text in summaries.items():
         with open(os.path.join(out, name + ".txt"), "w") as f:
             f.write(text + "\n")
@@ -301,7 +308,7 @@ def main(argv):
     elif len(argv) >= 2 and argv[0] == "counters":
         print(counter_summary(argv[1]))
     elif len(argv) >= 2 and argv[0] == "collect":
-        collect(argv[1])
+        collect(argv[1], argv[argv.index("--only") + 1].split(",") if "--only" in argv else None)
     elif len(argv) >= 3 and argv[0] == "traffic":
         text, data = traffic_summary(argv[1], argv[2])
         print(text)
