@@ -836,8 +836,9 @@ def main():
     ap.add_argument("--no-q8-step", action="store_true", help="skip the Q8_0 decode step")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the headline steps")
     ap.add_argument("--only", default=None,
-                    help="comma-separated label prefixes: time only the per-config rows that start with one of "
-                         "them, and skip the RMSNorm, prefill-GEMM, fp16-form and reference-stream legs")
+                    help="comma-separated label prefixes: time only the per-config, RMSNorm ('n ...') and "
+                         "prefill-GEMM ('g ...') rows that start with one of them, and skip the fp16-form and "
+                         "reference-stream legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-warm", action="store_true",
                     help="time only the cold calls of the per-config table (no warm column): every launch of a "
@@ -956,8 +957,9 @@ def main():
         norm_cases = cfg_calls.pop("norm")
         gemm_cases = cfg_calls.pop("gemm")
         only = [o for o in args.only.split(",") if o] if args.only else None
-        if only:
-            norm_cases, gemm_cases = [], []
+        if only:   # the RMSNorm ("n ...") and GEMM ("g ...") rows take the same prefixes
+            norm_cases = [c for c in norm_cases if any(c[0].startswith(o) for o in only)]
+            gemm_cases = [c for c in gemm_cases if any(c[0].startswith(o) for o in only)]
         for ci in sorted(cfg_calls):
             for c in cfg_calls[ci]:
                 if only and not any(c.label.startswith(o) for o in only):

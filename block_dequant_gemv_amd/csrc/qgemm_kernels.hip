@@ -32,6 +32,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "dequant.h"
 #include "layout.h"
 #include "qgemm_kernels.h"
@@ -118,53 +120,92 @@ __device__ __forceinline__ void group_transpose(uint32_t (&v)[4])
 }
 
 // ---------------------------------------------------------------------------
-// The GEMM. A workgroup of G wavefronts owns 16 RG G weight rows: wavefront w
-// covers RG groups of 16 rows (row tiles 2 RG (blockIdx.x G + w) + 2 rg and
-// + 1 for group rg), for the MT 16-row activation tiles [a.mt0, a.mt0 + MT).
-// K is walked in chunks of CB = gemm_chunk(MT) blocks, staged into two LDS buffers in
-// turn: the chunk's split activations (MT x 2 KiB per block) and the scales of
-// the workgroup's rows are copied with LDS-direct loads (global_load_lds, no
-// registers) one chunk ahead, so the copy of chunk c + 1 runs under the
-// matrix-core work of chunk c; one vmcnt wait and one barrier per chunk. The
-// weights of a chunk are loaded one chunk ahead too: load groups of 4 (Q4_0) or
-// 2 (Q8_0) blocks, one 16-byte load per lane and row group. Each wavefront
-// walks a chunk's groups: the group transpose, the dequant, and per block and
-// activation tile two MFMAs (hi, lo) per row group, each B operand read once
-// from LDS and used by the RG row groups; then acc = fma(d, S, acc).
-// Block sums are added per segment of 32 blocks and the segment sums in order.
-// With a.ksplit > 1, workgroup column blockIdx.y takes one range of segments
-// and writes its sums to a.part; launch_ksum then adds the ranges in order.
-template <int QT, int MT, int RG>
-__global__ void __launch_bounds__(256)
+// The GEMM. Workgroup (row block rb, activation group mg) of G wavefronts owns
+// the 16 RG G weight rows of row block rb (wavefront w: row tiles 2 RG (rb G + w)
+// + 2 rg and + 1 for row group rg) and the MT 16-row activation tiles
+// [mg MT, mg MT + MT); blockIdx.x = rb * n_mg + mg, so the groups that read the
+// same weights are launched next to each other. K is walked in chunks of
+// kGemmChunk blocks through a ring of kGemmRing staging buffers: while chunk c is
+// computed, the loads of chunks c + 1 and c + 2 are in flight (the time of two
+// chunks of matrix-core work covers the memory latency). Per chunk every
+// wavefront issues the same number of loads:
+//   * its share of the chunk's split activations, 1 KiB pieces copied with
+//     LDS-direct loads (global_load_lds, no registers), MT x kGemmChunk x 2 pieces
+//     over the G wavefronts;
+//   * one 64-lane copy of the scales of the workgroup's rows (LDS-direct);
+//   * its weights: load groups of 4 (Q4_0) or 2 (Q8_0) blocks, one 16-byte load
+//     per lane and row group (LDS-direct as well: no load has a register
+//     destination, so nothing but the one wait per chunk waits for them).
+// A ragged chunk (the end of a ragged K segment) re-reads valid pieces into
+// slots nobody reads, so the counts, and with them the one vmcnt wait per chunk,
+// stay fixed; one barrier per chunk then hands the staged data to every
+// wavefront and frees the buffer the next loads take. Per block and activation
+// tile each wavefront runs two MFMAs (hi, lo) per row group, each B operand read
+// once from LDS and used by the RG row groups, then acc = fma(d, S, acc). Block
+// sums are added per segment of 32 blocks and the segment sums in order; with
+// a.ksplit > 1, workgroup row blockIdx.y takes one range of chunks and writes its
+// sums to a.part, which launch_ksum adds in range order.
+//
+// Addressing: the chunk loop is unrolled over the three ring buffers, so every
+// LDS address is a per-lane base plus a constant. In a full segment of 32
+// blocks each load is a wave-uniform base (advanced per chunk on the scalar
+// unit) plus a 32-bit per-lane offset fixed for the whole walk; only the chunks
+// of a ragged last segment take the general address arithmetic.
+template <int V>
+using IntC = std::integral_constant<int, V>;
+
+typedef const __attribute__((address_space(1))) void *gvoid;
+typedef __attribute__((address_space(3))) void *lvoid;
+
+template <int QT, int MT, int RG, int G>
+__global__ void __launch_bounds__(64 * G)
 qgemm_kernel(const uint8_t *__restrict__ wp, const _Float16 *__restrict__ xs, const float *__restrict__ unscale,
              float *__restrict__ Y, GemmArgs a)
 {
     constexpr int NH = (QT == kQ8_0) ? 2 : 1;
     constexpr int BPG = (QT == kQ8_0) ? 2 : 4;   // blocks per load group
-    constexpr int CB = gemm_chunk(MT);           // blocks per staged chunk (a multiple of BPG)
+    constexpr int CB = kGemmChunk;               // blocks per staged chunk
+    constexpr int NG = CB / BPG;                 // load groups per chunk
+    constexpr int PIECES = MT * CB * 2;          // 1 KiB activation pieces per chunk
+    static_assert(PIECES % G == 0, "every wavefront copies the same number of pieces");
+    constexpr int PPW = PIECES / G;
+    constexpr int XBUF = MT * CB * 128;          // u32x4 per activation buffer
+    constexpr int SBUF = G * kGemmScaleWordsPerWave;
+    constexpr int WBUF = G * NG * RG * 64;       // u32x4 per weight buffer
+    constexpr int WG_TILES = 2 * RG * G;         // 8-row tiles per workgroup
+    constexpr int SWORDS = WG_TILES * 2 * CB * 2;   // scale words of a chunk: tile x slot x block x 8 B
+    static_assert(SWORDS <= SBUF, "one scale copy per wavefront");
+    constexpr int LOADS = PPW + 1 + NG * RG;     // vector-memory loads per chunk and wavefront
+    static_assert((kGemmDepth - 1) * LOADS < 64, "vmcnt range");
+    static_assert(kGemmDepth == 2 && kGemmRing == 3, "the chunk loop below is unrolled for a ring of three");
+    constexpr int CPS = kSegBlocks / CB;
+    static_assert(CPS == 8, "chunk positions below use shifts by 3");
     extern __shared__ u32x4 lds[];
-    u32x4 *lx = lds;   // 2 buffers x [mt][CB][h][64 lanes] x 16 B
-    // 2 buffers x [tile of the workgroup][slot][CB] x 4 fp16, in 4-byte words, padded to whole wavefront copies
-    uint32_t *lsc_base = (uint32_t *)(lds + 2 * MT * CB * 128);
+    u32x4 *lx = lds;                                              // kGemmRing x XBUF
+    u32x4 *lw = lds + kGemmRing * XBUF;                            // kGemmRing x WBUF
+    uint32_t *lsc = (uint32_t *)(lw + kGemmRing * WBUF);           // kGemmRing x SBUF words
 
     const Geometry &g = a.geo;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: its arithmetic stays scalar
-    const int G = blockDim.x >> 6;
     const int i = lane & 15, c = lane >> 4;
-    const int64_t wg_tile0 = (int64_t)blockIdx.x * G * 2 * RG;   // first row tile of the workgroup
-    const int wg_tiles = G * 2 * RG;
-    const int lsc_words = gemm_scale_words(wg_tiles, CB);
+    const int64_t mg = (int64_t)blockIdx.x % a.n_mg;
+    const int64_t rb = (int64_t)blockIdx.x / a.n_mg;
+    const int64_t mt0 = mg * MT;
+    const int64_t wg_tile0 = rb * WG_TILES;                       // first row tile of the workgroup
     const int64_t t_first = wg_tile0 + (int64_t)wave * 2 * RG;    // first row tile of this wavefront
     const int64_t t_last = g.n_tiles - 1;
     const int slotA = (i & 7) >> 2, browA = i & 3;
-    int64_t qoffA[RG];   // byte offset of this lane's A row in its tile (row group rg)
+    // every lane's A-row tile lies at or after tb (tiles past the end are clamped to the last)
+    const int64_t tb = t_first < t_last ? t_first : t_last;
+    uint32_t w_tile[RG];   // byte offset of this lane's A-row tile (row group rg) from tile tb
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
         int64_t t = t_first + 2 * rg + (i >> 3);
         t = t < t_last ? t : t_last;
-        qoffA[rg] = t * g.tile_q;
+        w_tile[rg] = (uint32_t)((t - tb) * g.tile_q);
     }
+    const uint8_t *w_wave = wp + tb * g.tile_q;
     const Consts k = make_consts();
     constexpr int64_t seg_q = (int64_t)kTileRows * kSegBlocks * NH * kUnit;
     constexpr int64_t seg_s = (int64_t)kTileRows * kSegBlocks * 2;
@@ -175,123 +216,164 @@ qgemm_kernel(const uint8_t *__restrict__ wp, const _Float16 *__restrict__ xs, co
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) tot[rg][mt] = seg[rg][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // Load group q of segment s (nb blocks): lane (i, c) loads the 16-byte unit
-    // of row i of each row group for block 4q + c (Q4_0) or block 2q + c/2, half
-    // c%2 (Q8_0); past a ragged segment's end it loads a valid unit, never used.
-    auto load_group = [&](u32x4 (&raw)[RG], int64_t s, int nb, int q) {
-        int jb = (QT == kQ4_0) ? 4 * q + c : 2 * q + (c >> 1);
-        const int hh = (QT == kQ4_0) ? 0 : (c & 1);
-        jb = jb < nb ? jb : nb - 1;
-        const int64_t off = s * seg_q + (int64_t)(((browA * NH + hh) * kSlots + slotA) * nb + jb) * kUnit;
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg) raw[rg] = __builtin_nontemporal_load((const u32x4 *)(wp + qoffA[rg] + off));
-    };
-
-    const int64_t KB = g.KB;
+    // K as a flat sequence of chunks: every segment but the matrix's last holds
+    // 32 / CB of them, and chunk ch covers blocks [ch CB, ch CB + CB) of the whole
+    // K (the split activations are laid out block after block); workgroup row ky
+    // takes chunks [c_begin, c_end).
+    const int64_t nseg_last = g.nseg - 1;
+    const int nb_last = (int)seg_blocks(g, nseg_last);
+    const bool ragged = nb_last < kSegBlocks;   // the last segment takes the general path
+    const int64_t n_all = nseg_last * CPS + (nb_last + CB - 1) / CB;
     const int64_t ky = blockIdx.y;
-    const int64_t s_begin = g.nseg * ky / a.ksplit, s_end = g.nseg * (ky + 1) / a.ksplit;
-    // The K range as a flat sequence of chunks of CB blocks: every segment but the
-    // matrix's last holds 32 / CB of them.
-    constexpr int CPS = kSegBlocks / CB;
-    struct ChunkPos {
-        int64_t s;
-        int j0, nb, nbc;
-    };
-    auto chunk_at = [&](int64_t c) {
-        ChunkPos p;
-        p.s = s_begin + c / CPS;
-        p.j0 = (int)(c % CPS) * CB;
-        p.nb = (int)seg_blocks(g, p.s);
-        p.nbc = p.nb - p.j0 < CB ? p.nb - p.j0 : CB;
-        return p;
-    };
-    const int64_t n_chunks =
-        s_end > s_begin ? (s_end - s_begin - 1) * CPS + (seg_blocks(g, s_end - 1) + CB - 1) / CB : 0;
+    const int64_t c_begin = n_all * ky / a.ksplit, c_end = n_all * (ky + 1) / a.ksplit;
+    const int n = (int)(c_end - c_begin);
+    const int64_t KB = g.KB;
 
-    // Stage chunk c into buffer `buf` with LDS-direct loads (no registers; they
-    // complete under vmcnt): wavefront w copies 1 KiB pieces w, w + G, ... of the
-    // activations (MT tiles x nbc blocks x 2 KiB, each tile's run contiguous in
-    // the workspace and in LDS), then its share of the scales as 4-byte words
-    // (run (tile, slot) = CB entries of 8 B; words past the chunk's blocks or
-    // past the runs re-read a valid word and land in the padding).
-    auto stage = [&](int buf, int64_t c) {
-        const ChunkPos p = chunk_at(c);
-        u32x4 *lxd = lx + buf * (MT * CB * 128);
-        const int nkib = MT * p.nbc * 2;
-        for (int q = wave; q < nkib; q += G) {
-            // a full chunk's run per tile is 2 CB pieces (a power of two)
-            const int mt = MT == 1 ? 0 : (p.nbc == CB ? q / (2 * CB) : q / (p.nbc * 2));
-            const int r = q - mt * (p.nbc * 2);
-            const u32x4 *src =
-                (const u32x4 *)xs + ((a.mt0 + mt) * KB + p.s * kSegBlocks + p.j0) * 128 + r * 64 + lane;
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                             (__attribute__((address_space(3))) void *)(lxd + mt * CB * 128 + r * 64),
-                                             16, 0, 0);
-        }
-        uint32_t *lsd = (uint32_t *)(lsc_base + buf * lsc_words);
-        const int nwords = wg_tiles * 2 * CB * 2;
-        // the workgroup's first tile and this segment (uniform), then per lane its
-        // tile (clamped to the matrix's last) and its place in the segment
-        const uint8_t *sbase = wp + g.scale_off + wg_tile0 * g.tile_s + p.s * seg_s;
-        const int tl_last = (int)(t_last - wg_tile0);
-        for (int q = wave; q * 64 < lsc_words; q += G) {
-            int wi = q * 64 + lane;
-            wi = wi < nwords ? wi : 0;
-            const int run = wi / (2 * CB), within = wi - run * (2 * CB);
-            int tl = run >> 1;
-            tl = tl < tl_last ? tl : tl_last;
-            const int sl = run & 1;
-            int jj = within >> 1;
-            jj = jj < p.nbc ? jj : p.nbc - 1;
-            const uint8_t *src = sbase + (uint64_t)(uint32_t)tl * (uint64_t)g.tile_s +
-                                 (uint32_t)((sl * p.nb + p.j0 + jj) * (kRowsPerLane * 2) + (within & 1) * 4);
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                             (__attribute__((address_space(3))) void *)(lsd + q * 64), 4, 0, 0);
-        }
-    };
-
-    // All NG load groups of a chunk, loaded one chunk ahead (a ragged last chunk's
-    // extra groups load valid units that are never used).
-    constexpr int NG = CB / BPG;
-    auto load_chunk = [&](u32x4 (&raw)[NG][RG], int64_t c) {
-        const ChunkPos p = chunk_at(c);
+    // Activations: this wavefront's pieces q = wave + G t of a full chunk are
+    // (tile q / 2CB, 1 KiB piece q % 2CB); byte offsets from the chunk's start
+    // (global) and from the buffer's start (LDS).
+    const uint8_t *x_wg = (const uint8_t *)xs + mt0 * KB * 2048;
+    const uint32_t lane16 = (uint32_t)lane * 16;
+    int64_t x_off[PPW];
+    int l_off[PPW];
 #pragma unroll
-        for (int q = 0; q < NG; ++q) load_group(raw[q], p.s, p.nb, p.j0 / BPG + q);
-    };
-    // Two register sets take turns: chunk ci computes from one while chunk
-    // ci + 1's weights load into the other (the loop is unrolled by two).
-    u32x4 rawA[NG][RG], rawB[NG][RG];
-    if (n_chunks > 0) {
-        stage(0, 0);
-        load_chunk(rawA, 0);
+    for (int t = 0; t < PPW; ++t) {
+        const int q = wave + G * t, mt = q / (2 * CB), r = q % (2 * CB);
+        x_off[t] = (int64_t)mt * KB * 2048 + r * 1024;
+        l_off[t] = (mt * CB * 128 + r * 64) * 16;
     }
-    auto chunk_step = [&](u32x4 (&cur)[NG][RG], u32x4 (&nxt)[NG][RG], int64_t ci) {
-        // Everything this wavefront issued is chunk ci's: its copies into buffer
-        // ci & 1 and its weight groups, both issued one chunk earlier. After the
-        // barrier every wavefront's copies are in LDS and every wavefront is past
-        // chunk ci - 1, whose buffer the next copies take. Nothing issued after a
-        // load comes between that load and its use, so no wait below covers the
-        // next chunk's loads.
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // Weights: lane (i, c) loads row i's unit of block jq = 4q + c (Q4_0) or
+    // 2q + c/2, half c%2 (Q8_0) of the load group; unit (b, h, slot, j) of a
+    // segment with nb blocks sits at ((b NH + h) kSlots + slot) nb + j.
+    const int hh = (QT == kQ4_0) ? 0 : (c & 1);
+    const int lane_unit = (browA * NH + hh) * kSlots + slotA;
+    auto jq = [&](int q) { return (QT == kQ4_0) ? 4 * q + c : 2 * q + (c >> 1); };
+    uint32_t w_lane[NG][RG];   // in a full segment: the lane's byte offset from the chunk's base
+#pragma unroll
+    for (int q = 0; q < NG; ++q)
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) w_lane[q][rg] = w_tile[rg] + (uint32_t)((lane_unit * kSegBlocks + jq(q)) * kUnit);
+    // Scales: word wi = wave 64 + lane of a chunk = (run = tile x 2 + slot, block jj, half).
+    int sc_tl, sc_sl, sc_jj, sc_half;
+    {
+        int wi = wave * kGemmScaleWordsPerWave + lane;
+        wi = wi < SWORDS ? wi : 0;
+        const int srun = wi / (2 * CB), within = wi - srun * (2 * CB);
+        const int tl_last = (int)(t_last - wg_tile0);
+        sc_tl = (srun >> 1) < tl_last ? (srun >> 1) : tl_last;
+        sc_sl = srun & 1;
+        sc_jj = within >> 1;
+        sc_half = within & 1;
+    }
+    const uint8_t *s_wg = wp + g.scale_off + wg_tile0 * g.tile_s;
+    const uint32_t s_tile = (uint32_t)(sc_tl * g.tile_s + sc_half * 4);
+    const uint32_t s_lane = s_tile + (uint32_t)((sc_sl * kSegBlocks + sc_jj) * (kRowsPerLane * 2));
+
+    // LDS byte addresses this lane reads (buffer 0; the others at constant distances)
+    const int lx_lane = lane * 16;
+    const int lw_lane = (kGemmRing * XBUF + wave * NG * RG * 64 + lane) * 16;
+    const int ls_lane = kGemmRing * (XBUF + WBUF) * 16 + (((wave * RG * 2 + (c >> 1)) * 2 + (c & 1)) * CB) * 8;
+    const uint8_t *lds_b = (const uint8_t *)lds;
+
+    // The LOADS loads of a chunk ch of a full segment into ring buffer BUF, as
+    // one list (the weights, then the scales, then the activation pieces), of
+    // which entries [lo, hi) are issued.
+    auto issue_full = [&](auto BUF, int64_t ch, int lo, int hi) {
+        const int B = BUF;
+        const int64_t s = ch >> 3;
+        const int j0 = (int)(ch & 7) * CB;
+        uint8_t *lb = (uint8_t *)lds;
+        const uint8_t *wu = w_wave + (s * seg_q + j0 * kUnit);
+        const uint8_t *xu = x_wg + ch * (CB * 2048);
+#pragma unroll
+        for (int l = 0; l < LOADS; ++l) {
+            if (l < lo || l >= hi) continue;
+            if (l < NG * RG) {
+                const int q = l / RG, rg = l % RG;
+                __builtin_amdgcn_global_load_lds(
+                    (gvoid)(wu + w_lane[q][rg]),
+                    (lvoid)(lb + (kGemmRing * XBUF + B * WBUF + ((wave * NG + q) * RG + rg) * 64) * 16), 16, 0, 0);
+            } else if (l == NG * RG) {
+                __builtin_amdgcn_global_load_lds(
+                    (gvoid)(s_wg + (s * seg_s + j0 * (kRowsPerLane * 2)) + s_lane),
+                    (lvoid)(lb + kGemmRing * (XBUF + WBUF) * 16 + (B * SBUF + wave * kGemmScaleWordsPerWave) * 4), 4,
+                    0, 0);
+            } else {
+                const int t = l - NG * RG - 1;
+                __builtin_amdgcn_global_load_lds((gvoid)(xu + x_off[t] + lane16),
+                                                 (lvoid)(lb + B * XBUF * 16 + l_off[t]), 16, 0, 0);
+            }
+        }
+    };
+
+    // The loads of any chunk ch into ring buffer BUF, all at once.
+    auto issue = [&](auto BUF, int64_t ch) {
+        const int B = BUF;
+        const int64_t s = ch >> 3;
+        const int j0 = (int)(ch & 7) * CB;
+        const uint8_t *xu = x_wg + ch * (CB * 2048);
+        uint8_t *lb = (uint8_t *)lds;
+        if (!(ragged && s == nseg_last)) {
+            issue_full(BUF, ch, 0, LOADS);
+            return;
+        }
+        // a chunk of the ragged last segment (nb_last blocks)
+        const int nb = nb_last;
+        const int nbc = nb - j0 < CB ? nb - j0 : CB;
+        if (nbc == CB) {
+#pragma unroll
+            for (int t = 0; t < PPW; ++t)
+                __builtin_amdgcn_global_load_lds((gvoid)(xu + x_off[t] + lane16),
+                                                 (lvoid)(lb + B * XBUF * 16 + l_off[t]), 16, 0, 0);
+        } else {
+            // tile runs of nbc x 2 KiB; spare copies re-read piece 0
+            const int run = nbc * 2;
+#pragma unroll
+            for (int t = 0; t < PPW; ++t) {
+                int q = wave + G * t;
+                q = q < MT * run ? q : 0;
+                const int mt = q / run, r = q - mt * run;
+                __builtin_amdgcn_global_load_lds((gvoid)(xu + (int64_t)mt * KB * 2048 + r * 1024 + lane16),
+                                                 (lvoid)(lb + B * XBUF * 16 + (mt * CB * 128 + r * 64) * 16), 16, 0,
+                                                 0);
+            }
+        }
+        {
+            const int jj = sc_jj < nbc ? sc_jj : nbc - 1;
+            const uint8_t *src = s_wg + s * seg_s + s_tile + (uint32_t)((sc_sl * nb + j0 + jj) * (kRowsPerLane * 2));
+            __builtin_amdgcn_global_load_lds(
+                (gvoid)src, (lvoid)(lb + kGemmRing * (XBUF + WBUF) * 16 + (B * SBUF + wave * kGemmScaleWordsPerWave) * 4),
+                4, 0, 0);
+        }
+        const uint8_t *wu = w_wave + s * seg_q;
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+            int jb = j0 + jq(q);
+            jb = jb < nb ? jb : nb - 1;   // past a ragged segment's end: a valid unit, never used
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg)
+                __builtin_amdgcn_global_load_lds(
+                    (gvoid)(wu + w_tile[rg] + (uint32_t)((lane_unit * nb + jb) * kUnit)),
+                    (lvoid)(lb + (kGemmRing * XBUF + B * WBUF + ((wave * NG + q) * RG + rg) * 64) * 16), 16, 0, 0);
+        }
+    };
+
+    // Chunk computation from ring buffer BUF: nbc valid blocks (CB in a full
+    // segment, a compile-time constant there).
+    auto compute = [&](auto BUF, auto NBC, auto hook) {
+        const int B = BUF;
+        const int nbc = NBC;
         uint32_t v[NG][RG][4];
 #pragma unroll
         for (int q = 0; q < NG; ++q)
 #pragma unroll
             for (int rg = 0; rg < RG; ++rg) {
-                v[q][rg][0] = cur[q][rg].x;
-                v[q][rg][1] = cur[q][rg].y;
-                v[q][rg][2] = cur[q][rg].z;
-                v[q][rg][3] = cur[q][rg].w;
+                const u32x4 w = *(const u32x4 *)(lds_b + lw_lane + (B * WBUF + (q * RG + rg) * 64) * 16);
+                v[q][rg][0] = w.x;
+                v[q][rg][1] = w.y;
+                v[q][rg][2] = w.z;
+                v[q][rg][3] = w.w;
             }
-        __syncthreads();
-        if (ci + 1 < n_chunks) {
-            stage((int)((ci + 1) & 1), ci + 1);
-            load_chunk(nxt, ci + 1);
-        }
-        const ChunkPos cp = chunk_at(ci);
-        const int nb = cp.nb, nbc = cp.nbc, j0 = cp.j0;
-        const u32x4 *lxb = lx + (ci & 1) * (MT * CB * 128);
-        const u32x2 *lscb = (const u32x2 *)(lsc_base + (ci & 1) * lsc_words);
 #pragma unroll
         for (int qq = 0; qq < NG; ++qq) {
             if (qq * BPG >= nbc) break;   // wave-uniform
@@ -316,56 +398,132 @@ qgemm_kernel(const uint8_t *__restrict__ wp, const _Float16 *__restrict__ xs, co
                         A[rg] = h8{p0[0].x, p0[0].y, p0[1].x, p0[1].y, p1[0].x, p1[0].y, p1[1].x, p1[1].y};
                     }
                     // rows 4c + r of row group rg: tile (wave*RG + rg)*2 + c/2 of the workgroup, slot c%2
-                    const u32x2 dd = lscb[(((wave * RG + rg) * 2 + (c >> 1)) * 2 + (c & 1)) * CB + jj];
+                    const u32x2 dd = *(const u32x2 *)(lds_b + ls_lane + B * SBUF * 4 + (rg * 4 * CB + jj) * 8);
                     d01[rg] = as_h2(dd.x);
                     d23[rg] = as_h2(dd.y);
                 }
+                // every MFMA of the block first, then the scale fmas: an fma never
+                // waits right behind the MFMA that feeds it
+                f32x4 S[MT][RG];
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    const h8 bh = __builtin_bit_cast(h8, lxb[(mt * CB + jj) * 128 + lane]);
-                    const h8 bl = __builtin_bit_cast(h8, lxb[(mt * CB + jj) * 128 + 64 + lane]);
-                    f32x4 S[RG];
+                    const uint8_t *xb = lds_b + lx_lane + (B * XBUF + (mt * CB + jj) * 128) * 16;
+                    const h8 bh = *(const h8 *)xb;
+                    const h8 bl = *(const h8 *)(xb + 1024);
 #pragma unroll
                     for (int rg = 0; rg < RG; ++rg)
-                        S[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[rg], bh, f32x4{0.0f, 0.0f, 0.0f, 0.0f},
-                                                                       0, 0, 0);
+                        S[mt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[rg], bh, f32x4{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                           0, 0, 0);
 #pragma unroll
                     for (int rg = 0; rg < RG; ++rg)
-                        S[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[rg], bl, S[rg], 0, 0, 0);
+                        S[mt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[rg], bl, S[mt][rg], 0, 0, 0);
+                }
+                hook(jj);   // loads of a later chunk, issued while the matrix cores work
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int rg = 0; rg < RG; ++rg) {
                         f32x4 &acc = seg[rg][mt];
-                        acc.x = __builtin_fmaf((float)d01[rg].x, S[rg].x, acc.x);
-                        acc.y = __builtin_fmaf((float)d01[rg].y, S[rg].y, acc.y);
-                        acc.z = __builtin_fmaf((float)d23[rg].x, S[rg].z, acc.z);
-                        acc.w = __builtin_fmaf((float)d23[rg].y, S[rg].w, acc.w);
+                        acc.x = __builtin_fmaf((float)d01[rg].x, S[mt][rg].x, acc.x);
+                        acc.y = __builtin_fmaf((float)d01[rg].y, S[mt][rg].y, acc.y);
+                        acc.z = __builtin_fmaf((float)d23[rg].x, S[mt][rg].z, acc.z);
+                        acc.w = __builtin_fmaf((float)d23[rg].y, S[mt][rg].w, acc.w);
                     }
-                }
             }
         }
-        if (j0 + nbc == nb) {   // the segment's last chunk: add its sum, in segment order
+    };
+
+    // the segment's last chunk: add its sum, in segment order
+    auto end_segment = [&]() {
 #pragma unroll
-            for (int rg = 0; rg < RG; ++rg)
+        for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    tot[rg][mt].x += seg[rg][mt].x;
-                    tot[rg][mt].y += seg[rg][mt].y;
-                    tot[rg][mt].z += seg[rg][mt].z;
-                    tot[rg][mt].w += seg[rg][mt].w;
-                    seg[rg][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                }
+            for (int mt = 0; mt < MT; ++mt) {
+                tot[rg][mt].x += seg[rg][mt].x;
+                tot[rg][mt].y += seg[rg][mt].y;
+                tot[rg][mt].z += seg[rg][mt].z;
+                tot[rg][mt].w += seg[rg][mt].w;
+                seg[rg][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+    };
+
+    // Step ci (ring buffer BUF = ci % 3): wait for chunk ci's loads (the LOADS
+    // of chunk ci + 1 may stay in flight), synchronise, then compute chunk ci
+    // and issue chunk ci + 2 into the buffers chunk ci - 1 used. FULL: chunks ci
+    // and ci + 2 lie in full segments or ci + 2 is past the range, BUF is a
+    // compile-time buffer, and the loads are spread over the chunk's blocks (past
+    // the range they re-read the range's first chunk into the free buffer, so
+    // every step issues the same loads).
+    auto step = [&](auto BUF, auto FULL, int ci) {
+        const int B = BUF;
+        if (ci + 1 < n)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        // Every wavefront's chunk-ci copies are in LDS once it passes its wait, and
+        // every wavefront is done reading chunk ci - 1's buffers (its reads fed the
+        // matrix cores in the previous step). A plain s_barrier: a fenced one
+        // would wait for the loads of chunk ci + 1 as well (they write LDS). The
+        // memory clobber keeps the compiler from moving LDS accesses across it.
+        asm volatile("s_barrier" ::: "memory");
+        if constexpr (decltype(FULL)::value) {
+            constexpr int BC = decltype(BUF)::value;
+            const int64_t ch2 = ci + kGemmDepth < n ? c_begin + ci + kGemmDepth : c_begin;
+            compute(BUF, IntC<CB>{}, [&](int jj) {
+                issue_full(IntC<(BC + kGemmDepth) % kGemmRing>{}, ch2, jj * LOADS / CB, (jj + 1) * LOADS / CB);
+            });
+            if (((c_begin + ci) & 7) == CPS - 1) end_segment();
+        } else {
+            if (ci + kGemmDepth < n) {
+                const int nb2 = B + kGemmDepth < kGemmRing ? B + kGemmDepth : B + kGemmDepth - kGemmRing;
+                issue(nb2, c_begin + ci + kGemmDepth);
+            }
+            const int64_t cc = c_begin + ci;
+            const int cj0 = (int)(cc & 7) * CB;
+            const int cnb = (cc >> 3) == nseg_last ? nb_last : kSegBlocks;
+            const int nbc = cnb - cj0 < CB ? cnb - cj0 : CB;
+            compute(B, nbc, [](int) {});
+            if (cj0 + nbc == cnb) end_segment();
         }
     };
-    int64_t ci = 0;
-    for (; ci + 1 < n_chunks; ci += 2) {
-        chunk_step(rawA, rawB, ci);
-        chunk_step(rawB, rawA, ci + 1);
+
+    // Chunks [0, n_full) of the range lie in full segments. The unrolled walk
+    // takes three steps at a time while the chunks it computes are full and the
+    // chunks it loads are full or past the range; the rest (a ragged last
+    // segment and the steps before it that load its chunks, one or two steps
+    // at the end) take the general step.
+    int n_full = n;
+    if (ragged) {
+        const int64_t f = nseg_last * CPS - c_begin;
+        n_full = f < 0 ? 0 : (f < n ? (int)f : n);
     }
-    if (ci < n_chunks) chunk_step(rawA, rawB, ci);
+    const int n_fast = n_full == n ? n : n_full - kGemmDepth;
+    if (n > 0) issue(IntC<0>{}, c_begin);
+    if (n > 1) issue(IntC<1>{}, c_begin + 1);
+    int ci = 0;
+    for (; ci + kGemmRing <= n_fast; ci += kGemmRing) {
+        step(IntC<0>{}, std::true_type{}, ci);
+        step(IntC<1>{}, std::true_type{}, ci + 1);
+        step(IntC<2>{}, std::true_type{}, ci + 2);
+    }
+    for (; ci < n; ++ci) step(ci % kGemmRing, std::false_type{}, ci);
+    // the unrolled walk's last steps may leave re-reads in flight: they write LDS
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+
+    // a range that ends inside a segment (K split) adds the segment's part
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            tot[rg][mt].x += seg[rg][mt].x;
+            tot[rg][mt].y += seg[rg][mt].y;
+            tot[rg][mt].z += seg[rg][mt].z;
+            tot[rg][mt].w += seg[rg][mt].w;
+        }
 
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int64_t m = (a.mt0 + mt) * 16 + i;
+        const int64_t m = (mt0 + mt) * 16 + i;
         if (m >= a.M) continue;
         const float us = unscale[m];
         // with K ranges, each range's sum goes to its own partial buffer (the
@@ -415,14 +573,13 @@ hipError_t launch_split_x(int qt, const float *X, _Float16 *xs, float *unscale, 
     return hipGetLastError();
 }
 
-template <int QT, int MT, int RG>
-static hipError_t launch_one(const uint8_t *wp, const _Float16 *xs, const float *unscale, float *Y,
-                             const GemmArgs &a, int G, hipStream_t s)
+template <int QT, int MT, int RG, int G>
+static hipError_t launch_one(int64_t row_blocks, const uint8_t *wp, const _Float16 *xs, const float *unscale, float *Y,
+                             const GemmArgs &a, hipStream_t s)
 {
-    auto kern = qgemm_kernel<QT, MT, RG>;
-    const int64_t grid = (a.geo.n_tiles + 2 * RG * G - 1) / (2 * RG * G);
-    const dim3 grid3((unsigned)grid, (unsigned)a.ksplit);
-    const size_t lds = gemm_lds_bytes(MT, G * 2 * RG);
+    auto kern = qgemm_kernel<QT, MT, RG, G>;
+    const dim3 grid3((unsigned)(row_blocks * a.n_mg), (unsigned)a.ksplit);
+    const size_t lds = gemm_lds_bytes(QT, MT, RG, G);
     static std::atomic<int> lds_set[16];
     hipError_t e = ensure_lds_limit((const void *)kern, lds, lds_set);
     if (e != hipSuccess) return e;
@@ -430,37 +587,46 @@ static hipError_t launch_one(const uint8_t *wp, const _Float16 *xs, const float 
     return hipGetLastError();
 }
 
-template <int QT, int MT>
-static hipError_t launch_rg(const uint8_t *wp, const _Float16 *xs, const float *unscale, float *Y, const GemmArgs &a,
-                            int RG, int G, hipStream_t s)
+template <int QT, int MT, int RG>
+static hipError_t launch_g(int G, int64_t rbs, const uint8_t *wp, const _Float16 *xs, const float *unscale, float *Y,
+                           const GemmArgs &a, hipStream_t s)
 {
-    switch (RG) {
-    case 1: return launch_one<QT, MT, 1>(wp, xs, unscale, Y, a, G, s);
-    case 2: return launch_one<QT, MT, 2>(wp, xs, unscale, Y, a, G, s);
-    default: return launch_one<QT, MT, 4>(wp, xs, unscale, Y, a, G, s);
+    switch (G) {
+    case 1: return launch_one<QT, MT, RG, 1>(rbs, wp, xs, unscale, Y, a, s);
+    case 2: return launch_one<QT, MT, RG, 2>(rbs, wp, xs, unscale, Y, a, s);
+    case 4: return launch_one<QT, MT, RG, 4>(rbs, wp, xs, unscale, Y, a, s);
+    case 8: return launch_one<QT, MT, RG, 8>(rbs, wp, xs, unscale, Y, a, s);
+    default: return hipErrorInvalidConfiguration;
     }
+}
+
+template <int QT, int MT>
+static hipError_t launch_rg(int RG, int G, int64_t rbs, const uint8_t *wp, const _Float16 *xs, const float *unscale,
+                            float *Y, const GemmArgs &a, hipStream_t s)
+{
+    if (RG == 1) return launch_g<QT, MT, 1>(G, rbs, wp, xs, unscale, Y, a, s);
+    if (RG == 2) return launch_g<QT, MT, 2>(G, rbs, wp, xs, unscale, Y, a, s);
+    return hipErrorInvalidConfiguration;
 }
 
 template <int QT>
-static hipError_t launch_mt(const uint8_t *wp, const _Float16 *xs, const float *unscale, float *Y, const GemmArgs &a,
-                            int MT, int RG, int G, hipStream_t s)
+static hipError_t launch_mt(int MT, int RG, int G, int64_t rbs, const uint8_t *wp, const _Float16 *xs,
+                            const float *unscale, float *Y, const GemmArgs &a, hipStream_t s)
 {
     switch (MT) {
-    case 1: return launch_rg<QT, 1>(wp, xs, unscale, Y, a, RG, G, s);
-    case 2: return launch_rg<QT, 2>(wp, xs, unscale, Y, a, RG, G, s);
-    case 3: return launch_one<QT, 3, 1>(wp, xs, unscale, Y, a, G, s);   // the tail pass of a 4-tile plan
-    default:
-        // four activation tiles: one or two row groups per wavefront (registers)
-        return RG == 1 ? launch_one<QT, 4, 1>(wp, xs, unscale, Y, a, G, s)
-                       : launch_one<QT, 4, 2>(wp, xs, unscale, Y, a, G, s);
+    case 1: return launch_rg<QT, 1>(RG, G, rbs, wp, xs, unscale, Y, a, s);
+    case 2: return launch_rg<QT, 2>(RG, G, rbs, wp, xs, unscale, Y, a, s);
+    case 3: return launch_rg<QT, 3>(RG, G, rbs, wp, xs, unscale, Y, a, s);
+    case 4: return launch_rg<QT, 4>(RG, G, rbs, wp, xs, unscale, Y, a, s);
+    default: return hipErrorInvalidConfiguration;
     }
 }
 
-hipError_t launch_qgemm(int qt, int MT, int RG, int G, const uint8_t *wp, const _Float16 *xs, const float *unscale,
-                        float *Y, const GemmArgs &a, hipStream_t s)
+hipError_t launch_qgemm(int qt, int MT, int RG, int G, int64_t row_blocks, const uint8_t *wp, const _Float16 *xs,
+                        const float *unscale, float *Y, const GemmArgs &a, hipStream_t s)
 {
-    if (qt == kQ8_0) return launch_mt<kQ8_0>(wp, xs, unscale, Y, a, MT, RG, G, s);
-    return launch_mt<kQ4_0>(wp, xs, unscale, Y, a, MT, RG, G, s);
+    if (qt == kQ8_0) return launch_mt<kQ8_0>(MT, RG, G, row_blocks, wp, xs, unscale, Y, a, s);
+    return launch_mt<kQ4_0>(MT, RG, G, row_blocks, wp, xs, unscale, Y, a, s);
 }
 
 }  // namespace qgk

@@ -408,51 +408,77 @@ void host_pack_rows(const Geometry &g, const uint8_t *canon, uint8_t *packed, in
             for (int64_t b = 0; b < g.KB; ++b) qgl::pack_block(g, nullptr, packed, r, b);
 }
 
-// Small-M GEMM: activation rows are processed in tiles of 16 (the last one
-// padded with zeros). The workspace holds, each part 256-byte aligned: one
-// unscale factor per padded row, the split activations (M_pad * K * 2
-// halves) and, when K is split across workgroups, the partial sums
-// (ksplit * M * N floats).
+// Small-M GEMM: activation rows are processed in tiles of 16, MT tiles per
+// workgroup (the last group padded with zero rows). The workspace holds, each
+// part 256-byte aligned: one unscale factor per padded row, the split
+// activations (M_pad * K * 2 halves) and, when K is split across workgroups,
+// the partial sums (ksplit * M * N floats).
 constexpr int64_t kGemmMaxM = (int64_t)1 << 20;
-
-int64_t gemm_m_pad(int64_t M) { return (M + qgk::kGemmTileM - 1) / qgk::kGemmTileM * qgk::kGemmTileM; }
 
 struct GemmPlan {
     int MT, RG, G;
-    int64_t ksplit;
+    int64_t n_mg, M_pad, row_blocks, ksplit;
     size_t off_xs, off_part, bytes;
 };
 
-// Launch plan of qgemm_prefill (depends on the shape and the device's CU count;
-// measured on MI355X): 4 wavefronts per workgroup, two (Q4_0) or four (Q8_0)
-// activation tiles per pass, two 16-row groups per wavefront (one where even a full K split would
-// leave fewer than two workgroups per CU), and the K segments split across
-// workgroups until there are about four workgroups per CU.
+// Launch plan of qgemm_prefill (depends on the shape and the device's CU count):
+//  - MT = min(4, activation tiles) tiles per workgroup, every group of MT tiles
+//    in the same dispatch (the weights of a row block are read once per group,
+//    by workgroups launched next to each other);
+//  - 8 wavefronts of two 16-row groups (256 weight rows) per workgroup, or 4
+//    wavefronts of two or one row group where the row blocks times the groups
+//    would not give two workgroups per CU, and fewer wavefronts where the
+//    staging ring would not fit in the LDS (Q8_0 with four activation tiles);
+//  - the K chunks split across workgroups (at least two chunks per range) until
+//    64-row blocks times ranges give about two workgroups per CU; the split
+//    depends on the weight's shape only, so M and the tiling never change a
+//    row's operations.
+// QG_GEMM_MT (1..4), QG_GEMM_WAVES (1, 2, 4, 8), QG_GEMM_ROWGROUPS (1, 2) and
+// QG_GEMM_KSPLIT override the choices for launch-shape sweeps.
 GemmPlan plan_gemm(int qt, int64_t N, int64_t K, int64_t M)
 {
     GemmPlan p;
     const Geometry g = qgl::geometry(qt, N, K);
-    p.G = 4;
-    const int64_t g_env = tune(kGemmWaves);
-    if (g_env >= 1 && g_env <= 4) p.G = (int)g_env;
-    const int64_t wgs_rg2 = (g.n_tiles + 4 * p.G - 1) / (4 * p.G);
-    p.RG = wgs_rg2 * g.nseg >= 2 * (int64_t)cu_count() ? 2 : 1;
-    const int64_t rg_env = tune(kGemmRowGroups);
-    if (rg_env == 1 || rg_env == 2 || rg_env == 4) p.RG = (int)rg_env;
-    // activation tiles per pass: 4, i.e. the weights are streamed once per 64 activation rows
-    // (measured with the double-buffered staging, cold, against 2: Q4_0 LM head 248320x5120
-    // at M = 128 1300 -> 1100 us, 17408x5120 138 -> 132 us; Q8_0 4096x1024 74 -> 50 us)
-    p.MT = 4;
+    const int64_t n_mt = (M + qgk::kGemmTileM - 1) / qgk::kGemmTileM;
+    p.MT = (int)std::min<int64_t>(qgk::kGemmMaxMT, n_mt);
     const int64_t mt_env = tune(kGemmMT);
     if (mt_env >= 1 && mt_env <= qgk::kGemmMaxMT) p.MT = (int)mt_env;
-    const int64_t wgs = (g.n_tiles + 2 * p.RG * p.G - 1) / (2 * p.RG * p.G);
-    const int64_t want = 4 * (int64_t)cu_count();
-    p.ksplit = wgs < want ? std::min<int64_t>(g.nseg, (want + wgs - 1) / wgs) : 1;
+    p.n_mg = (n_mt + p.MT - 1) / p.MT;
+    p.M_pad = p.n_mg * p.MT * qgk::kGemmTileM;
+    const int64_t cus = cu_count();
+    auto rbs = [&](int G, int RG) { return (g.n_tiles + 2 * RG * G - 1) / (2 * RG * G); };
+    constexpr int CPS = qgl::kSegBlocks / qgk::kGemmChunk;
+    const int64_t n_chunks =
+        (g.nseg - 1) * CPS + (qgl::seg_blocks(g, g.nseg - 1) + qgk::kGemmChunk - 1) / qgk::kGemmChunk;
+    // The K split changes a row's rounding, so it depends on the weight's shape
+    // alone (never on M or the tiling): enough 64-row blocks x K ranges for two
+    // workgroups per CU, at least two chunks per range.
+    const int64_t fine = rbs(4, 1);
+    p.ksplit = fine < 2 * cus ? std::min<int64_t>(std::max<int64_t>(n_chunks / 2, 1), (2 * cus + fine - 1) / fine) : 1;
     const int64_t ks_env = tune(kGemmKSplit);
-    if (ks_env >= 1) p.ksplit = std::min<int64_t>(g.nseg, ks_env);
-    const int64_t M_pad = gemm_m_pad(M);
-    p.off_xs = (size_t)qgl::round_up(M_pad * (int64_t)sizeof(float), 256);
-    p.off_part = p.off_xs + (size_t)qgl::round_up(M_pad * K * 2 * (int64_t)sizeof(_Float16), 256);
+    if (ks_env >= 1) p.ksplit = std::min<int64_t>(n_chunks, ks_env);
+    // Eight wavefronts over two row groups share each staged activation chunk
+    // between 32 rows (Q4_0); Q8_0's doubled weight bytes make the second row
+    // group cost more than it saves. Fewer rows per workgroup only where the
+    // launch would otherwise leave CUs idle. Measured on MI355X (us, 8 / 4
+    // wavefronts x 2 / 1 row groups): Q4_0 248320 x 5120 M=128 906 / 1204 (8x1)
+    // / 1855 (4x1); Q4_0 5120 x 17408 M=128 139 / 140 (8x1) / 183 (4x1); Q8_0
+    // 151936 x 1024 M=128 224 (8x1) / 237 (4x2); Q8_0 4096 x 1024 M=16 11.9 (4x1)
+    // / 12.8 (8x1).
+    auto wgs = [&](int G, int RG) { return rbs(G, RG) * p.n_mg * p.ksplit; };
+    p.G = 8;
+    p.RG = qt == qgl::kQ8_0 ? 1 : 2;
+    if (p.RG == 2 && wgs(8, 2) < cus) p.RG = 1;
+    if (wgs(8, p.RG) < cus) p.G = 4;
+    const int64_t g_env = tune(kGemmWaves);
+    if (g_env == 1 || g_env == 2 || g_env == 4 || g_env == 8) p.G = (int)g_env;
+    const int64_t rg_env = tune(kGemmRowGroups);
+    if (rg_env == 1 || rg_env == 2) p.RG = (int)rg_env;
+    // the staging ring must fit in the LDS of one workgroup (Q8_0 weights take twice Q4_0's)
+    while (p.G > 1 && qgk::gemm_lds_bytes(qt, p.MT, p.RG, p.G) > qgk::kLdsPerWorkgroup) p.G /= 2;
+    p.row_blocks = rbs(p.G, p.RG);
+    p.off_xs = (size_t)qgl::round_up(p.M_pad * (int64_t)sizeof(float), 256);
+    p.off_part = p.off_xs + (size_t)qgl::round_up(p.M_pad * K * 2 * (int64_t)sizeof(_Float16), 256);
     p.bytes = p.off_part + (p.ksplit > 1 ? (size_t)p.ksplit * (size_t)M * (size_t)N * sizeof(float) : 0);
     return p;
 }
@@ -511,27 +537,22 @@ qg_status run_prefill(int qtype, const void *w_packed, const float *X, float *Y,
 {
     const GemmPlan p = plan_gemm(qtype, N, K, M);
     const Geometry g = qgl::geometry(qtype, N, K);
-    const int64_t M_pad = gemm_m_pad(M);
     float *unscale = (float *)workspace;
     _Float16 *xs = (_Float16 *)((uint8_t *)workspace + p.off_xs);
     hipStream_t s = as_stream(stream);
-    // the split pass is not timed: a bound event pair goes to the first GEMM pass
-    hipError_t e = qgk::launch_split_x(qtype, X, xs, unscale, M, M_pad, K, s);
+    // the split pass is not timed: a bound event pair goes to the GEMM
+    hipError_t e = qgk::launch_split_x(qtype, X, xs, unscale, M, p.M_pad, K, s);
     if (e != hipSuccess) return hip_fail(e, fn);
-    const int64_t n_mt = M_pad / qgk::kGemmTileM;
     qgk::GemmArgs a;
     a.geo = g;
     a.N = N;
     a.M = M;
+    a.n_mg = p.n_mg;
     a.y_stride = N;
     a.ksplit = p.ksplit;
     a.part = p.ksplit > 1 ? (float *)((uint8_t *)workspace + p.off_part) : nullptr;
-    for (int64_t mt0 = 0; mt0 < n_mt; mt0 += p.MT) {
-        a.mt0 = mt0;
-        const int mt = (int)std::min<int64_t>(p.MT, n_mt - mt0);
-        e = qgk::launch_qgemm(qtype, mt, p.RG, p.G, (const uint8_t *)w_packed, xs, unscale, Y, a, s);
-        if (e != hipSuccess) return hip_fail(e, fn);
-    }
+    e = qgk::launch_qgemm(qtype, p.MT, p.RG, p.G, p.row_blocks, (const uint8_t *)w_packed, xs, unscale, Y, a, s);
+    if (e != hipSuccess) return hip_fail(e, fn);
     if (p.ksplit > 1) {
         e = qgk::launch_ksum(a.part, Y, p.ksplit, M, N, s);
         if (e != hipSuccess) return hip_fail(e, fn);

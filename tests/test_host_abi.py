@@ -270,12 +270,16 @@ def test_rmsnorm_argument_checks_without_gpu(L):
 def test_gemm_argument_checks_without_gpu(L):
     f = FAKE
     w, x, y, ws = f, f + (1 << 24), f + (2 << 24), f + (3 << 24)
-    # 20 rows padded to 32: one 256-byte block of row factors and 32 x 1024 x 4 bytes of split activations;
-    # a 64-row weight (8 row tiles, one workgroup) splits K only when it has several segments
+    # 20 rows padded to 32 (one group of two 16-row tiles): one 256-byte block of row factors and
+    # 32 x 1024 x 4 bytes of split activations; a 64-row weight makes one workgroup, so K is split
+    # into ranges of at least two 4-block chunks (32 blocks -> 4 ranges, 128 blocks -> 16), each
+    # range with its M x N partial sums
     need = qg.qg_prefill_workspace_size("q8_0", 64, 1024, 20)
-    assert need == 256 + 32 * 1024 * 4
+    assert need == 256 + 32 * 1024 * 4 + 4 * 20 * 64 * 4
     with_split = qg.qg_prefill_workspace_size("q8_0", 64, 4096, 20)
-    assert with_split == 256 + 32 * 4096 * 4 + 4 * 20 * 64 * 4      # 4 segments -> 4 K ranges of partial sums
+    assert with_split == 256 + 32 * 4096 * 4 + 16 * 20 * 64 * 4
+    # 70 rows: two groups of four tiles (128 padded rows); a weight with enough row blocks is not split
+    assert qg.qg_prefill_workspace_size("q4_0", 248320, 5120, 70) == 512 + 128 * 5120 * 4
     assert qg.qg_prefill_workspace_size("q8_0", 64, 1024, 0) == 0
     assert qg.qg_prefill_workspace_size("q8_0", 64, 1000, 4) == 0
     assert qg.qg_prefill_workspace_size(3, 64, 1024, 4) == 0
@@ -309,10 +313,10 @@ def test_prefill_noalloc_checks_without_gpu(L):
     assert na(2, w, x, x + 64, 64, 1024, 20, None) == qg.QG_EINVAL               # Y overlaps X
     assert na(3, w, x, y, 64, 1024, 20, None) == qg.QG_EUNSUPPORTED              # Q4_K: GEMV only
     assert na(1, w, x, y, 64, 1000, 20, None) == qg.QG_EINVAL                    # K % 32
-    # Q4_0 5120 x 17408 at M = 256 needs 17 K ranges of partials: about 107 MB
-    need = qg.qg_prefill_workspace_size("q4_0", 5120, 17408, 256)
+    # Q4_0 5120 x 17408 at M = 1024: 1024 x 17408 x 4 bytes of split activations alone (71 MB)
+    need = qg.qg_prefill_workspace_size("q4_0", 5120, 17408, 1024)
     assert need > qg.QG_PREFILL_NOALLOC_MAX_BYTES
-    assert na(2, w, x, f + (1 << 34), 5120, 17408, 256, None) == qg.QG_EUNSUPPORTED
+    assert na(2, w, x, f + (1 << 34), 5120, 17408, 1024, None) == qg.QG_EUNSUPPORTED
     assert "qg_prefill_workspace_size" in qg.qg_last_error()
 
 

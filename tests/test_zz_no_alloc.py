@@ -13,8 +13,9 @@ from gpu_helpers import THREADS, announce, assert_linear, empty_f32, sync, to_de
 
 pytestmark = pytest.mark.gpu
 
-# The first call splits K across workgroups (17 K ranges of partial sums in the
-# scratch) over 40 activation rows; the second is smaller: 5 rows, one K range.
+# The first call splits K across workgroups (K ranges of partial sums in the
+# scratch) over 40 activation rows; the second is smaller: 5 rows of a
+# 1000-row weight.
 CASES = [("q4_0", 5120, 17408, 40, 81), ("q8_0", 1000, 1024, 5, 82)]
 
 
@@ -36,7 +37,8 @@ def test_prefill_noalloc_matches_workspace_call_twice():
         sync()
         a_ws, a_na = y_ws.cpu().numpy(), y_na.cpu().numpy()
         assert np.all(a_na[M * N:] == -3.0), "wrote past Y"
-        assert a_na[:M * N].tobytes() == a_ws[:M * N].tobytes(), f"{kind} {N}x{K} M={M}: differs from qgemm_prefill"
+        assert np.array_equal(a_na[:M * N].view(np.uint32), a_ws[:M * N].view(np.uint32)), \
+            f"{kind} {N}x{K} M={M}: differs from qgemm_prefill"
         Y = a_na[:M * N].reshape(M, N)
         for m in range(M):
             y_ref, a_ref = O.gemv(kind, canon, np.ascontiguousarray(X[m]), N, K, threads=THREADS)
