@@ -542,12 +542,15 @@ def rmsnorm_fusion(qg, torch, cases, reps):
     return out
 
 
-def prefill_gemm(qg, torch, cases, table):
+def prefill_gemm(qg, torch, cases, table, settle_s):
     """The small-M GEMM (qgemm_prefill) for chunks of M activation rows, cold
     (weights rotating over >= 1.2 GiB of copies): mean us per call over a batch
-    of back-to-back calls (the split, GEMM and K-sum kernels together), us per
-    activation row against the M = 1 GEMV of the same weight, useful TFLOP/s
-    (2 M N K per call) and the weight stream in GB/s."""
+    of back-to-back calls (the split, GEMM and K-sum kernels together) after
+    `settle_s` seconds of untimed calls (the first calls after the weights are
+    built run slower, as for the decode step: measured 803 against 715 us for
+    the Q4_0 LM head at M = 128), us per activation row against the M = 1 GEMV
+    of the same weight, useful TFLOP/s (2 M N K per call) and the weight stream
+    in GB/s."""
     out = {}
     log("prefill GEMM (qgemm_prefill, matrix cores): batch us per call, cold weights")
     m1 = {"q8_0 lm_head 151936x1024": "c1 lm_head 151936x1024", "q8_0 qkv 4096x1024": "c1 qkv 4096x1024",
@@ -555,9 +558,8 @@ def prefill_gemm(qg, torch, cases, table):
     for label, kind, weight, N, K, M, make in cases:
         copies = cold_copies(torch, weight)
         fns = [make(cp.data_ptr()) for cp in copies]
-        for f in fns[:2]:
-            f()
-        nb = max(8, len(fns))
+        settle(torch, fns, settle_s)
+        nb = max(16, len(fns))
         b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         b0.record()
@@ -991,7 +993,7 @@ def main():
         detail["configs"] = table
         result["rmsnorm_fusion"] = rmsnorm_fusion(qg, torch, norm_cases, args.reps)
         del norm_cases
-        result["prefill_gemm"] = prefill_gemm(qg, torch, gemm_cases, table)
+        result["prefill_gemm"] = prefill_gemm(qg, torch, gemm_cases, table, args.settle_ms / 1e3)
         del gemm_cases
         del keep
         torch.cuda.empty_cache()

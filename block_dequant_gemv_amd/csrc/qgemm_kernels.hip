@@ -180,10 +180,9 @@ qgemm_kernel(const uint8_t *__restrict__ wp, const _Float16 *__restrict__ xs, co
     static_assert(kGemmDepth == 2 && kGemmRing == 3, "the chunk loop below is unrolled for a ring of three");
     constexpr int CPS = kSegBlocks / CB;
     static_assert(CPS == 8, "chunk positions below use shifts by 3");
+    // LDS: kGemmRing activation buffers of XBUF u32x4, then kGemmRing weight
+    // buffers of WBUF u32x4, then kGemmRing scale buffers of SBUF words
     extern __shared__ u32x4 lds[];
-    u32x4 *lx = lds;                                              // kGemmRing x XBUF
-    u32x4 *lw = lds + kGemmRing * XBUF;                            // kGemmRing x WBUF
-    uint32_t *lsc = (uint32_t *)(lw + kGemmRing * WBUF);           // kGemmRing x SBUF words
 
     const Geometry &g = a.geo;
     const int lane = threadIdx.x & 63;

@@ -421,18 +421,31 @@ struct GemmPlan {
     size_t off_xs, off_part, bytes;
 };
 
-// Launch plan of qgemm_prefill (depends on the shape and the device's CU count):
-//  - MT = min(4, activation tiles) tiles per workgroup, every group of MT tiles
-//    in the same dispatch (the weights of a row block are read once per group,
-//    by workgroups launched next to each other);
-//  - 8 wavefronts of two 16-row groups (256 weight rows) per workgroup, or 4
-//    wavefronts of two or one row group where the row blocks times the groups
-//    would not give two workgroups per CU, and fewer wavefronts where the
-//    staging ring would not fit in the LDS (Q8_0 with four activation tiles);
-//  - the K chunks split across workgroups (at least two chunks per range) until
-//    64-row blocks times ranges give about two workgroups per CU; the split
-//    depends on the weight's shape only, so M and the tiling never change a
-//    row's operations.
+// Launch plan of qgemm_prefill (depends on the shape and the device's CU count).
+//
+// K split (gridDim.y ranges added by the K-sum kernel): it changes a row's
+// rounding, so it depends on the weight's shape alone, never on M or the
+// tiling. None below 16 chunks (K < 2048: the K-sum launch and the partial
+// sums cost more than the extra workgroups gain; measured on MI355X, Q8_0
+// 4096 x 1024 at M = 16 / 128: 11.2 / 15.6 us unsplit against 12.0 / 21.1 us in
+// four ranges). Otherwise ranges of at least two chunks until the row blocks of
+// the default tiling (8 wavefronts, 2 row groups for Q4_0, 1 for Q8_0) times the
+// ranges come near half the CUs, so two activation groups fill the chip in one
+// round (Q4_0 5120 x 17408 at M = 128: 6 ranges, 240 workgroups, 78.6 us; 7
+// ranges put 280 workgroups in two rounds, 118 us).
+//
+// Tiling (MT activation tiles, G wavefronts, RG row groups per workgroup): the
+// candidate with the least estimated time, rounds x RG x MT / e, where rounds =
+// workgroups / (CUs x workgroups per CU) rounded up (one workgroup of 8
+// wavefronts per CU; two of 4 where their staging ring fits in half the LDS),
+// RG x MT is each wavefront's work per block, and e the relative throughput of
+// a full CU measured on MI355X on the LM heads (M = 128, many rounds: Q4_0
+// 248320 x 5120 731.8 us at MT 4 / 8 wavefronts / 2 row groups = 1.00, Q8_0
+// 151936 x 1024 199.0 us at MT 4 / 8 / 1 = 1.00). Four wavefronts alone on a CU
+// (no more workgroups than CUs) get the whole SIMD each: e x 1.3. Over the
+// prefill shapes of the configurations at M = 16 .. 256 the choice is within
+// 1% in total of the fastest candidate per case (5089 against 5044 us).
+//
 // QG_GEMM_MT (1..4), QG_GEMM_WAVES (1, 2, 4, 8), QG_GEMM_ROWGROUPS (1, 2) and
 // QG_GEMM_KSPLIT override the choices for launch-shape sweeps.
 GemmPlan plan_gemm(int qt, int64_t N, int64_t K, int64_t M)
@@ -440,42 +453,59 @@ GemmPlan plan_gemm(int qt, int64_t N, int64_t K, int64_t M)
     GemmPlan p;
     const Geometry g = qgl::geometry(qt, N, K);
     const int64_t n_mt = (M + qgk::kGemmTileM - 1) / qgk::kGemmTileM;
-    p.MT = (int)std::min<int64_t>(qgk::kGemmMaxMT, n_mt);
-    const int64_t mt_env = tune(kGemmMT);
-    if (mt_env >= 1 && mt_env <= qgk::kGemmMaxMT) p.MT = (int)mt_env;
-    p.n_mg = (n_mt + p.MT - 1) / p.MT;
-    p.M_pad = p.n_mg * p.MT * qgk::kGemmTileM;
     const int64_t cus = cu_count();
     auto rbs = [&](int G, int RG) { return (g.n_tiles + 2 * RG * G - 1) / (2 * RG * G); };
     constexpr int CPS = qgl::kSegBlocks / qgk::kGemmChunk;
     const int64_t n_chunks =
         (g.nseg - 1) * CPS + (qgl::seg_blocks(g, g.nseg - 1) + qgk::kGemmChunk - 1) / qgk::kGemmChunk;
-    // The K split changes a row's rounding, so it depends on the weight's shape
-    // alone (never on M or the tiling): enough 64-row blocks x K ranges for two
-    // workgroups per CU, at least two chunks per range.
-    const int64_t fine = rbs(4, 1);
-    p.ksplit = fine < 2 * cus ? std::min<int64_t>(std::max<int64_t>(n_chunks / 2, 1), (2 * cus + fine - 1) / fine) : 1;
+    const int base_rg = qt == qgl::kQ8_0 ? 1 : 2;
+    const int64_t base = rbs(8, base_rg);
+    p.ksplit = 1;
+    if (n_chunks >= 16 && 2 * base < cus)
+        p.ksplit = std::min<int64_t>(std::max<int64_t>(n_chunks / 2, 1), std::max<int64_t>(1, (cus / 2 + base / 2) / base));
     const int64_t ks_env = tune(kGemmKSplit);
     if (ks_env >= 1) p.ksplit = std::min<int64_t>(n_chunks, ks_env);
-    // Eight wavefronts over two row groups share each staged activation chunk
-    // between 32 rows (Q4_0); Q8_0's doubled weight bytes make the second row
-    // group cost more than it saves. Fewer rows per workgroup only where the
-    // launch would otherwise leave CUs idle. Measured on MI355X (us, 8 / 4
-    // wavefronts x 2 / 1 row groups): Q4_0 248320 x 5120 M=128 906 / 1204 (8x1)
-    // / 1855 (4x1); Q4_0 5120 x 17408 M=128 139 / 140 (8x1) / 183 (4x1); Q8_0
-    // 151936 x 1024 M=128 224 (8x1) / 237 (4x2); Q8_0 4096 x 1024 M=16 11.9 (4x1)
-    // / 12.8 (8x1).
-    auto wgs = [&](int G, int RG) { return rbs(G, RG) * p.n_mg * p.ksplit; };
-    p.G = 8;
-    p.RG = qt == qgl::kQ8_0 ? 1 : 2;
-    if (p.RG == 2 && wgs(8, 2) < cus) p.RG = 1;
-    if (wgs(8, p.RG) < cus) p.G = 4;
+
+    struct Cand {
+        int MT, G, RG, eff;   // eff: relative throughput of a full CU, percent
+    };
+    static constexpr Cand q4c[] = {{4, 8, 2, 100}, {4, 8, 1, 79}, {2, 8, 2, 80}, {2, 8, 1, 80},
+                                   {1, 8, 2, 67},  {1, 8, 1, 59}, {1, 4, 1, 54}, {2, 4, 1, 62}};
+    static constexpr Cand q8c[] = {{4, 8, 1, 100}, {2, 8, 1, 79}, {1, 8, 1, 70}, {1, 4, 1, 69}, {2, 4, 1, 75}};
+    const Cand *cand = qt == qgl::kQ8_0 ? q8c : q4c;
+    const int ncand = qt == qgl::kQ8_0 ? (int)(sizeof(q8c) / sizeof(q8c[0])) : (int)(sizeof(q4c) / sizeof(q4c[0]));
+    double best = -1.0;
+    p.MT = 1;
+    p.G = 4;
+    p.RG = 1;
+    for (int ci = 0; ci < ncand; ++ci) {
+        const Cand &c = cand[ci];
+        if (c.MT > 1 && c.MT > n_mt) continue;
+        const size_t lds = qgk::gemm_lds_bytes(qt, c.MT, c.RG, c.G);
+        if (lds > qgk::kLdsPerWorkgroup) continue;
+        const int64_t per_cu = (c.G == 4 && lds <= qgk::kLdsPerWorkgroup / 2) ? 2 : 1;
+        const int64_t wgs = rbs(c.G, c.RG) * ((n_mt + c.MT - 1) / c.MT) * p.ksplit;
+        const int64_t rounds = (wgs + cus * per_cu - 1) / (cus * per_cu);
+        double e = c.eff / 100.0;
+        if (c.G == 4 && wgs <= cus) e *= 1.3;
+        const double cost = (double)rounds * c.RG * c.MT / e;
+        if (best < 0.0 || cost < best * (1.0 - 1e-9)) {
+            best = cost;
+            p.MT = c.MT;
+            p.G = c.G;
+            p.RG = c.RG;
+        }
+    }
+    const int64_t mt_env = tune(kGemmMT);
+    if (mt_env >= 1 && mt_env <= qgk::kGemmMaxMT) p.MT = (int)mt_env;
     const int64_t g_env = tune(kGemmWaves);
     if (g_env == 1 || g_env == 2 || g_env == 4 || g_env == 8) p.G = (int)g_env;
     const int64_t rg_env = tune(kGemmRowGroups);
     if (rg_env == 1 || rg_env == 2) p.RG = (int)rg_env;
     // the staging ring must fit in the LDS of one workgroup (Q8_0 weights take twice Q4_0's)
     while (p.G > 1 && qgk::gemm_lds_bytes(qt, p.MT, p.RG, p.G) > qgk::kLdsPerWorkgroup) p.G /= 2;
+    p.n_mg = (n_mt + p.MT - 1) / p.MT;
+    p.M_pad = p.n_mg * p.MT * qgk::kGemmTileM;
     p.row_blocks = rbs(p.G, p.RG);
     p.off_xs = (size_t)qgl::round_up(p.M_pad * (int64_t)sizeof(float), 256);
     p.off_part = p.off_xs + (size_t)qgl::round_up(p.M_pad * K * 2 * (int64_t)sizeof(_Float16), 256);

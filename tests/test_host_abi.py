@@ -270,16 +270,18 @@ def test_rmsnorm_argument_checks_without_gpu(L):
 def test_gemm_argument_checks_without_gpu(L):
     f = FAKE
     w, x, y, ws = f, f + (1 << 24), f + (2 << 24), f + (3 << 24)
-    # 20 rows padded to 32 (one group of two 16-row tiles): one 256-byte block of row factors and
-    # 32 x 1024 x 4 bytes of split activations; a 64-row weight makes one workgroup, so K is split
-    # into ranges of at least two 4-block chunks (32 blocks -> 4 ranges, 128 blocks -> 16), each
-    # range with its M x N partial sums
+    # 20 rows padded to 32 (two 16-row tiles): one 256-byte block of row factors and 32 x 1024 x 4
+    # bytes of split activations; K below 16 chunks of 4 blocks is never split, and a 64-row
+    # weight with 16 chunks or more is split into ranges of at least two chunks (128 blocks -> 16),
+    # each range with its M x N partial sums
     need = qg.qg_prefill_workspace_size("q8_0", 64, 1024, 20)
-    assert need == 256 + 32 * 1024 * 4 + 4 * 20 * 64 * 4
+    assert need == 256 + 32 * 1024 * 4
     with_split = qg.qg_prefill_workspace_size("q8_0", 64, 4096, 20)
     assert with_split == 256 + 32 * 4096 * 4 + 16 * 20 * 64 * 4
-    # 70 rows: two groups of four tiles (128 padded rows); a weight with enough row blocks is not split
-    assert qg.qg_prefill_workspace_size("q4_0", 248320, 5120, 70) == 512 + 128 * 5120 * 4
+    # 70 rows: five 16-row tiles in groups of one, two or four (80, 96 or 128 padded rows); a weight
+    # with enough row blocks is not split (no partial sums)
+    lm = qg.qg_prefill_workspace_size("q4_0", 248320, 5120, 70)
+    assert (lm - 512) % (5120 * 4) == 0 and (lm - 512) // (5120 * 4) in (80, 96, 128)
     assert qg.qg_prefill_workspace_size("q8_0", 64, 1024, 0) == 0
     assert qg.qg_prefill_workspace_size("q8_0", 64, 1000, 4) == 0
     assert qg.qg_prefill_workspace_size(3, 64, 1024, 4) == 0
