@@ -50,10 +50,13 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 // the last 16-row tile are written as zeros). Writes unscale[m] = 2^-e and the
 // fp16 parts in B-operand order: xs[((mt * KB + b) * 2 + h) * 512 + lane * 8 + e]
 // with mt = m / 16, lane = 16 c + m % 16, h = 0 (hi) / 1 (lo), where (c, e)
-// is the position of the block's element in its lane (see above).
-constexpr int kSplitThreads = 1024;   // one workgroup per activation row
+// is the position of the block's element in its lane (see above). Each thread
+// takes whole lane runs (block b, chunk c: the 8 elements one MFMA lane holds)
+// and writes their hi and lo parts as two 16-byte stores; VEC: the row is
+// 16-byte aligned and read with 16-byte loads.
+constexpr int kSplitThreads = 256;
 
-template <int QT>
+template <int QT, bool VEC>
 __global__ void __launch_bounds__(kSplitThreads)
 split_x_kernel(const float *__restrict__ X, _Float16 *__restrict__ xs, float *__restrict__ unscale, int64_t M,
                int64_t K)
@@ -64,8 +67,18 @@ split_x_kernel(const float *__restrict__ X, _Float16 *__restrict__ xs, float *__
     const bool live = m < M;
     const float *xr = X + m * K;
     float mx = 0.0f;
-    if (live)
-        for (int64_t k = tid; k < K; k += kSplitThreads) mx = __builtin_fmaxf(mx, __builtin_fabsf(xr[k]));
+    if (live) {
+        if (VEC) {
+            const f32x4 *x4 = (const f32x4 *)xr;
+            for (int64_t k = tid; k < K / 4; k += kSplitThreads) {
+                const f32x4 v = x4[k];
+                mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)),
+                                                         __builtin_fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w))));
+            }
+        } else {
+            for (int64_t k = tid; k < K; k += kSplitThreads) mx = __builtin_fmaxf(mx, __builtin_fabsf(xr[k]));
+        }
+    }
     // workgroup maximum (max is exact, so the order does not matter)
     for (int o = 32; o >= 1; o >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o));
     if ((tid & 63) == 0) red[tid >> 6] = mx;
@@ -85,23 +98,40 @@ split_x_kernel(const float *__restrict__ X, _Float16 *__restrict__ xs, float *__
     const int64_t KB = K / 32;
     const int64_t mt = m >> 4;
     const int mi = (int)(m & 15);
-    for (int64_t k = tid; k < K; k += kSplitThreads) {
-        const float v = live ? xr[k] * sc : 0.0f;
-        const _Float16 hi = (_Float16)v;
-        const _Float16 lo = (_Float16)(v - (float)hi);
-        const int64_t b = k >> 5;
-        const int p = (int)(k & 31);
-        int c, el;
-        if (QT == kQ4_0) {
-            c = p >> 3;
-            el = p & 7;
+    // lane run u = (block b, chunk c): Q4_0 elements 8c..8c+7 of the block,
+    // Q8_0 elements 4c..4c+3 and 16+4c..16+4c+3
+    for (int64_t u = tid; u < KB * 4; u += kSplitThreads) {
+        const int64_t b = u >> 2;
+        const int c = (int)(u & 3);
+        const int64_t k0 = b * 32 + (QT == kQ4_0 ? 8 * c : 4 * c);
+        const int64_t k1 = QT == kQ4_0 ? k0 + 4 : k0 + 16;
+        float v[8];
+        if (!live) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+        } else if (VEC) {
+            const f32x4 a0 = *(const f32x4 *)(xr + k0);
+            const f32x4 a1 = *(const f32x4 *)(xr + k1);
+            v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
+            v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
         } else {
-            c = (p & 15) >> 2;
-            el = (p & 3) + (p >= 16 ? 4 : 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[j] = xr[k0 + j];
+                v[4 + j] = xr[k1 + j];
+            }
         }
-        const int64_t at = ((mt * KB + b) * 2) * 512 + (int64_t)(c * 16 + mi) * 8 + el;
-        xs[at] = hi;
-        xs[at + 512] = lo;
+        h8 hi, lo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float t = v[j] * sc;
+            const _Float16 h = (_Float16)t;
+            hi[j] = h;
+            lo[j] = (_Float16)(t - (float)h);
+        }
+        _Float16 *dst = xs + ((mt * KB + b) * 2) * 512 + (int64_t)(c * 16 + mi) * 8;
+        *(h8 *)dst = hi;
+        *(h8 *)(dst + 512) = lo;
     }
 }
 
@@ -563,12 +593,19 @@ hipError_t launch_ksum(const float *part, float *Y, int64_t ksplit, int64_t M, i
 hipError_t launch_split_x(int qt, const float *X, _Float16 *xs, float *unscale, int64_t M, int64_t M_pad, int64_t K,
                           hipStream_t s)
 {
-    if (qt == kQ8_0)
-        hipLaunchKernelGGL(split_x_kernel<kQ8_0>, dim3((unsigned)M_pad), dim3(kSplitThreads), 0, s, X, xs, unscale,
-                           M, K);
-    else
-        hipLaunchKernelGGL(split_x_kernel<kQ4_0>, dim3((unsigned)M_pad), dim3(kSplitThreads), 0, s, X, xs, unscale,
-                           M, K);
+    const bool vec = ((uintptr_t)X & 15) == 0;   // rows are K * 4 bytes, a multiple of 128
+    const dim3 grid((unsigned)M_pad), block(kSplitThreads);
+    if (qt == kQ8_0) {
+        if (vec)
+            hipLaunchKernelGGL((split_x_kernel<kQ8_0, true>), grid, block, 0, s, X, xs, unscale, M, K);
+        else
+            hipLaunchKernelGGL((split_x_kernel<kQ8_0, false>), grid, block, 0, s, X, xs, unscale, M, K);
+    } else {
+        if (vec)
+            hipLaunchKernelGGL((split_x_kernel<kQ4_0, true>), grid, block, 0, s, X, xs, unscale, M, K);
+        else
+            hipLaunchKernelGGL((split_x_kernel<kQ4_0, false>), grid, block, 0, s, X, xs, unscale, M, K);
+    }
     return hipGetLastError();
 }
 

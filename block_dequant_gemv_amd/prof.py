@@ -2,7 +2,7 @@
 
     python -m block_dequant_gemv_amd.prof trace  <dir> [--skip N] [--tail N]   # --kernel-trace --stats -f csv
     python -m block_dequant_gemv_amd.prof counters <dir>
-    python -m block_dequant_gemv_amd.prof collect <out_dir> [--only trace_step,trace_calls,traffic,sq]
+    python -m block_dequant_gemv_amd.prof collect <out_dir> [--only trace_step,trace_calls,traffic,sq,trace_gemm,gemm_sq]
     python -m block_dequant_gemv_amd.prof traffic <fetch_dir> <write_dir> [--json out.json]
                                               [--call LABEL=KERNEL|WORKGROUPSxWG ...]
 
@@ -28,6 +28,11 @@ child process of its own under `timeout -s KILL`, the program after `--`):
                configurations' calls (bench.py ... --calib-copy)
   sq           --pmc SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_BUSY_CYCLES
                SQ_INSTS_LDS GRBM_GUI_ACTIVE --kernel-trace, same calls
+  trace_gemm   --kernel-trace --stats of the prefill GEMM rows
+               (bench.py --no-cpu --no-graph --no-q8-step --only "g ")
+  gemm_sq      --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES
+               SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_SALU SQ_INSTS_LDS GRBM_GUI_ACTIVE
+               --kernel-trace, the same GEMM rows
 and writes <out>/*.txt summaries that start with the command that made them.
 
 `traffic` reads two counter runs (--pmc FETCH_SIZE, then --pmc WRITE_SIZE; the
@@ -165,7 +170,11 @@ def counter_summary(directory: str) -> str:
                 "the dispatch, so short kernels read high)" if "GRBM_GUI_ACTIVE" in names else "")
              + (";\nvalu_per_wave = SQ_INSTS_VALU / SQ_WAVES" if {"SQ_WAVES", "SQ_INSTS_VALU"} <= names else "")
              + (";\nvalu_busy = SQ_INSTS_VALU x 4 cycles (a wave64 instruction on a 16-lane SIMD) / (1024 SIMDs x "
-                "GRBM_GUI_ACTIVE / 8)" if {"GRBM_GUI_ACTIVE", "SQ_INSTS_VALU"} <= names else "")]
+                "GRBM_GUI_ACTIVE / 8)" if {"GRBM_GUI_ACTIVE", "SQ_INSTS_VALU"} <= names else "")
+             + (";\nmfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8); valu_per_mfma = "
+                "(SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA (SQ_INSTS_VALU counts the MFMA instructions too); "
+                "coexec = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES"
+                if {"GRBM_GUI_ACTIVE", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES"} <= names else "")]
     head = f"{'kernel':58s} {'wgs':>7s} {'wg':>5s} {'n':>4s} {'us':>9s} " + " ".join(f"{c:>20s}" for c in cols)
     extra = []
     if "GRBM_GUI_ACTIVE" in names:
@@ -174,6 +183,10 @@ def counter_summary(directory: str) -> str:
         extra.append("valu_per_wave")
     if {"GRBM_GUI_ACTIVE", "SQ_INSTS_VALU"} <= names:
         extra.append("valu_busy")
+    if {"GRBM_GUI_ACTIVE", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES"} <= names:
+        extra += ["mfma_busy", "valu_per_mfma"]
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in names:
+            extra.append("coexec")
     lines.append(head + "".join(f" {e:>14s}" for e in extra))
     for key in sorted(vals, key=lambda k: -st.mean(durs[k].values()) if durs[k] else 0):
         d = list(durs[key].values())
@@ -187,6 +200,13 @@ def counter_summary(directory: str) -> str:
             line += f" {means['SQ_INSTS_VALU'] / max(means['SQ_WAVES'], 1.0):14.1f}"
         if "valu_busy" in extra:
             line += f" {means['SQ_INSTS_VALU'] * 4 / (SIMDS * means['GRBM_GUI_ACTIVE'] / XCDS):14.3f}"
+        if "mfma_busy" in extra:
+            mb = means["SQ_VALU_MFMA_BUSY_CYCLES"]
+            mi = means["SQ_INSTS_MFMA"]
+            line += f" {mb / (SIMDS * means['GRBM_GUI_ACTIVE'] / XCDS):14.3f}"
+            line += f" {(means['SQ_INSTS_VALU'] - mi) / mi:14.2f}" if mi > 0 else f" {'-':>14s}"
+            if "coexec" in extra:
+                line += f" {means['SQ_VALU_MFMA_COEXEC_CYCLES'] / mb:14.3f}" if mb > 0 else f" {'-':>14s}"
         lines.append(line)
     return "\n".join(lines)
 
@@ -224,6 +244,11 @@ CALL_ARGS = ["--no-cpu", "--no-graph", "--no-warm", "--steps", "20", "--warmup",
 PMC_ARGS = ["--no-cpu", "--no-graph", "--no-warm", "--calib-copy", "--steps", "3", "--warmup", "2", "--reps", "5",
             "--only", "c0,c1,c2,c3,c4,k"]
 SQ_COUNTERS = ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CYCLES", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE"]
+# the prefill GEMM rows only (the headline step runs a few steps first)
+GEMM_ARGS = ["--no-cpu", "--no-graph", "--no-q8-step", "--steps", "3", "--warmup", "2", "--reps", "3", "--settle-ms",
+             "20", "--only", "g "]
+MFMA_COUNTERS = ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES",
+                 "SQ_INSTS_SALU", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE"]
 # the headline step's calls: bench.py label -> the kernel launch shape that runs it
 STEP_CALLS = {"gate|up 2x17408x5120 silu": "qgk::qgemv_kernel<2, 1, 1, 1, true, 1, false>|1088x256",
               "down 5120x17408": "qgk::qgemv_persist<2, 1, 0, true, false, false>|256x1024",
@@ -294,6 +319,14 @@ def collect(out: str, only=None):
         cmd, _ = _run_pass("sq", ["--pmc", *SQ_COUNTERS, "--kernel-trace"], PMC_ARGS, out, 600)
         summaries["sq"] = (f"command: {cmd}\nsummary: python -m block_dequant_gemv_amd.prof counters <out>/sq\n\n"
                            + counter_summary(os.path.join(out, "sq")))
+    if want("trace_gemm"):
+        cmd, _ = _run_pass("trace_gemm", ["--kernel-trace", "--stats"], GEMM_ARGS, out, 600)
+        summaries["trace_gemm"] = (f"command: {cmd}\nsummary: python -m block_dequant_gemv_amd.prof trace "
+                                   f"<out>/trace_gemm --skip 3\n\n" + trace_summary(os.path.join(out, "trace_gemm"), 3))
+    if want("gemm_sq"):
+        cmd, _ = _run_pass("gemm_sq", ["--pmc", *MFMA_COUNTERS, "--kernel-trace"], GEMM_ARGS, out, 600)
+        summaries["gemm_sq"] = (f"command: {cmd}\nsummary: python -m block_dequant_gemv_amd.prof counters "
+                                f"<out>/gemm_sq\n\n" + counter_summary(os.path.join(out, "gemm_sq")))
     for name, text in summaries.items():
         with open(os.path.join(out, name + ".txt"), "w") as f:
             f.write(text + "\n")

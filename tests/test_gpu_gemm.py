@@ -143,3 +143,30 @@ def test_gemm_closed_form_exact():
         Y, _, _ = _run(kind, packed, np.ones((M, K), np.float32), N, K, M)
         assert np.all(Y == expect), (kind, Y.min(), Y.max())
     del torch
+
+
+@pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
+def test_gemm_unaligned_activations_same_bits(kind):
+    # X only 4-byte aligned (the documented minimum) takes the activation split's
+    # scalar loads; the split's arithmetic is the same, so Y is the same bits as
+    # with a 16-byte-aligned X, and within the bound of the oracle
+    torch = torch_dev()
+    N, K, M = 300, 2080, 20
+    rng = np.random.default_rng(77)
+    canon = W.matrix(kind, N, K, rng)
+    X = W.activation(K, rng, M=M).reshape(M, K)
+    packed = qg.pack_weights(kind, canon, N, K)
+    announce(f"qgemm_prefill {kind} unaligned X")
+    Y_al, _, ws = _run(kind, packed, X, N, K, M)
+    buf = torch.empty(M * K + 4, dtype=torch.float32, device="cuda")
+    Xu = buf[1:1 + M * K]
+    assert Xu.data_ptr() % 16 == 4
+    Xu.copy_(torch.from_numpy(X.reshape(-1)))
+    Y = torch.full((M * N,), -9.0, dtype=torch.float32, device="cuda")
+    qg.qgemm_prefill(kind, packed, Xu, Y, N, K, M, workspace=ws)
+    sync()
+    Y_un = Y.cpu().numpy().reshape(M, N)
+    assert np.array_equal(Y_un.view(np.uint32), Y_al.view(np.uint32))
+    Y_ref, A_ref = O.verify(kind, canon, X, N, K, threads=THREADS)
+    for m in range(M):
+        assert_linear(Y_un[m], Y_ref[m], A_ref[m], f"gemm {kind} unaligned X row {m}")
