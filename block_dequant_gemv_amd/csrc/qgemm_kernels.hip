@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "dequant.h"
@@ -46,14 +47,16 @@ using namespace qgl;
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------
-// Activation split: one workgroup per activation row m (rows M..M_pad-1 of
-// the last 16-row tile are written as zeros). Writes unscale[m] = 2^-e and the
-// fp16 parts in B-operand order: xs[((mt * KB + b) * 2 + h) * 512 + lane * 8 + e]
-// with mt = m / 16, lane = 16 c + m % 16, h = 0 (hi) / 1 (lo), where (c, e)
-// is the position of the block's element in its lane (see above). Each thread
-// takes whole lane runs (block b, chunk c: the 8 elements one MFMA lane holds)
-// and writes their hi and lo parts as two 16-byte stores; VEC: the row is
-// 16-byte aligned and read with 16-byte loads.
+// Activation split: gridDim.y workgroups per activation row m = blockIdx.x
+// (rows M..M_pad-1 of the last 16-row tile are written as zeros). Writes
+// unscale[m] = 2^-e and the fp16 parts in B-operand order:
+// xs[((mt * KB + b) * 2 + h) * 512 + lane * 8 + e] with mt = m / 16,
+// lane = 16 c + m % 16, h = 0 (hi) / 1 (lo), where (c, e) is the position of the
+// block's element in its lane (see above). Every workgroup of a row finds the
+// row's maximum itself (the same value), then splits its share of the row's
+// lane runs (block b, chunk c: the 8 elements one MFMA lane holds), writing
+// their hi and lo parts as two 16-byte stores. Loads are issued four at a time
+// per thread. VEC: the row is 16-byte aligned and read with 16-byte loads.
 constexpr int kSplitThreads = 256;
 
 template <int QT, bool VEC>
@@ -61,7 +64,8 @@ __global__ void __launch_bounds__(kSplitThreads)
 split_x_kernel(const float *__restrict__ X, _Float16 *__restrict__ xs, float *__restrict__ unscale, int64_t M,
                int64_t K)
 {
-    __shared__ float red[kSplitThreads / 64];
+    constexpr int T = kSplitThreads;
+    __shared__ float red[T / 64];
     const int64_t m = blockIdx.x;
     const int tid = threadIdx.x;
     const bool live = m < M;
@@ -70,13 +74,24 @@ split_x_kernel(const float *__restrict__ X, _Float16 *__restrict__ xs, float *__
     if (live) {
         if (VEC) {
             const f32x4 *x4 = (const f32x4 *)xr;
-            for (int64_t k = tid; k < K / 4; k += kSplitThreads) {
-                const f32x4 v = x4[k];
-                mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)),
-                                                         __builtin_fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w))));
+            const int64_t K4 = K / 4;
+            for (int64_t k = tid; k < K4; k += 4 * T) {
+                f32x4 v[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = k + j * T < K4 ? x4[k + j * T] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[j].x), __builtin_fabsf(v[j].y)),
+                                                             __builtin_fmaxf(__builtin_fabsf(v[j].z), __builtin_fabsf(v[j].w))));
             }
         } else {
-            for (int64_t k = tid; k < K; k += kSplitThreads) mx = __builtin_fmaxf(mx, __builtin_fabsf(xr[k]));
+            for (int64_t k = tid; k < K; k += 4 * T) {
+                float v[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = k + j * T < K ? xr[k + j * T] : 0.0f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) mx = __builtin_fmaxf(mx, __builtin_fabsf(v[j]));
+            }
         }
     }
     // workgroup maximum (max is exact, so the order does not matter)
@@ -84,7 +99,7 @@ split_x_kernel(const float *__restrict__ X, _Float16 *__restrict__ xs, float *__
     if ((tid & 63) == 0) red[tid >> 6] = mx;
     __syncthreads();
     mx = red[0];
-    for (int w = 1; w < kSplitThreads / 64; ++w) mx = __builtin_fmaxf(mx, red[w]);
+    for (int w = 1; w < T / 64; ++w) mx = __builtin_fmaxf(mx, red[w]);
     // 2^e with max|x| * 2^e in [2^14, 2^15); 1 for a zero or non-finite maximum
     int e = 0;
     if (mx > 0.0f && mx <= 3.4028234663852886e38f) {
@@ -94,13 +109,15 @@ split_x_kernel(const float *__restrict__ X, _Float16 *__restrict__ xs, float *__
         e = e < -126 ? -126 : (e > 127 ? 127 : e);
     }
     const float sc = __builtin_ldexpf(1.0f, e);
-    if (tid == 0) unscale[m] = __builtin_ldexpf(1.0f, -e);
+    if (tid == 0 && blockIdx.y == 0) unscale[m] = __builtin_ldexpf(1.0f, -e);
     const int64_t KB = K / 32;
     const int64_t mt = m >> 4;
     const int mi = (int)(m & 15);
-    // lane run u = (block b, chunk c): Q4_0 elements 8c..8c+7 of the block,
-    // Q8_0 elements 4c..4c+3 and 16+4c..16+4c+3
-    for (int64_t u = tid; u < KB * 4; u += kSplitThreads) {
+    // this workgroup's lane runs u in [u0, u1): Q4_0 elements 8c..8c+7 of block
+    // b = u / 4 (c = u % 4), Q8_0 elements 4c..4c+3 and 16+4c..16+4c+3
+    const int64_t U = KB * 4;
+    const int64_t u0 = U * blockIdx.y / gridDim.y, u1 = U * (blockIdx.y + 1) / gridDim.y;
+    auto run = [&](int64_t u) {
         const int64_t b = u >> 2;
         const int c = (int)(u & 3);
         const int64_t k0 = b * 32 + (QT == kQ4_0 ? 8 * c : 4 * c);
@@ -132,7 +149,13 @@ split_x_kernel(const float *__restrict__ X, _Float16 *__restrict__ xs, float *__
         _Float16 *dst = xs + ((mt * KB + b) * 2) * 512 + (int64_t)(c * 16 + mi) * 8;
         *(h8 *)dst = hi;
         *(h8 *)(dst + 512) = lo;
+    };
+    int64_t u = u0 + tid;
+    for (; u + T < u1; u += 2 * T) {   // two runs per thread in flight
+        run(u);
+        run(u + T);
     }
+    if (u < u1) run(u);
 }
 
 // 4 x 4 transpose of (16-lane group, register): afterwards register r of lane
@@ -594,7 +617,11 @@ hipError_t launch_split_x(int qt, const float *X, _Float16 *xs, float *unscale, 
                           hipStream_t s)
 {
     const bool vec = ((uintptr_t)X & 15) == 0;   // rows are K * 4 bytes, a multiple of 128
-    const dim3 grid((unsigned)M_pad), block(kSplitThreads);
+    // up to four workgroups per row while fewer than 256 rows fill the chip,
+    // at least 512 lane runs (4096 elements) each
+    int64_t per_row = std::min<int64_t>(4, std::max<int64_t>(1, 256 / M_pad));
+    per_row = std::max<int64_t>(1, std::min<int64_t>(per_row, K / 8 / 512));
+    const dim3 grid((unsigned)M_pad, (unsigned)per_row), block(kSplitThreads);
     if (qt == kQ8_0) {
         if (vec)
             hipLaunchKernelGGL((split_x_kernel<kQ8_0, true>), grid, block, 0, s, X, xs, unscale, M, K);
