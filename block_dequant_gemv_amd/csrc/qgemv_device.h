@@ -424,62 +424,105 @@ __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][
         for (int b = 0; b < B; ++b) acc[m][b] = __builtin_fmaf((float)d[b], sb[m][b], acc[m][b]);
 }
 
-// Stage row m of X as xs4[m*nseg*256 + seg*256 + c*32 + jj], where float4
-// chunk i = seg*256 + jj*8 + c of the row holds x[4i .. 4i+3] (zero past K;
-// K % 32 == 0, so a chunk is wholly inside K or wholly past it). Indexing is
-// 32-bit shifts and masks (the staged area is at most LDS-sized); each thread
-// issues its global loads in batches of 4 before writing LDS.
+// Stage rows 0..M-1 of X as xs4[m*nseg*256 + seg*256 + c*32 + jj], where
+// float4 chunk i = seg*256 + jj*8 + c of a row holds x[4i .. 4i+3] (zero past
+// K; K % 32 == 0, so a chunk is wholly inside K or wholly past it). The staged
+// area is taken as one flat sequence of chunks f = m*nseg*256 + i over all M
+// rows; each thread loads a batch of NB chunks f = tid + q*nthreads before
+// writing any, so that an area of up to NB chunks per thread costs one memory
+// round trip, not one per row or per batch of 4 (every single-row
+// configuration needs at most 5 per thread: K = 5120 over 256 threads, K =
+// 17408 over 1024). The batch is sized to stay inside the kernels' register
+// budgets (x_batch). Reads are coalesced (consecutive threads, consecutive 16-byte
+// chunks); the LDS stores scatter into the lane-swizzled order. Indexing is
+// 32-bit (the staged area is at most LDS-sized).
 //
-// The first batch of row 0 is split off (stage_x_issue): a kernel issues it
-// before its first weight loads, so that the few activation lines reach the
-// memory queues ahead of the weight stream instead of behind it, and writes it
-// (stage_x_finish, which also stages the rest) after them. The caller
-// synchronises the workgroup afterwards.
+// The first batch is split off (stage_x_issue): a kernel issues it before its
+// first weight loads, so that the activation lines reach the memory queues
+// ahead of the weight stream instead of behind it, and writes it
+// (stage_x_finish, which also stages anything past the first batch) after
+// them. The caller synchronises the workgroup afterwards.
+// Chunks per thread and batch: 5 for one row; for several rows 8 in the
+// persistent form (launched at 2 or 3 wavefronts per SIMD, which its registers
+// allow) and 4 in the tile form, whose occupancy more registers would lower.
+constexpr int x_batch(int M, bool persistent) { return M == 1 ? 5 : (persistent ? 8 : 4); }
+
+template <int NB>
 struct XFirst {
-    f32x4 v[4];
+    f32x4 v[NB];
 };
 
 __device__ __forceinline__ uint32_t x_slot(uint32_t i) { return (i & ~255u) | ((i & 7u) << 5) | ((i >> 3) & 31u); }
 
-__device__ __forceinline__ void stage_x_issue(XFirst &f, const float *__restrict__ x, int64_t K)
+// Flat chunk f of the staged area -> (row m, chunk i of the row); inv = 1 / per_m.
+template <int M>
+__device__ __forceinline__ void x_place(uint32_t f, uint32_t per_m, float inv, uint32_t &m, uint32_t &i)
 {
+    if (M == 1) {
+        m = 0;
+        i = f;
+        return;
+    }
+    uint32_t q = (uint32_t)((float)f * inv);   // f < 2^24: within one of f / per_m
+    if (q * per_m > f)
+        --q;
+    else if ((q + 1) * per_m <= f)
+        ++q;
+    m = q;
+    i = f - q * per_m;
+}
+
+template <int M, int NB>
+__device__ __forceinline__ void stage_x_issue(XFirst<NB> &xf, const float *__restrict__ x, int64_t x_stride, int64_t nseg,
+                                              int64_t K)
+{
+    const uint32_t per_m = (uint32_t)nseg << 8;
+    const uint32_t total = (uint32_t)M * per_m;
     const uint32_t k4 = (uint32_t)(K >> 2);
+    const float inv = 1.0f / (float)per_m;
     const uint32_t nthr = blockDim.x, tid = threadIdx.x;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t i = tid + q * nthr;
-        f.v[q] = i < k4 ? *(const f32x4 *)(x + 4 * (size_t)i) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int q = 0; q < NB; ++q) {
+        const uint32_t f = tid + q * nthr;
+        uint32_t m, i;
+        x_place<M>(f, per_m, inv, m, i);
+        xf.v[q] = f < total && i < k4 ? *(const f32x4 *)(x + (int64_t)m * x_stride + 4 * (size_t)i)
+                                      : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 }
 
-template <int M>
-__device__ __forceinline__ void stage_x_finish(const XFirst &f, f32x4 *xs4, const float *__restrict__ x,
+template <int M, int NB>
+__device__ __forceinline__ void stage_x_finish(const XFirst<NB> &xf, f32x4 *xs4, const float *__restrict__ x,
                                                int64_t x_stride, int64_t nseg, int64_t K)
 {
     const uint32_t per_m = (uint32_t)nseg << 8;
+    const uint32_t total = (uint32_t)M * per_m;
     const uint32_t k4 = (uint32_t)(K >> 2);
+    const float inv = 1.0f / (float)per_m;
     const uint32_t nthr = blockDim.x, tid = threadIdx.x;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t i = tid + q * nthr;
-        if (i < per_m) xs4[x_slot(i)] = f.v[q];
+    for (int q = 0; q < NB; ++q) {
+        const uint32_t f = tid + q * nthr;
+        uint32_t m, i;
+        x_place<M>(f, per_m, inv, m, i);
+        if (f < total) xs4[m * per_m + x_slot(i)] = xf.v[q];
     }
+    for (uint32_t base = tid + NB * nthr; base < total; base += NB * nthr) {
+        f32x4 v[NB];
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-        const float *xm = x + (int64_t)m * x_stride;
-        f32x4 *dst = xs4 + (uint32_t)m * per_m;
-        for (uint32_t base = tid + (m == 0 ? 4 * nthr : 0u); base < per_m; base += 4 * nthr) {
-            f32x4 v[4];
+        for (int q = 0; q < NB; ++q) {
+            const uint32_t f = base + q * nthr;
+            uint32_t m, i;
+            x_place<M>(f, per_m, inv, m, i);
+            v[q] = f < total && i < k4 ? *(const f32x4 *)(x + (int64_t)m * x_stride + 4 * (size_t)i)
+                                       : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t i = base + q * nthr;
-                v[q] = i < k4 ? *(const f32x4 *)(xm + 4 * (size_t)i) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t i = base + q * nthr;
-                if (i < per_m) dst[x_slot(i)] = v[q];
-            }
+        for (int q = 0; q < NB; ++q) {
+            const uint32_t f = base + q * nthr;
+            uint32_t m, i;
+            x_place<M>(f, per_m, inv, m, i);
+            if (f < total) xs4[m * per_m + x_slot(i)] = v[q];
         }
     }
 }
@@ -656,8 +699,8 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
             tt += t_step;
         }
     };
-    XFirst xf;
-    if (XLDS) stage_x_issue(xf, x, K);
+    XFirst<x_batch(M, false)> xf;
+    if (XLDS) stage_x_issue<M>(xf, x, a.x_stride, nseg, K);
     Unit<QT> ring[S];
 #pragma unroll
     for (int r = 0; r < D; ++r) {
@@ -838,8 +881,10 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
         cu = ld;
         int64_t u_ld = 0;
 
-        XFirst xf;
-        if (XLDS) stage_x_issue(xf, xw, Kw);
+        // phased windows are staged in batches of 4 (the registers of the phased
+        // kernels are at their limit)
+        XFirst<PHASED ? 4 : x_batch(M, true)> xf;
+        if (XLDS) stage_x_issue<M>(xf, xw, a.x_stride, nsegw, Kw);
         Unit<QT> ring[S];
         load_unit<QT>(ring[0], wp, g, ld.t, ld.s, lp, u_ld < n_units);
         advance(ld);
