@@ -92,13 +92,13 @@ int64_t env_int(const char *name, int64_t dflt)
 // again on qg_reload_tuning(): a GEMV call itself reads no environment.
 enum TuneKey {
     kSplitK, kPersist, kXGlobal, kTilesPerGroup, kWavesPerWg, kPrefetch, kF16Rows, kF16Waves, kStrideGroups,
-    kGemmMT, kGemmWaves, kGemmRowGroups, kGemmKSplit, kF16Form, kF16Cpl, kNumTune
+    kGemmMT, kGemmWaves, kGemmRowGroups, kGemmKSplit, kF16Form, kF16Cpl, kVerifyRowGroups, kNumTune
 };
 const char *const kTuneNames[kNumTune] = {"QG_SPLIT_K",      "QG_PERSIST",  "QG_X_GLOBAL",  "QG_TILES_PER_GROUP",
                                           "QG_WAVES_PER_WG", "QG_PREFETCH", "QG_F16_ROWS",  "QG_F16_WAVES",
                                           "QG_STRIDE_GROUPS", "QG_GEMM_MT", "QG_GEMM_WAVES", "QG_GEMM_ROWGROUPS",
-                                          "QG_GEMM_KSPLIT", "QG_F16_FORM", "QG_F16_CPL"};
-const int64_t kTuneDefaults[kNumTune] = {0, -1, -1, 0, 0, 0, 0, 0, -1, 0, 0, 0, 0, -1, 0};
+                                          "QG_GEMM_KSPLIT", "QG_F16_FORM", "QG_F16_CPL", "QG_VERIFY_ROW_GROUPS"};
+const int64_t kTuneDefaults[kNumTune] = {0, -1, -1, 0, 0, 0, 0, 0, -1, 0, 0, 0, 0, -1, 0, 0};
 std::atomic<int64_t> g_tune[kNumTune];
 std::atomic<bool> g_tune_loaded{false};
 
@@ -330,6 +330,34 @@ struct Norm {
     float eps = 0.0f;
 };
 
+// Row groups of a verify call (see run_qgemv): where the tile form launches at
+// most half as many wavefronts as the chip has SIMDs, the fewest groups (a
+// divisor of M) that give every SIMD a wavefront, else M groups of one row.
+// Measured on MI355X, cold, interleaved (us, one group -> the chosen groups):
+// Q8_0 4096 x 1024 (512 wavefronts) M = 2 / 3 / 4 / 6: 5.15 -> 4.47, 5.31 ->
+// 4.81, 5.86 -> 5.36, 6.62 -> 5.27; Q8_0 1024 x 1024 (128) M = 3 / 6: 5.53 ->
+// 4.61, 8.71 -> 4.65; Q4_K 4096 x 1024 M = 6: 6.98 -> 5.17. With 768 wavefronts
+// (6144 x 1024) groups won at M = 2 and 6 and lost at M = 3 and 4, so they stay
+// off there. QG_VERIFY_ROW_GROUPS = g forces g groups where g divides M and the
+// tile form applies.
+int verify_row_groups(int qt, int64_t rows, int64_t K, int M, const qgk::QPlan &p, int epi, bool norm)
+{
+    if (M < 2 || epi != qgk::kEpiPlain || norm || p.persist) return 1;
+    auto usable = [&](int g) {
+        if (g < 2 || M % g != 0) return false;
+        const qgk::QPlan q = make_qplan(qt, rows, K, M / g, false);
+        return !q.persist;
+    };
+    const int64_t forced = tune(kVerifyRowGroups);
+    if (forced >= 1) return usable((int)forced) ? (int)forced : 1;
+    const int64_t simds = cu_count() * 4;
+    const int64_t waves = p.grid * (p.block / 64);
+    if (2 * waves > simds) return 1;
+    for (int g = 2; g <= M; ++g)
+        if (M % g == 0 && waves * g >= simds && usable(g)) return g;
+    return usable(M) ? M : 1;
+}
+
 qg_status run_qgemv(int qt, int epi, const void *w, const float *x, void *y, int64_t rows, int64_t n_out,
                     int64_t K, int M, void *stream, const char *fn, const Affine &af = Affine(),
                     const Norm &nm = Norm())
@@ -367,8 +395,18 @@ qg_status run_qgemv(int qt, int epi, const void *w, const float *x, void *y, int
     if (af.residual && !(af.residual == y && !f16) && overlap(y, ybytes, af.residual, abytes))
         return fail(QG_EINVAL, "%s: y overlaps residual (only residual == y with fp32 output is allowed)", fn);
 
-    const qgk::QPlan p = make_qplan(qt, rows, K, M, nm.on);
+    qgk::QPlan p = make_qplan(qt, rows, K, M, nm.on);
     if (nm.on && !p.x_in_lds) return fail(QG_EUNSUPPORTED, "%s: activations do not fit in LDS", fn);
+    // Verify on a matrix with few row tiles: split the activation rows into
+    // groups (gridDim.y) of M / groups rows, each group a launch-wide copy of
+    // the tile form over all tiles, so that more wavefronts share the work.
+    // Every row keeps the M = 1 operations.
+    const int groups = verify_row_groups(qt, rows, K, M, p, epi, nm.on);
+    if (groups > 1) {
+        p = make_qplan(qt, rows, K, M / groups, false);
+        p.row_groups = groups;
+        M /= groups;
+    }
     qgk::QArgs a;
     a.geo = g;
     a.n_out = n_out;
@@ -937,10 +975,16 @@ qg_status qg_plan_info(int qtype, int64_t N, int64_t K, int M, int rmsnorm, int 
     if (norm && K > kNormMaxK)
         return fail(QG_EUNSUPPORTED, "qg_plan_info: K=%lld above %lld (the normalised activations live in LDS)",
                     (long long)K, (long long)kNormMaxK);
-    const qgk::QPlan p = make_qplan(qtype, N, K, M, norm);
+    qgk::QPlan p = make_qplan(qtype, N, K, M, norm);
     if (norm && !p.x_in_lds) return fail(QG_EUNSUPPORTED, "qg_plan_info: activations do not fit in LDS");
+    // a verify call (M >= 2, plain store) as qgemv_verify launches it
+    const int groups = verify_row_groups(qtype, N, K, M, p, qgk::kEpiPlain, norm);
+    if (groups > 1) {
+        p = make_qplan(qtype, N, K, M / groups, false);
+        M /= groups;
+    }
     if (split_k_ways) *split_k_ways = p.W;
-    if (workgroups) *workgroups = p.grid;
+    if (workgroups) *workgroups = p.grid * groups;
     if (x_in_lds) *x_in_lds = p.x_in_lds ? 1 : 0;
     if (persistent) *persistent = p.persist ? 1 : 0;
     if (lds_bytes) {

@@ -653,11 +653,19 @@ __device__ __forceinline__ void store_tile(const float (&acc)[M][kRowsPerLane], 
 // Which group handles a tile changes none of its rows' operations.
 // Each wavefront walks its (tile, segment) sequence with the loads of the next
 // D units in flight while the current one is computed (a ring of D+1 units).
+// gridDim.y > 1 (plain store only): row group blockIdx.y takes activation rows
+// [blockIdx.y M, blockIdx.y M + M) of a call with gridDim.y M rows, so a small
+// matrix's verify spreads over more wavefronts; each row still goes through
+// the M = 1 operations.
 // The launch bound is qgemv_max_threads (qgemv_kernels.h).
 template <int QT, int M, int EPI, int W, bool XLDS, int D, bool NORM>
 __global__ void __launch_bounds__(qgemv_max_threads(QT, M, W))
 qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float *__restrict__ y, QArgs a)
 {
+    if (EPI == kEpiPlain) {
+        x += (int64_t)blockIdx.y * M * a.x_stride;
+        y += (int64_t)blockIdx.y * M * a.y_stride;
+    }
     static_assert(!NORM || (XLDS && M == 1), "the RMSNorm prologue works on staged single-row activations");
     constexpr int B = kRowsPerLane;
     constexpr int S = D + 1;   // ring size
@@ -974,19 +982,19 @@ static void launch(Kern kern, dim3 grid, dim3 block, uint32_t lds, hipStream_t s
 }
 
 template <int QT, int M, int EPI, int W, bool XLDS, int D, bool NORM = false>
-static hipError_t launch_q(const uint8_t *wp, const float *x, float *y, const QArgs &a, int64_t grid, int block,
+static hipError_t launch_q(const uint8_t *wp, const float *x, float *y, const QArgs &a, dim3 grid, int block,
                            size_t lds, hipStream_t stream)
 {
     auto kern = qgemv_kernel<QT, M, EPI, W, XLDS, D, NORM>;
     static std::atomic<int> lds_set[16];
     hipError_t e = ensure_lds_limit((const void *)kern, lds, lds_set);
     if (e != hipSuccess) return e;
-    launch(kern, dim3((unsigned)grid), dim3(block), (uint32_t)lds, stream, wp, x, y, a);
+    launch(kern, grid, dim3(block), (uint32_t)lds, stream, wp, x, y, a);
     return hipGetLastError();
 }
 
 template <int QT, int M, int EPI, int W>
-static hipError_t dispatch_x(const uint8_t *wp, const float *x, float *y, const QArgs &a, int64_t grid, int block,
+static hipError_t dispatch_x(const uint8_t *wp, const float *x, float *y, const QArgs &a, dim3 grid, int block,
                              size_t lds, bool xlds, int depth, bool norm, hipStream_t s)
 {
     // the RMSNorm prologue: single-row plain and gate|up kernels, staged activations, depth 1
@@ -1009,7 +1017,7 @@ static hipError_t dispatch_x(const uint8_t *wp, const float *x, float *y, const 
 }
 
 template <int QT, int M, int EPI>
-static hipError_t dispatch_w(const uint8_t *wp, const float *x, float *y, const QArgs &a, int W, int64_t grid,
+static hipError_t dispatch_w(const uint8_t *wp, const float *x, float *y, const QArgs &a, int W, dim3 grid,
                              int block, size_t lds, bool xlds, int depth, bool norm, hipStream_t s)
 {
     switch (W) {
@@ -1058,8 +1066,13 @@ template <int QT, int M, int EPI>
 static hipError_t dispatch_form(const uint8_t *wp, const float *x, float *y, const QArgs &a, const QPlan &p,
                                 hipStream_t s)
 {
-    if (p.persist) return launch_persist<QT, M, EPI>(wp, x, y, a, p, s);
-    return dispatch_w<QT, M, EPI>(wp, x, y, a, p.W, p.grid, p.block, p.lds_bytes, p.x_in_lds, p.depth, p.norm, s);
+    if (p.persist) {
+        if (p.row_groups != 1) return hipErrorInvalidConfiguration;
+        return launch_persist<QT, M, EPI>(wp, x, y, a, p, s);
+    }
+    if (p.row_groups < 1 || (p.row_groups > 1 && EPI != kEpiPlain)) return hipErrorInvalidConfiguration;
+    return dispatch_w<QT, M, EPI>(wp, x, y, a, p.W, dim3((unsigned)p.grid, (unsigned)p.row_groups), p.block,
+                                  p.lds_bytes, p.x_in_lds, p.depth, p.norm, s);
 }
 
 // The single-row calls of type QT: plain, gate|up and affine epilogues, with or

@@ -58,6 +58,7 @@ struct QPlan {
     bool x_in_lds;       // activations staged in LDS
     size_t lds_bytes;    // dynamic LDS per workgroup
     bool norm;           // RMSNorm prologue on the staged activations (M = 1, x_in_lds)
+    int row_groups = 1;  // tile form, plain store: gridDim.y groups of the kernel's M activation rows each
 };
 
 struct F16Plan {

@@ -232,7 +232,10 @@ qg_status qgemv_rmsnorm_gateup_silu(int qtype, const void *w_gateup_packed, cons
  * X fp32 row-major [M][K] (16-byte aligned; K % 32 == 0 keeps every row
  * 16-byte aligned), Y fp32 row-major [M][N] (4-byte aligned, not overlapping
  * X or the weights), w_packed 16-byte aligned. The packed weights are
- * streamed once for all M rows, and row m of Y is bit-for-bit (memcmp) equal
+ * streamed once for all M rows (on a matrix with so few row tiles that one
+ * pass would leave most of the chip idle, the rows are split into groups
+ * that each read the weights, the later reads mostly from the caches), and
+ * row m of Y is bit-for-bit (memcmp) equal
  * to what qgemv_q8_0 / qgemv_q4_0 return for x = X[m] (robotnurse.io post,
  * Update and "Correctness first": a 3-6-row verify pass in one weight stream,
  * checked against the decode kernel with memcmp). */
@@ -298,7 +301,9 @@ const char *qg_last_error(void);
  * Outputs (each may be NULL):
  *   split_k_ways  the number of K ranges a row tile's sum is split into (the
  *                 partial sums of a row are added in range order);
- *   workgroups    workgroups launched;
+ *   workgroups    workgroups launched (a verify call on a matrix with few row
+ *                 tiles splits its M rows into groups, each group its own set
+ *                 of workgroups: this counts them all);
  *   x_in_lds      1 when the activations are staged in LDS, 0 when read from L2;
  *   persistent    1 for the persistent form (one workgroup per CU, used for
  *                 matrices with few row tiles), 0 for one wavefront per tile;
