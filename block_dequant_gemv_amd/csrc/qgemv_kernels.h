@@ -116,13 +116,15 @@ constexpr int qgemv_max_threads(int QT, int M, int W)
 
 // Threads per workgroup of the persistent form (its launch bound): as many
 // wavefronts as one CU holds at the kernel's register count. Single-row
-// kernels fit 128 VGPRs (16 wavefronts); the multi-row kernels up to 168 (12
-// wavefronts) where they fit without spilling, else 256 (8); Q4_K with 5 or 6
-// rows 4 wavefronts (512 registers each, no scratch).
+// kernels, and Q4_0 with 2 or 3 rows, fit 128 VGPRs (16 wavefronts; Q4_0
+// 17408 x 5120 at M = 3: 22.2 -> 21.5 us against 12 wavefronts, M = 2
+// unchanged); the other multi-row kernels up to 168 (12 wavefronts) where they
+// fit without spilling, else 256 (8); Q4_K with 5 or 6 rows 4 wavefronts (512
+// registers each, no scratch).
 constexpr int persist_threads(int qt, int M, bool xlds)
 {
     if (M == 1) return 1024;
-    if (qt == qgl::kQ4_0) return (M <= 4 || xlds) ? 768 : 512;
+    if (qt == qgl::kQ4_0) return M <= 3 ? 1024 : ((M <= 4 || xlds) ? 768 : 512);
     if (qt == qgl::kQ4_K) return M <= 2 ? 768 : (M <= 4 ? 512 : 256);
     if (qt == qgl::kQ6_K) return M <= 2 ? 768 : 512;
     return (M <= 3 || xlds) ? 768 : 512;
