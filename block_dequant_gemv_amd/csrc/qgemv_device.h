@@ -9,7 +9,8 @@
 //   per lane, per block of 32 weights, per activation row m:
 //     s = 0;  s = fma(v_e, x_e, s) for e = 0..31      (v_e = q or nibble-8, exact in fp16)
 //     acc = fma(d, s, acc)                             (d = the block's fp16 scale)
-//   acc of the 32 lanes that share a row: fixed butterfly (DPP + swizzle)
+//   acc of the 32 lanes that share a row: one fixed tree of pairings
+//     (permlane16 swap and DPP; tile_sums)
 //   split-K wavefronts (if any): partials added in wavefront order in LDS
 //
 // Nothing in that sequence depends on M, on which wavefront or workgroup
@@ -41,7 +42,9 @@ using namespace qgl;
 
 // Sum over the 32 lanes of one wavefront half (lanes 0-31 and 32-63 separately).
 // Butterfly: xor 1, xor 2 (quad_perm), mirror within 8, mirror within 16 (DPP),
-// xor 16 (ds_swizzle). Every lane of the half ends with the same bits.
+// xor 16 (ds_swizzle). Every lane of the half ends with the same bits. Used for
+// single values (the RMSNorm sum of squares, the fp16 GEMV); the quantised row
+// tiles use tile_sums below.
 __device__ __forceinline__ float half_wave_sum(float v)
 {
     v += as_f(__builtin_amdgcn_update_dpp(0, as_i(v), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
@@ -56,6 +59,118 @@ __device__ __forceinline__ float silu_mul(float g, float u)
 {
     return g / (1.0f + expf(-g)) * u;
 }
+
+// ---------------------------------------------------------------------------
+// The sums of a row tile: each of the V = 4 M values a lane holds (activation
+// row m, weight row b of its slot; value index i = 4 m + b) is added over the
+// 32 lanes of the slot (lanes slot*32 + j, j = 0..31) through one fixed tree of
+// five pairing levels, in this order:
+//   L1 j ^ 16, L2 j ^ 8, L3 j ^ 7 (mirror within groups of 8), L4 j ^ 1, L5 j ^ 2.
+// Each level adds the partial sums of two disjoint halves of the final lane set
+// (lane sets {j, j^16}, then j ^ {0, 8, 16, 24}, then j ^ {0, 7, 8, 15, 16, 23,
+// 24, 31}, ...). A level is done either as a butterfly (both lanes of a pair
+// get every sum: one DPP add per value) or as a reduce-scatter: the two lanes
+// split a pair of values, each adding the partner's copy of the value it keeps,
+// so later levels have half as many values to add. The additions, and so the
+// bits of every sum, are the same either way (a + b == b + a); only which lanes
+// end up holding which sums differs. RS levels are reduce-scatter:
+//   L1 (v_permlane16_swap, one swap and one add per pair of values), then, for
+//   RS >= 2, L2 and for RS = 3 L3 (a select of the kept and the sent value and
+//   one DPP add per pair); the rest are butterflies.
+// After L1 the lanes with j bit 4 clear hold values i < 2M, the others i + 2M;
+// L2 splits each half by j bit 3 and L3 by j bit 2 (tile_sum_index).
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane 7 - l within 8 (l ^ 7)
+constexpr int kDppRor8 = 0x128;       // row_ror:8, lane l ^ 8 within 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_bfly(float v)
+{
+    return v + as_f(__builtin_amdgcn_update_dpp(0, as_i(v), CTRL, 0xF, 0xF, false));
+}
+
+// Lanes with hi clear keep p, the others q; each adds its partner's copy.
+template <int CTRL>
+__device__ __forceinline__ float dpp_split(float p, float q, bool hi)
+{
+    const float keep = hi ? q : p, send = hi ? p : q;
+    return keep + as_f(__builtin_amdgcn_update_dpp(0, as_i(send), CTRL, 0xF, 0xF, false));
+}
+
+// Registers a lane holds after the reduction.
+constexpr int tile_sum_regs(int M, int RS) { return RS == 1 ? 2 * M : (RS == 2 ? M : M / 2 + (M & 1)); }
+
+template <int M, int RS>
+__device__ __forceinline__ void tile_sums(const float (&acc)[M][kRowsPerLane], float (&out)[tile_sum_regs(M, RS)],
+                                          int j)
+{
+    constexpr int B = kRowsPerLane, H1 = 2 * M;
+    static_assert(RS >= 1 && RS <= 3, "one to three reduce-scatter levels");
+    float v1[H1];
+#pragma unroll
+    for (int i = 0; i < H1; ++i) {
+        const int i2 = i + H1;
+        const auto pr = __builtin_amdgcn_permlane16_swap(as_i(acc[i / B][i % B]), as_i(acc[i2 / B][i2 % B]), false,
+                                                         false);
+        v1[i] = as_f(pr[0]) + as_f(pr[1]);
+    }
+    if constexpr (RS == 1) {
+#pragma unroll
+        for (int i = 0; i < H1; ++i) {
+            float v = dpp_bfly<kDppRor8>(v1[i]);
+            v = dpp_bfly<kDppHalfMirror>(v);
+            v = dpp_bfly<kDppXor1>(v);
+            out[i] = dpp_bfly<kDppXor2>(v);
+        }
+    } else {
+        const bool h3 = (j & 8) != 0;
+        float v2[M];
+#pragma unroll
+        for (int i = 0; i < M; ++i) v2[i] = dpp_split<kDppRor8>(v1[i], v1[i + M], h3);
+        if constexpr (RS == 2) {
+#pragma unroll
+            for (int i = 0; i < M; ++i) {
+                float v = dpp_bfly<kDppHalfMirror>(v2[i]);
+                v = dpp_bfly<kDppXor1>(v);
+                out[i] = dpp_bfly<kDppXor2>(v);
+            }
+        } else {
+            constexpr int H3 = M / 2;
+            const bool h2 = (j & 4) != 0;
+#pragma unroll
+            for (int i = 0; i < H3; ++i) out[i] = dpp_split<kDppHalfMirror>(v2[i], v2[i + H3], h2);
+            if constexpr (M & 1) out[H3] = dpp_bfly<kDppHalfMirror>(v2[M - 1]);
+#pragma unroll
+            for (int i = 0; i < tile_sum_regs(M, RS); ++i) out[i] = dpp_bfly<kDppXor2>(dpp_bfly<kDppXor1>(out[i]));
+        }
+    }
+}
+
+// Value index i = 4 m + b that register r of lane j holds after tile_sums, and
+// whether lane j is the one lane of its slot that writes it (the lowest j
+// holding it).
+template <int M, int RS>
+__device__ __forceinline__ int tile_sum_index(int r, int j)
+{
+    const int b4 = (j >> 4) & 1, b3 = (j >> 3) & 1, b2 = (j >> 2) & 1;
+    if (RS == 1) return r + 2 * M * b4;
+    if (RS == 2) return r + M * b3 + 2 * M * b4;
+    constexpr int H3 = M / 2;
+    return (r < H3 ? r + H3 * b2 : M - 1) + M * b3 + 2 * M * b4;
+}
+template <int M, int RS>
+__device__ __forceinline__ bool tile_sum_owner(int r, int j)
+{
+    if (RS == 1) return (j & 15) == 0;
+    if (RS == 2) return (j & 7) == 0;
+    return (j & 3) == 0 && (r < M / 2 || (j & 4) == 0);
+}
+
+// Reduce-scatter depth of each epilogue: gate|up keeps a gate row and its up
+// row (values 2p, 2p + 1) in one lane, so it splits at L1 only.
+template <int EPI>
+constexpr int tile_rs() { return EPI == kEpiGateUp ? 1 : 3; }
 
 // One lane's packed data for one (row tile, segment): 16 bytes per row and
 // half-block, plus the fp16 scales of its 4 rows (Q4_K: their 6-bit scales and
@@ -597,39 +712,50 @@ __device__ __forceinline__ void store_out(float *__restrict__ y, const QArgs &a,
     }
 }
 
-// Write the finished rows of tile t from the lanes of one slot (acc already
-// reduced over the slot's 32 lanes, so every lane holds the sums).
-//   plain, affine: lane j < M*B stores row b = j % B of activation row m = j / B
-//   gate|up:       rows b = 2p (gate) and 2p+1 (up) give output n = row0/2 + p
+// The sums a lane holds after tile_sums for epilogue EPI.
 template <int M, int EPI>
-__device__ __forceinline__ void store_tile(const float (&acc)[M][kRowsPerLane], float *__restrict__ y, const QArgs &a,
+using TileSums = float[tile_sum_regs(M, tile_rs<EPI>())];
+
+// Write the finished rows of tile t from the sums of one slot (tile_sums).
+//   plain, affine: the owner lane of value i = 4 m + b stores row b of
+//                  activation row m
+//   gate|up (M = 1, one split level): registers 0 and 1 of lane j hold gate row
+//                  2p and up row 2p + 1, p = j bit 4; lane j = 16 p stores
+//                  output n = row0/2 + p
+template <int M, int EPI>
+__device__ __forceinline__ void store_tile(const TileSums<M, EPI> &sums, float *__restrict__ y, const QArgs &a,
                                            int64_t t, int slot, int j)
 {
-    constexpr int B = kRowsPerLane;
+    constexpr int B = kRowsPerLane, RS = tile_rs<EPI>();
     const int64_t n_out = a.n_out;
     const int64_t row0 = t * kTileRows + slot * kRowsPerLane;
     if (EPI != kEpiGateUp) {
-        if (j < M * B) {
-            float v = 0.0f;
 #pragma unroll
-            for (int m = 0; m < M; ++m)
-#pragma unroll
-                for (int b = 0; b < B; ++b)
-                    if (j == m * B + b) v = acc[m][b];
-            const int m = j / B, b = j % B;
-            if (row0 + b < n_out) store_out<M, EPI>(y, a, m, row0 + b, v);
+        for (int r = 0; r < tile_sum_regs(M, RS); ++r) {
+            if (tile_sum_owner<M, RS>(r, j)) {
+                const int i = tile_sum_index<M, RS>(r, j), m = i / B, b = i % B;
+                if (row0 + b < n_out) store_out<M, EPI>(y, a, m, row0 + b, sums[r]);
+            }
         }
     } else {
-        if (j < B / 2) {
-            float gv = 0.0f, uv = 0.0f;
+        if ((j & 15) == 0) {
+            const int64_t n = row0 / 2 + (j >> 4);
+            if (n < n_out) y[n] = silu_mul(sums[0], sums[1]);
+        }
+    }
+}
+
+// Park the sums of one slot at dst[m * kTileRows + b] (dst already offset by
+// the slot's first row): each value is written once, by its owner lane.
+template <int M, int EPI>
+__device__ __forceinline__ void park_tile(const TileSums<M, EPI> &sums, float *dst, int j)
+{
+    constexpr int B = kRowsPerLane, RS = tile_rs<EPI>();
 #pragma unroll
-            for (int p = 0; p < B / 2; ++p)
-                if (j == p) {
-                    gv = acc[0][2 * p];
-                    uv = acc[0][2 * p + 1];
-                }
-            const int64_t n = row0 / 2 + j;
-            if (n < n_out) y[n] = silu_mul(gv, uv);
+    for (int r = 0; r < tile_sum_regs(M, RS); ++r) {
+        if (tile_sum_owner<M, RS>(r, j)) {
+            const int i = tile_sum_index<M, RS>(r, j);
+            dst[(i / B) * kTileRows + i % B] = sums[r];
         }
     }
 }
@@ -745,33 +871,38 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
         compute_unit<QT, M, XLDS>(cur, acc, k, xs4, x, a.x_stride, nseg, s, last ? lp.j_last : j,
                                   !last || lp.live_last);
         if (s + 1 == s_end) {
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-#pragma unroll
-                for (int b = 0; b < B; ++b) acc[m][b] = half_wave_sum(acc[m][b]);
-            if (W > 1) {
-                // fixed-order combine of the split-K partials: ((p0 + p1) + p2) + p3
-                if (j == 0) {
-#pragma unroll
-                    for (int m = 0; m < M; ++m)
-#pragma unroll
-                        for (int b = 0; b < B; ++b) red[((wk * M + m) * kSlots + slot) * B + b] = acc[m][b];
-                }
+            TileSums<M, EPI> sums;
+            tile_sums<M, tile_rs<EPI>()>(acc, sums, j);
+            if (W == 1) {
+                store_tile<M, EPI>(sums, y, a, t, slot, j);
+            } else {
+                // fixed-order combine of the split-K partials: ((p0 + p1) + p2) + p3,
+                // red[w][m][slot][b]; lane j of wavefront 0 finishes value j
+                park_tile<M, EPI>(sums, red + wk * M * kTileRows + slot * B, j);
                 __syncthreads();
                 if (wk == 0) {
+                    const int64_t row0 = t * kTileRows + slot * B;
+                    if (EPI != kEpiGateUp) {
+                        if (j < M * B) {
+                            const int m = j / B, b = j % B;
+                            float v = red[m * kTileRows + slot * B + b];
 #pragma unroll
-                    for (int m = 0; m < M; ++m)
-#pragma unroll
-                        for (int b = 0; b < B; ++b) {
-                            float v = red[((0 * M + m) * kSlots + slot) * B + b];
-#pragma unroll
-                            for (int w = 1; w < W; ++w) v += red[((w * M + m) * kSlots + slot) * B + b];
-                            acc[m][b] = v;
+                            for (int w = 1; w < W; ++w) v += red[(w * M + m) * kTileRows + slot * B + b];
+                            if (row0 + b < a.n_out) store_out<M, EPI>(y, a, m, row0 + b, v);
                         }
+                    } else if (j < B / 2) {
+                        float gv = red[slot * B + 2 * j], uv = red[slot * B + 2 * j + 1];
+#pragma unroll
+                        for (int w = 1; w < W; ++w) {
+                            gv += red[w * kTileRows + slot * B + 2 * j];
+                            uv += red[w * kTileRows + slot * B + 2 * j + 1];
+                        }
+                        const int64_t n = row0 / 2 + j;
+                        if (n < a.n_out) y[n] = silu_mul(gv, uv);
+                    }
                 }
                 __syncthreads();
             }
-            if (wk == 0) store_tile<M, EPI>(acc, y, a, t, slot, j);
 #pragma unroll
             for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -803,7 +934,7 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
 // i = (tile T0 + i/R, range i%R) goes to wavefront i % G: the items, not whole
 // tiles, are spread over the wavefronts. A wavefront walks its items' units
 // with the next unit's loads in flight; after an item's last unit it reduces
-// the lanes (same butterfly as above) and, for R > 1, parks the 8-row partial
+// the lanes (tile_sums, the same tree as above) and, for R > 1, parks the 8-row partial
 // in LDS. When every wavefront is done, the partials of each row are added in
 // range order, ((p0 + p1) + p2) + ..., and stored (with the SiLU epilogue for
 // gate|up). For any M a row goes through the same operations, so the verify
@@ -913,19 +1044,12 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
             compute_unit<QT, M, XLDS>(cur, acc, k, xs4, x, a.x_stride, nsegw, cu.s - s0, last ? lp.j_last : j,
                                       !last || lp.live_last);
             if (cu.s + 1 == cu.s_end) {
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-#pragma unroll
-                    for (int b = 0; b < B; ++b) acc[m][b] = half_wave_sum(acc[m][b]);
-                if (R == 1) {
-                    store_tile<M, EPI>(acc, y, a, cu.t, slot, j);
-                } else if (j == 0) {
-                    float *pp = part + ((size_t)(cu.t - T0) * R + cu.r) * (M * kTileRows) + slot * B;
-#pragma unroll
-                    for (int m = 0; m < M; ++m)
-#pragma unroll
-                        for (int b = 0; b < B; ++b) pp[m * kTileRows + b] = acc[m][b];
-                }
+                TileSums<M, EPI> sums;
+                tile_sums<M, tile_rs<EPI>()>(acc, sums, j);
+                if (R == 1)
+                    store_tile<M, EPI>(sums, y, a, cu.t, slot, j);
+                else
+                    park_tile<M, EPI>(sums, part + ((size_t)(cu.t - T0) * R + cu.r) * (M * kTileRows) + slot * B, j);
 #pragma unroll
                 for (int m = 0; m < M; ++m)
 #pragma unroll
