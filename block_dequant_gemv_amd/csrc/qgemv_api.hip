@@ -415,7 +415,10 @@ qg_status run_qgemv(int qt, int epi, const void *w, const float *x, void *y, int
     a.tpg = p.tpg;
     a.tstride = p.tstride;
     a.n_wg = p.grid;
+    a.tiles_base = p.persist ? g.n_tiles / p.grid : 0;
+    a.tiles_extra = p.persist ? g.n_tiles % p.grid : 0;
     a.ranges = p.ranges;
+    a.range_segs = g.nseg / p.ranges;
     a.phases = p.phases;
     a.bias = af.bias;
     a.residual = af.residual;

@@ -549,8 +549,10 @@ __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][
 // configuration needs at most 5 per thread: K = 5120 over 256 threads, K =
 // 17408 over 1024). The batch is sized to stay inside the kernels' register
 // budgets (x_batch). Reads are coalesced (consecutive threads, consecutive 16-byte
-// chunks); the LDS stores scatter into the lane-swizzled order. Indexing is
-// 32-bit (the staged area is at most LDS-sized).
+// chunks); the LDS stores scatter into the lane-swizzled order. Each thread
+// walks its chunks incrementally (XWalk) and computes a chunk's row, offset and
+// LDS slot once, when its load is issued. Indexing is 32-bit (the staged area
+// is at most LDS-sized).
 //
 // The first batch is split off (stage_x_issue): a kernel issues it before its
 // first weight loads, so that the activation lines reach the memory queues
@@ -562,83 +564,86 @@ __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][
 // allow) and 4 in the tile form, whose occupancy more registers would lower.
 constexpr int x_batch(int M, bool persistent) { return M == 1 ? 5 : (persistent ? 8 : 4); }
 
+__device__ __forceinline__ uint32_t x_slot(uint32_t i) { return (i & ~255u) | ((i & 7u) << 5) | ((i >> 3) & 31u); }
+
+// Chunk walk of one thread: chunks f = tid, tid + nthr, tid + 2 nthr, ... of
+// the staged area as (row m, chunk i of the row). The stride nthr is dm rows
+// and di chunks, so a step is two adds and at most one wrap; only the first
+// position takes a division. m >= M means past the staged area.
+struct XWalk {
+    uint32_t m, i, dm, di, per_m;
+    __device__ __forceinline__ void step()
+    {
+        i += di;
+        m += dm;
+        if (i >= per_m) {
+            i -= per_m;
+            ++m;
+        }
+    }
+};
+
+__device__ __forceinline__ XWalk x_walk(int64_t nseg)
+{
+    XWalk w;
+    w.per_m = (uint32_t)nseg << 8;
+    const uint32_t nthr = blockDim.x, tid = threadIdx.x;
+    w.dm = nthr / w.per_m;
+    w.di = nthr - w.dm * w.per_m;
+    w.m = tid / w.per_m;
+    w.i = tid - w.m * w.per_m;
+    return w;
+}
+
+// One batch of NB chunks in flight: the values and the LDS float4 slot each one
+// goes to (kNoSlot past the staged area).
+constexpr uint32_t kNoSlot = ~0u;
 template <int NB>
 struct XFirst {
     f32x4 v[NB];
+    uint32_t at[NB];
+    XWalk w;
 };
 
-__device__ __forceinline__ uint32_t x_slot(uint32_t i) { return (i & ~255u) | ((i & 7u) << 5) | ((i >> 3) & 31u); }
-
-// Flat chunk f of the staged area -> (row m, chunk i of the row); inv = 1 / per_m.
-template <int M>
-__device__ __forceinline__ void x_place(uint32_t f, uint32_t per_m, float inv, uint32_t &m, uint32_t &i)
-{
-    if (M == 1) {
-        m = 0;
-        i = f;
-        return;
-    }
-    uint32_t q = (uint32_t)((float)f * inv);   // f < 2^24: within one of f / per_m
-    if (q * per_m > f)
-        --q;
-    else if ((q + 1) * per_m <= f)
-        ++q;
-    m = q;
-    i = f - q * per_m;
-}
-
 template <int M, int NB>
-__device__ __forceinline__ void stage_x_issue(XFirst<NB> &xf, const float *__restrict__ x, int64_t x_stride, int64_t nseg,
-                                              int64_t K)
+__device__ __forceinline__ void x_batch_load(f32x4 (&v)[NB], uint32_t (&at)[NB], XWalk &w,
+                                             const float *__restrict__ x, int64_t x_stride, uint32_t k4)
 {
-    const uint32_t per_m = (uint32_t)nseg << 8;
-    const uint32_t total = (uint32_t)M * per_m;
-    const uint32_t k4 = (uint32_t)(K >> 2);
-    const float inv = 1.0f / (float)per_m;
-    const uint32_t nthr = blockDim.x, tid = threadIdx.x;
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
-        const uint32_t f = tid + q * nthr;
-        uint32_t m, i;
-        x_place<M>(f, per_m, inv, m, i);
-        xf.v[q] = f < total && i < k4 ? *(const f32x4 *)(x + (int64_t)m * x_stride + 4 * (size_t)i)
-                                      : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        const bool in = w.m < (uint32_t)M;
+        v[q] = in && w.i < k4 ? *(const f32x4 *)(x + (uint64_t)w.m * (uint64_t)x_stride + 4 * (size_t)w.i)
+                              : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        at[q] = in ? w.m * w.per_m + x_slot(w.i) : kNoSlot;
+        w.step();
     }
 }
 
 template <int M, int NB>
-__device__ __forceinline__ void stage_x_finish(const XFirst<NB> &xf, f32x4 *xs4, const float *__restrict__ x,
+__device__ __forceinline__ void stage_x_issue(XFirst<NB> &xf, const float *__restrict__ x, int64_t x_stride,
+                                              int64_t nseg, int64_t K)
+{
+    xf.w = x_walk(nseg);
+    x_batch_load<M, NB>(xf.v, xf.at, xf.w, x, x_stride, (uint32_t)(K >> 2));
+}
+
+template <int M, int NB>
+__device__ __forceinline__ void stage_x_finish(XFirst<NB> &xf, f32x4 *xs4, const float *__restrict__ x,
                                                int64_t x_stride, int64_t nseg, int64_t K)
 {
     const uint32_t per_m = (uint32_t)nseg << 8;
     const uint32_t total = (uint32_t)M * per_m;
-    const uint32_t k4 = (uint32_t)(K >> 2);
-    const float inv = 1.0f / (float)per_m;
-    const uint32_t nthr = blockDim.x, tid = threadIdx.x;
+    const uint32_t nthr = blockDim.x;
 #pragma unroll
-    for (int q = 0; q < NB; ++q) {
-        const uint32_t f = tid + q * nthr;
-        uint32_t m, i;
-        x_place<M>(f, per_m, inv, m, i);
-        if (f < total) xs4[m * per_m + x_slot(i)] = xf.v[q];
-    }
-    for (uint32_t base = tid + NB * nthr; base < total; base += NB * nthr) {
+    for (int q = 0; q < NB; ++q)
+        if (xf.at[q] != kNoSlot) xs4[xf.at[q]] = xf.v[q];
+    for (uint32_t base = NB * nthr; base < total; base += NB * nthr) {   // uniform: batches after the first
         f32x4 v[NB];
+        uint32_t at[NB];
+        x_batch_load<M, NB>(v, at, xf.w, x, x_stride, (uint32_t)(K >> 2));
 #pragma unroll
-        for (int q = 0; q < NB; ++q) {
-            const uint32_t f = base + q * nthr;
-            uint32_t m, i;
-            x_place<M>(f, per_m, inv, m, i);
-            v[q] = f < total && i < k4 ? *(const f32x4 *)(x + (int64_t)m * x_stride + 4 * (size_t)i)
-                                       : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-#pragma unroll
-        for (int q = 0; q < NB; ++q) {
-            const uint32_t f = base + q * nthr;
-            uint32_t m, i;
-            x_place<M>(f, per_m, inv, m, i);
-            if (f < total) xs4[m * per_m + x_slot(i)] = v[q];
-        }
+        for (int q = 0; q < NB; ++q)
+            if (at[q] != kNoSlot) xs4[at[q]] = v[q];
     }
 }
 
@@ -928,8 +933,9 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
 // ---------------------------------------------------------------------------
 // Persistent form of the quantised GEMV, for matrices with too few row tiles
 // to balance the CUs one tile per wavefront. One workgroup per CU: workgroup b
-// owns the contiguous tiles [T0, T1) = [b*n_tiles/n_wg, (b+1)*n_tiles/n_wg)
-// (the same number to within one) and stages the activations once. Each tile
+// owns a contiguous run of n_tiles / n_wg tiles, one more for the first
+// n_tiles % n_wg workgroups (the same number to within one), and stages the
+// activations once. Each tile
 // splits along K into R = a.ranges equal ranges of nseg/R segments, and item
 // i = (tile T0 + i/R, range i%R) goes to wavefront i % G: the items, not whole
 // tiles, are spread over the wavefronts. A wavefront walks its items' units
@@ -953,7 +959,7 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
     __shared__ float nred[persist_red_floats(NORM)];
 
     const int tid = threadIdx.x;
-    const int G = blockDim.x >> 6;
+    constexpr int G = persist_threads(QT, M, XLDS) >> 6;   // the launch's wavefronts (checked by the host)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int slot = lane >> 5, j = lane & 31;
@@ -961,9 +967,10 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
     const Geometry &g = a.geo;
     const int64_t K = g.K, nseg = g.nseg;
     const uint32_t R = (uint32_t)a.ranges;
-    const uint32_t L = (uint32_t)(nseg / R);   // segments per range
-    const int64_t T0 = (int64_t)blockIdx.x * g.n_tiles / a.n_wg;
-    const int64_t T1 = ((int64_t)blockIdx.x + 1) * g.n_tiles / a.n_wg;
+    const uint32_t L = (uint32_t)a.range_segs;   // segments per range
+    const uint32_t bx = blockIdx.x, extra = (uint32_t)a.tiles_extra;
+    const int64_t T0 = (int64_t)bx * a.tiles_base + (bx < extra ? bx : extra);
+    const int64_t T1 = T0 + a.tiles_base + (bx < extra ? 1 : 0);
     // Phases: the ranges are walked in P phases; phase ph takes the ranges
     // [r0, r1) = [R ph / P, R (ph + 1) / P), stages only the activations of
     // their segments [r0 L, r1 L) (a window of nsegw segments; all of them when
@@ -977,26 +984,31 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
     const LanePlace lp = lane_place(g, slot, j);
 
     // A cursor over this wavefront's units of the phase whose first range is r0:
-    // item i, its tile and range, segment s.
+    // item i = q RP + rl (tile T0 + q, range r = r0 + rl), segment s. The items
+    // of a wavefront are i = wave, wave + G, ...: with G = qG RP + rG a step to
+    // the next item is two adds and at most one wrap.
     struct Cur {
-        uint32_t i, r;
+        uint32_t q, rl, r;
         int64_t t, s, s_end;
     };
-    uint32_t r0 = 0, RP = R;
+    uint32_t r0 = 0, RP = R, qG = 0, rG = 0;
     auto seat = [&](Cur &c) {
-        const uint32_t q = c.i / RP;
-        c.r = r0 + (c.i - q * RP);
-        c.t = T0 + q;
+        c.r = r0 + c.rl;
+        c.t = T0 + c.q;
         c.s = (int64_t)c.r * L;
         c.s_end = c.s + L;
     };
     auto advance = [&](Cur &c) {
         if (++c.s == c.s_end) {
-            c.i += G;
+            c.rl += rG;
+            c.q += qG;
+            if (c.rl >= RP) {
+                c.rl -= RP;
+                ++c.q;
+            }
             seat(c);
         }
     };
-
     float acc[M][B];
 #pragma unroll
     for (int m = 0; m < M; ++m)
@@ -1014,8 +1026,11 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
         const float *xw = x + s0 * kSegWeights;   // the window's first activation of row 0
         const int64_t Kw = K - s0 * kSegWeights;  // activations of a row from the window on
         if (PHASED && ph > 0) __syncthreads();    // every wavefront done with the previous window
+        qG = (uint32_t)G / RP;
+        rG = (uint32_t)G - qG * RP;
         Cur ld, cu;
-        ld.i = wave;
+        ld.q = (uint32_t)wave / RP;
+        ld.rl = (uint32_t)wave - ld.q * RP;
         seat(ld);
         cu = ld;
         int64_t u_ld = 0;

@@ -27,8 +27,12 @@ struct QArgs {
     int64_t tpg;         // row tiles walked by one group of W wavefronts (tstride == 0)
     int64_t tstride;     // > 0: group g walks tiles g, g + tstride, g + 2*tstride, ... (tstride = groups)
     // persistent form only
-    int64_t n_wg;        // workgroups; workgroup b owns tiles [b*n_tiles/n_wg, (b+1)*n_tiles/n_wg)
+    int64_t n_wg;        // workgroups; workgroup b owns tiles_base tiles, one more for b < tiles_extra
+                         // (tiles_base = n_tiles / n_wg, tiles_extra = n_tiles % n_wg), contiguous
+    int64_t tiles_base;
+    int64_t tiles_extra;
     int64_t ranges;      // K ranges per tile (divides nseg); item = (tile, range)
+    int64_t range_segs;  // segments per range (nseg / ranges)
     int64_t phases;      // divides ranges: the ranges are walked in phases of ranges/phases, each with
                          // only its segments' activations staged in LDS (1: all at once)
     // kEpiAffine only (M = 1): fp32 addends (either may be null) and the output type
