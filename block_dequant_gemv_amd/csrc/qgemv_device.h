@@ -559,10 +559,11 @@ __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][
 // ahead of the weight stream instead of behind it, and writes it
 // (stage_x_finish, which also stages anything past the first batch) after
 // them. The caller synchronises the workgroup afterwards.
-// Chunks per thread and batch: 5 for one row; for several rows 8 in the
+// Chunks per thread and batch: 5 for one row; for several rows in the
 // persistent form (launched at 2 or 3 wavefronts per SIMD, which its registers
-// allow) and 4 in the tile form, whose occupancy more registers would lower.
-constexpr int x_batch(int M, bool persistent) { return M == 1 ? 5 : (persistent ? 8 : 4); }
+// allow) 8, and 10 for 5 or 6 rows (K = 5120 at 768 threads: one batch); 4 in
+// the tile form, whose occupancy more registers would lower.
+constexpr int x_batch(int M, bool persistent) { return M == 1 ? 5 : (persistent ? (M >= 5 ? 10 : 8) : 4); }
 
 __device__ __forceinline__ uint32_t x_slot(uint32_t i) { return (i & ~255u) | ((i & 7u) << 5) | ((i >> 3) & 31u); }
 
