@@ -564,7 +564,10 @@ GemmPlan plan_gemm(int qt, int64_t N, int64_t K, int64_t M)
 //    48 and 256 rows x 5120 within 0.1-0.3 us (every form of these two reads
 //    the ~3.9 us dispatch floor by kernel timestamps);
 //  - row form (K = 512 L, L <= 16): one wavefront per row with the whole row's
-//    loads in flight at once, x staged in LDS once per workgroup of 4 rows.
+//    loads in flight at once, x staged in LDS once per workgroup of 4 rows
+//    (8 from 4096 rows on, which halves the activation copies: one 4 K-byte
+//    copy per 8 rows instead of per 4; cold, kernel timestamps: 5120 x 5120
+//    10.04 -> 9.84 us, 17408 x 5120 28.0 -> 27.7, 5120 x 8192 unchanged).
 //    Measured on MI355X, cold, against the lane-split form: 5120 x 5120 9.96
 //    against 10.78 us, 5120 x 8192 15.3 against 17.2, 17408 x 4096 22.4
 //    against 27.0;
@@ -686,7 +689,7 @@ qgk::F16Plan plan_f16(int64_t N, int64_t K, const void *w_f16, const float *x)
     const bool row_ok = p.vec && K % 512 == 0 && K / 512 <= qgk::kF16RowMaxL;
     if (row_ok && form != 0) {
         p.L = (int)(K / 512);
-        p.waves = (w_env == 2 || w_env == 4 || w_env == 8) ? (int)w_env : (N < 1024 ? 2 : 4);
+        p.waves = (w_env == 2 || w_env == 4 || w_env == 8) ? (int)w_env : (N < 1024 ? 2 : (N < 4096 ? 4 : 8));
         p.grid = (N + p.waves - 1) / p.waves;
         return p;
     }

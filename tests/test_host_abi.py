@@ -441,9 +441,11 @@ def test_f16_form_rule_as_documented(L):
         p = qg.qg_f16_plan_info(N, K)
         assert p["form"] == "split-K row" and p["workgroups"] == N, (N, K, p)
         assert p["waves"] == -(-(K // 8) // 256) and p["waves"] <= 16
-    for N, K in ((1024, 5120), (5120, 5120), (17408, 512), (2049, 8192)):
+    # row form: 4 rows per workgroup, 8 from 4096 rows on
+    for N, K in ((1024, 5120), (4095, 5120), (2049, 8192), (4096, 5120), (5120, 5120), (17408, 512)):
         p = qg.qg_f16_plan_info(N, K)
-        assert p["form"] == "row" and p["waves"] == 4, (N, K, p)
+        assert p["form"] == "row" and p["waves"] == (4 if N < 4096 else 8), (N, K, p)
+        assert p["workgroups"] == -(-N // p["waves"]), (N, K, p)
     for N, K in ((1023, 32776), (5120, 1000), (1024, 8200), (5120, 8704), (300, 7)):
         assert qg.qg_f16_plan_info(N, K)["form"] == "lane-split", (N, K)
     for N, K in ((48, 5120), (5120, 5120)):
