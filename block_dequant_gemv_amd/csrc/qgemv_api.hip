@@ -243,7 +243,8 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M, bool norm = false)
         if (lds || !norm) {
             p.x_in_lds = lds;
             p.lds_bytes = (lds ? window(p.phases) : 0) + part;
-            p.block = qgk::persist_threads(qt, M, lds);
+            p.one_unit = ranges == g.nseg;
+            p.block = qgk::persist_threads(qt, M, lds, p.one_unit);
             return p;
         }
         // The RMSNorm prologue needs the staged copy: when it does not fit next to

@@ -31,6 +31,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "dequant.h"
 #include "layout.h"
@@ -948,8 +949,8 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
 // rows still equal the M=1 rows bit for bit. PHASED (several activation rows
 // that do not fit in LDS at once): the ranges are walked in phases, each
 // staging only its segments' activations (see the phase loop below).
-template <int QT, int M, int EPI, bool XLDS, bool NORM, bool PHASED = false>
-__global__ void __launch_bounds__(persist_threads(QT, M, XLDS))
+template <int QT, int M, int EPI, bool XLDS, bool NORM, bool PHASED = false, bool ONE = false>
+__global__ void __launch_bounds__(persist_threads(QT, M, XLDS, ONE))
 qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float *__restrict__ y, QArgs a)
 {
     static_assert(!NORM || (XLDS && M == 1), "the RMSNorm prologue works on staged single-row activations");
@@ -960,7 +961,7 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
     __shared__ float nred[persist_red_floats(NORM)];
 
     const int tid = threadIdx.x;
-    constexpr int G = persist_threads(QT, M, XLDS) >> 6;   // the launch's wavefronts (checked by the host)
+    constexpr int G = persist_threads(QT, M, XLDS, ONE) >> 6;   // the launch's wavefronts (checked by the host)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int slot = lane >> 5, j = lane & 31;
@@ -1057,9 +1058,18 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
             ++u_ld;
             __builtin_amdgcn_sched_barrier(0);
             const bool last = cu.s == nseg - 1;
+            if (ONE) {
+                // every item is this one unit: its sums start from zero here, and no
+                // accumulator lives from one unit to the next (the same operations:
+                // the general form zeroes acc after each item)
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int b = 0; b < B; ++b) acc[m][b] = 0.0f;
+            }
             compute_unit<QT, M, XLDS>(cur, acc, k, xs4, x, a.x_stride, nsegw, cu.s - s0, last ? lp.j_last : j,
                                       !last || lp.live_last);
-            if (cu.s + 1 == cu.s_end) {
+            if (ONE || cu.s + 1 == cu.s_end) {
                 TileSums<M, EPI> sums;
                 tile_sums<M, tile_rs<EPI>()>(acc, sums, j);
                 if (R == 1)
@@ -1173,29 +1183,36 @@ template <int QT, int M, int EPI>
 static hipError_t launch_persist(const uint8_t *wp, const float *x, float *y, const QArgs &a, const QPlan &p,
                                  hipStream_t stream)
 {
-    auto kern = p.x_in_lds ? qgemv_persist<QT, M, EPI, true, false> : qgemv_persist<QT, M, EPI, false, false>;
-    int which = p.norm ? 2 : (p.x_in_lds ? 0 : 1);
-    if (p.phases > 1) {
-        // several activation rows walked in phases (staged windows), plain store only
-        if constexpr (M > 1 && EPI == kEpiPlain) {
-            if (!p.x_in_lds || p.norm) return hipErrorInvalidConfiguration;
-            kern = qgemv_persist<QT, M, EPI, true, false, true>;
-            which = 3;
-        } else {
-            return hipErrorInvalidConfiguration;
+    // ONE: every item is one unit (one segment per K range)
+    auto pick = [&](auto one) -> std::pair<decltype(&qgemv_persist<QT, M, EPI, true, false>), int> {
+        constexpr bool ONE = decltype(one)::value;
+        if (p.phases > 1) {
+            // several activation rows walked in phases (staged windows), plain store only
+            if constexpr (M > 1 && EPI == kEpiPlain) {
+                if (!p.x_in_lds || p.norm) return {nullptr, 0};
+                return {qgemv_persist<QT, M, EPI, true, false, true, ONE>, 3};
+            } else {
+                return {nullptr, 0};
+            }
         }
-    }
-    if (p.norm) {
-        // the RMSNorm prologue: single-row plain and gate|up kernels with staged activations
-        if constexpr (M == 1 && EPI != kEpiAffine) {
-            if (!p.x_in_lds) return hipErrorInvalidConfiguration;
-            kern = qgemv_persist<QT, M, EPI, true, true>;
-        } else {
-            return hipErrorInvalidConfiguration;
+        if (p.norm) {
+            // the RMSNorm prologue: single-row plain and gate|up kernels with staged activations
+            if constexpr (M == 1 && EPI != kEpiAffine) {
+                if (!p.x_in_lds) return {nullptr, 0};
+                return {qgemv_persist<QT, M, EPI, true, true, false, ONE>, 2};
+            } else {
+                return {nullptr, 0};
+            }
         }
-    }
-    if (p.block != persist_threads(QT, M, p.x_in_lds)) return hipErrorInvalidConfiguration;
-    static std::atomic<int> lds_set[4][16];   // one record per kernel chosen above
+        return p.x_in_lds ? std::make_pair(qgemv_persist<QT, M, EPI, true, false, false, ONE>, 0)
+                          : std::make_pair(qgemv_persist<QT, M, EPI, false, false, false, ONE>, 1);
+    };
+    const auto kw = p.one_unit ? pick(std::true_type{}) : pick(std::false_type{});
+    const auto kern = kw.first;
+    const int which = kw.second + (p.one_unit ? 4 : 0);
+    if (kern == nullptr) return hipErrorInvalidConfiguration;
+    if (p.block != persist_threads(QT, M, p.x_in_lds, p.one_unit)) return hipErrorInvalidConfiguration;
+    static std::atomic<int> lds_set[8][16];   // one record per kernel chosen above
     hipError_t e = ensure_lds_limit((const void *)kern, p.lds_bytes, lds_set[which]);
     if (e != hipSuccess) return e;
     launch(kern, dim3((unsigned)p.grid), dim3(p.block), (uint32_t)p.lds_bytes, stream, wp, x, y, a);

@@ -63,6 +63,7 @@ struct QPlan {
     size_t lds_bytes;    // dynamic LDS per workgroup
     bool norm;           // RMSNorm prologue on the staged activations (M = 1, x_in_lds)
     int row_groups = 1;  // tile form, plain store: gridDim.y groups of the kernel's M activation rows each
+    bool one_unit = false;   // persistent form with one segment per K range (every item is one unit)
 };
 
 struct F16Plan {
@@ -124,10 +125,20 @@ constexpr int qgemv_max_threads(int QT, int M, int W)
 // 17408 x 5120 at M = 3: 22.2 -> 21.5 us against 12 wavefronts, M = 2
 // unchanged); the other multi-row kernels up to 168 (12 wavefronts) where they
 // fit without spilling, else 256 (8); Q4_K with 5 or 6 rows 4 wavefronts (512
-// registers each, no scratch).
-constexpr int persist_threads(int qt, int M, bool xlds)
+// registers each, no scratch). one: every item is one unit (one segment per K
+// range), so no accumulator lives from one unit to the next (Q4_0 at M = 6
+// with staged activations: 149 -> 111 VGPRs): Q4_0 fits 128 VGPRs at every M
+// (with activations from L2 up to 5 rows), Q8_0 with staged activations up to 4
+// rows, 168 above; Q6_K fits 168 up to 3 rows (4 with staged activations) and
+// 256 without scratch at 5 and 6 (the general form spills there).
+constexpr int persist_threads(int qt, int M, bool xlds, bool one = false)
 {
     if (M == 1) return 1024;
+    if (one) {
+        if (qt == qgl::kQ4_0) return (xlds || M <= 5) ? 1024 : 768;
+        if (qt == qgl::kQ8_0 && xlds) return M <= 4 ? 1024 : 768;
+        if (qt == qgl::kQ6_K) return (M <= 3 || (M == 4 && xlds)) ? 768 : 512;
+    }
     if (qt == qgl::kQ4_0) return M <= 3 ? 1024 : ((M <= 4 || xlds) ? 768 : 512);
     if (qt == qgl::kQ4_K) return M <= 2 ? 768 : (M <= 4 ? 512 : 256);
     if (qt == qgl::kQ6_K) return M <= 2 ? 768 : 512;
