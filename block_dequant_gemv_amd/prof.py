@@ -251,7 +251,7 @@ MFMA_COUNTERS = ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUS
                  "SQ_INSTS_SALU", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE"]
 # the headline step's calls: bench.py label -> the kernel launch shape that runs it
 STEP_CALLS = {"gate|up 2x17408x5120 silu": "qgk::qgemv_kernel<2, 1, 1, 1, true, 1, false>|1088x256",
-              "down 5120x17408": "qgk::qgemv_persist<2, 1, 0, true, false, false>|256x1024",
+              "down 5120x17408": "qgk::qgemv_persist<2, 1, 0, true, false, false, true>|256x1024",
               "lm_head 248320x5120": "qgk::qgemv_kernel<2, 1, 0, 1, true, 1, false>|7760x256"}
 
 
