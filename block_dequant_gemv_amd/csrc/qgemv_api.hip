@@ -177,14 +177,22 @@ constexpr int64_t kPersistTiles = 4096;
 constexpr int64_t kPersistUnits = 2048;   // below this many (tile, segment) units the other form is faster
 constexpr size_t kPartialBudget = 64 * 1024;   // LDS for the range partials at M = 6
 
-bool plan_persist(int64_t rows, int64_t K, int64_t *ranges, int64_t *grid, int64_t *max_tiles)
+bool plan_persist(int qt, int64_t rows, int64_t K, int64_t *ranges, int64_t *grid, int64_t *max_tiles)
 {
     const int64_t n_tiles = (rows + qgl::kTileRows - 1) / qgl::kTileRows;
     const int64_t nseg = (K / 32 + qgl::kSegBlocks - 1) / qgl::kSegBlocks;
     const int64_t forced = tune(kPersist);
     if (forced == 0 || (forced != 1 && (n_tiles >= kPersistTiles || n_tiles * nseg < kPersistUnits))) return false;
     *grid = std::min<int64_t>(cu_count(), n_tiles);
-    *max_tiles = (n_tiles + *grid - 1) / *grid;
+    // a workgroup owns up to ceil(2 n_tiles / grid) half-tiles, which touch at
+    // most one tile more than half of them (a run may start at a tile's second half)
+    const int64_t halves = (2 * n_tiles + *grid - 1) / *grid;
+    *max_tiles = (halves + 2) / 2;
+    // the kernel addresses a workgroup's tiles with 32-bit offsets below 2^31,
+    // products of 24-bit tile indices and tile sizes
+    const qgl::Geometry g = qgl::geometry(qt, rows, K);
+    const int64_t tile_bytes = std::max(g.tile_q, std::max(g.tile_s, g.tile_u));
+    if (tile_bytes >= ((int64_t)1 << 24) || *max_tiles * tile_bytes >= ((int64_t)1 << 31)) return false;
     // one segment per item when the partials fit, else the largest divisor of nseg that fits
     int64_t r = std::min<int64_t>(nseg, 32);
     while (r > 1 && (nseg % r != 0 || (size_t)(*max_tiles * r * 6 * qgl::kTileRows * 4) > kPartialBudget)) --r;
@@ -207,7 +215,7 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M, bool norm = false)
     const size_t xbytes = (size_t)M * (size_t)g.nseg * qgl::kSegWeights * sizeof(float);
     const int64_t xg_env = tune(kXGlobal);
     int64_t ranges = 1, pgrid = 0, max_tiles = 0;
-    p.persist = plan_persist(rows, K, &ranges, &pgrid, &max_tiles);
+    p.persist = plan_persist(qt, rows, K, &ranges, &pgrid, &max_tiles);
     p.depth = 1;
     p.tpg = 1;
     p.tstride = 0;
@@ -244,7 +252,7 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M, bool norm = false)
             p.x_in_lds = lds;
             p.lds_bytes = (lds ? window(p.phases) : 0) + part;
             p.one_unit = ranges == g.nseg;
-            p.block = qgk::persist_threads(qt, M, lds, p.one_unit);
+            p.block = qgk::persist_threads(qt, M, lds, p.one_unit, p.phases > 1);
             return p;
         }
         // The RMSNorm prologue needs the staged copy: when it does not fit next to
@@ -416,8 +424,8 @@ qg_status run_qgemv(int qt, int epi, const void *w, const float *x, void *y, int
     a.tpg = p.tpg;
     a.tstride = p.tstride;
     a.n_wg = p.grid;
-    a.tiles_base = p.persist ? g.n_tiles / p.grid : 0;
-    a.tiles_extra = p.persist ? g.n_tiles % p.grid : 0;
+    a.halves_base = p.persist ? 2 * g.n_tiles / p.grid : 0;
+    a.halves_extra = p.persist ? 2 * g.n_tiles % p.grid : 0;
     a.ranges = p.ranges;
     a.range_segs = g.nseg / p.ranges;
     a.phases = p.phases;

@@ -276,6 +276,64 @@ __device__ __forceinline__ void load_unit(Unit<QT> &u, const uint8_t *__restrict
     }
 }
 
+// Per-lane form of load_unit for the persistent kernel, whose two wavefront
+// halves may work on different row tiles and segments: every plane's
+// descriptor is based at the workgroup's first tile T0 and covers the `span`
+// tiles it touches, and each lane's whole offset (tile, segment, slot, block,
+// row) is in its VGPR (24-bit multiplies: the host keeps a tile's planes below
+// 2^24 bytes and span * tile bytes below 2^31). No branch: a branch around the
+// loads makes the compiler wait for every load in flight. A lane with `alive`
+// false gets an offset past the descriptor's range, so its loads return zeros
+// without a memory access.
+constexpr uint32_t kDeadOffset = 0x80000000u;
+template <int QT>
+__device__ __forceinline__ void load_unit_lane(Unit<QT> &u, const uint8_t *__restrict__ wp, const Geometry &g,
+                                               int64_t T0, uint32_t span, uint32_t t_rel, uint32_t s,
+                                               uint32_t slot, int j, bool alive)
+{
+    constexpr int NH = Unit<QT>::NH;
+    constexpr uint32_t seg_q = (uint32_t)(kTileRows * kSegBlocks * packed_quant_bytes(QT));
+    constexpr uint32_t seg_s = (uint32_t)(kTileRows * kSegBlocks * 2);
+    const uint32_t tq = (uint32_t)g.tile_q, ts = (uint32_t)g.tile_s;
+    const uint32_t nb_last = (uint32_t)seg_blocks(g, g.nseg - 1);
+    const bool last = s == (uint32_t)(g.nseg - 1);
+    const uint32_t nb = last ? nb_last : (uint32_t)kSegBlocks;
+    const uint32_t jc = last && (uint32_t)j >= nb_last ? nb_last - 1 : (uint32_t)j;
+    const uint32_t ustride = (uint32_t)kSlots * nb * kUnit;
+    const uint32_t lane_u = (slot * nb + jc) * kUnit;
+    const uint32_t off = alive ? __umul24(t_rel, tq) + s * seg_q + lane_u : kDeadOffset;
+    const __amdgpu_buffer_rsrc_t rq = plane_rsrc(wp + T0 * g.tile_q, (int)(span * tq));
+#pragma unroll
+    for (int b = 0; b < kRowsPerLane; ++b)
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+            u.q[b][h] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(off + (uint32_t)(b * NH + h) * ustride), 0,
+                                                              kLoadNT);
+    const __amdgpu_buffer_rsrc_t rs = plane_rsrc(wp + g.scale_off + T0 * g.tile_s, (int)(span * ts));
+    const uint32_t off_s = alive ? __umul24(t_rel, ts) + s * seg_s + (lane_u >> 1) : kDeadOffset;
+    u.sc = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off_s, 0, kLoadNT);
+    if constexpr (QT == kQ4_K || QT == kQ6_K) {
+        constexpr uint32_t ub = (QT == kQ4_K) ? 4 : 2;   // super-plane bytes per row
+        const uint32_t tu = (uint32_t)g.tile_u;
+        const uint32_t sup = slot * (nb / kSuperBlocks) + jc / kSuperBlocks;
+        const uint32_t off_u = alive ? __umul24(t_rel, tu) +
+                                           s * (uint32_t)(kTileRows * (kSegBlocks / kSuperBlocks) * ub) +
+                                           sup * (kRowsPerLane * ub)
+                                     : kDeadOffset;
+        const __amdgpu_buffer_rsrc_t ru = plane_rsrc(wp + g.sup_off + T0 * g.tile_u, (int)(span * tu));
+        if constexpr (QT == kQ4_K)
+            u.sup = __builtin_amdgcn_raw_buffer_load_b128(ru, (int)off_u, 0, kLoadNT);
+        else
+            u.sup = __builtin_amdgcn_raw_buffer_load_b64(ru, (int)off_u, 0, kLoadNT);
+    }
+    if constexpr (QT == kQ6_K) {
+#pragma unroll
+        for (int bp = 0; bp < 2; ++bp)
+            u.hq[bp] = __builtin_amdgcn_raw_buffer_load_b128(
+                rq, (int)(off + (uint32_t)(kRowsPerLane + bp) * ustride), 0, kLoadNT);
+    }
+}
+
 // acc[m][b] += d_b * sum_e v_e * x_m[e] over the lane's block of segment s.
 // j is the block whose activations the lane reads; live is false only for
 // lanes past the end of a ragged last segment.
@@ -934,23 +992,27 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
 
 // ---------------------------------------------------------------------------
 // Persistent form of the quantised GEMV, for matrices with too few row tiles
-// to balance the CUs one tile per wavefront. One workgroup per CU: workgroup b
-// owns a contiguous run of n_tiles / n_wg tiles, one more for the first
-// n_tiles % n_wg workgroups (the same number to within one), and stages the
-// activations once. Each tile
-// splits along K into R = a.ranges equal ranges of nseg/R segments, and item
-// i = (tile T0 + i/R, range i%R) goes to wavefront i % G: the items, not whole
-// tiles, are spread over the wavefronts. A wavefront walks its items' units
-// with the next unit's loads in flight; after an item's last unit it reduces
-// the lanes (tile_sums, the same tree as above) and, for R > 1, parks the 8-row partial
-// in LDS. When every wavefront is done, the partials of each row are added in
-// range order, ((p0 + p1) + p2) + ..., and stored (with the SiLU epilogue for
-// gate|up). For any M a row goes through the same operations, so the verify
-// rows still equal the M=1 rows bit for bit. PHASED (several activation rows
-// that do not fit in LDS at once): the ranges are walked in phases, each
-// staging only its segments' activations (see the phase loop below).
+// to balance the CUs one tile per wavefront. One workgroup per CU, and the work
+// is split in half-tiles: the 4 rows of one slot of a row tile are outputs of
+// their own, so workgroup b owns a contiguous run of 2 n_tiles / n_wg
+// half-tiles, one more for the first 2 n_tiles % n_wg workgroups (the same
+// number to within one: 17408 x 5120 gives every CU 17, where whole tiles gave
+// half of them 9 and half 8), and stages the activations once. Each half-tile
+// splits along K into R = a.ranges equal ranges of nseg/R segments; each half
+// of a wavefront takes one (half-tile, range) item, the two halves usually the
+// same range of neighbouring half-tiles, so a wavefront-unit still reads two
+// 512-byte runs per load and shares its activation reads. A wavefront walks
+// its units with the next unit's loads in flight; after an item's last unit
+// each half reduces its 32 lanes (tile_sums, the same tree as above) and, for
+// R > 1, parks its 4-row partial in LDS. When every wavefront is done, the
+// partials of each row are added in range order, ((p0 + p1) + p2) + ..., and
+// stored (with the SiLU epilogue for gate|up). For any M a row goes through
+// the same operations, so the verify rows still equal the M=1 rows bit for
+// bit. PHASED (several activation rows that do not fit in LDS at once): the
+// ranges are walked in phases, each staging only its segments' activations
+// (see the phase loop below).
 template <int QT, int M, int EPI, bool XLDS, bool NORM, bool PHASED = false, bool ONE = false>
-__global__ void __launch_bounds__(persist_threads(QT, M, XLDS, ONE))
+__global__ void __launch_bounds__(persist_threads(QT, M, XLDS, ONE, PHASED))
 qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float *__restrict__ y, QArgs a)
 {
     static_assert(!NORM || (XLDS && M == 1), "the RMSNorm prologue works on staged single-row activations");
@@ -961,54 +1023,58 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
     __shared__ float nred[persist_red_floats(NORM)];
 
     const int tid = threadIdx.x;
-    constexpr int G = persist_threads(QT, M, XLDS, ONE) >> 6;   // the launch's wavefronts (checked by the host)
+    constexpr int G = persist_threads(QT, M, XLDS, ONE, PHASED) >> 6;   // the launch's wavefronts (checked by the host)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int slot = lane >> 5, j = lane & 31;
+    const uint32_t hw = (uint32_t)lane >> 5;   // wavefront half: its own (half-tile, K range) item
+    const int j = lane & 31;
 
     const Geometry &g = a.geo;
     const int64_t K = g.K, nseg = g.nseg;
     const uint32_t R = (uint32_t)a.ranges;
-    const uint32_t L = (uint32_t)a.range_segs;   // segments per range
-    const uint32_t bx = blockIdx.x, extra = (uint32_t)a.tiles_extra;
-    const int64_t T0 = (int64_t)bx * a.tiles_base + (bx < extra ? bx : extra);
-    const int64_t T1 = T0 + a.tiles_base + (bx < extra ? 1 : 0);
+    const uint32_t L = ONE ? 1u : (uint32_t)a.range_segs;   // segments per range (1 for single-unit items)
+    // Half-tiles h = 2 tile + slot (4 weight rows each). Workgroup b owns the
+    // half-tiles [H0, H0 + nh); it touches the tiles T0 = H0 / 2 .. T0 + span - 1
+    // (the first and the last may be shared with a neighbour, each owning its half).
+    const uint32_t bx = blockIdx.x, hextra = (uint32_t)a.halves_extra;
+    const int64_t H0 = (int64_t)bx * a.halves_base + (bx < hextra ? bx : hextra);
+    const uint32_t nh = (uint32_t)a.halves_base + (bx < hextra ? 1u : 0u);
+    const int64_t T0 = H0 >> 1;
+    const uint32_t h0 = (uint32_t)(H0 & 1);   // half-tile index of H0 within its tile
+    const uint32_t span = (h0 + nh + 1) >> 1;
     // Phases: the ranges are walked in P phases; phase ph takes the ranges
     // [r0, r1) = [R ph / P, R (ph + 1) / P), stages only the activations of
     // their segments [r0 L, r1 L) (a window of nsegw segments; all of them when
-    // P = 1) and spreads its items i = (tile T0 + i / RP, range r0 + i % RP),
-    // RP = r1 - r0, over the wavefronts. The partials follow the largest window.
+    // P = 1) and lists its items range by range: i = rl nh + hl (range r0 + rl,
+    // half-tile H0 + hl). Wavefront-unit u is the item pair (2u, 2u + 1), one
+    // per wavefront half, and wavefront w takes the units w, w + G, ...; so a
+    // workgroup's load is its half-tiles' share whatever the split into tiles.
+    // The partials follow the largest window.
     const uint32_t P = PHASED ? (uint32_t)a.phases : 1u;
     const uint32_t nsegw_max = PHASED ? (R + P - 1) / P * L : (uint32_t)nseg;
     float *part = (float *)(xs4 + (XLDS ? (uint32_t)M * (nsegw_max << 8) : 0u));   // [tile][range][m][8]
 
     const Consts k = make_consts();
-    const LanePlace lp = lane_place(g, slot, j);
 
     // A cursor over this wavefront's units of the phase whose first range is r0:
-    // item i = q RP + rl (tile T0 + q, range r = r0 + rl), segment s. The items
-    // of a wavefront are i = wave, wave + G, ...: with G = qG RP + rG a step to
-    // the next item is two adds and at most one wrap.
+    // wavefront-unit (pair) u, whose even item is 2u = rl nh + hl, and unit kk < L
+    // of the items; wave-uniform (scalar registers). The wavefront's pairs are
+    // u = wave, wave + G, ...: with 2 G = qH nh + rH a step to the next pair is
+    // two adds and at most one wrap. A half's own item is the pair's even item
+    // moved by hw (half): one add and at most one wrap, in `where`.
     struct Cur {
-        uint32_t q, rl, r;
-        int64_t t, s, s_end;
+        uint32_t rl, hl, kk;
     };
-    uint32_t r0 = 0, RP = R, qG = 0, rG = 0;
-    auto seat = [&](Cur &c) {
-        c.r = r0 + c.rl;
-        c.t = T0 + c.q;
-        c.s = (int64_t)c.r * L;
-        c.s_end = c.s + L;
-    };
+    uint32_t r0 = 0, RP = R, qH = 0, rH = 0;
     auto advance = [&](Cur &c) {
-        if (++c.s == c.s_end) {
-            c.rl += rG;
-            c.q += qG;
-            if (c.rl >= RP) {
-                c.rl -= RP;
-                ++c.q;
+        if (++c.kk == L) {
+            c.kk = 0;
+            c.hl += rH;
+            c.rl += qH;
+            if (c.hl >= nh) {
+                c.hl -= nh;
+                ++c.rl;
             }
-            seat(c);
         }
     };
     float acc[M][B];
@@ -1021,30 +1087,57 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
         r0 = PHASED ? R * ph / P : 0u;
         RP = PHASED ? R * (ph + 1) / P - r0 : R;
         const uint32_t nsegw = PHASED ? RP * L : (uint32_t)nseg;
-        const uint32_t n_items = (uint32_t)(T1 - T0) * RP;
-        const uint32_t my_items = n_items > (uint32_t)wave ? (n_items - (uint32_t)wave + G - 1) / G : 0u;
-        const int64_t n_units = (int64_t)my_items * L;
+        const uint32_t n_pairs = (nh * RP + 1) >> 1;
+        const uint32_t my_pairs = n_pairs > (uint32_t)wave ? (n_pairs - (uint32_t)wave + G - 1) / G : 0u;
+        const int64_t n_units = (int64_t)my_pairs * L;
         const int64_t s0 = PHASED ? (int64_t)r0 * L : 0;
         const float *xw = x + s0 * kSegWeights;   // the window's first activation of row 0
         const int64_t Kw = K - s0 * kSegWeights;  // activations of a row from the window on
         if (PHASED && ph > 0) __syncthreads();    // every wavefront done with the previous window
-        qG = (uint32_t)G / RP;
-        rG = (uint32_t)G - qG * RP;
+        qH = (uint32_t)(2 * G) / nh;
+        rH = (uint32_t)(2 * G) - qH * nh;
         Cur ld, cu;
-        ld.q = (uint32_t)wave / RP;
-        ld.rl = (uint32_t)wave - ld.q * RP;
-        seat(ld);
+        {
+            const uint32_t i0 = 2u * (uint32_t)wave;
+            ld.rl = i0 / nh;
+            ld.hl = i0 - ld.rl * nh;
+            ld.kk = 0;
+        }
         cu = ld;
         int64_t u_ld = 0;
+        // the unit of the pair cursor c for this lane's half: its tile (relative
+        // to T0), slot and segment, and whether the half has an item (the last
+        // pair of a phase may have one only); a dead half reads the window's
+        // first segment (in bounds; it loads zeros, and its sums are neither
+        // parked nor stored)
+        auto where = [&](const Cur &c, uint32_t &t_rel, uint32_t &slot, uint32_t &seg, uint32_t &r, bool &dead) {
+            uint32_t hl = c.hl + hw, rl = c.rl;
+            if (hl >= nh) {
+                hl -= nh;
+                ++rl;
+            }
+            dead = rl >= RP;
+            const uint32_t h = h0 + hl;
+            t_rel = h >> 1;
+            slot = h & 1u;
+            r = r0 + rl;
+            seg = dead ? r0 * L : r * L + c.kk;
+        };
+        auto load = [&](Unit<QT> &u) {
+            uint32_t t_rel, slot, seg, r;
+            bool dead;
+            where(ld, t_rel, slot, seg, r, dead);
+            load_unit_lane<QT>(u, wp, g, T0, span, t_rel, seg, slot, j, u_ld < n_units && !dead);
+            advance(ld);
+            ++u_ld;
+        };
 
         // phased windows are staged in batches of 4 (the registers of the phased
         // kernels are at their limit)
         XFirst<PHASED ? 4 : x_batch(M, true)> xf;
         if (XLDS) stage_x_issue<M>(xf, xw, a.x_stride, nsegw, Kw);
         Unit<QT> ring[S];
-        load_unit<QT>(ring[0], wp, g, ld.t, ld.s, lp, u_ld < n_units);
-        advance(ld);
-        ++u_ld;
+        load(ring[0]);
 
         if (XLDS) {
             stage_x_finish<M>(xf, xs4, xw, a.x_stride, nsegw, Kw);
@@ -1052,12 +1145,16 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
         }
         if (NORM) norm_staged_x(xs4, nred, a.gamma, a.eps, K);
 
+        const uint32_t nb_last = (uint32_t)seg_blocks(g, g.nseg - 1);
         auto step = [&](Unit<QT> &cur, Unit<QT> &nxt) {
-            load_unit<QT>(nxt, wp, g, ld.t, ld.s, lp, u_ld < n_units);
-            advance(ld);
-            ++u_ld;
+            load(nxt);
             __builtin_amdgcn_sched_barrier(0);
-            const bool last = cu.s == nseg - 1;
+            uint32_t t_rel, slot, seg, r;
+            bool dead;
+            where(cu, t_rel, slot, seg, r, dead);
+            const bool last = seg == (uint32_t)(nseg - 1);
+            const int jc = last && (uint32_t)j >= nb_last ? (int)nb_last - 1 : j;
+            const bool live = !last || (uint32_t)j < nb_last;
             if (ONE) {
                 // every item is this one unit: its sums start from zero here, and no
                 // accumulator lives from one unit to the next (the same operations:
@@ -1067,15 +1164,16 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
 #pragma unroll
                     for (int b = 0; b < B; ++b) acc[m][b] = 0.0f;
             }
-            compute_unit<QT, M, XLDS>(cur, acc, k, xs4, x, a.x_stride, nsegw, cu.s - s0, last ? lp.j_last : j,
-                                      !last || lp.live_last);
-            if (ONE || cu.s + 1 == cu.s_end) {
+            compute_unit<QT, M, XLDS>(cur, acc, k, xs4, x, a.x_stride, nsegw, (int64_t)seg - s0, jc, live);
+            if (ONE || cu.kk + 1 == L) {
                 TileSums<M, EPI> sums;
                 tile_sums<M, tile_rs<EPI>()>(acc, sums, j);
-                if (R == 1)
-                    store_tile<M, EPI>(sums, y, a, cu.t, slot, j);
-                else
-                    park_tile<M, EPI>(sums, part + ((size_t)(cu.t - T0) * R + cu.r) * (M * kTileRows) + slot * B, j);
+                if (!dead) {
+                    if (R == 1)
+                        store_tile<M, EPI>(sums, y, a, T0 + t_rel, (int)slot, j);
+                    else
+                        park_tile<M, EPI>(sums, part + ((size_t)t_rel * R + r) * (M * kTileRows) + slot * B, j);
+                }
 #pragma unroll
                 for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -1093,29 +1191,31 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
     }
 
     if (R > 1) {
-        // every wavefront reaches this barrier (no early exit above)
+        // every wavefront reaches this barrier (no early exit above); each row of
+        // the workgroup's own half-tiles adds its partials in range order
         __syncthreads();
-        const uint32_t ntile = (uint32_t)(T1 - T0);
         if (EPI != kEpiGateUp) {
-            for (uint32_t o = tid; o < ntile * (M * kTileRows); o += blockDim.x) {
-                const uint32_t tl = o / (M * kTileRows), rem = o - tl * (M * kTileRows);
-                const uint32_t m = rem / kTileRows, row = rem - m * kTileRows;
-                const float *pp = part + (size_t)tl * R * (M * kTileRows) + m * kTileRows + row;
+            for (uint32_t o = tid; o < nh * (M * B); o += blockDim.x) {
+                const uint32_t hl = o / (M * B), rem = o - hl * (M * B);
+                const uint32_t m = rem / B, b = rem - m * B;
+                const uint32_t h = h0 + hl, t_rel = h >> 1, row = (h & 1u) * B + b;
+                const float *pp = part + (size_t)t_rel * R * (M * kTileRows) + m * kTileRows + row;
                 float v = pp[0];
                 for (uint32_t r = 1; r < R; ++r) v += pp[(size_t)r * (M * kTileRows)];
-                const int64_t n = (T0 + tl) * kTileRows + row;
+                const int64_t n = (T0 + t_rel) * kTileRows + row;
                 if (n < a.n_out) store_out<M, EPI>(y, a, (int)m, n, v);
             }
         } else {
-            for (uint32_t o = tid; o < ntile * (kTileRows / 2); o += blockDim.x) {
-                const uint32_t tl = o / (kTileRows / 2), q = o - tl * (kTileRows / 2);
-                const float *pp = part + (size_t)tl * R * kTileRows + 2 * q;
+            for (uint32_t o = tid; o < nh * (B / 2); o += blockDim.x) {
+                const uint32_t hl = o / (B / 2), q = o - hl * (B / 2);
+                const uint32_t h = h0 + hl, t_rel = h >> 1, pr = (h & 1u) * (B / 2) + q;   // pair in the tile
+                const float *pp = part + (size_t)t_rel * R * kTileRows + 2 * pr;
                 float gv = pp[0], uv = pp[1];
                 for (uint32_t r = 1; r < R; ++r) {
                     gv += pp[(size_t)r * kTileRows];
                     uv += pp[(size_t)r * kTileRows + 1];
                 }
-                const int64_t n = (T0 + tl) * (kTileRows / 2) + q;
+                const int64_t n = (T0 + t_rel) * (kTileRows / 2) + pr;
                 if (n < a.n_out) y[n] = silu_mul(gv, uv);
             }
         }
@@ -1211,7 +1311,7 @@ static hipError_t launch_persist(const uint8_t *wp, const float *x, float *y, co
     const auto kern = kw.first;
     const int which = kw.second + (p.one_unit ? 4 : 0);
     if (kern == nullptr) return hipErrorInvalidConfiguration;
-    if (p.block != persist_threads(QT, M, p.x_in_lds, p.one_unit)) return hipErrorInvalidConfiguration;
+    if (p.block != persist_threads(QT, M, p.x_in_lds, p.one_unit, p.phases > 1)) return hipErrorInvalidConfiguration;
     static std::atomic<int> lds_set[8][16];   // one record per kernel chosen above
     hipError_t e = ensure_lds_limit((const void *)kern, p.lds_bytes, lds_set[which]);
     if (e != hipSuccess) return e;

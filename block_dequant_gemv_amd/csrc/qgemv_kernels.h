@@ -27,10 +27,11 @@ struct QArgs {
     int64_t tpg;         // row tiles walked by one group of W wavefronts (tstride == 0)
     int64_t tstride;     // > 0: group g walks tiles g, g + tstride, g + 2*tstride, ... (tstride = groups)
     // persistent form only
-    int64_t n_wg;        // workgroups; workgroup b owns tiles_base tiles, one more for b < tiles_extra
-                         // (tiles_base = n_tiles / n_wg, tiles_extra = n_tiles % n_wg), contiguous
-    int64_t tiles_base;
-    int64_t tiles_extra;
+    int64_t n_wg;        // workgroups; workgroup b owns halves_base half-tiles (4 rows), one more for
+                         // b < halves_extra (halves_base = 2 n_tiles / n_wg, halves_extra = 2 n_tiles % n_wg),
+                         // contiguous
+    int64_t halves_base;
+    int64_t halves_extra;
     int64_t ranges;      // K ranges per tile (divides nseg); item = (tile, range)
     int64_t range_segs;  // segments per range (nseg / ranges)
     int64_t phases;      // divides ranges: the ranges are walked in phases of ranges/phases, each with
@@ -52,7 +53,7 @@ struct QPlan {
     int ranges;          // persistent form: K ranges per tile (divides nseg)
     int phases;          // persistent form: phases of ranges/phases ranges (divides ranges), each
                          // staging only its segments' activations
-    int64_t max_tiles;   // persistent form: most tiles any workgroup owns
+    int64_t max_tiles;   // persistent form: most tiles any workgroup's half-tiles touch
     int W;               // classic form: wavefronts splitting one row tile along K (1, 2, 3, 4, 8)
     int64_t tpg;         // tiles per group (contiguous order)
     int64_t tstride;     // > 0: grid-stride tile order over this many groups (tpg unused)
@@ -128,14 +129,14 @@ constexpr int qgemv_max_threads(int QT, int M, int W)
 // registers each, no scratch). one: every item is one unit (one segment per K
 // range), so no accumulator lives from one unit to the next (Q4_0 at M = 6
 // with staged activations: 149 -> 111 VGPRs): Q4_0 fits 128 VGPRs at every M
-// (with activations from L2 up to 5 rows), Q8_0 with staged activations up to 4
+// (with activations from L2, or staged in phases, up to 4 rows), Q8_0 with staged activations up to 4
 // rows, 168 above; Q6_K fits 168 up to 3 rows (4 with staged activations) and
 // 256 without scratch at 5 and 6 (the general form spills there).
-constexpr int persist_threads(int qt, int M, bool xlds, bool one = false)
+constexpr int persist_threads(int qt, int M, bool xlds, bool one = false, bool phased = false)
 {
     if (M == 1) return 1024;
     if (one) {
-        if (qt == qgl::kQ4_0) return (xlds || M <= 5) ? 1024 : 768;
+        if (qt == qgl::kQ4_0) return ((xlds && !(phased && M >= 5)) || M <= 4) ? 1024 : 768;
         if (qt == qgl::kQ8_0 && xlds) return M <= 4 ? 1024 : 768;
         if (qt == qgl::kQ6_K) return (M <= 3 || (M == 4 && xlds)) ? 768 : 512;
     }
