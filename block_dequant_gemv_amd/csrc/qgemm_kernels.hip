@@ -59,6 +59,62 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 // per thread. VEC: the row is 16-byte aligned and read with 16-byte loads.
 constexpr int kSplitThreads = 256;
 
+// The 8 activations of lane run u of row xr: Q4_0 elements 8c..8c+7 of block
+// b = u / 4 (c = u % 4), Q8_0 elements 4c..4c+3 and 16+4c..16+4c+3.
+template <int QT, bool VEC>
+__device__ inline void split_load_run(const float *__restrict__ xr, int64_t u, float (&v)[8])
+{
+    const int64_t b = u >> 2;
+    const int c = (int)(u & 3);
+    const int64_t k0 = b * 32 + (QT == kQ4_0 ? 8 * c : 4 * c);
+    const int64_t k1 = QT == kQ4_0 ? k0 + 4 : k0 + 16;
+    if (VEC) {
+        const f32x4 a0 = *(const f32x4 *)(xr + k0);
+        const f32x4 a1 = *(const f32x4 *)(xr + k1);
+        v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
+        v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[j] = xr[k0 + j];
+            v[4 + j] = xr[k1 + j];
+        }
+    }
+}
+
+// 2^e with max|x| * 2^e in [2^14, 2^15); 1 for a zero or non-finite maximum.
+__device__ inline int split_exponent(float mx)
+{
+    int e = 0;
+    if (mx > 0.0f && mx <= 3.4028234663852886e38f) {
+        int E;
+        (void)__builtin_frexpf(mx, &E);   // mx = f * 2^E, f in [0.5, 1)
+        e = 15 - E;
+        e = e < -126 ? -126 : (e > 127 ? 127 : e);
+    }
+    return e;
+}
+
+// The hi and lo parts of lane run u of activation row m (scaled by sc), as two
+// 16-byte stores at the run's B-operand position.
+__device__ inline void split_store_run(_Float16 *__restrict__ xs, int64_t m, int64_t KB, int64_t u,
+                                       const float (&v)[8], float sc)
+{
+    const int64_t b = u >> 2;
+    const int c = (int)(u & 3);
+    h8 hi, lo;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float t = v[j] * sc;
+        const _Float16 h = (_Float16)t;
+        hi[j] = h;
+        lo[j] = (_Float16)(t - (float)h);
+    }
+    _Float16 *dst = xs + (((m >> 4) * KB + b) * 2) * 512 + (int64_t)(c * 16 + (int)(m & 15)) * 8;
+    *(h8 *)dst = hi;
+    *(h8 *)(dst + 512) = lo;
+}
+
 template <int QT, bool VEC>
 __global__ void __launch_bounds__(kSplitThreads)
 split_x_kernel(const float *__restrict__ X, _Float16 *__restrict__ xs, float *__restrict__ unscale, int64_t M,
@@ -100,55 +156,22 @@ split_x_kernel(const float *__restrict__ X, _Float16 *__restrict__ xs, float *__
     __syncthreads();
     mx = red[0];
     for (int w = 1; w < T / 64; ++w) mx = __builtin_fmaxf(mx, red[w]);
-    // 2^e with max|x| * 2^e in [2^14, 2^15); 1 for a zero or non-finite maximum
-    int e = 0;
-    if (mx > 0.0f && mx <= 3.4028234663852886e38f) {
-        int E;
-        (void)__builtin_frexpf(mx, &E);   // mx = f * 2^E, f in [0.5, 1)
-        e = 15 - E;
-        e = e < -126 ? -126 : (e > 127 ? 127 : e);
-    }
+    const int e = split_exponent(mx);
     const float sc = __builtin_ldexpf(1.0f, e);
     if (tid == 0 && blockIdx.y == 0) unscale[m] = __builtin_ldexpf(1.0f, -e);
     const int64_t KB = K / 32;
-    const int64_t mt = m >> 4;
-    const int mi = (int)(m & 15);
-    // this workgroup's lane runs u in [u0, u1): Q4_0 elements 8c..8c+7 of block
-    // b = u / 4 (c = u % 4), Q8_0 elements 4c..4c+3 and 16+4c..16+4c+3
+    // this workgroup's lane runs u in [u0, u1)
     const int64_t U = KB * 4;
     const int64_t u0 = U * blockIdx.y / gridDim.y, u1 = U * (blockIdx.y + 1) / gridDim.y;
     auto run = [&](int64_t u) {
-        const int64_t b = u >> 2;
-        const int c = (int)(u & 3);
-        const int64_t k0 = b * 32 + (QT == kQ4_0 ? 8 * c : 4 * c);
-        const int64_t k1 = QT == kQ4_0 ? k0 + 4 : k0 + 16;
         float v[8];
-        if (!live) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = 0.0f;
-        } else if (VEC) {
-            const f32x4 a0 = *(const f32x4 *)(xr + k0);
-            const f32x4 a1 = *(const f32x4 *)(xr + k1);
-            v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
-            v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+        if (live) {
+            split_load_run<QT, VEC>(xr, u, v);
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v[j] = xr[k0 + j];
-                v[4 + j] = xr[k1 + j];
-            }
+            for (int j = 0; j < 8; ++j) v[j] = 0.0f;
         }
-        h8 hi, lo;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float t = v[j] * sc;
-            const _Float16 h = (_Float16)t;
-            hi[j] = h;
-            lo[j] = (_Float16)(t - (float)h);
-        }
-        _Float16 *dst = xs + ((mt * KB + b) * 2) * 512 + (int64_t)(c * 16 + mi) * 8;
-        *(h8 *)dst = hi;
-        *(h8 *)(dst + 512) = lo;
+        split_store_run(xs, m, KB, u, v, sc);
     };
     int64_t u = u0 + tid;
     for (; u + T < u1; u += 2 * T) {   // two runs per thread in flight
@@ -156,6 +179,55 @@ split_x_kernel(const float *__restrict__ X, _Float16 *__restrict__ xs, float *__
         run(u + T);
     }
     if (u < u1) run(u);
+}
+
+// Activation split in one pass: one workgroup per activation row, thread t
+// holding the lane runs t, t + T, ..., t + (R - 1) T of the row (T = blockDim)
+// in registers. The row is read once; its maximum is taken from the registers
+// and the hi and lo parts are written from them, so the pass costs one memory
+// round trip where split_x_kernel takes two or more (a maximum pass and a
+// split pass). The parts are the same values as split_x_kernel's.
+template <int QT, bool VEC, int R>
+__global__ void __launch_bounds__(1024)
+split_x_row_kernel(const float *__restrict__ X, _Float16 *__restrict__ xs, float *__restrict__ unscale,
+                   int64_t M, int64_t K)
+{
+    __shared__ float red[16];
+    const int64_t m = blockIdx.x;
+    const int tid = threadIdx.x, T = blockDim.x;
+    const bool live = m < M;
+    const float *xr = X + m * K;
+    const int64_t KB = K / 32, U = KB * 4;
+    float v[R][8];
+    float mx = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t u = tid + (int64_t)r * T;
+        if (live && u < U) {
+            split_load_run<QT, VEC>(xr, u, v[r]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[r][j] = 0.0f;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mx = __builtin_fmaxf(mx, __builtin_fabsf(v[r][j]));
+    // workgroup maximum (max is exact, so the order does not matter)
+    for (int o = 32; o >= 1; o >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o));
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    mx = red[0];
+    for (int w = 1; w < T / 64; ++w) mx = __builtin_fmaxf(mx, red[w]);
+    const int e = split_exponent(mx);
+    const float sc = __builtin_ldexpf(1.0f, e);
+    if (tid == 0) unscale[m] = __builtin_ldexpf(1.0f, -e);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t u = tid + (int64_t)r * T;
+        if (u < U) split_store_run(xs, m, KB, u, v[r], sc);
+    }
 }
 
 // 4 x 4 transpose of (16-lane group, register): afterwards register r of lane
@@ -617,8 +689,32 @@ hipError_t launch_split_x(int qt, const float *X, _Float16 *xs, float *unscale, 
                           hipStream_t s)
 {
     const bool vec = ((uintptr_t)X & 15) == 0;   // rows are K * 4 bytes, a multiple of 128
-    // up to four workgroups per row while fewer than 256 rows fill the chip,
-    // at least 512 lane runs (4096 elements) each
+    const int64_t U = K / 32 * 4;                 // lane runs per row
+    if (U <= 4 * 1024) {
+        // one pass: one workgroup per row, at most 4 runs per thread
+        const int R = U <= 1024 ? 1 : (U <= 2048 ? 2 : 4);
+        const int64_t T = std::min<int64_t>(1024, (U + 63) / 64 * 64);
+        const dim3 grid((unsigned)M_pad), block((unsigned)T);
+        auto go = [&](auto q, auto v) {
+            constexpr int Q = decltype(q)::value;
+            constexpr bool V = decltype(v)::value;
+            switch (R) {
+            case 1: hipLaunchKernelGGL((split_x_row_kernel<Q, V, 1>), grid, block, 0, s, X, xs, unscale, M, K); break;
+            case 2: hipLaunchKernelGGL((split_x_row_kernel<Q, V, 2>), grid, block, 0, s, X, xs, unscale, M, K); break;
+            default: hipLaunchKernelGGL((split_x_row_kernel<Q, V, 4>), grid, block, 0, s, X, xs, unscale, M, K); break;
+            }
+        };
+        using Q8 = std::integral_constant<int, kQ8_0>;
+        using Q4 = std::integral_constant<int, kQ4_0>;
+        if (qt == kQ8_0) {
+            if (vec) go(Q8{}, std::true_type{}); else go(Q8{}, std::false_type{});
+        } else {
+            if (vec) go(Q4{}, std::true_type{}); else go(Q4{}, std::false_type{});
+        }
+        return hipGetLastError();
+    }
+    // longer rows: the two-pass form, up to four workgroups per row while fewer
+    // than 256 rows fill the chip, at least 512 lane runs (4096 elements) each
     int64_t per_row = std::min<int64_t>(4, std::max<int64_t>(1, 256 / M_pad));
     per_row = std::max<int64_t>(1, std::min<int64_t>(per_row, K / 8 / 512));
     const dim3 grid((unsigned)M_pad, (unsigned)per_row), block(kSplitThreads);
