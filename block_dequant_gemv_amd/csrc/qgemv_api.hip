@@ -212,7 +212,9 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M, bool norm = false)
     qgk::QPlan p;
     p.norm = norm;
     const Geometry g = qgl::geometry(qt, rows, K);
-    const size_t xbytes = (size_t)M * (size_t)g.nseg * qgl::kSegWeights * sizeof(float);
+    // the staged copy of the activations (with their block sums where
+    // x_sums_staged)
+    const size_t xbytes = (size_t)M * (size_t)g.nseg * qgk::staged_seg_bytes(qt, norm);
     const int64_t xg_env = tune(kXGlobal);
     int64_t ranges = 1, pgrid = 0, max_tiles = 0;
     p.persist = plan_persist(qt, rows, K, &ranges, &pgrid, &max_tiles);
@@ -235,7 +237,7 @@ qgk::QPlan make_qplan(int qt, int64_t rows, int64_t K, int M, bool norm = false)
         // activations from L2 (5120 x 17408 at M = 3..6: 47-82 us from L2).
         // Phases change which wavefront adds an item and when, not any row's
         // operations.
-        const size_t seg_bytes = (size_t)M * qgl::kSegWeights * sizeof(float);   // one segment, M rows
+        const size_t seg_bytes = (size_t)M * qgk::staged_seg_bytes(qt, norm);   // one segment, M rows
         const int64_t seg_per_range = g.nseg / ranges;
         auto window = [&](int64_t ph) { return (size_t)((ranges + ph - 1) / ph * seg_per_range) * seg_bytes; };
         if (!lds && M > 1 && !norm) {

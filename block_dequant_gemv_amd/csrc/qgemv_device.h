@@ -347,8 +347,10 @@ __device__ __forceinline__ void load_unit_lane(Unit<QT> &u, const uint8_t *__res
 // row; the 2^24 goes into d*sc. d*sc and dmin*mn are exact (11-bit by 6-bit
 // products) and d*sc*c - dmin*mn is one fma. Dead lanes of a ragged segment
 // get zero terms: they add 0. Every activation row goes through the same
-// operations for any M.
-template <int M, bool XLDS>
+// operations for any M. PRE: the block's sum of x comes from the workgroup's
+// staged sums (block_x_sums, the same additions in the same order) instead of
+// being added up here by every wavefront.
+template <int M, bool XLDS, bool PRE = false>
 __device__ __forceinline__ void compute_unit_q4k(const Unit<kQ4_K> &u, float (&acc)[M][kRowsPerLane],
                                                  const Consts &k, const f32x4 *xs4, const float *__restrict__ x,
                                                  int64_t x_stride, int64_t nseg, int64_t s, int j, bool live)
@@ -391,7 +393,8 @@ __device__ __forceinline__ void compute_unit_q4k(const Unit<kQ4_K> &u, float (&a
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc)
                 xv[cc] = XLDS ? xl[m * x_row + (c + cc) * 32] : *(const f32x4 *)(xg + m * x_stride + (c + cc) * 4);
-            sx[m] = sx[m] + (((xv[0].x + xv[0].y) + (xv[0].z + xv[0].w)) + ((xv[1].x + xv[1].y) + (xv[1].z + xv[1].w)));
+            if (!PRE)
+                sx[m] = sx[m] + (((xv[0].x + xv[0].y) + (xv[0].z + xv[0].w)) + ((xv[1].x + xv[1].y) + (xv[1].z + xv[1].w)));
         };
         if constexpr (M == 1) {
             f32x4 xv[2];
@@ -414,6 +417,12 @@ __device__ __forceinline__ void compute_unit_q4k(const Unit<kQ4_K> &u, float (&a
                 for (int b = 0; b < B; ++b) row_fma(p[b], xv, m, b);
             }
         }
+    }
+    if (PRE) {
+        // row m's sums follow the staged copy: float m * nseg * 32 + s * 32 + j
+        const float *xsl = (const float *)(xs4 + (uint32_t)M * x_row) + ((uint32_t)s << 5) + (uint32_t)j;
+#pragma unroll
+        for (int m = 0; m < M; ++m) sx[m] = xsl[(uint32_t)m * ((uint32_t)nseg << 5)];
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
@@ -531,13 +540,13 @@ __device__ __forceinline__ void rows_fma(const h2 (&p)[B][4], const f32x4 (&xv)[
     }
 }
 
-template <int QT, int M, bool XLDS>
+template <int QT, int M, bool XLDS, bool NORM = false>
 __device__ __forceinline__ void compute_unit(const Unit<QT> &u, float (&acc)[M][kRowsPerLane], const Consts &k,
                                              const f32x4 *xs4, const float *__restrict__ x, int64_t x_stride,
                                              int64_t nseg, int64_t s, int j, bool live)
 {
     if constexpr (QT == kQ4_K) {
-        compute_unit_q4k<M, XLDS>(u, acc, k, xs4, x, x_stride, nseg, s, j, live);
+        compute_unit_q4k<M, XLDS, x_sums_staged(QT, XLDS, NORM)>(u, acc, k, xs4, x, x_stride, nseg, s, j, live);
         return;
     }
     if constexpr (QT == kQ6_K) {
@@ -757,6 +766,30 @@ __device__ __forceinline__ void norm_staged_x(f32x4 *xs4, float *red, const floa
     __syncthreads();
 }
 
+// Block sums of the staged activations (Q4_K): for each row m, segment s and
+// block j of the staged copy, the sum of its 32 values in the order a wavefront
+// adds them (pairs of float4 chunks, ((x0 + x1) + (x2 + x3)) + ((x4 + x5) +
+// (x6 + x7)), added in chunk order), written after the copy at float
+// m * nseg * 32 + s * 32 + j. One thread per block, then a barrier. Every
+// thread of the workgroup must call it.
+template <int M>
+__device__ __forceinline__ void block_x_sums(f32x4 *xs4, uint32_t nseg)
+{
+    float *xsum = (float *)(xs4 + (uint32_t)M * (nseg << 8));
+    const uint32_t nb = (uint32_t)M * (nseg << 5);
+    for (uint32_t i = threadIdx.x; i < nb; i += blockDim.x) {
+        const f32x4 *xb = xs4 + ((i >> 5) << 8) + (i & 31u);   // chunk c of the block at xb[32 c]
+        float sx = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; c += 2) {
+            const f32x4 v0 = xb[c * 32], v1 = xb[(c + 1) * 32];
+            sx = sx + (((v0.x + v0.y) + (v0.z + v0.w)) + ((v1.x + v1.y) + (v1.z + v1.w)));
+        }
+        xsum[i] = sx;
+    }
+    __syncthreads();
+}
+
 // Store output n of activation row m (n < n_out). The affine epilogue adds the
 // bias and then the residual to the finished product, one fp32 addition each,
 // and writes fp32 or fp16 (v_cvt_f16_f32, round to nearest even). The residual
@@ -913,6 +946,7 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
         __syncthreads();
     }
     if (NORM) norm_staged_x(xs4, red, a.gamma, a.eps, K);
+    if (x_sums_staged(QT, XLDS, NORM)) block_x_sums<M>(xs4, (uint32_t)nseg);
     if (n_units == 0) return;   // uniform across the workgroup when W > 1
 
     float acc[M][B];
@@ -933,8 +967,8 @@ qgemv_kernel(const uint8_t *__restrict__ wp, const float *__restrict__ x, float 
         // keep the scheduler from sinking these loads into the compute below
         __builtin_amdgcn_sched_barrier(0);
         const bool last = s == nseg - 1;
-        compute_unit<QT, M, XLDS>(cur, acc, k, xs4, x, a.x_stride, nseg, s, last ? lp.j_last : j,
-                                  !last || lp.live_last);
+        compute_unit<QT, M, XLDS, NORM>(cur, acc, k, xs4, x, a.x_stride, nseg, s, last ? lp.j_last : j,
+                                        !last || lp.live_last);
         if (s + 1 == s_end) {
             TileSums<M, EPI> sums;
             tile_sums<M, tile_rs<EPI>()>(acc, sums, j);
@@ -1052,7 +1086,10 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
     // The partials follow the largest window.
     const uint32_t P = PHASED ? (uint32_t)a.phases : 1u;
     const uint32_t nsegw_max = PHASED ? (R + P - 1) / P * L : (uint32_t)nseg;
-    float *part = (float *)(xs4 + (XLDS ? (uint32_t)M * (nsegw_max << 8) : 0u));   // [tile][range][m][8]
+    // the partials [tile][range][m][8] follow the largest window (and its block
+    // sums where x_sums_staged)
+    float *part = (float *)(xs4 + (XLDS ? (uint32_t)M * (nsegw_max << 8) : 0u)) +
+                  (x_sums_staged(QT, XLDS, NORM) ? (uint32_t)M * (nsegw_max << 5) : 0u);
 
     const Consts k = make_consts();
 
@@ -1144,6 +1181,7 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
             __syncthreads();
         }
         if (NORM) norm_staged_x(xs4, nred, a.gamma, a.eps, K);
+        if (x_sums_staged(QT, XLDS, NORM)) block_x_sums<M>(xs4, nsegw);
 
         const uint32_t nb_last = (uint32_t)seg_blocks(g, g.nseg - 1);
         auto step = [&](Unit<QT> &cur, Unit<QT> &nxt) {
@@ -1164,7 +1202,7 @@ qgemv_persist(const uint8_t *__restrict__ wp, const float *__restrict__ x, float
 #pragma unroll
                     for (int b = 0; b < B; ++b) acc[m][b] = 0.0f;
             }
-            compute_unit<QT, M, XLDS>(cur, acc, k, xs4, x, a.x_stride, nsegw, (int64_t)seg - s0, jc, live);
+            compute_unit<QT, M, XLDS, NORM>(cur, acc, k, xs4, x, a.x_stride, nsegw, (int64_t)seg - s0, jc, live);
             if (ONE || cu.kk + 1 == L) {
                 TileSums<M, EPI> sums;
                 tile_sums<M, tile_rs<EPI>()>(acc, sums, j);

@@ -146,6 +146,19 @@ constexpr int persist_threads(int qt, int M, bool xlds, bool one = false, bool p
     return (M <= 3 || xlds) ? 768 : 512;
 }
 
+// Q4_K kernels with staged activations and no RMSNorm prologue follow the
+// staged copy with its block sums (one float per activation row and 32-weight
+// block, written once per workgroup after staging), so that every wavefront
+// reads a block's sum of x instead of adding it up. The RMSNorm kernels add
+// them up per unit as before, which keeps their activation limit that of the
+// other types. Bytes of LDS per staged 1024-weight segment of one activation
+// row, the sums included.
+constexpr bool x_sums_staged(int qt, bool xlds, bool norm) { return qt == qgl::kQ4_K && xlds && !norm; }
+constexpr size_t staged_seg_bytes(int qt, bool norm)
+{
+    return (size_t)qgl::kSegWeights * sizeof(float) + (x_sums_staged(qt, true, norm) ? 32 * sizeof(float) : 0);
+}
+
 // Static LDS of the quantised GEMV kernels. The kernels declare their arrays
 // with these sizes and the launch planner adds them to the dynamic activation
 // copy, so that a plan never asks for more than a CU's LDS:
