@@ -304,34 +304,37 @@ def roofline_of(run, K):
 
 
 def graph_replay(torch, qg, which, run, K, warmup, stream_unused=None):
-    """The same K steps replayed from HIP graphs: one torch.cuda.CUDAGraph per weight
-    copy capturing that step's launches on a side stream (the GEMV calls record plain
-    kernel launches and nothing else), then K replays cycling through the copies."""
+    """The headline steps replayed from HIP graphs: one torch.cuda.CUDAGraph capturing G
+    consecutive steps on a side stream (cycling through the weight copies; the GEMV
+    calls record plain kernel launches and nothing else), replayed until about K steps
+    have run, so that one graph launch covers G steps of kernels."""
     side = torch.cuda.Stream()
-    graphs = []
     copies = run["copies"]
-    for st in run["sets"]:
-        calls = step_calls(qg, which, st, run["xs"], run["ys"], side.cuda_stream)
-        with torch.cuda.stream(side):
-            for c in calls:
-                c.fn()
-        side.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=side, capture_error_mode="thread_local"):
-            for c in calls:
-                c.fn()
-        graphs.append(g)
+    per_graph = copies * max(1, 24 // copies)
+    calls = [c for i in range(per_graph)
+             for c in step_calls(qg, which, run["sets"][i % copies], run["xs"], run["ys"], side.cuda_stream)]
     with torch.cuda.stream(side):
-        for s in range(warmup):
-            graphs[s % copies].replay()
+        for c in calls:
+            c.fn()
+    side.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side, capture_error_mode="thread_local"):
+        for c in calls:
+            c.fn()
+    replays = max(1, round(K / per_graph))
+    with torch.cuda.stream(side):
+        for _ in range(max(1, warmup // per_graph)):
+            g.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for s in range(K):
-            graphs[s % copies].replay()
+        for _ in range(replays):
+            g.replay()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-    del graphs
-    return {"ms_per_step": round(wall / K * 1e3, 5), "value": round(run["bytes"] * K / wall / 1e9, 1)}
+    del g
+    steps = replays * per_graph
+    return {"ms_per_step": round(wall / steps * 1e3, 5), "value": round(run["bytes"] * steps / wall / 1e9, 1),
+            "steps": steps, "steps_per_graph": per_graph}
 
 
 def time_call(qg, torch, fns, reps):
@@ -917,8 +920,9 @@ def main():
     detail = {"q4_0_kernel_us": {c.label: run4["durs"][:, i].tolist() for i, c in enumerate(run4["steps"][0])}}
     if not args.no_graph:
         result["graph_replay"] = graph_replay(torch, qg, "q4_0", run4, K, args.warmup)
-        log(f"graph replay (q4_0 set): {result['graph_replay']['ms_per_step'] * 1e3:.1f} us/step, "
-            f"{result['graph_replay']['value']:.1f} GB/s")
+        gr = result["graph_replay"]
+        log(f"graph replay (q4_0 set, {gr['steps_per_graph']} steps per graph): {gr['ms_per_step'] * 1e3:.1f} us/step, "
+            f"{gr['value']:.1f} GB/s")
     q4_step = run4["steps"][0]
 
     # ---- the Q8_0 decode set ---------------------------------------------------------
