@@ -1,7 +1,7 @@
 """Summaries of rocprofv3 CSV output for this library's kernels.
 
     python -m block_dequant_gemv_amd.prof trace  <dir> [--skip N] [--tail N]   # --kernel-trace --stats -f csv
-    python -m block_dequant_gemv_amd.prof counters <dir>
+    python -m block_dequant_gemv_amd.prof counters <dir> [traffic.json]
     python -m block_dequant_gemv_amd.prof collect <out_dir> [--only trace_step,trace_calls,traffic,sq,trace_gemm,gemm_sq]
     python -m block_dequant_gemv_amd.prof traffic <fetch_dir> <write_dir> [--json out.json]
                                               [--call LABEL=KERNEL|WORKGROUPSxWG ...]
@@ -16,7 +16,9 @@ leaves out the first N dispatches of every shape, --tail N keeps only the last N
 and prints, per launch shape, the mean of every counter and of the dispatch
 time; with GRBM_GUI_ACTIVE it derives the shader clock (busy cycles per
 microsecond of dispatch), with SQ_WAVES and SQ_INSTS_VALU the VALU instructions
-per wavefront.
+per wavefront. Given the HBM bytes per dispatch of a traffic run (its
+traffic.json, or the same `collect`), it adds each launch shape's HBM rate over
+this run's dispatch time and HBM bytes per shader clock.
 
 `collect` runs the profiler passes behind profiles/ (each rocprofv3 pass a
 child process of its own under `timeout -s KILL`, the program after `--`):
@@ -149,7 +151,18 @@ def _counter_means(directory: str, counter: str):
     return {k: st.mean(v) for k, v in groups.items()}, {k: len(v) for k, v in groups.items()}
 
 
-def counter_summary(directory: str) -> str:
+def shape_bytes(traffic: dict) -> dict:
+    """(kernel, workgroups, workgroup size) -> HBM bytes per dispatch (fetch + write) of a
+    traffic summary's data (traffic_summary's second result, or its traffic.json)."""
+    out = {}
+    for key, v in traffic.get("kernels", {}).items():
+        name, shape = key.rsplit("|", 1)
+        wgs, wg = (int(t) for t in shape.split("x"))
+        out[(name, wgs, wg)] = v["fetch_bytes"] + v["write_bytes"]
+    return out
+
+
+def counter_summary(directory: str, hbm_bytes: dict | None = None) -> str:
     rows = _rows(os.path.join(directory, "**", "*counter_collection.csv"))
     vals = defaultdict(lambda: defaultdict(list))
     durs = defaultdict(dict)
@@ -174,7 +187,11 @@ def counter_summary(directory: str) -> str:
              + (";\nmfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8); valu_per_mfma = "
                 "(SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA (SQ_INSTS_VALU counts the MFMA instructions too); "
                 "coexec = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES"
-                if {"GRBM_GUI_ACTIVE", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES"} <= names else "")]
+                if {"GRBM_GUI_ACTIVE", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES"} <= names else "")
+             + (";\nhbm_GBps, hbm_B_per_clk = the launch shape's HBM bytes per dispatch from the traffic run (FETCH_SIZE "
+                "+ WRITE_SIZE, calibrated) over this run's dispatch time and over its GRBM_GUI_ACTIVE / 8 shader clocks "
+                "(the profiler serialises the dispatches of both runs)" if hbm_bytes and "GRBM_GUI_ACTIVE" in names
+                else "")]
     head = f"{'kernel':58s} {'wgs':>7s} {'wg':>5s} {'n':>4s} {'us':>9s} " + " ".join(f"{c:>20s}" for c in cols)
     extra = []
     if "GRBM_GUI_ACTIVE" in names:
@@ -187,6 +204,8 @@ def counter_summary(directory: str) -> str:
         extra += ["mfma_busy", "valu_per_mfma"]
         if "SQ_VALU_MFMA_COEXEC_CYCLES" in names:
             extra.append("coexec")
+    if hbm_bytes and "GRBM_GUI_ACTIVE" in names:
+        extra += ["hbm_GBps", "hbm_B_per_clk"]
     lines.append(head + "".join(f" {e:>14s}" for e in extra))
     for key in sorted(vals, key=lambda k: -st.mean(durs[k].values()) if durs[k] else 0):
         d = list(durs[key].values())
@@ -207,6 +226,12 @@ def counter_summary(directory: str) -> str:
             line += f" {(means['SQ_INSTS_VALU'] - mi) / mi:14.2f}" if mi > 0 else f" {'-':>14s}"
             if "coexec" in extra:
                 line += f" {means['SQ_VALU_MFMA_COEXEC_CYCLES'] / mb:14.3f}" if mb > 0 else f" {'-':>14s}"
+        if "hbm_GBps" in extra:
+            b = hbm_bytes.get(key)
+            if b is None:
+                line += f" {'-':>14s} {'-':>14s}"
+            else:
+                line += f" {b / us / 1e3:14.1f} {b / (means['GRBM_GUI_ACTIVE'] / XCDS):14.1f}"
         lines.append(line)
     return "\n".join(lines)
 
@@ -317,8 +342,13 @@ def collect(out: str, only=None):
                                 f"traffic <out>/fetch <out>/write\n\n" + text)
     if want("sq"):
         cmd, _ = _run_pass("sq", ["--pmc", *SQ_COUNTERS, "--kernel-trace"], PMC_ARGS, out, 600)
-        summaries["sq"] = (f"command: {cmd}\nsummary: python -m block_dequant_gemv_amd.prof counters <out>/sq\n\n"
-                           + counter_summary(os.path.join(out, "sq")))
+        hbm = None
+        if os.path.exists(os.path.join(out, "traffic.json")):
+            with open(os.path.join(out, "traffic.json")) as f:
+                hbm = shape_bytes(json.load(f))
+        summaries["sq"] = (f"command: {cmd}\nsummary: python -m block_dequant_gemv_amd.prof counters <out>/sq"
+                           + (" <out>/traffic.json" if hbm else "") + "\n\n"
+                           + counter_summary(os.path.join(out, "sq"), hbm))
     if want("trace_gemm"):
         cmd, _ = _run_pass("trace_gemm", ["--kernel-trace", "--stats"], GEMM_ARGS, out, 600)
         summaries["trace_gemm"] = (f"command: {cmd}\nsummary: python -m block_dequant_gemv_amd.prof trace "
@@ -339,7 +369,11 @@ def main(argv):
         tail = int(argv[argv.index("--tail") + 1]) if "--tail" in argv else 0
         print(trace_summary(argv[1], skip, tail))
     elif len(argv) >= 2 and argv[0] == "counters":
-        print(counter_summary(argv[1]))
+        hbm = None
+        if len(argv) >= 3:
+            with open(argv[2]) as f:
+                hbm = shape_bytes(json.load(f))
+        print(counter_summary(argv[1], hbm))
     elif len(argv) >= 2 and argv[0] == "collect":
         collect(argv[1], argv[argv.index("--only") + 1].split(",") if "--only" in argv else None)
     elif len(argv) >= 3 and argv[0] == "traffic":

@@ -52,3 +52,29 @@ def test_counter_summary_derives_clock_and_valu_per_wave(tmp_path):
     # waves' instructions; VALU busy 1200000 * 4 / (1024 * 25000) = 0.1875
     assert line[1:5] == ["1000", "256", "2", "100.00"]
     assert float(line[-3]) == 250.0 and float(line[-2]) == 300.0 and abs(float(line[-1]) - 0.1875) < 1e-3
+
+
+def test_counter_summary_adds_hbm_rate_from_traffic(tmp_path):
+    # the same counter run as above, with the traffic run's 8 MB per dispatch of that
+    # launch shape (and an entry for a shape this run does not have)
+    hdr = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Workgroup_Size", "Counter_Name", "Counter_Value",
+           "Start_Timestamp", "End_Timestamp"]
+    rows = []
+    for did in (1, 2):
+        for c, v in (("GRBM_GUI_ACTIVE", 200000), ("SQ_WAVES", 4000), ("SQ_INSTS_VALU", 1200000)):
+            rows.append([did, "qgk::k", 256000, 256, c, v, 0, 100000])   # 100 us each
+    rows.append([3, "qgk::other", 2560, 256, "GRBM_GUI_ACTIVE", 80000, 0, 10000])
+    _write(str(tmp_path / "c" / "run_counter_collection.csv"), hdr, rows)
+    traffic = {"kernels": {"qgk::k|1000x256": {"fetch_bytes": 7.5e6, "write_bytes": 0.5e6},
+                           "qgk::absent|4x64": {"fetch_bytes": 1.0, "write_bytes": 0.0}}}
+    hbm = prof.shape_bytes(traffic)
+    assert hbm == {("qgk::k", 1000, 256): 8.0e6, ("qgk::absent", 4, 64): 1.0}
+    text = prof.counter_summary(str(tmp_path / "c"), hbm)
+    assert "hbm_B_per_clk" in text
+    line = [ln for ln in text.splitlines() if ln.startswith("qgk::k")][0].split()
+    # 8 MB in 100 us = 80 GB/s; 8e6 bytes over 200000 / 8 = 25000 clocks = 320 bytes per clock
+    assert float(line[-2]) == 80.0 and float(line[-1]) == 320.0
+    other = [ln for ln in text.splitlines() if ln.startswith("qgk::other")][0].split()
+    assert other[-2:] == ["-", "-"]
+    # without traffic data the columns are not there
+    assert "hbm_GBps" not in prof.counter_summary(str(tmp_path / "c"))
