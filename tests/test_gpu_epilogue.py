@@ -7,7 +7,8 @@ Shapes cover both launch forms of the quantised GEMV: one wavefront group per
 row tile (fused QKV 4096x1024 with its bias; the 1024x2048 O projection split
 two ways along K, with the residual added in place; the 1024x3072 down projection
 split three ways; a ragged 9x1056) and the
-persistent form with K ranges combined in LDS (3300x5120, 640x17408); the Q4_K
+persistent form with K ranges combined in LDS (3300x5120, 640x17408) and with
+one K range, whose half-tiles store their sums directly (20000x1024); the Q4_K
 and Q6_K weights on two shapes each."""
 import numpy as np
 import pytest
@@ -19,7 +20,7 @@ from gpu_helpers import THREADS, announce, empty_f32, sync, to_dev, torch_dev
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(4096, 1024), (1024, 2048), (1024, 3072), (9, 1056), (3300, 5120), (640, 17408)]
+SHAPES = [(4096, 1024), (1024, 2048), (1024, 3072), (9, 1056), (3300, 5120), (640, 17408), (20000, 1024)]
 TAIL = 5
 
 

@@ -103,7 +103,7 @@ def test_q8_0_full_int8_range_and_zero_scales():
 
 @pytest.mark.parametrize("kind,N_ff,K", [(k, n, kk) for k in ("q8_0", "q4_0")
                                          for n, kk in ((1, 32), (7, 1056), (3072, 1024), (512, 3072), (300, 5120),
-                                                       (100, 17408), (2101, 5120))] +
+                                                       (100, 17408), (2101, 5120), (10000, 1024))] +
                          [(k, n, kk) for k in ("q4_k", "q6_k") for n, kk in ((7, 1280), (512, 3072), (300, 5120),
                                                                             (2101, 5120))])
 def test_fused_gateup_silu_matches_oracle(kind, N_ff, K):

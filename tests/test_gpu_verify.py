@@ -30,8 +30,15 @@ CASES = [("q4_0", 17408, 5120), ("q8_0", 4096, 1024), ("q8_0", 33, 2080), ("q4_0
          ("q4_k", 640, 17408), ("q6_k", 640, 17408),
          # eight split-K wavefronts over 8 segments: four staged rows take 128 KiB of
          # LDS; five rows (exactly 160 KiB) plus the partials do not fit, so M = 5, 6
-         # read their activations from L2
-         ("q4_0", 1280, 8192), ("q8_0", 1280, 8192)]
+         # read their activations from L2 (Q4_K: the four rows' block sums after
+         # them, 132 KiB in all)
+         ("q4_0", 1280, 8192), ("q8_0", 1280, 8192), ("q4_k", 1280, 8192),
+         # Q4_K's block sums per phase window of the persistent form (M >= 3)
+         ("q4_k", 2001, 17408),
+         # the persistent form with one K range, whose half-tiles store their sums
+         # directly: 37 segments (a prime count, activations from L2 from M = 2)
+         # with a ragged row tile, and one segment (single-unit items)
+         ("q4_0", 1001, 37888), ("q8_0", 20000, 1024)]
 
 
 @pytest.mark.parametrize("kind,N,K", CASES)

@@ -411,6 +411,14 @@ def test_plan_staged_copy_at_the_lds_boundary(L):
         assert p["lds_bytes"] <= LDS_PER_CU
         # four rows (128 KiB + 1 KiB) still fit
         assert qg.qg_plan_info(kind, 1280, 8192, 4)["x_in_lds"]
+    # Q4_K stages each row's 32-weight block sums after its activations: 4 rows x 8
+    # segments x (4096 + 128) bytes, next to the eight wavefronts' partials
+    p = qg.qg_plan_info("q4_k", 1280, 8192, 4)
+    assert p["lds_bytes"] == 4 * 8 * 4224 + 8 * 4 * 8 * 4, p
+    # the RMSNorm kernels add the sums up per unit: their staged copy is the activations alone
+    for N in (8, 1024, 24000):
+        pk = qg.qg_plan_info("q4_k", N, 39936, 1, rmsnorm=True)
+        assert pk == qg.qg_plan_info("q4_0", N, 39936, 1, rmsnorm=True), (N, pk)
     # the RMSNorm prologue: K = 39936 (39 segments) fits next to the largest
     # static array; 40960 does not, for any form
     for kind in ("q8_0", "q4_0", "q4_k", "q6_k"):
