@@ -19,9 +19,12 @@ from gpu_helpers import THREADS, announce, assert_linear, sync, to_dev, torch_de
 pytestmark = pytest.mark.gpu
 
 # (N, K, M); M = 80 runs two groups of four activation tiles, the second with
-# three zero tiles, over a ragged 33-block K (its last chunk holds one block)
+# three zero tiles, over a ragged 33-block K (its last chunk holds one block).
+# The activation split holds a row in registers up to K = 32768, 1, 2 or 4 lane
+# runs per thread (K <= 8192, <= 16384, <= 32768: 12288 and 17408 take the
+# last two), and splits longer rows in two passes (40960)
 SHAPES = [(4096, 1024, 16), (1024, 3072, 8), (300, 2080, 20), (33, 1056, 1), (257, 5120, 40), (2048, 17408, 3),
-          (1000, 1024, 64), (17408, 5120, 32), (300, 1056, 80)]
+          (1000, 1024, 64), (17408, 5120, 32), (300, 1056, 80), (100, 12288, 5), (64, 40960, 3)]
 
 
 def _run(kind, packed, X, N, K, M, tail=0, ws=None):
