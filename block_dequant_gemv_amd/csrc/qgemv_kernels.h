@@ -130,8 +130,9 @@ constexpr int qgemv_max_threads(int QT, int M, int W)
 // range), so no accumulator lives from one unit to the next (Q4_0 at M = 6
 // with staged activations: 149 -> 111 VGPRs): Q4_0 fits 128 VGPRs at every M
 // (with activations from L2, or staged in phases, up to 4 rows), Q8_0 with staged activations up to 4
-// rows, 168 above; Q6_K fits 168 up to 3 rows (4 with staged activations) and
-// 256 without scratch at 5 and 6 (the general form spills there); Q4_K with 5
+// rows, 168 above; Q6_K fits 168 up to 3 rows (4, and 5 unphased, with staged
+// activations; Q6_K 17408 x 5120 at M = 5: 32.1-32.9 -> 30.9-31.4 us against 8
+// wavefronts) and 256 without scratch at 5 and 6 (the general form spills there); Q4_K with 5
 // rows and staged activations (whose block sums it reads instead of adding
 // them up) fits 256 at 8 wavefronts (Q4_K 17408 x 5120 at M = 5: 34.5 -> 29.3 us
 // against 4 wavefronts, the same bits).
@@ -141,7 +142,7 @@ constexpr int persist_threads(int qt, int M, bool xlds, bool one = false, bool p
     if (one) {
         if (qt == qgl::kQ4_0) return ((xlds && !(phased && M >= 5)) || M <= 4) ? 1024 : 768;
         if (qt == qgl::kQ8_0 && xlds) return M <= 4 ? 1024 : 768;
-        if (qt == qgl::kQ6_K) return (M <= 3 || (M == 4 && xlds)) ? 768 : 512;
+        if (qt == qgl::kQ6_K) return (M <= 3 || ((M == 4 || (M == 5 && !phased)) && xlds)) ? 768 : 512;
         if (qt == qgl::kQ4_K && M == 5 && xlds) return 512;
     }
     if (qt == qgl::kQ4_0) return M <= 3 ? 1024 : ((M <= 4 || xlds) ? 768 : 512);
